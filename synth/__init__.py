@@ -1,0 +1,15 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the oracle's checks.
+
+Holds random-number draws only; none of the reductions is computed here.
+"""
+
+from .workloads import (  # noqa: F401
+    WORKLOADS,
+    Workload,
+    constant_pair,
+    generate,
+    past53_fullrange,
+    past53_mixed,
+    sha256,
+    uniform_planes,
+)

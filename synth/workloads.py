@@ -1,0 +1,173 @@
+"""Seeded synthetic luma-plane workloads.
+
+This module only draws random sample values.  It computes none of the
+reductions: the oracle and the HIP library both receive the arrays it returns
+and nothing else from here.
+
+Layout of every batch: a C-contiguous numpy array ``[nframes][h][w]`` of
+``uint8`` (8 bits per component) or ``uint16`` (9..16 bits, value in the low
+bits), one array for the reference planes and one for the distorted planes.
+
+The five named workloads stand in for the clips the pages measure on (Netflix
+576x324, BBB and the checkerboards at 1920x1080 and 3840x2160, full-range
+noise and the bright 16-bit pair), none of which exists here.  Each workload
+has one ``numpy.random.Generator(PCG64(1000 + number))``; frames are drawn in
+order, for each frame first the reference plane, then the distorted plane.
+"Uniform a..b" below means integers with both ends included; "rint" is
+``numpy.rint`` (ties to even).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    number: int
+    name: str
+    w: int
+    h: int
+    nframes: int
+    bpc: int
+    recipe: str
+
+    @property
+    def dtype(self):
+        return np.uint8 if self.bpc == 8 else np.uint16
+
+    @property
+    def bytes_per_sample(self) -> int:
+        return 1 if self.bpc == 8 else 2
+
+    @property
+    def bytes_per_frame(self) -> int:
+        """Bytes read per frame: both planes, each read once."""
+        return 2 * self.w * self.h * self.bytes_per_sample
+
+    @property
+    def seed(self) -> int:
+        return 1000 + self.number
+
+
+WORKLOADS = {
+    1: Workload(1, "576x324 8-bit", 576, 324, 4, 8,
+                "ref uniform 0..255; dist = clip(ref + rint(N(0,8)), 0, 255)"),
+    2: Workload(2, "1920x1080 10-bit", 1920, 1080, 48, 10,
+                "ref = clip(rint(1023*(x/(w-1) + y/(h-1))/2 + N(0,40)), 0, 1023) "
+                "(a diagonal ramp with texture redrawn per frame); "
+                "dist = clip(ref + rint(N(0,16)), 0, 1023)"),
+    3: Workload(3, "3840x2160 12-bit", 3840, 2160, 32, 12,
+                "ref and dist independent uniform 0..4095 (full-range noise)"),
+    4: Workload(4, "1920x1080 16-bit bright", 1920, 1080, 40, 16,
+                "ref and dist independent uniform 56000..64000"),
+    5: Workload(5, "3840x2160 16-bit", 3840, 2160, 32, 16,
+                "ref uniform 60000..65535; dist = clip(ref + rint(N(0,512)), 0, 65535)"),
+}
+
+
+def _frame_pair(number: int, rng: np.random.Generator, w: int, h: int):
+    if number == 1:
+        ref = rng.integers(0, 255, size=(h, w), endpoint=True, dtype=np.int64)
+        dist = np.clip(ref + np.rint(rng.normal(0.0, 8.0, size=(h, w))).astype(np.int64), 0, 255)
+        return ref.astype(np.uint8), dist.astype(np.uint8)
+    if number == 2:
+        x = np.arange(w, dtype=np.float64)[None, :] / (w - 1)
+        y = np.arange(h, dtype=np.float64)[:, None] / (h - 1)
+        ramp = 1023.0 * (x + y) / 2.0
+        ref = np.clip(np.rint(ramp + rng.normal(0.0, 40.0, size=(h, w))), 0, 1023).astype(np.int64)
+        dist = np.clip(ref + np.rint(rng.normal(0.0, 16.0, size=(h, w))).astype(np.int64), 0, 1023)
+        return ref.astype(np.uint16), dist.astype(np.uint16)
+    if number == 3:
+        ref = rng.integers(0, 4095, size=(h, w), endpoint=True, dtype=np.uint16)
+        dist = rng.integers(0, 4095, size=(h, w), endpoint=True, dtype=np.uint16)
+        return ref, dist
+    if number == 4:
+        ref = rng.integers(56000, 64000, size=(h, w), endpoint=True, dtype=np.uint16)
+        dist = rng.integers(56000, 64000, size=(h, w), endpoint=True, dtype=np.uint16)
+        return ref, dist
+    if number == 5:
+        ref = rng.integers(60000, 65535, size=(h, w), endpoint=True, dtype=np.int64)
+        dist = np.clip(ref + np.rint(rng.normal(0.0, 512.0, size=(h, w))).astype(np.int64), 0, 65535)
+        return ref.astype(np.uint16), dist.astype(np.uint16)
+    raise ValueError(f"no workload {number}")
+
+
+def generate(number: int, nframes: int | None = None, w: int | None = None, h: int | None = None):
+    """Return ``(ref, dist)`` for a named workload.
+
+    ``nframes``, ``w`` and ``h`` default to the workload's own; a smaller
+    value draws the same recipe at another size (the first ``k`` frames at
+    the workload's own size are the same whatever ``nframes`` is).
+    """
+    wl = WORKLOADS[number]
+    nframes = wl.nframes if nframes is None else nframes
+    w = wl.w if w is None else w
+    h = wl.h if h is None else h
+    rng = np.random.Generator(np.random.PCG64(wl.seed))
+    ref = np.empty((nframes, h, w), dtype=wl.dtype)
+    dist = np.empty((nframes, h, w), dtype=wl.dtype)
+    for f in range(nframes):
+        ref[f], dist[f] = _frame_pair(number, rng, w, h)
+    return ref, dist
+
+
+def uniform_planes(w: int, h: int, nframes: int, bpc: int, seed: int,
+                   lo: int = 0, hi: int | None = None, container_max: bool = False):
+    """Independent uniform ref and dist planes with values lo..hi.
+
+    ``hi`` defaults to ``2**bpc - 1``.  With ``container_max`` the values span
+    the whole container (0..255 or 0..65535) whatever ``bpc`` says: samples
+    above ``2**bpc - 1`` are legal input and must be reduced like any other.
+    """
+    dtype = np.uint8 if bpc == 8 else np.uint16
+    if container_max:
+        hi = 255 if bpc == 8 else 65535
+    elif hi is None:
+        hi = (1 << bpc) - 1
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ref = rng.integers(lo, hi, size=(nframes, h, w), endpoint=True, dtype=dtype)
+    dist = rng.integers(lo, hi, size=(nframes, h, w), endpoint=True, dtype=dtype)
+    return ref, dist
+
+
+def past53_mixed(seed: int = 2053, w: int = 2560, h: int = 1440, nframes: int = 1):
+    """16-bit frames with a tenth of the samples below 4096.
+
+    Stand-in for the 2560x1440 frame past 2**53 units that the float_moment
+    page measures.  A tenth of the positions, drawn at random, get uniform
+    0..4095; the rest get uniform 49152..65535, bright enough that the sum of
+    the float squares of one plane passes 2**53 units.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for _ in range(2):
+        low = rng.random(size=(nframes, h, w)) < 0.1
+        dark = rng.integers(0, 4095, size=(nframes, h, w), endpoint=True, dtype=np.uint16)
+        bright = rng.integers(49152, 65535, size=(nframes, h, w), endpoint=True, dtype=np.uint16)
+        out.append(np.where(low, dark, bright).astype(np.uint16))
+    return out[0], out[1]
+
+
+def past53_fullrange(seed: int = 3053, w: int = 3840, h: int = 2160, nframes: int = 1):
+    """Independent full-range 16-bit noise (uniform 0..65535) in ref and dist."""
+    return uniform_planes(w, h, nframes, 16, seed, 0, 65535)
+
+
+def constant_pair(w: int, h: int, nframes: int, bpc: int, ref_value: int, dist_value: int):
+    """Constant planes: every ref sample ``ref_value``, every dist sample ``dist_value``."""
+    dtype = np.uint8 if bpc == 8 else np.uint16
+    ref = np.full((nframes, h, w), ref_value, dtype=dtype)
+    dist = np.full((nframes, h, w), dist_value, dtype=dtype)
+    return ref, dist
+
+
+def sha256(*arrays) -> str:
+    """Digest of the raw bytes of the given arrays, in order."""
+    m = hashlib.sha256()
+    for a in arrays:
+        m.update(np.ascontiguousarray(a).tobytes())
+    return m.hexdigest()
