@@ -1,0 +1,19 @@
+"""Bit-exact luma-plane reductions (float_psnr noise, float_moment sums) on MI355X.
+
+The product is libvqx.so (include/vqx.h): hand-written HIP kernels for
+gfx950 behind a C ABI.  ``vqx`` is its thin ctypes binding over torch device
+tensors and streams.
+"""
+
+from . import vqx  # noqa: F401
+from .vqx import (  # noqa: F401
+    VqxError,
+    abi_version,
+    conclude_batch,
+    conclude_moments,
+    conclude_psnr,
+    plane_stats_batch,
+    plane_stats_batch_ws,
+    plane_stats_workspace_bytes,
+    status_string,
+)

@@ -1,0 +1,39 @@
+// Launch geometry and launcher of the plane-stats kernels (internal to libvqx).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vqx {
+
+// Number of 64-bit sums in one partial record, in this order.
+enum : int { kNoise = 0, kRef1 = 1, kDist1 = 2, kRef2 = 3, kDist2 = 4, kSums = 5 };
+
+// Work split of one batch.  Each plane is read as 16-byte vectors; the
+// vectors of a frame that lie wholly inside it are cut into chunks of
+// chunk_vecs vectors, one workgroup per (frame, chunk).  The few samples of a
+// frame before its first whole vector and after its last (frames need not
+// start on a 16-byte boundary) are taken by chunk 0.
+struct Geometry {
+    int bpc;
+    int sample_bytes;     // 1 (uint8, bpc 8) or 2 (uint16)
+    int vec_elems;        // samples per 16-byte vector
+    int64_t pixels;       // w*h
+    int nframes;
+    int chunk_vecs;       // 16-byte vectors per plane per workgroup
+    int chunks;           // workgroups per frame
+    int64_t workgroups;   // nframes * chunks
+    size_t workspace_bytes;
+};
+
+Geometry make_geometry(int w, int h, int bpc, int nframes);
+
+// Queues both stages on `stream`, recording `stage1_begin`/`stage1_end` (if
+// not null) around stage 1.  Returns hipSuccess or the first error.
+hipError_t launch_plane_stats(const Geometry &g, const void *ref, const void *dist,
+                              uint64_t *out_noise, uint64_t *out_moments, uint64_t *partials,
+                              hipStream_t stream, hipEvent_t stage1_begin = nullptr,
+                              hipEvent_t stage1_end = nullptr);
+
+}  // namespace vqx

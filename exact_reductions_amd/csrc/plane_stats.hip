@@ -1,0 +1,369 @@
+// Stage 1 and stage 2 of the bit-exact plane reductions for gfx950 (CDNA4).
+//
+// Sources (web pages, cited by title and section):
+//   [PSNR]   "ADR-1440: float_psnr_hip adds its squared differences as
+//            integers and returns the CPU's score bit for bit"
+//   [MOMENT] "ADR-1447: float_moment_hip adds the float squares the CPU adds,
+//            and is bit-identical while the CPU's own sum is exact"
+//   [ADM]    "ADR-1423: adm_hip takes its weights, shifts and score
+//            conclusion from the CPU, folds the denominator once per row and
+//            clears its accumulators after the upload"
+//
+// Stage 1 streams both planes once with 16-byte loads.  Every term is an
+// exact integer: the float square of a sample or of a sample difference,
+// converted to uint32 [PSNR, Decision; MOMENT, Decision], or a sample itself.
+// Lanes add terms into uint32 accumulators whose bounds are proven below,
+// waves add lanes with DPP, the workgroup adds its four waves in uint64 and
+// writes one partial record.  Nothing is added into memory that was cleared
+// beforehand [ADM, Context and Decision]: each record is written whole.
+// Stage 2 adds a frame's records in uint64 and writes the frame's five sums.
+// Integer addition is exact and associative, so neither the tiling nor the
+// wave size can change a result [ADM, Alternatives: the integer sum makes
+// the reduction order irrelevant].
+//
+// 8 bits: every square is below 2^16 (< 2^24, exact in binary32 [PSNR,
+// Context]), so the float square IS the integer square, and the kernel uses
+// integer dot products: sum r, sum d (v_sad_u8), sum r^2, sum d^2, sum r*d
+// (v_dot4_u32_u8), and noise = sum r^2 + sum d^2 - 2 sum r*d, an identity of
+// integers.
+// 9..16 bits: each sample is converted to float and the three products
+// (r-d)^2, r^2, d^2 are taken in binary32, round to nearest even, then read
+// back as uint32 (below 2^32 [MOMENT, Decision]).  A uint32 term is added as
+// its low and high 16-bit halves into two uint32 accumulators, the split the
+// float_psnr page uses at 16 bits [PSNR, Decision].
+
+#include "plane_stats.h"
+
+#pragma clang fp contract(off)
+
+namespace vqx {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;              // four wave64s
+constexpr int kWaves = kThreads / 64;
+constexpr int kIters = 16;                 // 16-byte vectors per lane per plane
+constexpr int kChunkVecs = kThreads * kIters;  // 64 KiB of each plane per workgroup
+
+// ----------------------------------------------------------------- budgets
+// A lane sees at most kIters vectors plus one edge sample.
+//  8 bits: a lane's sum r^2 <= (16*16 + 1) * 255^2 = 16 711 425 < 2^24, so a
+//          wave's sum < 2^30; sum r and sum r*d are no larger.
+// 16 bits: a lane's 16-bit halves sum to <= (16*8 + 1) * 65535 < 2^23, so a
+//          wave's sum < 2^29; sum r likewise.
+// Each wave64 total therefore fits uint32; the workgroup adds its waves in
+// uint64.
+static_assert((kIters * 16 + 1) * 255ull * 255ull * 64ull < (1ull << 32), "8-bit wave budget");
+static_assert((kIters * 8 + 1) * 65535ull * 64ull < (1ull << 32), "16-bit wave budget");
+
+// --------------------------------------------------------------- 8-bit terms
+struct Acc8 {
+    uint32_t r1 = 0, d1 = 0, r2 = 0, d2 = 0, rd = 0;
+};
+
+// Four samples of each plane packed in one dword.
+__device__ __forceinline__ void add_dword(Acc8 &a, uint32_t r, uint32_t d)
+{
+    a.r1 = __builtin_amdgcn_sad_u8(r, 0u, a.r1);          // + r0 + r1 + r2 + r3
+    a.d1 = __builtin_amdgcn_sad_u8(d, 0u, a.d1);
+    a.r2 = __builtin_amdgcn_udot4(r, r, a.r2, false);     // + sum r_i^2
+    a.d2 = __builtin_amdgcn_udot4(d, d, a.d2, false);
+    a.rd = __builtin_amdgcn_udot4(r, d, a.rd, false);     // + sum r_i*d_i
+}
+
+// -------------------------------------------------------------- 16-bit terms
+struct Acc16 {
+    uint32_t n_lo = 0, n_hi = 0, r1 = 0, d1 = 0, r2_lo = 0, r2_hi = 0, d2_lo = 0, d2_hi = 0;
+};
+
+// The float square of x read back as an integer: one binary32 product, round
+// to nearest even, then an exact conversion (the product is an integer below
+// 2^32) [MOMENT, Decision].
+__device__ __forceinline__ uint32_t float_square(float x)
+{
+    const float p = x * x;
+    return static_cast<uint32_t>(p);
+}
+
+__device__ __forceinline__ void add_halves(uint32_t &lo, uint32_t &hi, uint32_t t)
+{
+    lo += t & 0xffffu;
+    hi += t >> 16;
+}
+
+// Two samples of each plane packed in one dword.
+__device__ __forceinline__ void add_dword(Acc16 &a, uint32_t r, uint32_t d)
+{
+    const float r0 = static_cast<float>(r & 0xffffu), r1 = static_cast<float>(r >> 16);
+    const float d0 = static_cast<float>(d & 0xffffu), d1 = static_cast<float>(d >> 16);
+    // float_psnr: the square of the float difference [PSNR, Decision]
+    add_halves(a.n_lo, a.n_hi, float_square(r0 - d0));
+    add_halves(a.n_lo, a.n_hi, float_square(r1 - d1));
+    // float_moment: the float squares of the samples [MOMENT, Decision]
+    add_halves(a.r2_lo, a.r2_hi, float_square(r0));
+    add_halves(a.r2_lo, a.r2_hi, float_square(r1));
+    add_halves(a.d2_lo, a.d2_hi, float_square(d0));
+    add_halves(a.d2_lo, a.d2_hi, float_square(d1));
+    // the sample sums: r0 + r1 in one integer dot product
+    const u16x2 ones = {1, 1};
+    a.r1 = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, r), ones, a.r1, false);
+    a.d1 = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, d), ones, a.d1, false);
+}
+
+template <class Acc>
+__device__ __forceinline__ void add_vec(Acc &a, const u32x4 &r, const u32x4 &d)
+{
+    add_dword(a, r.x, d.x);
+    add_dword(a, r.y, d.y);
+    add_dword(a, r.z, d.z);
+    add_dword(a, r.w, d.w);
+}
+
+// ---------------------------------------------------------- wave64 reduction
+// Sum of v over the 64 lanes, returned to every lane.  Four DPP steps add
+// within each row of 16 lanes; row_bcast:15 and row_bcast:31 carry rows into
+// rows 1..3, so lane 63 ends with the total, which readlane broadcasts.
+__device__ __forceinline__ uint32_t dpp_step(uint32_t v, int ctrl_sel)
+{
+    switch (ctrl_sel) {
+    case 0: return __builtin_amdgcn_update_dpp(0u, v, 0xb1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
+    case 1: return __builtin_amdgcn_update_dpp(0u, v, 0x4e, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
+    case 2: return __builtin_amdgcn_update_dpp(0u, v, 0x124, 0xf, 0xf, false);  // row_ror:4
+    case 3: return __builtin_amdgcn_update_dpp(0u, v, 0x128, 0xf, 0xf, false);  // row_ror:8
+    case 4: return __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+    default: return __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false); // row_bcast:31 -> rows 2, 3
+    }
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v)
+{
+    v += dpp_step(v, 0);
+    v += dpp_step(v, 1);
+    v += dpp_step(v, 2);
+    v += dpp_step(v, 3);
+    v += dpp_step(v, 4);
+    v += dpp_step(v, 5);
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Adds every lane's accumulators of the workgroup: every thread gets the N
+// totals in uint64.  All threads must call it.
+template <int N>
+__device__ __forceinline__ void workgroup_sums(const uint32_t (&v)[N], uint64_t (&out)[N])
+{
+    __shared__ uint32_t lds[kWaves][N];
+    const int wave = threadIdx.x / 64;
+    uint32_t w[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+        w[k] = wave_sum(v[k]);
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+        for (int k = 0; k < N; ++k)
+            lds[wave][k] = w[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        uint64_t s = 0;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i)
+            s += lds[i][k];
+        out[k] = s;
+    }
+}
+
+__device__ __forceinline__ void write_record(uint64_t *part, int64_t nwg, int64_t wg,
+                                             uint64_t noise, uint64_t r1, uint64_t d1,
+                                             uint64_t r2, uint64_t d2)
+{
+    if (threadIdx.x == 0) {
+        part[kNoise * nwg + wg] = noise;
+        part[kRef1 * nwg + wg] = r1;
+        part[kDist1 * nwg + wg] = d1;
+        part[kRef2 * nwg + wg] = r2;
+        part[kDist2 * nwg + wg] = d2;
+    }
+}
+
+// One sample of each plane as the low lane of a dword (the other lanes zero,
+// which add nothing to any sum: q(0) = 0).
+template <int kBytes>
+__device__ __forceinline__ uint32_t load_sample(const void *plane, int64_t i)
+{
+    if constexpr (kBytes == 1)
+        return static_cast<const uint8_t *>(plane)[i];
+    else
+        return static_cast<const uint16_t *>(plane)[i];
+}
+
+// ------------------------------------------------------------------ stage 1
+template <int kBytes, class Acc>
+__device__ __forceinline__ void accumulate_chunk(Acc &acc, const void *ref, const void *dist,
+                                                 int64_t pixels, int chunk, int64_t frame)
+{
+    constexpr int V = 16 / kBytes;  // samples per vector
+    const int64_t e0 = frame * pixels;  // first sample of the frame
+    const int64_t e1 = e0 + pixels;
+    const int64_t vb = (e0 + V - 1) / V;  // first whole vector
+    const int64_t ve = e1 / V;            // one past the last whole vector
+
+    if (chunk == 0) {
+        // samples outside the whole vectors: fewer than 2V in all
+        const int64_t head_end = vb < ve ? vb * V : e1;
+        const int64_t tail_begin = vb < ve ? ve * V : e1;
+        const int head = static_cast<int>(head_end - e0);
+        const int tail = static_cast<int>(e1 - tail_begin);
+        const int t = threadIdx.x;
+        if (t < head + tail) {
+            const int64_t i = t < head ? e0 + t : tail_begin + (t - head);
+            add_dword(acc, load_sample<kBytes>(ref, i), load_sample<kBytes>(dist, i));
+        }
+    }
+    if (vb >= ve)
+        return;
+
+    const u32x4 *R = static_cast<const u32x4 *>(ref);
+    const u32x4 *D = static_cast<const u32x4 *>(dist);
+    const int64_t cb = vb + static_cast<int64_t>(chunk) * kChunkVecs;
+    const int64_t ce = cb + kChunkVecs < ve ? cb + kChunkVecs : ve;
+    if (ce - cb == kChunkVecs) {
+        const u32x4 *r = R + cb + threadIdx.x;
+        const u32x4 *d = D + cb + threadIdx.x;
+#pragma unroll 4
+        for (int i = 0; i < kIters; ++i) {
+            const u32x4 a = __builtin_nontemporal_load(r + i * kThreads);
+            const u32x4 b = __builtin_nontemporal_load(d + i * kThreads);
+            add_vec(acc, a, b);
+        }
+    } else {
+        for (int64_t v = cb + threadIdx.x; v < ce; v += kThreads) {
+            const u32x4 a = __builtin_nontemporal_load(R + v);
+            const u32x4 b = __builtin_nontemporal_load(D + v);
+            add_vec(acc, a, b);
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void stage1_u8(const void *ref, const void *dist,
+                                                      int64_t pixels, int chunks, int64_t nwg,
+                                                      uint64_t *part)
+{
+    const int64_t wg = blockIdx.x;
+    const int64_t frame = wg / chunks;
+    const int chunk = static_cast<int>(wg - frame * chunks);
+    Acc8 a;
+    accumulate_chunk<1>(a, ref, dist, pixels, chunk, frame);
+    const uint32_t v[5] = {a.r1, a.d1, a.r2, a.d2, a.rd};
+    uint64_t s[5];
+    workgroup_sums(v, s);
+    // sum (r-d)^2 = sum r^2 + sum d^2 - 2 sum r*d, exact in uint64
+    write_record(part, nwg, wg, s[2] + s[3] - 2 * s[4], s[0], s[1], s[2], s[3]);
+}
+
+__global__ __launch_bounds__(kThreads) void stage1_u16(const void *ref, const void *dist,
+                                                       int64_t pixels, int chunks, int64_t nwg,
+                                                       uint64_t *part)
+{
+    const int64_t wg = blockIdx.x;
+    const int64_t frame = wg / chunks;
+    const int chunk = static_cast<int>(wg - frame * chunks);
+    Acc16 a;
+    accumulate_chunk<2>(a, ref, dist, pixels, chunk, frame);
+    const uint32_t v[8] = {a.n_lo, a.n_hi, a.r1, a.d1, a.r2_lo, a.r2_hi, a.d2_lo, a.d2_hi};
+    uint64_t s[8];
+    workgroup_sums(v, s);
+    write_record(part, nwg, wg, s[0] + (s[1] << 16), s[2], s[3], s[4] + (s[5] << 16),
+                 s[6] + (s[7] << 16));
+}
+
+// ------------------------------------------------------------------ stage 2
+// One workgroup per frame adds the frame's records in uint64.
+constexpr int kCombineThreads = 256;
+
+__global__ __launch_bounds__(kCombineThreads) void stage2_combine(const uint64_t *part, int chunks,
+                                                                  int64_t nwg, uint64_t *out_noise,
+                                                                  uint64_t *out_moments)
+{
+    __shared__ uint64_t lds[kSums][kCombineThreads];
+    const int64_t frame = blockIdx.x;
+    const int t = threadIdx.x;
+    uint64_t s[kSums] = {0, 0, 0, 0, 0};
+    for (int c = t; c < chunks; c += kCombineThreads) {
+#pragma unroll
+        for (int k = 0; k < kSums; ++k)
+            s[k] += part[k * nwg + frame * chunks + c];
+    }
+#pragma unroll
+    for (int k = 0; k < kSums; ++k)
+        lds[k][t] = s[k];
+    __syncthreads();
+    for (int off = kCombineThreads / 2; off > 0; off >>= 1) {
+        if (t < off) {
+#pragma unroll
+            for (int k = 0; k < kSums; ++k)
+                lds[k][t] += lds[k][t + off];
+        }
+        __syncthreads();
+    }
+    if (t == 0) {
+        out_noise[frame] = lds[kNoise][0];
+        out_moments[4 * frame + 0] = lds[kRef1][0];
+        out_moments[4 * frame + 1] = lds[kDist1][0];
+        out_moments[4 * frame + 2] = lds[kRef2][0];
+        out_moments[4 * frame + 3] = lds[kDist2][0];
+    }
+}
+
+}  // namespace
+
+Geometry make_geometry(int w, int h, int bpc, int nframes)
+{
+    Geometry g{};
+    g.bpc = bpc;
+    g.sample_bytes = bpc == 8 ? 1 : 2;
+    g.vec_elems = 16 / g.sample_bytes;
+    g.pixels = static_cast<int64_t>(w) * h;
+    g.nframes = nframes;
+    g.chunk_vecs = kChunkVecs;
+    // A frame holds at most floor(pixels / vec_elems) whole vectors.
+    const int64_t max_vecs = g.pixels / g.vec_elems;
+    const int64_t chunks = (max_vecs + kChunkVecs - 1) / kChunkVecs;
+    g.chunks = static_cast<int>(chunks < 1 ? 1 : chunks);
+    g.workgroups = static_cast<int64_t>(g.chunks) * nframes;
+    g.workspace_bytes = static_cast<size_t>(g.workgroups) * kSums * sizeof(uint64_t);
+    return g;
+}
+
+hipError_t launch_plane_stats(const Geometry &g, const void *ref, const void *dist,
+                              uint64_t *out_noise, uint64_t *out_moments, uint64_t *partials,
+                              hipStream_t stream, hipEvent_t stage1_begin, hipEvent_t stage1_end)
+{
+    const dim3 grid1(static_cast<unsigned>(g.workgroups));
+    if (stage1_begin) {
+        hipError_t e = hipEventRecord(stage1_begin, stream);
+        if (e != hipSuccess)
+            return e;
+    }
+    if (g.sample_bytes == 1)
+        stage1_u8<<<grid1, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, g.workgroups,
+                                                  partials);
+    else
+        stage1_u16<<<grid1, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, g.workgroups,
+                                                   partials);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    if (stage1_end) {
+        err = hipEventRecord(stage1_end, stream);
+        if (err != hipSuccess)
+            return err;
+    }
+    stage2_combine<<<dim3(static_cast<unsigned>(g.nframes)), kCombineThreads, 0, stream>>>(
+        partials, g.chunks, g.workgroups, out_noise, out_moments);
+    return hipGetLastError();
+}
+
+}  // namespace vqx

@@ -1,0 +1,230 @@
+// C ABI of libvqx: argument checks, workspace, launches and the host-side
+// conclusions.  Declarations and argument contracts are in include/vqx.h.
+//
+// Sources (web pages, cited by title and section):
+//   [PSNR]   "ADR-1440: float_psnr_hip adds its squared differences as
+//            integers and returns the CPU's score bit for bit"
+//   [MOMENT] "ADR-1447: float_moment_hip adds the float squares the CPU adds,
+//            and is bit-identical while the CPU's own sum is exact"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "plane_stats.h"
+#include "vqx.h"
+
+#pragma clang fp contract(off)
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Shape checks shared by every entry point; no device call.
+int check_shape(int w, int h, int bpc)
+{
+    if (w < 1 || h < 1 || static_cast<int64_t>(w) * h > VQX_MAX_PIXELS)
+        return VQX_E_DIMS;
+    if (bpc < 8 || bpc > 16)
+        return VQX_E_BPC;
+    return VQX_OK;
+}
+
+int check_batch(int w, int h, int bpc, int nframes)
+{
+    int rc = check_shape(w, h, bpc);
+    if (rc != VQX_OK)
+        return rc;
+    if (nframes < 1)
+        return VQX_E_NFRAMES;
+    // one workgroup per (frame, chunk) must fit a 1-D grid
+    if (vqx::make_geometry(w, h, bpc, nframes).workgroups > INT32_MAX)
+        return VQX_E_NFRAMES;
+    return VQX_OK;
+}
+
+// All argument checks of the plane-stats entry points, in a fixed order.
+int check_stats_args(const void *ref, const void *dist, int w, int h, int bpc, int nframes,
+                     const uint64_t *out_noise, const uint64_t *out_moments)
+{
+    if (!ref || !dist || !out_noise || !out_moments)
+        return VQX_E_NULL;
+    int rc = check_batch(w, h, bpc, nframes);
+    if (rc != VQX_OK)
+        return rc;
+    if (!aligned(ref, 16) || !aligned(dist, 16) || !aligned(out_noise, 8) || !aligned(out_moments, 8))
+        return VQX_E_ALIGN;
+    return VQX_OK;
+}
+
+int device_ready()
+{
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n < 1) {
+        (void)hipGetLastError();
+        return VQX_E_NO_DEVICE;
+    }
+    return VQX_OK;
+}
+
+// (double)v rounds to nearest even, and only once v passes 2^53 [MOMENT,
+// Decision]; the divisions by s^k are by powers of two and exact.
+double unit_mean(uint64_t v, int power, int bpc, int64_t pixels)
+{
+    const double s = static_cast<double>(1 << (bpc - 8));
+    const double scale = power == 2 ? s * s : s;
+    return (static_cast<double>(v) / scale) / static_cast<double>(pixels);
+}
+
+double psnr_from_mse(double mse, int bpc, double psnr_max)
+{
+    if (mse == 0.0)
+        return psnr_max > 0.0 ? psnr_max : HUGE_VAL;
+    const double peak = static_cast<double>((1 << bpc) - 1) / static_cast<double>(1 << (bpc - 8));
+    const double db = 10.0 * log10(peak * peak / mse);
+    return (psnr_max > 0.0 && db > psnr_max) ? psnr_max : db;
+}
+
+}  // namespace
+
+extern "C" {
+
+int vqx_abi_version(void) { return VQX_ABI_VERSION; }
+
+const char *vqx_status_string(int status)
+{
+    switch (status) {
+    case VQX_OK: return "ok";
+    case VQX_E_NULL: return "a required pointer is NULL";
+    case VQX_E_DIMS: return "w and h must be >= 1 with w*h <= 2^25";
+    case VQX_E_BPC: return "bpc must be 8..16";
+    case VQX_E_NFRAMES: return "nframes must be >= 1 (and the batch must fit one launch)";
+    case VQX_E_ALIGN: return "ref/dist must be 16-byte aligned and outputs 8-byte aligned";
+    case VQX_E_WORKSPACE: return "workspace missing, misaligned or smaller than vqx_plane_stats_workspace_bytes()";
+    case VQX_E_HIP: return "the HIP runtime reported an error";
+    case VQX_E_NO_DEVICE: return "no usable HIP device";
+    default: return "unknown status";
+    }
+}
+
+int vqx_plane_stats_workspace_bytes(int w, int h, int bpc, int nframes, size_t *bytes)
+{
+    if (!bytes)
+        return VQX_E_NULL;
+    int rc = check_batch(w, h, bpc, nframes);
+    if (rc != VQX_OK)
+        return rc;
+    *bytes = vqx::make_geometry(w, h, bpc, nframes).workspace_bytes;
+    return VQX_OK;
+}
+
+int vqx_plane_stats_batch_ws_timed(const void *ref, const void *dist, int w, int h, int bpc,
+                                   int nframes, uint64_t *out_noise, uint64_t *out_moments,
+                                   void *workspace, size_t workspace_bytes, void *stream,
+                                   void *stage1_begin, void *stage1_end)
+{
+    int rc = check_stats_args(ref, dist, w, h, bpc, nframes, out_noise, out_moments);
+    if (rc != VQX_OK)
+        return rc;
+    const vqx::Geometry g = vqx::make_geometry(w, h, bpc, nframes);
+    if (!workspace || !aligned(workspace, 16) || workspace_bytes < g.workspace_bytes)
+        return VQX_E_WORKSPACE;
+    rc = device_ready();
+    if (rc != VQX_OK)
+        return rc;
+    hipError_t err = vqx::launch_plane_stats(g, ref, dist, out_noise, out_moments,
+                                             static_cast<uint64_t *>(workspace),
+                                             static_cast<hipStream_t>(stream),
+                                             static_cast<hipEvent_t>(stage1_begin),
+                                             static_cast<hipEvent_t>(stage1_end));
+    if (err != hipSuccess) {
+        (void)hipGetLastError();
+        return VQX_E_HIP;
+    }
+    return VQX_OK;
+}
+
+int vqx_plane_stats_batch_ws(const void *ref, const void *dist, int w, int h, int bpc, int nframes,
+                             uint64_t *out_noise, uint64_t *out_moments, void *workspace,
+                             size_t workspace_bytes, void *stream)
+{
+    return vqx_plane_stats_batch_ws_timed(ref, dist, w, h, bpc, nframes, out_noise, out_moments,
+                                          workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+int vqx_plane_stats_batch(const void *ref, const void *dist, int w, int h, int bpc, int nframes,
+                          uint64_t *out_noise, uint64_t *out_moments, void *stream)
+{
+    int rc = check_stats_args(ref, dist, w, h, bpc, nframes, out_noise, out_moments);
+    if (rc != VQX_OK)
+        return rc;
+    rc = device_ready();
+    if (rc != VQX_OK)
+        return rc;
+    const vqx::Geometry g = vqx::make_geometry(w, h, bpc, nframes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void *ws = nullptr;
+    if (hipMallocAsync(&ws, g.workspace_bytes, s) != hipSuccess) {
+        (void)hipGetLastError();
+        return VQX_E_HIP;
+    }
+    hipError_t err = vqx::launch_plane_stats(g, ref, dist, out_noise, out_moments,
+                                             static_cast<uint64_t *>(ws), s);
+    // freed in stream order, after the kernels that use it
+    hipError_t ferr = hipFreeAsync(ws, s);
+    if (err != hipSuccess || ferr != hipSuccess) {
+        (void)hipGetLastError();
+        return VQX_E_HIP;
+    }
+    return VQX_OK;
+}
+
+int vqx_conclude_psnr(uint64_t noise, int w, int h, int bpc, double psnr_max, double *mse,
+                      double *psnr_db)
+{
+    int rc = check_shape(w, h, bpc);
+    if (rc != VQX_OK)
+        return rc;
+    const double m = unit_mean(noise, 2, bpc, static_cast<int64_t>(w) * h);
+    if (mse)
+        *mse = m;
+    if (psnr_db)
+        *psnr_db = psnr_from_mse(m, bpc, psnr_max);
+    return VQX_OK;
+}
+
+int vqx_conclude_moments(const uint64_t sums[4], int w, int h, int bpc, double out[4])
+{
+    if (!sums || !out)
+        return VQX_E_NULL;
+    int rc = check_shape(w, h, bpc);
+    if (rc != VQX_OK)
+        return rc;
+    const int64_t pixels = static_cast<int64_t>(w) * h;
+    const int power[4] = {1, 1, 2, 2};
+    double tmp[4];
+    for (int k = 0; k < 4; ++k)
+        tmp[k] = unit_mean(sums[k], power[k], bpc, pixels);
+    for (int k = 0; k < 4; ++k)
+        out[k] = tmp[k];
+    return VQX_OK;
+}
+
+int vqx_conclude_batch(const uint64_t *noise, const uint64_t *moments, int w, int h, int bpc,
+                       int nframes, double psnr_max, double *out)
+{
+    if (!noise || !moments || !out)
+        return VQX_E_NULL;
+    int rc = check_shape(w, h, bpc);
+    if (rc != VQX_OK)
+        return rc;
+    if (nframes < 1)
+        return VQX_E_NFRAMES;
+    for (int f = 0; f < nframes; ++f) {
+        double *o = out + 6 * static_cast<size_t>(f);
+        vqx_conclude_psnr(noise[f], w, h, bpc, psnr_max, &o[0], &o[1]);
+        vqx_conclude_moments(moments + 4 * static_cast<size_t>(f), w, h, bpc, &o[2]);
+    }
+    return VQX_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,196 @@
+"""ctypes binding of libvqx (include/vqx.h), same names without the prefix.
+
+Argument marshalling only: every step of the reduction runs in libvqx's HIP
+kernels, and the conclusions in libvqx's host code.  Torch supplies device
+memory and the current stream.  There is no fallback: if libvqx.so is not
+built, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libvqx.so")
+
+OK = 0
+E_NULL, E_DIMS, E_BPC, E_NFRAMES, E_ALIGN, E_WORKSPACE, E_HIP, E_NO_DEVICE = range(-1, -9, -1)
+MAX_PIXELS = 1 << 25
+
+# Every symbol include/vqx.h declares.
+SYMBOLS = (
+    "vqx_abi_version",
+    "vqx_status_string",
+    "vqx_plane_stats_workspace_bytes",
+    "vqx_plane_stats_batch",
+    "vqx_plane_stats_batch_ws",
+    "vqx_plane_stats_batch_ws_timed",
+    "vqx_conclude_psnr",
+    "vqx_conclude_moments",
+    "vqx_conclude_batch",
+)
+
+
+class VqxError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libvqx; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError(f"{LIBRARY} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIBRARY)
+        vp, i, u64, sz, d = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_double
+        sigs = {
+            "vqx_abi_version": (i, []),
+            "vqx_status_string": (ctypes.c_char_p, [i]),
+            "vqx_plane_stats_workspace_bytes": (i, [i, i, i, i, ctypes.POINTER(sz)]),
+            "vqx_plane_stats_batch": (i, [vp, vp, i, i, i, i, vp, vp, vp]),
+            "vqx_plane_stats_batch_ws": (i, [vp, vp, i, i, i, i, vp, vp, vp, sz, vp]),
+            "vqx_plane_stats_batch_ws_timed": (i, [vp, vp, i, i, i, i, vp, vp, vp, sz, vp, vp, vp]),
+            "vqx_conclude_psnr": (i, [u64, i, i, i, d, ctypes.POINTER(d), ctypes.POINTER(d)]),
+            "vqx_conclude_moments": (i, [vp, i, i, i, vp]),
+            "vqx_conclude_batch": (i, [vp, vp, i, i, i, i, d, vp]),
+        }
+        for name, (res, args) in sigs.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def abi_version() -> int:
+    return lib().vqx_abi_version()
+
+
+def status_string(status: int) -> str:
+    return lib().vqx_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise VqxError(status, where)
+
+
+def plane_stats_workspace_bytes(w: int, h: int, bpc: int, nframes: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().vqx_plane_stats_workspace_bytes(w, h, bpc, nframes, ctypes.byref(out)),
+           "plane_stats_workspace_bytes")
+    return out.value
+
+
+def _planes(ref, dist, bpc):
+    import torch
+    if ref.dim() == 2:
+        ref, dist = ref.unsqueeze(0), dist.unsqueeze(0)
+    if ref.dim() != 3 or ref.shape != dist.shape:
+        raise ValueError("ref and dist must both be [nframes][h][w] (or [h][w])")
+    want = (torch.uint8,) if bpc == 8 else (torch.uint16, torch.int16)
+    if ref.dtype not in want or dist.dtype not in want:
+        raise TypeError(f"bpc {bpc} wants {'uint8' if bpc == 8 else 'uint16'} samples")
+    if not (ref.is_cuda and dist.is_cuda and ref.device == dist.device):
+        raise ValueError("ref and dist must be on one GPU")
+    if not (ref.is_contiguous() and dist.is_contiguous()):
+        raise ValueError("ref and dist must be contiguous")
+    return ref, dist
+
+
+def _stream_handle(device, stream):
+    import torch
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return s.cuda_stream
+
+
+def plane_stats_batch_ws(ref, dist, bpc: int, out_noise, out_moments, workspace, stream=None):
+    """Queue the five sums of every frame into ``out_noise`` [F] and
+    ``out_moments`` [F][4] (int64 device tensors), with a caller workspace
+    (a device tensor of at least plane_stats_workspace_bytes bytes)."""
+    ref, dist = _planes(ref, dist, bpc)
+    f, h, w = ref.shape
+    _check(lib().vqx_plane_stats_batch_ws(
+        ref.data_ptr(), dist.data_ptr(), w, h, bpc, f, out_noise.data_ptr(), out_moments.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream_handle(ref.device, stream)), "plane_stats_batch_ws")
+    return out_noise, out_moments
+
+
+def plane_stats_batch_ws_timed(ref, dist, bpc: int, out_noise, out_moments, workspace,
+                               stage1_begin, stage1_end, stream=None):
+    """plane_stats_batch_ws that records two hipEvent_t handles (ints) around
+    the streaming kernel on the stream."""
+    ref, dist = _planes(ref, dist, bpc)
+    f, h, w = ref.shape
+    _check(lib().vqx_plane_stats_batch_ws_timed(
+        ref.data_ptr(), dist.data_ptr(), w, h, bpc, f, out_noise.data_ptr(), out_moments.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream_handle(ref.device, stream), stage1_begin, stage1_end), "plane_stats_batch_ws_timed")
+    return out_noise, out_moments
+
+
+def plane_stats_batch(ref, dist, bpc: int, stream=None, out_noise=None, out_moments=None):
+    """The five exact sums of every frame: ``(noise [F], moments [F][4])`` as
+    int64 device tensors (the uint64 values, all below 2^58).  The workspace
+    comes from torch's caching allocator; the call only queues work on the
+    current (or given) stream."""
+    import torch
+    ref, dist = _planes(ref, dist, bpc)
+    f, h, w = ref.shape
+    dev = ref.device
+    if out_noise is None:
+        out_noise = torch.empty(f, dtype=torch.int64, device=dev)
+    if out_moments is None:
+        out_moments = torch.empty((f, 4), dtype=torch.int64, device=dev)
+    ws = torch.empty(plane_stats_workspace_bytes(w, h, bpc, f), dtype=torch.uint8, device=dev)
+    return plane_stats_batch_ws(ref, dist, bpc, out_noise, out_moments, ws, stream)
+
+
+def plane_stats_batch_selfalloc(ref, dist, bpc: int, out_noise, out_moments, stream=None):
+    """vqx_plane_stats_batch itself: the library allocates its scratch with
+    hipMallocAsync on the stream."""
+    ref, dist = _planes(ref, dist, bpc)
+    f, h, w = ref.shape
+    _check(lib().vqx_plane_stats_batch(
+        ref.data_ptr(), dist.data_ptr(), w, h, bpc, f, out_noise.data_ptr(), out_moments.data_ptr(),
+        _stream_handle(ref.device, stream)), "plane_stats_batch")
+    return out_noise, out_moments
+
+
+def conclude_psnr(noise: int, w: int, h: int, bpc: int, psnr_max: float = 0.0):
+    """(mse, psnr_db) of one frame from its exact noise (host)."""
+    mse, db = ctypes.c_double(), ctypes.c_double()
+    _check(lib().vqx_conclude_psnr(int(noise), w, h, bpc, float(psnr_max), ctypes.byref(mse),
+                                   ctypes.byref(db)), "conclude_psnr")
+    return mse.value, db.value
+
+
+def conclude_moments(sums4, w: int, h: int, bpc: int) -> np.ndarray:
+    """The four means of one frame from {ref1, dist1, ref2, dist2} (host)."""
+    s = np.ascontiguousarray(np.asarray(sums4, dtype=np.uint64).reshape(4))
+    out = np.zeros(4, dtype=np.float64)
+    _check(lib().vqx_conclude_moments(s.ctypes.data, w, h, bpc, out.ctypes.data), "conclude_moments")
+    return out
+
+
+def conclude_batch(noise, moments, w: int, h: int, bpc: int, psnr_max: float = 0.0) -> np.ndarray:
+    """[F][6] {mse, psnr_db, ref_mean, dist_mean, ref_mean_sq, dist_mean_sq}
+    from host copies of the sums (numpy or CPU tensors)."""
+    n = np.ascontiguousarray(np.asarray(noise).astype(np.uint64).reshape(-1))
+    m = np.ascontiguousarray(np.asarray(moments).astype(np.uint64).reshape(-1, 4))
+    f = n.shape[0]
+    if m.shape[0] != f:
+        raise ValueError("noise and moments disagree on nframes")
+    out = np.zeros((f, 6), dtype=np.float64)
+    _check(lib().vqx_conclude_batch(n.ctypes.data, m.ctypes.data, w, h, bpc, f, float(psnr_max),
+                                    out.ctypes.data), "conclude_batch")
+    return out

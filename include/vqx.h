@@ -1,0 +1,170 @@
+/*
+ * vqx -- bit-exact luma-plane reductions for float_psnr and float_moment on
+ * AMD Instinct MI355X (gfx950).  C ABI: plain pointers and sizes only.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [PSNR]   "ADR-1440: float_psnr_hip adds its squared differences as
+ *            integers and returns the CPU's score bit for bit"
+ *   [MOMENT] "ADR-1447: float_moment_hip adds the float squares the CPU
+ *            adds, and is bit-identical while the CPU's own sum is exact"
+ *   [ADM]    "ADR-1423: adm_hip takes its weights, shifts and score
+ *            conclusion from the CPU, folds the denominator once per row and
+ *            clears its accumulators after the upload"
+ *
+ * Terms and units.  For a frame of w*h samples at bpc bits per component,
+ * scaler s = 2^(bpc-8) [PSNR, Context].  q(x) is the binary32 product x*x of
+ * the sample value x (or sample difference) converted to float, rounded to
+ * nearest even and read back as an integer; it is below 2^32 for every
+ * 16-bit value [MOMENT, Decision].  Dividing a sample by s before squaring
+ * does not change which bits that product drops, so q(x) is the CPU's float
+ * term expressed in units of 1/s^2 [MOMENT, Decision; PSNR, Decision].
+ *
+ * Per frame the library returns five exact integer sums:
+ *   noise = sum q(ref - dist)  (units 1/s^2; float_psnr's noise [PSNR, Decision])
+ *   ref1  = sum ref,  dist1 = sum dist          (units 1/s)
+ *   ref2  = sum q(ref), dist2 = sum q(dist)      (units 1/s^2)
+ *   (float_moment's four sums [MOMENT, Context and Decision]).
+ * No term is rounded after the float product and no sum is ever rounded, so
+ * the sums are the exact integers whatever the summation order.  While a sum
+ * is below 2^53 units it equals the CPU's running double times the unit, bit
+ * for bit [PSNR, Context; MOMENT, Decision]; past 2^53 the CPU's own double
+ * rounds and these sums stay exact [PSNR, Consequences; MOMENT, Decision].
+ *
+ * Status codes: every entry point returns VQX_OK (0) or a negative VQX_E_*.
+ * An argument error is reported before anything is queued and leaves every
+ * output untouched.
+ */
+#ifndef VQX_H
+#define VQX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VQX_ABI_VERSION 1
+
+/* Largest frame accepted: 2^25 samples (an 8K frame, 7680x4320, has
+ * 33 177 600).  Up to 12 bits the CPU's noise then needs at most 49 bits
+ * [PSNR, Context]; every device sum stays below 2^57. */
+#define VQX_MAX_PIXELS (1 << 25)
+
+enum vqx_status {
+    VQX_OK = 0,
+    VQX_E_NULL = -1,      /* a required pointer is NULL */
+    VQX_E_DIMS = -2,      /* w < 1, h < 1 or w*h > VQX_MAX_PIXELS */
+    VQX_E_BPC = -3,       /* bpc outside 8..16 */
+    VQX_E_NFRAMES = -4,   /* nframes < 1 */
+    VQX_E_ALIGN = -5,     /* ref/dist not 16-byte aligned, or an output not 8-byte aligned */
+    VQX_E_WORKSPACE = -6, /* workspace smaller than vqx_plane_stats_workspace_bytes() */
+    VQX_E_HIP = -7,       /* the HIP runtime reported an error (launch or allocation) */
+    VQX_E_NO_DEVICE = -8  /* no usable HIP device */
+};
+
+/* VQX_ABI_VERSION of the loaded library. */
+int vqx_abi_version(void);
+
+/* Static English text for a status code; never NULL. */
+const char *vqx_status_string(int status);
+
+/*
+ * Device scratch needed by vqx_plane_stats_batch_ws for this batch shape
+ * (one partial record per workgroup).  Writes *bytes; host-only, no device
+ * call.  Errors: VQX_E_NULL, VQX_E_DIMS, VQX_E_BPC, VQX_E_NFRAMES.
+ */
+int vqx_plane_stats_workspace_bytes(int w, int h, int bpc, int nframes, size_t *bytes);
+
+/*
+ * The five exact sums of every frame of a batch, in one pass over each plane.
+ *
+ *   ref, dist    device pointers, 16-byte aligned, to [nframes][h][w] samples
+ *                stored back to back (row stride w, frame stride w*h): uint8
+ *                when bpc == 8, else uint16 holding the value in its low
+ *                bits.  A stored value above 2^bpc - 1 is not an error: it is
+ *                squared and summed like any other.  Frames inside the batch
+ *                need not start on a 16-byte boundary.
+ *   bpc          8..16.
+ *   out_noise    device uint64[nframes]: noise of frame f, units 1/s^2.
+ *   out_moments  device uint64[nframes][4]: {ref1, dist1, ref2, dist2} of
+ *                frame f (units 1/s, 1/s, 1/s^2, 1/s^2).
+ *   stream       a hipStream_t, or NULL for the null stream.
+ *
+ * Outputs are overwritten, never accumulated into, so they need no clearing
+ * beforehand: a clear queued ahead of other work can be lost or reordered
+ * [ADM, Context and Decision], and no clear is done here.  Every value is
+ * below 2^58 and may be viewed as int64.
+ *
+ * The call only queues work on `stream` and never waits: results are valid
+ * once the stream has passed this point.  The caller owns every buffer and
+ * keeps it alive until then; the library keeps no pointer after returning.
+ * This form takes its scratch from hipMallocAsync/hipFreeAsync on `stream`.
+ *
+ * Errors: VQX_E_NULL, VQX_E_DIMS, VQX_E_BPC, VQX_E_NFRAMES, VQX_E_ALIGN
+ * (before anything is queued); VQX_E_NO_DEVICE; VQX_E_HIP on a failed
+ * allocation or launch (the HIP error is consumed).
+ */
+int vqx_plane_stats_batch(const void *ref, const void *dist, int w, int h, int bpc, int nframes,
+                          uint64_t *out_noise, uint64_t *out_moments, void *stream);
+
+/*
+ * As vqx_plane_stats_batch, with caller-provided device scratch of at least
+ * vqx_plane_stats_workspace_bytes() bytes (16-byte aligned).  The workspace
+ * is written before it is read within the call, so its contents on entry do
+ * not matter; two calls may not share one workspace concurrently.
+ * Additional error: VQX_E_WORKSPACE (workspace NULL, too small or misaligned).
+ */
+int vqx_plane_stats_batch_ws(const void *ref, const void *dist, int w, int h, int bpc, int nframes,
+                             uint64_t *out_noise, uint64_t *out_moments,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * As vqx_plane_stats_batch_ws, and also records two caller-created
+ * hipEvent_t on `stream`: `stage1_begin` right before and `stage1_end` right
+ * after the streaming kernel (stage 1), so that hipEventElapsedTime gives
+ * that kernel's duration.  Either event may be NULL.  Results and errors are
+ * those of vqx_plane_stats_batch_ws; no event is recorded on an error.
+ */
+int vqx_plane_stats_batch_ws_timed(const void *ref, const void *dist, int w, int h, int bpc,
+                                   int nframes, uint64_t *out_noise, uint64_t *out_moments,
+                                   void *workspace, size_t workspace_bytes, void *stream,
+                                   void *stage1_begin, void *stage1_end);
+
+/*
+ * float_psnr's conclusion from a frame's exact noise (host only).
+ *   mse     = ((double)noise / s^2) / (w*h)    -- the 8-bit-scale mean
+ *             squared error; (double) rounds once, to nearest even, and only
+ *             at or past 2^53; the division by s^2 is exact [PSNR, Decision].
+ *   psnr_db = 10*log10(peak^2 / mse), peak = (2^bpc - 1)/s, the largest
+ *             sample on the 8-bit scale; min(psnr_db, psnr_max) when
+ *             psnr_max > 0.  mse == 0 gives psnr_max, or +inf when
+ *             psnr_max <= 0 (uncapped).
+ * Either output pointer may be NULL.  Errors: VQX_E_DIMS, VQX_E_BPC.
+ */
+int vqx_conclude_psnr(uint64_t noise, int w, int h, int bpc, double psnr_max,
+                      double *mse, double *psnr_db);
+
+/*
+ * float_moment's conclusion (host only): from {ref1, dist1, ref2, dist2} the
+ * four means {ref1/s, dist1/s, ref2/s^2, dist2/s^2} each divided by w*h --
+ * the conversion to double and the two divisions of [MOMENT, Decision].
+ * Errors: VQX_E_NULL, VQX_E_DIMS, VQX_E_BPC.
+ */
+int vqx_conclude_moments(const uint64_t sums[4], int w, int h, int bpc, double out[4]);
+
+/*
+ * Both conclusions for a whole batch of host-side sums (host only).
+ *   noise    host uint64[nframes], moments host uint64[nframes][4]
+ *   out      host double[nframes][6]: {mse, psnr_db, ref_mean, dist_mean,
+ *            ref_mean_sq, dist_mean_sq} per frame.
+ * Errors: VQX_E_NULL, VQX_E_DIMS, VQX_E_BPC, VQX_E_NFRAMES.
+ */
+int vqx_conclude_batch(const uint64_t *noise, const uint64_t *moments, int w, int h, int bpc,
+                       int nframes, double psnr_max, double *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VQX_H */

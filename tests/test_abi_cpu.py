@@ -1,0 +1,241 @@
+"""The C ABI without a GPU: symbols, argument checks, host conclusions."""
+
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_reductions_amd import vqx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vqx.h")
+
+
+def _header_text():
+    with open(HEADER) as f:
+        return f.read()
+
+
+def _declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", _header_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(vqx_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return vqx.lib()
+
+
+def test_library_exports_every_declared_symbol(L):
+    declared = _declared_functions()
+    assert declared == sorted(vqx.SYMBOLS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_abi_version_matches_header(L):
+    m = re.search(r"#define VQX_ABI_VERSION (\d+)", _header_text())
+    assert vqx.abi_version() == int(m.group(1))
+
+
+def test_status_codes_match_header():
+    text = _header_text()
+    for name, value in (("VQX_OK", 0), ("VQX_E_NULL", -1), ("VQX_E_DIMS", -2), ("VQX_E_BPC", -3),
+                        ("VQX_E_NFRAMES", -4), ("VQX_E_ALIGN", -5), ("VQX_E_WORKSPACE", -6),
+                        ("VQX_E_HIP", -7), ("VQX_E_NO_DEVICE", -8)):
+        assert re.search(rf"\b{name} = {value}\b", text), name
+    for s in range(-8, 1):
+        assert vqx.status_string(s) and vqx.status_string(s) != "unknown status"
+    assert vqx.status_string(-99) == "unknown status"
+
+
+def test_workspace_bytes():
+    # 3840x2160 uint16: 1 036 800 16-byte vectors, 4096 per workgroup -> 254 per frame
+    assert vqx.plane_stats_workspace_bytes(3840, 2160, 16, 32) == 254 * 32 * 40
+    assert vqx.plane_stats_workspace_bytes(576, 324, 8, 4) == 3 * 4 * 40
+    assert vqx.plane_stats_workspace_bytes(1, 1, 12, 7) == 7 * 40
+    for args, status in (((0, 5, 8, 1), vqx.E_DIMS), ((5, 0, 8, 1), vqx.E_DIMS),
+                         ((8192, 4097, 8, 1), vqx.E_DIMS), ((5, 5, 7, 1), vqx.E_BPC),
+                         ((5, 5, 17, 1), vqx.E_BPC), ((5, 5, 8, 0), vqx.E_NFRAMES)):
+        with pytest.raises(vqx.VqxError) as e:
+            vqx.plane_stats_workspace_bytes(*args)
+        assert e.value.status == status
+    assert vqx.lib().vqx_plane_stats_workspace_bytes(5, 5, 8, 1, None) == vqx.E_NULL
+
+
+def test_largest_frame_accepted():
+    assert vqx.plane_stats_workspace_bytes(8192, 4096, 16, 1) > 0   # exactly 2^25 pixels
+    assert vqx.plane_stats_workspace_bytes(7680, 4320, 16, 1) > 0   # 8K
+
+
+class _Buffers:
+    """Host memory standing in for device pointers: argument errors must be
+    reported before any of it is touched."""
+
+    def __init__(self):
+        self.planes = np.zeros(4096, dtype=np.uint8)
+        self.out = np.full(64, 0xFF, dtype=np.uint8)
+        base = self.planes.ctypes.data
+        self.ref = (base + 255) // 256 * 256
+        self.dist = self.ref + 1024
+        obase = self.out.ctypes.data
+        self.noise = (obase + 7) // 8 * 8
+        self.moments = self.noise + 8
+
+    def untouched(self):
+        return bool(np.all(self.out == 0xFF))
+
+
+ARG_ERRORS = [
+    ("null ref", dict(ref=0), vqx.E_NULL),
+    ("null dist", dict(dist=0), vqx.E_NULL),
+    ("null noise", dict(noise=0), vqx.E_NULL),
+    ("null moments", dict(moments=0), vqx.E_NULL),
+    ("w 0", dict(w=0), vqx.E_DIMS),
+    ("h -1", dict(h=-1), vqx.E_DIMS),
+    ("too many pixels", dict(w=8192, h=4097), vqx.E_DIMS),
+    ("bpc 7", dict(bpc=7), vqx.E_BPC),
+    ("bpc 17", dict(bpc=17), vqx.E_BPC),
+    ("nframes 0", dict(nframes=0), vqx.E_NFRAMES),
+    ("ref misaligned", dict(ref_off=8), vqx.E_ALIGN),
+    ("dist misaligned", dict(dist_off=2), vqx.E_ALIGN),
+    ("noise misaligned", dict(noise_off=4), vqx.E_ALIGN),
+]
+
+
+def _call(L, b, ws=None, ws_bytes=0, ref=None, dist=None, noise=None, moments=None, w=16, h=4,
+          bpc=8, nframes=2, ref_off=0, dist_off=0, noise_off=0):
+    ref = b.ref + ref_off if ref is None else ref
+    dist = b.dist + dist_off if dist is None else dist
+    noise = b.noise + noise_off if noise is None else noise
+    moments = b.moments if moments is None else moments
+    if ws is None:
+        return L.vqx_plane_stats_batch(ref or None, dist or None, w, h, bpc, nframes,
+                                       noise or None, moments or None, None)
+    return L.vqx_plane_stats_batch_ws(ref or None, dist or None, w, h, bpc, nframes,
+                                      noise or None, moments or None, ws or None, ws_bytes, None)
+
+
+@pytest.mark.parametrize("name,kw,status", ARG_ERRORS, ids=[a[0] for a in ARG_ERRORS])
+@pytest.mark.parametrize("form", ["self-allocating", "workspace"])
+def test_argument_errors_leave_outputs_untouched(L, name, kw, status, form):
+    b = _Buffers()
+    if form == "workspace":
+        ws = np.zeros(4096, dtype=np.uint8)
+        got = _call(L, b, ws=(ws.ctypes.data + 255) // 256 * 256, ws_bytes=1024, **kw)
+    else:
+        got = _call(L, b, **kw)
+    assert got == status
+    assert b.untouched()
+
+
+def test_workspace_errors(L):
+    b = _Buffers()
+    ws = np.zeros(4096, dtype=np.uint8)
+    base = (ws.ctypes.data + 255) // 256 * 256
+    need = vqx.plane_stats_workspace_bytes(16, 4, 8, 2)
+    assert _call(L, b, ws=base, ws_bytes=need - 1) == vqx.E_WORKSPACE
+    assert _call(L, b, ws=base + 8, ws_bytes=need) == vqx.E_WORKSPACE
+    assert L.vqx_plane_stats_batch_ws(b.ref, b.dist, 16, 4, 8, 2, b.noise, b.moments, None, need,
+                                      None) == vqx.E_WORKSPACE
+    assert b.untouched()
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_has_gpu(), reason="checks the no-device path")
+def test_valid_call_without_device_reports_no_device(L):
+    b = _Buffers()
+    assert _call(L, b) == vqx.E_NO_DEVICE
+    ws = np.zeros(4096, dtype=np.uint8)
+    base = (ws.ctypes.data + 255) // 256 * 256
+    assert _call(L, b, ws=base, ws_bytes=1024) == vqx.E_NO_DEVICE
+    assert b.untouched()
+
+
+# ------------------------------------------------------------------ conclusions
+
+def _random_sums(rng, w, h, bpc, past53=False):
+    pixels = w * h
+    top = 255 if bpc == 8 else 65535
+    q = oracle.q_int
+    noise = int(rng.integers(0, pixels * q(top) + 1))
+    r1 = int(rng.integers(0, pixels * top + 1))
+    d1 = int(rng.integers(0, pixels * top + 1))
+    r2 = int(rng.integers(0, pixels * q(top) + 1))
+    d2 = int(rng.integers(0, pixels * q(top) + 1))
+    if past53:
+        r2 = int(rng.integers(1 << 53, pixels * q(top) + 1))
+    return [noise, r1, d1, r2, d2]
+
+
+@pytest.mark.parametrize("bpc", [8, 10, 12, 13, 16])
+def test_conclusions_match_oracle_bitwise(bpc):
+    rng = np.random.Generator(np.random.PCG64(bpc))
+    for w, h in ((576, 324), (1920, 1080), (3840, 2160), (1, 1), (17, 3)):
+        for _ in range(50):
+            sums = _random_sums(rng, w, h, bpc, past53=(bpc == 16 and w * h > (1 << 21)))
+            want = oracle.conclude_from_ints(sums, w, h, bpc)
+            mse, db = vqx.conclude_psnr(sums[0], w, h, bpc, 0.0)
+            assert mse == want[0]
+            assert db == oracle.psnr_db(want[0], bpc, 0.0)
+            got = vqx.conclude_moments(sums[1:], w, h, bpc)
+            assert list(got) == list(want[1:])
+            batch = vqx.conclude_batch([sums[0]], [sums[1:]], w, h, bpc, 60.0)
+            assert list(batch[0]) == [want[0], oracle.psnr_db(want[0], bpc, 60.0)] + list(want[1:])
+
+
+def test_psnr_textbook_values():
+    # a constant 8-bit difference d gives mse = d^2 and PSNR = 20*log10(255/d)
+    for d in (1, 2, 5, 255):
+        mse, db = vqx.conclude_psnr(d * d * 100, 10, 10, 8)
+        assert mse == d * d
+        assert db == pytest.approx(20 * math.log10(255 / d), abs=1e-12)
+    # peak on the 8-bit scale: (2^bpc - 1)/scaler
+    _, db = vqx.conclude_psnr(16 * 16, 1, 1, 12)     # mse 1 on the 8-bit scale
+    assert db == pytest.approx(20 * math.log10(4095 / 16), abs=1e-12)
+
+
+def test_psnr_cap_and_zero_noise():
+    assert vqx.conclude_psnr(0, 8, 8, 8, 60.0) == (0.0, 60.0)
+    mse, db = vqx.conclude_psnr(0, 8, 8, 8, 0.0)
+    assert mse == 0.0 and db == math.inf
+    _, db = vqx.conclude_psnr(1, 1000, 1000, 8, 60.0)   # ~108 dB uncapped
+    assert db == 60.0
+    _, db = vqx.conclude_psnr(1, 1000, 1000, 8, 0.0)
+    assert db > 100
+
+
+def test_conclusion_errors():
+    L = vqx.lib()
+    out = np.zeros(24, dtype=np.float64)
+    s = np.zeros(8, dtype=np.uint64)
+    assert L.vqx_conclude_moments(None, 4, 4, 8, out.ctypes.data) == vqx.E_NULL
+    assert L.vqx_conclude_moments(s.ctypes.data, 0, 4, 8, out.ctypes.data) == vqx.E_DIMS
+    assert L.vqx_conclude_moments(s.ctypes.data, 4, 4, 18, out.ctypes.data) == vqx.E_BPC
+    assert L.vqx_conclude_batch(s.ctypes.data, s.ctypes.data, 4, 4, 8, 0, 0.0, out.ctypes.data) == vqx.E_NFRAMES
+    assert L.vqx_conclude_psnr(0, 4, 4, 7, 0.0, None, None) == vqx.E_BPC
+    assert L.vqx_conclude_psnr(0, 4, 4, 8, 0.0, None, None) == vqx.OK
+    assert np.all(out == 0)
+
+
+def test_past53_conclusion_is_one_rounding():
+    """Past 2^53 the conversion rounds once, to nearest even, like Python's
+    int-to-float; the result stays within the page's bound of the exact mean."""
+    w, h = 3840, 2160
+    exact = (1 << 54) + 3          # odd, past 2^54: the conversion must round
+    got = vqx.conclude_moments([0, 0, exact, 0], w, h, 16)[2]
+    assert got == (float(exact) / 65536.0) / (w * h)
+    from fractions import Fraction
+    err = abs(Fraction(got) - Fraction(exact, 65536 * w * h))
+    assert err <= oracle.past53_bound(w * h, 54, 16)

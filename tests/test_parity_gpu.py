@@ -1,0 +1,211 @@
+"""HIP path against the oracle, on an MI355X (marked gpu).
+
+Every device result is compared frame by frame and output by output with
+``oracle.acceptance``: the device integer equals the exact integer always;
+below 2^53 units the CPU's sequential double and every concluded mean are
+equal bit for bit; past 2^53 the means are within the float_moment page's
+bound.  The library's own host conclusions are checked the same way.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from exact_reductions_amd import vqx  # noqa: E402
+
+
+@pytest.fixture(scope="session", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    vqx.lib()  # raises if libvqx.so is missing: no fallback exists
+    return torch.device("cuda:0")
+
+
+def upload(a: np.ndarray):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to("cuda:0")
+
+
+def device_sums(ref, dist, bpc, entry="caching", stream=None, prefill=None):
+    """Run one batch through the library; return host int64 noise [F], moments [F][4]."""
+    r, d = upload(ref), upload(dist)
+    f = ref.shape[0]
+    noise = torch.empty(f, dtype=torch.int64, device="cuda:0")
+    moments = torch.empty((f, 4), dtype=torch.int64, device="cuda:0")
+    if prefill is not None:
+        noise.fill_(prefill)
+        moments.fill_(prefill)
+    if entry == "caching":
+        vqx.plane_stats_batch(r, d, bpc, stream=stream, out_noise=noise, out_moments=moments)
+    elif entry == "selfalloc":
+        vqx.plane_stats_batch_selfalloc(r, d, bpc, noise, moments, stream=stream)
+    elif entry == "workspace_ff":
+        h, w = ref.shape[1:]
+        ws = torch.full((vqx.plane_stats_workspace_bytes(w, h, bpc, f),), 0xFF, dtype=torch.uint8,
+                        device="cuda:0")
+        vqx.plane_stats_batch_ws(r, d, bpc, noise, moments, ws, stream=stream)
+    else:
+        raise ValueError(entry)
+    if stream is not None:
+        stream.synchronize()
+    torch.cuda.synchronize()
+    return noise.cpu().numpy(), moments.cpu().numpy()
+
+
+def check(ref, dist, bpc, noise, moments, psnr_max=0.0):
+    h, w = ref.shape[1:]
+    o1 = oracle.seq_batch_sums(ref, dist, bpc)
+    o2 = oracle.exact_batch_sums(ref, dist)
+    concl = vqx.conclude_batch(noise, moments, w, h, bpc, psnr_max)
+    for f in range(ref.shape[0]):
+        dev5 = [int(noise[f])] + [int(v) for v in moments[f]]
+        fails = oracle.acceptance(dev5, o1[f], o2[f], w, h, bpc)
+        assert not fails, f"frame {f}: {fails}"
+        # the library's conclusion against the oracle's, from the same sums
+        want = oracle.conclude_from_ints(dev5, w, h, bpc)
+        got = [concl[f, 0]] + list(concl[f, 2:])
+        assert got == list(want), f"frame {f}: library conclusion {got} != {want}"
+        assert concl[f, 1] == oracle.psnr_db(want[0], bpc, psnr_max)
+        # and the CPU's own conclusion wherever its double is exact
+        cpu = oracle.conclude_from_doubles(o1[f], w, h)
+        for k in range(5):
+            if int(o2[f][k]) < oracle.TWO53:
+                assert got[k] == cpu[k], f"frame {f} output {k}"
+    return o1, o2
+
+
+_cache = {}
+
+
+def workload(n):
+    if n not in _cache:
+        _cache[n] = synth.generate(n)
+    return _cache[n]
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_workload_full_size(n):
+    wl = synth.WORKLOADS[n]
+    ref, dist = workload(n)
+    noise, moments = device_sums(ref, dist, wl.bpc)
+    o1, o2 = check(ref, dist, wl.bpc, noise, moments)
+    if n == 5:
+        # the second-moment sums pass 2^53 units on every frame, so the bound
+        # is the gate there; yet no add of the CPU's rounds (every sample is
+        # above 46341, so every square is a multiple of 2^8): equality holds
+        assert np.all(o2[:, 3] >= oracle.TWO53)
+        assert all(int(moments[f, 2]) / 65536.0 == o1[f, 3] for f in range(ref.shape[0]))
+
+
+@pytest.mark.parametrize("entry", ["selfalloc", "workspace_ff"])
+def test_other_entry_points(entry):
+    ref, dist = synth.generate(4, nframes=6)
+    noise, moments = device_sums(ref, dist, 16, entry=entry)
+    check(ref, dist, 16, noise, moments)
+
+
+def test_outputs_prefilled_are_overwritten():
+    """Outputs full of 0xFF bytes are overwritten, not added to."""
+    ref, dist = synth.generate(3, nframes=3, w=640, h=360)
+    noise, moments = device_sums(ref, dist, 12, entry="workspace_ff", prefill=-1)
+    check(ref, dist, 12, noise, moments)
+
+
+def test_larger_call_after_smaller():
+    """A later, larger batch in the same process starts from its own sums."""
+    for (w, h, f) in ((64, 32, 2), (1920, 1080, 3), (3840, 2160, 2)):
+        ref, dist = synth.uniform_planes(w, h, f, 16, seed=w + f, container_max=True)
+        noise, moments = device_sums(ref, dist, 16, prefill=0x5A5A5A5A)
+        check(ref, dist, 16, noise, moments)
+
+
+def test_non_default_stream():
+    s = torch.cuda.Stream()
+    ref, dist = synth.generate(2, nframes=4)
+    with torch.cuda.stream(s):
+        noise, moments = device_sums(ref, dist, 10, stream=s)
+    check(ref, dist, 10, noise, moments)
+
+
+SHAPES = [
+    (1, 1, 1), (1, 1, 5), (3, 1, 2), (18, 22, 3), (7, 3, 1000), (577, 323, 3), (33, 1, 17),
+    (129, 65, 4), (4096, 1, 2), (1, 4099, 2), (4097, 3, 2),
+]
+
+
+@pytest.mark.parametrize("w,h,f", SHAPES, ids=[f"{w}x{h}x{f}" for w, h, f in SHAPES])
+@pytest.mark.parametrize("bpc", [8, 16])
+def test_shapes(w, h, f, bpc):
+    """Odd sizes: frames shorter than a 16-byte vector, frame starts that are
+    not 16-byte aligned inside the batch, chunks with a ragged tail."""
+    ref, dist = synth.uniform_planes(w, h, f, bpc, seed=w * 131 + h * 7 + f + bpc)
+    noise, moments = device_sums(ref, dist, bpc)
+    check(ref, dist, bpc, noise, moments)
+
+
+@pytest.mark.parametrize("bpc", list(range(8, 17)))
+def test_every_depth_full_container(bpc):
+    """Every depth 8..16, values over the whole container (stored values above
+    2^bpc - 1 are reduced like any other)."""
+    ref, dist = synth.uniform_planes(300, 201, 3, bpc, seed=900 + bpc, container_max=True)
+    noise, moments = device_sums(ref, dist, bpc)
+    check(ref, dist, bpc, noise, moments)
+
+
+def test_tall_frame_962x13542():
+    """The tall frame size the ADM page reports a failure on."""
+    ref, dist = synth.uniform_planes(962, 13542, 1, 10, seed=13542)
+    noise, moments = device_sums(ref, dist, 10)
+    check(ref, dist, 10, noise, moments)
+
+
+def test_largest_frame():
+    """2^25 samples, 16 bits, full range."""
+    ref, dist = synth.uniform_planes(8192, 4096, 1, 16, seed=25, container_max=True)
+    noise, moments = device_sums(ref, dist, 16)
+    check(ref, dist, 16, noise, moments)
+
+
+def test_ties_and_worst_case():
+    cases = [
+        (16, 4097, 0), (16, 0, 4097), (16, 65535, 0), (16, 46341, 1), (10, 1023, 0),
+        (8, 255, 0), (12, 4095, 4095), (16, 12345, 12345),
+    ]
+    for bpc, a, b in cases:
+        ref, dist = synth.constant_pair(3840, 2160, 1, bpc, a, b)
+        noise, moments = device_sums(ref, dist, bpc)
+        check(ref, dist, bpc, noise, moments)
+        d = abs(a - b)
+        assert int(noise[0]) == 3840 * 2160 * oracle.q_int(d)
+
+
+def test_past53_mixed_frame():
+    """2560x1440, a tenth of the samples below 4096: the second moments pass
+    2^53 units and the CPU's adds round; the device is exact and the means
+    stay within the page's bound."""
+    ref, dist = synth.past53_mixed(nframes=2)
+    noise, moments = device_sums(ref, dist, 16)
+    o1, o2 = check(ref, dist, 16, noise, moments)
+    assert np.all(o2[:, 3] >= oracle.TWO53)
+
+
+def test_past53_full_range_4k():
+    ref, dist = synth.past53_fullrange(nframes=2)
+    noise, moments = device_sums(ref, dist, 16)
+    o1, o2 = check(ref, dist, 16, noise, moments)
+    assert np.all(o2[:, 3] >= oracle.TWO53)
+
+
+def test_misaligned_base_is_rejected():
+    ref = torch.zeros(16 * 16 + 1, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(vqx.VqxError) as e:
+        vqx.plane_stats_batch(ref[1:].view(1, 16, 16), ref[1:].view(1, 16, 16), 8)
+    assert e.value.status == vqx.E_ALIGN
