@@ -1,0 +1,194 @@
+#!/usr/bin/env python3
+"""rocprofv3 passes over bench.py and short text summaries of them.
+
+Runs, each as a child process under its own time limit:
+
+1. ``rocprofv3 --kernel-trace --stats`` over a bench run: per-kernel call
+   counts and durations (the stage-1 average must agree with the HIP-event
+   figure bench.py reports);
+2. ``rocprofv3 --pmc FETCH_SIZE`` and 3. ``rocprofv3 --pmc WRITE_SIZE``, one
+   counter per run, over a short bench run that also runs three elementwise
+   kernels that each read and write a known 1 GiB (a plain streaming copy
+   through the shader cores); that kernel's counter reading scales the
+   stage-1 reading into HBM bytes.
+
+Writes ``<kernel>_<w>x<h>x<frames>_kernel_trace.txt`` and
+``..._hbm_traffic.txt`` into ``--out``.  This script never touches the GPU
+itself.
+
+    python bench_profile.py --workload 5 --out gpurun_out/profiles
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import shlex
+import statistics
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCE = os.path.join(ROOT, "exact_reductions_amd", "csrc", "plane_stats.hip")
+COPY_MIB = 1024
+
+
+def sh(cmd, timeout, log):
+    print(f"[bench_profile] {' '.join(shlex.quote(c) for c in cmd)}", flush=True)
+    with open(log, "w") as f:
+        r = subprocess.run(["timeout", "-s", "KILL", str(timeout)] + cmd, stdout=f, stderr=subprocess.STDOUT)
+    print(f"[bench_profile] exit {r.returncode}", flush=True)
+    return r.returncode
+
+
+def find(pattern_dir, suffix):
+    hits = sorted(glob.glob(os.path.join(pattern_dir, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {pattern_dir}")
+    return hits[-1]
+
+
+def rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def short(name: str) -> str:
+    for k in ("stage1_u16", "stage1_u8", "stage2_combine", "bitwise_not"):
+        if k in name:
+            return k
+    return name.split("(")[0][-60:]
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser()
+    p.add_argument("--workload", type=int, default=5)
+    p.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "profiles"))
+    p.add_argument("--work", default=os.path.join(ROOT, "gpurun_out", "rocprof"))
+    p.add_argument("--cache", default="/tmp/vqx_inputs")
+    p.add_argument("--steps", type=int, default=200)
+    args = p.parse_args(argv)
+
+    sys.path.insert(0, ROOT)
+    import synth
+    wl = synth.WORKLOADS[args.workload]
+    kernel = "stage1_u8" if wl.bpc == 8 else "stage1_u16"
+    wname = f"{wl.w}x{wl.h}x{wl.nframes}"
+    os.makedirs(args.out, exist_ok=True)
+    os.makedirs(args.work, exist_ok=True)
+    bench = ["python3", os.path.join(ROOT, "bench.py"), "--workload", str(args.workload),
+             "--no-cpu-baseline", "--input-cache", args.cache]
+    with open(KERNEL_SOURCE, "rb") as f:
+        src_sha = hashlib.sha256(f.read()).hexdigest()
+
+    # 0. make the input cache outside the profiler
+    rc = sh(bench + ["--steps", "1", "--warmup", "0"], 600, os.path.join(args.work, "prime.log"))
+    if rc != 0:
+        return rc
+
+    # 1. kernel trace + stats
+    tdir = os.path.join(args.work, "trace")
+    trace_cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", tdir,
+                 "-o", "trace", "--"] + bench + ["--steps", str(args.steps), "--warmup", "100"]
+    rc = sh(trace_cmd, 300, os.path.join(args.work, "trace.log"))
+    if rc != 0:
+        return rc
+    stats = rows(find(tdir, "kernel_stats.csv"))
+    with open(os.path.join(args.work, "trace.log")) as f:
+        bench_line = [ln for ln in f.read().splitlines() if ln.startswith("{")]
+    lines = [
+        f"# rocprofv3 kernel trace: {kernel}, {wl.name} ({wname})",
+        f"command: cd <repo> && {' '.join(shlex.quote(c) for c in trace_cmd).replace(ROOT + '/', '')}",
+        f"date_utc: {time.strftime('%Y-%m-%dT%H:%M:%SZ', time.gmtime())}",
+        f"kernel_source_sha256: {src_sha}",
+        "",
+        f"{'kernel':<16} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_us':>12}",
+    ]
+    stage1_avg = None
+    for r in stats:
+        name = short(r.get("Name", r.get("KernelName", "?")))
+        calls = int(r["Calls"])
+        avg = float(r["AverageNs"]) / 1e3
+        lines.append(f"{name:<16} {calls:>6} {avg:>10.2f} {float(r['MinNs']) / 1e3:>10.2f} "
+                     f"{float(r['MaxNs']) / 1e3:>10.2f} {float(r['TotalDurationNs']) / 1e3:>12.1f}")
+        if name == kernel:
+            stage1_avg = avg
+    if stage1_avg:
+        gbs = wl.bytes_per_frame * wl.nframes / (stage1_avg * 1e-6) / 1e9
+        lines += ["", f"stage1_avg_us: {stage1_avg:.2f}",
+                  f"stage1_algorithmic_bytes_per_launch: {wl.bytes_per_frame * wl.nframes}",
+                  f"stage1_achieved_GBps: {gbs:.1f}", f"stage1_frac_of_8000_GBps: {gbs / 8000:.4f}"]
+    if bench_line:
+        lines += ["", "bench line of the same run:", bench_line[-1]]
+    with open(os.path.join(args.out, f"{kernel}_{wname}_kernel_trace.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines), flush=True)
+
+    # 2./3. one counter per pass
+    readings = {}
+    cmds = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        cdir = os.path.join(args.work, counter.lower())
+        cmd = ["rocprofv3", "--pmc", counter, "--output-format", "csv", "-d", cdir, "-o", counter.lower(),
+               "--"] + bench + ["--steps", "5", "--warmup", "1", "--calibrate-copy", str(COPY_MIB)]
+        cmds[counter] = cmd
+        rc = sh(cmd, 240, os.path.join(args.work, f"{counter.lower()}.log"))
+        if rc != 0:
+            return rc
+        per_kernel = {}
+        for r in rows(find(cdir, "counter_collection.csv")):
+            if r.get("Counter_Name") != counter:
+                continue
+            per_kernel.setdefault(short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        readings[counter] = per_kernel
+
+    copy_bytes = COPY_MIB * (1 << 20)
+    out = [
+        f"# HBM traffic of {kernel}, {wl.name} ({wname}), from rocprofv3 counters",
+        f"command_fetch: cd <repo> && {' '.join(shlex.quote(c) for c in cmds['FETCH_SIZE']).replace(ROOT + '/', '')}",
+        f"command_write: cd <repo> && {' '.join(shlex.quote(c) for c in cmds['WRITE_SIZE']).replace(ROOT + '/', '')}",
+        f"date_utc: {time.strftime('%Y-%m-%dT%H:%M:%SZ', time.gmtime())}",
+        f"kernel_source_sha256: {src_sha}",
+        f"copy_kernel_bytes_read_and_written: {copy_bytes}",
+        "",
+        "per-dispatch means (KiB as the counter reports them):",
+    ]
+    for counter, per_kernel in readings.items():
+        for name, vals in sorted(per_kernel.items()):
+            out.append(f"  {counter:<10} {name:<48} n={len(vals):<3} mean={statistics.fmean(vals):.1f}")
+    # the known-size kernel: torch's bitwise_not over 1 GiB (its last three
+    # dispatches; earlier bitwise_not dispatches, if any, are not ours)
+    def copy_reading(per_kernel):
+        vals = per_kernel.get("bitwise_not")
+        return statistics.fmean(vals[-3:]) if vals else None
+    fetch_copy = copy_reading(readings["FETCH_SIZE"])
+    write_copy = copy_reading(readings["WRITE_SIZE"])
+    f_k = readings["FETCH_SIZE"].get(kernel)
+    w_k = readings["WRITE_SIZE"].get(kernel)
+    if fetch_copy and write_copy and f_k and w_k:
+        f_scale = copy_bytes / fetch_copy
+        w_scale = copy_bytes / write_copy
+        fetch_b = statistics.fmean(f_k) * f_scale
+        write_b = statistics.fmean(w_k) * w_scale
+        out += [
+            "",
+            f"fetch_scale_bytes_per_unit: {f_scale:.4f}",
+            f"write_scale_bytes_per_unit: {w_scale:.4f}",
+            f"stage1_fetch_bytes_per_launch: {fetch_b:.0f}",
+            f"stage1_write_bytes_per_launch: {write_b:.0f}",
+            f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}",
+            f"algorithmic_bytes_per_launch: {wl.bytes_per_frame * wl.nframes}",
+            f"traffic_over_algorithmic: {(fetch_b + write_b) / (wl.bytes_per_frame * wl.nframes):.4f}",
+        ]
+    with open(os.path.join(args.out, f"{kernel}_{wname}_hbm_traffic.txt"), "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

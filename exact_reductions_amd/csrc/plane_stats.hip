@@ -28,9 +28,10 @@
 // integers.
 // 9..16 bits: each sample is converted to float and the three products
 // (r-d)^2, r^2, d^2 are taken in binary32, round to nearest even, then read
-// back as uint32 (below 2^32 [MOMENT, Decision]).  A uint32 term is added as
-// its low and high 16-bit halves into two uint32 accumulators, the split the
-// float_psnr page uses at 16 bits [PSNR, Decision].
+// back as uint32 (below 2^32 [MOMENT, Decision]) and added into 64-bit
+// integer lane accumulators.  Across the wave each 64-bit lane sum travels
+// as its low 16 bits and the rest, two uint32 sums -- the page's low/high
+// split at 16 bits [PSNR, Decision], moved from every term to once per lane.
 
 #include "plane_stats.h"
 
@@ -44,19 +45,24 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;              // four wave64s
 constexpr int kWaves = kThreads / 64;
-constexpr int kIters = 16;                 // 16-byte vectors per lane per plane
-constexpr int kChunkVecs = kThreads * kIters;  // 64 KiB of each plane per workgroup
+constexpr int kIters = 8;                  // 16-byte vectors per lane per plane
+constexpr int kInFlight = 4;               // vectors of each plane loaded before use
+constexpr int kChunkVecs = kThreads * kIters;  // 32 KiB of each plane per workgroup
+static_assert(kIters % kInFlight == 0, "whole load groups");
 
 // ----------------------------------------------------------------- budgets
 // A lane sees at most kIters vectors plus one edge sample.
-//  8 bits: a lane's sum r^2 <= (16*16 + 1) * 255^2 = 16 711 425 < 2^24, so a
-//          wave's sum < 2^30; sum r and sum r*d are no larger.
-// 16 bits: a lane's 16-bit halves sum to <= (16*8 + 1) * 65535 < 2^23, so a
-//          wave's sum < 2^29; sum r likewise.
+//  8 bits: a lane's sum r^2 <= (8*16 + 1) * 255^2 < 2^23, so a wave's sum
+//          < 2^29; sum r and sum r*d are no larger.
+// 16 bits: a lane's 64-bit sum of squares is <= (8*8 + 1) * (2^32 - 1) <
+//          2^39; it is reduced across the wave as its low 16 bits (wave sum
+//          < 2^22) and the rest (lane value < 2^23, wave sum < 2^29); a
+//          lane's sample sum is <= 65 * 65535 < 2^23 (wave sum < 2^29).
 // Each wave64 total therefore fits uint32; the workgroup adds its waves in
 // uint64.
 static_assert((kIters * 16 + 1) * 255ull * 255ull * 64ull < (1ull << 32), "8-bit wave budget");
-static_assert((kIters * 8 + 1) * 65535ull * 64ull < (1ull << 32), "16-bit wave budget");
+static_assert(((kIters * 8 + 1) * 0xffffffffull >> 16) * 64ull < (1ull << 32), "16-bit wave budget");
+static_assert((kIters * 8 + 1) * 65535ull * 64ull < (1ull << 32), "16-bit sample-sum budget");
 
 // --------------------------------------------------------------- 8-bit terms
 struct Acc8 {
@@ -74,8 +80,14 @@ __device__ __forceinline__ void add_dword(Acc8 &a, uint32_t r, uint32_t d)
 }
 
 // -------------------------------------------------------------- 16-bit terms
+// The float terms go into 64-bit integer lane accumulators (one
+// v_lshl_add_u64 per term on gfx950).  This is the leanest exact form:
+// fewer VALU operations per byte than adding the 16-bit halves separately,
+// which matters because the kernel runs near the HBM roofline, where power
+// (and with it the clock) depends on the work per byte.
 struct Acc16 {
-    uint32_t n_lo = 0, n_hi = 0, r1 = 0, d1 = 0, r2_lo = 0, r2_hi = 0, d2_lo = 0, d2_hi = 0;
+    uint64_t noise = 0, r2 = 0, d2 = 0;
+    uint32_t r1 = 0, d1 = 0;
 };
 
 // The float square of x read back as an integer: one binary32 product, round
@@ -87,25 +99,19 @@ __device__ __forceinline__ uint32_t float_square(float x)
     return static_cast<uint32_t>(p);
 }
 
-__device__ __forceinline__ void add_halves(uint32_t &lo, uint32_t &hi, uint32_t t)
-{
-    lo += t & 0xffffu;
-    hi += t >> 16;
-}
-
 // Two samples of each plane packed in one dword.
 __device__ __forceinline__ void add_dword(Acc16 &a, uint32_t r, uint32_t d)
 {
     const float r0 = static_cast<float>(r & 0xffffu), r1 = static_cast<float>(r >> 16);
     const float d0 = static_cast<float>(d & 0xffffu), d1 = static_cast<float>(d >> 16);
     // float_psnr: the square of the float difference [PSNR, Decision]
-    add_halves(a.n_lo, a.n_hi, float_square(r0 - d0));
-    add_halves(a.n_lo, a.n_hi, float_square(r1 - d1));
+    a.noise += float_square(r0 - d0);
+    a.noise += float_square(r1 - d1);
     // float_moment: the float squares of the samples [MOMENT, Decision]
-    add_halves(a.r2_lo, a.r2_hi, float_square(r0));
-    add_halves(a.r2_lo, a.r2_hi, float_square(r1));
-    add_halves(a.d2_lo, a.d2_hi, float_square(d0));
-    add_halves(a.d2_lo, a.d2_hi, float_square(d1));
+    a.r2 += float_square(r0);
+    a.r2 += float_square(r1);
+    a.d2 += float_square(d0);
+    a.d2 += float_square(d1);
     // the sample sums: r0 + r1 in one integer dot product
     const u16x2 ones = {1, 1};
     a.r1 = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, r), ones, a.r1, false);
@@ -230,13 +236,22 @@ __device__ __forceinline__ void accumulate_chunk(Acc &acc, const void *ref, cons
     const int64_t cb = vb + static_cast<int64_t>(chunk) * kChunkVecs;
     const int64_t ce = cb + kChunkVecs < ve ? cb + kChunkVecs : ve;
     if (ce - cb == kChunkVecs) {
+        // whole chunk: issue kInFlight non-temporal 16-byte loads of each
+        // plane, then consume them (the data is read once, so it is not kept
+        // in the caches)
         const u32x4 *r = R + cb + threadIdx.x;
         const u32x4 *d = D + cb + threadIdx.x;
-#pragma unroll 4
-        for (int i = 0; i < kIters; ++i) {
-            const u32x4 a = __builtin_nontemporal_load(r + i * kThreads);
-            const u32x4 b = __builtin_nontemporal_load(d + i * kThreads);
-            add_vec(acc, a, b);
+#pragma unroll 1
+        for (int i = 0; i < kIters; i += kInFlight) {
+            u32x4 a[kInFlight], b[kInFlight];
+#pragma unroll
+            for (int u = 0; u < kInFlight; ++u) {
+                a[u] = __builtin_nontemporal_load(r + (i + u) * kThreads);
+                b[u] = __builtin_nontemporal_load(d + (i + u) * kThreads);
+            }
+#pragma unroll
+            for (int u = 0; u < kInFlight; ++u)
+                add_vec(acc, a[u], b[u]);
         }
     } else {
         for (int64_t v = cb + threadIdx.x; v < ce; v += kThreads) {
@@ -272,7 +287,11 @@ __global__ __launch_bounds__(kThreads) void stage1_u16(const void *ref, const vo
     const int chunk = static_cast<int>(wg - frame * chunks);
     Acc16 a;
     accumulate_chunk<2>(a, ref, dist, pixels, chunk, frame);
-    const uint32_t v[8] = {a.n_lo, a.n_hi, a.r1, a.d1, a.r2_lo, a.r2_hi, a.d2_lo, a.d2_hi};
+    // each 64-bit lane sum crosses the wave as (low 16 bits, the rest)
+    const uint32_t v[8] = {static_cast<uint32_t>(a.noise & 0xffffu), static_cast<uint32_t>(a.noise >> 16),
+                           a.r1, a.d1,
+                           static_cast<uint32_t>(a.r2 & 0xffffu), static_cast<uint32_t>(a.r2 >> 16),
+                           static_cast<uint32_t>(a.d2 & 0xffffu), static_cast<uint32_t>(a.d2 >> 16)};
     uint64_t s[8];
     workgroup_sums(v, s);
     write_record(part, nwg, wg, s[0] + (s[1] << 16), s[2], s[3], s[4] + (s[5] << 16),

@@ -49,6 +49,12 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIBRARY):
             raise RuntimeError(f"{LIBRARY} is not built; run __graft_entry__.build()")
+        # torch ships its own HIP runtime; load it first so that libvqx binds
+        # to that one (same soname) and stream handles mean the same thing.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIBRARY)
         vp, i, u64, sz, d = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_double
         sigs = {
@@ -68,6 +74,17 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = args
         _lib = L
     return _lib
+
+
+def hip_runtime() -> ctypes.CDLL:
+    """The HIP runtime already mapped into this process (torch's), for the
+    event calls of the bench; never a second copy."""
+    lib()
+    with open("/proc/self/maps") as f:
+        paths = sorted({line.split()[-1] for line in f if "libamdhip64" in line})
+    if not paths:
+        raise RuntimeError("no HIP runtime is loaded")
+    return ctypes.CDLL(paths[0])
 
 
 def abi_version() -> int:

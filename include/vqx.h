@@ -86,9 +86,13 @@ int vqx_plane_stats_workspace_bytes(int w, int h, int bpc, int nframes, size_t *
  *                squared and summed like any other.  Frames inside the batch
  *                need not start on a 16-byte boundary.
  *   bpc          8..16.
- *   out_noise    device uint64[nframes]: noise of frame f, units 1/s^2.
- *   out_moments  device uint64[nframes][4]: {ref1, dist1, ref2, dist2} of
- *                frame f (units 1/s, 1/s, 1/s^2, 1/s^2).
+ *   out_noise    uint64[nframes]: noise of frame f, units 1/s^2.
+ *   out_moments  uint64[nframes][4]: {ref1, dist1, ref2, dist2} of frame f
+ *                (units 1/s, 1/s, 1/s^2, 1/s^2).
+ *                Both outputs must be addressable by the device: device
+ *                memory, or pinned host memory mapped for the device (pass
+ *                the address hipHostGetDevicePointer returns), into which
+ *                the last kernel writes directly (40 bytes per frame).
  *   stream       a hipStream_t, or NULL for the null stream.
  *
  * Outputs are overwritten, never accumulated into, so they need no clearing

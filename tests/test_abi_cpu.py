@@ -54,9 +54,10 @@ def test_status_codes_match_header():
 
 
 def test_workspace_bytes():
-    # 3840x2160 uint16: 1 036 800 16-byte vectors, 4096 per workgroup -> 254 per frame
-    assert vqx.plane_stats_workspace_bytes(3840, 2160, 16, 32) == 254 * 32 * 40
-    assert vqx.plane_stats_workspace_bytes(576, 324, 8, 4) == 3 * 4 * 40
+    # 3840x2160 uint16: 1 036 800 16-byte vectors, 2048 per workgroup -> 507 per frame
+    assert vqx.plane_stats_workspace_bytes(3840, 2160, 16, 32) == 507 * 32 * 40
+    # 576x324 uint8: 11 664 vectors -> 6 per frame
+    assert vqx.plane_stats_workspace_bytes(576, 324, 8, 4) == 6 * 4 * 40
     assert vqx.plane_stats_workspace_bytes(1, 1, 12, 7) == 7 * 40
     for args, status in (((0, 5, 8, 1), vqx.E_DIMS), ((5, 0, 8, 1), vqx.E_DIMS),
                          ((8192, 4097, 8, 1), vqx.E_DIMS), ((5, 5, 7, 1), vqx.E_BPC),

@@ -119,6 +119,34 @@ def test_outputs_prefilled_are_overwritten():
     check(ref, dist, 12, noise, moments)
 
 
+def test_pinned_host_outputs():
+    """Outputs in pinned host memory mapped for the device: the combine
+    kernel writes the sums there directly (no copy)."""
+    import ctypes
+    ref, dist = synth.generate(5, nframes=3)
+    r, d = upload(ref), upload(dist)
+    host = torch.full((2, 15), -1, dtype=torch.int64, pin_memory=True)
+    rt = vqx.hip_runtime()
+    rt.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_uint]
+
+    def devptr(t):
+        out = ctypes.c_void_p()
+        assert rt.hipHostGetDevicePointer(ctypes.byref(out), ctypes.c_void_p(t.data_ptr()), 0) == 0
+        return out.value
+
+    ws = torch.empty(vqx.plane_stats_workspace_bytes(3840, 2160, 16, 3), dtype=torch.uint8, device="cuda:0")
+    for slot in range(2):
+        rc = vqx.lib().vqx_plane_stats_batch_ws(
+            r.data_ptr(), d.data_ptr(), 3840, 2160, 16, 3, devptr(host[slot, :3]), devptr(host[slot, 3:]),
+            ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
+        assert rc == 0
+    torch.cuda.synchronize()
+    for slot in range(2):
+        noise = host[slot, :3].numpy()
+        moments = host[slot, 3:].view(3, 4).numpy()
+        check(ref, dist, 16, noise, moments)
+
+
 def test_larger_call_after_smaller():
     """A later, larger batch in the same process starts from its own sums."""
     for (w, h, f) in ((64, 32, 2), (1920, 1080, 3), (3840, 2160, 2)):
