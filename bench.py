@@ -2,10 +2,14 @@
 """Throughput of the bit-exact plane reductions on one MI355X.
 
 One step = one batch through the whole path: the fused streaming kernel
-(stage 1), the exact per-frame combine (stage 2), the 40-byte-per-frame copy
-of the sums to pinned host memory, and the host conclusions (MSE, PSNR and
-the four moments) in libvqx.  Steps are pipelined: the host concludes batch
-i-1 while the GPU works on batch i.  Inputs are resident in HBM before the
+(stage 1), the exact per-frame combine (stage 2), which writes the frames'
+five sums (40 bytes each) straight into pinned host memory, and the host
+conclusions (MSE, PSNR and the four moments) in libvqx.  Steps run on one
+stream in groups of eight: each group ends with one completion event, and the
+host concludes a group's batches while the GPU runs the next group (an
+event record costs a few microseconds of command-processor time between
+kernels, so there is one per group, not per step).  Stage 1 of every step is
+timed with HIP events that its own dispatch stamps (hipExtLaunchKernel).  Inputs are resident in HBM before the
 timed region; two copies of the batch alternate so that the 256 MB Infinity
 Cache cannot serve a repeat.
 
@@ -24,6 +28,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import gc
 import hashlib
 import json
 import os
@@ -44,11 +49,12 @@ KERNEL_SOURCE = os.path.join(ROOT, "exact_reductions_amd", "csrc", "plane_stats.
 def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
-    # The first ~10 ms of sustained load run at reduced clocks while the
-    # power manager settles; 100 warm-up steps (~18 ms) get past that, and
-    # the timed steps measure steady streaming.
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=100)
+    # Under sustained load the pass runs slower for its first tens of
+    # milliseconds while the power manager settles (about 190 us per batch
+    # at first, 156 us after ~55 ms); 300 warm-up steps (~55 ms) get past
+    # that, and the timed steps measure steady streaming.
+    p.add_argument("--steps", type=int, default=500)
+    p.add_argument("--warmup", type=int, default=300)
     p.add_argument("--workload", type=int, default=5, help="workload number (5: 3840x2160 16-bit)")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the oracle leg (and with it the parity gate); for profiler runs")
@@ -118,6 +124,15 @@ class HipEvents:
             raise RuntimeError("pinned host memory is not mapped for the device")
         return out.value
 
+    def wait(self, stream: int, ev: int):
+        self.rt.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
+        if self.rt.hipStreamWaitEvent(ctypes.c_void_p(stream), ctypes.c_void_p(ev), 0) != 0:
+            raise RuntimeError("hipStreamWaitEvent failed")
+
+    def synchronize(self, ev: int):
+        if self.rt.hipEventSynchronize(ctypes.c_void_p(ev)) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+
     def record(self, ev: int, stream: int):
         if self.rt.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) != 0:
             raise RuntimeError("hipEventRecord failed")
@@ -135,9 +150,10 @@ def cpu_threads() -> int:
     return max(1, min(16, n))
 
 
-def cpu_baseline_and_gate(ref, dist, bpc, noise, moments, bytes_per_frame):
+def cpu_baseline_and_gate(ref, dist, bpc, noise, moments, bytes_per_frame, concl):
     """Time the CPU oracle on a bounded sample and check the device's last
-    batch against it.  Returns (cpu_baseline dict, parity dict)."""
+    batch, and the library's conclusion of it, against the oracle.  Returns
+    (cpu_baseline dict, parity dict)."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
@@ -156,6 +172,10 @@ def cpu_baseline_and_gate(ref, dist, bpc, noise, moments, bytes_per_frame):
     for f in range(nframes):
         dev5 = [int(noise[f])] + [int(v) for v in moments[f]]
         fails = oracle.acceptance(dev5, o1[f], o2[f], w, h, bpc)
+        want = oracle.conclude_from_ints(dev5, w, h, bpc)
+        got = [concl[f, 0]] + list(concl[f, 2:])
+        if got != list(want) or concl[f, 1] != oracle.psnr_db(want[0], bpc, 0.0):
+            fails.append(("conclusion", f"{got} != {list(want)}"))
         if fails:
             failures.append((f, fails))
         past53 += sum(1 for v in o2[f] if int(v) >= oracle.TWO53)
@@ -242,69 +262,103 @@ def main(argv=None):
     bufs = [(r0, d0), (r0.clone(), d0.clone())]
     # Sums land directly in pinned host memory that the GPU writes through
     # (zero-copy): stage 2 stores 40 bytes per frame there, and no copy
-    # kernel runs.  Two slots, so that batch i+1 can be queued while the host
-    # concludes batch i.
-    sums = torch.zeros((2, 5 * nframes), dtype=torch.int64, pin_memory=True)
-    noise = [sums[s, :nframes] for s in range(2)]
-    moments = [sums[s, nframes:].view(nframes, 4) for s in range(2)]
+    # kernel runs.  `depth` groups of slots, so that the GPU always has
+    # several groups queued while the host concludes the oldest one.
+    group = 8
+    depth = 4  # groups in flight: ~5 ms of queued work absorbs host hiccups
+    nslots = depth * group
+    sums = torch.zeros((nslots, 5 * nframes), dtype=torch.int64, pin_memory=True)
+    noise = [sums[s, :nframes] for s in range(nslots)]
+    moments = [sums[s, nframes:].view(nframes, 4) for s in range(nslots)]
+    stream = torch.cuda.current_stream(dev)
+    st = stream.cuda_stream
     ws_bytes = vqx.plane_stats_workspace_bytes(w, h, bpc, nframes)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
     hip = HipEvents(vqx.hip_runtime())
     L = vqx.lib()
     noise_dev = [hip.device_pointer(t.data_ptr()) for t in noise]
     moments_dev = [hip.device_pointer(t.data_ptr()) for t in moments]
     total = args.warmup + args.steps
-    ev_begin = [hip.create() for _ in range(total + 1)]
-    ev_end = [hip.create() for _ in range(total)]
+    timed_every = 1
+    ev_begin = {i: hip.create() for i in range(0, total, timed_every)}
+    ev_end = {i: hip.create() for i in ev_begin}
+    ev_done = [hip.create() for _ in range((total + group - 1) // group + 1)]
     torch.cuda.synchronize()
 
-    results = {}
+    # The host conclusion allocates nothing: libvqx concludes from the pinned
+    # sums into preallocated arrays, and each step's sums are copied in place
+    # into a preallocated history (to check afterwards that every step gave
+    # the same sums).  Allocating numpy temporaries per batch stalled the
+    # host for up to tens of milliseconds after the batch generation.
+    sums_np = sums.numpy()
+    concl = np.zeros((nslots, nframes, 6), dtype=np.float64)
+    concl_ptr = [concl[s].ctypes.data for s in range(nslots)]
+    noise_ptr = [noise[s].data_ptr() for s in range(nslots)]
+    moments_ptr = [moments[s].data_ptr() for s in range(nslots)]
+    history = np.zeros((total, 5 * nframes), dtype=np.int64)
 
     def enqueue(i):
-        # the begin event of step i also marks the end of step i-1 (same stream)
+        s = i % nslots
         r, d = bufs[i % 2]
         rc = L.vqx_plane_stats_batch_ws_timed(r.data_ptr(), d.data_ptr(), w, h, bpc, nframes,
-                                              noise_dev[i % 2], moments_dev[i % 2], ws.data_ptr(),
-                                              ws_bytes, stream.cuda_stream, ev_begin[i], ev_end[i])
+                                              noise_dev[s], moments_dev[s], ws.data_ptr(), ws_bytes,
+                                              st, ev_begin.get(i), ev_end.get(i))
         if rc != 0:
             raise vqx.VqxError(rc, "vqx_plane_stats_batch_ws_timed")
 
-    def conclude(i):
-        # wait for step i (the next begin event, or a final marker), then conclude it
-        if hip.rt.hipEventSynchronize(ctypes.c_void_p(ev_begin[i + 1])) != 0:
-            raise RuntimeError("hipEventSynchronize failed")
-        s = i % 2
-        results[i] = (vqx.conclude_batch(noise[s].numpy(), moments[s].numpy(), w, h, bpc),
-                      noise[s].numpy().copy(), moments[s].numpy().copy())
+    def conclude(steps, done):
+        hip.synchronize(done)
+        for i in steps:
+            s = i % nslots
+            rc = L.vqx_conclude_batch(noise_ptr[s], moments_ptr[s], w, h, bpc, nframes, 0.0,
+                                      concl_ptr[s])
+            if rc != 0:
+                raise vqx.VqxError(rc, "vqx_conclude_batch")
+            history[i] = sums_np[s]
 
     def run(first, count):
-        for i in range(first, first + count):
-            enqueue(i)
-            if i > first:
-                conclude(i - 1)
-        last = first + count - 1
-        hip.record(ev_begin[last + 1], stream.cuda_stream)
-        conclude(last)
+        # step i uses slot i % nslots; a slot is reused only after the group
+        # that last used it was concluded (at most `depth` groups in flight)
+        groups = [list(range(a, min(a + group, first + count))) for a in range(first, first + count, group)]
+        pending = []
+        for steps in groups:
+            if len(pending) == depth:
+                conclude(*pending.pop(0))
+            for i in steps:
+                enqueue(i)
+            done = ev_done[steps[0] // group]
+            hip.record(done, st)
+            pending.append((steps, done))
+        while pending:
+            conclude(*pending.pop(0))
 
-    if args.warmup > 0:
-        run(0, args.warmup)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    run(args.warmup, args.steps)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    gc_was_enabled = gc.isenabled()
+    gc.disable()
+    try:
+        if args.warmup > 0:
+            run(0, args.warmup)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run(args.warmup, args.steps)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    finally:
+        if gc_was_enabled:
+            gc.enable()
 
-    stage1_ms = [hip.elapsed_ms(ev_begin[i], ev_end[i]) for i in range(args.warmup, total)]
-    for ev in ev_begin + ev_end:
+    stage1_ms = [hip.elapsed_ms(ev_begin[i], ev_end[i]) for i in ev_begin if i >= args.warmup]
+    for ev in list(ev_begin.values()) + list(ev_end.values()) + ev_done:
         hip.destroy(ev)
 
-    # every timed step must have produced the same sums
-    last = results[total - 1]
-    for i in range(args.warmup, total):
-        if not (np.array_equal(results[i][1], last[1]) and np.array_equal(results[i][2], last[2])):
-            print(f"step {i} differs from the last step", file=sys.stderr)
-            return 1
+    # every step must have produced the same sums
+    if not np.all(history == history[total - 1]):
+        bad = int(np.nonzero(np.any(history != history[total - 1], axis=1))[0][0])
+        print(f"step {bad} differs from the last step", file=sys.stderr)
+        return 1
+    last_noise = history[total - 1, :nframes]
+    last_moments = history[total - 1, nframes:].reshape(nframes, 4)
+    # the library's conclusion of the last step, from the same sums
+    last_concl = concl[(total - 1) % nslots].copy()
 
     if args.calibrate_copy:
         # a kernel that reads exactly n bytes and writes exactly n bytes
@@ -352,15 +406,16 @@ def main(argv=None):
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "stage1_us_mean": round(mean_stage1 * 1e3, 2),
-            "stage1_us_median": round(statistics.median(stage1_ms) * 1e3, 2),
+            "kernel_us_mean": round(mean_stage1 * 1e3, 2),
+            "kernel_us_median": round(statistics.median(stage1_ms) * 1e3, 2),
             "algorithmic_bytes_per_launch": bytes_per_launch,
         },
         "generation_s": round(t_gen, 1),
     }
 
     if not args.no_cpu_baseline:
-        base, parity = cpu_baseline_and_gate(ref_np, dist_np, bpc, last[1], last[2], bytes_per_frame)
+        base, parity = cpu_baseline_and_gate(ref_np, dist_np, bpc, last_noise, last_moments,
+                                             bytes_per_frame, last_concl)
         out["cpu_baseline"] = base
         out["parity"] = parity
         if parity["failures"]:

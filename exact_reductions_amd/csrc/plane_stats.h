@@ -10,6 +10,10 @@ namespace vqx {
 // Number of 64-bit sums in one partial record, in this order.
 enum : int { kNoise = 0, kRef1 = 1, kDist1 = 2, kRef2 = 3, kDist2 = 4, kSums = 5 };
 
+// A workgroup's partial record occupies its own 64-byte slot (8 uint64, 5
+// used), so that no two workgroups write the same cache line.
+constexpr int kRecordStride = 8;
+
 // Work split of one batch.  Each plane is read as 16-byte vectors; the
 // vectors of a frame that lie wholly inside it are cut into chunks of
 // chunk_vecs vectors, one workgroup per (frame, chunk).  The few samples of a

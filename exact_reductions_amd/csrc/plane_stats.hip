@@ -33,6 +33,8 @@
 // as its low 16 bits and the rest, two uint32 sums -- the page's low/high
 // split at 16 bits [PSNR, Decision], moved from every term to once per lane.
 
+#include <hip/hip_ext.h>
+
 #include "plane_stats.h"
 
 #pragma clang fp contract(off)
@@ -181,16 +183,15 @@ __device__ __forceinline__ void workgroup_sums(const uint32_t (&v)[N], uint64_t 
     }
 }
 
-__device__ __forceinline__ void write_record(uint64_t *part, int64_t nwg, int64_t wg,
-                                             uint64_t noise, uint64_t r1, uint64_t d1,
-                                             uint64_t r2, uint64_t d2)
+// Thread 0 writes the workgroup's record; the combine kernel that follows
+// in the stream reads it.
+__device__ __forceinline__ void write_record(uint64_t *part, int64_t wg,
+                                             const uint64_t (&rec)[kSums])
 {
     if (threadIdx.x == 0) {
-        part[kNoise * nwg + wg] = noise;
-        part[kRef1 * nwg + wg] = r1;
-        part[kDist1 * nwg + wg] = d1;
-        part[kRef2 * nwg + wg] = r2;
-        part[kDist2 * nwg + wg] = d2;
+#pragma unroll
+        for (int k = 0; k < kSums; ++k)
+            part[wg * kRecordStride + k] = rec[k];
     }
 }
 
@@ -262,64 +263,25 @@ __device__ __forceinline__ void accumulate_chunk(Acc &acc, const void *ref, cons
     }
 }
 
-__global__ __launch_bounds__(kThreads) void stage1_u8(const void *ref, const void *dist,
-                                                      int64_t pixels, int chunks, int64_t nwg,
-                                                      uint64_t *part)
+// ------------------------------------------------------------- combine
+// Adds frame `frame`'s records in uint64 and writes its five sums.  All
+// kThreads threads of the workgroup must call it.
+__device__ __forceinline__ void combine_frame(const uint64_t *part, int chunks, int64_t frame, uint64_t *out_noise,
+                                              uint64_t *out_moments)
 {
-    const int64_t wg = blockIdx.x;
-    const int64_t frame = wg / chunks;
-    const int chunk = static_cast<int>(wg - frame * chunks);
-    Acc8 a;
-    accumulate_chunk<1>(a, ref, dist, pixels, chunk, frame);
-    const uint32_t v[5] = {a.r1, a.d1, a.r2, a.d2, a.rd};
-    uint64_t s[5];
-    workgroup_sums(v, s);
-    // sum (r-d)^2 = sum r^2 + sum d^2 - 2 sum r*d, exact in uint64
-    write_record(part, nwg, wg, s[2] + s[3] - 2 * s[4], s[0], s[1], s[2], s[3]);
-}
-
-__global__ __launch_bounds__(kThreads) void stage1_u16(const void *ref, const void *dist,
-                                                       int64_t pixels, int chunks, int64_t nwg,
-                                                       uint64_t *part)
-{
-    const int64_t wg = blockIdx.x;
-    const int64_t frame = wg / chunks;
-    const int chunk = static_cast<int>(wg - frame * chunks);
-    Acc16 a;
-    accumulate_chunk<2>(a, ref, dist, pixels, chunk, frame);
-    // each 64-bit lane sum crosses the wave as (low 16 bits, the rest)
-    const uint32_t v[8] = {static_cast<uint32_t>(a.noise & 0xffffu), static_cast<uint32_t>(a.noise >> 16),
-                           a.r1, a.d1,
-                           static_cast<uint32_t>(a.r2 & 0xffffu), static_cast<uint32_t>(a.r2 >> 16),
-                           static_cast<uint32_t>(a.d2 & 0xffffu), static_cast<uint32_t>(a.d2 >> 16)};
-    uint64_t s[8];
-    workgroup_sums(v, s);
-    write_record(part, nwg, wg, s[0] + (s[1] << 16), s[2], s[3], s[4] + (s[5] << 16),
-                 s[6] + (s[7] << 16));
-}
-
-// ------------------------------------------------------------------ stage 2
-// One workgroup per frame adds the frame's records in uint64.
-constexpr int kCombineThreads = 256;
-
-__global__ __launch_bounds__(kCombineThreads) void stage2_combine(const uint64_t *part, int chunks,
-                                                                  int64_t nwg, uint64_t *out_noise,
-                                                                  uint64_t *out_moments)
-{
-    __shared__ uint64_t lds[kSums][kCombineThreads];
-    const int64_t frame = blockIdx.x;
+    __shared__ uint64_t lds[kSums][kThreads];
     const int t = threadIdx.x;
     uint64_t s[kSums] = {0, 0, 0, 0, 0};
-    for (int c = t; c < chunks; c += kCombineThreads) {
+    for (int c = t; c < chunks; c += kThreads) {
 #pragma unroll
         for (int k = 0; k < kSums; ++k)
-            s[k] += part[k * nwg + frame * chunks + c];
+            s[k] += part[(frame * chunks + c) * kRecordStride + k];
     }
 #pragma unroll
     for (int k = 0; k < kSums; ++k)
         lds[k][t] = s[k];
     __syncthreads();
-    for (int off = kCombineThreads / 2; off > 0; off >>= 1) {
+    for (int off = kThreads / 2; off > 0; off >>= 1) {
         if (t < off) {
 #pragma unroll
             for (int k = 0; k < kSums; ++k)
@@ -334,6 +296,51 @@ __global__ __launch_bounds__(kCombineThreads) void stage2_combine(const uint64_t
         out_moments[4 * frame + 2] = lds[kRef2][0];
         out_moments[4 * frame + 3] = lds[kDist2][0];
     }
+}
+
+__global__ __launch_bounds__(kThreads) void stage1_u8(const void *ref, const void *dist,
+                                                      int64_t pixels, int chunks, uint64_t *part)
+{
+    const int64_t wg = blockIdx.x;
+    const int64_t frame = wg / chunks;
+    const int chunk = static_cast<int>(wg - frame * chunks);
+    Acc8 a;
+    accumulate_chunk<1>(a, ref, dist, pixels, chunk, frame);
+    const uint32_t v[5] = {a.r1, a.d1, a.r2, a.d2, a.rd};
+    uint64_t s[5];
+    workgroup_sums(v, s);
+    // sum (r-d)^2 = sum r^2 + sum d^2 - 2 sum r*d, exact in uint64
+    const uint64_t rec[kSums] = {s[2] + s[3] - 2 * s[4], s[0], s[1], s[2], s[3]};
+    write_record(part, wg, rec);
+}
+
+__global__ __launch_bounds__(kThreads) void stage1_u16(const void *ref, const void *dist,
+                                                       int64_t pixels, int chunks, uint64_t *part)
+{
+    const int64_t wg = blockIdx.x;
+    const int64_t frame = wg / chunks;
+    const int chunk = static_cast<int>(wg - frame * chunks);
+    Acc16 a;
+    accumulate_chunk<2>(a, ref, dist, pixels, chunk, frame);
+    // each 64-bit lane sum crosses the wave as (low 16 bits, the rest)
+    const uint32_t v[8] = {static_cast<uint32_t>(a.noise & 0xffffu), static_cast<uint32_t>(a.noise >> 16),
+                           a.r1, a.d1,
+                           static_cast<uint32_t>(a.r2 & 0xffffu), static_cast<uint32_t>(a.r2 >> 16),
+                           static_cast<uint32_t>(a.d2 & 0xffffu), static_cast<uint32_t>(a.d2 >> 16)};
+    uint64_t s[8];
+    workgroup_sums(v, s);
+    const uint64_t rec[kSums] = {s[0] + (s[1] << 16), s[2], s[3], s[4] + (s[5] << 16),
+                                 s[6] + (s[7] << 16)};
+    write_record(part, wg, rec);
+}
+
+// ------------------------------------------------------------------ stage 2
+// One workgroup per frame adds the frame's records in uint64.
+__global__ __launch_bounds__(kThreads) void stage2_combine(const uint64_t *part, int chunks,
+                                                           uint64_t *out_noise,
+                                                           uint64_t *out_moments)
+{
+    combine_frame(part, chunks, blockIdx.x, out_noise, out_moments);
 }
 
 }  // namespace
@@ -352,7 +359,7 @@ Geometry make_geometry(int w, int h, int bpc, int nframes)
     const int64_t chunks = (max_vecs + kChunkVecs - 1) / kChunkVecs;
     g.chunks = static_cast<int>(chunks < 1 ? 1 : chunks);
     g.workgroups = static_cast<int64_t>(g.chunks) * nframes;
-    g.workspace_bytes = static_cast<size_t>(g.workgroups) * kSums * sizeof(uint64_t);
+    g.workspace_bytes = static_cast<size_t>(g.workgroups) * kRecordStride * sizeof(uint64_t);
     return g;
 }
 
@@ -361,27 +368,29 @@ hipError_t launch_plane_stats(const Geometry &g, const void *ref, const void *di
                               hipStream_t stream, hipEvent_t stage1_begin, hipEvent_t stage1_end)
 {
     const dim3 grid1(static_cast<unsigned>(g.workgroups));
-    if (stage1_begin) {
-        hipError_t e = hipEventRecord(stage1_begin, stream);
+    int64_t pixels = g.pixels;
+    int chunks = g.chunks;
+    if (stage1_begin || stage1_end) {
+        // AMD's launch with events: the dispatch itself stamps the events,
+        // so no marker packets are queued around the kernel
+        void *args[] = {const_cast<void **>(&ref), const_cast<void **>(&dist), &pixels, &chunks,
+                        &partials};
+        const void *fn = g.sample_bytes == 1 ? reinterpret_cast<const void *>(&stage1_u8)
+                                             : reinterpret_cast<const void *>(&stage1_u16);
+        hipError_t e = hipExtLaunchKernel(fn, grid1, dim3(kThreads), args, 0, stream, stage1_begin,
+                                          stage1_end, 0);
         if (e != hipSuccess)
             return e;
+    } else if (g.sample_bytes == 1) {
+        stage1_u8<<<grid1, kThreads, 0, stream>>>(ref, dist, pixels, chunks, partials);
+    } else {
+        stage1_u16<<<grid1, kThreads, 0, stream>>>(ref, dist, pixels, chunks, partials);
     }
-    if (g.sample_bytes == 1)
-        stage1_u8<<<grid1, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, g.workgroups,
-                                                  partials);
-    else
-        stage1_u16<<<grid1, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, g.workgroups,
-                                                   partials);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    if (stage1_end) {
-        err = hipEventRecord(stage1_end, stream);
-        if (err != hipSuccess)
-            return err;
-    }
-    stage2_combine<<<dim3(static_cast<unsigned>(g.nframes)), kCombineThreads, 0, stream>>>(
-        partials, g.chunks, g.workgroups, out_noise, out_moments);
+    stage2_combine<<<dim3(static_cast<unsigned>(g.nframes)), kThreads, 0, stream>>>(
+        partials, chunks, out_noise, out_moments);
     return hipGetLastError();
 }
 

@@ -124,11 +124,12 @@ int vqx_plane_stats_batch_ws(const void *ref, const void *dist, int w, int h, in
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * As vqx_plane_stats_batch_ws, and also records two caller-created
- * hipEvent_t on `stream`: `stage1_begin` right before and `stage1_end` right
- * after the streaming kernel (stage 1), so that hipEventElapsedTime gives
- * that kernel's duration.  Either event may be NULL.  Results and errors are
- * those of vqx_plane_stats_batch_ws; no event is recorded on an error.
+ * As vqx_plane_stats_batch_ws, and also stamps two caller-created
+ * hipEvent_t with the start and the end of the streaming kernel (stage 1):
+ * the kernel is launched with hipExtLaunchKernel, whose dispatch records the
+ * events itself, so hipEventElapsedTime gives that kernel's duration and no
+ * extra packet is queued.  Either event may be NULL.  Results and errors are
+ * those of vqx_plane_stats_batch_ws.
  */
 int vqx_plane_stats_batch_ws_timed(const void *ref, const void *dist, int w, int h, int bpc,
                                    int nframes, uint64_t *out_noise, uint64_t *out_moments,

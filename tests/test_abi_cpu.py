@@ -54,11 +54,12 @@ def test_status_codes_match_header():
 
 
 def test_workspace_bytes():
+    # one 64-byte record per workgroup
     # 3840x2160 uint16: 1 036 800 16-byte vectors, 2048 per workgroup -> 507 per frame
-    assert vqx.plane_stats_workspace_bytes(3840, 2160, 16, 32) == 507 * 32 * 40
+    assert vqx.plane_stats_workspace_bytes(3840, 2160, 16, 32) == 507 * 32 * 64
     # 576x324 uint8: 11 664 vectors -> 6 per frame
-    assert vqx.plane_stats_workspace_bytes(576, 324, 8, 4) == 6 * 4 * 40
-    assert vqx.plane_stats_workspace_bytes(1, 1, 12, 7) == 7 * 40
+    assert vqx.plane_stats_workspace_bytes(576, 324, 8, 4) == 6 * 4 * 64
+    assert vqx.plane_stats_workspace_bytes(1, 1, 12, 7) == 7 * 64
     for args, status in (((0, 5, 8, 1), vqx.E_DIMS), ((5, 0, 8, 1), vqx.E_DIMS),
                          ((8192, 4097, 8, 1), vqx.E_DIMS), ((5, 5, 7, 1), vqx.E_BPC),
                          ((5, 5, 17, 1), vqx.E_BPC), ((5, 5, 8, 0), vqx.E_NFRAMES)):

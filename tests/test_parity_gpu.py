@@ -92,10 +92,11 @@ def workload(n):
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
-def test_workload_full_size(n):
+@pytest.mark.parametrize("entry", ["caching", "workspace_ff"])
+def test_workload_full_size(n, entry):
     wl = synth.WORKLOADS[n]
     ref, dist = workload(n)
-    noise, moments = device_sums(ref, dist, wl.bpc)
+    noise, moments = device_sums(ref, dist, wl.bpc, entry=entry, prefill=-1)
     o1, o2 = check(ref, dist, wl.bpc, noise, moments)
     if n == 5:
         # the second-moment sums pass 2^53 units on every frame, so the bound
@@ -171,11 +172,12 @@ SHAPES = [
 
 @pytest.mark.parametrize("w,h,f", SHAPES, ids=[f"{w}x{h}x{f}" for w, h, f in SHAPES])
 @pytest.mark.parametrize("bpc", [8, 16])
-def test_shapes(w, h, f, bpc):
+@pytest.mark.parametrize("entry", ["caching", "workspace_ff"])
+def test_shapes(w, h, f, bpc, entry):
     """Odd sizes: frames shorter than a 16-byte vector, frame starts that are
     not 16-byte aligned inside the batch, chunks with a ragged tail."""
     ref, dist = synth.uniform_planes(w, h, f, bpc, seed=w * 131 + h * 7 + f + bpc)
-    noise, moments = device_sums(ref, dist, bpc)
+    noise, moments = device_sums(ref, dist, bpc, entry=entry, prefill=-1)
     check(ref, dist, bpc, noise, moments)
 
 
@@ -186,6 +188,47 @@ def test_every_depth_full_container(bpc):
     ref, dist = synth.uniform_planes(300, 201, 3, bpc, seed=900 + bpc, container_max=True)
     noise, moments = device_sums(ref, dist, bpc)
     check(ref, dist, bpc, noise, moments)
+
+
+def test_one_workspace_reused_across_sizes():
+    """One workspace, large enough for the largest call, reused by calls of
+    changing size: each call writes every record it reads."""
+    shapes = ((64, 32, 2, 16), (3840, 2160, 3, 16), (18, 22, 1000, 8), (1920, 1080, 40, 16),
+              (7, 3, 5, 10), (3840, 2160, 1, 12), (1, 1, 70, 16), (640, 360, 130, 8))
+    need = max(vqx.plane_stats_workspace_bytes(w, h, bpc, f) for w, h, f, bpc in shapes)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda:0")
+    for (w, h, f, bpc) in shapes:
+        ref, dist = synth.uniform_planes(w, h, f, bpc, seed=w * 7 + h + f, container_max=True)
+        r, d = upload(ref), upload(dist)
+        noise = torch.full((f,), -1, dtype=torch.int64, device="cuda:0")
+        moments = torch.full((f, 4), -1, dtype=torch.int64, device="cuda:0")
+        vqx.plane_stats_batch_ws(r, d, bpc, noise, moments, ws)
+        torch.cuda.synchronize()
+        check(ref, dist, bpc, noise.cpu().numpy(), moments.cpu().numpy())
+
+
+def test_two_streams_two_workspaces():
+    """Calls alternating between two streams, each with its own workspace
+    and outputs, so that one call's combine overlaps the next call's pass."""
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    cases = [synth.generate(4, nframes=6), synth.uniform_planes(1920, 1080, 6, 16, seed=5, container_max=True)]
+    ups = [(upload(r), upload(d)) for r, d in cases]
+    torch.cuda.synchronize()
+    need = vqx.plane_stats_workspace_bytes(1920, 1080, 16, 6)
+    wss = [torch.empty(need, dtype=torch.uint8, device="cuda:0") for _ in range(2)]
+    outs = []
+    for rep in range(4):
+        for k, s in enumerate((s1, s2)):
+            r, d = ups[k]
+            with torch.cuda.stream(s):
+                n = torch.full((6,), -1, dtype=torch.int64, device="cuda:0")
+                m = torch.full((6, 4), -1, dtype=torch.int64, device="cuda:0")
+                vqx.plane_stats_batch_ws(r, d, 16, n, m, wss[k])
+                outs.append((k, n, m))
+    torch.cuda.synchronize()
+    for k, n, m in outs:
+        ref, dist = cases[k]
+        check(ref, dist, 16, n.cpu().numpy(), m.cpu().numpy())
 
 
 def test_tall_frame_962x13542():
