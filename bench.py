@@ -375,7 +375,7 @@ def main(argv=None):
     mean_stage1 = statistics.fmean(stage1_ms)
     achieved = bytes_per_launch / (mean_stage1 * 1e-3) / 1e9
     kernel = "stage1_u8" if bpc == 8 else "stage1_u16"
-    wname = f"{w}x{h}x{nframes}"
+    wname = f"{w}x{h}x{nframes}_{bpc}bit"
     traffic = stored_traffic(kernel, wname)
 
     out = {

@@ -78,7 +78,7 @@ def main(argv=None):
     import synth
     wl = synth.WORKLOADS[args.workload]
     kernel = "stage1_u8" if wl.bpc == 8 else "stage1_u16"
-    wname = f"{wl.w}x{wl.h}x{wl.nframes}"
+    wname = f"{wl.w}x{wl.h}x{wl.nframes}_{wl.bpc}bit"
     os.makedirs(args.out, exist_ok=True)
     os.makedirs(args.work, exist_ok=True)
     bench = ["python3", os.path.join(ROOT, "bench.py"), "--workload", str(args.workload),
