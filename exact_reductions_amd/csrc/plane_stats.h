@@ -10,6 +10,9 @@ namespace vqx {
 // Number of 64-bit sums in one partial record, in this order.
 enum : int { kNoise = 0, kRef1 = 1, kDist1 = 2, kRef2 = 3, kDist2 = 4, kSums = 5 };
 
+// 16-byte vectors of each plane per chunk (one stage-1 workgroup each).
+constexpr int kChunkVectors = 2048;
+
 // A workgroup's partial record occupies its own 64-byte slot (8 uint64, 5
 // used), so that no two workgroups write the same cache line.
 constexpr int kRecordStride = 8;
@@ -39,5 +42,19 @@ hipError_t launch_plane_stats(const Geometry &g, const void *ref, const void *di
                               uint64_t *out_noise, uint64_t *out_moments, uint64_t *partials,
                               hipStream_t stream, hipEvent_t stage1_begin = nullptr,
                               hipEvent_t stage1_end = nullptr);
+
+// Workspace of the CPU-order form: byte offsets of its parts.
+struct CpuOrderLayout {
+    size_t records, prefix, totals, maps, bytes;
+};
+CpuOrderLayout cpu_order_layout(const Geometry &g);
+
+// Both stages, then the three kernels that reproduce the CPU's running
+// double sums (cpu_order.hip): out_cpu_noise[F] and out_cpu_moments[F][4],
+// in the same units as the exact sums.
+hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, const void *dist,
+                                        uint64_t *out_noise, uint64_t *out_moments,
+                                        uint64_t *out_cpu_noise, uint64_t *out_cpu_moments,
+                                        void *workspace, hipStream_t stream);
 
 }  // namespace vqx

@@ -36,6 +36,7 @@
 #include <hip/hip_ext.h>
 
 #include "plane_stats.h"
+#include "terms.h"
 
 #pragma clang fp contract(off)
 
@@ -50,6 +51,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kIters = 8;                  // 16-byte vectors per lane per plane
 constexpr int kInFlight = 4;               // vectors of each plane loaded before use
 constexpr int kChunkVecs = kThreads * kIters;  // 32 KiB of each plane per workgroup
+static_assert(kChunkVecs == kChunkVectors, "one chunk size for every kernel");
 static_assert(kIters % kInFlight == 0, "whole load groups");
 
 // ----------------------------------------------------------------- budgets
@@ -91,15 +93,6 @@ struct Acc16 {
     uint64_t noise = 0, r2 = 0, d2 = 0;
     uint32_t r1 = 0, d1 = 0;
 };
-
-// The float square of x read back as an integer: one binary32 product, round
-// to nearest even, then an exact conversion (the product is an integer below
-// 2^32) [MOMENT, Decision].
-__device__ __forceinline__ uint32_t float_square(float x)
-{
-    const float p = x * x;
-    return static_cast<uint32_t>(p);
-}
 
 // Two samples of each plane packed in one dword.
 __device__ __forceinline__ void add_dword(Acc16 &a, uint32_t r, uint32_t d)

@@ -178,6 +178,46 @@ int vqx_plane_stats_batch(const void *ref, const void *dist, int w, int h, int b
     return VQX_OK;
 }
 
+int vqx_plane_stats_cpu_order_workspace_bytes(int w, int h, int bpc, int nframes, size_t *bytes)
+{
+    if (!bytes)
+        return VQX_E_NULL;
+    int rc = check_batch(w, h, bpc, nframes);
+    if (rc != VQX_OK)
+        return rc;
+    *bytes = vqx::cpu_order_layout(vqx::make_geometry(w, h, bpc, nframes)).bytes;
+    return VQX_OK;
+}
+
+int vqx_plane_stats_batch_cpu_order_ws(const void *ref, const void *dist, int w, int h, int bpc,
+                                       int nframes, uint64_t *out_noise, uint64_t *out_moments,
+                                       uint64_t *out_cpu_noise, uint64_t *out_cpu_moments,
+                                       void *workspace, size_t workspace_bytes, void *stream)
+{
+    int rc = check_stats_args(ref, dist, w, h, bpc, nframes, out_noise, out_moments);
+    if (rc != VQX_OK)
+        return rc;
+    if (!out_cpu_noise || !out_cpu_moments)
+        return VQX_E_NULL;
+    if (!aligned(out_cpu_noise, 8) || !aligned(out_cpu_moments, 8))
+        return VQX_E_ALIGN;
+    const vqx::Geometry g = vqx::make_geometry(w, h, bpc, nframes);
+    if (!workspace || !aligned(workspace, 16) ||
+        workspace_bytes < vqx::cpu_order_layout(g).bytes)
+        return VQX_E_WORKSPACE;
+    rc = device_ready();
+    if (rc != VQX_OK)
+        return rc;
+    hipError_t err = vqx::launch_plane_stats_cpu_order(g, ref, dist, out_noise, out_moments,
+                                                       out_cpu_noise, out_cpu_moments, workspace,
+                                                       static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) {
+        (void)hipGetLastError();
+        return VQX_E_HIP;
+    }
+    return VQX_OK;
+}
+
 int vqx_conclude_psnr(uint64_t noise, int w, int h, int bpc, double psnr_max, double *mse,
                       double *psnr_db)
 {

@@ -28,6 +28,8 @@ SYMBOLS = (
     "vqx_plane_stats_batch",
     "vqx_plane_stats_batch_ws",
     "vqx_plane_stats_batch_ws_timed",
+    "vqx_plane_stats_cpu_order_workspace_bytes",
+    "vqx_plane_stats_batch_cpu_order_ws",
     "vqx_conclude_psnr",
     "vqx_conclude_moments",
     "vqx_conclude_batch",
@@ -64,6 +66,8 @@ def lib() -> ctypes.CDLL:
             "vqx_plane_stats_batch": (i, [vp, vp, i, i, i, i, vp, vp, vp]),
             "vqx_plane_stats_batch_ws": (i, [vp, vp, i, i, i, i, vp, vp, vp, sz, vp]),
             "vqx_plane_stats_batch_ws_timed": (i, [vp, vp, i, i, i, i, vp, vp, vp, sz, vp, vp, vp]),
+            "vqx_plane_stats_cpu_order_workspace_bytes": (i, [i, i, i, i, ctypes.POINTER(sz)]),
+            "vqx_plane_stats_batch_cpu_order_ws": (i, [vp, vp, i, i, i, i, vp, vp, vp, vp, vp, sz, vp]),
             "vqx_conclude_psnr": (i, [u64, i, i, i, d, ctypes.POINTER(d), ctypes.POINTER(d)]),
             "vqx_conclude_moments": (i, [vp, i, i, i, vp]),
             "vqx_conclude_batch": (i, [vp, vp, i, i, i, i, d, vp]),
@@ -170,6 +174,31 @@ def plane_stats_batch(ref, dist, bpc: int, stream=None, out_noise=None, out_mome
         out_moments = torch.empty((f, 4), dtype=torch.int64, device=dev)
     ws = torch.empty(plane_stats_workspace_bytes(w, h, bpc, f), dtype=torch.uint8, device=dev)
     return plane_stats_batch_ws(ref, dist, bpc, out_noise, out_moments, ws, stream)
+
+
+def plane_stats_cpu_order_workspace_bytes(w: int, h: int, bpc: int, nframes: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().vqx_plane_stats_cpu_order_workspace_bytes(w, h, bpc, nframes, ctypes.byref(out)),
+           "plane_stats_cpu_order_workspace_bytes")
+    return out.value
+
+
+def plane_stats_batch_cpu_order(ref, dist, bpc: int, stream=None):
+    """The exact sums and the CPU's running double sums of every frame:
+    ``(noise [F], moments [F][4], cpu_noise [F], cpu_moments [F][4])`` as
+    int64 device tensors.  The CPU's sums are the values its sequential
+    double accumulators hold (times the unit), bit for bit, also past 2^53."""
+    import torch
+    ref, dist = _planes(ref, dist, bpc)
+    f, h, w = ref.shape
+    dev = ref.device
+    out = torch.empty((2, 5 * f), dtype=torch.int64, device=dev)
+    ws = torch.empty(plane_stats_cpu_order_workspace_bytes(w, h, bpc, f), dtype=torch.uint8, device=dev)
+    _check(lib().vqx_plane_stats_batch_cpu_order_ws(
+        ref.data_ptr(), dist.data_ptr(), w, h, bpc, f, out[0, :f].data_ptr(), out[0, f:].data_ptr(),
+        out[1, :f].data_ptr(), out[1, f:].data_ptr(), ws.data_ptr(), ws.numel(),
+        _stream_handle(dev, stream)), "plane_stats_batch_cpu_order_ws")
+    return out[0, :f], out[0, f:].view(f, 4), out[1, :f], out[1, f:].view(f, 4)
 
 
 def plane_stats_batch_selfalloc(ref, dist, bpc: int, out_noise, out_moments, stream=None):

@@ -137,6 +137,39 @@ int vqx_plane_stats_batch_ws_timed(const void *ref, const void *dist, int w, int
                                    void *stage1_begin, void *stage1_end);
 
 /*
+ * Device scratch needed by vqx_plane_stats_batch_cpu_order_ws.  Host-only.
+ * Errors: VQX_E_NULL, VQX_E_DIMS, VQX_E_BPC, VQX_E_NFRAMES.
+ */
+int vqx_plane_stats_cpu_order_workspace_bytes(int w, int h, int bpc, int nframes, size_t *bytes);
+
+/*
+ * The exact sums, as vqx_plane_stats_batch_ws, and also the values the
+ * CPU extractors' running double sums hold after their last add, bit for
+ * bit, on every frame:
+ *   out_cpu_noise    uint64[nframes], out_cpu_moments uint64[nframes][4],
+ *                    in the units of the exact sums (every such double is an
+ *                    integer in these units, below 2^58).
+ * Below 2^53 units they equal the exact sums.  Past it the CPU rounds
+ * every add to the sum's last place [PSNR, Consequences; MOMENT, Decision]
+ * and these are its rounded values, reproduced by composing the
+ * round-to-nearest-even steps of runs of adds (a two-state map per run
+ * inside one binade) and walking the frame in the CPU's raster order --
+ * the sequence of roundings that the float_moment page leaves to a later
+ * change [MOMENT, Alternatives].  Concluding them with
+ * vqx_conclude_batch gives the CPU's scores bit for bit on every frame.
+ *
+ * Frames whose sums stay below 2^53 cost only three small kernels more
+ * than vqx_plane_stats_batch_ws; a frame past 2^53 costs one more read of
+ * its planes.  Arguments, layout, ownership and errors otherwise as
+ * vqx_plane_stats_batch_ws, with the workspace sized by
+ * vqx_plane_stats_cpu_order_workspace_bytes.
+ */
+int vqx_plane_stats_batch_cpu_order_ws(const void *ref, const void *dist, int w, int h, int bpc,
+                                       int nframes, uint64_t *out_noise, uint64_t *out_moments,
+                                       uint64_t *out_cpu_noise, uint64_t *out_cpu_moments,
+                                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * float_psnr's conclusion from a frame's exact noise (host only).
  *   mse     = ((double)noise / s^2) / (w*h)    -- the 8-bit-scale mean
  *             squared error; (double) rounds once, to nearest even, and only

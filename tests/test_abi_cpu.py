@@ -135,6 +135,22 @@ def test_argument_errors_leave_outputs_untouched(L, name, kw, status, form):
     assert b.untouched()
 
 
+def test_cpu_order_arguments(L):
+    b = _Buffers()
+    ws = np.zeros(8192, dtype=np.uint8)
+    base = (ws.ctypes.data + 255) // 256 * 256
+    need = vqx.plane_stats_cpu_order_workspace_bytes(16, 4, 8, 2)
+    assert need >= vqx.plane_stats_workspace_bytes(16, 4, 8, 2)
+    f = L.vqx_plane_stats_batch_cpu_order_ws
+    assert f(b.ref, b.dist, 16, 4, 8, 2, b.noise, b.moments, None, b.moments, base, need, None) == vqx.E_NULL
+    assert f(b.ref, b.dist, 16, 4, 8, 2, b.noise, b.moments, b.noise, b.moments + 4, base, need, None) == vqx.E_ALIGN
+    assert f(b.ref, b.dist, 16, 4, 8, 2, b.noise, b.moments, b.noise, b.moments, base, need - 1, None) == vqx.E_WORKSPACE
+    assert f(b.ref, b.dist, 0, 4, 8, 2, b.noise, b.moments, b.noise, b.moments, base, need, None) == vqx.E_DIMS
+    assert b.untouched()
+    with pytest.raises(vqx.VqxError):
+        vqx.plane_stats_cpu_order_workspace_bytes(4, 4, 20, 1)
+
+
 def test_workspace_errors(L):
     b = _Buffers()
     ws = np.zeros(4096, dtype=np.uint8)

@@ -1,0 +1,133 @@
+"""The CPU's running double sums, reproduced on the device (marked gpu).
+
+``vqx_plane_stats_batch_cpu_order_ws`` returns, besides the exact sums, the
+value each of the CPU extractor's double accumulators holds after its last
+add.  The oracle's sequential C loop (``oracle.seq_batch_sums``) is that
+accumulator itself, so the check is plain bitwise equality on every frame
+and output -- past 2^53 too, where the exact sums only meet the bound.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from exact_reductions_amd import vqx  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    vqx.lib()
+
+
+UNIT_POWER = (2, 1, 1, 2, 2)
+
+
+def run(ref, dist, bpc):
+    r = torch.from_numpy(np.ascontiguousarray(ref)).to("cuda:0")
+    d = torch.from_numpy(np.ascontiguousarray(dist)).to("cuda:0")
+    n, m, cn, cm = vqx.plane_stats_batch_cpu_order(r, d, bpc)
+    torch.cuda.synchronize()
+    return n.cpu().numpy(), m.cpu().numpy(), cn.cpu().numpy(), cm.cpu().numpy()
+
+
+def check(ref, dist, bpc, expect_past53=None):
+    """Exact sums equal the exact oracle; CPU-order sums equal the CPU's
+    sequential doubles bit for bit; their conclusions equal the CPU's."""
+    h, w = ref.shape[1:]
+    n, m, cn, cm = run(ref, dist, bpc)
+    o1 = oracle.seq_batch_sums(ref, dist, bpc)
+    o2 = oracle.exact_batch_sums(ref, dist)
+    s = 1 << (bpc - 8)
+    past = 0
+    for f in range(ref.shape[0]):
+        exact = [int(n[f])] + [int(v) for v in m[f]]
+        cpu = [int(cn[f])] + [int(v) for v in cm[f]]
+        assert exact == [int(v) for v in o2[f]], f"frame {f}: exact sums"
+        for k in range(5):
+            want = float(o1[f][k]) * float(s ** UNIT_POWER[k])
+            assert float(cpu[k]) == want and cpu[k] == int(want), (
+                f"frame {f} output {k}: device {cpu[k]} CPU {int(want)} exact {exact[k]}")
+            if exact[k] >= oracle.TWO53:
+                past += 1
+        concl = vqx.conclude_batch([cpu[0]], [cpu[1:]], w, h, bpc)[0]
+        want_concl = oracle.conclude_from_doubles(o1[f], w, h)
+        assert [concl[0]] + list(concl[2:]) == list(want_concl), f"frame {f}: conclusion"
+    if expect_past53 is not None:
+        assert (past > 0) == expect_past53
+    return past
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_workloads(n):
+    wl = synth.WORKLOADS[n]
+    ref, dist = synth.generate(n, nframes=min(wl.nframes, 8))
+    check(ref, dist, wl.bpc, expect_past53=(n == 5))
+
+
+def test_past53_mixed_bit_identical():
+    """The 2560x1440 frame with a tenth of its samples below 4096: the CPU's
+    adds round, and the device returns the CPU's rounded value exactly."""
+    ref, dist = synth.past53_mixed(nframes=2)
+    assert check(ref, dist, 16, expect_past53=True) == 4
+
+
+def test_past53_full_range_bit_identical():
+    ref, dist = synth.past53_fullrange(nframes=2)
+    check(ref, dist, 16, expect_past53=True)
+
+
+def test_container_values_above_bpc():
+    """A 10-bit container holding full-range values passes 2^53 too."""
+    ref, dist = synth.uniform_planes(3840, 2160, 1, 10, seed=11, container_max=True)
+    check(ref, dist, 10, expect_past53=True)
+
+
+@pytest.mark.parametrize("bpc", [13, 14, 15])
+def test_depths_13_to_15(bpc):
+    ref, dist = synth.uniform_planes(3840, 2160, 1, bpc, seed=bpc, container_max=True)
+    check(ref, dist, bpc, expect_past53=True)
+
+
+def test_unaligned_frame_starts_past53():
+    """Odd frame sizes: frames 1 and 2 start inside a 16-byte vector, so the
+    head and tail samples of each frame are walked separately, first and
+    last, in the CPU's order."""
+    ref, dist = synth.uniform_planes(4097, 2049, 3, 16, seed=4097, container_max=True)
+    check(ref, dist, 16, expect_past53=True)
+
+
+def test_largest_frame_past53():
+    """2^25 samples at full range: the sums reach binade 55."""
+    ref, dist = synth.uniform_planes(8192, 4096, 1, 16, seed=25, container_max=True)
+    check(ref, dist, 16, expect_past53=True)
+
+
+def test_constant_worst_case():
+    """65535 against 0 everywhere: every noise term is 4294836224 and the
+    noise passes 2^54; all rounding steps meet the same term."""
+    ref, dist = synth.constant_pair(3840, 2160, 1, 16, 65535, 0)
+    check(ref, dist, 16, expect_past53=True)
+
+
+def test_ties_past53():
+    """Terms that are odd multiples of half an ulp: with u = 2 (binade 53)
+    every odd term is a tie, decided by the sum's parity."""
+    rng = np.random.Generator(np.random.PCG64(53))
+    ref = rng.integers(46341, 65535, size=(1, 2160, 3840), endpoint=True).astype(np.uint16)
+    ref[:, ::2] = rng.integers(1, 4095, size=(1, 1080, 3840)).astype(np.uint16) | 1
+    dist = np.zeros_like(ref)
+    check(ref, dist, 16)
+
+
+def test_small_frames_equal_exact():
+    ref, dist = synth.uniform_planes(18, 22, 50, 16, seed=3, container_max=True)
+    check(ref, dist, 16, expect_past53=False)
