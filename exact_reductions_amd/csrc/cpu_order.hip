@@ -17,28 +17,39 @@
 // Alternatives; HVS, Alternatives).  This file computes it.
 //
 // In integer units (the terms are integers below 2^32, the sum an integer
-// below 2^58) one CPU step is S <- RN53(S + t): the exact sum rounded to 53
+// below 2^57) one CPU step is S <- RN53(S + t): the exact sum rounded to 53
 // significant bits, ties to even.  While S stays inside one binade
-// [2^e, 2^(e+1)) with e >= 53, S = m * u with u = 2^(e-52), and adding t =
-// q*u + r moves m to m + q + d, where d depends only on r against u/2 and,
-// on a tie, on the parity of m + q.  So a run of terms acts on S, inside a
-// binade, as a two-state machine: from the parity of m it gives the total
-// increase of m and the parity after the run.  Such maps compose in order.
+// [2^e, 2^(e+1)) with e >= 53, S = m * u with u = 2^k, k = e - 52.  Write
+// t + u/2 = h * u + rr.  Then adding t moves m to m + h, except on a tie
+// (rr = 0, i.e. t's remainder is exactly u/2), where it moves to m + h - 1
+// if m + h is odd and to m + h if it is even; after a tie m is always even.
+// So a run of terms acts on S, inside a binade, as a two-state machine on
+// the parity of m: the increase of m is the run's sum of h less the ties
+// rounded down, both of which, and the parity after the run, depend only
+// on the parity before it.  Such maps compose in order.
 //
 //  1. stage 1 + stage 2 (plane_stats.hip) give each chunk's exact totals;
 //  2. cpu_order_prefix scans them per frame (the exact running sum at each
-//     chunk start, which predicts the binade the CPU's sum is in there);
-//  3. cpu_order_maps computes, for every chunk past 2^53, the chunk's map
-//     in the predicted binade (lanes map contiguous runs; the runs' maps
-//     are composed in order);
-//  4. cpu_order_walk, one wave per frame and sum, walks the chunks in order
-//     with the exact running value S: a chunk that stays below 2^53 adds
-//     exactly; a chunk whose map is for S's binade and keeps S inside it is
-//     applied; any other chunk (the one crossing 2^53 or a binade edge, or a
-//     wrong prediction) is walked in 64 sub-runs with maps for S's binade
-//     and the next, and a sub-run that still does not fit is walked term by
-//     term.  Every step is checked against S itself, so a prediction only
-//     decides how fast the walk is, never what it returns.
+//     chunk start, which predicts the binade the CPU's sum is in there) and
+//     writes every sum the CPU gets exactly (all of them below 2^53);
+//  3. cpu_order_maps computes, for every chunk past 2^53, maps in the
+//     predicted binade (and the next one where the chunk may cross into
+//     it): each lane chains the terms of four consecutive vectors, a wave's
+//     lanes are composed in order into the map of a slab of 256 vectors,
+//     and the chunk's eight slabs into the chunk's map;
+//  4. cpu_order_walk, one wave per frame and sum past 2^53, walks the frame
+//     in order with the running value S, 64 chunks at a time: a block that
+//     stays below 2^53 adds exactly; a block whose chunk maps are all for
+//     S's binade is composed into one map and applied if S stays in the
+//     binade; otherwise chunk by chunk, then slab by slab, then 64 vectors
+//     at a time with maps made on the spot for S's binade and the next, and
+//     only within a single vector term by term.  Every step is checked
+//     against S itself, so a prediction only decides how fast the walk is,
+//     never what it returns.
+//
+// One-byte samples (8 bits per component) never get there: their squares
+// are below 2^16 and a frame has at most 2^25 samples, so every sum stays
+// below 2^41 and step 2 already gives the CPU's values.
 
 #include "plane_stats.h"
 #include "terms.h"
@@ -50,6 +61,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr uint64_t kTwo53 = 1ull << 53;
+constexpr int kTerms = 8;  // terms of one 16-byte vector of two-byte samples
 
 // record field of square sum kk (noise, ref^2, dist^2)
 __device__ __forceinline__ int record_field(int kk) { return kk == kSqNoise ? kNoise : kk == kSqRef ? kRef2 : kDist2; }
@@ -73,149 +85,258 @@ __device__ __forceinline__ uint64_t cpu_add(uint64_t S, uint32_t t)
     return q << k;
 }
 
-// The two-state map of a run of adds inside binade e (k = e - 52 >= 1):
-// starting from parity x of m, the run adds dm[x] to m and leaves parity p[x].
+// ------------------------------------------------------------- wave helpers
+// lane i receives lane i + s of its row of 16 (row_shl:s); a lane whose
+// source lies outside the row receives 0
+template <int S>
+__device__ __forceinline__ uint32_t from_next(uint32_t v)
+{
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x100 + S, 0xf, 0xf, false));
+}
+
+template <int S>
+__device__ __forceinline__ uint64_t from_next64(uint64_t v)
+{
+    return static_cast<uint64_t>(from_next<S>(static_cast<uint32_t>(v))) |
+           (static_cast<uint64_t>(from_next<S>(static_cast<uint32_t>(v >> 32))) << 32);
+}
+
+// lane l's value (l wave-uniform): the result is wave-uniform
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, int l)
+{
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
+}
+
+__device__ __forceinline__ uint64_t lane_value64(uint64_t v, int l)
+{
+    return static_cast<uint64_t>(lane_value(static_cast<uint32_t>(v), l)) |
+           (static_cast<uint64_t>(lane_value(static_cast<uint32_t>(v >> 32), l)) << 32);
+}
+
+__device__ __forceinline__ uint32_t wave_total32(uint32_t v)
+{
+    v += from_next<1>(v);
+    v += from_next<2>(v);
+    v += from_next<4>(v);
+    v += from_next<8>(v);
+    return lane_value(v, 0) + lane_value(v, 16) + lane_value(v, 32) + lane_value(v, 48);
+}
+
+__device__ __forceinline__ uint64_t wave_total64(uint64_t v)
+{
+    v += from_next64<1>(v);
+    v += from_next64<2>(v);
+    v += from_next64<4>(v);
+    v += from_next64<8>(v);
+    return lane_value64(v, 0) + lane_value64(v, 16) + lane_value64(v, 32) + lane_value64(v, 48);
+}
+
+// ---------------------------------------------------------- run maps (u32)
+// The map of a run of terms inside binade 2^(k+52), for both parities s of
+// m before the run: C holds, per s, the number of ties rounded down (low 16
+// bits s = 0, high 16 bits s = 1), P the parity of m after the run (bit 0
+// s = 0, bit 16 s = 1).  The run's sum of h is kept apart: it is the same
+// for both parities, and is recovered from the run's exact total and the
+// sum of its rr.  Counts stay below 2^16 for runs of at most 8192 terms.
+struct RunMap {
+    uint32_t C = 0;
+    uint32_t P = 0x10000u;
+};
+
+// Appends term t (below 2^32 - 2^17, so t + 2^(k-1) does not wrap).
+__device__ __forceinline__ void run_add(RunMap &m, uint32_t &rr_sum, uint32_t t, int k)
+{
+    const uint32_t t2 = t + (1u << (k - 1));
+    const uint32_t rr = t2 & ((1u << k) - 1);
+    rr_sum += rr;
+    const uint32_t x = m.P ^ (((t2 >> k) & 1u) * 0x10001u);  // parity of m + h, per s
+    const bool tie = rr == 0;
+    m.C += tie ? x : 0u;  // a tie rounds down from m + h exactly when m + h is odd
+    m.P = tie ? 0u : x;
+}
+
+__device__ __forceinline__ uint32_t swap_halves(uint32_t x) { return __builtin_amdgcn_alignbit(x, x, 16); }
+
+// a then b
+__device__ __forceinline__ RunMap run_then(const RunMap &a, const RunMap &b)
+{
+    // per half: where b is entered from the other parity than the half's own
+    const uint32_t other = (a.P * 0xffffu) ^ 0xffff0000u;
+    RunMap c;
+    c.C = a.C + ((swap_halves(b.C) & other) | (b.C & ~other));
+    c.P = (swap_halves(b.P) & other) | (b.P & ~other);
+    return c;
+}
+
+template <int S>
+__device__ __forceinline__ RunMap run_from_next(const RunMap &m)
+{
+    RunMap o;
+    o.C = from_next<S>(m.C);
+    o.P = from_next<S>(m.P);
+    return o;
+}
+
+// The wave's lane maps composed in lane order (lane 0's first); uniform.
+__device__ __forceinline__ RunMap wave_run(RunMap m)
+{
+    m = run_then(m, run_from_next<1>(m));
+    m = run_then(m, run_from_next<2>(m));
+    m = run_then(m, run_from_next<4>(m));
+    m = run_then(m, run_from_next<8>(m));
+    RunMap w;
+    w.C = lane_value(m.C, 0);
+    w.P = lane_value(m.P, 0);
+#pragma unroll
+    for (int row = 1; row < 4; ++row) {
+        RunMap r;
+        r.C = lane_value(m.C, 16 * row);
+        r.P = lane_value(m.P, 16 * row);
+        w = run_then(w, r);
+    }
+    return w;
+}
+
+// ---------------------------------------------------------- maps (64-bit)
+// The same two-state map with its increases of m written out: from parity
+// s, m grows by dm_s and ends with parity p_s.
 struct Map2 {
     uint64_t dm0 = 0, dm1 = 0;
     uint32_t p0 = 0, p1 = 1;
 };
 
-__device__ __forceinline__ void map_add(Map2 &m, uint32_t t, int k)
+// A run of n terms with exact total `total` and sum of rr `rr_sum` in
+// binade 2^(k+52): its sum of h is (total + n * 2^(k-1) - rr_sum) / 2^k.
+__device__ __forceinline__ Map2 run_map(const RunMap &m, uint64_t total, uint64_t n, uint64_t rr_sum, int k)
 {
-    const uint32_t q = t >> k;
-    const uint32_t r = t & ((1u << k) - 1);
-    const uint32_t half = 1u << (k - 1);
-    const uint32_t up = r > half ? 1u : 0u;
-    const uint32_t tie = r == half ? 1u : 0u;
-    // on a tie, round up exactly when m + q is odd
-    const uint32_t d0 = up | (tie & ((m.p0 + q) & 1u));
-    const uint32_t d1 = up | (tie & ((m.p1 + q) & 1u));
-    m.dm0 += q + d0;
-    m.dm1 += q + d1;
-    m.p0 = (m.p0 + q + d0) & 1u;
-    m.p1 = (m.p1 + q + d1) & 1u;
+    const uint64_t h = (total + (n << (k - 1)) - rr_sum) >> k;
+    Map2 r;
+    r.dm0 = h - (m.C & 0xffffu);
+    r.dm1 = h - (m.C >> 16);
+    r.p0 = m.P & 1u;
+    r.p1 = m.P >> 16;
+    return r;
+}
+
+// x if bit 0 of s is clear, y if it is set.  (Written with a mask: a plain
+// ?: between two fields of one struct can become an indexed load from a
+// stack copy of it.)
+__device__ __forceinline__ uint64_t pick(uint64_t s, uint64_t x, uint64_t y)
+{
+    const uint64_t mask = 0 - (s & 1u);
+    return (x & ~mask) | (y & mask);
 }
 
 // a then b
 __device__ __forceinline__ Map2 map_then(const Map2 &a, const Map2 &b)
 {
     Map2 c;
-    c.dm0 = a.dm0 + (a.p0 ? b.dm1 : b.dm0);
-    c.p0 = a.p0 ? b.p1 : b.p0;
-    c.dm1 = a.dm1 + (a.p1 ? b.dm1 : b.dm0);
-    c.p1 = a.p1 ? b.p1 : b.p0;
+    c.dm0 = a.dm0 + pick(a.p0, b.dm0, b.dm1);
+    c.p0 = static_cast<uint32_t>(pick(a.p0, b.p0, b.p1));
+    c.dm1 = a.dm1 + pick(a.p1, b.dm0, b.dm1);
+    c.p1 = static_cast<uint32_t>(pick(a.p1, b.p0, b.p1));
     return c;
 }
 
+template <int S>
+__device__ __forceinline__ Map2 map_from_next(const Map2 &m)
+{
+    Map2 o;
+    o.dm0 = from_next64<S>(m.dm0);
+    o.dm1 = from_next64<S>(m.dm1);
+    o.p0 = from_next<S>(m.p0);
+    o.p1 = from_next<S>(m.p1);
+    return o;
+}
+
+__device__ __forceinline__ Map2 map_lane(const Map2 &m, int l)
+{
+    Map2 o;
+    o.dm0 = lane_value64(m.dm0, l);
+    o.dm1 = lane_value64(m.dm1, l);
+    o.p0 = lane_value(m.p0, l);
+    o.p1 = lane_value(m.p1, l);
+    return o;
+}
+
+// The wave's maps composed in lane order; uniform.
+__device__ __forceinline__ Map2 wave_map(Map2 m)
+{
+    m = map_then(m, map_from_next<1>(m));
+    m = map_then(m, map_from_next<2>(m));
+    m = map_then(m, map_from_next<4>(m));
+    m = map_then(m, map_from_next<8>(m));
+    Map2 w = map_lane(m, 0);
+#pragma unroll
+    for (int row = 1; row < 4; ++row)
+        w = map_then(w, map_lane(m, 16 * row));
+    return w;
+}
+
 // Applies map `m` (made for binade e) to S if S is in binade e and stays
-// there; returns false otherwise (S unchanged).
+// there; returns false otherwise (S unchanged).  m only grows, so if it
+// ends inside the binade every step of the run stayed inside it.
 __device__ __forceinline__ bool map_apply(uint64_t &S, const Map2 &m, int e)
 {
     if (S < kTwo53 || binade(S) != e)
         return false;
     const int k = e - 52;
     const uint64_t mm = S >> k;
-    const uint64_t m2 = mm + ((mm & 1) ? m.dm1 : m.dm0);
-    if (m2 >= kTwo53)  // would leave the binade: the map does not hold
+    const uint64_t m2 = mm + pick(mm, m.dm0, m.dm1);
+    if (m2 >= kTwo53)
         return false;
     S = m2 << k;
     return true;
 }
 
-template <int kBytes>
-__device__ __forceinline__ uint32_t sample(const void *plane, int64_t i)
+// Stored maps: {dm0, dm1, flags}; flags bit 0 valid, bits 8..15 the
+// binade, bit 16 p0, bit 17 p1.
+__device__ __forceinline__ uint64_t map_flags(const Map2 &m, int e)
 {
-    if constexpr (kBytes == 1)
-        return static_cast<const uint8_t *>(plane)[i];
-    else
-        return static_cast<const uint16_t *>(plane)[i];
+    return 1u | (static_cast<uint64_t>(e) << 8) | (static_cast<uint64_t>(m.p0 & 1u) << 16) |
+           (static_cast<uint64_t>(m.p1 & 1u) << 17);
 }
 
-// The samples of one 32-bit word of a 16-byte vector, lowest first.
-template <int kBytes>
-__device__ __forceinline__ uint32_t word_sample(uint32_t w, int j)
+__device__ __forceinline__ Map2 map_from(uint64_t dm0, uint64_t dm1, uint64_t flags)
 {
-    if constexpr (kBytes == 1)
-        return (w >> (8 * j)) & 0xffu;
-    else
-        return (w >> (16 * j)) & 0xffffu;
+    Map2 m;
+    m.dm0 = dm0;
+    m.dm1 = dm1;
+    m.p0 = static_cast<uint32_t>((flags >> 16) & 1u);
+    m.p1 = static_cast<uint32_t>((flags >> 17) & 1u);
+    return m;
 }
 
-// Adds the terms of vectors [v0, v1) of the batch, in order, to the maps of
-// the square sums selected by `want` (one map per sum, binade e[kk]).
-template <int kBytes>
-__device__ __forceinline__ void map_vectors(Map2 (&m)[kSquares], const bool (&want)[kSquares],
-                                            const int (&k)[kSquares], const u32x4 *R,
-                                            const u32x4 *D, int64_t v0, int64_t v1)
+__device__ __forceinline__ int flags_binade(uint64_t flags) { return static_cast<int>((flags >> 8) & 0xffu); }
+
+// ------------------------------------------------------------------ terms
+// Term i (raster order) of square sum KK in one 16-byte vector of each plane.
+template <int KK>
+__device__ __forceinline__ uint32_t vector_term(const u32x4 &a, const u32x4 &b, int i)
 {
-    constexpr int per_word = 4 / kBytes;
-    const bool needR = want[kSqNoise] || want[kSqRef];
-    const bool needD = want[kSqNoise] || want[kSqDist];
-    for (int64_t v = v0; v < v1; ++v) {
-        const u32x4 a = needR ? __builtin_nontemporal_load(R + v) : u32x4{0, 0, 0, 0};
-        const u32x4 b = needD ? __builtin_nontemporal_load(D + v) : u32x4{0, 0, 0, 0};
-        const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
-        const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-#pragma unroll
-            for (int j = 0; j < per_word; ++j) {
-                const uint32_t r = word_sample<kBytes>(aw[wd], j);
-                const uint32_t d = word_sample<kBytes>(bw[wd], j);
-#pragma unroll
-                for (int kk = 0; kk < kSquares; ++kk)
-                    if (want[kk])
-                        map_add(m[kk], square_term<kBytes>(kk, r, d), k[kk]);
-            }
-        }
-    }
+    const uint32_t wa = a[i >> 1], wb = b[i >> 1];
+    const uint32_t r = (i & 1) ? wa >> 16 : wa & 0xffffu;
+    const uint32_t d = (i & 1) ? wb >> 16 : wb & 0xffffu;
+    return square_term<2>(KK, r, d);
 }
 
-// One pass over vectors [v0, v1) for square sum kk: the exact total of its
-// terms and their maps in binades eA and eA + 1.
-template <int kBytes>
-__device__ __forceinline__ void run_maps(int kk, int eA, const u32x4 *R, const u32x4 *D, int64_t v0,
-                                         int64_t v1, uint64_t &total, Map2 &mA, Map2 &mB)
+template <int KK>
+__device__ __forceinline__ void load_vector(const u32x4 *R, const u32x4 *D, int64_t v, bool ok, u32x4 &a, u32x4 &b)
 {
-    constexpr int per_word = 4 / kBytes;
-    const int kA = eA - 52, kB = eA - 51;
-    uint64_t s = 0;
-    for (int64_t v = v0; v < v1; ++v) {
-        const u32x4 a = __builtin_nontemporal_load(R + v);
-        const u32x4 b = __builtin_nontemporal_load(D + v);
-        const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
-        const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-#pragma unroll
-            for (int j = 0; j < per_word; ++j) {
-                const uint32_t t = square_term<kBytes>(kk, word_sample<kBytes>(aw[wd], j),
-                                                       word_sample<kBytes>(bw[wd], j));
-                s += t;
-                map_add(mA, t, kA);
-                map_add(mB, t, kB);
-            }
-        }
-    }
-    total = s;
-}
-
-__device__ __forceinline__ uint64_t wave_sum64(uint64_t v)
-{
-#pragma unroll
-    for (int m = 32; m > 0; m >>= 1)
-        v += __shfl_xor(v, m, 64);
-    return v;
+    const u32x4 zero = {0, 0, 0, 0};
+    a = (ok && KK != kSqDist) ? __builtin_nontemporal_load(R + v) : zero;
+    b = (ok && KK != kSqRef) ? __builtin_nontemporal_load(D + v) : zero;
 }
 
 // ------------------------------------------------------------ 2. prefix scan
 // One workgroup per frame.  prefix[(f*chunks + c)*3 + kk] = exact sum of
 // square kk over chunks 0..c-1 (chunk 0's record also holds the frame's few
 // samples outside whole vectors); totals[f*3 + kk] = the frame's exact sum.
-// The first moments never reach 2^53 (below 2^25 * 2^16 = 2^41): the CPU's
-// values are the exact sums, written here.
+// The CPU's values of the sums that stay below 2^53 are the exact sums,
+// written here; the first moments always do (below 2^25 * 2^16 = 2^41).
 __global__ __launch_bounds__(kThreads) void cpu_order_prefix(const uint64_t *rec, int chunks,
                                                              uint64_t *prefix, uint64_t *totals,
+                                                             uint64_t *out_cpu_noise,
                                                              uint64_t *out_cpu_moments)
 {
     __shared__ uint64_t lds[kThreads];
@@ -245,29 +366,118 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(const uint64_t *rec
                 prefix[(f * chunks + c) * kSquares + kk] = run;
                 run += rec[(f * chunks + c) * kRecordStride + field];
             }
-            if (t == 0)
+        }
+        if (t == 0) {
+            if (kk < kSquares)
                 totals[f * kSquares + kk] = total;
-        } else if (t == 0) {
-            out_cpu_moments[4 * f + (kk - kSquares)] = total;
+            uint64_t *dst = kk == kSqNoise  ? &out_cpu_noise[f]
+                          : kk < kSquares   ? &out_cpu_moments[4 * f + 1 + kk]
+                                            : &out_cpu_moments[4 * f + (kk - kSquares)];
+            if (total < kTwo53)  // otherwise the walk writes it
+                *dst = total;
         }
         __syncthreads();
     }
 }
 
 // ------------------------------------------------------------ 3. chunk maps
-// Map entry of chunk wg, square kk: {dm0, dm1, flags}; flags bit 0 = valid,
-// bits 8..15 = binade e, bit 16 = p0, bit 17 = p1.  Written for every chunk
-// on every call (invalid where not computed), so nothing stale is read.
-constexpr int kMapStride = 4;  // uint64 per entry
+// Entry of chunk wg, square kk (kEntry uint64): the chunk's map {dm0, dm1,
+// flags}, the maps of its kSlabs slabs in the predicted binade e, their
+// maps in binade e + 1 (made only where the chunk's exact range reaches
+// 2^(e+1), i.e. where the CPU's sum probably changes binade inside it), and
+// the slabs' exact totals.  Every entry's flags are written on every call
+// (invalid where no map was made).
+constexpr int kSlabVectors = 256;
+constexpr int kSlabs = kChunkVectors / kSlabVectors;
+constexpr int kLaneVectors = kSlabVectors / 64;  // consecutive vectors one lane chains
+constexpr int kSlabMapsA = 3;
+constexpr int kSlabMapsB = 3 + 3 * kSlabs;
+constexpr int kSlabTotals = 3 + 6 * kSlabs;
+constexpr int kEntry = kSlabTotals + kSlabs;
+static_assert(kSlabs == 2 * (kThreads / 64), "two slabs per wave");
 
-template <int kBytes>
-__global__ __launch_bounds__(kThreads) void cpu_order_maps(const void *ref, const void *dist,
-                                                           int64_t pixels, int chunks,
-                                                           const uint64_t *rec,
-                                                           const uint64_t *prefix,
-                                                           const uint64_t *totals, uint64_t *maps)
+// A chunk's slab maps in LDS, for the chunk map.
+struct SlabMaps {
+    uint64_t dm0[kSlabs], dm1[kSlabs];
+    uint32_t p[kSlabs];
+};
+
+template <int KK>
+__device__ __forceinline__ void chunk_maps(const u32x4 *R, const u32x4 *D, int64_t cb, int64_t ce, int e,
+                                           bool dual, uint64_t *entry, SlabMaps &s_slab)
 {
-    constexpr int V = 16 / kBytes;
+    const int wave = threadIdx.x / 64, lane = threadIdx.x & 63;
+    const int k = e - 52;
+    u32x4 a[2][kLaneVectors], b[2][kLaneVectors];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int j = 0; j < kLaneVectors; ++j) {
+            const int64_t v = cb + static_cast<int64_t>(2 * wave + s) * kSlabVectors + kLaneVectors * lane + j;
+            load_vector<KK>(R, D, v, v < ce, a[s][j], b[s][j]);
+        }
+    // Vectors past the chunk's end read as zero terms, which change
+    // neither a map nor a total: each slab is a full 256 * 8 terms.
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        RunMap mA, mB;
+        uint32_t rA = 0, rB = 0;
+        uint64_t tot = 0;
+#pragma unroll
+        for (int j = 0; j < kLaneVectors; ++j)
+#pragma unroll
+            for (int i = 0; i < kTerms; ++i) {
+                const uint32_t t = vector_term<KK>(a[s][j], b[s][j], i);
+                tot += t;
+                run_add(mA, rA, t, k);
+                if (dual)
+                    run_add(mB, rB, t, k + 1);
+            }
+        constexpr uint64_t n = static_cast<uint64_t>(kSlabVectors) * kTerms;
+        const uint64_t T = wave_total64(tot);
+        const Map2 slab = run_map(wave_run(mA), T, n, wave_total32(rA), k);
+        Map2 slab_b;
+        if (dual)
+            slab_b = run_map(wave_run(mB), T, n, wave_total32(rB), k + 1);
+        const int si = 2 * wave + s;
+        if (lane == 0) {
+            entry[kSlabMapsA + 3 * si + 0] = slab.dm0;
+            entry[kSlabMapsA + 3 * si + 1] = slab.dm1;
+            entry[kSlabMapsA + 3 * si + 2] = map_flags(slab, e);
+            entry[kSlabMapsB + 3 * si + 0] = slab_b.dm0;
+            entry[kSlabMapsB + 3 * si + 1] = slab_b.dm1;
+            entry[kSlabMapsB + 3 * si + 2] = dual ? map_flags(slab_b, e + 1) : 0;
+            entry[kSlabTotals + si] = T;
+            s_slab.dm0[si] = slab.dm0;
+            s_slab.dm1[si] = slab.dm1;
+            s_slab.p[si] = slab.p0 | (slab.p1 << 1);
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        Map2 chunk;
+        for (int si = 0; si < kSlabs; ++si) {
+            Map2 x;
+            x.dm0 = s_slab.dm0[si];
+            x.dm1 = s_slab.dm1[si];
+            x.p0 = s_slab.p[si] & 1u;
+            x.p1 = s_slab.p[si] >> 1;
+            chunk = map_then(chunk, x);
+        }
+        entry[0] = chunk.dm0;
+        entry[1] = chunk.dm1;
+        entry[2] = map_flags(chunk, e);
+    }
+}
+
+// One workgroup per (frame, chunk); two-byte samples only.
+__global__ __launch_bounds__(kThreads) void cpu_order_maps(const void *ref, const void *dist, int64_t pixels,
+                                                           int chunks, const uint64_t *rec,
+                                                           const uint64_t *prefix, const uint64_t *totals,
+                                                           uint64_t *maps)
+{
+    constexpr int V = 8;
+    __shared__ SlabMaps s_slab[kSquares];
     const int64_t wg = blockIdx.x;
     const int64_t frame = wg / chunks;
     const int chunk = static_cast<int>(wg - frame * chunks);
@@ -275,206 +485,253 @@ __global__ __launch_bounds__(kThreads) void cpu_order_maps(const void *ref, cons
     const int64_t vb = (e0 + V - 1) / V, ve = e1 / V;
     const int64_t cb = vb + static_cast<int64_t>(chunk) * kChunkVectors;
     const int64_t ce = cb + kChunkVectors < ve ? cb + kChunkVectors : ve;
-
-    bool want[kSquares];
-    int k[kSquares];
-    bool any = false;
-#pragma unroll
+    const u32x4 *R = static_cast<const u32x4 *>(ref);
+    const u32x4 *D = static_cast<const u32x4 *>(dist);
     for (int kk = 0; kk < kSquares; ++kk) {
+        uint64_t *entry = maps + (wg * kSquares + kk) * kEntry;
         const uint64_t p = prefix[wg * kSquares + kk];
         const uint64_t r = rec[wg * kRecordStride + record_field(kk)];
-        want[kk] = vb < ve && totals[frame * kSquares + kk] >= kTwo53 && p + r >= kTwo53;
-        const int e = binade(p > kTwo53 ? p : kTwo53);
-        k[kk] = e - 52;
-        any = any || want[kk];
-    }
-    __shared__ uint64_t s_dm0[kSquares][kThreads], s_dm1[kSquares][kThreads];
-    __shared__ uint32_t s_p[kSquares][kThreads];
-    const int t = threadIdx.x;
-    if (any) {
-        Map2 m[kSquares];
-        const int64_t v0 = cb + static_cast<int64_t>(t) * (kChunkVectors / kThreads);
-        int64_t v1 = v0 + kChunkVectors / kThreads;
-        v1 = v1 < ce ? v1 : ce;
-        map_vectors<kBytes>(m, want, k, static_cast<const u32x4 *>(ref), static_cast<const u32x4 *>(dist),
-                            v0, v0 < v1 ? v1 : v0);
-#pragma unroll
-        for (int kk = 0; kk < kSquares; ++kk) {
-            s_dm0[kk][t] = m[kk].dm0;
-            s_dm1[kk][t] = m[kk].dm1;
-            s_p[kk][t] = m[kk].p0 | (m[kk].p1 << 1);
-        }
-        // compose the 256 run maps in order (lane 0's run comes first)
-        for (int s = 1; s < kThreads; s <<= 1) {
-            __syncthreads();
-            if ((t & (2 * s - 1)) == 0) {
-#pragma unroll
-                for (int kk = 0; kk < kSquares; ++kk) {
-                    Map2 a, b;
-                    a.dm0 = s_dm0[kk][t]; a.dm1 = s_dm1[kk][t];
-                    a.p0 = s_p[kk][t] & 1u; a.p1 = s_p[kk][t] >> 1;
-                    b.dm0 = s_dm0[kk][t + s]; b.dm1 = s_dm1[kk][t + s];
-                    b.p0 = s_p[kk][t + s] & 1u; b.p1 = s_p[kk][t + s] >> 1;
-                    const Map2 c = map_then(a, b);
-                    s_dm0[kk][t] = c.dm0;
-                    s_dm1[kk][t] = c.dm1;
-                    s_p[kk][t] = c.p0 | (c.p1 << 1);
+        // uniform across the workgroup
+        if (!(cb < ce && totals[frame * kSquares + kk] >= kTwo53 && p + r >= kTwo53)) {
+            if (threadIdx.x == 0) {
+                entry[2] = 0;
+                for (int j = 0; j < kSlabs; ++j) {
+                    entry[kSlabMapsA + 3 * j + 2] = 0;
+                    entry[kSlabMapsB + 3 * j + 2] = 0;
                 }
             }
+            continue;
         }
-        __syncthreads();
-    }
-    if (t == 0) {
-#pragma unroll
-        for (int kk = 0; kk < kSquares; ++kk) {
-            uint64_t *e = maps + (wg * kSquares + kk) * kMapStride;
-            if (any && want[kk]) {
-                e[0] = s_dm0[kk][0];
-                e[1] = s_dm1[kk][0];
-                e[2] = 1u | (static_cast<uint64_t>(k[kk] + 52) << 8) |
-                       (static_cast<uint64_t>(s_p[kk][0] & 1u) << 16) |
-                       (static_cast<uint64_t>(s_p[kk][0] >> 1) << 17);
-            } else {
-                e[0] = 0;
-                e[1] = 0;
-                e[2] = 0;
-            }
+        const int e = binade(p > kTwo53 ? p : kTwo53);
+        const bool dual = e < 56 && p + r >= (1ull << (e + 1));
+        switch (kk) {
+        case kSqNoise: chunk_maps<kSqNoise>(R, D, cb, ce, e, dual, entry, s_slab[kk]); break;
+        case kSqRef: chunk_maps<kSqRef>(R, D, cb, ce, e, dual, entry, s_slab[kk]); break;
+        default: chunk_maps<kSqDist>(R, D, cb, ce, e, dual, entry, s_slab[kk]); break;
         }
     }
 }
 
 // ------------------------------------------------------------------ 4. walk
-// Walks sub-run by sub-run through vectors [cb, ce) of one chunk from the
-// exact running value S.  All 64 lanes hold the same S throughout.
-template <int kBytes>
-__device__ uint64_t walk_chunk(uint64_t S, int kk, const u32x4 *R, const u32x4 *D, int64_t cb,
-                               int64_t ce, const void *ref, const void *dist)
+// All 64 lanes of the walking wave hold the same S throughout.
+
+// Term by term through one vector.
+template <int KK>
+__device__ __forceinline__ uint64_t walk_vector(uint64_t S, const u32x4 *R, const u32x4 *D, int64_t v)
 {
-    constexpr int V = 16 / kBytes;
-    constexpr int kSub = kChunkVectors / 64;  // vectors per lane's sub-run
-    constexpr int kPer = kSub * V / 64;           // samples per lane in a sub-run walk
+    u32x4 a, b;
+    load_vector<KK>(R, D, v, true, a, b);
+#pragma unroll
+    for (int i = 0; i < kTerms; ++i)
+        S = cpu_add(S, vector_term<KK>(a, b, i));
+    return S;
+}
+
+// Vectors [sb, se) (at most 256): maps made here, for S's binade and the
+// next, 64 vectors (one per lane) at a time.
+template <int KK>
+__device__ __forceinline__ uint64_t walk_slab(uint64_t S, const u32x4 *R, const u32x4 *D, int64_t sb, int64_t se)
+{
     const int lane = threadIdx.x;
     const int eA = S >= kTwo53 ? binade(S) : 53;
-    Map2 mA, mB;
-    uint64_t tot = 0;
-    const int64_t v0 = cb + static_cast<int64_t>(lane) * kSub;
-    int64_t v1 = v0 + kSub;
-    v1 = v1 < ce ? v1 : ce;
-    run_maps<kBytes>(kk, eA, R, D, v0, v0 < v1 ? v1 : v0, tot, mA, mB);
-    for (int j = 0; j < 64; ++j) {
-        const uint64_t tj = __shfl(tot, j, 64);
-        if (S + tj < kTwo53) {
-            S += tj;
+    const int kA = eA - 52;
+    for (int64_t base = sb; base < se; base += 64) {
+        const int64_t v = base + lane;
+        u32x4 a, b;
+        load_vector<KK>(R, D, v, v < se, a, b);
+        RunMap mA, mB;
+        uint32_t rA = 0, rB = 0;
+        uint64_t tot = 0;
+#pragma unroll
+        for (int i = 0; i < kTerms; ++i) {
+            const uint32_t t = vector_term<KK>(a, b, i);
+            tot += t;
+            run_add(mA, rA, t, kA);
+            run_add(mB, rB, t, kA + 1);
+        }
+        const uint64_t block = wave_total64(tot);
+        if (S + block < kTwo53) {
+            S += block;
             continue;
         }
-        Map2 a, b;
-        a.dm0 = __shfl(mA.dm0, j, 64); a.dm1 = __shfl(mA.dm1, j, 64);
-        a.p0 = __shfl(mA.p0, j, 64); a.p1 = __shfl(mA.p1, j, 64);
-        if (map_apply(S, a, eA))
-            continue;
-        b.dm0 = __shfl(mB.dm0, j, 64); b.dm1 = __shfl(mB.dm1, j, 64);
-        b.p0 = __shfl(mB.p0, j, 64); b.p1 = __shfl(mB.p1, j, 64);
-        if (map_apply(S, b, eA + 1))
-            continue;
-        // term by term through sub-run j: lane i holds its kPer samples
-        const int64_t sv0 = cb + static_cast<int64_t>(j) * kSub;
-        const int64_t nsamp = ((sv0 + kSub < ce ? sv0 + kSub : ce) - sv0) * V;
-        uint32_t term[kPer];
-#pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-            const int64_t idx = static_cast<int64_t>(lane) * kPer + q;
-            term[q] = idx < nsamp ? square_term<kBytes>(kk, sample<kBytes>(ref, sv0 * V + idx),
-                                                        sample<kBytes>(dist, sv0 * V + idx))
-                                  : 0u;
-        }
-        for (int src = 0; src < 64; ++src) {
-#pragma unroll
-            for (int q = 0; q < kPer; ++q) {
-                const uint32_t tq = __shfl(term[q], src, 64);
-                if (static_cast<int64_t>(src) * kPer + q < nsamp)
-                    S = cpu_add(S, tq);
+        if (S >= kTwo53) {
+            const int e = binade(S);
+            if (e == eA || e == eA + 1) {
+                const bool inA = e == eA;
+                const Map2 comp = run_map(wave_run(inA ? mA : mB), block, 64 * kTerms,
+                                          wave_total32(inA ? rA : rB), e - 52);
+                if (map_apply(S, comp, e))
+                    continue;
             }
+        }
+        const int n = se - base < 64 ? static_cast<int>(se - base) : 64;
+        for (int j = 0; j < n; ++j) {
+            const uint64_t tj = lane_value64(tot, j);
+            if (S + tj < kTwo53) {
+                S += tj;
+                continue;
+            }
+            RunMap x;
+            x.C = lane_value(mA.C, j);
+            x.P = lane_value(mA.P, j);
+            if (map_apply(S, run_map(x, tj, kTerms, lane_value(rA, j), kA), eA))
+                continue;
+            x.C = lane_value(mB.C, j);
+            x.P = lane_value(mB.P, j);
+            if (map_apply(S, run_map(x, tj, kTerms, lane_value(rB, j), kA + 1), eA + 1))
+                continue;
+            S = walk_vector<KK>(S, R, D, base + j);
         }
     }
     return S;
 }
 
-// One wave per (frame, square sum).
-template <int kBytes>
-__global__ __launch_bounds__(64) void cpu_order_walk(const void *ref, const void *dist, int64_t pixels,
-                                                     int chunks, const uint64_t *rec,
-                                                     const uint64_t *totals, const uint64_t *maps,
-                                                     uint64_t *out_cpu_noise, uint64_t *out_cpu_moments)
+// One chunk, slab by slab with the slabs' stored maps.
+template <int KK>
+__device__ __forceinline__ uint64_t walk_chunk(uint64_t S, const u32x4 *R, const u32x4 *D, const uint64_t *entry, int64_t cb,
+                               int64_t ce)
 {
-    constexpr int V = 16 / kBytes;
-    const int64_t frame = blockIdx.x / kSquares;
-    const int kk = static_cast<int>(blockIdx.x - frame * kSquares);
     const int lane = threadIdx.x;
-    uint64_t *dst = kk == kSqNoise ? &out_cpu_noise[frame] : &out_cpu_moments[4 * frame + 1 + kk];
-    const uint64_t total = totals[frame * kSquares + kk];
-    if (total < kTwo53) {  // every add of the CPU is exact: its sum is the exact one
-        if (lane == 0)
-            *dst = total;
-        return;
+    uint64_t T = 0, dm0 = 0, dm1 = 0, flags = 0, bdm0 = 0, bdm1 = 0, bflags = 0;
+    if (lane < kSlabs) {
+        T = entry[kSlabTotals + lane];
+        dm0 = entry[kSlabMapsA + 3 * lane + 0];
+        dm1 = entry[kSlabMapsA + 3 * lane + 1];
+        flags = entry[kSlabMapsA + 3 * lane + 2];
+        bdm0 = entry[kSlabMapsB + 3 * lane + 0];
+        bdm1 = entry[kSlabMapsB + 3 * lane + 1];
+        bflags = entry[kSlabMapsB + 3 * lane + 2];
     }
+    for (int j = 0; j < kSlabs; ++j) {
+        const int64_t sb = cb + static_cast<int64_t>(j) * kSlabVectors;
+        if (sb >= ce)
+            break;
+        const int64_t se = sb + kSlabVectors < ce ? sb + kSlabVectors : ce;
+        const uint64_t fl = lane_value64(flags, j);
+        const uint64_t Tj = lane_value64(T, j);
+        if ((fl & 1u) && S + Tj < kTwo53) {  // totals are only stored with a map
+            S += Tj;
+            continue;
+        }
+        if ((fl & 1u) && map_apply(S, map_from(lane_value64(dm0, j), lane_value64(dm1, j), fl), flags_binade(fl)))
+            continue;
+        const uint64_t bfl = lane_value64(bflags, j);
+        if ((bfl & 1u) &&
+            map_apply(S, map_from(lane_value64(bdm0, j), lane_value64(bdm1, j), bfl), flags_binade(bfl)))
+            continue;
+        S = walk_slab<KK>(S, R, D, sb, se);
+    }
+    return S;
+}
+
+// The vectors' part of chunk c's record (chunk 0's also holds the head and
+// tail samples), and its stored map.
+struct ChunkView {
+    uint64_t T = 0, dm0 = 0, dm1 = 0, flags = 0;
+};
+
+__device__ __forceinline__ ChunkView load_chunk(const uint64_t *rec, const uint64_t *maps, int64_t frame, int chunks,
+                                                int c, int kk, uint64_t head_tail)
+{
+    ChunkView x;
+    if (c < chunks) {
+        const int64_t wg = frame * chunks + c;
+        const uint64_t *entry = maps + (wg * kSquares + kk) * kEntry;
+        x.T = rec[wg * kRecordStride + record_field(kk)] - (c == 0 ? head_tail : 0);
+        x.dm0 = entry[0];
+        x.dm1 = entry[1];
+        x.flags = entry[2];
+    }
+    return x;
+}
+
+template <int KK>
+__device__ __forceinline__ void walk_frame(const void *ref, const void *dist, int64_t pixels, int chunks, const uint64_t *rec,
+                           const uint64_t *maps, int64_t frame, uint64_t *dst)
+{
+    constexpr int V = 8;
+    const int lane = threadIdx.x;
     const int64_t e0 = frame * pixels, e1 = e0 + pixels;
     const int64_t vb = (e0 + V - 1) / V, ve = e1 / V;
     const int64_t head_end = vb < ve ? vb * V : e1;
     const int64_t tail_begin = vb < ve ? ve * V : e1;
     const int head = static_cast<int>(head_end - e0), tail = static_cast<int>(e1 - tail_begin);
-    const uint32_t hterm = lane < head ? square_term<kBytes>(kk, sample<kBytes>(ref, e0 + lane),
-                                                             sample<kBytes>(dist, e0 + lane))
-                                       : 0u;
-    const uint32_t tterm = lane < tail ? square_term<kBytes>(kk, sample<kBytes>(ref, tail_begin + lane),
-                                                             sample<kBytes>(dist, tail_begin + lane))
-                                       : 0u;
-    const uint64_t hsum = wave_sum64(hterm), tsum = wave_sum64(tterm);
+    const uint16_t *r16 = static_cast<const uint16_t *>(ref);
+    const uint16_t *d16 = static_cast<const uint16_t *>(dist);
+    const uint32_t hterm = lane < head ? square_term<2>(KK, r16[e0 + lane], d16[e0 + lane]) : 0u;
+    const uint32_t tterm = lane < tail ? square_term<2>(KK, r16[tail_begin + lane], d16[tail_begin + lane]) : 0u;
+    const uint64_t hsum = wave_total64(hterm), tsum = wave_total64(tterm);
     // the head comes first in raster order; it is far below 2^53, so exact
     uint64_t S = hsum;
     const u32x4 *R = static_cast<const u32x4 *>(ref);
     const u32x4 *D = static_cast<const u32x4 *>(dist);
-    const int field = record_field(kk);
+    ChunkView cur = load_chunk(rec, maps, frame, chunks, lane, KK, hsum + tsum);
     for (int base = 0; base < chunks; base += 64) {
-        // one chunk per lane: its exact total and its map entry
+        // one chunk per lane; the next block's records are read meanwhile
+        const ChunkView next = load_chunk(rec, maps, frame, chunks, base + 64 + lane, KK, 0);
         const int c = base + lane;
-        const int64_t wg = frame * chunks + c;
-        uint64_t T = 0, dm0 = 0, dm1 = 0, flags = 0;
-        if (c < chunks) {
-            T = rec[wg * kRecordStride + field];
-            if (c == 0)
-                T -= hsum + tsum;  // chunk 0's record also holds the head and tail
-            dm0 = maps[(wg * kSquares + kk) * kMapStride + 0];
-            dm1 = maps[(wg * kSquares + kk) * kMapStride + 1];
-            flags = maps[(wg * kSquares + kk) * kMapStride + 2];
-        }
-        const int n = chunks - base < 64 ? chunks - base : 64;
-        for (int j = 0; j < n; ++j) {
-            const uint64_t Tj = __shfl(T, j, 64);
-            if (S + Tj < kTwo53) {
-                S += Tj;
-                continue;
+        const uint64_t block = wave_total64(cur.T);
+        bool done = false;
+        if (S + block < kTwo53) {
+            S += block;
+            done = true;
+        } else if (S >= kTwo53) {
+            const int e = binade(S);
+            const bool fits = c >= chunks || ((cur.flags & 1u) && flags_binade(cur.flags) == e);
+            if (__all(fits)) {
+                const Map2 mine = c < chunks ? map_from(cur.dm0, cur.dm1, cur.flags) : Map2{};
+                done = map_apply(S, wave_map(mine), e);
             }
-            const uint64_t fl = __shfl(flags, j, 64);
-            if (fl & 1u) {
-                Map2 m;
-                m.dm0 = __shfl(dm0, j, 64);
-                m.dm1 = __shfl(dm1, j, 64);
-                m.p0 = static_cast<uint32_t>((fl >> 16) & 1u);
-                m.p1 = static_cast<uint32_t>((fl >> 17) & 1u);
-                if (map_apply(S, m, static_cast<int>((fl >> 8) & 0xffu)))
+        }
+        if (!done) {
+            const int n = chunks - base < 64 ? chunks - base : 64;
+            for (int j = 0; j < n; ++j) {
+                const uint64_t Tj = lane_value64(cur.T, j);
+                if (S + Tj < kTwo53) {
+                    S += Tj;
                     continue;
+                }
+                const uint64_t fl = lane_value64(cur.flags, j);
+                if ((fl & 1u) &&
+                    map_apply(S, map_from(lane_value64(cur.dm0, j), lane_value64(cur.dm1, j), fl), flags_binade(fl)))
+                    continue;
+                const int64_t cb = vb + static_cast<int64_t>(base + j) * kChunkVectors;
+                const int64_t ce = cb + kChunkVectors < ve ? cb + kChunkVectors : ve;
+                if (cb < ce)
+                    S = walk_chunk<KK>(S, R, D, maps + ((frame * chunks + base + j) * kSquares + KK) * kEntry, cb, ce);
             }
-            const int64_t cb = vb + static_cast<int64_t>(base + j) * kChunkVectors;
-            const int64_t ce = cb + kChunkVectors < ve ? cb + kChunkVectors : ve;
-            if (cb < ce)
-                S = walk_chunk<kBytes>(S, kk, R, D, cb, ce, ref, dist);
         }
+        cur = next;
     }
     // the tail comes last
     for (int j = 0; j < tail; ++j)
-        S = cpu_add(S, __shfl(tterm, j, 64));
+        S = cpu_add(S, lane_value(tterm, j));
     if (lane == 0)
         *dst = S;
+}
+
+// One wave per (frame, square sum); two-byte samples only.  Sums that stay
+// below 2^53 were written by the prefix scan.
+__global__ __launch_bounds__(64) void cpu_order_walk(const void *ref, const void *dist, int64_t pixels, int chunks,
+                                                     const uint64_t *rec, const uint64_t *totals,
+                                                     const uint64_t *maps, uint64_t *out_cpu_noise,
+                                                     uint64_t *out_cpu_moments)
+{
+    const int64_t frame = blockIdx.x / kSquares;
+    const int kk = static_cast<int>(blockIdx.x - frame * kSquares);
+    if (totals[frame * kSquares + kk] < kTwo53)
+        return;
+    switch (kk) {
+    case kSqNoise:
+        walk_frame<kSqNoise>(ref, dist, pixels, chunks, rec, maps, frame, &out_cpu_noise[frame]);
+        break;
+    case kSqRef:
+        walk_frame<kSqRef>(ref, dist, pixels, chunks, rec, maps, frame, &out_cpu_moments[4 * frame + 2]);
+        break;
+    default:
+        walk_frame<kSqDist>(ref, dist, pixels, chunks, rec, maps, frame, &out_cpu_moments[4 * frame + 3]);
+        break;
+    }
 }
 
 }  // namespace
@@ -488,7 +745,7 @@ CpuOrderLayout cpu_order_layout(const Geometry &g)
     l.prefix = up(l.records + g.workspace_bytes);
     l.totals = up(l.prefix + wgs * kSquares * sizeof(uint64_t));
     l.maps = up(l.totals + static_cast<size_t>(g.nframes) * kSquares * sizeof(uint64_t));
-    l.bytes = up(l.maps + wgs * kSquares * kMapStride * sizeof(uint64_t));
+    l.bytes = up(l.maps + wgs * kSquares * kEntry * sizeof(uint64_t));
     return l;
 }
 
@@ -507,26 +764,18 @@ hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, cons
     if (err != hipSuccess)
         return err;
     const unsigned nf = static_cast<unsigned>(g.nframes);
-    cpu_order_prefix<<<dim3(nf), kThreads, 0, stream>>>(rec, g.chunks, prefix, totals, out_cpu_moments);
+    cpu_order_prefix<<<dim3(nf), kThreads, 0, stream>>>(rec, g.chunks, prefix, totals, out_cpu_noise,
+                                                        out_cpu_moments);
+    err = hipGetLastError();
+    if (err != hipSuccess || g.sample_bytes == 1)  // one-byte sums never reach 2^53
+        return err;
+    cpu_order_maps<<<dim3(static_cast<unsigned>(g.workgroups)), kThreads, 0, stream>>>(
+        ref, dist, g.pixels, g.chunks, rec, prefix, totals, maps);
     err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    const dim3 grid(static_cast<unsigned>(g.workgroups));
-    if (g.sample_bytes == 1) {
-        cpu_order_maps<1><<<grid, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, rec, prefix, totals, maps);
-        err = hipGetLastError();
-        if (err != hipSuccess)
-            return err;
-        cpu_order_walk<1><<<dim3(nf * kSquares), 64, 0, stream>>>(ref, dist, g.pixels, g.chunks, rec, totals,
-                                                                  maps, out_cpu_noise, out_cpu_moments);
-    } else {
-        cpu_order_maps<2><<<grid, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, rec, prefix, totals, maps);
-        err = hipGetLastError();
-        if (err != hipSuccess)
-            return err;
-        cpu_order_walk<2><<<dim3(nf * kSquares), 64, 0, stream>>>(ref, dist, g.pixels, g.chunks, rec, totals,
-                                                                  maps, out_cpu_noise, out_cpu_moments);
-    }
+    cpu_order_walk<<<dim3(nf * kSquares), 64, 0, stream>>>(ref, dist, g.pixels, g.chunks, rec, totals, maps,
+                                                           out_cpu_noise, out_cpu_moments);
     return hipGetLastError();
 }
 
