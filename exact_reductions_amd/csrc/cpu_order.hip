@@ -32,20 +32,23 @@
 //  2. cpu_order_prefix scans them per frame (the exact running sum at each
 //     chunk start, which predicts the binade the CPU's sum is in there) and
 //     writes every sum the CPU gets exactly (all of them below 2^53);
-//  3. cpu_order_maps computes, for every chunk past 2^53, maps in the
-//     predicted binade (and the next one where the chunk may cross into
-//     it): each lane chains the terms of four consecutive vectors, a wave's
-//     lanes are composed in order into the map of a slab of 256 vectors,
-//     and the chunk's eight slabs into the chunk's map;
+//  3. cpu_order_maps computes, for every slab of 256 vectors of a chunk
+//     past 2^53, its exact total and maps in the predicted binade (and the
+//     next one where the chunk may cross into it).  Most slabs need no
+//     ordered work: if every term is a multiple of the binade's unit nothing
+//     rounds, and without ties the map follows from two plain sums; only
+//     slabs with ties chain their terms and compose the lanes' maps in
+//     order.  One wave takes the slabs of a few chunks in turn, reading the
+//     next while mapping the current one;
 //  4. cpu_order_walk, one wave per frame and sum past 2^53, walks the frame
 //     in order with the running value S, 64 chunks at a time: a block that
-//     stays below 2^53 adds exactly; a block whose chunk maps are all for
-//     S's binade is composed into one map and applied if S stays in the
-//     binade; otherwise chunk by chunk, then slab by slab, then 64 vectors
-//     at a time with maps made on the spot for S's binade and the next, and
-//     only within a single vector term by term.  Every step is checked
-//     against S itself, so a prediction only decides how fast the walk is,
-//     never what it returns.
+//     stays below 2^53 adds exactly; a block whose chunk maps (composed from
+//     their slab maps) are all for S's binade is composed into one map and
+//     applied if S stays in the binade; otherwise chunk by chunk, then slab
+//     by slab, then 64 vectors at a time with maps made on the spot for S's
+//     binade and the next, and only within a single vector term by term.
+//     Every step is checked against S itself, so a prediction only decides
+//     how fast the walk is, never what it returns.
 //
 // One-byte samples (8 bits per component) never get there: their squares
 // are below 2^16 and a frame has at most 2^25 samples, so every sum stays
@@ -60,6 +63,7 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
+static_assert(kThreads == kChunkThreads, "dispatch-size check");
 constexpr uint64_t kTwo53 = 1ull << 53;
 constexpr int kTerms = 8;  // terms of one 16-byte vector of two-byte samples
 
@@ -143,16 +147,23 @@ struct RunMap {
     uint32_t P = 0x10000u;
 };
 
-// Appends term t (below 2^32 - 2^17, so t + 2^(k-1) does not wrap).
+// Appends a term given as t2 = t + 2^(k-1) (terms are below 2^32 - 2^17,
+// so t2 does not wrap).
+__device__ __forceinline__ void run_step(RunMap &m, uint32_t t2, int k)
+{
+    const uint32_t hb = __builtin_amdgcn_ubfe(t2, static_cast<uint32_t>(k), 1u);
+    const uint32_t x = m.P ^ (hb | (hb << 16));  // parity of m + h, per s
+    const bool tie = (t2 & ((1u << k) - 1)) == 0;
+    m.C += tie ? x : 0u;  // a tie rounds down from m + h exactly when m + h is odd
+    m.P = tie ? 0u : x;
+}
+
+// Appends term t, also adding its rr to rr_sum.
 __device__ __forceinline__ void run_add(RunMap &m, uint32_t &rr_sum, uint32_t t, int k)
 {
     const uint32_t t2 = t + (1u << (k - 1));
-    const uint32_t rr = t2 & ((1u << k) - 1);
-    rr_sum += rr;
-    const uint32_t x = m.P ^ (((t2 >> k) & 1u) * 0x10001u);  // parity of m + h, per s
-    const bool tie = rr == 0;
-    m.C += tie ? x : 0u;  // a tie rounds down from m + h exactly when m + h is odd
-    m.P = tie ? 0u : x;
+    rr_sum += t2 & ((1u << k) - 1);
+    run_step(m, t2, k);
 }
 
 __device__ __forceinline__ uint32_t swap_halves(uint32_t x) { return __builtin_amdgcn_alignbit(x, x, 16); }
@@ -225,6 +236,17 @@ __device__ __forceinline__ uint64_t pick(uint64_t s, uint64_t x, uint64_t y)
 {
     const uint64_t mask = 0 - (s & 1u);
     return (x & ~mask) | (y & mask);
+}
+
+// The map of a run without ties whose sum of h is h: m grows by h from
+// either parity, and the parity flips with h's.
+__device__ __forceinline__ Map2 untied_map(uint64_t h)
+{
+    Map2 m;
+    m.dm0 = m.dm1 = h;
+    m.p0 = static_cast<uint32_t>(h) & 1u;
+    m.p1 = m.p0 ^ 1u;
+    return m;
 }
 
 // a then b
@@ -320,12 +342,36 @@ __device__ __forceinline__ uint32_t vector_term(const u32x4 &a, const u32x4 &b, 
     return square_term<2>(KK, r, d);
 }
 
+// Vector v of the planes square sum KK reads; a lane with !ok reads vector
+// `safe` (one known to exist) instead, for the caller to drop (keep_if).
+// Every lane loads, so no branch separates the loads from the waits for
+// them and the next vectors can be in flight while these are used.
 template <int KK>
-__device__ __forceinline__ void load_vector(const u32x4 *R, const u32x4 *D, int64_t v, bool ok, u32x4 &a, u32x4 &b)
+__device__ __forceinline__ void load_vector(const u32x4 *R, const u32x4 *D, int64_t v, bool ok, int64_t safe,
+                                            u32x4 &a, u32x4 &b)
 {
     const u32x4 zero = {0, 0, 0, 0};
-    a = (ok && KK != kSqDist) ? __builtin_nontemporal_load(R + v) : zero;
-    b = (ok && KK != kSqRef) ? __builtin_nontemporal_load(D + v) : zero;
+    const int64_t at = ok ? v : safe;
+    if constexpr (KK != kSqDist)
+        a = __builtin_nontemporal_load(R + at);
+    else
+        a = zero;
+    if constexpr (KK != kSqRef)
+        b = __builtin_nontemporal_load(D + at);
+    else
+        b = zero;
+}
+
+// Zeros a loaded vector that lies past the end (zero terms change neither
+// a map nor a total).
+template <int KK>
+__device__ __forceinline__ void keep_if(bool ok, u32x4 &a, u32x4 &b)
+{
+    const u32x4 zero = {0, 0, 0, 0};
+    if constexpr (KK != kSqDist)
+        a = ok ? a : zero;
+    if constexpr (KK != kSqRef)
+        b = ok ? b : zero;
 }
 
 // ------------------------------------------------------------ 2. prefix scan
@@ -380,67 +426,142 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(const uint64_t *rec
     }
 }
 
-// ------------------------------------------------------------ 3. chunk maps
-// Entry of chunk wg, square kk (kEntry uint64): the chunk's map {dm0, dm1,
-// flags}, the maps of its kSlabs slabs in the predicted binade e, their
-// maps in binade e + 1 (made only where the chunk's exact range reaches
-// 2^(e+1), i.e. where the CPU's sum probably changes binade inside it), and
-// the slabs' exact totals.  Every entry's flags are written on every call
-// (invalid where no map was made).
+// ------------------------------------------------------------ 3. slab maps
+// Entry of chunk wg, square kk (kEntry uint64): the maps {dm0, dm1, flags}
+// of its kSlabs slabs in the predicted binade e, their maps in binade e + 1
+// (made only where the chunk's exact range reaches 2^(e+1), i.e. where the
+// CPU's sum probably changes binade inside it; flags 0 otherwise), and the
+// slabs' exact totals.  Only chunks past 2^53 get an entry; the walk reads
+// no other (below 2^53 it adds chunk totals exactly).
 constexpr int kSlabVectors = 256;
 constexpr int kSlabs = kChunkVectors / kSlabVectors;
-constexpr int kLaneVectors = kSlabVectors / 64;  // consecutive vectors one lane chains
-constexpr int kSlabMapsA = 3;
-constexpr int kSlabMapsB = 3 + 3 * kSlabs;
-constexpr int kSlabTotals = 3 + 6 * kSlabs;
+constexpr int kLaneVectors = kSlabVectors / 64;  // vectors of a slab per lane
+constexpr int kSlabMapsA = 0;
+constexpr int kSlabMapsB = 3 * kSlabs;
+constexpr int kSlabTotals = 6 * kSlabs;
 constexpr int kEntry = kSlabTotals + kSlabs;
-static_assert(kSlabs == 2 * (kThreads / 64), "two slabs per wave");
 
-// A chunk's slab maps in LDS, for the chunk map.
-struct SlabMaps {
-    uint64_t dm0[kSlabs], dm1[kSlabs];
-    uint32_t p[kSlabs];
+// Work of the maps kernel: one wave per (frame, square sum, group of
+// kGroupChunks chunks); an item is kItemSlabs consecutive slabs.
+constexpr int kItemSlabs = 1;
+constexpr int kItems = kSlabs / kItemSlabs;  // items per chunk
+constexpr int kGroupChunks = 4;
+constexpr int kGroupItems = kGroupChunks * kItems;
+static_assert(kGroupItems <= 64, "one lane per item");
+
+// The planes' vectors of one item: lane l holds vectors l, 64 + l, 128 + l
+// and 192 + l of each slab (each load instruction reads 1 KB in one piece);
+// bit (4s + j) of ok is set where vector 64j + l of slab s lies inside the
+// chunk.
+struct ItemData {
+    u32x4 a[kItemSlabs][kLaneVectors], b[kItemSlabs][kLaneVectors];
+    uint32_t ok;
 };
 
+// Makes the compiler forget what it knows of the vectors' values, so that
+// the terms derived from them are recomputed rather than kept live (the
+// paths that need them again are the uncommon ones).
 template <int KK>
-__device__ __forceinline__ void chunk_maps(const u32x4 *R, const u32x4 *D, int64_t cb, int64_t ce, int e,
-                                           bool dual, uint64_t *entry, SlabMaps &s_slab)
+__device__ __forceinline__ void forget(u32x4 (&a)[kLaneVectors], u32x4 (&b)[kLaneVectors])
 {
-    const int wave = threadIdx.x / 64, lane = threadIdx.x & 63;
-    const int k = e - 52;
-    u32x4 a[2][kLaneVectors], b[2][kLaneVectors];
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int j = 0; j < kLaneVectors; ++j) {
+        if constexpr (KK != kSqDist)
+            asm volatile("" : "+v"(a[j]));
+        if constexpr (KK != kSqRef)
+            asm volatile("" : "+v"(b[j]));
+    }
+}
+
+// The slabs from sb on of the chunk [cb, ce), cb < ce; a slab may start
+// past ce in the chunk after a frame's last whole vector.
+template <int KK>
+__device__ __forceinline__ void load_item(ItemData &x, const u32x4 *R, const u32x4 *D, int64_t cb, int64_t sb,
+                                          int64_t ce)
+{
+    const int lane = threadIdx.x & 63;
+    x.ok = 0;
+#pragma unroll
+    for (int s = 0; s < kItemSlabs; ++s)
 #pragma unroll
         for (int j = 0; j < kLaneVectors; ++j) {
-            const int64_t v = cb + static_cast<int64_t>(2 * wave + s) * kSlabVectors + kLaneVectors * lane + j;
-            load_vector<KK>(R, D, v, v < ce, a[s][j], b[s][j]);
+            const int64_t v = sb + static_cast<int64_t>(s) * kSlabVectors + 64 * j + lane;
+            load_vector<KK>(R, D, v, v < ce, cb, x.a[s][j], x.b[s][j]);
+            x.ok |= (v < ce ? 1u : 0u) << (kLaneVectors * s + j);
         }
-    // Vectors past the chunk's end read as zero terms, which change
-    // neither a map nor a total: each slab is a full 256 * 8 terms.
+}
+
+// The map, in binade 2^(k+52), of the slab whose vectors the wave's lanes
+// hold (vector 64j + l in lane l), with exact total T.  Three cases,
+// decided for the whole wave: every term a multiple of 2^k (nothing rounds:
+// m grows by T / 2^k); no ties (m grows by the sum of h, both parities flip
+// with its parity) -- neither needs the terms' order; otherwise each lane
+// chains the terms of each of its vectors, the lanes' maps of each row of
+// 64 vectors are composed in lane order and the four rows in turn.
+template <int KK>
+__device__ __forceinline__ Map2 slab_map(u32x4 (&a)[kLaneVectors], u32x4 (&b)[kLaneVectors], uint32_t low_bits,
+                                         uint64_t T, int k)
+{
+    constexpr uint64_t n = 64 * kLaneVectors * kTerms;
+    const uint32_t half = 1u << (k - 1), mask = (1u << k) - 1;
+    if (__all((low_bits & mask) == 0))
+        return untied_map(T >> k);
+    uint32_t rr_sum = 0, rr_min = ~0u;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        RunMap mA, mB;
-        uint32_t rA = 0, rB = 0;
+    for (int j = 0; j < kLaneVectors; ++j)
+#pragma unroll
+        for (int i = 0; i < kTerms; ++i) {
+            const uint32_t rr = (vector_term<KK>(a[j], b[j], i) + half) & mask;
+            rr_sum += rr;
+            rr_min = min(rr_min, rr);
+        }
+    forget<KK>(a, b);
+    const uint32_t RR = wave_total32(rr_sum);
+    if (!__any(rr_min == 0))
+        return untied_map((T + (n << (k - 1)) - RR) >> k);
+    RunMap slab;
+#pragma unroll
+    for (int j = 0; j < kLaneVectors; ++j) {
+        RunMap m;
+#pragma unroll
+        for (int i = 0; i < kTerms; ++i)
+            run_step(m, vector_term<KK>(a[j], b[j], i) + half, k);
+        slab = run_then(slab, wave_run(m));
+    }
+    return run_map(slab, T, n, RR, k);
+}
+
+// The slabs of one item (from slab si0 of its chunk on); lane 0 writes
+// their part of the entry.
+template <int KK>
+__device__ __forceinline__ void item_maps(ItemData &x, int si0, int e, bool dual, uint64_t *entry)
+{
+    const int k = e - 52;
+#pragma unroll
+    for (int s = 0; s < kItemSlabs; ++s) {
+#pragma unroll
+        for (int j = 0; j < kLaneVectors; ++j)
+            keep_if<KK>((x.ok >> (kLaneVectors * s + j)) & 1u, x.a[s][j], x.b[s][j]);
         uint64_t tot = 0;
+        uint32_t low_bits = 0;
 #pragma unroll
         for (int j = 0; j < kLaneVectors; ++j)
 #pragma unroll
             for (int i = 0; i < kTerms; ++i) {
-                const uint32_t t = vector_term<KK>(a[s][j], b[s][j], i);
+                const uint32_t t = vector_term<KK>(x.a[s][j], x.b[s][j], i);
                 tot += t;
-                run_add(mA, rA, t, k);
-                if (dual)
-                    run_add(mB, rB, t, k + 1);
+                low_bits |= t;
             }
-        constexpr uint64_t n = static_cast<uint64_t>(kSlabVectors) * kTerms;
+        forget<KK>(x.a[s], x.b[s]);
         const uint64_t T = wave_total64(tot);
-        const Map2 slab = run_map(wave_run(mA), T, n, wave_total32(rA), k);
+        const Map2 slab = slab_map<KK>(x.a[s], x.b[s], low_bits, T, k);
         Map2 slab_b;
-        if (dual)
-            slab_b = run_map(wave_run(mB), T, n, wave_total32(rB), k + 1);
-        const int si = 2 * wave + s;
-        if (lane == 0) {
+        if (dual) {
+            forget<KK>(x.a[s], x.b[s]);
+            slab_b = slab_map<KK>(x.a[s], x.b[s], low_bits, T, k + 1);
+        }
+        const int si = si0 + s;
+        if ((threadIdx.x & 63) == 0) {
             entry[kSlabMapsA + 3 * si + 0] = slab.dm0;
             entry[kSlabMapsA + 3 * si + 1] = slab.dm1;
             entry[kSlabMapsA + 3 * si + 2] = map_flags(slab, e);
@@ -448,67 +569,130 @@ __device__ __forceinline__ void chunk_maps(const u32x4 *R, const u32x4 *D, int64
             entry[kSlabMapsB + 3 * si + 1] = slab_b.dm1;
             entry[kSlabMapsB + 3 * si + 2] = dual ? map_flags(slab_b, e + 1) : 0;
             entry[kSlabTotals + si] = T;
-            s_slab.dm0[si] = slab.dm0;
-            s_slab.dm1[si] = slab.dm1;
-            s_slab.p[si] = slab.p0 | (slab.p1 << 1);
         }
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        Map2 chunk;
-        for (int si = 0; si < kSlabs; ++si) {
-            Map2 x;
-            x.dm0 = s_slab.dm0[si];
-            x.dm1 = s_slab.dm1[si];
-            x.p0 = s_slab.p[si] & 1u;
-            x.p1 = s_slab.p[si] >> 1;
-            chunk = map_then(chunk, x);
-        }
-        entry[0] = chunk.dm0;
-        entry[1] = chunk.dm1;
-        entry[2] = map_flags(chunk, e);
     }
 }
 
-// One workgroup per (frame, chunk); two-byte samples only.
+// Where the items of a group lie.
+struct Group {
+    const u32x4 *R, *D;
+    uint64_t *maps;
+    int64_t frame, vb, ve;
+    int chunks, g;
+};
+
+template <int KK>
+__device__ __forceinline__ void group_item(const Group &G, int item, int64_t &cb, int64_t &sb, int64_t &ce,
+                                           uint64_t *&entry, int &si)
+{
+    const int c = G.g * kGroupChunks + item / kItems;
+    si = (item % kItems) * kItemSlabs;
+    cb = G.vb + static_cast<int64_t>(c) * kChunkVectors;
+    ce = cb + kChunkVectors < G.ve ? cb + kChunkVectors : G.ve;
+    sb = cb + static_cast<int64_t>(si) * kSlabVectors;
+    entry = G.maps + ((G.frame * G.chunks + c) * kSquares + KK) * kEntry;
+}
+
+// The wanted items of one group, in order (the set bits of `want`; lane j
+// holds item j's binade and dual flag).  The next item's vectors are read
+// while the current one is mapped, except for the noise, which reads both
+// planes.
+template <int KK>
+__device__ __forceinline__ void group_maps(const Group &G, uint64_t want, int e_lane, int dual_lane)
+{
+    int64_t cb, sb, ce;
+    uint64_t *entry;
+    int si;
+    ItemData x, y;
+    int j = __builtin_ctzll(want);
+    want &= want - 1;
+    group_item<KK>(G, j, cb, sb, ce, entry, si);
+    load_item<KK>(x, G.R, G.D, cb, sb, ce);
+    if constexpr (KK == kSqNoise) {
+        for (;;) {
+            item_maps<KK>(x, si, lane_value(e_lane, j), lane_value(dual_lane, j) != 0, entry);
+            if (!want)
+                return;
+            j = __builtin_ctzll(want);
+            want &= want - 1;
+            group_item<KK>(G, j, cb, sb, ce, entry, si);
+            load_item<KK>(x, G.R, G.D, cb, sb, ce);
+        }
+    } else {
+        // Two buffers, taken in turn.  Each item mapped inside the loop
+        // follows the loads of the next one, and the last item is mapped
+        // apart, so that the waits before mapping an item never cover the
+        // loads of the one after it.
+        int j2, si2;
+        uint64_t *entry2;
+        for (;;) {
+            if (!want) {
+                item_maps<KK>(x, si, lane_value(e_lane, j), lane_value(dual_lane, j) != 0, entry);
+                return;
+            }
+            j2 = __builtin_ctzll(want);
+            want &= want - 1;
+            group_item<KK>(G, j2, cb, sb, ce, entry2, si2);
+            load_item<KK>(y, G.R, G.D, cb, sb, ce);
+            item_maps<KK>(x, si, lane_value(e_lane, j), lane_value(dual_lane, j) != 0, entry);
+            if (!want) {
+                item_maps<KK>(y, si2, lane_value(e_lane, j2), lane_value(dual_lane, j2) != 0, entry2);
+                return;
+            }
+            j = __builtin_ctzll(want);
+            want &= want - 1;
+            group_item<KK>(G, j, cb, sb, ce, entry, si);
+            load_item<KK>(x, G.R, G.D, cb, sb, ce);
+            item_maps<KK>(y, si2, lane_value(e_lane, j2), lane_value(dual_lane, j2) != 0, entry2);
+        }
+    }
+}
+
+// One wave per (frame, square sum, group of chunks); two-byte samples only.
 __global__ __launch_bounds__(kThreads) void cpu_order_maps(const void *ref, const void *dist, int64_t pixels,
-                                                           int chunks, const uint64_t *rec,
+                                                           int chunks, int nframes, const uint64_t *rec,
                                                            const uint64_t *prefix, const uint64_t *totals,
                                                            uint64_t *maps)
 {
     constexpr int V = 8;
-    __shared__ SlabMaps s_slab[kSquares];
-    const int64_t wg = blockIdx.x;
-    const int64_t frame = wg / chunks;
-    const int chunk = static_cast<int>(wg - frame * chunks);
-    const int64_t e0 = frame * pixels, e1 = e0 + pixels;
-    const int64_t vb = (e0 + V - 1) / V, ve = e1 / V;
-    const int64_t cb = vb + static_cast<int64_t>(chunk) * kChunkVectors;
-    const int64_t ce = cb + kChunkVectors < ve ? cb + kChunkVectors : ve;
-    const u32x4 *R = static_cast<const u32x4 *>(ref);
-    const u32x4 *D = static_cast<const u32x4 *>(dist);
-    for (int kk = 0; kk < kSquares; ++kk) {
-        uint64_t *entry = maps + (wg * kSquares + kk) * kEntry;
+    const int lane = threadIdx.x & 63;
+    const int groups = (chunks + kGroupChunks - 1) / kGroupChunks;
+    const int64_t gw = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + threadIdx.x / 64;
+    const int64_t fk = gw / groups;  // frame * kSquares + kk
+    if (fk >= static_cast<int64_t>(nframes) * kSquares || totals[fk] < kTwo53)
+        return;
+    Group G;
+    G.frame = fk / kSquares;
+    const int kk = static_cast<int>(fk - G.frame * kSquares);
+    G.g = static_cast<int>(gw - fk * groups);
+    G.chunks = chunks;
+    G.maps = maps;
+    G.R = static_cast<const u32x4 *>(ref);
+    G.D = static_cast<const u32x4 *>(dist);
+    const int64_t e0 = G.frame * pixels, e1 = e0 + pixels;
+    G.vb = (e0 + V - 1) / V;
+    G.ve = e1 / V;
+    // lane j < kGroupItems: item j, i.e. slabs from (j % kItems) *
+    // kItemSlabs on of chunk j / kItems
+    const int c = G.g * kGroupChunks + lane / kItems;
+    bool want = false;
+    int e = 0, dual = 0;
+    if (lane < kGroupItems && c < chunks) {
+        const int64_t wg = G.frame * chunks + c;
         const uint64_t p = prefix[wg * kSquares + kk];
         const uint64_t r = rec[wg * kRecordStride + record_field(kk)];
-        // uniform across the workgroup
-        if (!(cb < ce && totals[frame * kSquares + kk] >= kTwo53 && p + r >= kTwo53)) {
-            if (threadIdx.x == 0) {
-                entry[2] = 0;
-                for (int j = 0; j < kSlabs; ++j) {
-                    entry[kSlabMapsA + 3 * j + 2] = 0;
-                    entry[kSlabMapsB + 3 * j + 2] = 0;
-                }
-            }
-            continue;
-        }
-        const int e = binade(p > kTwo53 ? p : kTwo53);
-        const bool dual = e < 56 && p + r >= (1ull << (e + 1));
-        switch (kk) {
-        case kSqNoise: chunk_maps<kSqNoise>(R, D, cb, ce, e, dual, entry, s_slab[kk]); break;
-        case kSqRef: chunk_maps<kSqRef>(R, D, cb, ce, e, dual, entry, s_slab[kk]); break;
-        default: chunk_maps<kSqDist>(R, D, cb, ce, e, dual, entry, s_slab[kk]); break;
-        }
+        const int64_t cb = G.vb + static_cast<int64_t>(c) * kChunkVectors;
+        want = cb < G.ve && p + r >= kTwo53;
+        e = binade(p > kTwo53 ? p : kTwo53);
+        dual = e < 56 && p + r >= (1ull << (e + 1));
+    }
+    const uint64_t mask = __ballot(want);
+    if (!mask)
+        return;
+    switch (kk) {
+    case kSqNoise: group_maps<kSqNoise>(G, mask, e, dual); break;
+    case kSqRef: group_maps<kSqRef>(G, mask, e, dual); break;
+    default: group_maps<kSqDist>(G, mask, e, dual); break;
     }
 }
 
@@ -520,7 +704,7 @@ template <int KK>
 __device__ __forceinline__ uint64_t walk_vector(uint64_t S, const u32x4 *R, const u32x4 *D, int64_t v)
 {
     u32x4 a, b;
-    load_vector<KK>(R, D, v, true, a, b);
+    load_vector<KK>(R, D, v, true, v, a, b);
 #pragma unroll
     for (int i = 0; i < kTerms; ++i)
         S = cpu_add(S, vector_term<KK>(a, b, i));
@@ -538,7 +722,8 @@ __device__ __forceinline__ uint64_t walk_slab(uint64_t S, const u32x4 *R, const 
     for (int64_t base = sb; base < se; base += 64) {
         const int64_t v = base + lane;
         u32x4 a, b;
-        load_vector<KK>(R, D, v, v < se, a, b);
+        load_vector<KK>(R, D, v, v < se, base, a, b);
+        keep_if<KK>(v < se, a, b);
         RunMap mA, mB;
         uint32_t rA = 0, rB = 0;
         uint64_t tot = 0;
@@ -625,29 +810,36 @@ __device__ __forceinline__ uint64_t walk_chunk(uint64_t S, const u32x4 *R, const
 }
 
 // The vectors' part of chunk c's record (chunk 0's also holds the head and
-// tail samples), and its stored map.
-struct ChunkView {
-    uint64_t T = 0, dm0 = 0, dm1 = 0, flags = 0;
-};
-
-__device__ __forceinline__ ChunkView load_chunk(const uint64_t *rec, const uint64_t *maps, int64_t frame, int chunks,
-                                                int c, int kk, uint64_t head_tail)
+// tail samples).
+__device__ __forceinline__ uint64_t chunk_total(const uint64_t *rec, int64_t frame, int chunks, int c, int kk,
+                                                uint64_t head_tail)
 {
-    ChunkView x;
-    if (c < chunks) {
-        const int64_t wg = frame * chunks + c;
-        const uint64_t *entry = maps + (wg * kSquares + kk) * kEntry;
-        x.T = rec[wg * kRecordStride + record_field(kk)] - (c == 0 ? head_tail : 0);
-        x.dm0 = entry[0];
-        x.dm1 = entry[1];
-        x.flags = entry[2];
+    if (c >= chunks)
+        return 0;
+    return rec[(frame * chunks + c) * kRecordStride + record_field(kk)] - (c == 0 ? head_tail : 0);
+}
+
+// Chunk c's map, composed from its slab maps; flags 0 unless all of them
+// are valid and for one binade.  Read only for non-empty chunks past 2^53,
+// whose entries the maps kernel has written.
+__device__ __forceinline__ Map2 chunk_map(const uint64_t *entry, uint64_t &flags)
+{
+    Map2 m;
+    const uint64_t key = entry[kSlabMapsA + 2] & 0xffffu;  // valid bit and binade of slab 0
+    bool ok = (key & 1u) != 0;
+#pragma unroll
+    for (int j = 0; j < kSlabs; ++j) {
+        const uint64_t fl = entry[kSlabMapsA + 3 * j + 2];
+        m = map_then(m, map_from(entry[kSlabMapsA + 3 * j], entry[kSlabMapsA + 3 * j + 1], fl));
+        ok = ok && (fl & 0xffffu) == key;
     }
-    return x;
+    flags = ok ? map_flags(m, flags_binade(key)) : 0;
+    return m;
 }
 
 template <int KK>
-__device__ __forceinline__ void walk_frame(const void *ref, const void *dist, int64_t pixels, int chunks, const uint64_t *rec,
-                           const uint64_t *maps, int64_t frame, uint64_t *dst)
+__device__ __forceinline__ void walk_frame(const void *ref, const void *dist, int64_t pixels, int chunks,
+                                           const uint64_t *rec, const uint64_t *maps, int64_t frame, uint64_t *dst)
 {
     constexpr int V = 8;
     const int lane = threadIdx.x;
@@ -665,43 +857,52 @@ __device__ __forceinline__ void walk_frame(const void *ref, const void *dist, in
     uint64_t S = hsum;
     const u32x4 *R = static_cast<const u32x4 *>(ref);
     const u32x4 *D = static_cast<const u32x4 *>(dist);
-    ChunkView cur = load_chunk(rec, maps, frame, chunks, lane, KK, hsum + tsum);
+    const uint64_t *entries = maps + (frame * chunks * kSquares + KK) * kEntry;  // chunk c: + c * kSquares * kEntry
+    uint64_t T = chunk_total(rec, frame, chunks, lane, KK, hsum + tsum);
     for (int base = 0; base < chunks; base += 64) {
-        // one chunk per lane; the next block's records are read meanwhile
-        const ChunkView next = load_chunk(rec, maps, frame, chunks, base + 64 + lane, KK, 0);
+        // one chunk per lane; the next block's totals are read meanwhile
+        const uint64_t T_next = chunk_total(rec, frame, chunks, base + 64 + lane, KK, 0);
         const int c = base + lane;
-        const uint64_t block = wave_total64(cur.T);
-        bool done = false;
+        const uint64_t block = wave_total64(T);
         if (S + block < kTwo53) {
             S += block;
-            done = true;
-        } else if (S >= kTwo53) {
+            T = T_next;
+            continue;
+        }
+        // past 2^53 within this block: every non-empty chunk from the one
+        // where the exact sum gets there on has its slab maps; an empty
+        // chunk (the last one of a frame may be) adds nothing
+        const bool empty = c >= chunks || vb + static_cast<int64_t>(c) * kChunkVectors >= ve;
+        uint64_t flags = 0;
+        Map2 cm;
+        if (!empty)
+            cm = chunk_map(entries + static_cast<int64_t>(c) * kSquares * kEntry, flags);
+        bool done = false;
+        if (S >= kTwo53) {
             const int e = binade(S);
-            const bool fits = c >= chunks || ((cur.flags & 1u) && flags_binade(cur.flags) == e);
-            if (__all(fits)) {
-                const Map2 mine = c < chunks ? map_from(cur.dm0, cur.dm1, cur.flags) : Map2{};
-                done = map_apply(S, wave_map(mine), e);
-            }
+            if (__all(empty || ((flags & 1u) && flags_binade(flags) == e)))
+                done = map_apply(S, wave_map(cm), e);
         }
         if (!done) {
             const int n = chunks - base < 64 ? chunks - base : 64;
             for (int j = 0; j < n; ++j) {
-                const uint64_t Tj = lane_value64(cur.T, j);
+                const int64_t cb = vb + static_cast<int64_t>(base + j) * kChunkVectors;
+                const int64_t ce = cb + kChunkVectors < ve ? cb + kChunkVectors : ve;
+                if (cb >= ce)
+                    continue;
+                const uint64_t Tj = lane_value64(T, j);
                 if (S + Tj < kTwo53) {
                     S += Tj;
                     continue;
                 }
-                const uint64_t fl = lane_value64(cur.flags, j);
+                const uint64_t fl = lane_value64(flags, j);
                 if ((fl & 1u) &&
-                    map_apply(S, map_from(lane_value64(cur.dm0, j), lane_value64(cur.dm1, j), fl), flags_binade(fl)))
+                    map_apply(S, map_from(lane_value64(cm.dm0, j), lane_value64(cm.dm1, j), fl), flags_binade(fl)))
                     continue;
-                const int64_t cb = vb + static_cast<int64_t>(base + j) * kChunkVectors;
-                const int64_t ce = cb + kChunkVectors < ve ? cb + kChunkVectors : ve;
-                if (cb < ce)
-                    S = walk_chunk<KK>(S, R, D, maps + ((frame * chunks + base + j) * kSquares + KK) * kEntry, cb, ce);
+                S = walk_chunk<KK>(S, R, D, entries + static_cast<int64_t>(base + j) * kSquares * kEntry, cb, ce);
             }
         }
-        cur = next;
+        T = T_next;
     }
     // the tail comes last
     for (int j = 0; j < tail; ++j)
@@ -769,8 +970,10 @@ hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, cons
     err = hipGetLastError();
     if (err != hipSuccess || g.sample_bytes == 1)  // one-byte sums never reach 2^53
         return err;
-    cpu_order_maps<<<dim3(static_cast<unsigned>(g.workgroups)), kThreads, 0, stream>>>(
-        ref, dist, g.pixels, g.chunks, rec, prefix, totals, maps);
+    const int64_t groups = (g.chunks + kGroupChunks - 1) / kGroupChunks;
+    const int64_t waves = static_cast<int64_t>(g.nframes) * kSquares * groups;
+    cpu_order_maps<<<dim3(static_cast<unsigned>((waves + kThreads / 64 - 1) / (kThreads / 64))), kThreads, 0,
+                     stream>>>(ref, dist, g.pixels, g.chunks, g.nframes, rec, prefix, totals, maps);
     err = hipGetLastError();
     if (err != hipSuccess)
         return err;

@@ -36,6 +36,17 @@ struct Geometry {
 
 Geometry make_geometry(int w, int h, int bpc, int nframes);
 
+// Work-items per workgroup of the launches over (frame, chunk).
+constexpr int kChunkThreads = 256;
+
+// A dispatch counts its work-items in 32 bits.  The plane-stats launch has
+// one workgroup per (frame, chunk); the CPU-order maps launch one per
+// (frame, chunk, square sum), i.e. per_chunk = 3.
+inline bool fits_dispatch(const Geometry &g, int per_chunk)
+{
+    return g.workgroups * per_chunk * kChunkThreads <= static_cast<int64_t>(0xffffffffu);
+}
+
 // Queues both stages on `stream`, recording `stage1_begin`/`stage1_end` (if
 // not null) around stage 1.  Returns hipSuccess or the first error.
 hipError_t launch_plane_stats(const Geometry &g, const void *ref, const void *dist,

@@ -47,6 +47,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;              // four wave64s
+static_assert(kThreads == kChunkThreads, "dispatch-size check");
 constexpr int kWaves = kThreads / 64;
 constexpr int kIters = 8;                  // 16-byte vectors per lane per plane
 constexpr int kInFlight = 4;               // vectors of each plane loaded before use

@@ -11,6 +11,7 @@
 #include <stdint.h>
 
 #include "plane_stats.h"
+#include "terms.h"
 #include "vqx.h"
 
 #pragma clang fp contract(off)
@@ -29,26 +30,28 @@ int check_shape(int w, int h, int bpc)
     return VQX_OK;
 }
 
-int check_batch(int w, int h, int bpc, int nframes)
+// per_chunk: workgroups per (frame, chunk) of the widest launch of the
+// entry point (1 plane stats, 3 the CPU-order form).
+int check_batch(int w, int h, int bpc, int nframes, int per_chunk = 1)
 {
     int rc = check_shape(w, h, bpc);
     if (rc != VQX_OK)
         return rc;
     if (nframes < 1)
         return VQX_E_NFRAMES;
-    // one workgroup per (frame, chunk) must fit a 1-D grid
-    if (vqx::make_geometry(w, h, bpc, nframes).workgroups > INT32_MAX)
+    // every launch must fit one dispatch
+    if (!vqx::fits_dispatch(vqx::make_geometry(w, h, bpc, nframes), per_chunk))
         return VQX_E_NFRAMES;
     return VQX_OK;
 }
 
 // All argument checks of the plane-stats entry points, in a fixed order.
 int check_stats_args(const void *ref, const void *dist, int w, int h, int bpc, int nframes,
-                     const uint64_t *out_noise, const uint64_t *out_moments)
+                     const uint64_t *out_noise, const uint64_t *out_moments, int per_chunk = 1)
 {
     if (!ref || !dist || !out_noise || !out_moments)
         return VQX_E_NULL;
-    int rc = check_batch(w, h, bpc, nframes);
+    int rc = check_batch(w, h, bpc, nframes, per_chunk);
     if (rc != VQX_OK)
         return rc;
     if (!aligned(ref, 16) || !aligned(dist, 16) || !aligned(out_noise, 8) || !aligned(out_moments, 8))
@@ -182,7 +185,7 @@ int vqx_plane_stats_cpu_order_workspace_bytes(int w, int h, int bpc, int nframes
 {
     if (!bytes)
         return VQX_E_NULL;
-    int rc = check_batch(w, h, bpc, nframes);
+    int rc = check_batch(w, h, bpc, nframes, vqx::kSquares);
     if (rc != VQX_OK)
         return rc;
     *bytes = vqx::cpu_order_layout(vqx::make_geometry(w, h, bpc, nframes)).bytes;
@@ -194,7 +197,7 @@ int vqx_plane_stats_batch_cpu_order_ws(const void *ref, const void *dist, int w,
                                        uint64_t *out_cpu_noise, uint64_t *out_cpu_moments,
                                        void *workspace, size_t workspace_bytes, void *stream)
 {
-    int rc = check_stats_args(ref, dist, w, h, bpc, nframes, out_noise, out_moments);
+    int rc = check_stats_args(ref, dist, w, h, bpc, nframes, out_noise, out_moments, vqx::kSquares);
     if (rc != VQX_OK)
         return rc;
     if (!out_cpu_noise || !out_cpu_moments)

@@ -56,7 +56,10 @@ enum vqx_status {
     VQX_E_NULL = -1,      /* a required pointer is NULL */
     VQX_E_DIMS = -2,      /* w < 1, h < 1 or w*h > VQX_MAX_PIXELS */
     VQX_E_BPC = -3,       /* bpc outside 8..16 */
-    VQX_E_NFRAMES = -4,   /* nframes < 1 */
+    VQX_E_NFRAMES = -4,   /* nframes < 1, or a batch too large for one dispatch: more
+                             than (2^32-1)/256 chunks of 2048 16-byte vectors per plane
+                             (frames round up to whole chunks), a third of that for
+                             the CPU-order entry points */
     VQX_E_ALIGN = -5,     /* ref/dist not 16-byte aligned, or an output not 8-byte aligned */
     VQX_E_WORKSPACE = -6, /* workspace smaller than vqx_plane_stats_workspace_bytes() */
     VQX_E_HIP = -7,       /* the HIP runtime reported an error (launch or allocation) */
@@ -158,9 +161,9 @@ int vqx_plane_stats_cpu_order_workspace_bytes(int w, int h, int bpc, int nframes
  * change [MOMENT, Alternatives].  Concluding them with
  * vqx_conclude_batch gives the CPU's scores bit for bit on every frame.
  *
- * Frames whose sums stay below 2^53 cost only three small kernels more
- * than vqx_plane_stats_batch_ws; a frame past 2^53 costs one more read of
- * its planes.  Arguments, layout, ownership and errors otherwise as
+ * Frames whose sums stay below 2^53 cost only small kernels more than
+ * vqx_plane_stats_batch_ws; a frame past 2^53 costs one more read of its
+ * planes.  Arguments, layout, ownership and errors otherwise as
  * vqx_plane_stats_batch_ws, with the workspace sized by
  * vqx_plane_stats_cpu_order_workspace_bytes.
  */

@@ -8,6 +8,7 @@ from .workloads import (  # noqa: F401
     Workload,
     constant_pair,
     generate,
+    odd_dark_bright,
     past53_fullrange,
     past53_mixed,
     sha256,

@@ -152,6 +152,23 @@ def past53_mixed(seed: int = 2053, w: int = 2560, h: int = 1440, nframes: int = 
     return out[0], out[1]
 
 
+def odd_dark_bright(seed: int = 4053, w: int = 3840, h: int = 2160, nframes: int = 1):
+    """16-bit frames where a tenth of the samples are odd values 1..4095.
+
+    The rest are uniform 49152..65535, so each plane's sum of float squares
+    runs well past 2**54 units.  The squares of the dark samples are odd and
+    exact; those of the bright ones are multiples of 2**8.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for _ in range(2):
+        low = rng.random(size=(nframes, h, w)) < 0.1
+        dark = (2 * rng.integers(0, 2047, size=(nframes, h, w), endpoint=True) + 1).astype(np.uint16)
+        bright = rng.integers(49152, 65535, size=(nframes, h, w), endpoint=True, dtype=np.uint16)
+        out.append(np.where(low, dark, bright).astype(np.uint16))
+    return out[0], out[1]
+
+
 def past53_fullrange(seed: int = 3053, w: int = 3840, h: int = 2160, nframes: int = 1):
     """Independent full-range 16-bit noise (uniform 0..65535) in ref and dist."""
     return uniform_planes(w, h, nframes, 16, seed, 0, 65535)

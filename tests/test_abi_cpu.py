@@ -74,6 +74,27 @@ def test_largest_frame_accepted():
     assert vqx.plane_stats_workspace_bytes(7680, 4320, 16, 1) > 0   # 8K
 
 
+def test_batch_must_fit_one_dispatch():
+    """A dispatch counts its work-items in 32 bits: at 256 per workgroup the
+    plane-stats launch takes at most (2^32-1)//256 chunks, the CPU-order maps
+    launch (three workgroups per chunk) a third of that.  1x1 frames are one
+    chunk each."""
+    top = (2**32 - 1) // 256
+    assert vqx.plane_stats_workspace_bytes(1, 1, 16, top) == top * 64
+    with pytest.raises(vqx.VqxError) as e:
+        vqx.plane_stats_workspace_bytes(1, 1, 16, top + 1)
+    assert e.value.status == vqx.E_NFRAMES
+    top3 = (2**32 - 1) // (3 * 256)
+    assert vqx.plane_stats_cpu_order_workspace_bytes(1, 1, 16, top3) > 0
+    with pytest.raises(vqx.VqxError) as e:
+        vqx.plane_stats_cpu_order_workspace_bytes(1, 1, 16, top3 + 1)
+    assert e.value.status == vqx.E_NFRAMES
+    # 4K 16-bit frames: 507 chunks each
+    assert vqx.plane_stats_workspace_bytes(3840, 2160, 16, top // 507) > 0
+    with pytest.raises(vqx.VqxError):
+        vqx.plane_stats_workspace_bytes(3840, 2160, 16, top // 507 + 1)
+
+
 class _Buffers:
     """Host memory standing in for device pointers: argument errors must be
     reported before any of it is touched."""

@@ -85,6 +85,17 @@ def test_past53_full_range_bit_identical():
     check(ref, dist, 16, expect_past53=True)
 
 
+def test_odd_dark_samples_past54():
+    """Odd dark squares among bright ones: they tie at 2^53..2^54 (one unit
+    of rounding there) but not past 2^54, where runs holding them round
+    without ties -- a case between the runs whose terms all are multiples of
+    the binade's unit and those with ties."""
+    ref, dist = synth.odd_dark_bright()
+    h, w = ref.shape[1:]
+    assert oracle.exact_frame_sums(ref[0], dist[0])[3] >= 2 * oracle.TWO53
+    check(ref, dist, 16, expect_past53=True)
+
+
 def test_container_values_above_bpc():
     """A 10-bit container holding full-range values passes 2^53 too."""
     ref, dist = synth.uniform_planes(3840, 2160, 1, 10, seed=11, container_max=True)
@@ -103,6 +114,17 @@ def test_unaligned_frame_starts_past53():
     last, in the CPU's order."""
     ref, dist = synth.uniform_planes(4097, 2049, 3, 16, seed=4097, container_max=True)
     check(ref, dist, 16, expect_past53=True)
+
+
+def test_empty_last_chunk_past53():
+    """3779x1305 = 8*(2048*301 + 1) + 3 samples: frame 0 has 2048*301 + 1
+    whole vectors, so a frame takes 302 chunks, but frame 1 starts 3 samples
+    past a vector boundary and has one vector fewer -- its last chunk is
+    empty, after the sums have passed 2^53 (and 2^54)."""
+    w, h = 3779, 1305
+    assert w * h == 8 * (2048 * 301 + 1) + 3
+    ref, dist = synth.uniform_planes(w, h, 3, 16, seed=3779, lo=60000, hi=65535)
+    assert check(ref, dist, 16, expect_past53=True) == 6
 
 
 def test_largest_frame_past53():
