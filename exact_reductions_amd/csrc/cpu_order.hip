@@ -208,6 +208,64 @@ __device__ __forceinline__ RunMap wave_run(RunMap m)
     return w;
 }
 
+// ------------------------------------------------------------ wave scans
+// Inclusive scans in lane order: row_shr steps within each row of 16, then
+// row_bcast:15 (rows 1 and 3) and row_bcast:31 (rows 2 and 3) carry the
+// rows below in.  A lane without a source takes `identity`.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t from_below(uint32_t identity, uint32_t v)
+{
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(static_cast<int>(identity), static_cast<int>(v), CTRL, ROWS, 0xf, false));
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t scan_step64(uint64_t v)
+{
+    return v + (static_cast<uint64_t>(from_below<CTRL, ROWS>(0u, static_cast<uint32_t>(v))) |
+                (static_cast<uint64_t>(from_below<CTRL, ROWS>(0u, static_cast<uint32_t>(v >> 32))) << 32));
+}
+
+__device__ __forceinline__ uint64_t wave_scan64(uint64_t v)
+{
+    v = scan_step64<0x111, 0xf>(v);
+    v = scan_step64<0x112, 0xf>(v);
+    v = scan_step64<0x114, 0xf>(v);
+    v = scan_step64<0x118, 0xf>(v);
+    v = scan_step64<0x142, 0xa>(v);
+    return scan_step64<0x143, 0xc>(v);
+}
+
+__device__ __forceinline__ uint32_t wave_scan32(uint32_t v)
+{
+    v += from_below<0x111, 0xf>(0u, v);
+    v += from_below<0x112, 0xf>(0u, v);
+    v += from_below<0x114, 0xf>(0u, v);
+    v += from_below<0x118, 0xf>(0u, v);
+    v += from_below<0x142, 0xa>(0u, v);
+    return v + from_below<0x143, 0xc>(0u, v);
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ RunMap run_scan_step(const RunMap &m)
+{
+    RunMap o;
+    o.C = from_below<CTRL, ROWS>(0u, m.C);
+    o.P = from_below<CTRL, ROWS>(0x10000u, m.P);  // the identity map
+    return run_then(o, m);
+}
+
+// Lane j gets the composite of the maps of lanes 0..j.
+__device__ __forceinline__ RunMap wave_scan_run(RunMap m)
+{
+    m = run_scan_step<0x111, 0xf>(m);
+    m = run_scan_step<0x112, 0xf>(m);
+    m = run_scan_step<0x114, 0xf>(m);
+    m = run_scan_step<0x118, 0xf>(m);
+    m = run_scan_step<0x142, 0xa>(m);
+    return run_scan_step<0x143, 0xc>(m);
+}
+
 // ---------------------------------------------------------- maps (64-bit)
 // The same two-state map with its increases of m written out: from parity
 // s, m grows by dm_s and ends with parity p_s.
@@ -431,30 +489,27 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(const uint64_t *rec
 // of its kSlabs slabs in the predicted binade e, their maps in binade e + 1
 // (made only where the chunk's exact range reaches 2^(e+1), i.e. where the
 // CPU's sum probably changes binade inside it; flags 0 otherwise), and the
-// slabs' exact totals.  Only chunks past 2^53 get an entry; the walk reads
+// slabs' exact totals.  Only chunks past 2^53 get an entry; the walk uses
 // no other (below 2^53 it adds chunk totals exactly).
 constexpr int kSlabVectors = 256;
 constexpr int kSlabs = kChunkVectors / kSlabVectors;
 constexpr int kLaneVectors = kSlabVectors / 64;  // vectors of a slab per lane
 constexpr int kSlabMapsA = 0;
-constexpr int kSlabMapsB = 3 * kSlabs;
-constexpr int kSlabTotals = 6 * kSlabs;
+constexpr int kSlabMapsB = kSlabMapsA + 3 * kSlabs;
+constexpr int kSlabTotals = kSlabMapsB + 3 * kSlabs;
 constexpr int kEntry = kSlabTotals + kSlabs;
 
 // Work of the maps kernel: one wave per (frame, square sum, group of
-// kGroupChunks chunks); an item is kItemSlabs consecutive slabs.
-constexpr int kItemSlabs = 1;
-constexpr int kItems = kSlabs / kItemSlabs;  // items per chunk
+// kGroupChunks chunks); an item is one slab.
 constexpr int kGroupChunks = 4;
-constexpr int kGroupItems = kGroupChunks * kItems;
+constexpr int kGroupItems = kGroupChunks * kSlabs;
 static_assert(kGroupItems <= 64, "one lane per item");
 
-// The planes' vectors of one item: lane l holds vectors l, 64 + l, 128 + l
-// and 192 + l of each slab (each load instruction reads 1 KB in one piece);
-// bit (4s + j) of ok is set where vector 64j + l of slab s lies inside the
-// chunk.
+// The planes' vectors of one slab: lane l holds vectors l, 64 + l, 128 + l
+// and 192 + l (each load instruction reads 1 KB in one piece); bit j of ok
+// is set where vector 64j + l lies inside the chunk.
 struct ItemData {
-    u32x4 a[kItemSlabs][kLaneVectors], b[kItemSlabs][kLaneVectors];
+    u32x4 a[kLaneVectors], b[kLaneVectors];
     uint32_t ok;
 };
 
@@ -473,7 +528,7 @@ __device__ __forceinline__ void forget(u32x4 (&a)[kLaneVectors], u32x4 (&b)[kLan
     }
 }
 
-// The slabs from sb on of the chunk [cb, ce), cb < ce; a slab may start
+// Slab [sb, sb + 256) of the chunk [cb, ce), cb < ce; the slab may start
 // past ce in the chunk after a frame's last whole vector.
 template <int KK>
 __device__ __forceinline__ void load_item(ItemData &x, const u32x4 *R, const u32x4 *D, int64_t cb, int64_t sb,
@@ -482,13 +537,11 @@ __device__ __forceinline__ void load_item(ItemData &x, const u32x4 *R, const u32
     const int lane = threadIdx.x & 63;
     x.ok = 0;
 #pragma unroll
-    for (int s = 0; s < kItemSlabs; ++s)
-#pragma unroll
-        for (int j = 0; j < kLaneVectors; ++j) {
-            const int64_t v = sb + static_cast<int64_t>(s) * kSlabVectors + 64 * j + lane;
-            load_vector<KK>(R, D, v, v < ce, cb, x.a[s][j], x.b[s][j]);
-            x.ok |= (v < ce ? 1u : 0u) << (kLaneVectors * s + j);
-        }
+    for (int j = 0; j < kLaneVectors; ++j) {
+        const int64_t v = sb + 64 * j + lane;
+        load_vector<KK>(R, D, v, v < ce, cb, x.a[j], x.b[j]);
+        x.ok |= (v < ce ? 1u : 0u) << j;
+    }
 }
 
 // The map, in binade 2^(k+52), of the slab whose vectors the wave's lanes
@@ -531,45 +584,40 @@ __device__ __forceinline__ Map2 slab_map(u32x4 (&a)[kLaneVectors], u32x4 (&b)[kL
     return run_map(slab, T, n, RR, k);
 }
 
-// The slabs of one item (from slab si0 of its chunk on); lane 0 writes
-// their part of the entry.
+// Slab si of its chunk; lane 0 writes its part of the entry.
 template <int KK>
-__device__ __forceinline__ void item_maps(ItemData &x, int si0, int e, bool dual, uint64_t *entry)
+__device__ __forceinline__ void item_maps(ItemData &x, int si, int e, bool dual, uint64_t *entry)
 {
     const int k = e - 52;
 #pragma unroll
-    for (int s = 0; s < kItemSlabs; ++s) {
+    for (int j = 0; j < kLaneVectors; ++j)
+        keep_if<KK>((x.ok >> j) & 1u, x.a[j], x.b[j]);
+    uint64_t tot = 0;
+    uint32_t low_bits = 0;
 #pragma unroll
-        for (int j = 0; j < kLaneVectors; ++j)
-            keep_if<KK>((x.ok >> (kLaneVectors * s + j)) & 1u, x.a[s][j], x.b[s][j]);
-        uint64_t tot = 0;
-        uint32_t low_bits = 0;
+    for (int j = 0; j < kLaneVectors; ++j)
 #pragma unroll
-        for (int j = 0; j < kLaneVectors; ++j)
-#pragma unroll
-            for (int i = 0; i < kTerms; ++i) {
-                const uint32_t t = vector_term<KK>(x.a[s][j], x.b[s][j], i);
-                tot += t;
-                low_bits |= t;
-            }
-        forget<KK>(x.a[s], x.b[s]);
-        const uint64_t T = wave_total64(tot);
-        const Map2 slab = slab_map<KK>(x.a[s], x.b[s], low_bits, T, k);
-        Map2 slab_b;
-        if (dual) {
-            forget<KK>(x.a[s], x.b[s]);
-            slab_b = slab_map<KK>(x.a[s], x.b[s], low_bits, T, k + 1);
+        for (int i = 0; i < kTerms; ++i) {
+            const uint32_t t = vector_term<KK>(x.a[j], x.b[j], i);
+            tot += t;
+            low_bits |= t;
         }
-        const int si = si0 + s;
-        if ((threadIdx.x & 63) == 0) {
-            entry[kSlabMapsA + 3 * si + 0] = slab.dm0;
-            entry[kSlabMapsA + 3 * si + 1] = slab.dm1;
-            entry[kSlabMapsA + 3 * si + 2] = map_flags(slab, e);
-            entry[kSlabMapsB + 3 * si + 0] = slab_b.dm0;
-            entry[kSlabMapsB + 3 * si + 1] = slab_b.dm1;
-            entry[kSlabMapsB + 3 * si + 2] = dual ? map_flags(slab_b, e + 1) : 0;
-            entry[kSlabTotals + si] = T;
-        }
+    forget<KK>(x.a, x.b);
+    const uint64_t T = wave_total64(tot);
+    const Map2 slab = slab_map<KK>(x.a, x.b, low_bits, T, k);
+    Map2 slab_b;
+    if (dual) {
+        forget<KK>(x.a, x.b);
+        slab_b = slab_map<KK>(x.a, x.b, low_bits, T, k + 1);
+    }
+    if ((threadIdx.x & 63) == 0) {
+        entry[kSlabMapsA + 3 * si + 0] = slab.dm0;
+        entry[kSlabMapsA + 3 * si + 1] = slab.dm1;
+        entry[kSlabMapsA + 3 * si + 2] = map_flags(slab, e);
+        entry[kSlabMapsB + 3 * si + 0] = slab_b.dm0;
+        entry[kSlabMapsB + 3 * si + 1] = slab_b.dm1;
+        entry[kSlabMapsB + 3 * si + 2] = dual ? map_flags(slab_b, e + 1) : 0;
+        entry[kSlabTotals + si] = T;
     }
 }
 
@@ -585,8 +633,8 @@ template <int KK>
 __device__ __forceinline__ void group_item(const Group &G, int item, int64_t &cb, int64_t &sb, int64_t &ce,
                                            uint64_t *&entry, int &si)
 {
-    const int c = G.g * kGroupChunks + item / kItems;
-    si = (item % kItems) * kItemSlabs;
+    const int c = G.g * kGroupChunks + item / kSlabs;
+    si = item % kSlabs;
     cb = G.vb + static_cast<int64_t>(c) * kChunkVectors;
     ce = cb + kChunkVectors < G.ve ? cb + kChunkVectors : G.ve;
     sb = cb + static_cast<int64_t>(si) * kSlabVectors;
@@ -604,13 +652,16 @@ __device__ __forceinline__ void group_maps(const Group &G, uint64_t want, int e_
     uint64_t *entry;
     int si;
     ItemData x, y;
+    auto map_item = [&](ItemData &d, int j, int s, uint64_t *en) {
+        item_maps<KK>(d, s, lane_value(e_lane, j), lane_value(dual_lane, j) != 0, en);
+    };
     int j = __builtin_ctzll(want);
     want &= want - 1;
     group_item<KK>(G, j, cb, sb, ce, entry, si);
     load_item<KK>(x, G.R, G.D, cb, sb, ce);
     if constexpr (KK == kSqNoise) {
         for (;;) {
-            item_maps<KK>(x, si, lane_value(e_lane, j), lane_value(dual_lane, j) != 0, entry);
+            map_item(x, j, si, entry);
             if (!want)
                 return;
             j = __builtin_ctzll(want);
@@ -627,23 +678,23 @@ __device__ __forceinline__ void group_maps(const Group &G, uint64_t want, int e_
         uint64_t *entry2;
         for (;;) {
             if (!want) {
-                item_maps<KK>(x, si, lane_value(e_lane, j), lane_value(dual_lane, j) != 0, entry);
+                map_item(x, j, si, entry);
                 return;
             }
             j2 = __builtin_ctzll(want);
             want &= want - 1;
             group_item<KK>(G, j2, cb, sb, ce, entry2, si2);
             load_item<KK>(y, G.R, G.D, cb, sb, ce);
-            item_maps<KK>(x, si, lane_value(e_lane, j), lane_value(dual_lane, j) != 0, entry);
+            map_item(x, j, si, entry);
             if (!want) {
-                item_maps<KK>(y, si2, lane_value(e_lane, j2), lane_value(dual_lane, j2) != 0, entry2);
+                map_item(y, j2, si2, entry2);
                 return;
             }
             j = __builtin_ctzll(want);
             want &= want - 1;
             group_item<KK>(G, j, cb, sb, ce, entry, si);
             load_item<KK>(x, G.R, G.D, cb, sb, ce);
-            item_maps<KK>(y, si2, lane_value(e_lane, j2), lane_value(dual_lane, j2) != 0, entry2);
+            map_item(y, j2, si2, entry2);
         }
     }
 }
@@ -672,9 +723,8 @@ __global__ __launch_bounds__(kThreads) void cpu_order_maps(const void *ref, cons
     const int64_t e0 = G.frame * pixels, e1 = e0 + pixels;
     G.vb = (e0 + V - 1) / V;
     G.ve = e1 / V;
-    // lane j < kGroupItems: item j, i.e. slabs from (j % kItems) *
-    // kItemSlabs on of chunk j / kItems
-    const int c = G.g * kGroupChunks + lane / kItems;
+    // lane j < kGroupItems: item j, i.e. slab j % kSlabs of chunk j / kSlabs
+    const int c = G.g * kGroupChunks + lane / kSlabs;
     bool want = false;
     int e = 0, dual = 0;
     if (lane < kGroupItems && c < chunks) {
@@ -699,74 +749,112 @@ __global__ __launch_bounds__(kThreads) void cpu_order_maps(const void *ref, cons
 // ------------------------------------------------------------------ 4. walk
 // All 64 lanes of the walking wave hold the same S throughout.
 
-// Term by term through one vector.
+// Term by term through the vector that lane j holds.
 template <int KK>
-__device__ __forceinline__ uint64_t walk_vector(uint64_t S, const u32x4 *R, const u32x4 *D, int64_t v)
+__device__ __forceinline__ uint64_t walk_vector(uint64_t S, const u32x4 &a, const u32x4 &b, int j)
 {
-    u32x4 a, b;
-    load_vector<KK>(R, D, v, true, v, a, b);
+    u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
+    if constexpr (KK != kSqDist) {
+        x.x = lane_value(a.x, j);
+        x.y = lane_value(a.y, j);
+        x.z = lane_value(a.z, j);
+        x.w = lane_value(a.w, j);
+    }
+    if constexpr (KK != kSqRef) {
+        y.x = lane_value(b.x, j);
+        y.y = lane_value(b.y, j);
+        y.z = lane_value(b.z, j);
+        y.w = lane_value(b.w, j);
+    }
 #pragma unroll
     for (int i = 0; i < kTerms; ++i)
-        S = cpu_add(S, vector_term<KK>(a, b, i));
+        S = cpu_add(S, vector_term<KK>(x, y, i));
     return S;
 }
 
-// Vectors [sb, se) (at most 256): maps made here, for S's binade and the
-// next, 64 vectors (one per lane) at a time.
+// One row of 64 vectors, vector j in lane j (zero terms past the end, n of
+// them real), each lane with its vector's exact total and maps for binades
+// eA and eA + 1.  Repeatedly: if the rest of the row keeps S below 2^53, or
+// inside its binade, it is added or mapped at once; otherwise prefix scans
+// find the vector in which S crosses 2^53 or leaves its binade, S is moved
+// to just before it, and that one vector is walked term by term.
+template <int KK>
+__device__ __forceinline__ uint64_t walk_row(uint64_t S, const u32x4 &a, const u32x4 &b, int n, uint64_t tot,
+                                             const RunMap &mA, uint32_t rA, const RunMap &mB, uint32_t rB, int eA)
+{
+    const int lane = threadIdx.x;
+    int from = 0;  // vectors before `from` are done
+    while (from < n) {
+        const bool act = lane >= from;
+        const uint64_t t = act ? tot : 0;
+        const uint64_t incl = wave_scan64(t);
+        const uint64_t rest = lane_value64(incl, 63);
+        if (S + rest < kTwo53)
+            return S + rest;
+        int jx;  // the vector in which the sum crosses 2^53 or leaves its binade
+        if (S < kTwo53) {
+            jx = __builtin_ctzll(__ballot(act && S + incl >= kTwo53));
+            S += lane_value64(incl - t, jx);  // exact: every add before it stays below 2^53
+        } else {
+            const int e = binade(S);
+            if (e != eA && e != eA + 1) {  // no maps for this binade
+                for (int j = from; j < n; ++j)
+                    S = walk_vector<KK>(S, a, b, j);
+                return S;
+            }
+            const bool inA = e == eA;
+            const int k = e - 52;
+            const RunMap pre = wave_scan_run(act ? (inA ? mA : mB) : RunMap{});
+            const uint32_t rin = wave_scan32(act ? (inA ? rA : rB) : 0u);
+            const uint64_t terms = act ? static_cast<uint64_t>(lane - from + 1) * kTerms : 0;
+            const Map2 pm = run_map(pre, incl, terms, rin, k);
+            const uint64_t mm = S >> k;
+            const uint64_t m2 = mm + pick(mm, pm.dm0, pm.dm1);  // m after vectors from..lane
+            const uint64_t leaves = __ballot(act && m2 >= kTwo53);
+            if (!leaves)
+                return lane_value64(m2, 63) << k;
+            jx = __builtin_ctzll(leaves);
+            if (jx > from)
+                S = lane_value64(m2, jx - 1) << k;
+        }
+        S = walk_vector<KK>(S, a, b, jx);
+        from = jx + 1;
+    }
+    return S;
+}
+
+// Vectors [sb, se) (at most 256), read at once, one row of 64 at a time
+// with maps made here for S's binade and the next.
 template <int KK>
 __device__ __forceinline__ uint64_t walk_slab(uint64_t S, const u32x4 *R, const u32x4 *D, int64_t sb, int64_t se)
 {
     const int lane = threadIdx.x;
     const int eA = S >= kTwo53 ? binade(S) : 53;
     const int kA = eA - 52;
-    for (int64_t base = sb; base < se; base += 64) {
-        const int64_t v = base + lane;
-        u32x4 a, b;
-        load_vector<KK>(R, D, v, v < se, base, a, b);
-        keep_if<KK>(v < se, a, b);
+    u32x4 a[kLaneVectors], b[kLaneVectors];
+#pragma unroll
+    for (int j = 0; j < kLaneVectors; ++j) {
+        const int64_t v = sb + 64 * j + lane;
+        load_vector<KK>(R, D, v, v < se, sb, a[j], b[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kLaneVectors; ++j) {
+        const int64_t base = sb + 64 * j;
+        if (base >= se)
+            break;
+        keep_if<KK>(base + lane < se, a[j], b[j]);
         RunMap mA, mB;
         uint32_t rA = 0, rB = 0;
         uint64_t tot = 0;
 #pragma unroll
         for (int i = 0; i < kTerms; ++i) {
-            const uint32_t t = vector_term<KK>(a, b, i);
+            const uint32_t t = vector_term<KK>(a[j], b[j], i);
             tot += t;
             run_add(mA, rA, t, kA);
             run_add(mB, rB, t, kA + 1);
         }
-        const uint64_t block = wave_total64(tot);
-        if (S + block < kTwo53) {
-            S += block;
-            continue;
-        }
-        if (S >= kTwo53) {
-            const int e = binade(S);
-            if (e == eA || e == eA + 1) {
-                const bool inA = e == eA;
-                const Map2 comp = run_map(wave_run(inA ? mA : mB), block, 64 * kTerms,
-                                          wave_total32(inA ? rA : rB), e - 52);
-                if (map_apply(S, comp, e))
-                    continue;
-            }
-        }
         const int n = se - base < 64 ? static_cast<int>(se - base) : 64;
-        for (int j = 0; j < n; ++j) {
-            const uint64_t tj = lane_value64(tot, j);
-            if (S + tj < kTwo53) {
-                S += tj;
-                continue;
-            }
-            RunMap x;
-            x.C = lane_value(mA.C, j);
-            x.P = lane_value(mA.P, j);
-            if (map_apply(S, run_map(x, tj, kTerms, lane_value(rA, j), kA), eA))
-                continue;
-            x.C = lane_value(mB.C, j);
-            x.P = lane_value(mB.P, j);
-            if (map_apply(S, run_map(x, tj, kTerms, lane_value(rB, j), kA + 1), eA + 1))
-                continue;
-            S = walk_vector<KK>(S, R, D, base + j);
-        }
+        S = walk_row<KK>(S, a[j], b[j], n, tot, mA, rA, mB, rB, eA);
     }
     return S;
 }
@@ -809,29 +897,44 @@ __device__ __forceinline__ uint64_t walk_chunk(uint64_t S, const u32x4 *R, const
     return S;
 }
 
-// The vectors' part of chunk c's record (chunk 0's also holds the head and
-// tail samples).
-__device__ __forceinline__ uint64_t chunk_total(const uint64_t *rec, int64_t frame, int chunks, int c, int kk,
-                                                uint64_t head_tail)
+// Chunk c of a frame as the walk sees it: the vectors' part of its record
+// (chunk 0's also holds the head and tail samples) and its map, composed
+// from its slab maps (flags 0 unless all are valid and for one binade).
+// Every lane reads (chunk chunks - 1 stands in past the end), so that no
+// branch holds the reads back from the waits for them; the map fields hold
+// whatever the workspace held for chunks without an entry (empty ones, and
+// those before the exact sum reaches 2^53), and the walk uses them only for
+// non-empty chunks past 2^53.
+struct ChunkView {
+    uint64_t T, dm[kSlabs][2], fl[kSlabs];
+};
+
+__device__ __forceinline__ ChunkView load_chunk(const uint64_t *rec, const uint64_t *entries, int64_t frame,
+                                                int chunks, int c, int kk, uint64_t head_tail)
 {
-    if (c >= chunks)
-        return 0;
-    return rec[(frame * chunks + c) * kRecordStride + record_field(kk)] - (c == 0 ? head_tail : 0);
+    const int cc = c < chunks ? c : chunks - 1;
+    const uint64_t *entry = entries + static_cast<int64_t>(cc) * kSquares * kEntry;
+    ChunkView x;
+    const uint64_t r = rec[(frame * chunks + cc) * kRecordStride + record_field(kk)];
+    x.T = c < chunks ? r - (c == 0 ? head_tail : 0) : 0;
+#pragma unroll
+    for (int j = 0; j < kSlabs; ++j) {
+        x.dm[j][0] = entry[kSlabMapsA + 3 * j];
+        x.dm[j][1] = entry[kSlabMapsA + 3 * j + 1];
+        x.fl[j] = entry[kSlabMapsA + 3 * j + 2];
+    }
+    return x;
 }
 
-// Chunk c's map, composed from its slab maps; flags 0 unless all of them
-// are valid and for one binade.  Read only for non-empty chunks past 2^53,
-// whose entries the maps kernel has written.
-__device__ __forceinline__ Map2 chunk_map(const uint64_t *entry, uint64_t &flags)
+__device__ __forceinline__ Map2 chunk_map(const ChunkView &x, uint64_t &flags)
 {
     Map2 m;
-    const uint64_t key = entry[kSlabMapsA + 2] & 0xffffu;  // valid bit and binade of slab 0
+    const uint64_t key = x.fl[0] & 0xffffu;  // valid bit and binade of slab 0
     bool ok = (key & 1u) != 0;
 #pragma unroll
     for (int j = 0; j < kSlabs; ++j) {
-        const uint64_t fl = entry[kSlabMapsA + 3 * j + 2];
-        m = map_then(m, map_from(entry[kSlabMapsA + 3 * j], entry[kSlabMapsA + 3 * j + 1], fl));
-        ok = ok && (fl & 0xffffu) == key;
+        m = map_then(m, map_from(x.dm[j][0], x.dm[j][1], x.fl[j]));
+        ok = ok && (x.fl[j] & 0xffffu) == key;
     }
     flags = ok ? map_flags(m, flags_binade(key)) : 0;
     return m;
@@ -858,25 +961,27 @@ __device__ __forceinline__ void walk_frame(const void *ref, const void *dist, in
     const u32x4 *R = static_cast<const u32x4 *>(ref);
     const u32x4 *D = static_cast<const u32x4 *>(dist);
     const uint64_t *entries = maps + (frame * chunks * kSquares + KK) * kEntry;  // chunk c: + c * kSquares * kEntry
-    uint64_t T = chunk_total(rec, frame, chunks, lane, KK, hsum + tsum);
+    ChunkView cur = load_chunk(rec, entries, frame, chunks, lane, KK, hsum + tsum);
     for (int base = 0; base < chunks; base += 64) {
-        // one chunk per lane; the next block's totals are read meanwhile
-        const uint64_t T_next = chunk_total(rec, frame, chunks, base + 64 + lane, KK, 0);
+        // one chunk per lane; the next block is read meanwhile
+        const ChunkView next = load_chunk(rec, entries, frame, chunks, base + 64 + lane, KK, 0);
         const int c = base + lane;
-        const uint64_t block = wave_total64(T);
+        const uint64_t block = wave_total64(cur.T);
         if (S + block < kTwo53) {
             S += block;
-            T = T_next;
+            cur = next;
             continue;
         }
         // past 2^53 within this block: every non-empty chunk from the one
         // where the exact sum gets there on has its slab maps; an empty
         // chunk (the last one of a frame may be) adds nothing
         const bool empty = c >= chunks || vb + static_cast<int64_t>(c) * kChunkVectors >= ve;
-        uint64_t flags = 0;
-        Map2 cm;
-        if (!empty)
-            cm = chunk_map(entries + static_cast<int64_t>(c) * kSquares * kEntry, flags);
+        uint64_t flags;
+        Map2 cm = chunk_map(cur, flags);
+        if (empty) {
+            cm = Map2{};
+            flags = 0;
+        }
         bool done = false;
         if (S >= kTwo53) {
             const int e = binade(S);
@@ -890,7 +995,7 @@ __device__ __forceinline__ void walk_frame(const void *ref, const void *dist, in
                 const int64_t ce = cb + kChunkVectors < ve ? cb + kChunkVectors : ve;
                 if (cb >= ce)
                     continue;
-                const uint64_t Tj = lane_value64(T, j);
+                const uint64_t Tj = lane_value64(cur.T, j);
                 if (S + Tj < kTwo53) {
                     S += Tj;
                     continue;
@@ -902,7 +1007,7 @@ __device__ __forceinline__ void walk_frame(const void *ref, const void *dist, in
                 S = walk_chunk<KK>(S, R, D, entries + static_cast<int64_t>(base + j) * kSquares * kEntry, cb, ce);
             }
         }
-        T = T_next;
+        cur = next;
     }
     // the tail comes last
     for (int j = 0; j < tail; ++j)
