@@ -21,7 +21,16 @@ timed batch must match the oracle (exact integers; bit-identical doubles
 below 2^53 units; within the float_moment bound past it) or nothing is
 reported.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5]
+``--mode cpu-order`` measures the other entry point instead: each step also
+reproduces the CPU's own rounding past 2^53 (vqx_plane_stats_batch_cpu_order_ws:
+stage 1, stage 2, the prefix scan, the maps pass over what lies past 2^53,
+the walk), and the host concludes those sums.  Its roofline is the whole
+step against the bytes it must read (both planes once, and again the part
+of each plane past 2^53), timed with HIP events around each group of steps;
+the gate is bit-identity with the oracle's sequential doubles on every
+frame.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5] [--mode exact|cpu-order]
 """
 
 from __future__ import annotations
@@ -42,8 +51,13 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published peak
 METRIC = "frames/s and HBM GB/s (fraction of peak) at 3840x2160 16-bit, bit-exact"
+METRIC_CPU_ORDER = ("frames/s with the CPU's own rounding past 2^53 (sums bit-identical to the "
+                    "sequential doubles) at 3840x2160 16-bit")
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCE = os.path.join(ROOT, "exact_reductions_amd", "csrc", "plane_stats.hip")
+CSRC = os.path.join(ROOT, "exact_reductions_amd", "csrc")
+KERNEL_SOURCE = os.path.join(CSRC, "plane_stats.hip")
+CPU_ORDER_SOURCES = [os.path.join(CSRC, f) for f in ("plane_stats.hip", "cpu_order.hip")]
+UNIT_POWER = (2, 1, 1, 2, 2)  # noise, ref1, dist1, ref2, dist2: units 1/s^power
 
 
 def parse_args(argv=None):
@@ -60,18 +74,23 @@ def parse_args(argv=None):
                    help="skip the oracle leg (and with it the parity gate); for profiler runs")
     p.add_argument("--input-cache", default=None, metavar="DIR",
                    help="keep the generated batch as .npy files in DIR and reuse them")
+    p.add_argument("--mode", choices=("exact", "cpu-order"), default="exact",
+                   help="exact: the exact sums (default); cpu-order: also the CPU's rounding past 2^53")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="after the timed steps, run 3 elementwise kernels that each read and "
                         "write MIB MiB (the known-size kernel that scales the HBM counters)")
     return p.parse_args(argv)
 
 
-def kernel_source_sha256() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def kernel_source_sha256(paths=(KERNEL_SOURCE,)) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
-def stored_traffic(kernel: str, workload: str):
+def stored_traffic(kernel: str, workload: str, sources=(KERNEL_SOURCE,)):
     """HBM bytes per launch from the committed counter summary, or None when
     there is none or the kernel source changed since it was taken."""
     path = os.path.join(PROFILES, f"{kernel}_{workload}_hbm_traffic.txt")
@@ -83,7 +102,7 @@ def stored_traffic(kernel: str, workload: str):
             m = re.match(r"^([A-Za-z0-9_]+):\s*(\S+)", line)
             if m:
                 fields[m.group(1)] = m.group(2)
-    if fields.get("kernel_source_sha256") != kernel_source_sha256():
+    if fields.get("kernel_source_sha256") != kernel_source_sha256(sources):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -150,23 +169,25 @@ def cpu_threads() -> int:
     return max(1, min(16, n))
 
 
-def cpu_baseline_and_gate(ref, dist, bpc, noise, moments, bytes_per_frame, concl):
-    """Time the CPU oracle on a bounded sample and check the device's last
-    batch, and the library's conclusion of it, against the oracle.  Returns
-    (cpu_baseline dict, parity dict)."""
+def _oracle_o1_o2(ref, dist, bpc, threads):
     from concurrent.futures import ThreadPoolExecutor
-
-    import numpy as np
 
     import oracle
 
-    nframes, h, w = ref.shape
-    threads = cpu_threads()
-
-    # parity of the timed batch: every frame, both oracles
+    n = ref.shape[0]
     with ThreadPoolExecutor(threads) as ex:
-        o2 = list(ex.map(lambda f: oracle.exact_frame_sums(ref[f], dist[f]), range(nframes)))
-        o1 = list(ex.map(lambda f: oracle.seq_frame_sums(ref[f], dist[f], bpc), range(nframes)))
+        o2 = list(ex.map(lambda f: oracle.exact_frame_sums(ref[f], dist[f]), range(n)))
+        o1 = list(ex.map(lambda f: oracle.seq_frame_sums(ref[f], dist[f], bpc), range(n)))
+    return o1, o2
+
+
+def gate_exact(ref, dist, bpc, noise, moments, concl, threads):
+    """The device's exact sums of the last batch, and the library's
+    conclusion of them, against both oracles."""
+    import oracle
+
+    nframes, h, w = ref.shape
+    o1, o2 = _oracle_o1_o2(ref, dist, bpc, threads)
     failures = []
     past53 = 0
     for f in range(nframes):
@@ -183,8 +204,50 @@ def cpu_baseline_and_gate(ref, dist, bpc, noise, moments, bytes_per_frame, concl
               "rule": "exact integers; doubles bit-identical below 2^53 units; bound past it"}
     if failures:
         parity["first_failure"] = str(failures[0])
+    return parity
 
-    # timing: the oracle as it stands, one frame per task, on `threads` threads
+
+def gate_cpu_order(ref, dist, bpc, exact, cpu, concl, threads):
+    """The last batch of the CPU-order mode: exact sums equal the exact
+    oracle, the CPU-order sums equal the CPU's sequential doubles bit for bit
+    on every frame, and the library's conclusion of them the CPU's scores."""
+    import oracle
+
+    nframes, h, w = ref.shape
+    o1, o2 = _oracle_o1_o2(ref, dist, bpc, threads)
+    s = 1 << (bpc - 8)
+    failures = []
+    past53 = 0
+    for f in range(nframes):
+        fails = []
+        if [int(v) for v in exact[f]] != [int(v) for v in o2[f]]:
+            fails.append("exact sums")
+        for k in range(5):
+            want = float(o1[f][k]) * float(s ** UNIT_POWER[k])
+            if float(cpu[f][k]) != want or int(cpu[f][k]) != int(want):
+                fails.append(f"output {k}: device {int(cpu[f][k])} CPU {int(want)}")
+        want_concl = oracle.conclude_from_doubles(o1[f], w, h)
+        if [concl[f, 0]] + list(concl[f, 2:]) != list(want_concl):
+            fails.append("conclusion")
+        if fails:
+            failures.append((f, fails))
+        past53 += sum(1 for v in o2[f] if int(v) >= oracle.TWO53)
+    parity = {"frames": nframes, "failures": len(failures), "outputs_past_2^53": past53,
+              "rule": "exact integers; the CPU-order sums bit-identical to the sequential doubles "
+                      "on every frame and output"}
+    if failures:
+        parity["first_failure"] = str(failures[0])
+    return parity
+
+
+def time_oracle(ref, dist, bpc, bytes_per_frame, threads):
+    """The oracle as it stands (the CPU's sequential double loop), one frame
+    per task on `threads` threads, over a bounded sample of the batch."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    nframes, h, w = ref.shape
     t = time.perf_counter()
     oracle.seq_frame_sums(ref[0], dist[0], bpc)
     one = max(time.perf_counter() - t, 1e-6)
@@ -195,14 +258,48 @@ def cpu_baseline_and_gate(ref, dist, bpc, noise, moments, bytes_per_frame, concl
         list(ex.map(lambda f: oracle.seq_frame_sums(ref[f], dist[f], bpc), work))
     wall = time.perf_counter() - t
     fps = len(work) / wall
-    base = {
+    return {
         "value": round(fps, 3), "unit": "frames/s", "cores": threads, "kind": "oracle",
         "sample": f"{passes} passes over the {nframes} frames of the batch ({len(work)} frames of "
                   f"{w}x{h} at {bpc} bits), the C sequential-double oracle, one frame per task",
         "gbs": round(fps * bytes_per_frame / 1e9, 3),
         "single_thread_frames_per_s": round(1.0 / one, 3),
     }
-    return base, parity
+
+
+def past53_bytes(ref, dist, bpc):
+    """Bytes the CPU-order maps pass must read for this batch: for each frame
+    and square sum whose exact total reaches 2^53 units, the planes' 16-byte
+    vectors from the 2048-vector chunk in which the running sum gets there
+    to the frame's last whole vector (one plane for a sum of squares of one
+    plane, both for the noise).  Plain numpy over the batch (float32 squares
+    read back as integers); no part of the library or the oracle."""
+    import numpy as np
+
+    if bpc == 8:
+        return 0
+    nframes, h, w = ref.shape
+    pixels = w * h
+    table = (np.arange(65536, dtype=np.float32) ** 2).astype(np.uint64)
+    total = 0
+    for f in range(nframes):
+        e0, e1 = f * pixels, (f + 1) * pixels
+        vb, ve = -(-e0 // 8), e1 // 8
+        if vb >= ve:
+            continue
+        head = vb * 8 - e0
+        r = ref[f].reshape(-1)
+        d = dist[f].reshape(-1)
+        diff = np.abs(r.astype(np.float32) - d.astype(np.float32))
+        kinds = ((np.rint(diff * diff).astype(np.uint64), 2), (table[r], 1), (table[d], 1))
+        for terms, planes in kinds:
+            cs = np.cumsum(terms, dtype=np.uint64)
+            if int(cs[-1]) < (1 << 53):
+                continue
+            i0 = int(np.searchsorted(cs, np.uint64(1 << 53), side="left"))
+            c_first = max(0, i0 - head) // (8 * 2048)
+            total += (ve - (vb + c_first * 2048)) * 16 * planes
+    return total
 
 
 def load_or_generate(number, cache_dir):
@@ -267,22 +364,37 @@ def main(argv=None):
     group = 8
     depth = 4  # groups in flight: ~5 ms of queued work absorbs host hiccups
     nslots = depth * group
-    sums = torch.zeros((nslots, 5 * nframes), dtype=torch.int64, pin_memory=True)
+    cpu_order = args.mode == "cpu-order"
+    # per slot: the exact sums {noise[F], moments[F][4]}, and in the
+    # CPU-order mode the CPU's sums after them in the same layout
+    width = (10 if cpu_order else 5) * nframes
+    sums = torch.zeros((nslots, width), dtype=torch.int64, pin_memory=True)
     noise = [sums[s, :nframes] for s in range(nslots)]
-    moments = [sums[s, nframes:].view(nframes, 4) for s in range(nslots)]
+    moments = [sums[s, nframes:5 * nframes].view(nframes, 4) for s in range(nslots)]
+    cnoise = [sums[s, 5 * nframes:6 * nframes] for s in range(nslots)] if cpu_order else None
+    cmoments = [sums[s, 6 * nframes:].view(nframes, 4) for s in range(nslots)] if cpu_order else None
     stream = torch.cuda.current_stream(dev)
     st = stream.cuda_stream
-    ws_bytes = vqx.plane_stats_workspace_bytes(w, h, bpc, nframes)
+    if cpu_order:
+        ws_bytes = vqx.plane_stats_cpu_order_workspace_bytes(w, h, bpc, nframes)
+    else:
+        ws_bytes = vqx.plane_stats_workspace_bytes(w, h, bpc, nframes)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     hip = HipEvents(vqx.hip_runtime())
     L = vqx.lib()
     noise_dev = [hip.device_pointer(t.data_ptr()) for t in noise]
     moments_dev = [hip.device_pointer(t.data_ptr()) for t in moments]
+    if cpu_order:
+        cnoise_dev = [hip.device_pointer(t.data_ptr()) for t in cnoise]
+        cmoments_dev = [hip.device_pointer(t.data_ptr()) for t in cmoments]
     total = args.warmup + args.steps
-    timed_every = 1
-    ev_begin = {i: hip.create() for i in range(0, total, timed_every)}
+    # exact mode: stage 1 of every step stamps its own events; CPU-order
+    # mode: events around each group of steps
+    ev_begin = {i: hip.create() for i in range(total)} if not cpu_order else {}
     ev_end = {i: hip.create() for i in ev_begin}
-    ev_done = [hip.create() for _ in range((total + group - 1) // group + 1)]
+    ngroups = (total + group - 1) // group + 1
+    ev_start = [hip.create() for _ in range(ngroups)] if cpu_order else []
+    ev_done = [hip.create() for _ in range(ngroups)]
     torch.cuda.synchronize()
 
     # The host conclusion allocates nothing: libvqx concludes from the pinned
@@ -293,18 +405,24 @@ def main(argv=None):
     sums_np = sums.numpy()
     concl = np.zeros((nslots, nframes, 6), dtype=np.float64)
     concl_ptr = [concl[s].ctypes.data for s in range(nslots)]
-    noise_ptr = [noise[s].data_ptr() for s in range(nslots)]
-    moments_ptr = [moments[s].data_ptr() for s in range(nslots)]
-    history = np.zeros((total, 5 * nframes), dtype=np.int64)
+    # the sums concluded: the exact ones, or in the CPU-order mode the CPU's
+    noise_ptr = [(cnoise if cpu_order else noise)[s].data_ptr() for s in range(nslots)]
+    moments_ptr = [(cmoments if cpu_order else moments)[s].data_ptr() for s in range(nslots)]
+    history = np.zeros((total, width), dtype=np.int64)
 
     def enqueue(i):
         s = i % nslots
         r, d = bufs[i % 2]
-        rc = L.vqx_plane_stats_batch_ws_timed(r.data_ptr(), d.data_ptr(), w, h, bpc, nframes,
-                                              noise_dev[s], moments_dev[s], ws.data_ptr(), ws_bytes,
-                                              st, ev_begin.get(i), ev_end.get(i))
+        if cpu_order:
+            rc = L.vqx_plane_stats_batch_cpu_order_ws(r.data_ptr(), d.data_ptr(), w, h, bpc, nframes,
+                                                      noise_dev[s], moments_dev[s], cnoise_dev[s],
+                                                      cmoments_dev[s], ws.data_ptr(), ws_bytes, st)
+        else:
+            rc = L.vqx_plane_stats_batch_ws_timed(r.data_ptr(), d.data_ptr(), w, h, bpc, nframes,
+                                                  noise_dev[s], moments_dev[s], ws.data_ptr(), ws_bytes,
+                                                  st, ev_begin.get(i), ev_end.get(i))
         if rc != 0:
-            raise vqx.VqxError(rc, "vqx_plane_stats_batch_ws_timed")
+            raise vqx.VqxError(rc, "libvqx entry point")
 
     def conclude(steps, done):
         hip.synchronize(done)
@@ -324,6 +442,8 @@ def main(argv=None):
         for steps in groups:
             if len(pending) == depth:
                 conclude(*pending.pop(0))
+            if cpu_order:
+                hip.record(ev_start[steps[0] // group], st)
             for i in steps:
                 enqueue(i)
             done = ev_done[steps[0] // group]
@@ -346,8 +466,16 @@ def main(argv=None):
         if gc_was_enabled:
             gc.enable()
 
-    stage1_ms = [hip.elapsed_ms(ev_begin[i], ev_end[i]) for i in ev_begin if i >= args.warmup]
-    for ev in list(ev_begin.values()) + list(ev_end.values()) + ev_done:
+    if cpu_order:
+        # device time per step, from the events around each timed group
+        step_ms = []
+        for a in range(args.warmup, total, group):
+            g = a // group
+            n = min(group, total - a)
+            step_ms += [hip.elapsed_ms(ev_start[g], ev_done[g]) / n] * n
+    else:
+        step_ms = [hip.elapsed_ms(ev_begin[i], ev_end[i]) for i in ev_begin if i >= args.warmup]
+    for ev in list(ev_begin.values()) + list(ev_end.values()) + ev_start + ev_done:
         hip.destroy(ev)
 
     # every step must have produced the same sums
@@ -356,7 +484,7 @@ def main(argv=None):
         print(f"step {bad} differs from the last step", file=sys.stderr)
         return 1
     last_noise = history[total - 1, :nframes]
-    last_moments = history[total - 1, nframes:].reshape(nframes, 4)
+    last_moments = history[total - 1, nframes:5 * nframes].reshape(nframes, 4)
     # the library's conclusion of the last step, from the same sums
     last_concl = concl[(total - 1) % nslots].copy()
 
@@ -372,14 +500,20 @@ def main(argv=None):
 
     bytes_per_frame = wl.bytes_per_frame
     bytes_per_launch = bytes_per_frame * nframes
-    mean_stage1 = statistics.fmean(stage1_ms)
-    achieved = bytes_per_launch / (mean_stage1 * 1e-3) / 1e9
-    kernel = "stage1_u8" if bpc == 8 else "stage1_u16"
+    mean_ms = statistics.fmean(step_ms)
     wname = f"{w}x{h}x{nframes}_{bpc}bit"
-    traffic = stored_traffic(kernel, wname)
+    if cpu_order:
+        kernel = "cpu_order_step"
+        alg_bytes = bytes_per_launch + past53_bytes(ref_np, dist_np, bpc)
+        traffic = stored_traffic(kernel, wname, CPU_ORDER_SOURCES)
+    else:
+        kernel = "stage1_u8" if bpc == 8 else "stage1_u16"
+        alg_bytes = bytes_per_launch
+        traffic = stored_traffic(kernel, wname)
+    achieved = alg_bytes / (mean_ms * 1e-3) / 1e9
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC_CPU_ORDER if cpu_order else METRIC,
         "value": round(args.steps * nframes / elapsed, 1),
         "unit": "frames/s",
         "n_gpus": 1,
@@ -394,29 +528,37 @@ def main(argv=None):
         "config": {
             "workload": f"{w}x{h} {bpc}-bit luma pair, {nframes} frames, "
                         f"{'uint8' if bpc == 8 else 'uint16'} ({wl.recipe})",
-            "w": w, "h": h, "bpc": bpc, "nframes": nframes,
+            "w": w, "h": h, "bpc": bpc, "nframes": nframes, "mode": args.mode,
             "bytes_per_step": bytes_per_launch,
             "hbm_gbs_whole_step": round(bytes_per_launch * args.steps / elapsed / 1e9, 1),
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": kernel,
+            "kernel": (kernel if not cpu_order else
+                       "cpu_order_step (stage1_u16, stage2_combine, cpu_order_prefix, cpu_order_maps, "
+                       "cpu_order_walk)"),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel_us_mean": round(mean_stage1 * 1e3, 2),
-            "kernel_us_median": round(statistics.median(stage1_ms) * 1e3, 2),
-            "algorithmic_bytes_per_launch": bytes_per_launch,
+            "kernel_us_mean": round(mean_ms * 1e3, 2),
+            "kernel_us_median": round(statistics.median(step_ms) * 1e3, 2),
+            "algorithmic_bytes_per_launch": alg_bytes,
         },
         "generation_s": round(t_gen, 1),
     }
 
     if not args.no_cpu_baseline:
-        base, parity = cpu_baseline_and_gate(ref_np, dist_np, bpc, last_noise, last_moments,
-                                             bytes_per_frame, last_concl)
-        out["cpu_baseline"] = base
+        threads = cpu_threads()
+        if cpu_order:
+            last = history[total - 1]
+            exact = np.concatenate([last[:nframes, None], last[nframes:5 * nframes].reshape(nframes, 4)], 1)
+            cpu = np.concatenate([last[5 * nframes:6 * nframes, None], last[6 * nframes:].reshape(nframes, 4)], 1)
+            parity = gate_cpu_order(ref_np, dist_np, bpc, exact, cpu, last_concl, threads)
+        else:
+            parity = gate_exact(ref_np, dist_np, bpc, last_noise, last_moments, last_concl, threads)
+        out["cpu_baseline"] = time_oracle(ref_np, dist_np, bpc, bytes_per_frame, threads)
         out["parity"] = parity
         if parity["failures"]:
             print(json.dumps({"error": "timed batch does not match the oracle", "parity": parity}),

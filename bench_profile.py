@@ -13,10 +13,12 @@ Runs, each as a child process under its own time limit:
    stage-1 reading into HBM bytes.
 
 Writes ``<kernel>_<w>x<h>x<frames>_kernel_trace.txt`` and
-``..._hbm_traffic.txt`` into ``--out``.  This script never touches the GPU
-itself.
+``..._hbm_traffic.txt`` into ``--out``.  With ``--mode cpu-order`` the
+kernel is the whole CPU-order step (``cpu_order_step``): the trace lists
+each of its kernels, and the traffic sums their counters per step.  This
+script never touches the GPU itself.
 
-    python bench_profile.py --workload 5 --out gpurun_out/profiles
+    python bench_profile.py --workload 5 [--mode cpu-order] --out gpurun_out/profiles
 """
 
 from __future__ import annotations
@@ -33,7 +35,10 @@ import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCE = os.path.join(ROOT, "exact_reductions_amd", "csrc", "plane_stats.hip")
+CSRC = os.path.join(ROOT, "exact_reductions_amd", "csrc")
+KERNEL_SOURCE = os.path.join(CSRC, "plane_stats.hip")
+CPU_ORDER_SOURCES = [os.path.join(CSRC, f) for f in ("plane_stats.hip", "cpu_order.hip")]
+CPU_ORDER_KERNELS = ("stage1_u16", "stage2_combine", "cpu_order_prefix", "cpu_order_maps", "cpu_order_walk")
 COPY_MIB = 1024
 WARMUP = 300
 
@@ -59,7 +64,8 @@ def rows(path):
 
 
 def short(name: str) -> str:
-    for k in ("stage1_u16", "stage1_u8", "stage2_combine", "bitwise_not"):
+    for k in ("stage1_u16", "stage1_u8", "stage2_combine", "bitwise_not", "cpu_order_prefix",
+              "cpu_order_maps", "cpu_order_walk"):
         if k in name:
             return k
     return name.split("(")[0][-60:]
@@ -72,19 +78,31 @@ def main(argv=None):
     p.add_argument("--work", default=os.path.join(ROOT, "gpurun_out", "rocprof"))
     p.add_argument("--cache", default="/tmp/vqx_inputs")
     p.add_argument("--steps", type=int, default=500)
+    p.add_argument("--mode", choices=("exact", "cpu-order"), default="exact")
     args = p.parse_args(argv)
+    cpu_order = args.mode == "cpu-order"
 
     sys.path.insert(0, ROOT)
     import synth
     wl = synth.WORKLOADS[args.workload]
-    kernel = "stage1_u8" if wl.bpc == 8 else "stage1_u16"
+    kernel = "cpu_order_step" if cpu_order else ("stage1_u8" if wl.bpc == 8 else "stage1_u16")
+    step_kernels = CPU_ORDER_KERNELS if cpu_order else (kernel,)
     wname = f"{wl.w}x{wl.h}x{wl.nframes}_{wl.bpc}bit"
     os.makedirs(args.out, exist_ok=True)
     os.makedirs(args.work, exist_ok=True)
     bench = ["python3", os.path.join(ROOT, "bench.py"), "--workload", str(args.workload),
-             "--no-cpu-baseline", "--input-cache", args.cache]
-    with open(KERNEL_SOURCE, "rb") as f:
-        src_sha = hashlib.sha256(f.read()).hexdigest()
+             "--no-cpu-baseline", "--input-cache", args.cache, "--mode", args.mode]
+    h = hashlib.sha256()
+    for path in (CPU_ORDER_SOURCES if cpu_order else [KERNEL_SOURCE]):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    src_sha = h.hexdigest()
+    alg = wl.bytes_per_frame * wl.nframes
+    if cpu_order:
+        import bench as bench_mod
+        ref, dist = synth.generate(args.workload)
+        alg += bench_mod.past53_bytes(ref, dist, wl.bpc)
+        del ref, dist
 
     # 0. make the input cache outside the profiler
     rc = sh(bench + ["--steps", "1", "--warmup", "0"], 600, os.path.join(args.work, "prime.log"))
@@ -109,32 +127,29 @@ def main(argv=None):
         "",
         f"{'kernel':<18} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_us':>12}",
     ]
-    stage1_avg = None
     for r in stats:
         name = short(r.get("Name", r.get("KernelName", "?")))
-        calls = int(r["Calls"])
-        avg = float(r["AverageNs"]) / 1e3
-        lines.append(f"{name:<18} {calls:>6} {avg:>10.2f} {float(r['MinNs']) / 1e3:>10.2f} "
-                     f"{float(r['MaxNs']) / 1e3:>10.2f} {float(r['TotalDurationNs']) / 1e3:>12.1f}")
-        if name == kernel:
-            stage1_avg = avg
-    # the same kernel's dispatches in launch order, from the trace; the bench
+        lines.append(f"{name:<18} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
+                     f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f} "
+                     f"{float(r['TotalDurationNs']) / 1e3:>12.1f}")
+    # each kernel's dispatches in launch order, from the trace; the bench
     # times the dispatches after its warm-up ones
     trace = rows(find(tdir, "kernel_trace.csv"))
-    disp = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in trace
-                  if short(r["Kernel_Name"]) == kernel)
-    timed = [(e - b) / 1e3 for b, e in disp[WARMUP:]]
-    if timed:
-        lines += ["", f"dispatches: {len(disp)} (the first {WARMUP} are the bench's warm-up)",
-                  f"kernel_avg_us_timed_dispatches: {statistics.fmean(timed):.2f}",
-                  f"kernel_median_us_timed_dispatches: {statistics.median(timed):.2f}"]
-        stage1_avg_all = stage1_avg
-        stage1_avg = statistics.fmean(timed)
-    if stage1_avg:
-        gbs = wl.bytes_per_frame * wl.nframes / (stage1_avg * 1e-6) / 1e9
-        lines += [f"kernel_avg_us_all_dispatches: {stage1_avg_all:.2f}" if timed else "",
-                  f"kernel_avg_us: {stage1_avg:.2f}",
-                  f"kernel_algorithmic_bytes_per_launch: {wl.bytes_per_frame * wl.nframes}",
+    timed_avg = {}
+    for kname in step_kernels:
+        disp = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in trace
+                      if short(r["Kernel_Name"]) == kname)
+        timed = [(e - b) / 1e3 for b, e in disp[WARMUP:]]
+        if timed:
+            timed_avg[kname] = statistics.fmean(timed)
+            lines += ["", f"{kname}: dispatches {len(disp)} (the first {WARMUP} are the bench's warm-up)",
+                      f"{kname}_avg_us_timed_dispatches: {statistics.fmean(timed):.2f}",
+                      f"{kname}_median_us_timed_dispatches: {statistics.median(timed):.2f}"]
+    if len(timed_avg) == len(step_kernels):
+        step_us = sum(timed_avg.values())
+        gbs = alg / (step_us * 1e-6) / 1e9
+        lines += ["", f"kernel_avg_us: {step_us:.2f}" + ("  (sum of the step's kernels)" if cpu_order else ""),
+                  f"kernel_algorithmic_bytes_per_launch: {alg}",
                   f"kernel_achieved_GBps: {gbs:.1f}", f"kernel_frac_of_8000_GBps: {gbs / 8000:.4f}"]
     if bench_line:
         lines += ["", "bench line of the same run:", bench_line[-1]]
@@ -162,7 +177,8 @@ def main(argv=None):
 
     copy_bytes = COPY_MIB * (1 << 20)
     out = [
-        f"# HBM traffic of {kernel}, {wl.name} ({wname}), from rocprofv3 counters",
+        f"# HBM traffic of {kernel}, {wl.name} ({wname}), from rocprofv3 counters"
+        + (f" (summed over {', '.join(step_kernels)})" if cpu_order else ""),
         f"command_fetch: cd <repo> && {' '.join(shlex.quote(c) for c in cmds['FETCH_SIZE']).replace(ROOT + '/', '')}",
         f"command_write: cd <repo> && {' '.join(shlex.quote(c) for c in cmds['WRITE_SIZE']).replace(ROOT + '/', '')}",
         f"date_utc: {time.strftime('%Y-%m-%dT%H:%M:%SZ', time.gmtime())}",
@@ -181,13 +197,13 @@ def main(argv=None):
         return statistics.fmean(vals[-3:]) if vals else None
     fetch_copy = copy_reading(readings["FETCH_SIZE"])
     write_copy = copy_reading(readings["WRITE_SIZE"])
-    f_k = readings["FETCH_SIZE"].get(kernel)
-    w_k = readings["WRITE_SIZE"].get(kernel)
-    if fetch_copy and write_copy and f_k and w_k:
+    # per step: the mean per dispatch of each of the step's kernels, summed
+    have = all(readings[c].get(k) for c in ("FETCH_SIZE", "WRITE_SIZE") for k in step_kernels)
+    if fetch_copy and write_copy and have:
         f_scale = copy_bytes / fetch_copy
         w_scale = copy_bytes / write_copy
-        fetch_b = statistics.fmean(f_k) * f_scale
-        write_b = statistics.fmean(w_k) * w_scale
+        fetch_b = sum(statistics.fmean(readings["FETCH_SIZE"][k]) for k in step_kernels) * f_scale
+        write_b = sum(statistics.fmean(readings["WRITE_SIZE"][k]) for k in step_kernels) * w_scale
         out += [
             "",
             f"fetch_scale_bytes_per_unit: {f_scale:.4f}",
@@ -195,9 +211,13 @@ def main(argv=None):
             f"kernel_fetch_bytes_per_launch: {fetch_b:.0f}",
             f"kernel_write_bytes_per_launch: {write_b:.0f}",
             f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}",
-            f"algorithmic_bytes_per_launch: {wl.bytes_per_frame * wl.nframes}",
-            f"traffic_over_algorithmic: {(fetch_b + write_b) / (wl.bytes_per_frame * wl.nframes):.4f}",
+            f"algorithmic_bytes_per_launch: {alg}",
+            f"traffic_over_algorithmic: {(fetch_b + write_b) / alg:.4f}",
         ]
+        if cpu_order:
+            for k in step_kernels:
+                out.append(f"  {k}: fetch {statistics.fmean(readings['FETCH_SIZE'][k]) * f_scale:.0f} "
+                           f"write {statistics.fmean(readings['WRITE_SIZE'][k]) * w_scale:.0f} bytes per dispatch")
     with open(os.path.join(args.out, f"{kernel}_{wname}_hbm_traffic.txt"), "w") as f:
         f.write("\n".join(out) + "\n")
     print("\n".join(out), flush=True)
