@@ -11,6 +11,8 @@ Two independent forms of the same definition:
   (``float_sums.c``).
 * ``exact_*`` -- O2, the exact integer sums with an integer-only
   round-to-24-bits for the float square (``exact.py``).
+* ``int_*`` -- O3, the integer psnr twin: exact sums of (ref - dist)^2 and
+  their score (``int_psnr.py``).
 
 Below 2^53 units the two agree bit for bit; past it O1 is the CPU's rounded
 value and O2 the exact one, within ``past53_bound``.
@@ -29,6 +31,7 @@ from .exact import (  # noqa: F401
     acceptance, binade, conclude_from_doubles, conclude_from_ints, exact_batch_sums,
     exact_frame_sums, past53_bound, peak, psnr_db, q_int, q_table, rne24, scaler,
 )
+from .int_psnr import int_mse, int_noise, int_noise_batch, int_psnr_db  # noqa: F401
 
 _lib = None
 
