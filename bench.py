@@ -55,8 +55,8 @@ METRIC_CPU_ORDER = ("frames/s with the CPU's own rounding past 2^53 (sums bit-id
                     "sequential doubles) at 3840x2160 16-bit")
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "exact_reductions_amd", "csrc")
-KERNEL_SOURCE = os.path.join(CSRC, "plane_stats.hip")
-CPU_ORDER_SOURCES = [os.path.join(CSRC, f) for f in ("plane_stats.hip", "cpu_order.hip")]
+STAGE1_SOURCES = [os.path.join(CSRC, f) for f in ("plane_stats.hip", "reduce.h")]
+CPU_ORDER_SOURCES = STAGE1_SOURCES + [os.path.join(CSRC, "cpu_order.hip")]
 UNIT_POWER = (2, 1, 1, 2, 2)  # noise, ref1, dist1, ref2, dist2: units 1/s^power
 
 
@@ -82,7 +82,7 @@ def parse_args(argv=None):
     return p.parse_args(argv)
 
 
-def kernel_source_sha256(paths=(KERNEL_SOURCE,)) -> str:
+def kernel_source_sha256(paths=tuple(STAGE1_SOURCES)) -> str:
     h = hashlib.sha256()
     for path in paths:
         with open(path, "rb") as f:
@@ -90,7 +90,7 @@ def kernel_source_sha256(paths=(KERNEL_SOURCE,)) -> str:
     return h.hexdigest()
 
 
-def stored_traffic(kernel: str, workload: str, sources=(KERNEL_SOURCE,)):
+def stored_traffic(kernel: str, workload: str, sources=tuple(STAGE1_SOURCES)):
     """HBM bytes per launch from the committed counter summary, or None when
     there is none or the kernel source changed since it was taken."""
     path = os.path.join(PROFILES, f"{kernel}_{workload}_hbm_traffic.txt")

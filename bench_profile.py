@@ -36,8 +36,8 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "exact_reductions_amd", "csrc")
-KERNEL_SOURCE = os.path.join(CSRC, "plane_stats.hip")
-CPU_ORDER_SOURCES = [os.path.join(CSRC, f) for f in ("plane_stats.hip", "cpu_order.hip")]
+STAGE1_SOURCES = [os.path.join(CSRC, f) for f in ("plane_stats.hip", "reduce.h")]
+CPU_ORDER_SOURCES = STAGE1_SOURCES + [os.path.join(CSRC, "cpu_order.hip")]
 CPU_ORDER_KERNELS = ("stage1_u16", "stage2_combine", "cpu_order_prefix", "cpu_order_maps", "cpu_order_walk")
 COPY_MIB = 1024
 WARMUP = 300
@@ -93,7 +93,7 @@ def main(argv=None):
     bench = ["python3", os.path.join(ROOT, "bench.py"), "--workload", str(args.workload),
              "--no-cpu-baseline", "--input-cache", args.cache, "--mode", args.mode]
     h = hashlib.sha256()
-    for path in (CPU_ORDER_SOURCES if cpu_order else [KERNEL_SOURCE]):
+    for path in (CPU_ORDER_SOURCES if cpu_order else STAGE1_SOURCES):
         with open(path, "rb") as f:
             h.update(f.read())
     src_sha = h.hexdigest()

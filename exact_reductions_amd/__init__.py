@@ -1,4 +1,4 @@
-"""Bit-exact luma-plane reductions (float_psnr noise, float_moment sums) on MI355X.
+"""Bit-exact plane reductions (float_psnr and integer psnr noise, float_moment sums) on MI355X.
 
 The product is libvqx.so (include/vqx.h): hand-written HIP kernels for
 gfx950 behind a C ABI.  ``vqx`` is its thin ctypes binding over torch device
@@ -12,8 +12,12 @@ from .vqx import (  # noqa: F401
     conclude_batch,
     conclude_moments,
     conclude_psnr,
+    conclude_psnr_int,
     plane_stats_batch,
     plane_stats_batch_ws,
+    plane_stats_view,
     plane_stats_workspace_bytes,
+    plane_view_workspace_bytes,
+    psnr_int_view,
     status_string,
 )

@@ -54,6 +54,41 @@ hipError_t launch_plane_stats(const Geometry &g, const void *ref, const void *di
                               hipStream_t stream, hipEvent_t stage1_begin = nullptr,
                               hipEvent_t stage1_end = nullptr);
 
+// A plane of every frame of a batch, addressed sample by sample: sample
+// (x, y) of frame f is at base + (f*frame_stride + y*row_stride + x) samples.
+struct PlaneView {
+    const void *base;
+    int64_t row_stride;    // samples, >= w
+    int64_t frame_stride;  // samples, >= 0
+};
+
+// Work split of the view kernels: one workgroup per (frame, tile).  A tile
+// is rows_per_tile whole rows, or (rows_per_tile == 0, for rows longer than
+// one tile) a segment of seg_samples samples of one row.
+struct ViewGeometry {
+    int bpc;
+    int sample_bytes;
+    int w, h, nframes;
+    int rows_per_tile;
+    int seg_samples, segs_per_row;
+    int tiles;            // per frame
+    int64_t workgroups;   // nframes * tiles
+    size_t workspace_bytes;
+};
+
+ViewGeometry make_view_geometry(int w, int h, int bpc, int nframes);
+
+// The five sums of every frame over plane views (stage 1 over tiles, then
+// the per-frame combine); out_moments may be null for the noise only.
+hipError_t launch_view_stats(const ViewGeometry &g, const PlaneView &ref, const PlaneView &dist,
+                             uint64_t *out_noise, uint64_t *out_moments, uint64_t *partials,
+                             hipStream_t stream);
+
+// The integer psnr noise, sum of (ref - dist)^2 in exact integers, of
+// every frame over plane views.
+hipError_t launch_view_psnr_int(const ViewGeometry &g, const PlaneView &ref, const PlaneView &dist,
+                                uint64_t *out_noise, uint64_t *partials, hipStream_t stream);
+
 // Workspace of the CPU-order form: byte offsets of its parts.
 struct CpuOrderLayout {
     size_t records, prefix, totals, maps, bytes;

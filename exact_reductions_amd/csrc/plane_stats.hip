@@ -36,6 +36,7 @@
 #include <hip/hip_ext.h>
 
 #include "plane_stats.h"
+#include "reduce.h"
 #include "terms.h"
 
 #pragma clang fp contract(off)
@@ -43,12 +44,6 @@
 namespace vqx {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kThreads = 256;              // four wave64s
-static_assert(kThreads == kChunkThreads, "dispatch-size check");
-constexpr int kWaves = kThreads / 64;
 constexpr int kIters = 8;                  // 16-byte vectors per lane per plane
 constexpr int kInFlight = 4;               // vectors of each plane loaded before use
 constexpr int kChunkVecs = kThreads * kIters;  // 32 KiB of each plane per workgroup
@@ -68,137 +63,6 @@ static_assert(kIters % kInFlight == 0, "whole load groups");
 static_assert((kIters * 16 + 1) * 255ull * 255ull * 64ull < (1ull << 32), "8-bit wave budget");
 static_assert(((kIters * 8 + 1) * 0xffffffffull >> 16) * 64ull < (1ull << 32), "16-bit wave budget");
 static_assert((kIters * 8 + 1) * 65535ull * 64ull < (1ull << 32), "16-bit sample-sum budget");
-
-// --------------------------------------------------------------- 8-bit terms
-struct Acc8 {
-    uint32_t r1 = 0, d1 = 0, r2 = 0, d2 = 0, rd = 0;
-};
-
-// Four samples of each plane packed in one dword.
-__device__ __forceinline__ void add_dword(Acc8 &a, uint32_t r, uint32_t d)
-{
-    a.r1 = __builtin_amdgcn_sad_u8(r, 0u, a.r1);          // + r0 + r1 + r2 + r3
-    a.d1 = __builtin_amdgcn_sad_u8(d, 0u, a.d1);
-    a.r2 = __builtin_amdgcn_udot4(r, r, a.r2, false);     // + sum r_i^2
-    a.d2 = __builtin_amdgcn_udot4(d, d, a.d2, false);
-    a.rd = __builtin_amdgcn_udot4(r, d, a.rd, false);     // + sum r_i*d_i
-}
-
-// -------------------------------------------------------------- 16-bit terms
-// The float terms go into 64-bit integer lane accumulators (one
-// v_lshl_add_u64 per term on gfx950).  This is the leanest exact form:
-// fewer VALU operations per byte than adding the 16-bit halves separately,
-// which matters because the kernel runs near the HBM roofline, where power
-// (and with it the clock) depends on the work per byte.
-struct Acc16 {
-    uint64_t noise = 0, r2 = 0, d2 = 0;
-    uint32_t r1 = 0, d1 = 0;
-};
-
-// Two samples of each plane packed in one dword.
-__device__ __forceinline__ void add_dword(Acc16 &a, uint32_t r, uint32_t d)
-{
-    const float r0 = static_cast<float>(r & 0xffffu), r1 = static_cast<float>(r >> 16);
-    const float d0 = static_cast<float>(d & 0xffffu), d1 = static_cast<float>(d >> 16);
-    // float_psnr: the square of the float difference [PSNR, Decision]
-    a.noise += float_square(r0 - d0);
-    a.noise += float_square(r1 - d1);
-    // float_moment: the float squares of the samples [MOMENT, Decision]
-    a.r2 += float_square(r0);
-    a.r2 += float_square(r1);
-    a.d2 += float_square(d0);
-    a.d2 += float_square(d1);
-    // the sample sums: r0 + r1 in one integer dot product
-    const u16x2 ones = {1, 1};
-    a.r1 = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, r), ones, a.r1, false);
-    a.d1 = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, d), ones, a.d1, false);
-}
-
-template <class Acc>
-__device__ __forceinline__ void add_vec(Acc &a, const u32x4 &r, const u32x4 &d)
-{
-    add_dword(a, r.x, d.x);
-    add_dword(a, r.y, d.y);
-    add_dword(a, r.z, d.z);
-    add_dword(a, r.w, d.w);
-}
-
-// ---------------------------------------------------------- wave64 reduction
-// Sum of v over the 64 lanes, returned to every lane.  Four DPP steps add
-// within each row of 16 lanes; row_bcast:15 and row_bcast:31 carry rows into
-// rows 1..3, so lane 63 ends with the total, which readlane broadcasts.
-__device__ __forceinline__ uint32_t dpp_step(uint32_t v, int ctrl_sel)
-{
-    switch (ctrl_sel) {
-    case 0: return __builtin_amdgcn_update_dpp(0u, v, 0xb1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
-    case 1: return __builtin_amdgcn_update_dpp(0u, v, 0x4e, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
-    case 2: return __builtin_amdgcn_update_dpp(0u, v, 0x124, 0xf, 0xf, false);  // row_ror:4
-    case 3: return __builtin_amdgcn_update_dpp(0u, v, 0x128, 0xf, 0xf, false);  // row_ror:8
-    case 4: return __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
-    default: return __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false); // row_bcast:31 -> rows 2, 3
-    }
-}
-
-__device__ __forceinline__ uint32_t wave_sum(uint32_t v)
-{
-    v += dpp_step(v, 0);
-    v += dpp_step(v, 1);
-    v += dpp_step(v, 2);
-    v += dpp_step(v, 3);
-    v += dpp_step(v, 4);
-    v += dpp_step(v, 5);
-    return __builtin_amdgcn_readlane(v, 63);
-}
-
-// Adds every lane's accumulators of the workgroup: every thread gets the N
-// totals in uint64.  All threads must call it.
-template <int N>
-__device__ __forceinline__ void workgroup_sums(const uint32_t (&v)[N], uint64_t (&out)[N])
-{
-    __shared__ uint32_t lds[kWaves][N];
-    const int wave = threadIdx.x / 64;
-    uint32_t w[N];
-#pragma unroll
-    for (int k = 0; k < N; ++k)
-        w[k] = wave_sum(v[k]);
-    if ((threadIdx.x & 63) == 0) {
-#pragma unroll
-        for (int k = 0; k < N; ++k)
-            lds[wave][k] = w[k];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-        uint64_t s = 0;
-#pragma unroll
-        for (int i = 0; i < kWaves; ++i)
-            s += lds[i][k];
-        out[k] = s;
-    }
-}
-
-// Thread 0 writes the workgroup's record; the combine kernel that follows
-// in the stream reads it.
-__device__ __forceinline__ void write_record(uint64_t *part, int64_t wg,
-                                             const uint64_t (&rec)[kSums])
-{
-    if (threadIdx.x == 0) {
-#pragma unroll
-        for (int k = 0; k < kSums; ++k)
-            part[wg * kRecordStride + k] = rec[k];
-    }
-}
-
-// One sample of each plane as the low lane of a dword (the other lanes zero,
-// which add nothing to any sum: q(0) = 0).
-template <int kBytes>
-__device__ __forceinline__ uint32_t load_sample(const void *plane, int64_t i)
-{
-    if constexpr (kBytes == 1)
-        return static_cast<const uint8_t *>(plane)[i];
-    else
-        return static_cast<const uint16_t *>(plane)[i];
-}
 
 // ------------------------------------------------------------------ stage 1
 template <int kBytes, class Acc>
@@ -254,41 +118,6 @@ __device__ __forceinline__ void accumulate_chunk(Acc &acc, const void *ref, cons
             const u32x4 b = __builtin_nontemporal_load(D + v);
             add_vec(acc, a, b);
         }
-    }
-}
-
-// ------------------------------------------------------------- combine
-// Adds frame `frame`'s records in uint64 and writes its five sums.  All
-// kThreads threads of the workgroup must call it.
-__device__ __forceinline__ void combine_frame(const uint64_t *part, int chunks, int64_t frame, uint64_t *out_noise,
-                                              uint64_t *out_moments)
-{
-    __shared__ uint64_t lds[kSums][kThreads];
-    const int t = threadIdx.x;
-    uint64_t s[kSums] = {0, 0, 0, 0, 0};
-    for (int c = t; c < chunks; c += kThreads) {
-#pragma unroll
-        for (int k = 0; k < kSums; ++k)
-            s[k] += part[(frame * chunks + c) * kRecordStride + k];
-    }
-#pragma unroll
-    for (int k = 0; k < kSums; ++k)
-        lds[k][t] = s[k];
-    __syncthreads();
-    for (int off = kThreads / 2; off > 0; off >>= 1) {
-        if (t < off) {
-#pragma unroll
-            for (int k = 0; k < kSums; ++k)
-                lds[k][t] += lds[k][t + off];
-        }
-        __syncthreads();
-    }
-    if (t == 0) {
-        out_noise[frame] = lds[kNoise][0];
-        out_moments[4 * frame + 0] = lds[kRef1][0];
-        out_moments[4 * frame + 1] = lds[kDist1][0];
-        out_moments[4 * frame + 2] = lds[kRef2][0];
-        out_moments[4 * frame + 3] = lds[kDist2][0];
     }
 }
 

@@ -1,0 +1,316 @@
+// Stage 1 over plane views: planes read with a row stride and a frame stride
+// (chroma planes, padded pitches, regions of interest, planar YUV frames),
+// for the five sums and for the integer psnr noise.
+//
+// Sources (web pages, cited by title and section):
+//   [PSNR]   "ADR-1440: float_psnr_hip adds its squared differences as
+//            integers and returns the CPU's score bit for bit"
+//   [MOMENT] "ADR-1447: float_moment_hip adds the float squares the CPU adds,
+//            and is bit-identical while the CPU's own sum is exact"
+//
+// The terms are those of stage 1 (plane_stats.hip) for the five sums; the
+// integer psnr twin keeps one integer per frame [PSNR, Alternatives], the
+// sum of the exact squares of the sample differences (|r - d| < 2^16, so a
+// square is below 2^32; at 8 bits it is stage 1's noise identity).  Only
+// the addressing differs: a workgroup takes a tile of whole rows (or a
+// segment of one long row) of one frame.  Where the tile's rows all start
+// at the same offset within 16 bytes, and ref and dist at the same one,
+// its 16-byte vectors are walked as one flat range across the rows (each
+// row's few samples before its first and after its last whole vector are
+// taken one by one); otherwise the tile is read sample by sample.  Integer
+// sums make the tiling irrelevant to the result.
+
+#include "plane_stats.h"
+#include "reduce.h"
+#include "terms.h"
+
+#pragma clang fp contract(off)
+
+namespace vqx {
+namespace {
+
+constexpr int kTileVecs = 2048;  // 16-byte vectors of each plane per tile, at most
+
+// ----------------------------------------------------------------- budgets
+// A lane takes at most kTileVecs / kThreads = 8 vectors and kTileVecs * V /
+// kThreads samples (64 at two bytes, 128 at one):
+//  8 bits: a lane's sum r^2 <= (8*16 + 128) * 255^2 < 2^24, wave sum < 2^30;
+// 16 bits: a lane's 64-bit sum of squares <= (8*8 + 64) * (2^32 - 1) < 2^39,
+//          crossing the wave as its low 16 bits and the rest (< 2^23, wave
+//          sum < 2^29); a lane's sample sum <= 128 * 65535 < 2^23.
+static_assert((8 * 16 + 128) * 255ull * 255ull * 64ull < (1ull << 32), "8-bit wave budget");
+static_assert(((8 * 8 + 64) * 0xffffffffull >> 16) * 64ull < (1ull << 32), "16-bit wave budget");
+static_assert((8 * 8 + 64) * 65535ull * 64ull < (1ull << 32), "16-bit sample-sum budget");
+static_assert(kTileVecs / kThreads == 8, "lane share");
+
+// ------------------------------------------------------- integer psnr terms
+// 8 bits: sum (r-d)^2 = sum r^2 + sum d^2 - 2 sum r*d from dot products.
+struct AccInt8 {
+    uint32_t r2 = 0, d2 = 0, rd = 0;
+};
+
+__device__ __forceinline__ void add_dword(AccInt8 &a, uint32_t r, uint32_t d)
+{
+    a.r2 = __builtin_amdgcn_udot4(r, r, a.r2, false);
+    a.d2 = __builtin_amdgcn_udot4(d, d, a.d2, false);
+    a.rd = __builtin_amdgcn_udot4(r, d, a.rd, false);
+}
+
+// 9..16 bits: the absolute difference, below 2^16, squared in unsigned
+// 32-bit arithmetic: the square is below 2^32, so the product is exact, and
+// it is widened without sign.  (The 24-bit multiply builtin returns a signed
+// int, which would sign-extend squares of 2^31 and above.)
+struct AccInt16 {
+    uint64_t noise = 0;
+};
+
+__device__ __forceinline__ uint32_t abs_diff(uint32_t a, uint32_t b) { return a > b ? a - b : b - a; }
+
+__device__ __forceinline__ void add_dword(AccInt16 &a, uint32_t r, uint32_t d)
+{
+    const uint32_t e0 = abs_diff(r & 0xffffu, d & 0xffffu);
+    const uint32_t e1 = abs_diff(r >> 16, d >> 16);
+    a.noise += static_cast<uint64_t>(e0 * e0);
+    a.noise += static_cast<uint64_t>(e1 * e1);
+}
+
+// ------------------------------------------------------------------ records
+__device__ __forceinline__ void finish(const Acc8 &a, int64_t wg, uint64_t *part)
+{
+    const uint32_t v[5] = {a.r1, a.d1, a.r2, a.d2, a.rd};
+    uint64_t s[5];
+    workgroup_sums(v, s);
+    const uint64_t rec[kSums] = {s[2] + s[3] - 2 * s[4], s[0], s[1], s[2], s[3]};
+    write_record(part, wg, rec);
+}
+
+__device__ __forceinline__ void finish(const Acc16 &a, int64_t wg, uint64_t *part)
+{
+    const uint32_t v[8] = {static_cast<uint32_t>(a.noise & 0xffffu), static_cast<uint32_t>(a.noise >> 16),
+                           a.r1, a.d1,
+                           static_cast<uint32_t>(a.r2 & 0xffffu), static_cast<uint32_t>(a.r2 >> 16),
+                           static_cast<uint32_t>(a.d2 & 0xffffu), static_cast<uint32_t>(a.d2 >> 16)};
+    uint64_t s[8];
+    workgroup_sums(v, s);
+    const uint64_t rec[kSums] = {s[0] + (s[1] << 16), s[2], s[3], s[4] + (s[5] << 16), s[6] + (s[7] << 16)};
+    write_record(part, wg, rec);
+}
+
+__device__ __forceinline__ void finish(const AccInt8 &a, int64_t wg, uint64_t *part)
+{
+    const uint32_t v[3] = {a.r2, a.d2, a.rd};
+    uint64_t s[3];
+    workgroup_sums(v, s);
+    const uint64_t rec[kSums] = {s[0] + s[1] - 2 * s[2], 0, 0, 0, 0};
+    write_record(part, wg, rec);
+}
+
+__device__ __forceinline__ void finish(const AccInt16 &a, int64_t wg, uint64_t *part)
+{
+    const uint32_t v[2] = {static_cast<uint32_t>(a.noise & 0xffffu), static_cast<uint32_t>(a.noise >> 16)};
+    uint64_t s[2];
+    workgroup_sums(v, s);
+    const uint64_t rec[kSums] = {s[0] + (s[1] << 16), 0, 0, 0, 0};
+    write_record(part, wg, rec);
+}
+
+// ------------------------------------------------------------------- tiles
+struct Tile {
+    int y0, rows;  // rows [y0, y0 + rows)
+    int x0, cw;    // columns [x0, x0 + cw)
+};
+
+__device__ __forceinline__ Tile tile_of(int t, int w, int h, int rows_per_tile, int seg, int segs)
+{
+    Tile T;
+    if (rows_per_tile > 0) {
+        T.y0 = t * rows_per_tile;
+        T.rows = h - T.y0 < rows_per_tile ? h - T.y0 : rows_per_tile;
+        T.x0 = 0;
+        T.cw = w;
+    } else {
+        T.y0 = t / segs;
+        T.rows = 1;
+        T.x0 = (t - T.y0 * segs) * seg;
+        T.cw = w - T.x0 < seg ? w - T.x0 : seg;
+    }
+    return T;
+}
+
+// Walks j = threadIdx.x, + kThreads, ... over a range laid out as rows of
+// n items, keeping (row, column) without a division per step.
+struct FlatWalk {
+    int row, col, drow, dcol, n;
+    __device__ __forceinline__ FlatWalk(int start, int n_)
+        : row(start / n_), col(start % n_), drow(kThreads / n_), dcol(kThreads % n_), n(n_)
+    {
+    }
+    __device__ __forceinline__ void next()
+    {
+        row += drow;
+        col += dcol;
+        if (col >= n) {
+            col -= n;
+            ++row;
+        }
+    }
+};
+
+template <int kBytes>
+__device__ __forceinline__ const char *row_ptr(const PlaneView &P, int64_t frame, int y, int x)
+{
+    return static_cast<const char *>(P.base) +
+           (frame * P.frame_stride + static_cast<int64_t>(y) * P.row_stride + x) * kBytes;
+}
+
+template <int kBytes, class Acc>
+__device__ __forceinline__ void add_samples(Acc &acc, const char *r, const char *d)
+{
+    add_dword(acc, load_sample<kBytes>(r, 0), load_sample<kBytes>(d, 0));
+}
+
+template <int kBytes, class Acc>
+__device__ __forceinline__ void accumulate_tile(Acc &acc, const PlaneView &R, const PlaneView &D, int64_t frame,
+                                                const Tile &T)
+{
+    constexpr int V = 16 / kBytes;
+    const int t = threadIdx.x;
+    const char *r0 = row_ptr<kBytes>(R, frame, T.y0, T.x0);
+    const char *d0 = row_ptr<kBytes>(D, frame, T.y0, T.x0);
+    const int phase_r = static_cast<int>(reinterpret_cast<uintptr_t>(r0) & 15);
+    const int phase_d = static_cast<int>(reinterpret_cast<uintptr_t>(d0) & 15);
+    // every row of the tile starts at the same offset within 16 bytes
+    const bool same_rows = T.rows == 1 || (((R.row_stride * kBytes) & 15) == 0 && ((D.row_stride * kBytes) & 15) == 0);
+    if (same_rows && phase_r == phase_d) {
+        int head = ((16 - phase_r) & 15) / kBytes;
+        head = head < T.cw ? head : T.cw;
+        const int nvec = (T.cw - head) / V;
+        const int tail = T.cw - head - nvec * V;
+        const int edges = head + tail;
+        // the samples outside whole vectors, row by row
+        if (edges > 0) {
+            const int n = T.rows * edges;
+            FlatWalk fw(t, edges);
+            for (int s = t; s < n; s += kThreads, fw.next()) {
+                const int x = fw.col < head ? fw.col : head + nvec * V + (fw.col - head);
+                add_samples<kBytes>(acc, row_ptr<kBytes>(R, frame, T.y0 + fw.row, T.x0 + x),
+                                    row_ptr<kBytes>(D, frame, T.y0 + fw.row, T.x0 + x));
+            }
+        }
+        if (nvec == 0)
+            return;
+        // the whole vectors: one flat range across the rows, at most 8 per
+        // lane, read in two groups of four; a lane past the end reads the
+        // tile's first vector and drops it
+        const int n = T.rows * nvec;
+        FlatWalk fw(t, nvec);
+#pragma unroll
+        for (int g = 0; g < kTileVecs / kThreads; g += 4) {
+            if (g * kThreads >= n)
+                break;
+            u32x4 a[4], b[4];
+            bool ok[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int j = t + (g + u) * kThreads;
+                ok[u] = j < n;
+                const int y = ok[u] ? T.y0 + fw.row : T.y0;
+                const int x = T.x0 + head + (ok[u] ? fw.col : 0) * V;
+                a[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row_ptr<kBytes>(R, frame, y, x)));
+                b[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row_ptr<kBytes>(D, frame, y, x)));
+                fw.next();
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const u32x4 zero = {0, 0, 0, 0};
+                add_vec(acc, ok[u] ? a[u] : zero, ok[u] ? b[u] : zero);
+            }
+        }
+    } else {
+        // rows at different offsets within 16 bytes, or ref and dist at
+        // different ones: sample by sample
+        const int n = T.rows * T.cw;
+        FlatWalk fw(t, T.cw);
+        for (int s = t; s < n; s += kThreads, fw.next())
+            add_samples<kBytes>(acc, row_ptr<kBytes>(R, frame, T.y0 + fw.row, T.x0 + fw.col),
+                                row_ptr<kBytes>(D, frame, T.y0 + fw.row, T.x0 + fw.col));
+    }
+}
+
+template <int kBytes, class Acc>
+__global__ __launch_bounds__(kThreads) void view_stage1(PlaneView R, PlaneView D, int w, int h, int rows_per_tile,
+                                                        int seg, int segs, int tiles, uint64_t *part)
+{
+    const int64_t wg = blockIdx.x;
+    const int64_t frame = wg / tiles;
+    const int t = static_cast<int>(wg - frame * tiles);
+    Acc acc;
+    accumulate_tile<kBytes>(acc, R, D, frame, tile_of(t, w, h, rows_per_tile, seg, segs));
+    finish(acc, wg, part);
+}
+
+__global__ __launch_bounds__(kThreads) void view_combine(const uint64_t *part, int tiles, uint64_t *out_noise,
+                                                         uint64_t *out_moments)
+{
+    combine_frame(part, tiles, blockIdx.x, out_noise, out_moments);
+}
+
+template <class Acc8T, class Acc16T>
+hipError_t launch_views(const ViewGeometry &g, const PlaneView &ref, const PlaneView &dist, uint64_t *out_noise,
+                        uint64_t *out_moments, uint64_t *partials, hipStream_t stream)
+{
+    const dim3 grid(static_cast<unsigned>(g.workgroups));
+    if (g.sample_bytes == 1)
+        view_stage1<1, Acc8T><<<grid, kThreads, 0, stream>>>(ref, dist, g.w, g.h, g.rows_per_tile, g.seg_samples,
+                                                             g.segs_per_row, g.tiles, partials);
+    else
+        view_stage1<2, Acc16T><<<grid, kThreads, 0, stream>>>(ref, dist, g.w, g.h, g.rows_per_tile, g.seg_samples,
+                                                              g.segs_per_row, g.tiles, partials);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    view_combine<<<dim3(static_cast<unsigned>(g.nframes)), kThreads, 0, stream>>>(partials, g.tiles, out_noise,
+                                                                                 out_moments);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+ViewGeometry make_view_geometry(int w, int h, int bpc, int nframes)
+{
+    ViewGeometry g{};
+    g.bpc = bpc;
+    g.sample_bytes = bpc == 8 ? 1 : 2;
+    g.w = w;
+    g.h = h;
+    g.nframes = nframes;
+    const int tile_samples = kTileVecs * (16 / g.sample_bytes);
+    if (w <= tile_samples) {
+        g.rows_per_tile = tile_samples / w;
+        g.seg_samples = w;
+        g.segs_per_row = 1;
+        g.tiles = (h + g.rows_per_tile - 1) / g.rows_per_tile;
+    } else {
+        g.rows_per_tile = 0;
+        g.seg_samples = tile_samples;
+        g.segs_per_row = (w + tile_samples - 1) / tile_samples;
+        g.tiles = h * g.segs_per_row;
+    }
+    g.workgroups = static_cast<int64_t>(g.tiles) * nframes;
+    g.workspace_bytes = static_cast<size_t>(g.workgroups) * kRecordStride * sizeof(uint64_t);
+    return g;
+}
+
+hipError_t launch_view_stats(const ViewGeometry &g, const PlaneView &ref, const PlaneView &dist,
+                             uint64_t *out_noise, uint64_t *out_moments, uint64_t *partials, hipStream_t stream)
+{
+    return launch_views<Acc8, Acc16>(g, ref, dist, out_noise, out_moments, partials, stream);
+}
+
+hipError_t launch_view_psnr_int(const ViewGeometry &g, const PlaneView &ref, const PlaneView &dist,
+                                uint64_t *out_noise, uint64_t *partials, hipStream_t stream)
+{
+    return launch_views<AccInt8, AccInt16>(g, ref, dist, out_noise, nullptr, partials, stream);
+}
+
+}  // namespace vqx

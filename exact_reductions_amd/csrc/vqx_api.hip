@@ -78,6 +78,55 @@ double unit_mean(uint64_t v, int power, int bpc, int64_t pixels)
     return (static_cast<double>(v) / scale) / static_cast<double>(pixels);
 }
 
+// ------------------------------------------------------------ plane views
+int check_view_batch(int w, int h, int bpc, int nframes)
+{
+    int rc = check_shape(w, h, bpc);
+    if (rc != VQX_OK)
+        return rc;
+    if (nframes < 1)
+        return VQX_E_NFRAMES;
+    const vqx::ViewGeometry g = vqx::make_view_geometry(w, h, bpc, nframes);
+    if (g.workgroups * vqx::kChunkThreads > static_cast<int64_t>(0xffffffffu))
+        return VQX_E_NFRAMES;
+    return VQX_OK;
+}
+
+// A view's last sample, (nframes-1)*frame_stride + (h-1)*row_stride + w - 1
+// samples past its base, must lie within 2^62 bytes; each product is
+// bounded before it is formed.
+bool view_extent_ok(int64_t row_stride, int64_t frame_stride, int w, int h, int nframes, int bytes)
+{
+    if (row_stride < w || frame_stride < 0)
+        return false;
+    const int64_t limit = (static_cast<int64_t>(1) << 62) / bytes;  // in samples
+    if (h > 1 && row_stride > limit / (h - 1))
+        return false;
+    if (nframes > 1 && frame_stride > limit / (nframes - 1))
+        return false;
+    const int64_t rows = static_cast<int64_t>(h - 1) * row_stride;
+    const int64_t frames = static_cast<int64_t>(nframes - 1) * frame_stride;
+    return rows <= limit - w && frames <= limit - w - rows;
+}
+
+int check_view_args(const void *ref, int64_t rrs, int64_t rfs, const void *dist, int64_t drs, int64_t dfs, int w,
+                    int h, int bpc, int nframes, const uint64_t *out_noise, const uint64_t *out_moments,
+                    bool need_moments)
+{
+    if (!ref || !dist || !out_noise || (need_moments && !out_moments))
+        return VQX_E_NULL;
+    int rc = check_view_batch(w, h, bpc, nframes);
+    if (rc != VQX_OK)
+        return rc;
+    const int bytes = bpc == 8 ? 1 : 2;
+    if (!view_extent_ok(rrs, rfs, w, h, nframes, bytes) || !view_extent_ok(drs, dfs, w, h, nframes, bytes))
+        return VQX_E_STRIDE;
+    if (!aligned(ref, bytes) || !aligned(dist, bytes) || !aligned(out_noise, 8) ||
+        (need_moments && !aligned(out_moments, 8)))
+        return VQX_E_ALIGN;
+    return VQX_OK;
+}
+
 double psnr_from_mse(double mse, int bpc, double psnr_max)
 {
     if (mse == 0.0)
@@ -105,6 +154,7 @@ const char *vqx_status_string(int status)
     case VQX_E_WORKSPACE: return "workspace missing, misaligned or smaller than vqx_plane_stats_workspace_bytes()";
     case VQX_E_HIP: return "the HIP runtime reported an error";
     case VQX_E_NO_DEVICE: return "no usable HIP device";
+    case VQX_E_STRIDE: return "plane view: row stride below w, negative frame stride, or extent past 2^62 bytes";
     default: return "unknown status";
     }
 }
@@ -266,6 +316,86 @@ int vqx_conclude_batch(const uint64_t *noise, const uint64_t *moments, int w, in
         double *o = out + 6 * static_cast<size_t>(f);
         vqx_conclude_psnr(noise[f], w, h, bpc, psnr_max, &o[0], &o[1]);
         vqx_conclude_moments(moments + 4 * static_cast<size_t>(f), w, h, bpc, &o[2]);
+    }
+    return VQX_OK;
+}
+
+int vqx_plane_view_workspace_bytes(int w, int h, int bpc, int nframes, size_t *bytes)
+{
+    if (!bytes)
+        return VQX_E_NULL;
+    int rc = check_view_batch(w, h, bpc, nframes);
+    if (rc != VQX_OK)
+        return rc;
+    *bytes = vqx::make_view_geometry(w, h, bpc, nframes).workspace_bytes;
+    return VQX_OK;
+}
+
+int vqx_plane_stats_view_ws(const void *ref, int64_t ref_row_stride, int64_t ref_frame_stride, const void *dist,
+                            int64_t dist_row_stride, int64_t dist_frame_stride, int w, int h, int bpc, int nframes,
+                            uint64_t *out_noise, uint64_t *out_moments, void *workspace, size_t workspace_bytes,
+                            void *stream)
+{
+    int rc = check_view_args(ref, ref_row_stride, ref_frame_stride, dist, dist_row_stride, dist_frame_stride, w, h,
+                             bpc, nframes, out_noise, out_moments, true);
+    if (rc != VQX_OK)
+        return rc;
+    const vqx::ViewGeometry g = vqx::make_view_geometry(w, h, bpc, nframes);
+    if (!workspace || !aligned(workspace, 16) || workspace_bytes < g.workspace_bytes)
+        return VQX_E_WORKSPACE;
+    rc = device_ready();
+    if (rc != VQX_OK)
+        return rc;
+    const vqx::PlaneView R{ref, ref_row_stride, ref_frame_stride};
+    const vqx::PlaneView D{dist, dist_row_stride, dist_frame_stride};
+    if (vqx::launch_view_stats(g, R, D, out_noise, out_moments, static_cast<uint64_t *>(workspace),
+                               static_cast<hipStream_t>(stream)) != hipSuccess) {
+        (void)hipGetLastError();
+        return VQX_E_HIP;
+    }
+    return VQX_OK;
+}
+
+int vqx_psnr_int_view_ws(const void *ref, int64_t ref_row_stride, int64_t ref_frame_stride, const void *dist,
+                         int64_t dist_row_stride, int64_t dist_frame_stride, int w, int h, int bpc, int nframes,
+                         uint64_t *out_noise, void *workspace, size_t workspace_bytes, void *stream)
+{
+    int rc = check_view_args(ref, ref_row_stride, ref_frame_stride, dist, dist_row_stride, dist_frame_stride, w, h,
+                             bpc, nframes, out_noise, nullptr, false);
+    if (rc != VQX_OK)
+        return rc;
+    const vqx::ViewGeometry g = vqx::make_view_geometry(w, h, bpc, nframes);
+    if (!workspace || !aligned(workspace, 16) || workspace_bytes < g.workspace_bytes)
+        return VQX_E_WORKSPACE;
+    rc = device_ready();
+    if (rc != VQX_OK)
+        return rc;
+    const vqx::PlaneView R{ref, ref_row_stride, ref_frame_stride};
+    const vqx::PlaneView D{dist, dist_row_stride, dist_frame_stride};
+    if (vqx::launch_view_psnr_int(g, R, D, out_noise, static_cast<uint64_t *>(workspace),
+                                  static_cast<hipStream_t>(stream)) != hipSuccess) {
+        (void)hipGetLastError();
+        return VQX_E_HIP;
+    }
+    return VQX_OK;
+}
+
+int vqx_conclude_psnr_int(uint64_t noise, int w, int h, int bpc, double psnr_max, double *mse, double *psnr_db)
+{
+    int rc = check_shape(w, h, bpc);
+    if (rc != VQX_OK)
+        return rc;
+    const double m = static_cast<double>(noise) / static_cast<double>(static_cast<int64_t>(w) * h);
+    if (mse)
+        *mse = m;
+    if (psnr_db) {
+        if (m == 0.0) {
+            *psnr_db = psnr_max > 0.0 ? psnr_max : HUGE_VAL;
+        } else {
+            const double peak = static_cast<double>((1 << bpc) - 1);
+            const double db = 10.0 * log10(peak * peak / m);
+            *psnr_db = (psnr_max > 0.0 && db > psnr_max) ? psnr_max : db;
+        }
     }
     return VQX_OK;
 }

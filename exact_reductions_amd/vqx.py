@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libvqx.so")
 
 OK = 0
-E_NULL, E_DIMS, E_BPC, E_NFRAMES, E_ALIGN, E_WORKSPACE, E_HIP, E_NO_DEVICE = range(-1, -9, -1)
+E_NULL, E_DIMS, E_BPC, E_NFRAMES, E_ALIGN, E_WORKSPACE, E_HIP, E_NO_DEVICE, E_STRIDE = range(-1, -10, -1)
 MAX_PIXELS = 1 << 25
 
 # Every symbol include/vqx.h declares.
@@ -33,6 +33,10 @@ SYMBOLS = (
     "vqx_conclude_psnr",
     "vqx_conclude_moments",
     "vqx_conclude_batch",
+    "vqx_plane_view_workspace_bytes",
+    "vqx_plane_stats_view_ws",
+    "vqx_psnr_int_view_ws",
+    "vqx_conclude_psnr_int",
 )
 
 
@@ -59,6 +63,7 @@ def lib() -> ctypes.CDLL:
             pass
         L = ctypes.CDLL(LIBRARY)
         vp, i, u64, sz, d = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_double
+        i64 = ctypes.c_int64
         sigs = {
             "vqx_abi_version": (i, []),
             "vqx_status_string": (ctypes.c_char_p, [i]),
@@ -71,6 +76,10 @@ def lib() -> ctypes.CDLL:
             "vqx_conclude_psnr": (i, [u64, i, i, i, d, ctypes.POINTER(d), ctypes.POINTER(d)]),
             "vqx_conclude_moments": (i, [vp, i, i, i, vp]),
             "vqx_conclude_batch": (i, [vp, vp, i, i, i, i, d, vp]),
+            "vqx_plane_view_workspace_bytes": (i, [i, i, i, i, ctypes.POINTER(sz)]),
+            "vqx_plane_stats_view_ws": (i, [vp, i64, i64, vp, i64, i64, i, i, i, i, vp, vp, vp, sz, vp]),
+            "vqx_psnr_int_view_ws": (i, [vp, i64, i64, vp, i64, i64, i, i, i, i, vp, vp, sz, vp]),
+            "vqx_conclude_psnr_int": (i, [u64, i, i, i, d, ctypes.POINTER(d), ctypes.POINTER(d)]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -240,3 +249,78 @@ def conclude_batch(noise, moments, w: int, h: int, bpc: int, psnr_max: float = 0
     _check(lib().vqx_conclude_batch(n.ctypes.data, m.ctypes.data, w, h, bpc, f, float(psnr_max),
                                     out.ctypes.data), "conclude_batch")
     return out
+
+
+# ------------------------------------------------------------- plane views
+def plane_view_workspace_bytes(w: int, h: int, bpc: int, nframes: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().vqx_plane_view_workspace_bytes(w, h, bpc, nframes, ctypes.byref(out)),
+           "plane_view_workspace_bytes")
+    return out.value
+
+
+def _view(t, bpc):
+    """(base pointer, row stride, frame stride) of a [F][h][w] (or [h][w])
+    tensor view whose samples are adjacent along w: slices of larger planes,
+    chroma planes of planar YUV frames, padded pitches."""
+    import torch
+    if t.dim() == 2:
+        t = t.unsqueeze(0)
+    if t.dim() != 3:
+        raise ValueError("a plane view is [nframes][h][w] or [h][w]")
+    want = (torch.uint8,) if bpc == 8 else (torch.uint16, torch.int16)
+    if t.dtype not in want:
+        raise TypeError(f"bpc {bpc} wants {'uint8' if bpc == 8 else 'uint16'} samples")
+    if not t.is_cuda:
+        raise ValueError("plane views must be on the GPU")
+    if t.shape[2] > 1 and t.stride(2) != 1:
+        raise ValueError("samples of a row must be adjacent (stride 1 along w)")
+    row = t.stride(1) if t.shape[1] > 1 else t.shape[2]
+    frame = t.stride(0) if t.shape[0] > 1 else 0
+    return t, t.data_ptr(), row, frame
+
+
+def _views(ref, dist, bpc):
+    ref, rp, rr, rf = _view(ref, bpc)
+    dist, dp, dr, df = _view(dist, bpc)
+    if ref.shape != dist.shape or ref.device != dist.device:
+        raise ValueError("ref and dist views differ in shape or device")
+    return ref, (rp, rr, rf, dp, dr, df)
+
+
+def plane_stats_view(ref, dist, bpc: int, stream=None):
+    """The five exact sums of every frame over plane views (tensor views of
+    any row and frame stride): ``(noise [F], moments [F][4])`` as int64
+    device tensors."""
+    import torch
+    ref, args = _views(ref, dist, bpc)
+    f, h, w = ref.shape
+    dev = ref.device
+    out = torch.empty(5 * f, dtype=torch.int64, device=dev)
+    ws = torch.empty(plane_view_workspace_bytes(w, h, bpc, f), dtype=torch.uint8, device=dev)
+    _check(lib().vqx_plane_stats_view_ws(*args, w, h, bpc, f, out[:f].data_ptr(), out[f:].data_ptr(),
+                                         ws.data_ptr(), ws.numel(), _stream_handle(dev, stream)),
+           "plane_stats_view_ws")
+    return out[:f], out[f:].view(f, 4)
+
+
+def psnr_int_view(ref, dist, bpc: int, stream=None):
+    """The integer psnr noise of every frame over plane views: int64 [F]
+    device tensor of exact sums of (ref - dist)^2."""
+    import torch
+    ref, args = _views(ref, dist, bpc)
+    f, h, w = ref.shape
+    dev = ref.device
+    out = torch.empty(f, dtype=torch.int64, device=dev)
+    ws = torch.empty(plane_view_workspace_bytes(w, h, bpc, f), dtype=torch.uint8, device=dev)
+    _check(lib().vqx_psnr_int_view_ws(*args, w, h, bpc, f, out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                      _stream_handle(dev, stream)), "psnr_int_view_ws")
+    return out
+
+
+def conclude_psnr_int(noise: int, w: int, h: int, bpc: int, psnr_max: float = 0.0):
+    """(mse, psnr_db) of the integer psnr twin from one exact noise (host)."""
+    mse, db = ctypes.c_double(), ctypes.c_double()
+    _check(lib().vqx_conclude_psnr_int(int(noise), w, h, bpc, float(psnr_max), ctypes.byref(mse),
+                                       ctypes.byref(db)), "conclude_psnr_int")
+    return mse.value, db.value

@@ -63,7 +63,9 @@ enum vqx_status {
     VQX_E_ALIGN = -5,     /* ref/dist not 16-byte aligned, or an output not 8-byte aligned */
     VQX_E_WORKSPACE = -6, /* workspace smaller than vqx_plane_stats_workspace_bytes() */
     VQX_E_HIP = -7,       /* the HIP runtime reported an error (launch or allocation) */
-    VQX_E_NO_DEVICE = -8  /* no usable HIP device */
+    VQX_E_NO_DEVICE = -8, /* no usable HIP device */
+    VQX_E_STRIDE = -9     /* plane views: a row stride below w, a negative frame stride,
+                             or a plane whose last sample lies past 2^62 bytes */
 };
 
 /* VQX_ABI_VERSION of the loaded library. */
@@ -203,6 +205,74 @@ int vqx_conclude_moments(const uint64_t sums[4], int w, int h, int bpc, double o
  */
 int vqx_conclude_batch(const uint64_t *noise, const uint64_t *moments, int w, int h, int bpc,
                        int nframes, double psnr_max, double *out);
+
+/*
+ * ------------------------------------------------------------ plane views
+ * The same reductions over planes that are not one contiguous [nframes][h][w]
+ * array: chroma planes, planes with a padded row pitch, a region of interest
+ * inside larger planes, or one plane of planar YUV frames stored one after
+ * another.  A view addresses one plane of every frame of a batch: sample
+ * (x, y) of frame f is at
+ *     base + f*frame_stride + y*row_stride + x        (in samples)
+ * with samples uint8 at 8 bits and uint16 otherwise.  row_stride >= w;
+ * frame_stride >= 0 (0: the same plane for every frame); views may overlap
+ * (they are only read).  The caller owns the memory and must make every
+ * addressed sample readable.  ref and dist have views of their own, with the
+ * same w, h and nframes.  The results are the same function of the selected
+ * samples as the contiguous entry points' [PSNR, Context and Decision;
+ * MOMENT, Decision]; the tiling never changes an integer sum.  Fastest where
+ * the rows of a plane start at one offset within 16 bytes (row_stride*bytes
+ * a multiple of 16) and ref and dist at the same one; any other layout is
+ * read sample by sample, still exactly.
+ *
+ * Common errors, in this order: VQX_E_NULL, VQX_E_DIMS, VQX_E_BPC,
+ * VQX_E_NFRAMES (also when the batch needs more than (2^32-1)/256 tiles of
+ * 2048 16-byte vectors per plane), VQX_E_STRIDE, VQX_E_ALIGN (ref/dist not
+ * aligned to one sample, an output not to 8 bytes), VQX_E_WORKSPACE
+ * (missing, not 16-byte aligned or smaller than
+ * vqx_plane_view_workspace_bytes()), VQX_E_NO_DEVICE, VQX_E_HIP.  Outputs
+ * are written once each, never accumulated into; they may be pinned host
+ * memory mapped for the device.  The calls queue work on `stream` and return.
+ */
+
+/* Device scratch of the plane-view entry points for this batch shape
+ * (64 bytes per frame and tile).  Host-only. */
+int vqx_plane_view_workspace_bytes(int w, int h, int bpc, int nframes, size_t *bytes);
+
+/* The five sums of vqx_plane_stats_batch_ws, over plane views. */
+int vqx_plane_stats_view_ws(const void *ref, int64_t ref_row_stride, int64_t ref_frame_stride,
+                            const void *dist, int64_t dist_row_stride, int64_t dist_frame_stride,
+                            int w, int h, int bpc, int nframes, uint64_t *out_noise,
+                            uint64_t *out_moments, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/*
+ * The integer psnr twin's noise over plane views: per frame one uint64,
+ *   out_noise[f] = sum over the plane of (ref - dist)^2,
+ * the squares exact integers of the stored samples (below 2^32), the sum
+ * exact (below 2^57) -- the one integer per frame that the integer psnr twin
+ * keeps [PSNR, Alternatives].  It equals the float noise of
+ * vqx_plane_stats_* wherever |ref - dist| < 4096 (there the float square is
+ * exact); above that the float square rounds and this one does not.
+ */
+int vqx_psnr_int_view_ws(const void *ref, int64_t ref_row_stride, int64_t ref_frame_stride,
+                         const void *dist, int64_t dist_row_stride, int64_t dist_frame_stride,
+                         int w, int h, int bpc, int nframes, uint64_t *out_noise,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The integer psnr conclusion (host only), on the stored scale:
+ *   mse     = (double)noise / (w*h)   -- one rounding of the integer (only
+ *             at or past 2^53), one division;
+ *   psnr_db = 10*log10(peak^2 / mse), peak = 2^bpc - 1; min(psnr_db,
+ *             psnr_max) when psnr_max > 0; mse == 0 gives psnr_max, or +inf
+ *             when psnr_max <= 0.
+ * The pages give no formula for it; this is float_psnr's ratio [PSNR,
+ * Consequences] taken on the stored scale.  Either output pointer may be
+ * NULL.  Errors: VQX_E_DIMS, VQX_E_BPC.
+ */
+int vqx_conclude_psnr_int(uint64_t noise, int w, int h, int bpc, double psnr_max, double *mse,
+                          double *psnr_db);
 
 #ifdef __cplusplus
 }

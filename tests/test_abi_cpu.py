@@ -46,9 +46,9 @@ def test_status_codes_match_header():
     text = _header_text()
     for name, value in (("VQX_OK", 0), ("VQX_E_NULL", -1), ("VQX_E_DIMS", -2), ("VQX_E_BPC", -3),
                         ("VQX_E_NFRAMES", -4), ("VQX_E_ALIGN", -5), ("VQX_E_WORKSPACE", -6),
-                        ("VQX_E_HIP", -7), ("VQX_E_NO_DEVICE", -8)):
+                        ("VQX_E_HIP", -7), ("VQX_E_NO_DEVICE", -8), ("VQX_E_STRIDE", -9)):
         assert re.search(rf"\b{name} = {value}\b", text), name
-    for s in range(-8, 1):
+    for s in range(-9, 1):
         assert vqx.status_string(s) and vqx.status_string(s) != "unknown status"
     assert vqx.status_string(-99) == "unknown status"
 
@@ -278,3 +278,96 @@ def test_past53_conclusion_is_one_rounding():
     from fractions import Fraction
     err = abs(Fraction(got) - Fraction(exact, 65536 * w * h))
     assert err <= oracle.past53_bound(w * h, 54, 16)
+
+
+# ------------------------------------------------------------------ plane views
+
+def test_view_workspace_bytes():
+    # 3840x2160 16-bit: 4 rows per tile (4*3840 <= 2048*8), 540 tiles per frame
+    assert vqx.plane_view_workspace_bytes(3840, 2160, 16, 32) == 540 * 32 * 64
+    # rows longer than a tile are cut into segments of 2048 vectors
+    assert vqx.plane_view_workspace_bytes(40000, 3, 16, 1) == 3 * 3 * 64
+    assert vqx.plane_view_workspace_bytes(40000, 3, 8, 1) == 3 * 2 * 64
+    assert vqx.plane_view_workspace_bytes(1, 1, 10, 5) == 5 * 64
+    with pytest.raises(vqx.VqxError) as e:
+        vqx.plane_view_workspace_bytes(1, 1, 10, (2**32 - 1) // 256 + 1)
+    assert e.value.status == vqx.E_NFRAMES
+
+
+VIEW_ERRORS = [
+    ("null ref", dict(ref=0), vqx.E_NULL),
+    ("null noise", dict(noise=0), vqx.E_NULL),
+    ("w 0", dict(w=0), vqx.E_DIMS),
+    ("bpc 17", dict(bpc=17), vqx.E_BPC),
+    ("nframes 0", dict(nframes=0), vqx.E_NFRAMES),
+    ("row stride below w", dict(rrs=15), vqx.E_STRIDE),
+    ("negative frame stride", dict(dfs=-1), vqx.E_STRIDE),
+    ("extent past 2^62 bytes", dict(rfs=2**62 - 8), vqx.E_STRIDE),
+    ("16-bit extent past 2^62 bytes", dict(bpc=16, rfs=2**61), vqx.E_STRIDE),
+    ("huge row stride", dict(drs=2**62), vqx.E_STRIDE),
+    ("16-bit ref on an odd byte", dict(bpc=16, ref_off=1), vqx.E_ALIGN),
+    ("noise misaligned", dict(noise_off=4), vqx.E_ALIGN),
+]
+
+
+def _view_call(L, b, fn, ws, ws_bytes, ref=None, noise=None, w=16, h=4, bpc=8, nframes=2, rrs=None, rfs=None,
+               drs=None, dfs=None, ref_off=0, noise_off=0):
+    ref = b.ref + ref_off if ref is None else ref
+    noise = b.noise + noise_off if noise is None else noise
+    rrs = w if rrs is None else rrs
+    drs = w if drs is None else drs
+    rfs = w * h if rfs is None else rfs
+    dfs = w * h if dfs is None else dfs
+    if fn == "stats":
+        return L.vqx_plane_stats_view_ws(ref or None, rrs, rfs, b.dist, drs, dfs, w, h, bpc, nframes,
+                                         noise or None, b.moments, ws, ws_bytes, None)
+    return L.vqx_psnr_int_view_ws(ref or None, rrs, rfs, b.dist, drs, dfs, w, h, bpc, nframes,
+                                  noise or None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("name,kw,status", VIEW_ERRORS, ids=[a[0] for a in VIEW_ERRORS])
+@pytest.mark.parametrize("fn", ["stats", "psnr_int"])
+def test_view_argument_errors(L, name, kw, status, fn):
+    b = _Buffers()
+    ws = np.zeros(4096, dtype=np.uint8)
+    base = (ws.ctypes.data + 255) // 256 * 256
+    assert _view_call(L, b, fn, base, 1024, **kw) == status
+    assert b.untouched()
+
+
+def test_view_workspace_and_moments_errors(L):
+    b = _Buffers()
+    ws = np.zeros(4096, dtype=np.uint8)
+    base = (ws.ctypes.data + 255) // 256 * 256
+    need = vqx.plane_view_workspace_bytes(16, 4, 8, 2)
+    for fn in ("stats", "psnr_int"):
+        assert _view_call(L, b, fn, base, need - 1) == vqx.E_WORKSPACE
+        assert _view_call(L, b, fn, base + 8, need) == vqx.E_WORKSPACE
+        assert _view_call(L, b, fn, None, need) == vqx.E_WORKSPACE
+    assert L.vqx_plane_stats_view_ws(b.ref, 16, 64, b.dist, 16, 64, 16, 4, 8, 2, b.noise, None, base, need,
+                                     None) == vqx.E_NULL
+    # an odd 8-bit base is fine; overlapping views (frame stride 0) are fine
+    if not _has_gpu():
+        assert _view_call(L, b, "stats", base, need, ref_off=1, rfs=0) == vqx.E_NO_DEVICE
+    assert b.untouched()
+
+
+@pytest.mark.parametrize("bpc", [8, 10, 12, 16])
+def test_psnr_int_conclusion_matches_oracle_bitwise(bpc):
+    rng = np.random.Generator(np.random.PCG64(100 + bpc))
+    top = (1 << bpc) - 1
+    for w, h in ((576, 324), (3840, 2160), (1, 1), (17, 3), (960, 540)):
+        for _ in range(50):
+            noise = int(rng.integers(0, w * h * top * top + 1))
+            mse, db = vqx.conclude_psnr_int(noise, w, h, bpc, 0.0)
+            assert mse == oracle.int_mse(noise, w, h)
+            assert db == oracle.int_psnr_db(noise, w, h, bpc, 0.0)
+            _, capped = vqx.conclude_psnr_int(noise, w, h, bpc, 6.0 * bpc + 12.0)
+            assert capped == oracle.int_psnr_db(noise, w, h, bpc, 6.0 * bpc + 12.0)
+    assert vqx.conclude_psnr_int(0, 4, 4, bpc, 0.0)[1] == math.inf
+    assert vqx.conclude_psnr_int(0, 4, 4, bpc, 50.0) == (0.0, 50.0)
+    # past 2^53: one rounding of the integer, then the division
+    big = (1 << 55) + 1
+    assert vqx.conclude_psnr_int(big, 7680, 4320, 16)[0] == float(big) / (7680 * 4320)
+    assert vqx.lib().vqx_conclude_psnr_int(0, 0, 4, 8, 0.0, None, None) == vqx.E_DIMS
+    assert vqx.lib().vqx_conclude_psnr_int(0, 4, 4, 17, 0.0, None, None) == vqx.E_BPC

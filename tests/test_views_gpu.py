@@ -1,0 +1,205 @@
+"""Plane views and the integer psnr twin on the device (marked gpu).
+
+Every case builds its planes as views of larger tensors (a padded pitch, a
+region of interest, one plane of planar YUV frames), runs
+``vqx_plane_stats_view_ws`` and ``vqx_psnr_int_view_ws`` through the C ABI,
+and compares element by element with the oracle applied to the same samples
+(numpy slices): the five exact sums with O2, the integer noise with O3, the
+integer psnr conclusion with O3's.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from exact_reductions_amd import vqx  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    vqx.lib()
+
+
+def _dtype(bpc):
+    return np.uint8 if bpc == 8 else np.uint16
+
+
+def _rand(rng, shape, bpc, lo=0, hi=None):
+    hi = (1 << bpc) - 1 if hi is None else hi
+    return rng.integers(lo, hi, size=shape, endpoint=True).astype(_dtype(bpc))
+
+
+def check_views(ref_np, dist_np, ref_dev, dist_dev, bpc, label=""):
+    """ref_np/dist_np: [F][h][w] numpy views of the samples that the device
+    views ref_dev/dist_dev select."""
+    f = ref_np.shape[0]
+    h, w = ref_np.shape[1:]
+    noise, moments = vqx.plane_stats_view(ref_dev, dist_dev, bpc)
+    inoise = vqx.psnr_int_view(ref_dev, dist_dev, bpc)
+    torch.cuda.synchronize()
+    noise, moments, inoise = noise.cpu().numpy(), moments.cpu().numpy(), inoise.cpu().numpy()
+    for k in range(f):
+        r = np.ascontiguousarray(ref_np[k])
+        d = np.ascontiguousarray(dist_np[k])
+        want = oracle.exact_frame_sums(r, d)
+        got = [int(noise[k])] + [int(v) for v in moments[k]]
+        assert got == list(want), f"{label} frame {k}: five sums"
+        wn = oracle.int_noise(r, d)
+        assert int(inoise[k]) == wn, f"{label} frame {k}: integer noise"
+        assert vqx.conclude_psnr_int(int(inoise[k]), w, h, bpc, 0.0)[1] == oracle.int_psnr_db(wn, w, h, bpc)
+    return noise, moments, inoise
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_contiguous_workloads_as_views(n):
+    """A contiguous batch is the view with row stride w and frame stride w*h;
+    the results equal those of the contiguous entry point too."""
+    wl = synth.WORKLOADS[n]
+    ref, dist = synth.generate(n, nframes=min(wl.nframes, 6))
+    r = torch.from_numpy(ref).cuda()
+    d = torch.from_numpy(dist).cuda()
+    noise, moments, _ = check_views(ref, dist, r, d, wl.bpc, f"workload {n}")
+    n2, m2 = vqx.plane_stats_batch(r, d, wl.bpc)
+    torch.cuda.synchronize()
+    assert (n2.cpu().numpy() == noise).all() and (m2.cpu().numpy() == moments).all()
+
+
+@pytest.mark.parametrize("bpc", [8, 10, 16])
+@pytest.mark.parametrize("w,h,pitch,x0,y0", [
+    (1920, 1080, 2048, 0, 0),      # padded pitch, rows 16-byte aligned
+    (1920, 1080, 1920 + 64, 32, 8),  # a region of interest, aligned
+    (1000, 301, 1037, 3, 5),       # odd pitch: rows at varying offsets
+    (333, 77, 400, 7, 1),          # region starting mid-vector
+    (7, 9, 13, 1, 2),              # narrower than a vector
+    (1, 1, 1, 0, 0),
+])
+def test_pitched_regions(bpc, w, h, pitch, x0, y0):
+    rng = np.random.default_rng(w * 31 + pitch + bpc)
+    f = 3
+    big_r = _rand(rng, (f, h + y0 + 2, pitch + x0), bpc, hi=255 if bpc == 8 else 65535)
+    big_d = _rand(rng, (f, h + y0 + 2, pitch + x0), bpc, hi=255 if bpc == 8 else 65535)
+    sl = (slice(None), slice(y0, y0 + h), slice(x0, x0 + w))
+    R = torch.from_numpy(big_r).cuda()
+    D = torch.from_numpy(big_d).cuda()
+    check_views(big_r[sl], big_d[sl], R[sl], D[sl], bpc, f"{w}x{h} pitch {pitch} at ({x0},{y0})")
+
+
+@pytest.mark.parametrize("bpc", [8, 10])
+@pytest.mark.parametrize("chroma", ["420", "422", "444"])
+def test_planar_yuv_frames(bpc, chroma):
+    """Y, U and V of each frame stored one after another, frames one after
+    another: each plane is a view with its own row stride, a frame stride of
+    the whole frame, and a base offset."""
+    w, h, f = 1920, 1080, 4
+    cw = w // 2 if chroma in ("420", "422") else w
+    ch = h // 2 if chroma == "420" else h
+    sizes = [w * h, cw * ch, cw * ch]
+    frame = sum(sizes)
+    rng = np.random.default_rng(hash(chroma) % 1000 + bpc)
+    buf_r = _rand(rng, (f, frame), bpc)
+    buf_d = buf_r.astype(np.int64) + rng.integers(-20, 20, size=buf_r.shape, endpoint=True)
+    buf_d = np.clip(buf_d, 0, (1 << bpc) - 1).astype(_dtype(bpc))
+    R = torch.from_numpy(buf_r).cuda()
+    D = torch.from_numpy(buf_d).cuda()
+    off = 0
+    for p, (pw, ph) in enumerate(((w, h), (cw, ch), (cw, ch))):
+        rv = torch.as_strided(R, (f, ph, pw), (frame, pw, 1), off)
+        dv = torch.as_strided(D, (f, ph, pw), (frame, pw, 1), off)
+        rn = np.lib.stride_tricks.as_strided(buf_r.reshape(-1)[off:], (f, ph, pw),
+                                             (frame * buf_r.itemsize, pw * buf_r.itemsize, buf_r.itemsize))
+        dn = np.lib.stride_tricks.as_strided(buf_d.reshape(-1)[off:], (f, ph, pw),
+                                             (frame * buf_d.itemsize, pw * buf_d.itemsize, buf_d.itemsize))
+        check_views(rn, dn, rv, dv, bpc, f"{chroma} plane {p}")
+        off += sizes[p]
+
+
+def test_ref_and_dist_at_different_offsets():
+    """ref contiguous, dist in a pitched buffer one sample off: their vectors
+    do not pair, and the tile is read sample by sample."""
+    rng = np.random.default_rng(41)
+    f, h, w = 2, 300, 1000
+    ref = _rand(rng, (f, h, w), 16, hi=65535)
+    big = _rand(rng, (f, h, w + 9), 16, hi=65535)
+    dist = big[:, :, 1:1 + w]
+    check_views(ref, dist, torch.from_numpy(ref).cuda(), torch.from_numpy(big).cuda()[:, :, 1:1 + w], 16)
+
+
+@pytest.mark.parametrize("bpc,w", [(16, 40000), (8, 70000), (16, 16384), (16, 16385)])
+def test_rows_longer_than_a_tile(bpc, w):
+    rng = np.random.default_rng(w)
+    f, h = 2, 3
+    big_r = _rand(rng, (f, h, w + 5), bpc)
+    big_d = _rand(rng, (f, h, w + 5), bpc)
+    sl = (slice(None), slice(None), slice(2, 2 + w))
+    check_views(big_r[sl], big_d[sl], torch.from_numpy(big_r).cuda()[sl],
+                torch.from_numpy(big_d).cuda()[sl], bpc, f"w {w}")
+
+
+def test_frame_stride_zero():
+    """Every frame reads the same plane."""
+    rng = np.random.default_rng(3)
+    ref = _rand(rng, (1, 64, 80), 12)
+    dist = _rand(rng, (1, 64, 80), 12)
+    R = torch.from_numpy(ref).cuda().expand(5, 64, 80)
+    D = torch.from_numpy(dist).cuda().expand(5, 64, 80)
+    assert R.stride(0) == 0
+    noise, moments, inoise = check_views(np.broadcast_to(ref, (5, 64, 80)), np.broadcast_to(dist, (5, 64, 80)),
+                                         R, D, 12, "stride 0")
+    assert len(set(int(v) for v in inoise)) == 1
+
+
+def test_integer_noise_differs_from_float_past_4096():
+    """16-bit differences above 4096: the float square rounds, the integer
+    one does not -- e.g. 4097^2 = 2^24 + 8193 vs its float square 16 785 408."""
+    f, h, w = 2, 1080, 1920
+    ref = np.full((f, h, w), 4097 + 500, dtype=np.uint16)
+    dist = np.full((f, h, w), 500, dtype=np.uint16)
+    R, D = torch.from_numpy(ref).cuda(), torch.from_numpy(dist).cuda()
+    noise, _, inoise = check_views(ref, dist, R, D, 16)
+    assert int(inoise[0]) - int(noise[0]) == w * h
+    rng = np.random.default_rng(9)
+    ref = _rand(rng, (f, h, w), 16, hi=65535)
+    dist = _rand(rng, (f, h, w), 16, hi=65535)
+    noise, _, inoise = check_views(ref, dist, torch.from_numpy(ref).cuda(), torch.from_numpy(dist).cuda(), 16)
+    assert (inoise != noise).all()
+
+
+def test_largest_frame_pitched():
+    rng = np.random.default_rng(8192)
+    big_r = _rand(rng, (1, 4096, 8192 + 64), 16, hi=65535)
+    big_d = _rand(rng, (1, 4096, 8192 + 64), 16, hi=65535)
+    sl = (slice(None), slice(None), slice(64, 64 + 8192))
+    check_views(big_r[sl], big_d[sl], torch.from_numpy(big_r).cuda()[sl], torch.from_numpy(big_d).cuda()[sl], 16)
+
+
+def test_outputs_written_not_accumulated():
+    rng = np.random.default_rng(12)
+    ref = _rand(rng, (3, 50, 70), 10)
+    dist = _rand(rng, (3, 50, 70), 10)
+    R, D = torch.from_numpy(ref).cuda(), torch.from_numpy(dist).cuda()
+    f, h, w = ref.shape
+    L = vqx.lib()
+    out = torch.full((6 * f,), -1, dtype=torch.int64, device="cuda")
+    ws = torch.full((vqx.plane_view_workspace_bytes(w, h, 10, f),), 0xFF, dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    for _ in range(2):
+        assert L.vqx_plane_stats_view_ws(R.data_ptr(), w, w * h, D.data_ptr(), w, w * h, w, h, 10, f,
+                                         out[:f].data_ptr(), out[f:5 * f].data_ptr(), ws.data_ptr(),
+                                         ws.numel(), st) == 0
+        assert L.vqx_psnr_int_view_ws(R.data_ptr(), w, w * h, D.data_ptr(), w, w * h, w, h, 10, f,
+                                      out[5 * f:].data_ptr(), ws.data_ptr(), ws.numel(), st) == 0
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    for k in range(f):
+        want = oracle.exact_frame_sums(ref[k], dist[k])
+        assert [int(o[k])] + [int(v) for v in o[f + 4 * k:f + 4 * k + 4]] == list(want)
+        assert int(o[5 * f + k]) == oracle.int_noise(ref[k], dist[k])
