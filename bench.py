@@ -53,10 +53,14 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published peak
 METRIC = "frames/s and HBM GB/s (fraction of peak) at 3840x2160 16-bit, bit-exact"
 METRIC_CPU_ORDER = ("frames/s with the CPU's own rounding past 2^53 (sums bit-identical to the "
                     "sequential doubles) at 3840x2160 16-bit")
+METRIC_PSNR_INT = "frames/s of the integer psnr twin (exact uint64 sum of (ref - dist)^2 per frame)"
+METRIC_YUV420 = ("frames/s of the integer psnr twin on all three planes of planar 4:2:0 frames "
+                 "(Y, U, V through plane views)")
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "exact_reductions_amd", "csrc")
 STAGE1_SOURCES = [os.path.join(CSRC, f) for f in ("plane_stats.hip", "reduce.h")]
 CPU_ORDER_SOURCES = STAGE1_SOURCES + [os.path.join(CSRC, "cpu_order.hip")]
+VIEW_SOURCES = [os.path.join(CSRC, f) for f in ("plane_views.hip", "reduce.h")]
 UNIT_POWER = (2, 1, 1, 2, 2)  # noise, ref1, dist1, ref2, dist2: units 1/s^power
 
 
@@ -69,13 +73,16 @@ def parse_args(argv=None):
     # that, and the timed steps measure steady streaming.
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--warmup", type=int, default=300)
-    p.add_argument("--workload", type=int, default=5, help="workload number (5: 3840x2160 16-bit)")
+    p.add_argument("--workload", type=int, default=None,
+                   help="workload number (default 5, 3840x2160 16-bit; 2, 1920x1080 10-bit, for yuv420)")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the oracle leg (and with it the parity gate); for profiler runs")
     p.add_argument("--input-cache", default=None, metavar="DIR",
                    help="keep the generated batch as .npy files in DIR and reuse them")
-    p.add_argument("--mode", choices=("exact", "cpu-order"), default="exact",
-                   help="exact: the exact sums (default); cpu-order: also the CPU's rounding past 2^53")
+    p.add_argument("--mode", choices=("exact", "cpu-order", "psnr-int", "yuv420"), default="exact",
+                   help="exact: the exact sums (default); cpu-order: also the CPU's rounding past 2^53; "
+                        "psnr-int: the integer psnr twin; yuv420: the integer psnr twin on the Y, U and V "
+                        "planes of planar 4:2:0 frames")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="after the timed steps, run 3 elementwise kernels that each read and "
                         "write MIB MiB (the known-size kernel that scales the HBM counters)")
@@ -240,6 +247,67 @@ def gate_cpu_order(ref, dist, bpc, exact, cpu, concl, threads):
     return parity
 
 
+def _psnr_int_planes(ref, dist, planes, w, h):
+    """(plane index, frame, ref view, dist view, pw, ph) of every plane of the
+    batch: the luma pair itself, or the three planes of planar frames."""
+    nframes = ref.shape[0]
+    if planes is None:
+        return [(0, f, ref[f], dist[f], w, h) for f in range(nframes)]
+    out = []
+    for p, (off, pw, ph) in enumerate(planes):
+        for f in range(nframes):
+            out.append((p, f, ref[f, off:off + pw * ph].reshape(ph, pw), dist[f, off:off + pw * ph].reshape(ph, pw),
+                        pw, ph))
+    return out
+
+
+def gate_psnr_int(ref, dist, bpc, planes, w, h, last, concl):
+    """The integer noise of every plane and frame of the last step against O3,
+    and the library's conclusion of it against O3's."""
+    import oracle
+
+    nframes = ref.shape[0]
+    failures = []
+    for row, (p, f, r, d, pw, ph) in enumerate(_psnr_int_planes(ref, dist, planes, w, h)):
+        want = oracle.int_noise(r, d)
+        got = int(last[p * nframes + f])
+        if got != want:
+            failures.append((p, f, f"device {got} != exact {want}"))
+        elif concl[row, 1] != oracle.int_psnr_db(want, pw, ph, bpc):
+            failures.append((p, f, "conclusion"))
+    parity = {"frames": nframes, "planes": 1 if planes is None else len(planes), "failures": len(failures),
+              "rule": "exact integers; the conclusion bit-identical to the oracle's"}
+    if failures:
+        parity["first_failure"] = str(failures[0])
+    return parity
+
+
+def time_oracle_psnr_int(ref, dist, bpc, planes, w, h, threads):
+    """O3 (numpy int64 sums of squared differences), one plane of one frame
+    per task, over a bounded sample of the batch."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    work = _psnr_int_planes(ref, dist, planes, w, h)
+    t = time.perf_counter()
+    oracle.int_noise(work[0][2], work[0][3])
+    one = max(time.perf_counter() - t, 1e-6)
+    passes = max(1, min(50, int(12.0 / (one * len(work)))))
+    items = [x for _ in range(passes) for x in work]
+    t = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda x: oracle.int_noise(x[2], x[3]), items))
+    wall = time.perf_counter() - t
+    frames = passes * ref.shape[0]
+    return {
+        "value": round(frames / wall, 3), "unit": "frames/s", "cores": threads, "kind": "oracle",
+        "sample": f"{passes} passes over the {ref.shape[0]} frames of the batch "
+                  f"({'all three planes' if planes is not None else 'the plane pair'}), O3 "
+                  "(numpy int64), one plane of one frame per task",
+    }
+
+
 def time_oracle(ref, dist, bpc, bytes_per_frame, threads):
     """The oracle as it stands (the CPU's sequential double loop), one frame
     per task on `threads` threads, over a bounded sample of the batch."""
@@ -327,8 +395,61 @@ def load_or_generate(number, cache_dir):
     return ref, dist
 
 
+class Mode:
+    """What one bench step runs, per mode: the sums per slot (int64), the
+    enqueue of one step, the host conclusion of one slot, the step's
+    algorithmic bytes and the gate of the last step."""
+
+
+def make_mode(args, vqx, L, hip, np, torch, dev, st, wl, ref_np, dist_np, planes, bufs):
+    """Builds the Mode of ``args.mode``.  Device outputs are pinned host
+    memory written through its device mapping; ``bufs`` holds the two
+    resident copies of the batch."""
+    w, h, bpc, nframes = wl.w, wl.h, wl.bpc, wl.nframes
+    m = Mode()
+    m.name = args.mode
+    m.per_step_events = args.mode == "exact"
+    if args.mode == "exact":
+        m.width = 5 * nframes
+        m.ws_bytes = vqx.plane_stats_workspace_bytes(w, h, bpc, nframes)
+        m.metric = METRIC
+        m.kernel = "stage1_u8" if bpc == 8 else "stage1_u16"
+        m.kernel_label = m.kernel
+        m.sources = STAGE1_SOURCES
+        m.alg_bytes = wl.bytes_per_frame * nframes
+    elif args.mode == "cpu-order":
+        m.width = 10 * nframes
+        m.ws_bytes = vqx.plane_stats_cpu_order_workspace_bytes(w, h, bpc, nframes)
+        m.metric = METRIC_CPU_ORDER
+        m.kernel = "cpu_order_step"
+        m.kernel_label = ("cpu_order_step (stage1_u16, stage2_combine, cpu_order_prefix, cpu_order_maps, "
+                          "cpu_order_walk)")
+        m.sources = CPU_ORDER_SOURCES
+        m.alg_bytes = wl.bytes_per_frame * nframes + past53_bytes(ref_np, dist_np, bpc)
+    elif args.mode == "psnr-int":
+        m.width = nframes
+        m.ws_bytes = vqx.plane_view_workspace_bytes(w, h, bpc, nframes)
+        m.metric = METRIC_PSNR_INT
+        m.kernel = "psnr_int_step"
+        m.kernel_label = "psnr_int_step (view_stage1 integer noise, view_combine)"
+        m.sources = VIEW_SOURCES
+        m.alg_bytes = wl.bytes_per_frame * nframes
+    else:  # yuv420
+        m.width = 3 * nframes
+        m.ws_bytes = max(vqx.plane_view_workspace_bytes(pw, ph, bpc, nframes) for _, pw, ph in planes)
+        m.metric = METRIC_YUV420
+        m.kernel = "psnr_int_yuv420_step"
+        m.kernel_label = "psnr_int_yuv420_step (view_stage1 integer noise, view_combine; Y, U, V)"
+        m.sources = VIEW_SOURCES
+        m.alg_bytes = 2 * ref_np.shape[1] * wl.bytes_per_sample * nframes
+    m.ws = torch.empty(m.ws_bytes, dtype=torch.uint8, device=dev)
+    return m
+
+
 def main(argv=None):
     args = parse_args(argv)
+    if args.workload is None:
+        args.workload = 2 if args.mode == "yuv420" else 5
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -350,7 +471,11 @@ def main(argv=None):
     w, h, bpc, nframes = wl.w, wl.h, wl.bpc, wl.nframes
 
     t_gen = time.perf_counter()
-    ref_np, dist_np = load_or_generate(args.workload, args.input_cache)
+    planes = None
+    if args.mode == "yuv420":
+        ref_np, dist_np, planes = synth.planar_yuv(args.workload, "420")
+    else:
+        ref_np, dist_np = load_or_generate(args.workload, args.input_cache)
     t_gen = time.perf_counter() - t_gen
 
     # two resident copies of the batch, alternated step by step
@@ -358,42 +483,30 @@ def main(argv=None):
     d0 = torch.from_numpy(dist_np).to(dev)
     bufs = [(r0, d0), (r0.clone(), d0.clone())]
     # Sums land directly in pinned host memory that the GPU writes through
-    # (zero-copy): stage 2 stores 40 bytes per frame there, and no copy
-    # kernel runs.  `depth` groups of slots, so that the GPU always has
-    # several groups queued while the host concludes the oldest one.
+    # (zero-copy): the last kernel of a step stores its few bytes per frame
+    # there, and no copy kernel runs.  `depth` groups of slots, so that the
+    # GPU always has several groups queued while the host concludes the
+    # oldest one.
     group = 8
     depth = 4  # groups in flight: ~5 ms of queued work absorbs host hiccups
     nslots = depth * group
-    cpu_order = args.mode == "cpu-order"
-    # per slot: the exact sums {noise[F], moments[F][4]}, and in the
-    # CPU-order mode the CPU's sums after them in the same layout
-    width = (10 if cpu_order else 5) * nframes
-    sums = torch.zeros((nslots, width), dtype=torch.int64, pin_memory=True)
-    noise = [sums[s, :nframes] for s in range(nslots)]
-    moments = [sums[s, nframes:5 * nframes].view(nframes, 4) for s in range(nslots)]
-    cnoise = [sums[s, 5 * nframes:6 * nframes] for s in range(nslots)] if cpu_order else None
-    cmoments = [sums[s, 6 * nframes:].view(nframes, 4) for s in range(nslots)] if cpu_order else None
     stream = torch.cuda.current_stream(dev)
     st = stream.cuda_stream
-    if cpu_order:
-        ws_bytes = vqx.plane_stats_cpu_order_workspace_bytes(w, h, bpc, nframes)
-    else:
-        ws_bytes = vqx.plane_stats_workspace_bytes(w, h, bpc, nframes)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     hip = HipEvents(vqx.hip_runtime())
     L = vqx.lib()
-    noise_dev = [hip.device_pointer(t.data_ptr()) for t in noise]
-    moments_dev = [hip.device_pointer(t.data_ptr()) for t in moments]
-    if cpu_order:
-        cnoise_dev = [hip.device_pointer(t.data_ptr()) for t in cnoise]
-        cmoments_dev = [hip.device_pointer(t.data_ptr()) for t in cmoments]
+    mode = make_mode(args, vqx, L, hip, np, torch, dev, st, wl, ref_np, dist_np, planes, bufs)
+    width = mode.width
+    sums = torch.zeros((nslots, width), dtype=torch.int64, pin_memory=True)
+    sums_dev = [hip.device_pointer(sums[s].data_ptr()) for s in range(nslots)]
+    sums_np = sums.numpy()
+    ws, ws_bytes = mode.ws, mode.ws_bytes
     total = args.warmup + args.steps
-    # exact mode: stage 1 of every step stamps its own events; CPU-order
-    # mode: events around each group of steps
-    ev_begin = {i: hip.create() for i in range(total)} if not cpu_order else {}
+    # exact mode: stage 1 of every step stamps its own events; other modes:
+    # events around each group of steps
+    ev_begin = {i: hip.create() for i in range(total)} if mode.per_step_events else {}
     ev_end = {i: hip.create() for i in ev_begin}
     ngroups = (total + group - 1) // group + 1
-    ev_start = [hip.create() for _ in range(ngroups)] if cpu_order else []
+    ev_start = [hip.create() for _ in range(ngroups)] if not mode.per_step_events else []
     ev_done = [hip.create() for _ in range(ngroups)]
     torch.cuda.synchronize()
 
@@ -402,36 +515,58 @@ def main(argv=None):
     # into a preallocated history (to check afterwards that every step gave
     # the same sums).  Allocating numpy temporaries per batch stalled the
     # host for up to tens of milliseconds after the batch generation.
-    sums_np = sums.numpy()
-    concl = np.zeros((nslots, nframes, 6), dtype=np.float64)
+    ncon = 6 if args.mode in ("exact", "cpu-order") else 2
+    nrows = nframes * (3 if args.mode == "yuv420" else 1)
+    concl = np.zeros((nslots, nrows, ncon), dtype=np.float64)
     concl_ptr = [concl[s].ctypes.data for s in range(nslots)]
-    # the sums concluded: the exact ones, or in the CPU-order mode the CPU's
-    noise_ptr = [(cnoise if cpu_order else noise)[s].data_ptr() for s in range(nslots)]
-    moments_ptr = [(cmoments if cpu_order else moments)[s].data_ptr() for s in range(nslots)]
+    base_ptr = [sums[s].data_ptr() for s in range(nslots)]
     history = np.zeros((total, width), dtype=np.int64)
+    plane_dims = [(w, h)] if planes is None else [(pw, ph) for _, pw, ph in planes]
+    itemsize = 8
 
     def enqueue(i):
         s = i % nslots
         r, d = bufs[i % 2]
-        if cpu_order:
-            rc = L.vqx_plane_stats_batch_cpu_order_ws(r.data_ptr(), d.data_ptr(), w, h, bpc, nframes,
-                                                      noise_dev[s], moments_dev[s], cnoise_dev[s],
-                                                      cmoments_dev[s], ws.data_ptr(), ws_bytes, st)
-        else:
+        o = sums_dev[s]
+        if args.mode == "exact":
             rc = L.vqx_plane_stats_batch_ws_timed(r.data_ptr(), d.data_ptr(), w, h, bpc, nframes,
-                                                  noise_dev[s], moments_dev[s], ws.data_ptr(), ws_bytes,
+                                                  o, o + itemsize * nframes, ws.data_ptr(), ws_bytes,
                                                   st, ev_begin.get(i), ev_end.get(i))
+        elif args.mode == "cpu-order":
+            rc = L.vqx_plane_stats_batch_cpu_order_ws(r.data_ptr(), d.data_ptr(), w, h, bpc, nframes,
+                                                      o, o + itemsize * nframes, o + itemsize * 5 * nframes,
+                                                      o + itemsize * 6 * nframes, ws.data_ptr(), ws_bytes, st)
+        elif args.mode == "psnr-int":
+            rc = L.vqx_psnr_int_view_ws(r.data_ptr(), w, w * h, d.data_ptr(), w, w * h, w, h, bpc, nframes,
+                                        o, ws.data_ptr(), ws_bytes, st)
+        else:
+            fs = ref_np.shape[1]
+            rc = 0
+            for p, (off, pw, ph) in enumerate(planes):
+                rc = rc or L.vqx_psnr_int_view_ws(r.data_ptr() + off * wl.bytes_per_sample, pw, fs,
+                                                  d.data_ptr() + off * wl.bytes_per_sample, pw, fs, pw, ph, bpc,
+                                                  nframes, o + itemsize * p * nframes, ws.data_ptr(), ws_bytes,
+                                                  st)
         if rc != 0:
-            raise vqx.VqxError(rc, "libvqx entry point")
+            raise vqx.VqxError(rc, f"libvqx entry point ({args.mode})")
 
     def conclude(steps, done):
         hip.synchronize(done)
         for i in steps:
             s = i % nslots
-            rc = L.vqx_conclude_batch(noise_ptr[s], moments_ptr[s], w, h, bpc, nframes, 0.0,
-                                      concl_ptr[s])
-            if rc != 0:
-                raise vqx.VqxError(rc, "vqx_conclude_batch")
+            if args.mode in ("exact", "cpu-order"):
+                # the exact sums, or in the CPU-order mode the CPU's
+                off = 5 * nframes if args.mode == "cpu-order" else 0
+                rc = L.vqx_conclude_batch(base_ptr[s] + itemsize * off, base_ptr[s] + itemsize * (off + nframes),
+                                          w, h, bpc, nframes, 0.0, concl_ptr[s])
+                if rc != 0:
+                    raise vqx.VqxError(rc, "vqx_conclude_batch")
+            else:
+                for p, (pw, ph) in enumerate(plane_dims):
+                    rc = L.vqx_conclude_psnr_int_batch(base_ptr[s] + itemsize * p * nframes, pw, ph, bpc,
+                                                       nframes, 0.0, concl_ptr[s] + 2 * itemsize * p * nframes)
+                    if rc != 0:
+                        raise vqx.VqxError(rc, "vqx_conclude_psnr_int_batch")
             history[i] = sums_np[s]
 
     def run(first, count):
@@ -442,7 +577,7 @@ def main(argv=None):
         for steps in groups:
             if len(pending) == depth:
                 conclude(*pending.pop(0))
-            if cpu_order:
+            if not mode.per_step_events:
                 hip.record(ev_start[steps[0] // group], st)
             for i in steps:
                 enqueue(i)
@@ -466,15 +601,15 @@ def main(argv=None):
         if gc_was_enabled:
             gc.enable()
 
-    if cpu_order:
+    if mode.per_step_events:
+        step_ms = [hip.elapsed_ms(ev_begin[i], ev_end[i]) for i in ev_begin if i >= args.warmup]
+    else:
         # device time per step, from the events around each timed group
         step_ms = []
         for a in range(args.warmup, total, group):
             g = a // group
             n = min(group, total - a)
             step_ms += [hip.elapsed_ms(ev_start[g], ev_done[g]) / n] * n
-    else:
-        step_ms = [hip.elapsed_ms(ev_begin[i], ev_end[i]) for i in ev_begin if i >= args.warmup]
     for ev in list(ev_begin.values()) + list(ev_end.values()) + ev_start + ev_done:
         hip.destroy(ev)
 
@@ -483,9 +618,7 @@ def main(argv=None):
         bad = int(np.nonzero(np.any(history != history[total - 1], axis=1))[0][0])
         print(f"step {bad} differs from the last step", file=sys.stderr)
         return 1
-    last_noise = history[total - 1, :nframes]
-    last_moments = history[total - 1, nframes:5 * nframes].reshape(nframes, 4)
-    # the library's conclusion of the last step, from the same sums
+    last = history[total - 1]
     last_concl = concl[(total - 1) % nslots].copy()
 
     if args.calibrate_copy:
@@ -499,21 +632,14 @@ def main(argv=None):
         del src, dst
 
     bytes_per_frame = wl.bytes_per_frame
-    bytes_per_launch = bytes_per_frame * nframes
+    bytes_per_step = ref_np[0].size * wl.bytes_per_sample * 2 * nframes
     mean_ms = statistics.fmean(step_ms)
-    wname = f"{w}x{h}x{nframes}_{bpc}bit"
-    if cpu_order:
-        kernel = "cpu_order_step"
-        alg_bytes = bytes_per_launch + past53_bytes(ref_np, dist_np, bpc)
-        traffic = stored_traffic(kernel, wname, CPU_ORDER_SOURCES)
-    else:
-        kernel = "stage1_u8" if bpc == 8 else "stage1_u16"
-        alg_bytes = bytes_per_launch
-        traffic = stored_traffic(kernel, wname)
-    achieved = alg_bytes / (mean_ms * 1e-3) / 1e9
+    wname = f"{w}x{h}x{nframes}_{bpc}bit" + ("_yuv420" if args.mode == "yuv420" else "")
+    traffic = stored_traffic(mode.kernel, wname, tuple(mode.sources))
+    achieved = mode.alg_bytes / (mean_ms * 1e-3) / 1e9
 
     out = {
-        "metric": METRIC_CPU_ORDER if cpu_order else METRIC,
+        "metric": mode.metric,
         "value": round(args.steps * nframes / elapsed, 1),
         "unit": "frames/s",
         "n_gpus": 1,
@@ -523,20 +649,20 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32 squares, u64 sums",
+        "dtype": "fp32 squares, u64 sums" if args.mode in ("exact", "cpu-order") else "u32 squares, u64 sums",
         "data": "synthetic",
         "config": {
             "workload": f"{w}x{h} {bpc}-bit luma pair, {nframes} frames, "
-                        f"{'uint8' if bpc == 8 else 'uint16'} ({wl.recipe})",
+                        f"{'uint8' if bpc == 8 else 'uint16'} ({wl.recipe})"
+                        + (", as planar 4:2:0 frames (Y, U, V each drawn with the recipe at its size)"
+                           if args.mode == "yuv420" else ""),
             "w": w, "h": h, "bpc": bpc, "nframes": nframes, "mode": args.mode,
-            "bytes_per_step": bytes_per_launch,
-            "hbm_gbs_whole_step": round(bytes_per_launch * args.steps / elapsed / 1e9, 1),
+            "bytes_per_step": bytes_per_step,
+            "hbm_gbs_whole_step": round(bytes_per_step * args.steps / elapsed / 1e9, 1),
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": (kernel if not cpu_order else
-                       "cpu_order_step (stage1_u16, stage2_combine, cpu_order_prefix, cpu_order_maps, "
-                       "cpu_order_walk)"),
+            "kernel": mode.kernel_label,
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -544,21 +670,26 @@ def main(argv=None):
             "traffic": traffic,
             "kernel_us_mean": round(mean_ms * 1e3, 2),
             "kernel_us_median": round(statistics.median(step_ms) * 1e3, 2),
-            "algorithmic_bytes_per_launch": alg_bytes,
+            "algorithmic_bytes_per_launch": mode.alg_bytes,
         },
         "generation_s": round(t_gen, 1),
     }
 
     if not args.no_cpu_baseline:
         threads = cpu_threads()
-        if cpu_order:
-            last = history[total - 1]
+        if args.mode == "cpu-order":
             exact = np.concatenate([last[:nframes, None], last[nframes:5 * nframes].reshape(nframes, 4)], 1)
             cpu = np.concatenate([last[5 * nframes:6 * nframes, None], last[6 * nframes:].reshape(nframes, 4)], 1)
             parity = gate_cpu_order(ref_np, dist_np, bpc, exact, cpu, last_concl, threads)
+        elif args.mode == "exact":
+            parity = gate_exact(ref_np, dist_np, bpc, last[:nframes], last[nframes:].reshape(nframes, 4),
+                                last_concl, threads)
         else:
-            parity = gate_exact(ref_np, dist_np, bpc, last_noise, last_moments, last_concl, threads)
-        out["cpu_baseline"] = time_oracle(ref_np, dist_np, bpc, bytes_per_frame, threads)
+            parity = gate_psnr_int(ref_np, dist_np, bpc, planes, w, h, last, last_concl)
+        if args.mode in ("exact", "cpu-order"):
+            out["cpu_baseline"] = time_oracle(ref_np, dist_np, bpc, bytes_per_frame, threads)
+        else:
+            out["cpu_baseline"] = time_oracle_psnr_int(ref_np, dist_np, bpc, planes, w, h, threads)
         out["parity"] = parity
         if parity["failures"]:
             print(json.dumps({"error": "timed batch does not match the oracle", "parity": parity}),

@@ -39,6 +39,8 @@ CSRC = os.path.join(ROOT, "exact_reductions_amd", "csrc")
 STAGE1_SOURCES = [os.path.join(CSRC, f) for f in ("plane_stats.hip", "reduce.h")]
 CPU_ORDER_SOURCES = STAGE1_SOURCES + [os.path.join(CSRC, "cpu_order.hip")]
 CPU_ORDER_KERNELS = ("stage1_u16", "stage2_combine", "cpu_order_prefix", "cpu_order_maps", "cpu_order_walk")
+VIEW_SOURCES = [os.path.join(CSRC, f) for f in ("plane_views.hip", "reduce.h")]
+VIEW_KERNELS = ("view_stage1", "view_combine")
 COPY_MIB = 1024
 WARMUP = 300
 
@@ -65,7 +67,7 @@ def rows(path):
 
 def short(name: str) -> str:
     for k in ("stage1_u16", "stage1_u8", "stage2_combine", "bitwise_not", "cpu_order_prefix",
-              "cpu_order_maps", "cpu_order_walk"):
+              "cpu_order_maps", "cpu_order_walk", "view_stage1", "view_combine"):
         if k in name:
             return k
     return name.split("(")[0][-60:]
@@ -73,31 +75,44 @@ def short(name: str) -> str:
 
 def main(argv=None):
     p = argparse.ArgumentParser()
-    p.add_argument("--workload", type=int, default=5)
+    p.add_argument("--workload", type=int, default=None)
     p.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "profiles"))
     p.add_argument("--work", default=os.path.join(ROOT, "gpurun_out", "rocprof"))
     p.add_argument("--cache", default="/tmp/vqx_inputs")
     p.add_argument("--steps", type=int, default=500)
-    p.add_argument("--mode", choices=("exact", "cpu-order"), default="exact")
+    p.add_argument("--mode", choices=("exact", "cpu-order", "psnr-int", "yuv420"), default="exact")
     args = p.parse_args(argv)
     cpu_order = args.mode == "cpu-order"
+    views = args.mode in ("psnr-int", "yuv420")
+    if args.workload is None:
+        args.workload = 2 if args.mode == "yuv420" else 5
 
     sys.path.insert(0, ROOT)
     import synth
     wl = synth.WORKLOADS[args.workload]
-    kernel = "cpu_order_step" if cpu_order else ("stage1_u8" if wl.bpc == 8 else "stage1_u16")
-    step_kernels = CPU_ORDER_KERNELS if cpu_order else (kernel,)
-    wname = f"{wl.w}x{wl.h}x{wl.nframes}_{wl.bpc}bit"
+    if cpu_order:
+        kernel, step_kernels, sources = "cpu_order_step", CPU_ORDER_KERNELS, CPU_ORDER_SOURCES
+    elif args.mode == "psnr-int":
+        kernel, step_kernels, sources = "psnr_int_step", VIEW_KERNELS, VIEW_SOURCES
+    elif args.mode == "yuv420":
+        kernel, step_kernels, sources = "psnr_int_yuv420_step", VIEW_KERNELS, VIEW_SOURCES
+    else:
+        kernel = "stage1_u8" if wl.bpc == 8 else "stage1_u16"
+        step_kernels, sources = (kernel,), STAGE1_SOURCES
+    wname = f"{wl.w}x{wl.h}x{wl.nframes}_{wl.bpc}bit" + ("_yuv420" if args.mode == "yuv420" else "")
     os.makedirs(args.out, exist_ok=True)
     os.makedirs(args.work, exist_ok=True)
     bench = ["python3", os.path.join(ROOT, "bench.py"), "--workload", str(args.workload),
              "--no-cpu-baseline", "--input-cache", args.cache, "--mode", args.mode]
     h = hashlib.sha256()
-    for path in (CPU_ORDER_SOURCES if cpu_order else STAGE1_SOURCES):
+    for path in sources:
         with open(path, "rb") as f:
             h.update(f.read())
     src_sha = h.hexdigest()
     alg = wl.bytes_per_frame * wl.nframes
+    if args.mode == "yuv420":
+        frame = wl.w * wl.h + 2 * (-(-wl.w // 2)) * (-(-wl.h // 2))
+        alg = 2 * frame * wl.bytes_per_sample * wl.nframes
     if cpu_order:
         import bench as bench_mod
         ref, dist = synth.generate(args.workload)
@@ -136,19 +151,24 @@ def main(argv=None):
     # times the dispatches after its warm-up ones
     trace = rows(find(tdir, "kernel_trace.csv"))
     timed_avg = {}
+    per_step = {}
     for kname in step_kernels:
         disp = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in trace
                       if short(r["Kernel_Name"]) == kname)
-        timed = [(e - b) / 1e3 for b, e in disp[WARMUP:]]
+        k = max(1, round(len(disp) / (WARMUP + args.steps)))  # dispatches of this kernel per step
+        timed = [(e - b) / 1e3 for b, e in disp[k * WARMUP:]]
         if timed:
             timed_avg[kname] = statistics.fmean(timed)
-            lines += ["", f"{kname}: dispatches {len(disp)} (the first {WARMUP} are the bench's warm-up)",
+            per_step[kname] = k
+            lines += ["", f"{kname}: dispatches {len(disp)}, {k} per step (the first {k * WARMUP} are the "
+                          "bench's warm-up)",
                       f"{kname}_avg_us_timed_dispatches: {statistics.fmean(timed):.2f}",
                       f"{kname}_median_us_timed_dispatches: {statistics.median(timed):.2f}"]
     if len(timed_avg) == len(step_kernels):
-        step_us = sum(timed_avg.values())
+        step_us = sum(timed_avg[k] * per_step[k] for k in step_kernels)
         gbs = alg / (step_us * 1e-6) / 1e9
-        lines += ["", f"kernel_avg_us: {step_us:.2f}" + ("  (sum of the step's kernels)" if cpu_order else ""),
+        lines += ["", f"kernel_avg_us: {step_us:.2f}" + ("  (sum of the step's kernels)" if len(step_kernels) > 1
+                                                         else ""),
                   f"kernel_algorithmic_bytes_per_launch: {alg}",
                   f"kernel_achieved_GBps: {gbs:.1f}", f"kernel_frac_of_8000_GBps: {gbs / 8000:.4f}"]
     if bench_line:
@@ -178,7 +198,7 @@ def main(argv=None):
     copy_bytes = COPY_MIB * (1 << 20)
     out = [
         f"# HBM traffic of {kernel}, {wl.name} ({wname}), from rocprofv3 counters"
-        + (f" (summed over {', '.join(step_kernels)})" if cpu_order else ""),
+        + (f" (summed over {', '.join(step_kernels)} per step)" if len(step_kernels) > 1 else ""),
         f"command_fetch: cd <repo> && {' '.join(shlex.quote(c) for c in cmds['FETCH_SIZE']).replace(ROOT + '/', '')}",
         f"command_write: cd <repo> && {' '.join(shlex.quote(c) for c in cmds['WRITE_SIZE']).replace(ROOT + '/', '')}",
         f"date_utc: {time.strftime('%Y-%m-%dT%H:%M:%SZ', time.gmtime())}",
@@ -202,8 +222,9 @@ def main(argv=None):
     if fetch_copy and write_copy and have:
         f_scale = copy_bytes / fetch_copy
         w_scale = copy_bytes / write_copy
-        fetch_b = sum(statistics.fmean(readings["FETCH_SIZE"][k]) for k in step_kernels) * f_scale
-        write_b = sum(statistics.fmean(readings["WRITE_SIZE"][k]) for k in step_kernels) * w_scale
+        ps = {k: per_step.get(k, 1) for k in step_kernels}
+        fetch_b = sum(statistics.fmean(readings["FETCH_SIZE"][k]) * ps[k] for k in step_kernels) * f_scale
+        write_b = sum(statistics.fmean(readings["WRITE_SIZE"][k]) * ps[k] for k in step_kernels) * w_scale
         out += [
             "",
             f"fetch_scale_bytes_per_unit: {f_scale:.4f}",
@@ -214,7 +235,7 @@ def main(argv=None):
             f"algorithmic_bytes_per_launch: {alg}",
             f"traffic_over_algorithmic: {(fetch_b + write_b) / alg:.4f}",
         ]
-        if cpu_order:
+        if len(step_kernels) > 1:
             for k in step_kernels:
                 out.append(f"  {k}: fetch {statistics.fmean(readings['FETCH_SIZE'][k]) * f_scale:.0f} "
                            f"write {statistics.fmean(readings['WRITE_SIZE'][k]) * w_scale:.0f} bytes per dispatch")

@@ -13,6 +13,7 @@ from .vqx import (  # noqa: F401
     conclude_moments,
     conclude_psnr,
     conclude_psnr_int,
+    conclude_psnr_int_batch,
     plane_stats_batch,
     plane_stats_batch_ws,
     plane_stats_view,

@@ -138,26 +138,35 @@ __device__ __forceinline__ Tile tile_of(int t, int w, int h, int rows_per_tile, 
 }
 
 // Walks j = threadIdx.x, + kThreads, ... over a range laid out as rows of
-// n items, keeping (row, column) without a division per step.
+// n items, keeping the item's column and, for each plane, the sample offset
+// of its row from the tile's first row -- adds only, no multiply per step.
 struct FlatWalk {
-    int row, col, drow, dcol, n;
-    __device__ __forceinline__ FlatWalk(int start, int n_)
-        : row(start / n_), col(start % n_), drow(kThreads / n_), dcol(kThreads % n_), n(n_)
+    int col, dcol, n;
+    int64_t off_r, off_d, step_r, step_d, rs_r, rs_d;
+    __device__ __forceinline__ FlatWalk(int start, int n_, int64_t rs_r_, int64_t rs_d_)
+        : col(start % n_), dcol(kThreads % n_), n(n_), rs_r(rs_r_), rs_d(rs_d_)
     {
+        const int row = start / n_, drow = kThreads / n_;
+        off_r = row * rs_r;
+        off_d = row * rs_d;
+        step_r = drow * rs_r;
+        step_d = drow * rs_d;
     }
     __device__ __forceinline__ void next()
     {
-        row += drow;
+        off_r += step_r;
+        off_d += step_d;
         col += dcol;
         if (col >= n) {
             col -= n;
-            ++row;
+            off_r += rs_r;
+            off_d += rs_d;
         }
     }
 };
 
 template <int kBytes>
-__device__ __forceinline__ const char *row_ptr(const PlaneView &P, int64_t frame, int y, int x)
+__device__ __forceinline__ const char *tile_base(const PlaneView &P, int64_t frame, int y, int x)
 {
     return static_cast<const char *>(P.base) +
            (frame * P.frame_stride + static_cast<int64_t>(y) * P.row_stride + x) * kBytes;
@@ -175,8 +184,8 @@ __device__ __forceinline__ void accumulate_tile(Acc &acc, const PlaneView &R, co
 {
     constexpr int V = 16 / kBytes;
     const int t = threadIdx.x;
-    const char *r0 = row_ptr<kBytes>(R, frame, T.y0, T.x0);
-    const char *d0 = row_ptr<kBytes>(D, frame, T.y0, T.x0);
+    const char *r0 = tile_base<kBytes>(R, frame, T.y0, T.x0);  // (x0, y0) of the tile
+    const char *d0 = tile_base<kBytes>(D, frame, T.y0, T.x0);
     const int phase_r = static_cast<int>(reinterpret_cast<uintptr_t>(r0) & 15);
     const int phase_d = static_cast<int>(reinterpret_cast<uintptr_t>(d0) & 15);
     // every row of the tile starts at the same offset within 16 bytes
@@ -190,11 +199,10 @@ __device__ __forceinline__ void accumulate_tile(Acc &acc, const PlaneView &R, co
         // the samples outside whole vectors, row by row
         if (edges > 0) {
             const int n = T.rows * edges;
-            FlatWalk fw(t, edges);
+            FlatWalk fw(t, edges, R.row_stride, D.row_stride);
             for (int s = t; s < n; s += kThreads, fw.next()) {
                 const int x = fw.col < head ? fw.col : head + nvec * V + (fw.col - head);
-                add_samples<kBytes>(acc, row_ptr<kBytes>(R, frame, T.y0 + fw.row, T.x0 + x),
-                                    row_ptr<kBytes>(D, frame, T.y0 + fw.row, T.x0 + x));
+                add_samples<kBytes>(acc, r0 + (fw.off_r + x) * kBytes, d0 + (fw.off_d + x) * kBytes);
             }
         }
         if (nvec == 0)
@@ -202,8 +210,10 @@ __device__ __forceinline__ void accumulate_tile(Acc &acc, const PlaneView &R, co
         // the whole vectors: one flat range across the rows, at most 8 per
         // lane, read in two groups of four; a lane past the end reads the
         // tile's first vector and drops it
+        const char *rv = r0 + head * kBytes;
+        const char *dv = d0 + head * kBytes;
         const int n = T.rows * nvec;
-        FlatWalk fw(t, nvec);
+        FlatWalk fw(t, nvec, R.row_stride, D.row_stride);
 #pragma unroll
         for (int g = 0; g < kTileVecs / kThreads; g += 4) {
             if (g * kThreads >= n)
@@ -212,12 +222,11 @@ __device__ __forceinline__ void accumulate_tile(Acc &acc, const PlaneView &R, co
             bool ok[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int j = t + (g + u) * kThreads;
-                ok[u] = j < n;
-                const int y = ok[u] ? T.y0 + fw.row : T.y0;
-                const int x = T.x0 + head + (ok[u] ? fw.col : 0) * V;
-                a[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row_ptr<kBytes>(R, frame, y, x)));
-                b[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row_ptr<kBytes>(D, frame, y, x)));
+                ok[u] = t + (g + u) * kThreads < n;
+                const int64_t xr = ok[u] ? fw.off_r + fw.col * V : 0;
+                const int64_t xd = ok[u] ? fw.off_d + fw.col * V : 0;
+                a[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(rv + xr * kBytes));
+                b[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(dv + xd * kBytes));
                 fw.next();
             }
 #pragma unroll
@@ -230,10 +239,9 @@ __device__ __forceinline__ void accumulate_tile(Acc &acc, const PlaneView &R, co
         // rows at different offsets within 16 bytes, or ref and dist at
         // different ones: sample by sample
         const int n = T.rows * T.cw;
-        FlatWalk fw(t, T.cw);
+        FlatWalk fw(t, T.cw, R.row_stride, D.row_stride);
         for (int s = t; s < n; s += kThreads, fw.next())
-            add_samples<kBytes>(acc, row_ptr<kBytes>(R, frame, T.y0 + fw.row, T.x0 + fw.col),
-                                row_ptr<kBytes>(D, frame, T.y0 + fw.row, T.x0 + fw.col));
+            add_samples<kBytes>(acc, r0 + (fw.off_r + fw.col) * kBytes, d0 + (fw.off_d + fw.col) * kBytes);
     }
 }
 

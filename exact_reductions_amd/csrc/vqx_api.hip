@@ -400,4 +400,20 @@ int vqx_conclude_psnr_int(uint64_t noise, int w, int h, int bpc, double psnr_max
     return VQX_OK;
 }
 
+int vqx_conclude_psnr_int_batch(const uint64_t *noise, int w, int h, int bpc, int nframes, double psnr_max,
+                                double *out)
+{
+    if (!noise || !out)
+        return VQX_E_NULL;
+    int rc = check_shape(w, h, bpc);
+    if (rc != VQX_OK)
+        return rc;
+    if (nframes < 1)
+        return VQX_E_NFRAMES;
+    for (int f = 0; f < nframes; ++f)
+        vqx_conclude_psnr_int(noise[f], w, h, bpc, psnr_max, &out[2 * static_cast<size_t>(f)],
+                              &out[2 * static_cast<size_t>(f) + 1]);
+    return VQX_OK;
+}
+
 }  // extern "C"

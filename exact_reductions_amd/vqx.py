@@ -37,6 +37,7 @@ SYMBOLS = (
     "vqx_plane_stats_view_ws",
     "vqx_psnr_int_view_ws",
     "vqx_conclude_psnr_int",
+    "vqx_conclude_psnr_int_batch",
 )
 
 
@@ -80,6 +81,7 @@ def lib() -> ctypes.CDLL:
             "vqx_plane_stats_view_ws": (i, [vp, i64, i64, vp, i64, i64, i, i, i, i, vp, vp, vp, sz, vp]),
             "vqx_psnr_int_view_ws": (i, [vp, i64, i64, vp, i64, i64, i, i, i, i, vp, vp, sz, vp]),
             "vqx_conclude_psnr_int": (i, [u64, i, i, i, d, ctypes.POINTER(d), ctypes.POINTER(d)]),
+            "vqx_conclude_psnr_int_batch": (i, [vp, i, i, i, i, d, vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -324,3 +326,12 @@ def conclude_psnr_int(noise: int, w: int, h: int, bpc: int, psnr_max: float = 0.
     _check(lib().vqx_conclude_psnr_int(int(noise), w, h, bpc, float(psnr_max), ctypes.byref(mse),
                                        ctypes.byref(db)), "conclude_psnr_int")
     return mse.value, db.value
+
+
+def conclude_psnr_int_batch(noise, w: int, h: int, bpc: int, psnr_max: float = 0.0) -> np.ndarray:
+    """[F][2] {mse, psnr_db} of the integer psnr twin from host noises."""
+    n = np.ascontiguousarray(np.asarray(noise).astype(np.uint64).reshape(-1))
+    out = np.zeros((n.shape[0], 2), dtype=np.float64)
+    _check(lib().vqx_conclude_psnr_int_batch(n.ctypes.data, w, h, bpc, n.shape[0], float(psnr_max),
+                                             out.ctypes.data), "conclude_psnr_int_batch")
+    return out

@@ -274,6 +274,15 @@ int vqx_psnr_int_view_ws(const void *ref, int64_t ref_row_stride, int64_t ref_fr
 int vqx_conclude_psnr_int(uint64_t noise, int w, int h, int bpc, double psnr_max, double *mse,
                           double *psnr_db);
 
+/*
+ * vqx_conclude_psnr_int for a batch (host only).
+ *   noise  host uint64[nframes]
+ *   out    host double[nframes][2]: {mse, psnr_db} per frame
+ * Errors: VQX_E_NULL, VQX_E_DIMS, VQX_E_BPC, VQX_E_NFRAMES.
+ */
+int vqx_conclude_psnr_int_batch(const uint64_t *noise, int w, int h, int bpc, int nframes,
+                                double psnr_max, double *out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,6 +11,7 @@ from .workloads import (  # noqa: F401
     odd_dark_bright,
     past53_fullrange,
     past53_mixed,
+    planar_yuv,
     sha256,
     uniform_planes,
 )

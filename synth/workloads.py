@@ -115,6 +115,35 @@ def generate(number: int, nframes: int | None = None, w: int | None = None, h: i
     return ref, dist
 
 
+CHROMA = {"420": (2, 2), "422": (2, 1), "444": (1, 1)}  # horizontal, vertical subsampling
+
+
+def planar_yuv(number: int, chroma: str = "420", nframes: int | None = None):
+    """Planar YUV frames of a workload: ``(ref, dist, planes)``.
+
+    ``ref`` and ``dist`` are ``[nframes][frame_samples]`` arrays, each frame
+    its Y plane then its U and V planes, row after row; ``planes`` lists
+    ``(offset, w, h)`` of the three planes inside a frame.  Each plane is drawn
+    with the workload's recipe at the plane's size, Y then U then V, frame
+    after frame, from one generator seeded like the workload.
+    """
+    wl = WORKLOADS[number]
+    nframes = wl.nframes if nframes is None else nframes
+    sx, sy = CHROMA[chroma]
+    cw, ch = -(-wl.w // sx), -(-wl.h // sy)
+    planes = [(0, wl.w, wl.h), (wl.w * wl.h, cw, ch), (wl.w * wl.h + cw * ch, cw, ch)]
+    frame = wl.w * wl.h + 2 * cw * ch
+    rng = np.random.Generator(np.random.PCG64(wl.seed + 7000))
+    ref = np.empty((nframes, frame), dtype=wl.dtype)
+    dist = np.empty((nframes, frame), dtype=wl.dtype)
+    for f in range(nframes):
+        for off, pw, ph in planes:
+            r, d = _frame_pair(number, rng, pw, ph)
+            ref[f, off:off + pw * ph] = r.ravel()
+            dist[f, off:off + pw * ph] = d.ravel()
+    return ref, dist, planes
+
+
 def uniform_planes(w: int, h: int, nframes: int, bpc: int, seed: int,
                    lo: int = 0, hi: int | None = None, container_max: bool = False):
     """Independent uniform ref and dist planes with values lo..hi.

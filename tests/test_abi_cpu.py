@@ -369,5 +369,14 @@ def test_psnr_int_conclusion_matches_oracle_bitwise(bpc):
     # past 2^53: one rounding of the integer, then the division
     big = (1 << 55) + 1
     assert vqx.conclude_psnr_int(big, 7680, 4320, 16)[0] == float(big) / (7680 * 4320)
+    noises = [int(v) for v in rng.integers(0, 1920 * 1080 * top * top + 1, size=7)] + [0]
+    batch = vqx.conclude_psnr_int_batch(noises, 1920, 1080, bpc, 50.0)
+    for k, n in enumerate(noises):
+        assert list(batch[k]) == [oracle.int_mse(n, 1920, 1080), oracle.int_psnr_db(n, 1920, 1080, bpc, 50.0)]
+    out = np.zeros(4)
+    L = vqx.lib()
+    assert L.vqx_conclude_psnr_int_batch(None, 4, 4, 8, 1, 0.0, out.ctypes.data) == vqx.E_NULL
+    assert L.vqx_conclude_psnr_int_batch(np.zeros(2, np.uint64).ctypes.data, 4, 4, 8, 0, 0.0,
+                                         out.ctypes.data) == vqx.E_NFRAMES
     assert vqx.lib().vqx_conclude_psnr_int(0, 0, 4, 8, 0.0, None, None) == vqx.E_DIMS
     assert vqx.lib().vqx_conclude_psnr_int(0, 4, 4, 17, 0.0, None, None) == vqx.E_BPC
