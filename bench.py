@@ -56,11 +56,15 @@ METRIC_CPU_ORDER = ("frames/s with the CPU's own rounding past 2^53 (sums bit-id
 METRIC_PSNR_INT = "frames/s of the integer psnr twin (exact uint64 sum of (ref - dist)^2 per frame)"
 METRIC_YUV420 = ("frames/s of the integer psnr twin on all three planes of planar 4:2:0 frames "
                  "(Y, U, V through plane views)")
+METRIC_HOST = ("frames/s of the exact sums of a batch in pinned host memory, PCIe upload included "
+               "(3840x2160 16-bit)")
+PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction, the published link rate
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "exact_reductions_amd", "csrc")
 STAGE1_SOURCES = [os.path.join(CSRC, f) for f in ("plane_stats.hip", "reduce.h")]
 CPU_ORDER_SOURCES = STAGE1_SOURCES + [os.path.join(CSRC, "cpu_order.hip")]
 VIEW_SOURCES = [os.path.join(CSRC, f) for f in ("plane_views.hip", "reduce.h")]
+HOST_SOURCES = STAGE1_SOURCES + [os.path.join(CSRC, "host_stream.hip")]
 UNIT_POWER = (2, 1, 1, 2, 2)  # noise, ref1, dist1, ref2, dist2: units 1/s^power
 
 
@@ -79,10 +83,13 @@ def parse_args(argv=None):
                    help="skip the oracle leg (and with it the parity gate); for profiler runs")
     p.add_argument("--input-cache", default=None, metavar="DIR",
                    help="keep the generated batch as .npy files in DIR and reuse them")
-    p.add_argument("--mode", choices=("exact", "cpu-order", "psnr-int", "yuv420"), default="exact",
+    p.add_argument("--mode", choices=("exact", "cpu-order", "psnr-int", "yuv420", "host"), default="exact",
                    help="exact: the exact sums (default); cpu-order: also the CPU's rounding past 2^53; "
                         "psnr-int: the integer psnr twin; yuv420: the integer psnr twin on the Y, U and V "
-                        "planes of planar 4:2:0 frames")
+                        "planes of planar 4:2:0 frames; host: the exact sums of a batch in pinned host "
+                        "memory, uploads overlapped with the reduction")
+    p.add_argument("--frames-per-upload", type=int, default=4,
+                   help="host mode: frames per upload")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="after the timed steps, run 3 elementwise kernels that each read and "
                         "write MIB MiB (the known-size kernel that scales the HBM counters)")
@@ -395,6 +402,114 @@ def load_or_generate(number, cache_dir):
     return ref, dist
 
 
+def run_host_mode(args, np, torch, vqx, wl, ref_np, dist_np, t_gen):
+    """The host-fed mode: every step reduces the whole batch from pinned
+    host memory (vqx_plane_stats_host_ws returns when it is done), so a
+    step's wall time is the PCIe-inclusive time.  Also times a plain upload
+    of the same bytes (two hipMemcpyAsync calls, no reduction) for the link
+    rate this host reaches."""
+    w, h, bpc, nframes = wl.w, wl.h, wl.bpc, wl.nframes
+    dev = torch.device("cuda:0")
+    L = vqx.lib()
+    hip = HipEvents(vqx.hip_runtime())
+    r = torch.from_numpy(ref_np).pin_memory()
+    d = torch.from_numpy(dist_np).pin_memory()
+    out = torch.zeros(5 * nframes, dtype=torch.int64, pin_memory=True)
+    out_dev = hip.device_pointer(out.data_ptr())
+    fpu = args.frames_per_upload
+    ws_bytes = vqx.plane_stats_host_workspace_bytes(w, h, bpc, fpu)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    st = torch.cuda.current_stream(dev).cuda_stream
+    copy = torch.cuda.Stream(dev)  # default priority
+    history = np.zeros((args.warmup + args.steps, 5 * nframes), dtype=np.int64)
+
+    def step(i):
+        rc = L.vqx_plane_stats_host_ws(r.data_ptr(), d.data_ptr(), w, h, bpc, nframes, fpu, out_dev,
+                                       out_dev + 8 * nframes, ws.data_ptr(), ws_bytes, st, copy.cuda_stream)
+        if rc != 0:
+            raise vqx.VqxError(rc, "vqx_plane_stats_host_ws")
+        history[i] = out.numpy()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    times = []
+    for i in range(args.warmup, args.warmup + args.steps):
+        t = time.perf_counter()
+        step(i)
+        times.append(time.perf_counter() - t)
+    elapsed = time.perf_counter() - t0
+    if not np.all(history == history[-1]):
+        print("the steps disagree", file=sys.stderr)
+        return 1
+
+    # the link alone: the same bytes uploaded into device memory, no kernels
+    dst_r = torch.empty(r.shape, dtype=r.dtype, device=dev)
+    dst_d = torch.empty(d.shape, dtype=d.dtype, device=dev)
+    copy_s = []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        dst_r.copy_(r, non_blocking=True)
+        dst_d.copy_(d, non_blocking=True)
+        torch.cuda.synchronize()
+        copy_s.append(time.perf_counter() - t)
+    link_gbs = 2 * ref_np.nbytes / min(copy_s) / 1e9
+
+    upload = 2 * ref_np.nbytes
+    mean_s = statistics.fmean(times)
+    achieved = upload / mean_s / 1e9
+    result = {
+        "metric": METRIC_HOST,
+        "value": round(args.steps * nframes / elapsed, 1),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32 squares, u64 sums",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w}x{h} {bpc}-bit luma pair, {nframes} frames, "
+                        f"{'uint8' if bpc == 8 else 'uint16'} ({wl.recipe}), in pinned host memory",
+            "w": w, "h": h, "bpc": bpc, "nframes": nframes, "mode": "host",
+            "frames_per_upload": fpu, "bytes_per_step": upload,
+        },
+        "roofline": {
+            "bound": "pcie",
+            "kernel": "host-fed step (H2D uploads overlapped with stage1_u16 + stage2_combine)",
+            "achieved": round(achieved, 2),
+            "peak": PCIE_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PCIE_PEAK_GBS, 4),
+            "traffic": None,
+            "step_ms_mean": round(mean_s * 1e3, 3),
+            "step_ms_median": round(statistics.median(times) * 1e3, 3),
+            "algorithmic_bytes_per_launch": upload,
+            "plain_upload_gbs_this_host": round(link_gbs, 2),
+            "frac_of_plain_upload": round(achieved / link_gbs, 4),
+        },
+        "generation_s": round(t_gen, 1),
+    }
+    if not args.no_cpu_baseline:
+        threads = cpu_threads()
+        last = history[-1]
+        concl = vqx.conclude_batch(last[:nframes], last[nframes:].reshape(nframes, 4), w, h, bpc, 0.0)
+        result["parity"] = gate_exact(ref_np, dist_np, bpc, last[:nframes], last[nframes:].reshape(nframes, 4),
+                                      concl, threads)
+        result["cpu_baseline"] = time_oracle(ref_np, dist_np, bpc, wl.bytes_per_frame, threads)
+        if result["parity"]["failures"]:
+            print(json.dumps({"error": "timed batch does not match the oracle", "parity": result["parity"]}),
+                  file=sys.stderr)
+            return 1
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 class Mode:
     """What one bench step runs, per mode: the sums per slot (int64), the
     enqueue of one step, the host conclusion of one slot, the step's
@@ -477,6 +592,10 @@ def main(argv=None):
     else:
         ref_np, dist_np = load_or_generate(args.workload, args.input_cache)
     t_gen = time.perf_counter() - t_gen
+    if args.mode == "host":
+        if args.steps == 500 and args.warmup == 300:  # the defaults of the device-resident modes
+            args.steps, args.warmup = 20, 3
+        return run_host_mode(args, np, torch, vqx, wl, ref_np, dist_np, t_gen)
 
     # two resident copies of the batch, alternated step by step
     r0 = torch.from_numpy(ref_np).to(dev)

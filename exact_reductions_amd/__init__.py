@@ -16,6 +16,8 @@ from .vqx import (  # noqa: F401
     conclude_psnr_int_batch,
     plane_stats_batch,
     plane_stats_batch_ws,
+    plane_stats_host,
+    plane_stats_host_workspace_bytes,
     plane_stats_view,
     plane_stats_workspace_bytes,
     plane_view_workspace_bytes,

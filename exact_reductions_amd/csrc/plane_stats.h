@@ -89,6 +89,20 @@ hipError_t launch_view_stats(const ViewGeometry &g, const PlaneView &ref, const 
 hipError_t launch_view_psnr_int(const ViewGeometry &g, const PlaneView &ref, const PlaneView &dist,
                                 uint64_t *out_noise, uint64_t *partials, hipStream_t stream);
 
+// Workspace of the host-fed form: two staging slots (ref and dist planes of
+// frames_per_upload frames each) and the stage-1 records of one sub-batch.
+struct HostStreamLayout {
+    size_t plane_bytes;  // one plane of frames_per_upload frames
+    size_t ref[2], dist[2], partials, bytes;
+};
+HostStreamLayout host_stream_layout(int w, int h, int bpc, int frames_per_upload);
+
+// Uploads the batch from host memory in sub-batches on `copy` while
+// reducing earlier sub-batches on `compute`; returns when all is done.
+hipError_t run_host_stream(int w, int h, int bpc, int nframes, int frames_per_upload, const void *ref_host,
+                           const void *dist_host, uint64_t *out_noise, uint64_t *out_moments, void *workspace,
+                           hipStream_t compute, hipStream_t copy);
+
 // Workspace of the CPU-order form: byte offsets of its parts.
 struct CpuOrderLayout {
     size_t records, prefix, totals, maps, bytes;

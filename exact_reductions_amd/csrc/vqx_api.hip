@@ -271,6 +271,59 @@ int vqx_plane_stats_batch_cpu_order_ws(const void *ref, const void *dist, int w,
     return VQX_OK;
 }
 
+int vqx_plane_stats_host_workspace_bytes(int w, int h, int bpc, int frames_per_upload, size_t *bytes)
+{
+    if (!bytes)
+        return VQX_E_NULL;
+    int rc = check_batch(w, h, bpc, frames_per_upload);
+    if (rc != VQX_OK)
+        return rc;
+    *bytes = vqx::host_stream_layout(w, h, bpc, frames_per_upload).bytes;
+    return VQX_OK;
+}
+
+int vqx_plane_stats_host_ws(const void *ref_host, const void *dist_host, int w, int h, int bpc, int nframes,
+                            int frames_per_upload, uint64_t *out_noise, uint64_t *out_moments, void *workspace,
+                            size_t workspace_bytes, void *stream, void *copy_stream)
+{
+    if (!ref_host || !dist_host || !out_noise || !out_moments)
+        return VQX_E_NULL;
+    int rc = check_shape(w, h, bpc);
+    if (rc != VQX_OK)
+        return rc;
+    if (nframes < 1)
+        return VQX_E_NFRAMES;
+    rc = check_batch(w, h, bpc, frames_per_upload);
+    if (rc != VQX_OK)
+        return rc;
+    if (!aligned(out_noise, 8) || !aligned(out_moments, 8))
+        return VQX_E_ALIGN;
+    if (!workspace || !aligned(workspace, 16) ||
+        workspace_bytes < vqx::host_stream_layout(w, h, bpc, frames_per_upload).bytes)
+        return VQX_E_WORKSPACE;
+    rc = device_ready();
+    if (rc != VQX_OK)
+        return rc;
+    hipStream_t copy = static_cast<hipStream_t>(copy_stream);
+    bool own = false;
+    if (!copy) {
+        if (hipStreamCreateWithFlags(&copy, hipStreamNonBlocking) != hipSuccess) {
+            (void)hipGetLastError();
+            return VQX_E_HIP;
+        }
+        own = true;
+    }
+    hipError_t err = vqx::run_host_stream(w, h, bpc, nframes, frames_per_upload, ref_host, dist_host, out_noise,
+                                          out_moments, workspace, static_cast<hipStream_t>(stream), copy);
+    if (own)
+        (void)hipStreamDestroy(copy);
+    if (err != hipSuccess) {
+        (void)hipGetLastError();
+        return VQX_E_HIP;
+    }
+    return VQX_OK;
+}
+
 int vqx_conclude_psnr(uint64_t noise, int w, int h, int bpc, double psnr_max, double *mse,
                       double *psnr_db)
 {

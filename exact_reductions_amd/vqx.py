@@ -38,6 +38,8 @@ SYMBOLS = (
     "vqx_psnr_int_view_ws",
     "vqx_conclude_psnr_int",
     "vqx_conclude_psnr_int_batch",
+    "vqx_plane_stats_host_workspace_bytes",
+    "vqx_plane_stats_host_ws",
 )
 
 
@@ -82,6 +84,8 @@ def lib() -> ctypes.CDLL:
             "vqx_psnr_int_view_ws": (i, [vp, i64, i64, vp, i64, i64, i, i, i, i, vp, vp, sz, vp]),
             "vqx_conclude_psnr_int": (i, [u64, i, i, i, d, ctypes.POINTER(d), ctypes.POINTER(d)]),
             "vqx_conclude_psnr_int_batch": (i, [vp, i, i, i, i, d, vp]),
+            "vqx_plane_stats_host_workspace_bytes": (i, [i, i, i, i, ctypes.POINTER(sz)]),
+            "vqx_plane_stats_host_ws": (i, [vp, vp, i, i, i, i, i, vp, vp, vp, sz, vp, vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -335,3 +339,41 @@ def conclude_psnr_int_batch(noise, w: int, h: int, bpc: int, psnr_max: float = 0
     _check(lib().vqx_conclude_psnr_int_batch(n.ctypes.data, w, h, bpc, n.shape[0], float(psnr_max),
                                              out.ctypes.data), "conclude_psnr_int_batch")
     return out
+
+
+# ---------------------------------------------------------- host-fed batches
+def plane_stats_host_workspace_bytes(w: int, h: int, bpc: int, frames_per_upload: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().vqx_plane_stats_host_workspace_bytes(w, h, bpc, frames_per_upload, ctypes.byref(out)),
+           "plane_stats_host_workspace_bytes")
+    return out.value
+
+
+def plane_stats_host(ref, dist, bpc: int, frames_per_upload: int = 4, device=0, stream=None, copy_stream=None):
+    """The five exact sums of a batch held in host memory (CPU tensors,
+    pinned for overlap, or numpy arrays), uploaded frames_per_upload frames
+    at a time while earlier uploads are reduced.  Returns ``(noise [F],
+    moments [F][4])`` as int64 device tensors; the call returns when all is
+    done."""
+    import torch
+    r = torch.as_tensor(ref)
+    d = torch.as_tensor(dist)
+    if r.dim() == 2:
+        r, d = r.unsqueeze(0), d.unsqueeze(0)
+    if r.dim() != 3 or r.shape != d.shape:
+        raise ValueError("ref and dist must both be [nframes][h][w] (or [h][w])")
+    want = (torch.uint8,) if bpc == 8 else (torch.uint16, torch.int16)
+    if r.dtype not in want or d.dtype not in want:
+        raise TypeError(f"bpc {bpc} wants {'uint8' if bpc == 8 else 'uint16'} samples")
+    if r.is_cuda or d.is_cuda or not (r.is_contiguous() and d.is_contiguous()):
+        raise ValueError("ref and dist must be contiguous host tensors")
+    f, h, w = r.shape
+    dev = torch.device("cuda", device) if isinstance(device, int) else torch.device(device)
+    out = torch.empty(5 * f, dtype=torch.int64, device=dev)
+    ws = torch.empty(plane_stats_host_workspace_bytes(w, h, bpc, frames_per_upload), dtype=torch.uint8,
+                     device=dev)
+    cs = copy_stream.cuda_stream if copy_stream is not None else None
+    _check(lib().vqx_plane_stats_host_ws(r.data_ptr(), d.data_ptr(), w, h, bpc, f, frames_per_upload,
+                                         out[:f].data_ptr(), out[f:].data_ptr(), ws.data_ptr(), ws.numel(),
+                                         _stream_handle(dev, stream), cs), "plane_stats_host_ws")
+    return out[:f], out[f:].view(f, 4)

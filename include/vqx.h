@@ -175,6 +175,49 @@ int vqx_plane_stats_batch_cpu_order_ws(const void *ref, const void *dist, int w,
                                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Device scratch of vqx_plane_stats_host_ws for this frame shape and upload
+ * size: two staging slots of frames_per_upload frames of both planes, and
+ * stage 1's records of one upload.  Host-only.
+ * Errors: VQX_E_NULL, VQX_E_DIMS, VQX_E_BPC, VQX_E_NFRAMES (frames_per_upload).
+ */
+int vqx_plane_stats_host_workspace_bytes(int w, int h, int bpc, int frames_per_upload, size_t *bytes);
+
+/*
+ * The five sums of vqx_plane_stats_batch_ws for a batch that lies in HOST
+ * memory: the planes are uploaded frames_per_upload frames at a time into
+ * the workspace's two staging slots, and each upload overlaps the reduction
+ * of the one before (copies on copy_stream, kernels on stream, ordered by
+ * events).  As in the tool, a frame's work is queued after its upload
+ * [ADM, Decision].
+ *   ref_host, dist_host  host [nframes][h][w] samples (uint8 at 8 bits,
+ *                        uint16 otherwise), contiguous.  Page-locked memory
+ *                        (hipHostMalloc, or a pinned tensor) is what lets
+ *                        the copies run asynchronously and overlap; pageable
+ *                        memory gives the same results, without overlap.
+ *   frames_per_upload    frames per upload, >= 1 (a last, smaller upload
+ *                        takes the rest)
+ *   out_noise, out_moments  as vqx_plane_stats_batch_ws: device memory or
+ *                        pinned host memory mapped for the device
+ *   stream               where the kernels run (work queued on it before
+ *                        the call comes first); copy_stream: where the
+ *                        copies run, or NULL for a stream of the call's own
+ *                        (created and destroyed by the call, default
+ *                        priority).  One stream for both is allowed:
+ *                        the results are the same, nothing overlaps.
+ * The call returns when every frame has been reduced and every copy is
+ * done: the host buffers and the outputs are the caller's again.
+ * Errors: VQX_E_NULL, VQX_E_DIMS, VQX_E_BPC, VQX_E_NFRAMES (nframes or
+ * frames_per_upload < 1, or an upload too large for one dispatch),
+ * VQX_E_ALIGN (an output not 8-byte aligned), VQX_E_WORKSPACE (missing, not
+ * 16-byte aligned or smaller than vqx_plane_stats_host_workspace_bytes()),
+ * VQX_E_NO_DEVICE, VQX_E_HIP.
+ */
+int vqx_plane_stats_host_ws(const void *ref_host, const void *dist_host, int w, int h, int bpc,
+                            int nframes, int frames_per_upload, uint64_t *out_noise,
+                            uint64_t *out_moments, void *workspace, size_t workspace_bytes,
+                            void *stream, void *copy_stream);
+
+/*
  * float_psnr's conclusion from a frame's exact noise (host only).
  *   mse     = ((double)noise / s^2) / (w*h)    -- the 8-bit-scale mean
  *             squared error; (double) rounds once, to nearest even, and only

@@ -380,3 +380,45 @@ def test_psnr_int_conclusion_matches_oracle_bitwise(bpc):
                                          out.ctypes.data) == vqx.E_NFRAMES
     assert vqx.lib().vqx_conclude_psnr_int(0, 0, 4, 8, 0.0, None, None) == vqx.E_DIMS
     assert vqx.lib().vqx_conclude_psnr_int(0, 4, 4, 17, 0.0, None, None) == vqx.E_BPC
+
+
+# ------------------------------------------------------------ host-fed batches
+
+def test_host_workspace_bytes():
+    up = lambda x: (x + 255) // 256 * 256
+    # two staging slots of 4 frames of both planes, then 4 frames of records
+    plane = 3840 * 2160 * 2 * 4
+    assert vqx.plane_stats_host_workspace_bytes(3840, 2160, 16, 4) == up(4 * up(plane) + 507 * 4 * 64)
+    # 17x9 8-bit: 153 bytes per frame and plane, one chunk per frame
+    assert vqx.plane_stats_host_workspace_bytes(17, 9, 8, 3) == up(4 * up(153 * 3) + 3 * 64)
+    with pytest.raises(vqx.VqxError) as e:
+        vqx.plane_stats_host_workspace_bytes(17, 9, 8, 0)
+    assert e.value.status == vqx.E_NFRAMES
+
+
+def test_host_argument_errors(L):
+    b = _Buffers()
+    ws = np.zeros(8192, dtype=np.uint8)
+    base = (ws.ctypes.data + 255) // 256 * 256
+    need = vqx.plane_stats_host_workspace_bytes(16, 4, 8, 2)
+    f = L.vqx_plane_stats_host_ws
+    host = np.zeros(16 * 4 * 5, dtype=np.uint8)
+    h = host.ctypes.data
+    cases = [
+        ((None, h, 16, 4, 8, 5, 2, b.noise, b.moments, base, need, None, None), vqx.E_NULL),
+        ((h, h, 16, 4, 8, 5, 2, b.noise, None, base, need, None, None), vqx.E_NULL),
+        ((h, h, 0, 4, 8, 5, 2, b.noise, b.moments, base, need, None, None), vqx.E_DIMS),
+        ((h, h, 16, 4, 7, 5, 2, b.noise, b.moments, base, need, None, None), vqx.E_BPC),
+        ((h, h, 16, 4, 8, 0, 2, b.noise, b.moments, base, need, None, None), vqx.E_NFRAMES),
+        ((h, h, 16, 4, 8, 5, 0, b.noise, b.moments, base, need, None, None), vqx.E_NFRAMES),
+        ((h, h, 16, 4, 8, 5, 2, b.noise + 4, b.moments, base, need, None, None), vqx.E_ALIGN),
+        ((h, h, 16, 4, 8, 5, 2, b.noise, b.moments, base, need - 1, None, None), vqx.E_WORKSPACE),
+        ((h, h, 16, 4, 8, 5, 2, b.noise, b.moments, base + 8, need, None, None), vqx.E_WORKSPACE),
+        ((h, h, 16, 4, 8, 5, 2, b.noise, b.moments, None, need, None, None), vqx.E_WORKSPACE),
+    ]
+    for args, status in cases:
+        assert f(*args) == status, (args, status)
+    assert b.untouched()
+    if not _has_gpu():
+        assert f(h, h, 16, 4, 8, 5, 2, b.noise, b.moments, base, need, None, None) == vqx.E_NO_DEVICE
+        assert b.untouched()
