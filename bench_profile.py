@@ -41,6 +41,7 @@ CPU_ORDER_SOURCES = STAGE1_SOURCES + [os.path.join(CSRC, "cpu_order.hip")]
 CPU_ORDER_KERNELS = ("stage1_u16", "stage2_combine", "cpu_order_prefix", "cpu_order_maps", "cpu_order_walk")
 VIEW_SOURCES = [os.path.join(CSRC, f) for f in ("plane_views.hip", "reduce.h")]
 VIEW_KERNELS = ("view_stage1", "view_combine")
+HOST_SOURCES = STAGE1_SOURCES + [os.path.join(CSRC, "host_stream.hip")]
 COPY_MIB = 1024
 WARMUP = 300
 
@@ -73,6 +74,89 @@ def short(name: str) -> str:
     return name.split("(")[0][-60:]
 
 
+def _union(intervals):
+    out = []
+    for b, e in sorted(intervals):
+        if out and b <= out[-1][1]:
+            out[-1][1] = max(out[-1][1], e)
+        else:
+            out.append([b, e])
+    return out
+
+
+def _overlap(a, b):
+    """Total length of the intersection of two unions of intervals."""
+    i = j = 0
+    total = 0
+    while i < len(a) and j < len(b):
+        lo = max(a[i][0], b[j][0])
+        hi = min(a[i][1], b[j][1])
+        if hi > lo:
+            total += hi - lo
+        if a[i][1] < b[j][1]:
+            i += 1
+        else:
+            j += 1
+    return total
+
+
+def profile_host(args, wl, wname, bench, src_sha):
+    """Kernel and memory-copy trace of the host-fed mode: the uploads, the
+    kernels, and how much of the kernels' time runs while an upload is in
+    flight (the overlap the two streams are for)."""
+    rc = sh(bench + ["--steps", "1", "--warmup", "0", "--no-cpu-baseline"], 600,
+            os.path.join(args.work, "prime.log"))
+    if rc != 0:
+        return rc
+    tdir = os.path.join(args.work, "trace")
+    steps = 20
+    cmd = ["rocprofv3", "--kernel-trace", "--memory-copy-trace", "--stats", "--output-format", "csv", "-d", tdir,
+           "-o", "trace", "--"] + bench + ["--steps", str(steps), "--warmup", "3"]
+    rc = sh(cmd, 300, os.path.join(args.work, "trace.log"))
+    if rc != 0:
+        return rc
+    with open(os.path.join(args.work, "trace.log")) as f:
+        bench_line = [ln for ln in f.read().splitlines() if ln.startswith("{")]
+    kernels = rows(find(tdir, "kernel_trace.csv"))
+    copies = rows(find(tdir, "memory_copy_trace.csv"))
+    kint = _union([(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in kernels
+                   if short(r["Kernel_Name"]) in ("stage1_u16", "stage1_u8", "stage2_combine")])
+    h2d = [r for r in copies if "HOST_TO_DEVICE" in (r.get("Direction", "") + r.get("Kind", "")).upper()
+           or "H2D" in (r.get("Direction", "") + r.get("Kind", "")).upper()]
+    cint = _union([(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in h2d])
+    k_time = sum(e - b for b, e in kint)
+    c_time = sum(e - b for b, e in cint)
+    both = _overlap(kint, cint)
+    lines = [
+        f"# rocprofv3 kernel and memory-copy trace: host-fed step, {wl.name} ({wname}), "
+        f"{args.frames_per_upload} frames per upload",
+        f"command: cd <repo> && {' '.join(shlex.quote(c) for c in cmd).replace(ROOT + '/', '')}",
+        f"date_utc: {time.strftime('%Y-%m-%dT%H:%M:%SZ', time.gmtime())}",
+        f"kernel_source_sha256: {src_sha}",
+        "",
+        f"{'kernel':<18} {'calls':>6} {'avg_us':>10} {'total_us':>12}",
+    ]
+    for r in rows(find(tdir, "kernel_stats.csv")):
+        lines.append(f"{short(r.get('Name', '?')):<18} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
+                     f"{float(r['TotalDurationNs']) / 1e3:>12.1f}")
+    lines += [
+        "",
+        f"host_to_device_copies: {len(h2d)} (all copies in the trace: {len(copies)}; kinds: "
+        f"{sorted({(r.get('Kind', ''), r.get('Direction', '')) for r in copies})})",
+        f"copy_busy_ms: {c_time / 1e6:.2f}",
+        f"kernel_busy_ms: {k_time / 1e6:.2f}",
+        f"kernel_time_under_a_copy_ms: {both / 1e6:.2f}",
+        f"kernel_time_hidden_fraction: {both / k_time:.4f}" if k_time else "kernel_time_hidden_fraction: n/a",
+        "(the trace also holds the bench's plain-upload timing, copies with no kernel beside them)",
+    ]
+    if bench_line:
+        lines += ["", "bench line of the same run:", bench_line[-1]]
+    with open(os.path.join(args.out, f"host_step_{wname}_trace.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines), flush=True)
+    return 0
+
+
 def main(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--workload", type=int, default=None)
@@ -80,7 +164,8 @@ def main(argv=None):
     p.add_argument("--work", default=os.path.join(ROOT, "gpurun_out", "rocprof"))
     p.add_argument("--cache", default="/tmp/vqx_inputs")
     p.add_argument("--steps", type=int, default=500)
-    p.add_argument("--mode", choices=("exact", "cpu-order", "psnr-int", "yuv420"), default="exact")
+    p.add_argument("--frames-per-upload", type=int, default=4)
+    p.add_argument("--mode", choices=("exact", "cpu-order", "psnr-int", "yuv420", "host"), default="exact")
     args = p.parse_args(argv)
     cpu_order = args.mode == "cpu-order"
     views = args.mode in ("psnr-int", "yuv420")
@@ -96,6 +181,8 @@ def main(argv=None):
         kernel, step_kernels, sources = "psnr_int_step", VIEW_KERNELS, VIEW_SOURCES
     elif args.mode == "yuv420":
         kernel, step_kernels, sources = "psnr_int_yuv420_step", VIEW_KERNELS, VIEW_SOURCES
+    elif args.mode == "host":
+        kernel, step_kernels, sources = "host_step", ("stage1_u16", "stage2_combine"), HOST_SOURCES
     else:
         kernel = "stage1_u8" if wl.bpc == 8 else "stage1_u16"
         step_kernels, sources = (kernel,), STAGE1_SOURCES
@@ -104,6 +191,8 @@ def main(argv=None):
     os.makedirs(args.work, exist_ok=True)
     bench = ["python3", os.path.join(ROOT, "bench.py"), "--workload", str(args.workload),
              "--no-cpu-baseline", "--input-cache", args.cache, "--mode", args.mode]
+    if args.mode == "host":
+        bench += ["--frames-per-upload", str(args.frames_per_upload)]
     h = hashlib.sha256()
     for path in sources:
         with open(path, "rb") as f:
@@ -118,6 +207,9 @@ def main(argv=None):
         ref, dist = synth.generate(args.workload)
         alg += bench_mod.past53_bytes(ref, dist, wl.bpc)
         del ref, dist
+
+    if args.mode == "host":
+        return profile_host(args, wl, wname, bench, src_sha)
 
     # 0. make the input cache outside the profiler
     rc = sh(bench + ["--steps", "1", "--warmup", "0"], 600, os.path.join(args.work, "prime.log"))
