@@ -488,16 +488,23 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(const uint64_t *rec
 // Entry of chunk wg, square kk (kEntry uint64): the maps {dm0, dm1, flags}
 // of its kSlabs slabs in the predicted binade e, their maps in binade e + 1
 // (made only where the chunk's exact range reaches 2^(e+1), i.e. where the
-// CPU's sum probably changes binade inside it; flags 0 otherwise), and the
-// slabs' exact totals.  Only chunks past 2^53 get an entry; the walk uses
-// no other (below 2^53 it adds chunk totals exactly).
+// CPU's sum probably changes binade inside it; flags 0 otherwise), the
+// slabs' exact totals, and a chunk map (flags 0 unless kChunkOnly).  Only
+// chunks past 2^53 get an entry; the walk uses no other (below 2^53 it adds
+// chunk totals exactly).
 constexpr int kSlabVectors = 256;
 constexpr int kSlabs = kChunkVectors / kSlabVectors;
 constexpr int kLaneVectors = kSlabVectors / 64;  // vectors of a slab per lane
 constexpr int kSlabMapsA = 0;
 constexpr int kSlabMapsB = kSlabMapsA + 3 * kSlabs;
 constexpr int kSlabTotals = kSlabMapsB + 3 * kSlabs;
-constexpr int kEntry = kSlabTotals + kSlabs;
+constexpr int kChunkMap = kSlabTotals + kSlabs;  // {dm0, dm1, flags}: see kChunkOnly
+constexpr int kEntry = kChunkMap + 3;
+// Set in the chunk map's flags of a chunk whose entry holds only that map:
+// every term of the chunk's sum is a multiple of its predicted binade's unit
+// (from stage 1's low bits), so nothing rounds inside the chunk, and no
+// crossing is predicted in it.  Its slabs are not mapped.
+constexpr uint64_t kChunkOnly = 1ull << 20;
 
 // Work of the maps kernel: one wave per (frame, square sum, group of
 // kGroupChunks chunks); an item is one slab.
@@ -735,6 +742,25 @@ __global__ __launch_bounds__(kThreads) void cpu_order_maps(const void *ref, cons
         want = cb < G.ve && p + r >= kTwo53;
         e = binade(p > kTwo53 ? p : kTwo53);
         dual = e < 56 && p + r >= (1ull << (e + 1));
+        // A chunk that starts past 2^53, is not predicted to change binade
+        // and whose terms are all multiples of 2^k gets its map from its
+        // total alone (r: chunk 0, the only one holding other samples, starts
+        // at 0); the others are mapped slab by slab.
+        const int k = e - 52;
+        const uint32_t low = static_cast<uint32_t>(rec[wg * kRecordStride + kLowBits] >> (4 * kk)) & 15u;
+        const bool chunk_only = want && !dual && p >= kTwo53 && (low & ((1u << k) - 1)) == 0;
+        if (want && lane % kSlabs == 0) {
+            uint64_t *entry = G.maps + (wg * kSquares + kk) * kEntry;
+            if (chunk_only) {
+                const Map2 m = untied_map(r >> k);
+                entry[kChunkMap + 0] = m.dm0;
+                entry[kChunkMap + 1] = m.dm1;
+                entry[kChunkMap + 2] = map_flags(m, e) | kChunkOnly;
+            } else {
+                entry[kChunkMap + 2] = 0;
+            }
+        }
+        want = want && !chunk_only;
     }
     const uint64_t mask = __ballot(want);
     if (!mask)
@@ -865,6 +891,13 @@ __device__ __forceinline__ uint64_t walk_chunk(uint64_t S, const u32x4 *R, const
                                int64_t ce)
 {
     const int lane = threadIdx.x;
+    if (entry[kChunkMap + 2] & kChunkOnly) {
+        // no slab maps (S is not where the chunk map expects it): map each
+        // slab on the spot
+        for (int64_t sb = cb; sb < ce; sb += kSlabVectors)
+            S = walk_slab<KK>(S, R, D, sb, sb + kSlabVectors < ce ? sb + kSlabVectors : ce);
+        return S;
+    }
     uint64_t T = 0, dm0 = 0, dm1 = 0, flags = 0, bdm0 = 0, bdm1 = 0, bflags = 0;
     if (lane < kSlabs) {
         T = entry[kSlabTotals + lane];
@@ -906,7 +939,7 @@ __device__ __forceinline__ uint64_t walk_chunk(uint64_t S, const u32x4 *R, const
 // those before the exact sum reaches 2^53), and the walk uses them only for
 // non-empty chunks past 2^53.
 struct ChunkView {
-    uint64_t T, dm[kSlabs][2], fl[kSlabs];
+    uint64_t T, dm[kSlabs][2], fl[kSlabs], cm[3];
 };
 
 __device__ __forceinline__ ChunkView load_chunk(const uint64_t *rec, const uint64_t *entries, int64_t frame,
@@ -923,11 +956,18 @@ __device__ __forceinline__ ChunkView load_chunk(const uint64_t *rec, const uint6
         x.dm[j][1] = entry[kSlabMapsA + 3 * j + 1];
         x.fl[j] = entry[kSlabMapsA + 3 * j + 2];
     }
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+        x.cm[j] = entry[kChunkMap + j];
     return x;
 }
 
 __device__ __forceinline__ Map2 chunk_map(const ChunkView &x, uint64_t &flags)
 {
+    if (x.cm[2] & kChunkOnly) {
+        flags = x.cm[2] & ~kChunkOnly;
+        return map_from(x.cm[0], x.cm[1], x.cm[2]);
+    }
     Map2 m;
     const uint64_t key = x.fl[0] & 0xffffu;  // valid bit and binade of slab 0
     bool ok = (key & 1u) != 0;
@@ -1066,7 +1106,9 @@ hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, cons
     uint64_t *prefix = reinterpret_cast<uint64_t *>(ws + l.prefix);
     uint64_t *totals = reinterpret_cast<uint64_t *>(ws + l.totals);
     uint64_t *maps = reinterpret_cast<uint64_t *>(ws + l.maps);
-    hipError_t err = launch_plane_stats(g, ref, dist, out_noise, out_moments, rec, stream);
+    // stage 1 with the low bits of the terms, at two-byte samples
+    hipError_t err = launch_plane_stats(g, ref, dist, out_noise, out_moments, rec, stream, nullptr, nullptr,
+                                        g.sample_bytes == 2);
     if (err != hipSuccess)
         return err;
     const unsigned nf = static_cast<unsigned>(g.nframes);

@@ -17,6 +17,12 @@ constexpr int kChunkVectors = 2048;
 // used), so that no two workgroups write the same cache line.
 constexpr int kRecordStride = 8;
 
+// Slot kLowBits of a record, written by the stage 1 of the CPU-order form
+// only (two-byte samples): the OR of the low 4 bits of the workgroup's
+// terms of each square sum -- noise in bits 0..3, ref^2 in 4..7, dist^2 in
+// 8..11.
+constexpr int kLowBits = 5;
+
 // Work split of one batch.  Each plane is read as 16-byte vectors; the
 // vectors of a frame that lie wholly inside it are cut into chunks of
 // chunk_vecs vectors, one workgroup per (frame, chunk).  The few samples of a
@@ -52,7 +58,7 @@ inline bool fits_dispatch(const Geometry &g, int per_chunk)
 hipError_t launch_plane_stats(const Geometry &g, const void *ref, const void *dist,
                               uint64_t *out_noise, uint64_t *out_moments, uint64_t *partials,
                               hipStream_t stream, hipEvent_t stage1_begin = nullptr,
-                              hipEvent_t stage1_end = nullptr);
+                              hipEvent_t stage1_end = nullptr, bool low_bits = false);
 
 // A plane of every frame of a batch, addressed sample by sample: sample
 // (x, y) of frame f is at base + (f*frame_stride + y*row_stride + x) samples.

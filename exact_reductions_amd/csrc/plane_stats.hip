@@ -35,6 +35,8 @@
 
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "plane_stats.h"
 #include "reduce.h"
 #include "terms.h"
@@ -137,13 +139,17 @@ __global__ __launch_bounds__(kThreads) void stage1_u8(const void *ref, const voi
     write_record(part, wg, rec);
 }
 
+// kLowBits: also the OR of the low bits of each square sum's terms, in the
+// record's slot kLowBits (for the CPU-order form).
+template <bool kLowBitsOut>
 __global__ __launch_bounds__(kThreads) void stage1_u16(const void *ref, const void *dist,
                                                        int64_t pixels, int chunks, uint64_t *part)
 {
     const int64_t wg = blockIdx.x;
     const int64_t frame = wg / chunks;
     const int chunk = static_cast<int>(wg - frame * chunks);
-    Acc16 a;
+    using Acc = typename std::conditional<kLowBitsOut, Acc16Low, Acc16>::type;
+    Acc a;
     accumulate_chunk<2>(a, ref, dist, pixels, chunk, frame);
     // each 64-bit lane sum crosses the wave as (low 16 bits, the rest)
     const uint32_t v[8] = {static_cast<uint32_t>(a.noise & 0xffffu), static_cast<uint32_t>(a.noise >> 16),
@@ -155,6 +161,11 @@ __global__ __launch_bounds__(kThreads) void stage1_u16(const void *ref, const vo
     const uint64_t rec[kSums] = {s[0] + (s[1] << 16), s[2], s[3], s[4] + (s[5] << 16),
                                  s[6] + (s[7] << 16)};
     write_record(part, wg, rec);
+    if constexpr (kLowBitsOut) {
+        const uint32_t low = workgroup_or((a.or_noise & 15u) | ((a.or_r2 & 15u) << 4) | ((a.or_d2 & 15u) << 8));
+        if (threadIdx.x == 0)
+            part[wg * kRecordStride + kLowBits] = low;
+    }
 }
 
 // ------------------------------------------------------------------ stage 2
@@ -188,7 +199,7 @@ Geometry make_geometry(int w, int h, int bpc, int nframes)
 
 hipError_t launch_plane_stats(const Geometry &g, const void *ref, const void *dist,
                               uint64_t *out_noise, uint64_t *out_moments, uint64_t *partials,
-                              hipStream_t stream, hipEvent_t stage1_begin, hipEvent_t stage1_end)
+                              hipStream_t stream, hipEvent_t stage1_begin, hipEvent_t stage1_end, bool low_bits)
 {
     const dim3 grid1(static_cast<unsigned>(g.workgroups));
     int64_t pixels = g.pixels;
@@ -199,15 +210,18 @@ hipError_t launch_plane_stats(const Geometry &g, const void *ref, const void *di
         void *args[] = {const_cast<void **>(&ref), const_cast<void **>(&dist), &pixels, &chunks,
                         &partials};
         const void *fn = g.sample_bytes == 1 ? reinterpret_cast<const void *>(&stage1_u8)
-                                             : reinterpret_cast<const void *>(&stage1_u16);
+                         : low_bits           ? reinterpret_cast<const void *>(&stage1_u16<true>)
+                                              : reinterpret_cast<const void *>(&stage1_u16<false>);
         hipError_t e = hipExtLaunchKernel(fn, grid1, dim3(kThreads), args, 0, stream, stage1_begin,
                                           stage1_end, 0);
         if (e != hipSuccess)
             return e;
     } else if (g.sample_bytes == 1) {
         stage1_u8<<<grid1, kThreads, 0, stream>>>(ref, dist, pixels, chunks, partials);
+    } else if (low_bits) {
+        stage1_u16<true><<<grid1, kThreads, 0, stream>>>(ref, dist, pixels, chunks, partials);
     } else {
-        stage1_u16<<<grid1, kThreads, 0, stream>>>(ref, dist, pixels, chunks, partials);
+        stage1_u16<false><<<grid1, kThreads, 0, stream>>>(ref, dist, pixels, chunks, partials);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)

@@ -77,6 +77,34 @@ __device__ __forceinline__ void add_dword(Acc16 &a, uint32_t r, uint32_t d)
     a.d1 = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, d), ones, a.d1, false);
 }
 
+// Acc16 that also ORs together the terms of each square sum, for their low
+// bits: a run of terms all multiples of 2^k rounds nowhere in a binade of
+// unit 2^k (the CPU-order mode reads this).
+struct Acc16Low : Acc16 {
+    uint32_t or_noise = 0, or_r2 = 0, or_d2 = 0;
+};
+
+__device__ __forceinline__ void add_dword(Acc16Low &a, uint32_t r, uint32_t d)
+{
+    const float r0 = static_cast<float>(r & 0xffffu), r1 = static_cast<float>(r >> 16);
+    const float d0 = static_cast<float>(d & 0xffffu), d1 = static_cast<float>(d >> 16);
+    const uint32_t n0 = float_square(r0 - d0), n1 = float_square(r1 - d1);
+    const uint32_t a0 = float_square(r0), a1 = float_square(r1);
+    const uint32_t b0 = float_square(d0), b1 = float_square(d1);
+    a.noise += n0;
+    a.noise += n1;
+    a.r2 += a0;
+    a.r2 += a1;
+    a.d2 += b0;
+    a.d2 += b1;
+    a.or_noise |= n0 | n1;
+    a.or_r2 |= a0 | a1;
+    a.or_d2 |= b0 | b1;
+    const u16x2 ones = {1, 1};
+    a.r1 = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, r), ones, a.r1, false);
+    a.d1 = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, d), ones, a.d1, false);
+}
+
 template <class Acc>
 __device__ __forceinline__ void add_vec(Acc &a, const u32x4 &r, const u32x4 &d)
 {
@@ -111,6 +139,33 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v)
     v += dpp_step(v, 4);
     v += dpp_step(v, 5);
     return __builtin_amdgcn_readlane(v, 63);
+}
+
+// OR of v over the 64 lanes (the wave_sum steps with | for +).
+__device__ __forceinline__ uint32_t wave_or(uint32_t v)
+{
+    v |= dpp_step(v, 0);
+    v |= dpp_step(v, 1);
+    v |= dpp_step(v, 2);
+    v |= dpp_step(v, 3);
+    v |= dpp_step(v, 4);
+    v |= dpp_step(v, 5);
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+// OR of v over the workgroup, in every thread.  All threads must call it.
+__device__ __forceinline__ uint32_t workgroup_or(uint32_t v)
+{
+    __shared__ uint32_t lds[kWaves];
+    const uint32_t w = wave_or(v);
+    if ((threadIdx.x & 63) == 0)
+        lds[threadIdx.x / 64] = w;
+    __syncthreads();
+    uint32_t o = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i)
+        o |= lds[i];
+    return o;
 }
 
 // Adds every lane's accumulators of the workgroup: every thread gets the N
