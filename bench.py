@@ -343,12 +343,17 @@ def time_oracle(ref, dist, bpc, bytes_per_frame, threads):
 
 
 def past53_bytes(ref, dist, bpc):
-    """Bytes the CPU-order maps pass must read for this batch: for each frame
-    and square sum whose exact total reaches 2^53 units, the planes' 16-byte
-    vectors from the 2048-vector chunk in which the running sum gets there
-    to the frame's last whole vector (one plane for a sum of squares of one
-    plane, both for the noise).  Plain numpy over the batch (float32 squares
-    read back as integers); no part of the library or the oracle."""
+    """Bytes the CPU-order maps pass must read again for this batch.
+
+    Per frame and square sum, the frame's whole 16-byte vectors are cut into
+    chunks of 2048 (the few samples before the first and after the last whole
+    vector count with chunk 0).  A chunk is read again, one plane for a sum
+    of squares of one plane and both for the noise, when the running sum
+    passes 2^53 units by its end, unless its terms cannot round: it starts
+    past 2^53 inside one binade [2^e, 2^(e+1)) that its exact end stays in,
+    and every one of its terms is a multiple of 2^(e-52).  Plain numpy and
+    Python ints over the batch (float32 squares read back as integers); no
+    part of the library or the oracle."""
     import numpy as np
 
     if bpc == 8:
@@ -356,24 +361,39 @@ def past53_bytes(ref, dist, bpc):
     nframes, h, w = ref.shape
     pixels = w * h
     table = (np.arange(65536, dtype=np.float32) ** 2).astype(np.uint64)
+    two53 = 1 << 53
+    chunk = 8 * 2048
     total = 0
     for f in range(nframes):
         e0, e1 = f * pixels, (f + 1) * pixels
         vb, ve = -(-e0 // 8), e1 // 8
         if vb >= ve:
             continue
-        head = vb * 8 - e0
+        head, tail = vb * 8 - e0, e1 - ve * 8
         r = ref[f].reshape(-1)
         d = dist[f].reshape(-1)
         diff = np.abs(r.astype(np.float32) - d.astype(np.float32))
         kinds = ((np.rint(diff * diff).astype(np.uint64), 2), (table[r], 1), (table[d], 1))
         for terms, planes in kinds:
-            cs = np.cumsum(terms, dtype=np.uint64)
-            if int(cs[-1]) < (1 << 53):
+            if int(terms.sum()) < two53:
                 continue
-            i0 = int(np.searchsorted(cs, np.uint64(1 << 53), side="left"))
-            c_first = max(0, i0 - head) // (8 * 2048)
-            total += (ve - (vb + c_first * 2048)) * 16 * planes
+            body = terms[head:pixels - tail]
+            starts = np.arange(0, body.size, chunk)
+            sums = [int(v) for v in np.add.reduceat(body, starts)]
+            ors = [int(v) for v in np.bitwise_or.reduceat(body, starts)]
+            edge = np.concatenate((terms[:head], terms[pixels - tail:]))
+            sums[0] += int(edge.sum())
+            ors[0] |= int(np.bitwise_or.reduce(edge)) if edge.size else 0
+            p = 0
+            for c, (s, o) in enumerate(zip(sums, ors)):
+                if p + s >= two53:
+                    e = max(p, two53).bit_length() - 1
+                    one_binade = p + s < (1 << (e + 1))
+                    aligned = o & ((1 << (e - 52)) - 1) == 0
+                    if not (p >= two53 and one_binade and aligned):
+                        vectors = min(2048, (ve - vb) - c * 2048)
+                        total += vectors * 16 * planes
+                p += s
     return total
 
 

@@ -8,9 +8,11 @@ Layout of every batch: a C-contiguous numpy array ``[nframes][h][w]`` of
 ``uint8`` (8 bits per component) or ``uint16`` (9..16 bits, value in the low
 bits), one array for the reference planes and one for the distorted planes.
 
-The five named workloads stand in for the clips the pages measure on (Netflix
-576x324, BBB and the checkerboards at 1920x1080 and 3840x2160, full-range
-noise and the bright 16-bit pair), none of which exists here.  Each workload
+The first five named workloads stand in for the clips the pages measure on
+(Netflix 576x324, BBB and the checkerboards at 1920x1080 and 3840x2160,
+full-range noise and the bright 16-bit pair), none of which exists here; the
+sixth for the 2560x1440 frame whose sums pass 2**53 units, with dark samples
+whose squares are not multiples of the binade's unit.  Each workload
 has one ``numpy.random.Generator(PCG64(1000 + number))``; frames are drawn in
 order, for each frame first the reference plane, then the distorted plane.
 "Uniform a..b" below means integers with both ends included; "rint" is
@@ -66,6 +68,9 @@ WORKLOADS = {
                 "ref and dist independent uniform 56000..64000"),
     5: Workload(5, "3840x2160 16-bit", 3840, 2160, 32, 16,
                 "ref uniform 60000..65535; dist = clip(ref + rint(N(0,512)), 0, 65535)"),
+    6: Workload(6, "2560x1440 16-bit mixed", 2560, 1440, 64, 16,
+                "per plane: a tenth of the positions (uniform(0,1) < 0.1) uniform 0..4095, "
+                "the rest uniform 49152..65535; ref and dist drawn alike and independently"),
 }
 
 
@@ -93,6 +98,14 @@ def _frame_pair(number: int, rng: np.random.Generator, w: int, h: int):
         ref = rng.integers(60000, 65535, size=(h, w), endpoint=True, dtype=np.int64)
         dist = np.clip(ref + np.rint(rng.normal(0.0, 512.0, size=(h, w))).astype(np.int64), 0, 65535)
         return ref.astype(np.uint16), dist.astype(np.uint16)
+    if number == 6:
+        out = []
+        for _ in range(2):
+            low = rng.random(size=(h, w)) < 0.1
+            dark = rng.integers(0, 4095, size=(h, w), endpoint=True, dtype=np.uint16)
+            bright = rng.integers(49152, 65535, size=(h, w), endpoint=True, dtype=np.uint16)
+            out.append(np.where(low, dark, bright).astype(np.uint16))
+        return out[0], out[1]
     raise ValueError(f"no workload {number}")
 
 
