@@ -30,16 +30,18 @@
 //
 //  1. stage 1 + stage 2 (plane_stats.hip) give each chunk's exact totals;
 //  2. cpu_order_prefix scans them per frame (the exact running sum at each
-//     chunk start, which predicts the binade the CPU's sum is in there) and
-//     writes every sum the CPU gets exactly (all of them below 2^53);
-//  3. cpu_order_maps computes, for every slab of 256 vectors of a chunk
-//     past 2^53, its exact total and maps in the predicted binade (and the
+//     chunk start, which predicts the binade the CPU's sum is in there),
+//     writes every sum the CPU gets exactly (all of them below 2^53), maps
+//     the chunks past 2^53 inside which nothing can round, and queues the
+//     other chunks past 2^53;
+//  3. cpu_order_maps computes, for every slab of 256 vectors of a queued
+//     chunk, its exact total and maps in the predicted binade (and the
 //     next one where the chunk may cross into it).  Most slabs need no
 //     ordered work: if every term is a multiple of the binade's unit nothing
 //     rounds, and without ties the map follows from two plain sums; only
 //     slabs with ties chain their terms and compose the lanes' maps in
-//     order.  One wave takes the slabs of a few chunks in turn, reading the
-//     next while mapping the current one;
+//     order.  A fixed grid of waves shares out the queued slabs, each wave
+//     reading its next slab while mapping the current one;
 //  4. cpu_order_walk, one wave per frame and sum past 2^53, walks the frame
 //     in order with the running value S, 64 chunks at a time: a block that
 //     stays below 2^53 adds exactly; a block whose chunk maps (composed from
@@ -432,58 +434,6 @@ __device__ __forceinline__ void keep_if(bool ok, u32x4 &a, u32x4 &b)
         b = ok ? b : zero;
 }
 
-// ------------------------------------------------------------ 2. prefix scan
-// One workgroup per frame.  prefix[(f*chunks + c)*3 + kk] = exact sum of
-// square kk over chunks 0..c-1 (chunk 0's record also holds the frame's few
-// samples outside whole vectors); totals[f*3 + kk] = the frame's exact sum.
-// The CPU's values of the sums that stay below 2^53 are the exact sums,
-// written here; the first moments always do (below 2^25 * 2^16 = 2^41).
-__global__ __launch_bounds__(kThreads) void cpu_order_prefix(const uint64_t *rec, int chunks,
-                                                             uint64_t *prefix, uint64_t *totals,
-                                                             uint64_t *out_cpu_noise,
-                                                             uint64_t *out_cpu_moments)
-{
-    __shared__ uint64_t lds[kThreads];
-    const int64_t f = blockIdx.x;
-    const int t = threadIdx.x;
-    const int per = (chunks + kThreads - 1) / kThreads;
-    const int c0 = t * per;
-    const int c1 = c0 + per < chunks ? c0 + per : chunks;
-    for (int kk = 0; kk < kSquares + 2; ++kk) {
-        const int field = kk < kSquares ? record_field(kk) : (kk == kSquares ? kRef1 : kDist1);
-        uint64_t local = 0;
-        for (int c = c0; c < c1; ++c)
-            local += rec[(f * chunks + c) * kRecordStride + field];
-        // inclusive scan of the per-thread sums (Hillis-Steele)
-        lds[t] = local;
-        __syncthreads();
-        for (int off = 1; off < kThreads; off <<= 1) {
-            const uint64_t add = t >= off ? lds[t - off] : 0;
-            __syncthreads();
-            lds[t] += add;
-            __syncthreads();
-        }
-        const uint64_t total = lds[kThreads - 1];
-        if (kk < kSquares) {
-            uint64_t run = lds[t] - local;  // exclusive
-            for (int c = c0; c < c1; ++c) {
-                prefix[(f * chunks + c) * kSquares + kk] = run;
-                run += rec[(f * chunks + c) * kRecordStride + field];
-            }
-        }
-        if (t == 0) {
-            if (kk < kSquares)
-                totals[f * kSquares + kk] = total;
-            uint64_t *dst = kk == kSqNoise  ? &out_cpu_noise[f]
-                          : kk < kSquares   ? &out_cpu_moments[4 * f + 1 + kk]
-                                            : &out_cpu_moments[4 * f + (kk - kSquares)];
-            if (total < kTwo53)  // otherwise the walk writes it
-                *dst = total;
-        }
-        __syncthreads();
-    }
-}
-
 // ------------------------------------------------------------ 3. slab maps
 // Entry of chunk wg, square kk (kEntry uint64): the maps {dm0, dm1, flags}
 // of its kSlabs slabs in the predicted binade e, their maps in binade e + 1
@@ -506,11 +456,164 @@ constexpr int kEntry = kChunkMap + 3;
 // crossing is predicted in it.  Its slabs are not mapped.
 constexpr uint64_t kChunkOnly = 1ull << 20;
 
-// Work of the maps kernel: one wave per (frame, square sum, group of
-// kGroupChunks chunks); an item is one slab.
-constexpr int kGroupChunks = 4;
-constexpr int kGroupItems = kGroupChunks * kSlabs;
-static_assert(kGroupItems <= 64, "one lane per item");
+// Queues of chunks to map, one per square sum, each of capacity
+// nframes * chunks: an item is (frame * chunks + chunk) | e << 32 |
+// dual << 40, e the binade predicted at the chunk's start, dual set where
+// the chunk's exact range reaches 2^(e+1).  Their lengths sit in record 0
+// (kQueueCounts).
+__device__ __forceinline__ uint32_t *queue_counts(uint64_t *rec) { return reinterpret_cast<uint32_t *>(rec + kQueueCounts); }
+
+// ------------------------------------------------------------ 2. prefix scan
+// One workgroup per frame; thread t takes chunks [t * per, (t + 1) * per).
+//  * The exact sum of each square over the chunks before chunk c (chunk 0's
+//    record also holds the frame's few samples outside whole vectors)
+//    predicts the CPU's sum there; totals[f*3 + kk] = the frame's exact sum.
+//  * The CPU's values of the sums that stay below 2^53 are the exact sums,
+//    written here; the first moments always do (below 2^25 * 2^16 = 2^41).
+//  * With `maps` (two-byte samples), each chunk whose exact range ends past
+//    2^53 gets its case: a chunk that starts past 2^53, is not predicted to
+//    change binade and whose terms are all multiples of 2^k (stage 1's low
+//    bits; k <= 4 since sums stay below 2^57) gets its map from its total
+//    alone, since nothing inside it rounds; every other such chunk gets
+//    chunk flags 0 and goes on its sum's queue for the maps kernel.
+__device__ __forceinline__ uint64_t wave_inclusive_then_total(uint64_t v, uint64_t *lds_totals, uint64_t &total)
+{
+    // inclusive scan inside the wave, then the totals of the waves below
+    const int wave = threadIdx.x / 64;
+    const uint64_t inc = wave_scan64(v);
+    if ((threadIdx.x & 63) == 63)
+        lds_totals[wave] = inc;
+    __syncthreads();
+    uint64_t below = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+        const uint64_t x = lds_totals[w];
+        below += w < wave ? x : 0;
+        total += x;
+    }
+    __syncthreads();
+    return inc + below;
+}
+
+struct ChunkCase {
+    bool queued, chunk_only;
+    int e;
+    bool dual;
+};
+
+__device__ __forceinline__ ChunkCase chunk_case(uint64_t p, uint64_t r, uint32_t low, bool exists)
+{
+    ChunkCase x;
+    const bool want = exists && p + r >= kTwo53;
+    x.e = binade(p > kTwo53 ? p : kTwo53);
+    x.dual = x.e < 56 && p + r >= (1ull << (x.e + 1));
+    const uint32_t unit_bits = (1u << (x.e - 52)) - 1;
+    x.chunk_only = want && !x.dual && p >= kTwo53 && (low & unit_bits) == 0;
+    x.queued = want && !x.chunk_only;
+    return x;
+}
+
+__global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int64_t pixels, int chunks,
+                                                             uint64_t *totals,
+                                                             uint64_t *out_cpu_noise,
+                                                             uint64_t *out_cpu_moments, uint64_t *maps,
+                                                             uint64_t *queue)
+{
+    constexpr int V = 8;
+    __shared__ uint64_t lds[kSums + 1][kThreads / 64];
+    __shared__ uint32_t base[kSquares];
+    const int64_t f = blockIdx.x;
+    const int t = threadIdx.x;
+    const int per = (chunks + kThreads - 1) / kThreads;
+    const int c0 = t * per < chunks ? t * per : chunks;
+    const int c1 = c0 + per < chunks ? c0 + per : chunks;
+    const uint64_t *frec = rec + f * chunks * kRecordStride;
+    // the thread's sums of each record field, then their exclusive prefixes
+    // over the frame and the frame's totals
+    uint64_t local[kSums], run[kSums], total[kSums];
+#pragma unroll
+    for (int j = 0; j < kSums; ++j)
+        local[j] = 0;
+    for (int c = c0; c < c1; ++c)
+#pragma unroll
+        for (int j = 0; j < kSums; ++j)
+            local[j] += frec[c * kRecordStride + j];
+#pragma unroll
+    for (int j = 0; j < kSums; ++j)
+        run[j] = wave_inclusive_then_total(local[j], lds[j], total[j]) - local[j];
+    if (t == 0) {
+#pragma unroll
+        for (int kk = 0; kk < kSquares; ++kk)
+            totals[f * kSquares + kk] = total[record_field(kk)];
+        // otherwise the walk writes it
+        if (total[kNoise] < kTwo53)
+            out_cpu_noise[f] = total[kNoise];
+        out_cpu_moments[4 * f + 0] = total[kRef1];
+        out_cpu_moments[4 * f + 1] = total[kDist1];
+        if (total[kRef2] < kTwo53)
+            out_cpu_moments[4 * f + 2] = total[kRef2];
+        if (total[kDist2] < kTwo53)
+            out_cpu_moments[4 * f + 3] = total[kDist2];
+    }
+    const int64_t e0 = f * pixels;
+    const int64_t nvec = (e0 + pixels) / V - (e0 + V - 1) / V;  // the frame's whole vectors
+    if (!maps)  // one-byte samples: every sum stays below 2^53
+        return;
+    // pass 1: chunk maps, and how many chunks the thread queues
+    uint64_t nq = 0;  // 21 bits per square sum
+#pragma unroll
+    for (int kk = 0; kk < kSquares; ++kk) {
+        const int field = record_field(kk);
+        uint64_t p = run[field];
+        for (int c = c0; c < c1; ++c) {
+            const uint64_t *r = frec + c * kRecordStride;
+            const uint32_t low = static_cast<uint32_t>(r[kLowBits] >> (4 * kk)) & 15u;
+            const ChunkCase x = chunk_case(p, r[field], low, static_cast<int64_t>(c) * kChunkVectors < nvec);
+            uint64_t *entry = maps + ((f * chunks + c) * kSquares + kk) * kEntry;
+            if (x.chunk_only) {
+                const Map2 m = untied_map(r[field] >> (x.e - 52));
+                entry[kChunkMap + 0] = m.dm0;
+                entry[kChunkMap + 1] = m.dm1;
+                entry[kChunkMap + 2] = map_flags(m, x.e) | kChunkOnly;
+            } else if (x.queued) {
+                entry[kChunkMap + 2] = 0;
+                nq += 1ull << (21 * kk);
+            }
+            p += r[field];
+        }
+    }
+    // each queue's part for this frame, reserved in one add per sum
+    uint64_t nq_total;
+    uint64_t at = wave_inclusive_then_total(nq, lds[kSums], nq_total) - nq;
+    if (t == 0) {
+        uint32_t *counts = queue_counts(rec);
+#pragma unroll
+        for (int kk = 0; kk < kSquares; ++kk) {
+            const uint32_t n = static_cast<uint32_t>(nq_total >> (21 * kk)) & 0x1fffffu;
+            base[kk] = n ? atomicAdd(&counts[kk], n) : 0u;
+        }
+    }
+    __syncthreads();
+    // pass 2: the queue items, in chunk order within the frame
+    const int64_t cap = static_cast<int64_t>(gridDim.x) * chunks;
+#pragma unroll
+    for (int kk = 0; kk < kSquares; ++kk) {
+        const int field = record_field(kk);
+        uint64_t p = run[field];
+        int64_t slot = base[kk] + ((at >> (21 * kk)) & 0x1fffffu);
+        for (int c = c0; c < c1; ++c) {
+            const uint64_t *r = frec + c * kRecordStride;
+            const uint32_t low = static_cast<uint32_t>(r[kLowBits] >> (4 * kk)) & 15u;
+            const ChunkCase x = chunk_case(p, r[field], low, static_cast<int64_t>(c) * kChunkVectors < nvec);
+            if (x.queued)
+                queue[kk * cap + slot++] = static_cast<uint64_t>(f * chunks + c) |
+                                           (static_cast<uint64_t>(x.e) << 32) |
+                                           (static_cast<uint64_t>(x.dual) << 40);
+            p += r[field];
+        }
+    }
+}
 
 // The planes' vectors of one slab: lane l holds vectors l, 64 + l, 128 + l
 // and 192 + l (each load instruction reads 1 KB in one piece); bit j of ok
@@ -628,148 +731,122 @@ __device__ __forceinline__ void item_maps(ItemData &x, int si, int e, bool dual,
     }
 }
 
-// Where the items of a group lie.
-struct Group {
+// Where the slabs of the queues lie.  Slab item i of square sum KK's queue
+// is slab i % kSlabs of the chunk queued at i / kSlabs.
+struct Slabs {
     const u32x4 *R, *D;
+    const uint64_t *queue;  // this square sum's queue
     uint64_t *maps;
-    int64_t frame, vb, ve;
-    int chunks, g;
+    int64_t pixels;
+    uint32_t chunks;
+};
+
+struct SlabItem {
+    int64_t cb, sb, ce;
+    uint64_t *entry;
+    int si, e;
+    bool dual;
 };
 
 template <int KK>
-__device__ __forceinline__ void group_item(const Group &G, int item, int64_t &cb, int64_t &sb, int64_t &ce,
-                                           uint64_t *&entry, int &si)
+__device__ __forceinline__ SlabItem slab_item(const Slabs &Q, int64_t i)
 {
-    const int c = G.g * kGroupChunks + item / kSlabs;
-    si = item % kSlabs;
-    cb = G.vb + static_cast<int64_t>(c) * kChunkVectors;
-    ce = cb + kChunkVectors < G.ve ? cb + kChunkVectors : G.ve;
-    sb = cb + static_cast<int64_t>(si) * kSlabVectors;
-    entry = G.maps + ((G.frame * G.chunks + c) * kSquares + KK) * kEntry;
+    constexpr int V = 8;
+    const uint64_t q = Q.queue[i / kSlabs];
+    const uint32_t idx = static_cast<uint32_t>(q);
+    const uint32_t f = idx / Q.chunks, c = idx - f * Q.chunks;
+    const int64_t e0 = static_cast<int64_t>(f) * Q.pixels;
+    const int64_t vb = (e0 + V - 1) / V, ve = (e0 + Q.pixels) / V;
+    SlabItem x;
+    x.si = static_cast<int>(i % kSlabs);
+    x.e = static_cast<int>((q >> 32) & 0xffu);
+    x.dual = ((q >> 40) & 1u) != 0;
+    x.cb = vb + static_cast<int64_t>(c) * kChunkVectors;
+    x.ce = x.cb + kChunkVectors < ve ? x.cb + kChunkVectors : ve;
+    x.sb = x.cb + static_cast<int64_t>(x.si) * kSlabVectors;
+    x.entry = Q.maps + (static_cast<uint64_t>(idx) * kSquares + KK) * kEntry;
+    return x;
 }
 
-// The wanted items of one group, in order (the set bits of `want`; lane j
-// holds item j's binade and dual flag).  The next item's vectors are read
-// while the current one is mapped, except for the noise, which reads both
-// planes.
+// Slab items i, i + stride, ... below n, in turn.  The next item's vectors
+// are read while the current one is mapped, except for the noise, which
+// reads both planes.
 template <int KK>
-__device__ __forceinline__ void group_maps(const Group &G, uint64_t want, int e_lane, int dual_lane)
+__device__ __forceinline__ void queue_maps(const Slabs &Q, int64_t i, int64_t stride, int64_t n)
 {
-    int64_t cb, sb, ce;
-    uint64_t *entry;
-    int si;
     ItemData x, y;
-    auto map_item = [&](ItemData &d, int j, int s, uint64_t *en) {
-        item_maps<KK>(d, s, lane_value(e_lane, j), lane_value(dual_lane, j) != 0, en);
-    };
-    int j = __builtin_ctzll(want);
-    want &= want - 1;
-    group_item<KK>(G, j, cb, sb, ce, entry, si);
-    load_item<KK>(x, G.R, G.D, cb, sb, ce);
+    auto map_item = [&](ItemData &d, const SlabItem &it) { item_maps<KK>(d, it.si, it.e, it.dual, it.entry); };
+    SlabItem u = slab_item<KK>(Q, i);
+    load_item<KK>(x, Q.R, Q.D, u.cb, u.sb, u.ce);
     if constexpr (KK == kSqNoise) {
         for (;;) {
-            map_item(x, j, si, entry);
-            if (!want)
+            map_item(x, u);
+            i += stride;
+            if (i >= n)
                 return;
-            j = __builtin_ctzll(want);
-            want &= want - 1;
-            group_item<KK>(G, j, cb, sb, ce, entry, si);
-            load_item<KK>(x, G.R, G.D, cb, sb, ce);
+            u = slab_item<KK>(Q, i);
+            load_item<KK>(x, Q.R, Q.D, u.cb, u.sb, u.ce);
         }
     } else {
         // Two buffers, taken in turn.  Each item mapped inside the loop
         // follows the loads of the next one, and the last item is mapped
         // apart, so that the waits before mapping an item never cover the
         // loads of the one after it.
-        int j2, si2;
-        uint64_t *entry2;
+        SlabItem v;
         for (;;) {
-            if (!want) {
-                map_item(x, j, si, entry);
+            i += stride;
+            if (i >= n) {
+                map_item(x, u);
                 return;
             }
-            j2 = __builtin_ctzll(want);
-            want &= want - 1;
-            group_item<KK>(G, j2, cb, sb, ce, entry2, si2);
-            load_item<KK>(y, G.R, G.D, cb, sb, ce);
-            map_item(x, j, si, entry);
-            if (!want) {
-                map_item(y, j2, si2, entry2);
+            v = slab_item<KK>(Q, i);
+            load_item<KK>(y, Q.R, Q.D, v.cb, v.sb, v.ce);
+            map_item(x, u);
+            i += stride;
+            if (i >= n) {
+                map_item(y, v);
                 return;
             }
-            j = __builtin_ctzll(want);
-            want &= want - 1;
-            group_item<KK>(G, j, cb, sb, ce, entry, si);
-            load_item<KK>(x, G.R, G.D, cb, sb, ce);
-            map_item(y, j2, si2, entry2);
+            u = slab_item<KK>(Q, i);
+            load_item<KK>(x, Q.R, Q.D, u.cb, u.sb, u.ce);
+            map_item(y, v);
         }
     }
 }
 
-// One wave per (frame, square sum, group of chunks); two-byte samples only.
+// Waves of the maps kernel: 4 per SIMD (its register use allows 4) on 256
+// CUs of 4 SIMDs.
+constexpr int64_t kMapWaves = 4096;
+
+// A fixed grid of waves shares out the slabs of the three queues: wave w
+// takes slab items w, w + W, w + 2W, ... of each queue in turn (W waves in
+// all).  Two-byte samples only.
 __global__ __launch_bounds__(kThreads) void cpu_order_maps(const void *ref, const void *dist, int64_t pixels,
                                                            int chunks, int nframes, const uint64_t *rec,
-                                                           const uint64_t *prefix, const uint64_t *totals,
-                                                           uint64_t *maps)
+                                                           const uint64_t *queue, uint64_t *maps)
 {
-    constexpr int V = 8;
-    const int lane = threadIdx.x & 63;
-    const int groups = (chunks + kGroupChunks - 1) / kGroupChunks;
-    const int64_t gw = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + threadIdx.x / 64;
-    const int64_t fk = gw / groups;  // frame * kSquares + kk
-    if (fk >= static_cast<int64_t>(nframes) * kSquares || totals[fk] < kTwo53)
-        return;
-    Group G;
-    G.frame = fk / kSquares;
-    const int kk = static_cast<int>(fk - G.frame * kSquares);
-    G.g = static_cast<int>(gw - fk * groups);
-    G.chunks = chunks;
-    G.maps = maps;
-    G.R = static_cast<const u32x4 *>(ref);
-    G.D = static_cast<const u32x4 *>(dist);
-    const int64_t e0 = G.frame * pixels, e1 = e0 + pixels;
-    G.vb = (e0 + V - 1) / V;
-    G.ve = e1 / V;
-    // lane j < kGroupItems: item j, i.e. slab j % kSlabs of chunk j / kSlabs
-    const int c = G.g * kGroupChunks + lane / kSlabs;
-    bool want = false;
-    int e = 0, dual = 0;
-    if (lane < kGroupItems && c < chunks) {
-        const int64_t wg = G.frame * chunks + c;
-        const uint64_t p = prefix[wg * kSquares + kk];
-        const uint64_t r = rec[wg * kRecordStride + record_field(kk)];
-        const int64_t cb = G.vb + static_cast<int64_t>(c) * kChunkVectors;
-        want = cb < G.ve && p + r >= kTwo53;
-        e = binade(p > kTwo53 ? p : kTwo53);
-        dual = e < 56 && p + r >= (1ull << (e + 1));
-        // A chunk that starts past 2^53, is not predicted to change binade
-        // and whose terms are all multiples of 2^k gets its map from its
-        // total alone (r: chunk 0, the only one holding other samples, starts
-        // at 0); the others are mapped slab by slab.
-        const int k = e - 52;
-        const uint32_t low = static_cast<uint32_t>(rec[wg * kRecordStride + kLowBits] >> (4 * kk)) & 15u;
-        const bool chunk_only = want && !dual && p >= kTwo53 && (low & ((1u << k) - 1)) == 0;
-        if (want && lane % kSlabs == 0) {
-            uint64_t *entry = G.maps + (wg * kSquares + kk) * kEntry;
-            if (chunk_only) {
-                const Map2 m = untied_map(r >> k);
-                entry[kChunkMap + 0] = m.dm0;
-                entry[kChunkMap + 1] = m.dm1;
-                entry[kChunkMap + 2] = map_flags(m, e) | kChunkOnly;
-            } else {
-                entry[kChunkMap + 2] = 0;
-            }
-        }
-        want = want && !chunk_only;
-    }
-    const uint64_t mask = __ballot(want);
-    if (!mask)
-        return;
-    switch (kk) {
-    case kSqNoise: group_maps<kSqNoise>(G, mask, e, dual); break;
-    case kSqRef: group_maps<kSqRef>(G, mask, e, dual); break;
-    default: group_maps<kSqDist>(G, mask, e, dual); break;
-    }
+    const int64_t w = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + threadIdx.x / 64;
+    const int64_t W = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
+    const uint32_t *counts = reinterpret_cast<const uint32_t *>(rec + kQueueCounts);
+    const int64_t cap = static_cast<int64_t>(nframes) * chunks;
+    Slabs Q;
+    Q.R = static_cast<const u32x4 *>(ref);
+    Q.D = static_cast<const u32x4 *>(dist);
+    Q.maps = maps;
+    Q.pixels = pixels;
+    Q.chunks = static_cast<uint32_t>(chunks);
+    int64_t n = static_cast<int64_t>(counts[kSqNoise]) * kSlabs;
+    Q.queue = queue + kSqNoise * cap;
+    if (w < n)
+        queue_maps<kSqNoise>(Q, w, W, n);
+    n = static_cast<int64_t>(counts[kSqRef]) * kSlabs;
+    Q.queue = queue + kSqRef * cap;
+    if (w < n)
+        queue_maps<kSqRef>(Q, w, W, n);
+    n = static_cast<int64_t>(counts[kSqDist]) * kSlabs;
+    Q.queue = queue + kSqDist * cap;
+    if (w < n)
+        queue_maps<kSqDist>(Q, w, W, n);
 }
 
 // ------------------------------------------------------------------ 4. walk
@@ -1088,8 +1165,8 @@ CpuOrderLayout cpu_order_layout(const Geometry &g)
     CpuOrderLayout l{};
     const size_t wgs = static_cast<size_t>(g.workgroups);
     l.records = 0;
-    l.prefix = up(l.records + g.workspace_bytes);
-    l.totals = up(l.prefix + wgs * kSquares * sizeof(uint64_t));
+    l.queue = up(l.records + g.workspace_bytes);
+    l.totals = up(l.queue + wgs * kSquares * sizeof(uint64_t));
     l.maps = up(l.totals + static_cast<size_t>(g.nframes) * kSquares * sizeof(uint64_t));
     l.bytes = up(l.maps + wgs * kSquares * kEntry * sizeof(uint64_t));
     return l;
@@ -1103,7 +1180,7 @@ hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, cons
     const CpuOrderLayout l = cpu_order_layout(g);
     char *ws = static_cast<char *>(workspace);
     uint64_t *rec = reinterpret_cast<uint64_t *>(ws + l.records);
-    uint64_t *prefix = reinterpret_cast<uint64_t *>(ws + l.prefix);
+    uint64_t *queue = reinterpret_cast<uint64_t *>(ws + l.queue);
     uint64_t *totals = reinterpret_cast<uint64_t *>(ws + l.totals);
     uint64_t *maps = reinterpret_cast<uint64_t *>(ws + l.maps);
     // stage 1 with the low bits of the terms, at two-byte samples
@@ -1112,15 +1189,18 @@ hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, cons
     if (err != hipSuccess)
         return err;
     const unsigned nf = static_cast<unsigned>(g.nframes);
-    cpu_order_prefix<<<dim3(nf), kThreads, 0, stream>>>(rec, g.chunks, prefix, totals, out_cpu_noise,
-                                                        out_cpu_moments);
+    const bool two_byte = g.sample_bytes == 2;  // one-byte sums never reach 2^53
+    cpu_order_prefix<<<dim3(nf), kThreads, 0, stream>>>(rec, g.pixels, g.chunks, totals, out_cpu_noise,
+                                                        out_cpu_moments, two_byte ? maps : nullptr, queue);
     err = hipGetLastError();
-    if (err != hipSuccess || g.sample_bytes == 1)  // one-byte sums never reach 2^53
+    if (err != hipSuccess || !two_byte)
         return err;
-    const int64_t groups = (g.chunks + kGroupChunks - 1) / kGroupChunks;
-    const int64_t waves = static_cast<int64_t>(g.nframes) * kSquares * groups;
+    // enough waves to fill the chip at the maps kernel's occupancy, never
+    // more than there can be slabs
+    const int64_t slabs = g.workgroups * kSquares * kSlabs;
+    const int64_t waves = slabs < kMapWaves ? slabs : kMapWaves;
     cpu_order_maps<<<dim3(static_cast<unsigned>((waves + kThreads / 64 - 1) / (kThreads / 64))), kThreads, 0,
-                     stream>>>(ref, dist, g.pixels, g.chunks, g.nframes, rec, prefix, totals, maps);
+                     stream>>>(ref, dist, g.pixels, g.chunks, g.nframes, rec, queue, maps);
     err = hipGetLastError();
     if (err != hipSuccess)
         return err;

@@ -23,6 +23,11 @@ constexpr int kRecordStride = 8;
 // 8..11.
 constexpr int kLowBits = 5;
 
+// Slots kQueueCounts and kQueueCounts + 1 of record 0 hold the three uint32
+// lengths of the CPU-order form's queues of chunks to map (noise, ref^2,
+// dist^2); its stage 1 zeroes them, and its prefix kernel adds to them.
+constexpr int kQueueCounts = 6;
+
 // Work split of one batch.  Each plane is read as 16-byte vectors; the
 // vectors of a frame that lie wholly inside it are cut into chunks of
 // chunk_vecs vectors, one workgroup per (frame, chunk).  The few samples of a
@@ -111,7 +116,7 @@ hipError_t run_host_stream(int w, int h, int bpc, int nframes, int frames_per_up
 
 // Workspace of the CPU-order form: byte offsets of its parts.
 struct CpuOrderLayout {
-    size_t records, prefix, totals, maps, bytes;
+    size_t records, queue, totals, maps, bytes;
 };
 CpuOrderLayout cpu_order_layout(const Geometry &g);
 
