@@ -56,6 +56,8 @@
 // are below 2^16 and a frame has at most 2^25 samples, so every sum stays
 // below 2^41 and step 2 already gives the CPU's values.
 
+#include <atomic>
+
 #include "plane_stats.h"
 #include "terms.h"
 
@@ -615,9 +617,10 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int6
     }
 }
 
-// The planes' vectors of one slab: lane l holds vectors l, 64 + l, 128 + l
-// and 192 + l (each load instruction reads 1 KB in one piece); bit j of ok
-// is set where vector 64j + l lies inside the chunk.
+// The planes' vectors of one slab.  As loaded, lane l holds vectors l,
+// 64 + l, 128 + l and 192 + l (each load instruction reads 1 KB in one
+// piece), and bit j of ok is set where vector 64j + l lies inside the
+// chunk; `consecutive` then gives lane l vectors 4l .. 4l + 3.
 struct ItemData {
     u32x4 a[kLaneVectors], b[kLaneVectors];
     uint32_t ok;
@@ -654,56 +657,89 @@ __device__ __forceinline__ void load_item(ItemData &x, const u32x4 *R, const u32
     }
 }
 
-// The map, in binade 2^(k+52), of the slab whose vectors the wave's lanes
-// hold (vector 64j + l in lane l), with exact total T.  Three cases,
-// decided for the whole wave: every term a multiple of 2^k (nothing rounds:
-// m grows by T / 2^k); no ties (m grows by the sum of h, both parities flip
-// with its parity) -- neither needs the terms' order; otherwise each lane
-// chains the terms of each of its vectors, the lanes' maps of each row of
-// 64 vectors are composed in lane order and the four rows in turn.
-template <int KK>
-__device__ __forceinline__ Map2 slab_map(u32x4 (&a)[kLaneVectors], u32x4 (&b)[kLaneVectors], uint32_t low_bits,
-                                         uint64_t T, int k)
+// Orders the wave's LDS accesses on either side of it (the lanes of one
+// wave exchange data through LDS; its accesses are carried out in order).
+__device__ __forceinline__ void wave_lds_sync()
 {
-    constexpr uint64_t n = 64 * kLaneVectors * kTerms;
-    const uint32_t half = 1u << (k - 1), mask = (1u << k) - 1;
-    if (__all((low_bits & mask) == 0))
-        return untied_map(T >> k);
-    uint32_t rr_sum = 0, rr_min = ~0u;
-#pragma unroll
-    for (int j = 0; j < kLaneVectors; ++j)
-#pragma unroll
-        for (int i = 0; i < kTerms; ++i) {
-            const uint32_t rr = (vector_term<KK>(a[j], b[j], i) + half) & mask;
-            rr_sum += rr;
-            rr_min = min(rr_min, rr);
-        }
-    forget<KK>(a, b);
-    const uint32_t RR = wave_total32(rr_sum);
-    if (!__any(rr_min == 0))
-        return untied_map((T + (n << (k - 1)) - RR) >> k);
-    RunMap slab;
-#pragma unroll
-    for (int j = 0; j < kLaneVectors; ++j) {
-        RunMap m;
-#pragma unroll
-        for (int i = 0; i < kTerms; ++i)
-            run_step(m, vector_term<KK>(a[j], b[j], i) + half, k);
-        slab = run_then(slab, wave_run(m));
-    }
-    return run_map(slab, T, n, RR, k);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Slab si of its chunk; lane 0 writes its part of the entry.
+// Rearranges the slab through the wave's LDS (kSlabVectors vectors per
+// plane) so that lane l holds vectors 4l .. 4l + 3: its 32 terms are then
+// consecutive in raster order.
 template <int KK>
-__device__ __forceinline__ void item_maps(ItemData &x, int si, int e, bool dual, uint64_t *entry)
+__device__ __forceinline__ void consecutive(u32x4 (&a)[kLaneVectors], u32x4 (&b)[kLaneVectors], u32x4 *lds)
+{
+    const int lane = threadIdx.x & 63;
+    u32x4 *la = lds, *lb = lds + kSlabVectors;
+#pragma unroll
+    for (int j = 0; j < kLaneVectors; ++j) {
+        if constexpr (KK != kSqDist)
+            la[64 * j + lane] = a[j];
+        if constexpr (KK != kSqRef)
+            lb[64 * j + lane] = b[j];
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < kLaneVectors; ++j) {
+        if constexpr (KK != kSqDist)
+            a[j] = la[kLaneVectors * lane + j];
+        if constexpr (KK != kSqRef)
+            b[j] = lb[kLaneVectors * lane + j];
+    }
+    wave_lds_sync();  // the next slab may overwrite the buffer
+}
+
+// What one pass over the lane's consecutive terms gathers for binade
+// 2^(k+52): their sum of rr and its smallest rr (a tie where 0), and their
+// run map.
+struct SlabPass {
+    uint32_t rr_sum = 0, rr_min = ~0u;
+    RunMap m;
+};
+
+__device__ __forceinline__ void pass_term(SlabPass &p, uint32_t t, int k)
+{
+    const uint32_t t2 = t + (1u << (k - 1));
+    const uint32_t rr = t2 & ((1u << k) - 1);
+    p.rr_sum += rr;
+    p.rr_min = min(p.rr_min, rr);
+    run_step(p.m, t2, k);
+}
+
+// The slab's map in binade 2^(k+52) from its exact total T, the OR of its
+// terms (per lane) and the pass.  Three cases, decided for the whole wave:
+// every term a multiple of 2^k (nothing rounds: m grows by T / 2^k); no
+// ties (m grows by the sum of h, both parities flip with its parity);
+// otherwise the lanes' run maps composed in lane order.
+__device__ __forceinline__ Map2 slab_map(uint64_t T, uint32_t low_bits, const SlabPass &p, int k)
+{
+    constexpr uint64_t n = 64 * kLaneVectors * kTerms;
+    if (__all((low_bits & ((1u << k) - 1)) == 0))
+        return untied_map(T >> k);
+    const uint32_t RR = wave_total32(p.rr_sum);
+    if (!__any(p.rr_min == 0))
+        return untied_map((T + (n << (k - 1)) - RR) >> k);
+    return run_map(wave_run(p.m), T, n, RR, k);
+}
+
+// Slab si of its chunk; lane 0 writes its part of the entry.  One pass over
+// the terms gives the total, the low bits and the pass for the predicted
+// binade; a slab whose chunk may cross into the next binade gets a second
+// pass for it.
+template <int KK>
+__device__ __forceinline__ void item_maps(ItemData &x, int si, int e, bool dual, uint64_t *entry, u32x4 *lds)
 {
     const int k = e - 52;
 #pragma unroll
     for (int j = 0; j < kLaneVectors; ++j)
         keep_if<KK>((x.ok >> j) & 1u, x.a[j], x.b[j]);
+    consecutive<KK>(x.a, x.b, lds);
     uint64_t tot = 0;
     uint32_t low_bits = 0;
+    SlabPass p;
 #pragma unroll
     for (int j = 0; j < kLaneVectors; ++j)
 #pragma unroll
@@ -711,14 +747,20 @@ __device__ __forceinline__ void item_maps(ItemData &x, int si, int e, bool dual,
             const uint32_t t = vector_term<KK>(x.a[j], x.b[j], i);
             tot += t;
             low_bits |= t;
+            pass_term(p, t, k);
         }
-    forget<KK>(x.a, x.b);
     const uint64_t T = wave_total64(tot);
-    const Map2 slab = slab_map<KK>(x.a, x.b, low_bits, T, k);
+    const Map2 slab = slab_map(T, low_bits, p, k);
     Map2 slab_b;
     if (dual) {
         forget<KK>(x.a, x.b);
-        slab_b = slab_map<KK>(x.a, x.b, low_bits, T, k + 1);
+        SlabPass q;
+#pragma unroll
+        for (int j = 0; j < kLaneVectors; ++j)
+#pragma unroll
+            for (int i = 0; i < kTerms; ++i)
+                pass_term(q, vector_term<KK>(x.a[j], x.b[j], i), k + 1);
+        slab_b = slab_map(T, low_bits, q, k + 1);
     }
     if ((threadIdx.x & 63) == 0) {
         entry[kSlabMapsA + 3 * si + 0] = slab.dm0;
@@ -772,10 +814,12 @@ __device__ __forceinline__ SlabItem slab_item(const Slabs &Q, int64_t i)
 // are read while the current one is mapped, except for the noise, which
 // reads both planes.
 template <int KK>
-__device__ __forceinline__ void queue_maps(const Slabs &Q, int64_t i, int64_t stride, int64_t n)
+__device__ __forceinline__ void queue_maps(const Slabs &Q, int64_t i, int64_t stride, int64_t n, u32x4 *lds)
 {
     ItemData x, y;
-    auto map_item = [&](ItemData &d, const SlabItem &it) { item_maps<KK>(d, it.si, it.e, it.dual, it.entry); };
+    auto map_item = [&](ItemData &d, const SlabItem &it) {
+        item_maps<KK>(d, it.si, it.e, it.dual, it.entry, lds);
+    };
     SlabItem u = slab_item<KK>(Q, i);
     load_item<KK>(x, Q.R, Q.D, u.cb, u.sb, u.ce);
     if constexpr (KK == kSqNoise) {
@@ -814,10 +858,6 @@ __device__ __forceinline__ void queue_maps(const Slabs &Q, int64_t i, int64_t st
     }
 }
 
-// Waves of the maps kernel: 4 per SIMD (its register use allows 4) on 256
-// CUs of 4 SIMDs.
-constexpr int64_t kMapWaves = 4096;
-
 // A fixed grid of waves shares out the slabs of the three queues: wave w
 // takes slab items w, w + W, w + 2W, ... of each queue in turn (W waves in
 // all).  Two-byte samples only.
@@ -828,6 +868,8 @@ __global__ __launch_bounds__(kThreads) void cpu_order_maps(const void *ref, cons
     const int64_t w = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + threadIdx.x / 64;
     const int64_t W = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
     const uint32_t *counts = reinterpret_cast<const uint32_t *>(rec + kQueueCounts);
+    __shared__ u32x4 lds_all[kThreads / 64][2 * kSlabVectors];
+    u32x4 *lds = lds_all[threadIdx.x / 64];
     const int64_t cap = static_cast<int64_t>(nframes) * chunks;
     Slabs Q;
     Q.R = static_cast<const u32x4 *>(ref);
@@ -838,15 +880,15 @@ __global__ __launch_bounds__(kThreads) void cpu_order_maps(const void *ref, cons
     int64_t n = static_cast<int64_t>(counts[kSqNoise]) * kSlabs;
     Q.queue = queue + kSqNoise * cap;
     if (w < n)
-        queue_maps<kSqNoise>(Q, w, W, n);
+        queue_maps<kSqNoise>(Q, w, W, n, lds);
     n = static_cast<int64_t>(counts[kSqRef]) * kSlabs;
     Q.queue = queue + kSqRef * cap;
     if (w < n)
-        queue_maps<kSqRef>(Q, w, W, n);
+        queue_maps<kSqRef>(Q, w, W, n, lds);
     n = static_cast<int64_t>(counts[kSqDist]) * kSlabs;
     Q.queue = queue + kSqDist * cap;
     if (w < n)
-        queue_maps<kSqDist>(Q, w, W, n);
+        queue_maps<kSqDist>(Q, w, W, n, lds);
 }
 
 // ------------------------------------------------------------------ 4. walk
@@ -1157,6 +1199,32 @@ __global__ __launch_bounds__(64) void cpu_order_walk(const void *ref, const void
     }
 }
 
+// Workgroups of the maps kernel that the current device holds at once (its
+// occupancy per CU, from its register and LDS use, times the CUs), asked
+// once per device.
+hipError_t maps_resident_workgroups(int64_t &wgs)
+{
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int64_t> cache[kMaxDevices];
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return err;
+    const bool cached = dev >= 0 && dev < kMaxDevices;
+    if (cached && (wgs = cache[dev].load(std::memory_order_relaxed)) > 0)
+        return hipSuccess;
+    int per_cu = 0, cus = 0;
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, cpu_order_maps, kThreads, 0);
+    if (err == hipSuccess)
+        err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess)
+        return err;
+    wgs = static_cast<int64_t>(per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+    if (cached)
+        cache[dev].store(wgs, std::memory_order_relaxed);
+    return hipSuccess;
+}
+
 }  // namespace
 
 CpuOrderLayout cpu_order_layout(const Geometry &g)
@@ -1195,12 +1263,16 @@ hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, cons
     err = hipGetLastError();
     if (err != hipSuccess || !two_byte)
         return err;
-    // enough waves to fill the chip at the maps kernel's occupancy, never
-    // more than there can be slabs
-    const int64_t slabs = g.workgroups * kSquares * kSlabs;
-    const int64_t waves = slabs < kMapWaves ? slabs : kMapWaves;
-    cpu_order_maps<<<dim3(static_cast<unsigned>((waves + kThreads / 64 - 1) / (kThreads / 64))), kThreads, 0,
-                     stream>>>(ref, dist, g.pixels, g.chunks, g.nframes, rec, queue, maps);
+    // as many workgroups as the device holds at once, never more than there
+    // can be slabs
+    int64_t resident = 0;
+    err = maps_resident_workgroups(resident);
+    if (err != hipSuccess)
+        return err;
+    const int64_t slab_wgs = (g.workgroups * kSquares * kSlabs + kThreads / 64 - 1) / (kThreads / 64);
+    const int64_t wgs = slab_wgs < resident ? slab_wgs : resident;
+    cpu_order_maps<<<dim3(static_cast<unsigned>(wgs)), kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks,
+                                                                             g.nframes, rec, queue, maps);
     err = hipGetLastError();
     if (err != hipSuccess)
         return err;
