@@ -21,14 +21,19 @@ timed batch must match the oracle (exact integers; bit-identical doubles
 below 2^53 units; within the float_moment bound past it) or nothing is
 reported.
 
+``read_ceiling`` (this mode only) times the library's read probe, which
+reads the same batch with stage 1's grid, chunks and loads but does no
+arithmetic: the practical read ceiling of stage 1's access pattern, beside
+which stage 1's own time is put.
+
 ``--mode cpu-order`` measures the other entry point instead: each step also
 reproduces the CPU's own rounding past 2^53 (vqx_plane_stats_batch_cpu_order_ws:
-stage 1, stage 2, the prefix scan, the maps pass over what lies past 2^53,
-the walk), and the host concludes those sums.  Its roofline is the whole
-step against the bytes it must read (both planes once, and again the part
-of each plane past 2^53), timed with HIP events around each group of steps;
-the gate is bit-identity with the oracle's sequential doubles on every
-frame.
+stage 1, stage 2, the prefix scan, the maps pass over the chunks past 2^53
+inside which adds can round, the walk), and the host concludes those sums.
+Its roofline is the whole step against the bytes it must read (both planes
+once, and those chunks again), timed with HIP events around each group of
+steps; the gate is bit-identity with the oracle's sequential doubles on
+every frame.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5] [--mode exact|cpu-order]
 """
@@ -397,6 +402,36 @@ def past53_bytes(ref, dist, bpc):
     return total
 
 
+def measure_read_ceiling(L, hip, torch, bufs, wl, ws, ws_bytes, st, stage1_ms, alg_bytes, n):
+    """The read time of stage 1's access pattern: the library's read probe
+    (stage 1's grid, chunks and loads, no arithmetic) dispatched n times after
+    20 untimed ones, alternating the two batch copies, each dispatch stamping
+    its own events."""
+    warm = 20
+    evs = [(hip.create(), hip.create()) for _ in range(warm + n)]
+    for j, (b, e) in enumerate(evs):
+        r, d = bufs[j % 2]
+        rc = L.vqx_read_probe_timed(r.data_ptr(), d.data_ptr(), wl.w, wl.h, wl.bpc, wl.nframes, ws.data_ptr(),
+                                    ws_bytes, st, b, e)
+        if rc != 0:
+            raise RuntimeError(f"vqx_read_probe_timed: status {rc}")
+    torch.cuda.synchronize()
+    ms = [hip.elapsed_ms(b, e) for b, e in evs[warm:]]
+    for b, e in evs:
+        hip.destroy(b)
+        hip.destroy(e)
+    probe_ms = statistics.fmean(ms)
+    gbs = alg_bytes / (probe_ms * 1e-3) / 1e9
+    return {
+        "kernel": "read_probe (stage 1's grid, chunks and 16-byte loads; an XOR of every word, no arithmetic)",
+        "dispatches": n,
+        "us_mean": round(probe_ms * 1e3, 2),
+        "GBps": round(gbs, 1),
+        "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "stage1_frac_of_ceiling": round(probe_ms / stage1_ms, 4),
+    }
+
+
 def load_or_generate(number, cache_dir):
     """The workload's batch, from ``cache_dir`` when it holds a copy whose
     digest matches the recipe's, else freshly generated (and stored there)."""
@@ -515,6 +550,7 @@ def run_host_mode(args, np, torch, vqx, wl, ref_np, dist_np, t_gen):
         },
         "generation_s": round(t_gen, 1),
     }
+
     if not args.no_cpu_baseline:
         threads = cpu_threads()
         last = history[-1]
@@ -773,6 +809,11 @@ def main(argv=None):
     bytes_per_frame = wl.bytes_per_frame
     bytes_per_step = ref_np[0].size * wl.bytes_per_sample * 2 * nframes
     mean_ms = statistics.fmean(step_ms)
+    read_ceiling = None
+    if args.mode == "exact":
+        read_ceiling = measure_read_ceiling(L, hip, torch, bufs, wl, ws, ws_bytes, st, mean_ms,
+                                            mode.alg_bytes, min(args.steps, 200))
+
     wname = f"{w}x{h}x{nframes}_{bpc}bit" + ("_yuv420" if args.mode == "yuv420" else "")
     traffic = stored_traffic(mode.kernel, wname, tuple(mode.sources))
     achieved = mode.alg_bytes / (mean_ms * 1e-3) / 1e9
@@ -813,6 +854,8 @@ def main(argv=None):
         },
         "generation_s": round(t_gen, 1),
     }
+    if read_ceiling:
+        out["read_ceiling"] = read_ceiling
 
     if not args.no_cpu_baseline:
         threads = cpu_threads()

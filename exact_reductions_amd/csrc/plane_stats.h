@@ -50,13 +50,18 @@ Geometry make_geometry(int w, int h, int bpc, int nframes);
 // Work-items per workgroup of the launches over (frame, chunk).
 constexpr int kChunkThreads = 256;
 
-// A dispatch counts its work-items in 32 bits.  The plane-stats launch has
-// one workgroup per (frame, chunk); the CPU-order maps launch one per
-// (frame, chunk, square sum), i.e. per_chunk = 3.
-inline bool fits_dispatch(const Geometry &g, int per_chunk)
+// A dispatch counts its work-items in 32 bits.  The widest launch of every
+// entry point is stage 1's (or its view form's), one workgroup per (frame,
+// chunk).
+inline bool fits_dispatch(const Geometry &g)
 {
-    return g.workgroups * per_chunk * kChunkThreads <= static_cast<int64_t>(0xffffffffu);
+    return g.workgroups * kChunkThreads <= static_cast<int64_t>(0xffffffffu);
 }
+
+// Stage 1's grid and loads with no arithmetic (measurement only); the
+// dispatch stamps `begin` and `end`, either of which may be null.
+hipError_t launch_read_probe(const Geometry &g, const void *ref, const void *dist, uint64_t *partials,
+                             hipStream_t stream, hipEvent_t begin, hipEvent_t end);
 
 // Queues both stages on `stream`, recording `stage1_begin`/`stage1_end` (if
 // not null) around stage 1.  Returns hipSuccess or the first error.

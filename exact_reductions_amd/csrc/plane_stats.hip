@@ -174,6 +174,30 @@ __global__ __launch_bounds__(kThreads) void stage1_u16(const void *ref, const vo
     }
 }
 
+// ------------------------------------------------------- read-rate probe
+// Measurement only, no result of the method: stage 1's grid, chunks and
+// loads with no arithmetic but an XOR of every word, so that its duration
+// is the read time of stage 1's access pattern.  Nothing is written unless
+// the XOR hits one chosen value (which keeps the loads live).
+struct AccXor {
+    uint32_t x = 0;
+};
+
+__device__ __forceinline__ void add_dword(AccXor &a, uint32_t r, uint32_t d) { a.x ^= r ^ d; }
+
+template <int kBytes>
+__global__ __launch_bounds__(kThreads) void read_probe(const void *ref, const void *dist, int64_t pixels,
+                                                       int chunks, uint64_t *part)
+{
+    const int64_t wg = blockIdx.x;
+    const int64_t frame = wg / chunks;
+    const int chunk = static_cast<int>(wg - frame * chunks);
+    AccXor a;
+    accumulate_chunk<kBytes>(a, ref, dist, pixels, chunk, frame);
+    if (a.x == 0x9e3779b9u)
+        part[wg * kRecordStride] = a.x;
+}
+
 // ------------------------------------------------------------------ stage 2
 // One workgroup per frame adds the frame's records in uint64.
 __global__ __launch_bounds__(kThreads) void stage2_combine(const uint64_t *part, int chunks,
@@ -235,6 +259,18 @@ hipError_t launch_plane_stats(const Geometry &g, const void *ref, const void *di
     stage2_combine<<<dim3(static_cast<unsigned>(g.nframes)), kThreads, 0, stream>>>(
         partials, chunks, out_noise, out_moments);
     return hipGetLastError();
+}
+
+hipError_t launch_read_probe(const Geometry &g, const void *ref, const void *dist, uint64_t *partials,
+                             hipStream_t stream, hipEvent_t begin, hipEvent_t end)
+{
+    int64_t pixels = g.pixels;
+    int chunks = g.chunks;
+    void *args[] = {const_cast<void **>(&ref), const_cast<void **>(&dist), &pixels, &chunks, &partials};
+    const void *fn = g.sample_bytes == 1 ? reinterpret_cast<const void *>(&read_probe<1>)
+                                         : reinterpret_cast<const void *>(&read_probe<2>);
+    return hipExtLaunchKernel(fn, dim3(static_cast<unsigned>(g.workgroups)), dim3(kThreads), args, 0, stream, begin,
+                              end, 0);
 }
 
 }  // namespace vqx

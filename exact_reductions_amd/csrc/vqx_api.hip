@@ -30,9 +30,7 @@ int check_shape(int w, int h, int bpc)
     return VQX_OK;
 }
 
-// per_chunk: workgroups per (frame, chunk) of the widest launch of the
-// entry point (1 plane stats, 3 the CPU-order form).
-int check_batch(int w, int h, int bpc, int nframes, int per_chunk = 1)
+int check_batch(int w, int h, int bpc, int nframes)
 {
     int rc = check_shape(w, h, bpc);
     if (rc != VQX_OK)
@@ -40,18 +38,18 @@ int check_batch(int w, int h, int bpc, int nframes, int per_chunk = 1)
     if (nframes < 1)
         return VQX_E_NFRAMES;
     // every launch must fit one dispatch
-    if (!vqx::fits_dispatch(vqx::make_geometry(w, h, bpc, nframes), per_chunk))
+    if (!vqx::fits_dispatch(vqx::make_geometry(w, h, bpc, nframes)))
         return VQX_E_NFRAMES;
     return VQX_OK;
 }
 
 // All argument checks of the plane-stats entry points, in a fixed order.
 int check_stats_args(const void *ref, const void *dist, int w, int h, int bpc, int nframes,
-                     const uint64_t *out_noise, const uint64_t *out_moments, int per_chunk = 1)
+                     const uint64_t *out_noise, const uint64_t *out_moments)
 {
     if (!ref || !dist || !out_noise || !out_moments)
         return VQX_E_NULL;
-    int rc = check_batch(w, h, bpc, nframes, per_chunk);
+    int rc = check_batch(w, h, bpc, nframes);
     if (rc != VQX_OK)
         return rc;
     if (!aligned(ref, 16) || !aligned(dist, 16) || !aligned(out_noise, 8) || !aligned(out_moments, 8))
@@ -196,6 +194,30 @@ int vqx_plane_stats_batch_ws_timed(const void *ref, const void *dist, int w, int
     return VQX_OK;
 }
 
+int vqx_read_probe_timed(const void *ref, const void *dist, int w, int h, int bpc, int nframes, void *workspace,
+                         size_t workspace_bytes, void *stream, void *begin, void *end)
+{
+    if (!ref || !dist)
+        return VQX_E_NULL;
+    int rc = check_batch(w, h, bpc, nframes);
+    if (rc != VQX_OK)
+        return rc;
+    if (!aligned(ref, 16) || !aligned(dist, 16))
+        return VQX_E_ALIGN;
+    const vqx::Geometry g = vqx::make_geometry(w, h, bpc, nframes);
+    if (!workspace || !aligned(workspace, 16) || workspace_bytes < g.workspace_bytes)
+        return VQX_E_WORKSPACE;
+    rc = device_ready();
+    if (rc != VQX_OK)
+        return rc;
+    if (vqx::launch_read_probe(g, ref, dist, static_cast<uint64_t *>(workspace), static_cast<hipStream_t>(stream),
+                               static_cast<hipEvent_t>(begin), static_cast<hipEvent_t>(end)) != hipSuccess) {
+        (void)hipGetLastError();
+        return VQX_E_HIP;
+    }
+    return VQX_OK;
+}
+
 int vqx_plane_stats_batch_ws(const void *ref, const void *dist, int w, int h, int bpc, int nframes,
                              uint64_t *out_noise, uint64_t *out_moments, void *workspace,
                              size_t workspace_bytes, void *stream)
@@ -235,7 +257,7 @@ int vqx_plane_stats_cpu_order_workspace_bytes(int w, int h, int bpc, int nframes
 {
     if (!bytes)
         return VQX_E_NULL;
-    int rc = check_batch(w, h, bpc, nframes, vqx::kSquares);
+    int rc = check_batch(w, h, bpc, nframes);
     if (rc != VQX_OK)
         return rc;
     *bytes = vqx::cpu_order_layout(vqx::make_geometry(w, h, bpc, nframes)).bytes;
@@ -247,7 +269,7 @@ int vqx_plane_stats_batch_cpu_order_ws(const void *ref, const void *dist, int w,
                                        uint64_t *out_cpu_noise, uint64_t *out_cpu_moments,
                                        void *workspace, size_t workspace_bytes, void *stream)
 {
-    int rc = check_stats_args(ref, dist, w, h, bpc, nframes, out_noise, out_moments, vqx::kSquares);
+    int rc = check_stats_args(ref, dist, w, h, bpc, nframes, out_noise, out_moments);
     if (rc != VQX_OK)
         return rc;
     if (!out_cpu_noise || !out_cpu_moments)

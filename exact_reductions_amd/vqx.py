@@ -28,6 +28,7 @@ SYMBOLS = (
     "vqx_plane_stats_batch",
     "vqx_plane_stats_batch_ws",
     "vqx_plane_stats_batch_ws_timed",
+    "vqx_read_probe_timed",
     "vqx_plane_stats_cpu_order_workspace_bytes",
     "vqx_plane_stats_batch_cpu_order_ws",
     "vqx_conclude_psnr",
@@ -74,6 +75,7 @@ def lib() -> ctypes.CDLL:
             "vqx_plane_stats_batch": (i, [vp, vp, i, i, i, i, vp, vp, vp]),
             "vqx_plane_stats_batch_ws": (i, [vp, vp, i, i, i, i, vp, vp, vp, sz, vp]),
             "vqx_plane_stats_batch_ws_timed": (i, [vp, vp, i, i, i, i, vp, vp, vp, sz, vp, vp, vp]),
+            "vqx_read_probe_timed": (i, [vp, vp, i, i, i, i, vp, sz, vp, vp, vp]),
             "vqx_plane_stats_cpu_order_workspace_bytes": (i, [i, i, i, i, ctypes.POINTER(sz)]),
             "vqx_plane_stats_batch_cpu_order_ws": (i, [vp, vp, i, i, i, i, vp, vp, vp, vp, vp, sz, vp]),
             "vqx_conclude_psnr": (i, [u64, i, i, i, d, ctypes.POINTER(d), ctypes.POINTER(d)]),

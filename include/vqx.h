@@ -58,8 +58,7 @@ enum vqx_status {
     VQX_E_BPC = -3,       /* bpc outside 8..16 */
     VQX_E_NFRAMES = -4,   /* nframes < 1, or a batch too large for one dispatch: more
                              than (2^32-1)/256 chunks of 2048 16-byte vectors per plane
-                             (frames round up to whole chunks), a third of that for
-                             the CPU-order entry points */
+                             (frames round up to whole chunks) */
     VQX_E_ALIGN = -5,     /* ref/dist not 16-byte aligned, or an output not 8-byte aligned */
     VQX_E_WORKSPACE = -6, /* workspace smaller than vqx_plane_stats_workspace_bytes() */
     VQX_E_HIP = -7,       /* the HIP runtime reported an error (launch or allocation) */
@@ -140,6 +139,19 @@ int vqx_plane_stats_batch_ws_timed(const void *ref, const void *dist, int w, int
                                    int nframes, uint64_t *out_noise, uint64_t *out_moments,
                                    void *workspace, size_t workspace_bytes, void *stream,
                                    void *stage1_begin, void *stage1_end);
+
+/*
+ * Measurement only; it computes nothing of the method.  Reads both planes
+ * with exactly the grid, chunks and 16-byte loads of
+ * vqx_plane_stats_batch_ws's first kernel, but without its arithmetic (an
+ * XOR of every word, written nowhere), so that its duration between the
+ * events its dispatch stamps (either may be NULL) is the read time of that
+ * access pattern: the practical ceiling to compare that kernel with.
+ * Arguments, workspace and errors are those of vqx_plane_stats_batch_ws_timed
+ * without the outputs; the workspace's contents are left unspecified.
+ */
+int vqx_read_probe_timed(const void *ref, const void *dist, int w, int h, int bpc, int nframes,
+                         void *workspace, size_t workspace_bytes, void *stream, void *begin, void *end);
 
 /*
  * Device scratch needed by vqx_plane_stats_batch_cpu_order_ws.  Host-only.

@@ -76,18 +76,16 @@ def test_largest_frame_accepted():
 
 def test_batch_must_fit_one_dispatch():
     """A dispatch counts its work-items in 32 bits: at 256 per workgroup the
-    plane-stats launch takes at most (2^32-1)//256 chunks, the CPU-order maps
-    launch (three workgroups per chunk) a third of that.  1x1 frames are one
-    chunk each."""
+    widest launch, stage 1's, takes at most (2^32-1)//256 chunks, in the
+    CPU-order form too.  1x1 frames are one chunk each."""
     top = (2**32 - 1) // 256
     assert vqx.plane_stats_workspace_bytes(1, 1, 16, top) == top * 64
     with pytest.raises(vqx.VqxError) as e:
         vqx.plane_stats_workspace_bytes(1, 1, 16, top + 1)
     assert e.value.status == vqx.E_NFRAMES
-    top3 = (2**32 - 1) // (3 * 256)
-    assert vqx.plane_stats_cpu_order_workspace_bytes(1, 1, 16, top3) > 0
+    assert vqx.plane_stats_cpu_order_workspace_bytes(1, 1, 16, top) > 0
     with pytest.raises(vqx.VqxError) as e:
-        vqx.plane_stats_cpu_order_workspace_bytes(1, 1, 16, top3 + 1)
+        vqx.plane_stats_cpu_order_workspace_bytes(1, 1, 16, top + 1)
     assert e.value.status == vqx.E_NFRAMES
     # 4K 16-bit frames: 507 chunks each
     assert vqx.plane_stats_workspace_bytes(3840, 2160, 16, top // 507) > 0
@@ -170,6 +168,24 @@ def test_cpu_order_arguments(L):
     assert b.untouched()
     with pytest.raises(vqx.VqxError):
         vqx.plane_stats_cpu_order_workspace_bytes(4, 4, 20, 1)
+
+
+def test_read_probe_arguments(L):
+    """The measurement probe checks its arguments like the timed entry point
+    and queues nothing when they are wrong."""
+    b = _Buffers()
+    ws = np.zeros(4096, dtype=np.uint8)
+    base = (ws.ctypes.data + 255) // 256 * 256
+    need = vqx.plane_stats_workspace_bytes(16, 4, 8, 2)
+    f = L.vqx_read_probe_timed
+    assert f(None, b.dist, 16, 4, 8, 2, base, need, None, None, None) == vqx.E_NULL
+    assert f(b.ref, b.dist + 8, 16, 4, 8, 2, base, need, None, None, None) == vqx.E_ALIGN
+    assert f(b.ref, b.dist, 16, 4, 8, 2, base, need - 1, None, None, None) == vqx.E_WORKSPACE
+    assert f(b.ref, b.dist, 16, 4, 8, 2, None, need, None, None, None) == vqx.E_WORKSPACE
+    assert f(b.ref, b.dist, 16, 0, 8, 2, base, need, None, None, None) == vqx.E_DIMS
+    assert f(b.ref, b.dist, 16, 4, 17, 2, base, need, None, None, None) == vqx.E_BPC
+    assert f(b.ref, b.dist, 16, 4, 8, 0, base, need, None, None, None) == vqx.E_NFRAMES
+    assert np.all(ws == 0)
 
 
 def test_workspace_errors(L):

@@ -280,3 +280,38 @@ def test_misaligned_base_is_rejected():
     with pytest.raises(vqx.VqxError) as e:
         vqx.plane_stats_batch(ref[1:].view(1, 16, 16), ref[1:].view(1, 16, 16), 8)
     assert e.value.status == vqx.E_ALIGN
+
+
+@pytest.mark.parametrize("n,frames", [(1, 4), (5, 2), (2, 3)])
+def test_read_probe_then_sums(n, frames):
+    """The measurement probe runs on a batch (its dispatch stamping both
+    events), and a following call that reuses its workspace is still exact."""
+    wl = synth.WORKLOADS[n]
+    ref, dist = synth.generate(n, nframes=frames)
+    r, d = upload(ref), upload(dist)
+    f, h, w = ref.shape
+    ws = torch.full((vqx.plane_stats_workspace_bytes(w, h, wl.bpc, f),), 0xFF, dtype=torch.uint8, device="cuda:0")
+    rt = vqx.hip_runtime()
+    import ctypes
+    rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for e in evs:
+        assert rt.hipEventCreate(ctypes.byref(e)) == 0
+    st = torch.cuda.current_stream().cuda_stream
+    L = vqx.lib()
+    assert L.vqx_read_probe_timed(r.data_ptr(), d.data_ptr(), w, h, wl.bpc, f, ws.data_ptr(), ws.numel(), st,
+                                  evs[0], evs[1]) == 0
+    noise = torch.empty(f, dtype=torch.int64, device="cuda:0")
+    moments = torch.empty((f, 4), dtype=torch.int64, device="cuda:0")
+    vqx.plane_stats_batch_ws(r, d, wl.bpc, noise, moments, ws)
+    torch.cuda.synchronize()
+    ms = ctypes.c_float()
+    assert rt.hipEventElapsedTime(ctypes.byref(ms), evs[0], evs[1]) == 0 and ms.value > 0
+    for e in evs:
+        rt.hipEventDestroy(e)
+    n_np, m_np = noise.cpu().numpy(), moments.cpu().numpy()
+    for k in range(f):
+        want = oracle.exact_frame_sums(ref[k], dist[k])
+        assert [int(n_np[k])] + [int(v) for v in m_np[k]] == list(want)
