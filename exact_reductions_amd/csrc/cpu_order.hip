@@ -457,6 +457,9 @@ constexpr int kEntry = kChunkMap + 3;
 // (from stage 1's low bits), so nothing rounds inside the chunk, and no
 // crossing is predicted in it.  Its slabs are not mapped.
 constexpr uint64_t kChunkOnly = 1ull << 20;
+// The chunk-map flags of a queued chunk: its slabs are mapped.  A chunk
+// that ends below 2^53 (or holds no vector) has flags 0.
+constexpr uint64_t kQueued = 1ull << 21;
 
 // Queues of chunks to map, one per square sum, each of capacity
 // nframes * chunks: an item is (frame * chunks + chunk) | e << 32 |
@@ -578,9 +581,9 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int6
                 entry[kChunkMap + 0] = m.dm0;
                 entry[kChunkMap + 1] = m.dm1;
                 entry[kChunkMap + 2] = map_flags(m, x.e) | kChunkOnly;
-            } else if (x.queued) {
-                entry[kChunkMap + 2] = 0;
-                nq += 1ull << (21 * kk);
+            } else {
+                entry[kChunkMap + 2] = x.queued ? kQueued : 0;
+                nq += x.queued ? 1ull << (21 * kk) : 0;
             }
             p += r[field];
         }
@@ -1049,128 +1052,259 @@ __device__ __forceinline__ uint64_t walk_chunk(uint64_t S, const u32x4 *R, const
     return S;
 }
 
-// Chunk c of a frame as the walk sees it: the vectors' part of its record
-// (chunk 0's also holds the head and tail samples) and its map, composed
-// from its slab maps (flags 0 unless all are valid and for one binade).
-// Every lane reads (chunk chunks - 1 stands in past the end), so that no
-// branch holds the reads back from the waits for them; the map fields hold
-// whatever the workspace held for chunks without an entry (empty ones, and
-// those before the exact sum reaches 2^53), and the walk uses them only for
-// non-empty chunks past 2^53.
-struct ChunkView {
-    uint64_t T, dm[kSlabs][2], fl[kSlabs], cm[3];
+// ---------------------------------------------------- 4a. chunk and block maps
+// Compact maps for the walk, one record {T, dm0, dm1, flags} (kCompact
+// uint64) per (frame, chunk, square sum) and per (frame, block of 64
+// chunks, square sum):
+//  * T: the exact total of the chunk's whole vectors (chunk 0's record
+//    less the frame's head and tail samples), or of the block's chunks;
+//  * the map composed from the chunk's slab maps (or its own map when it
+//    cannot round), or from the block's chunk maps; flags 0 (no map) unless
+//    every part holds a map for one binade.  Chunks without vectors count
+//    as the identity.
+constexpr int kCompact = 4;
+constexpr int kBlockChunks = 64;
+
+__host__ __device__ __forceinline__ int frame_blocks(int chunks) { return (chunks + kBlockChunks - 1) / kBlockChunks; }
+
+// Terms of the frame's samples before its first whole vector (lane < head)
+// and after its last (lane < tail); both are fewer than 8.
+struct FrameEdges {
+    int64_t vb, ve, tail_begin;
+    int head, tail;
+    uint32_t hterm, tterm;
 };
 
-__device__ __forceinline__ ChunkView load_chunk(const uint64_t *rec, const uint64_t *entries, int64_t frame,
-                                                int chunks, int c, int kk, uint64_t head_tail)
+template <int KK>
+__device__ __forceinline__ FrameEdges frame_edges(const void *ref, const void *dist, int64_t pixels, int64_t frame)
 {
-    const int cc = c < chunks ? c : chunks - 1;
-    const uint64_t *entry = entries + static_cast<int64_t>(cc) * kSquares * kEntry;
-    ChunkView x;
-    const uint64_t r = rec[(frame * chunks + cc) * kRecordStride + record_field(kk)];
-    x.T = c < chunks ? r - (c == 0 ? head_tail : 0) : 0;
-#pragma unroll
-    for (int j = 0; j < kSlabs; ++j) {
-        x.dm[j][0] = entry[kSlabMapsA + 3 * j];
-        x.dm[j][1] = entry[kSlabMapsA + 3 * j + 1];
-        x.fl[j] = entry[kSlabMapsA + 3 * j + 2];
-    }
-#pragma unroll
-    for (int j = 0; j < 3; ++j)
-        x.cm[j] = entry[kChunkMap + j];
+    constexpr int V = 8;
+    const int lane = threadIdx.x & 63;
+    const int64_t e0 = frame * pixels, e1 = e0 + pixels;
+    FrameEdges x;
+    x.vb = (e0 + V - 1) / V;
+    x.ve = e1 / V;
+    const int64_t head_end = x.vb < x.ve ? x.vb * V : e1;
+    x.tail_begin = x.vb < x.ve ? x.ve * V : e1;
+    x.head = static_cast<int>(head_end - e0);
+    x.tail = static_cast<int>(e1 - x.tail_begin);
+    const uint16_t *r16 = static_cast<const uint16_t *>(ref);
+    const uint16_t *d16 = static_cast<const uint16_t *>(dist);
+    x.hterm = lane < x.head ? square_term<2>(KK, r16[e0 + lane], d16[e0 + lane]) : 0u;
+    x.tterm = lane < x.tail ? square_term<2>(KK, r16[x.tail_begin + lane], d16[x.tail_begin + lane]) : 0u;
     return x;
 }
 
-__device__ __forceinline__ Map2 chunk_map(const ChunkView &x, uint64_t &flags)
+// The map of a chunk from its entry (flags 0 where it has none for one
+// binade).
+__device__ __forceinline__ Map2 entry_map(const uint64_t *entry, uint64_t &flags)
 {
-    if (x.cm[2] & kChunkOnly) {
-        flags = x.cm[2] & ~kChunkOnly;
-        return map_from(x.cm[0], x.cm[1], x.cm[2]);
+    const uint64_t cf = entry[kChunkMap + 2];
+    if (cf & kChunkOnly) {
+        flags = cf & ~kChunkOnly;
+        return map_from(entry[kChunkMap + 0], entry[kChunkMap + 1], cf);
     }
     Map2 m;
-    const uint64_t key = x.fl[0] & 0xffffu;  // valid bit and binade of slab 0
+    flags = 0;
+    if (!(cf & kQueued))
+        return m;
+    const uint64_t key = entry[kSlabMapsA + 2] & 0xffffu;  // valid bit and binade of slab 0
     bool ok = (key & 1u) != 0;
 #pragma unroll
     for (int j = 0; j < kSlabs; ++j) {
-        m = map_then(m, map_from(x.dm[j][0], x.dm[j][1], x.fl[j]));
-        ok = ok && (x.fl[j] & 0xffffu) == key;
+        const uint64_t fl = entry[kSlabMapsA + 3 * j + 2];
+        m = map_then(m, map_from(entry[kSlabMapsA + 3 * j], entry[kSlabMapsA + 3 * j + 1], fl));
+        ok = ok && (fl & 0xffffu) == key;
     }
     flags = ok ? map_flags(m, flags_binade(key)) : 0;
     return m;
 }
 
 template <int KK>
-__device__ __forceinline__ void walk_frame(const void *ref, const void *dist, int64_t pixels, int chunks,
-                                           const uint64_t *rec, const uint64_t *maps, int64_t frame, uint64_t *dst)
+__device__ __forceinline__ void compose_block(const void *ref, const void *dist, int64_t pixels, int chunks,
+                                              const uint64_t *rec, const uint64_t *maps, int64_t frame, int block,
+                                              uint64_t *cmaps, uint64_t *bmaps)
 {
-    constexpr int V = 8;
+    const int lane = threadIdx.x & 63;
+    const FrameEdges fe = frame_edges<KK>(ref, dist, pixels, frame);
+    const uint64_t edges = block == 0 ? wave_total64(fe.hterm) + wave_total64(fe.tterm) : 0;
+    const int c = block * kBlockChunks + lane;
+    const bool in = c < chunks;
+    const bool empty = !in || fe.vb + static_cast<int64_t>(c) * kChunkVectors >= fe.ve;
+    uint64_t T = 0, flags = 0;
+    Map2 m;
+    if (in) {
+        const int64_t wg = frame * chunks + c;
+        T = rec[wg * kRecordStride + record_field(KK)] - (c == 0 ? edges : 0);
+        if (!empty)
+            m = entry_map(maps + (wg * kSquares + KK) * kEntry, flags);
+        uint64_t *out = cmaps + (wg * kSquares + KK) * kCompact;
+        out[0] = T;
+        out[1] = m.dm0;
+        out[2] = m.dm1;
+        out[3] = flags;
+    }
+    // the block: one binade for every chunk with vectors, else no map
+    const uint64_t key = lane_value64(flags, 0) & 0xffffu;
+    const bool ok = __all(empty || ((flags & 1u) && (flags & 0xffffu) == key));
+    const Map2 bm = wave_map(m);
+    const uint64_t BT = wave_total64(T);
+    if (lane == 0) {
+        uint64_t *out = bmaps + ((frame * frame_blocks(chunks) + block) * kSquares + KK) * kCompact;
+        out[0] = BT;
+        out[1] = bm.dm0;
+        out[2] = bm.dm1;
+        out[3] = ok && (key & 1u) ? map_flags(bm, flags_binade(key)) : 0;
+    }
+}
+
+// One wave per (frame, square sum past 2^53, block); two-byte samples only.
+__global__ __launch_bounds__(kThreads) void cpu_order_compose(const void *ref, const void *dist, int64_t pixels,
+                                                              int chunks, int nframes, const uint64_t *rec,
+                                                              const uint64_t *totals, const uint64_t *maps,
+                                                              uint64_t *cmaps, uint64_t *bmaps)
+{
+    const int blocks = frame_blocks(chunks);
+    const int64_t w = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + threadIdx.x / 64;
+    const int64_t fk = w / blocks;  // frame * kSquares + kk
+    if (fk >= static_cast<int64_t>(nframes) * kSquares || totals[fk] < kTwo53)
+        return;
+    const int64_t frame = fk / kSquares;
+    const int kk = static_cast<int>(fk - frame * kSquares);
+    const int block = static_cast<int>(w - fk * blocks);
+    switch (kk) {
+    case kSqNoise: compose_block<kSqNoise>(ref, dist, pixels, chunks, rec, maps, frame, block, cmaps, bmaps); break;
+    case kSqRef: compose_block<kSqRef>(ref, dist, pixels, chunks, rec, maps, frame, block, cmaps, bmaps); break;
+    default: compose_block<kSqDist>(ref, dist, pixels, chunks, rec, maps, frame, block, cmaps, bmaps); break;
+    }
+}
+
+// ---------------------------------------------------------- 4b. the walk
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t from_below64(uint64_t identity, uint64_t v)
+{
+    return static_cast<uint64_t>(from_below<CTRL, ROWS>(static_cast<uint32_t>(identity), static_cast<uint32_t>(v))) |
+           (static_cast<uint64_t>(
+                from_below<CTRL, ROWS>(static_cast<uint32_t>(identity >> 32), static_cast<uint32_t>(v >> 32)))
+            << 32);
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ Map2 map_scan_step(const Map2 &m)
+{
+    Map2 o;  // the identity where there is no source
+    o.dm0 = from_below64<CTRL, ROWS>(0, m.dm0);
+    o.dm1 = from_below64<CTRL, ROWS>(0, m.dm1);
+    o.p0 = from_below<CTRL, ROWS>(0u, m.p0);
+    o.p1 = from_below<CTRL, ROWS>(1u, m.p1);
+    return map_then(o, m);
+}
+
+// Lane j gets the composite of the maps of lanes 0..j, in lane order.
+__device__ __forceinline__ Map2 wave_scan_map(Map2 m)
+{
+    m = map_scan_step<0x111, 0xf>(m);
+    m = map_scan_step<0x112, 0xf>(m);
+    m = map_scan_step<0x114, 0xf>(m);
+    m = map_scan_step<0x118, 0xf>(m);
+    m = map_scan_step<0x142, 0xa>(m);
+    return map_scan_step<0x143, 0xc>(m);
+}
+
+// The 64 chunks of one block, chunk b*64 + j in lane j, from S.
+// Repeatedly: below 2^53, prefix sums of the chunk totals find the chunk in
+// which S gets there; past it, prefix compositions of the chunk maps find
+// the first chunk without a map for S's binade or in which S leaves it;
+// S is moved to just before that chunk, which is walked slab by slab.
+template <int KK>
+__device__ __forceinline__ uint64_t walk_block(uint64_t S, const u32x4 *R, const u32x4 *D, const uint64_t *cmaps,
+                                               const uint64_t *entries, int64_t frame, int chunks, int block,
+                                               const FrameEdges &fe)
+{
+    const int lane = threadIdx.x & 63;
+    const int c = block * kBlockChunks + lane;
+    const int n = chunks - block * kBlockChunks < kBlockChunks ? chunks - block * kBlockChunks : kBlockChunks;
+    const bool in = lane < n;
+    const bool empty = !in || fe.vb + static_cast<int64_t>(c) * kChunkVectors >= fe.ve;
+    uint64_t T = 0, flags = 0;
+    Map2 m;
+    if (in) {
+        const uint64_t *x = cmaps + ((frame * chunks + c) * kSquares + KK) * kCompact;
+        T = x[0];
+        m = map_from(x[1], x[2], x[3]);
+        flags = x[3];
+    }
+    int from = 0;  // chunks before `from` are done
+    while (from < n) {
+        const bool act = lane >= from;
+        int jx;  // the chunk to walk slab by slab
+        if (S < kTwo53) {
+            const uint64_t t = act ? T : 0;
+            const uint64_t incl = wave_scan64(t);
+            const uint64_t rest = lane_value64(incl, 63);
+            if (S + rest < kTwo53)
+                return S + rest;
+            jx = __builtin_ctzll(__ballot(act && S + incl >= kTwo53));
+            S += lane_value64(incl - t, jx);  // exact: every add before it stays below 2^53
+        } else {
+            const int e = binade(S);
+            const int k = e - 52;
+            const bool ok = empty || ((flags & 1u) && flags_binade(flags) == e);
+            const Map2 pm = wave_scan_map(act && !empty ? m : Map2{});
+            const uint64_t mm = S >> k;
+            const uint64_t m2 = mm + pick(mm, pm.dm0, pm.dm1);  // m after chunks from..lane
+            const uint64_t bad = __ballot(act && (!ok || m2 >= kTwo53));
+            if (!bad)
+                return lane_value64(m2, 63) << k;
+            jx = __builtin_ctzll(bad);
+            if (jx > from)
+                S = lane_value64(m2, jx - 1) << k;
+        }
+        const int64_t cb = fe.vb + static_cast<int64_t>(block * kBlockChunks + jx) * kChunkVectors;
+        const int64_t ce = cb + kChunkVectors < fe.ve ? cb + kChunkVectors : fe.ve;
+        S = walk_chunk<KK>(S, R, D, entries + static_cast<int64_t>(block * kBlockChunks + jx) * kSquares * kEntry,
+                           cb, ce);
+        from = jx + 1;
+    }
+    return S;
+}
+
+template <int KK>
+__device__ __forceinline__ void walk_frame(const void *ref, const void *dist, int64_t pixels, int chunks,
+                                           const uint64_t *maps, const uint64_t *cmaps, const uint64_t *bmaps,
+                                           int64_t frame, uint64_t *dst)
+{
     const int lane = threadIdx.x;
-    const int64_t e0 = frame * pixels, e1 = e0 + pixels;
-    const int64_t vb = (e0 + V - 1) / V, ve = e1 / V;
-    const int64_t head_end = vb < ve ? vb * V : e1;
-    const int64_t tail_begin = vb < ve ? ve * V : e1;
-    const int head = static_cast<int>(head_end - e0), tail = static_cast<int>(e1 - tail_begin);
-    const uint16_t *r16 = static_cast<const uint16_t *>(ref);
-    const uint16_t *d16 = static_cast<const uint16_t *>(dist);
-    const uint32_t hterm = lane < head ? square_term<2>(KK, r16[e0 + lane], d16[e0 + lane]) : 0u;
-    const uint32_t tterm = lane < tail ? square_term<2>(KK, r16[tail_begin + lane], d16[tail_begin + lane]) : 0u;
-    const uint64_t hsum = wave_total64(hterm), tsum = wave_total64(tterm);
+    const FrameEdges fe = frame_edges<KK>(ref, dist, pixels, frame);
     // the head comes first in raster order; it is far below 2^53, so exact
-    uint64_t S = hsum;
+    uint64_t S = wave_total64(fe.hterm);
     const u32x4 *R = static_cast<const u32x4 *>(ref);
     const u32x4 *D = static_cast<const u32x4 *>(dist);
     const uint64_t *entries = maps + (frame * chunks * kSquares + KK) * kEntry;  // chunk c: + c * kSquares * kEntry
-    ChunkView cur = load_chunk(rec, entries, frame, chunks, lane, KK, hsum + tsum);
-    for (int base = 0; base < chunks; base += 64) {
-        // one chunk per lane; the next block is read meanwhile
-        const ChunkView next = load_chunk(rec, entries, frame, chunks, base + 64 + lane, KK, 0);
-        const int c = base + lane;
-        const uint64_t block = wave_total64(cur.T);
-        if (S + block < kTwo53) {
-            S += block;
-            cur = next;
+    // block b's record in lane b (a frame has at most 2^22 vectors: 32 blocks)
+    const int blocks = frame_blocks(chunks);
+    uint64_t BT = 0, bdm0 = 0, bdm1 = 0, bfl = 0;
+    if (lane < blocks) {
+        const uint64_t *x = bmaps + ((frame * blocks + lane) * kSquares + KK) * kCompact;
+        BT = x[0];
+        bdm0 = x[1];
+        bdm1 = x[2];
+        bfl = x[3];
+    }
+    for (int b = 0; b < blocks; ++b) {
+        const uint64_t T = lane_value64(BT, b);
+        if (S + T < kTwo53) {
+            S += T;
             continue;
         }
-        // past 2^53 within this block: every non-empty chunk from the one
-        // where the exact sum gets there on has its slab maps; an empty
-        // chunk (the last one of a frame may be) adds nothing
-        const bool empty = c >= chunks || vb + static_cast<int64_t>(c) * kChunkVectors >= ve;
-        uint64_t flags;
-        Map2 cm = chunk_map(cur, flags);
-        if (empty) {
-            cm = Map2{};
-            flags = 0;
-        }
-        bool done = false;
-        if (S >= kTwo53) {
-            const int e = binade(S);
-            if (__all(empty || ((flags & 1u) && flags_binade(flags) == e)))
-                done = map_apply(S, wave_map(cm), e);
-        }
-        if (!done) {
-            const int n = chunks - base < 64 ? chunks - base : 64;
-            for (int j = 0; j < n; ++j) {
-                const int64_t cb = vb + static_cast<int64_t>(base + j) * kChunkVectors;
-                const int64_t ce = cb + kChunkVectors < ve ? cb + kChunkVectors : ve;
-                if (cb >= ce)
-                    continue;
-                const uint64_t Tj = lane_value64(cur.T, j);
-                if (S + Tj < kTwo53) {
-                    S += Tj;
-                    continue;
-                }
-                const uint64_t fl = lane_value64(flags, j);
-                if ((fl & 1u) &&
-                    map_apply(S, map_from(lane_value64(cm.dm0, j), lane_value64(cm.dm1, j), fl), flags_binade(fl)))
-                    continue;
-                S = walk_chunk<KK>(S, R, D, entries + static_cast<int64_t>(base + j) * kSquares * kEntry, cb, ce);
-            }
-        }
-        cur = next;
+        const uint64_t fl = lane_value64(bfl, b);
+        if ((fl & 1u) && map_apply(S, map_from(lane_value64(bdm0, b), lane_value64(bdm1, b), fl), flags_binade(fl)))
+            continue;
+        S = walk_block<KK>(S, R, D, cmaps, entries, frame, chunks, b, fe);
     }
     // the tail comes last
-    for (int j = 0; j < tail; ++j)
-        S = cpu_add(S, lane_value(tterm, j));
+    for (int j = 0; j < fe.tail; ++j)
+        S = cpu_add(S, lane_value(fe.tterm, j));
     if (lane == 0)
         *dst = S;
 }
@@ -1178,9 +1312,9 @@ __device__ __forceinline__ void walk_frame(const void *ref, const void *dist, in
 // One wave per (frame, square sum); two-byte samples only.  Sums that stay
 // below 2^53 were written by the prefix scan.
 __global__ __launch_bounds__(64) void cpu_order_walk(const void *ref, const void *dist, int64_t pixels, int chunks,
-                                                     const uint64_t *rec, const uint64_t *totals,
-                                                     const uint64_t *maps, uint64_t *out_cpu_noise,
-                                                     uint64_t *out_cpu_moments)
+                                                     const uint64_t *totals, const uint64_t *maps,
+                                                     const uint64_t *cmaps, const uint64_t *bmaps,
+                                                     uint64_t *out_cpu_noise, uint64_t *out_cpu_moments)
 {
     const int64_t frame = blockIdx.x / kSquares;
     const int kk = static_cast<int>(blockIdx.x - frame * kSquares);
@@ -1188,13 +1322,13 @@ __global__ __launch_bounds__(64) void cpu_order_walk(const void *ref, const void
         return;
     switch (kk) {
     case kSqNoise:
-        walk_frame<kSqNoise>(ref, dist, pixels, chunks, rec, maps, frame, &out_cpu_noise[frame]);
+        walk_frame<kSqNoise>(ref, dist, pixels, chunks, maps, cmaps, bmaps, frame, &out_cpu_noise[frame]);
         break;
     case kSqRef:
-        walk_frame<kSqRef>(ref, dist, pixels, chunks, rec, maps, frame, &out_cpu_moments[4 * frame + 2]);
+        walk_frame<kSqRef>(ref, dist, pixels, chunks, maps, cmaps, bmaps, frame, &out_cpu_moments[4 * frame + 2]);
         break;
     default:
-        walk_frame<kSqDist>(ref, dist, pixels, chunks, rec, maps, frame, &out_cpu_moments[4 * frame + 3]);
+        walk_frame<kSqDist>(ref, dist, pixels, chunks, maps, cmaps, bmaps, frame, &out_cpu_moments[4 * frame + 3]);
         break;
     }
 }
@@ -1236,7 +1370,10 @@ CpuOrderLayout cpu_order_layout(const Geometry &g)
     l.queue = up(l.records + g.workspace_bytes);
     l.totals = up(l.queue + wgs * kSquares * sizeof(uint64_t));
     l.maps = up(l.totals + static_cast<size_t>(g.nframes) * kSquares * sizeof(uint64_t));
-    l.bytes = up(l.maps + wgs * kSquares * kEntry * sizeof(uint64_t));
+    l.cmaps = up(l.maps + wgs * kSquares * kEntry * sizeof(uint64_t));
+    l.bmaps = up(l.cmaps + wgs * kSquares * kCompact * sizeof(uint64_t));
+    l.bytes = up(l.bmaps + static_cast<size_t>(g.nframes) * frame_blocks(g.chunks) * kSquares * kCompact *
+                               sizeof(uint64_t));
     return l;
 }
 
@@ -1251,6 +1388,8 @@ hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, cons
     uint64_t *queue = reinterpret_cast<uint64_t *>(ws + l.queue);
     uint64_t *totals = reinterpret_cast<uint64_t *>(ws + l.totals);
     uint64_t *maps = reinterpret_cast<uint64_t *>(ws + l.maps);
+    uint64_t *cmaps = reinterpret_cast<uint64_t *>(ws + l.cmaps);
+    uint64_t *bmaps = reinterpret_cast<uint64_t *>(ws + l.bmaps);
     // stage 1 with the low bits of the terms, at two-byte samples
     hipError_t err = launch_plane_stats(g, ref, dist, out_noise, out_moments, rec, stream, nullptr, nullptr,
                                         g.sample_bytes == 2);
@@ -1276,8 +1415,14 @@ hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, cons
     err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    cpu_order_walk<<<dim3(nf * kSquares), 64, 0, stream>>>(ref, dist, g.pixels, g.chunks, rec, totals, maps,
-                                                           out_cpu_noise, out_cpu_moments);
+    const int64_t compose_waves = static_cast<int64_t>(g.nframes) * kSquares * frame_blocks(g.chunks);
+    cpu_order_compose<<<dim3(static_cast<unsigned>((compose_waves + kThreads / 64 - 1) / (kThreads / 64))), kThreads,
+                        0, stream>>>(ref, dist, g.pixels, g.chunks, g.nframes, rec, totals, maps, cmaps, bmaps);
+    err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    cpu_order_walk<<<dim3(nf * kSquares), 64, 0, stream>>>(ref, dist, g.pixels, g.chunks, totals, maps, cmaps,
+                                                           bmaps, out_cpu_noise, out_cpu_moments);
     return hipGetLastError();
 }
 

@@ -121,7 +121,7 @@ hipError_t run_host_stream(int w, int h, int bpc, int nframes, int frames_per_up
 
 // Workspace of the CPU-order form: byte offsets of its parts.
 struct CpuOrderLayout {
-    size_t records, queue, totals, maps, bytes;
+    size_t records, queue, totals, maps, cmaps, bmaps, bytes;
 };
 CpuOrderLayout cpu_order_layout(const Geometry &g);
 
