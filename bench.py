@@ -28,8 +28,9 @@ which stage 1's own time is put.
 
 ``--mode cpu-order`` measures the other entry point instead: each step also
 reproduces the CPU's own rounding past 2^53 (vqx_plane_stats_batch_cpu_order_ws:
-stage 1, stage 2, the prefix scan, the maps pass over the chunks past 2^53
-inside which adds can round, the walk), and the host concludes those sums.
+stage 1, the prefix scan, which also writes the exact sums, the maps pass
+over the chunks past 2^53 inside which adds can round, the chunk and block
+maps, the walk), and the host concludes those sums.
 Its roofline is the whole step against the bytes it must read (both planes
 once, and those chunks again), timed with HIP events around each group of
 steps; the gate is bit-identity with the oracle's sequential doubles on
@@ -593,7 +594,7 @@ def make_mode(args, vqx, L, hip, np, torch, dev, st, wl, ref_np, dist_np, planes
         m.ws_bytes = vqx.plane_stats_cpu_order_workspace_bytes(w, h, bpc, nframes)
         m.metric = METRIC_CPU_ORDER
         m.kernel = "cpu_order_step"
-        m.kernel_label = ("cpu_order_step (stage1_u16, stage2_combine, cpu_order_prefix, cpu_order_maps, "
+        m.kernel_label = ("cpu_order_step (stage1_u16, cpu_order_prefix, cpu_order_maps, cpu_order_compose, "
                           "cpu_order_walk)")
         m.sources = CPU_ORDER_SOURCES
         m.alg_bytes = wl.bytes_per_frame * nframes + past53_bytes(ref_np, dist_np, bpc)

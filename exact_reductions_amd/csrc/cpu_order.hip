@@ -28,7 +28,7 @@
 // rounded down, both of which, and the parity after the run, depend only
 // on the parity before it.  Such maps compose in order.
 //
-//  1. stage 1 + stage 2 (plane_stats.hip) give each chunk's exact totals;
+//  1. stage 1 (plane_stats.hip) gives each chunk's exact totals;
 //  2. cpu_order_prefix scans them per frame (the exact running sum at each
 //     chunk start, which predicts the binade the CPU's sum is in there),
 //     writes every sum the CPU gets exactly (all of them below 2^53), maps
@@ -473,8 +473,10 @@ __device__ __forceinline__ uint32_t *queue_counts(uint64_t *rec) { return reinte
 //  * The exact sum of each square over the chunks before chunk c (chunk 0's
 //    record also holds the frame's few samples outside whole vectors)
 //    predicts the CPU's sum there; totals[f*3 + kk] = the frame's exact sum.
-//  * The CPU's values of the sums that stay below 2^53 are the exact sums,
-//    written here; the first moments always do (below 2^25 * 2^16 = 2^41).
+//  * It writes the frame's five exact sums (so the CPU-order form needs no
+//    stage 2), and the CPU's values of the sums that stay below 2^53, which
+//    are the exact sums; the first moments always do (below 2^25 * 2^16 =
+//    2^41).
 //  * With `maps` (two-byte samples), each chunk whose exact range ends past
 //    2^53 gets its case: a chunk that starts past 2^53, is not predicted to
 //    change binade and whose terms are all multiples of 2^k (stage 1's low
@@ -520,8 +522,8 @@ __device__ __forceinline__ ChunkCase chunk_case(uint64_t p, uint64_t r, uint32_t
 }
 
 __global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int64_t pixels, int chunks,
-                                                             uint64_t *totals,
-                                                             uint64_t *out_cpu_noise,
+                                                             uint64_t *totals, uint64_t *out_noise,
+                                                             uint64_t *out_moments, uint64_t *out_cpu_noise,
                                                              uint64_t *out_cpu_moments, uint64_t *maps,
                                                              uint64_t *queue)
 {
@@ -548,6 +550,13 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int6
     for (int j = 0; j < kSums; ++j)
         run[j] = wave_inclusive_then_total(local[j], lds[j], total[j]) - local[j];
     if (t == 0) {
+        // the exact sums (stage 2's results), then the CPU's where they are
+        // the exact ones
+        out_noise[f] = total[kNoise];
+        out_moments[4 * f + 0] = total[kRef1];
+        out_moments[4 * f + 1] = total[kDist1];
+        out_moments[4 * f + 2] = total[kRef2];
+        out_moments[4 * f + 3] = total[kDist2];
 #pragma unroll
         for (int kk = 0; kk < kSquares; ++kk)
             totals[f * kSquares + kk] = total[record_field(kk)];
@@ -1391,14 +1400,15 @@ hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, cons
     uint64_t *cmaps = reinterpret_cast<uint64_t *>(ws + l.cmaps);
     uint64_t *bmaps = reinterpret_cast<uint64_t *>(ws + l.bmaps);
     // stage 1 with the low bits of the terms, at two-byte samples
-    hipError_t err = launch_plane_stats(g, ref, dist, out_noise, out_moments, rec, stream, nullptr, nullptr,
+    hipError_t err = launch_plane_stats(g, ref, dist, nullptr, nullptr, rec, stream, nullptr, nullptr,
                                         g.sample_bytes == 2);
     if (err != hipSuccess)
         return err;
     const unsigned nf = static_cast<unsigned>(g.nframes);
     const bool two_byte = g.sample_bytes == 2;  // one-byte sums never reach 2^53
-    cpu_order_prefix<<<dim3(nf), kThreads, 0, stream>>>(rec, g.pixels, g.chunks, totals, out_cpu_noise,
-                                                        out_cpu_moments, two_byte ? maps : nullptr, queue);
+    cpu_order_prefix<<<dim3(nf), kThreads, 0, stream>>>(rec, g.pixels, g.chunks, totals, out_noise, out_moments,
+                                                        out_cpu_noise, out_cpu_moments, two_byte ? maps : nullptr,
+                                                        queue);
     err = hipGetLastError();
     if (err != hipSuccess || !two_byte)
         return err;

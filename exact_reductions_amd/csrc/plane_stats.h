@@ -64,7 +64,8 @@ hipError_t launch_read_probe(const Geometry &g, const void *ref, const void *dis
                              hipStream_t stream, hipEvent_t begin, hipEvent_t end);
 
 // Queues both stages on `stream`, recording `stage1_begin`/`stage1_end` (if
-// not null) around stage 1.  Returns hipSuccess or the first error.
+// not null) around stage 1; with both outputs null, stage 1 only (the
+// caller combines the records).  Returns hipSuccess or the first error.
 hipError_t launch_plane_stats(const Geometry &g, const void *ref, const void *dist,
                               uint64_t *out_noise, uint64_t *out_moments, uint64_t *partials,
                               hipStream_t stream, hipEvent_t stage1_begin = nullptr,

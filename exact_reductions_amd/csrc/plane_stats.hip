@@ -254,7 +254,7 @@ hipError_t launch_plane_stats(const Geometry &g, const void *ref, const void *di
         stage1_u16<false><<<grid1, kThreads, 0, stream>>>(ref, dist, pixels, chunks, partials);
     }
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess)
+    if (err != hipSuccess || (!out_noise && !out_moments))
         return err;
     stage2_combine<<<dim3(static_cast<unsigned>(g.nframes)), kThreads, 0, stream>>>(
         partials, chunks, out_noise, out_moments);
