@@ -521,6 +521,10 @@ __device__ __forceinline__ ChunkCase chunk_case(uint64_t p, uint64_t r, uint32_t
     return x;
 }
 
+// Chunks of one frame at most: 2^25 two-byte samples hold at most 2^22
+// whole vectors, 2048 chunks.
+constexpr int kMaxFrameChunks = 2048;
+
 __global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int64_t pixels, int chunks,
                                                              uint64_t *totals, uint64_t *out_noise,
                                                              uint64_t *out_moments, uint64_t *out_cpu_noise,
@@ -530,6 +534,10 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int6
     constexpr int V = 8;
     __shared__ uint64_t lds[kSums + 1][kThreads / 64];
     __shared__ uint32_t base[kSquares];
+    // each chunk's square sums and low bits, kept from the one read of its
+    // record for the passes below (each thread uses only its own chunks)
+    __shared__ uint64_t sq[kSquares][kMaxFrameChunks];
+    __shared__ uint16_t low_bits[kMaxFrameChunks];
     const int64_t f = blockIdx.x;
     const int t = threadIdx.x;
     const int per = (chunks + kThreads - 1) / kThreads;
@@ -542,10 +550,19 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int6
 #pragma unroll
     for (int j = 0; j < kSums; ++j)
         local[j] = 0;
-    for (int c = c0; c < c1; ++c)
+    for (int c = c0; c < c1; ++c) {
+        uint64_t x[kSums + 1];
+#pragma unroll
+        for (int j = 0; j <= kSums; ++j)
+            x[j] = frec[c * kRecordStride + j];  // slot kSums is kLowBits
 #pragma unroll
         for (int j = 0; j < kSums; ++j)
-            local[j] += frec[c * kRecordStride + j];
+            local[j] += x[j];
+#pragma unroll
+        for (int kk = 0; kk < kSquares; ++kk)
+            sq[kk][c] = x[record_field(kk)];
+        low_bits[c] = static_cast<uint16_t>(x[kSums]);
+    }
 #pragma unroll
     for (int j = 0; j < kSums; ++j)
         run[j] = wave_inclusive_then_total(local[j], lds[j], total[j]) - local[j];
@@ -581,12 +598,12 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int6
         const int field = record_field(kk);
         uint64_t p = run[field];
         for (int c = c0; c < c1; ++c) {
-            const uint64_t *r = frec + c * kRecordStride;
-            const uint32_t low = static_cast<uint32_t>(r[kLowBits] >> (4 * kk)) & 15u;
-            const ChunkCase x = chunk_case(p, r[field], low, static_cast<int64_t>(c) * kChunkVectors < nvec);
+            const uint64_t T = sq[kk][c];
+            const uint32_t low = (static_cast<uint32_t>(low_bits[c]) >> (4 * kk)) & 15u;
+            const ChunkCase x = chunk_case(p, T, low, static_cast<int64_t>(c) * kChunkVectors < nvec);
             uint64_t *entry = maps + ((f * chunks + c) * kSquares + kk) * kEntry;
             if (x.chunk_only) {
-                const Map2 m = untied_map(r[field] >> (x.e - 52));
+                const Map2 m = untied_map(T >> (x.e - 52));
                 entry[kChunkMap + 0] = m.dm0;
                 entry[kChunkMap + 1] = m.dm1;
                 entry[kChunkMap + 2] = map_flags(m, x.e) | kChunkOnly;
@@ -594,7 +611,7 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int6
                 entry[kChunkMap + 2] = x.queued ? kQueued : 0;
                 nq += x.queued ? 1ull << (21 * kk) : 0;
             }
-            p += r[field];
+            p += T;
         }
     }
     // each queue's part for this frame, reserved in one add per sum
@@ -617,14 +634,14 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int6
         uint64_t p = run[field];
         int64_t slot = base[kk] + ((at >> (21 * kk)) & 0x1fffffu);
         for (int c = c0; c < c1; ++c) {
-            const uint64_t *r = frec + c * kRecordStride;
-            const uint32_t low = static_cast<uint32_t>(r[kLowBits] >> (4 * kk)) & 15u;
-            const ChunkCase x = chunk_case(p, r[field], low, static_cast<int64_t>(c) * kChunkVectors < nvec);
+            const uint64_t T = sq[kk][c];
+            const uint32_t low = (static_cast<uint32_t>(low_bits[c]) >> (4 * kk)) & 15u;
+            const ChunkCase x = chunk_case(p, T, low, static_cast<int64_t>(c) * kChunkVectors < nvec);
             if (x.queued)
                 queue[kk * cap + slot++] = static_cast<uint64_t>(f * chunks + c) |
                                            (static_cast<uint64_t>(x.e) << 32) |
                                            (static_cast<uint64_t>(x.dual) << 40);
-            p += r[field];
+            p += T;
         }
     }
 }
@@ -1406,6 +1423,8 @@ hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, cons
         return err;
     const unsigned nf = static_cast<unsigned>(g.nframes);
     const bool two_byte = g.sample_bytes == 2;  // one-byte sums never reach 2^53
+    if (g.chunks > kMaxFrameChunks)
+        return hipErrorInvalidValue;
     cpu_order_prefix<<<dim3(nf), kThreads, 0, stream>>>(rec, g.pixels, g.chunks, totals, out_noise, out_moments,
                                                         out_cpu_noise, out_cpu_moments, two_byte ? maps : nullptr,
                                                         queue);
