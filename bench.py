@@ -608,10 +608,17 @@ def make_mode(args, vqx, L, hip, np, torch, dev, st, wl, ref_np, dist_np, planes
         m.alg_bytes = wl.bytes_per_frame * nframes
     else:  # yuv420
         m.width = 3 * nframes
-        m.ws_bytes = max(vqx.plane_view_workspace_bytes(pw, ph, bpc, nframes) for _, pw, ph in planes)
+        m.ws_bytes = vqx.planes_workspace_bytes([(pw, ph) for _, pw, ph in planes], bpc, nframes)
+        # the three planes of each batch copy as views of its frames
+        fs = ref_np.shape[1]
+        m.plane_arrays = []
+        for r, d in bufs:
+            pairs = [(torch.as_strided(r, (nframes, ph, pw), (fs, pw, 1), off),
+                      torch.as_strided(d, (nframes, ph, pw), (fs, pw, 1), off)) for off, pw, ph in planes]
+            m.plane_arrays.append(vqx.plane_pairs(pairs, bpc)[0])
         m.metric = METRIC_YUV420
         m.kernel = "psnr_int_yuv420_step"
-        m.kernel_label = "psnr_int_yuv420_step (view_stage1 integer noise, view_combine; Y, U, V)"
+        m.kernel_label = "psnr_int_yuv420_step (views_stage1 integer noise, views_combine; Y, U, V in one launch each)"
         m.sources = VIEW_SOURCES
         m.alg_bytes = 2 * ref_np.shape[1] * wl.bytes_per_sample * nframes
     m.ws = torch.empty(m.ws_bytes, dtype=torch.uint8, device=dev)
@@ -716,13 +723,8 @@ def main(argv=None):
             rc = L.vqx_psnr_int_view_ws(r.data_ptr(), w, w * h, d.data_ptr(), w, w * h, w, h, bpc, nframes,
                                         o, ws.data_ptr(), ws_bytes, st)
         else:
-            fs = ref_np.shape[1]
-            rc = 0
-            for p, (off, pw, ph) in enumerate(planes):
-                rc = rc or L.vqx_psnr_int_view_ws(r.data_ptr() + off * wl.bytes_per_sample, pw, fs,
-                                                  d.data_ptr() + off * wl.bytes_per_sample, pw, fs, pw, ph, bpc,
-                                                  nframes, o + itemsize * p * nframes, ws.data_ptr(), ws_bytes,
-                                                  st)
+            rc = L.vqx_psnr_int_planes_ws(mode.plane_arrays[i % 2], len(planes), bpc, nframes, o, ws.data_ptr(),
+                                          ws_bytes, st)
         if rc != 0:
             raise vqx.VqxError(rc, f"libvqx entry point ({args.mode})")
 

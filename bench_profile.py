@@ -41,6 +41,7 @@ CPU_ORDER_SOURCES = STAGE1_SOURCES + [os.path.join(CSRC, "cpu_order.hip")]
 CPU_ORDER_KERNELS = ("stage1_u16", "cpu_order_prefix", "cpu_order_maps", "cpu_order_compose", "cpu_order_walk")
 VIEW_SOURCES = [os.path.join(CSRC, f) for f in ("plane_views.hip", "reduce.h")]
 VIEW_KERNELS = ("view_stage1", "view_combine")
+PLANES_KERNELS = ("views_stage1", "views_combine")
 HOST_SOURCES = STAGE1_SOURCES + [os.path.join(CSRC, "host_stream.hip")]
 COPY_MIB = 1024
 WARMUP = 300
@@ -68,7 +69,8 @@ def rows(path):
 
 def short(name: str) -> str:
     for k in ("stage1_u16", "stage1_u8", "stage2_combine", "bitwise_not", "cpu_order_prefix",
-              "cpu_order_maps", "cpu_order_compose", "cpu_order_walk", "view_stage1", "view_combine", "read_probe"):
+              "cpu_order_maps", "cpu_order_compose", "cpu_order_walk", "views_stage1", "views_combine",
+              "view_stage1", "view_combine", "read_probe"):
         if k in name:
             return k
     return name.split("(")[0][-60:]
@@ -180,7 +182,7 @@ def main(argv=None):
     elif args.mode == "psnr-int":
         kernel, step_kernels, sources = "psnr_int_step", VIEW_KERNELS, VIEW_SOURCES
     elif args.mode == "yuv420":
-        kernel, step_kernels, sources = "psnr_int_yuv420_step", VIEW_KERNELS, VIEW_SOURCES
+        kernel, step_kernels, sources = "psnr_int_yuv420_step", PLANES_KERNELS, VIEW_SOURCES
     elif args.mode == "host":
         kernel, step_kernels, sources = "host_step", ("stage1_u16", "stage2_combine"), HOST_SOURCES
     else:

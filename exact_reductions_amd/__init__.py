@@ -18,9 +18,12 @@ from .vqx import (  # noqa: F401
     plane_stats_batch_ws,
     plane_stats_host,
     plane_stats_host_workspace_bytes,
+    plane_stats_planes,
     plane_stats_view,
     plane_stats_workspace_bytes,
     plane_view_workspace_bytes,
+    planes_workspace_bytes,
+    psnr_int_planes,
     psnr_int_view,
     status_string,
 )

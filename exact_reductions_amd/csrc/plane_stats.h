@@ -106,6 +106,16 @@ hipError_t launch_view_stats(const ViewGeometry &g, const PlaneView &ref, const 
 hipError_t launch_view_psnr_int(const ViewGeometry &g, const PlaneView &ref, const PlaneView &dist,
                                 uint64_t *out_noise, uint64_t *partials, hipStream_t stream);
 
+// Several planes of the same frames (same bpc and nframes, each with its
+// own geometry, made by make_view_geometry) in one launch of each stage:
+// out_noise[p][f], out_moments[p][f][4]; the workspace holds every plane's
+// records, plane after plane.
+constexpr int kMaxViewPlanes = 4;
+hipError_t launch_planes_stats(const ViewGeometry *g, const PlaneView *ref, const PlaneView *dist, int nplanes,
+                               uint64_t *out_noise, uint64_t *out_moments, uint64_t *partials, hipStream_t stream);
+hipError_t launch_planes_psnr_int(const ViewGeometry *g, const PlaneView *ref, const PlaneView *dist, int nplanes,
+                                  uint64_t *out_noise, uint64_t *partials, hipStream_t stream);
+
 // Workspace of the host-fed form: two staging slots (ref and dist planes of
 // frames_per_upload frames each) and the stage-1 records of one sub-batch.
 struct HostStreamLayout {

@@ -263,6 +263,107 @@ __global__ __launch_bounds__(kThreads) void view_combine(const uint64_t *part, i
     combine_frame(part, tiles, blockIdx.x, out_noise, out_moments);
 }
 
+// ----------------------------------------------------------- several planes
+// Up to kMaxViewPlanes planes of the same frames in one launch of each
+// stage: the workgroups of plane p are [wg_begin[p], wg_begin[p+1]), frame
+// by frame, tile by tile, as in the one-plane launch; the combine takes one
+// workgroup per (plane, frame).  The descriptors travel as kernel
+// arguments; a plane is picked by selects, never by indexing into them.
+struct MultiViews {
+    PlaneView R[kMaxViewPlanes], D[kMaxViewPlanes];
+    int w[kMaxViewPlanes], h[kMaxViewPlanes];
+    int rows_per_tile[kMaxViewPlanes], seg[kMaxViewPlanes], segs[kMaxViewPlanes], tiles[kMaxViewPlanes];
+    int64_t wg_begin[kMaxViewPlanes + 1];
+    int nplanes;
+};
+
+// Plane p's value among four, selected as values (a select of the array
+// elements' addresses would make the compiler copy the descriptors to the
+// stack).
+template <class T>
+__device__ __forceinline__ T pick4(T a, T b, T c, T d, int p)
+{
+    return p == 0 ? a : p == 1 ? b : p == 2 ? c : d;
+}
+
+__device__ __forceinline__ PlaneView pick_view(const PlaneView (&v)[kMaxViewPlanes], int p)
+{
+    static_assert(kMaxViewPlanes == 4, "one select per plane");
+    PlaneView x;
+    x.base = pick4(v[0].base, v[1].base, v[2].base, v[3].base, p);
+    x.row_stride = pick4(v[0].row_stride, v[1].row_stride, v[2].row_stride, v[3].row_stride, p);
+    x.frame_stride = pick4(v[0].frame_stride, v[1].frame_stride, v[2].frame_stride, v[3].frame_stride, p);
+    return x;
+}
+
+#define VQX_PICK(arr, p) pick4((arr)[0], (arr)[1], (arr)[2], (arr)[3], (p))
+
+template <int kBytes, class Acc>
+__global__ __launch_bounds__(kThreads) void views_stage1(MultiViews M, uint64_t *part)
+{
+    const int64_t wg = blockIdx.x;
+    int p = 0;
+#pragma unroll
+    for (int q = 1; q < kMaxViewPlanes; ++q)
+        p += q < M.nplanes && wg >= M.wg_begin[q] ? 1 : 0;
+    const int64_t begin = VQX_PICK(M.wg_begin, p);
+    const int tiles = VQX_PICK(M.tiles, p);
+    const int64_t frame = (wg - begin) / tiles;
+    const int t = static_cast<int>(wg - begin - frame * tiles);
+    Acc acc;
+    accumulate_tile<kBytes>(acc, pick_view(M.R, p), pick_view(M.D, p), frame,
+                            tile_of(t, VQX_PICK(M.w, p), VQX_PICK(M.h, p), VQX_PICK(M.rows_per_tile, p),
+                                    VQX_PICK(M.seg, p), VQX_PICK(M.segs, p)));
+    finish(acc, wg, part);
+}
+
+__global__ __launch_bounds__(kThreads) void views_combine(MultiViews M, int nframes, const uint64_t *part,
+                                                          uint64_t *out_noise, uint64_t *out_moments)
+{
+    const int p = static_cast<int>(blockIdx.x / nframes);
+    const int64_t f = blockIdx.x - static_cast<int64_t>(p) * nframes;
+    const int64_t begin = VQX_PICK(M.wg_begin, p);
+    const int64_t at = static_cast<int64_t>(p) * nframes;
+    combine_frame(part + begin * kRecordStride, VQX_PICK(M.tiles, p), f, out_noise + at,
+                  out_moments ? out_moments + 4 * at : nullptr);
+}
+
+template <class Acc8T, class Acc16T>
+hipError_t launch_multi(const ViewGeometry *g, const PlaneView *ref, const PlaneView *dist, int nplanes,
+                        uint64_t *out_noise, uint64_t *out_moments, uint64_t *partials, hipStream_t stream)
+{
+    MultiViews M{};
+    M.nplanes = nplanes;
+    int64_t at = 0;
+    for (int p = 0; p < kMaxViewPlanes; ++p) {
+        M.wg_begin[p] = at;
+        if (p >= nplanes)
+            continue;
+        M.R[p] = ref[p];
+        M.D[p] = dist[p];
+        M.w[p] = g[p].w;
+        M.h[p] = g[p].h;
+        M.rows_per_tile[p] = g[p].rows_per_tile;
+        M.seg[p] = g[p].seg_samples;
+        M.segs[p] = g[p].segs_per_row;
+        M.tiles[p] = g[p].tiles;
+        at += g[p].workgroups;
+    }
+    M.wg_begin[kMaxViewPlanes] = at;
+    const dim3 grid(static_cast<unsigned>(at));
+    if (g[0].sample_bytes == 1)
+        views_stage1<1, Acc8T><<<grid, kThreads, 0, stream>>>(M, partials);
+    else
+        views_stage1<2, Acc16T><<<grid, kThreads, 0, stream>>>(M, partials);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    const int nframes = g[0].nframes;
+    views_combine<<<dim3(static_cast<unsigned>(nplanes * nframes)), kThreads, 0, stream>>>(M, nframes, partials,
+                                                                                          out_noise, out_moments);
+    return hipGetLastError();
+}
+
 template <class Acc8T, class Acc16T>
 hipError_t launch_views(const ViewGeometry &g, const PlaneView &ref, const PlaneView &dist, uint64_t *out_noise,
                         uint64_t *out_moments, uint64_t *partials, hipStream_t stream)
@@ -319,6 +420,18 @@ hipError_t launch_view_psnr_int(const ViewGeometry &g, const PlaneView &ref, con
                                 uint64_t *out_noise, uint64_t *partials, hipStream_t stream)
 {
     return launch_views<AccInt8, AccInt16>(g, ref, dist, out_noise, nullptr, partials, stream);
+}
+
+hipError_t launch_planes_stats(const ViewGeometry *g, const PlaneView *ref, const PlaneView *dist, int nplanes,
+                               uint64_t *out_noise, uint64_t *out_moments, uint64_t *partials, hipStream_t stream)
+{
+    return launch_multi<Acc8, Acc16>(g, ref, dist, nplanes, out_noise, out_moments, partials, stream);
+}
+
+hipError_t launch_planes_psnr_int(const ViewGeometry *g, const PlaneView *ref, const PlaneView *dist, int nplanes,
+                                  uint64_t *out_noise, uint64_t *partials, hipStream_t stream)
+{
+    return launch_multi<AccInt8, AccInt16>(g, ref, dist, nplanes, out_noise, nullptr, partials, stream);
 }
 
 }  // namespace vqx

@@ -134,6 +134,55 @@ double psnr_from_mse(double mse, int bpc, double psnr_max)
     return (psnr_max > 0.0 && db > psnr_max) ? psnr_max : db;
 }
 
+static_assert(VQX_MAX_PLANES == vqx::kMaxViewPlanes, "one plane limit");
+
+// Checks the planes and fills their geometries and views; `launch`: also
+// the pointers, strides and outputs of a call that queues work.
+int check_planes(const vqx_plane_pair *planes, int nplanes, int bpc, int nframes, bool launch,
+                 const uint64_t *out_noise, const uint64_t *out_moments, bool need_moments, vqx::ViewGeometry *g,
+                 vqx::PlaneView *R, vqx::PlaneView *D, size_t *ws_bytes)
+{
+    if (!planes || (launch && (!out_noise || (need_moments && !out_moments))))
+        return VQX_E_NULL;
+    if (nplanes < 1 || nplanes > VQX_MAX_PLANES)
+        return VQX_E_PLANES;
+    int64_t wgs = 0;
+    size_t bytes = 0;
+    for (int p = 0; p < nplanes; ++p) {
+        const vqx_plane_pair &P = planes[p];
+        if (launch && (!P.ref || !P.dist))
+            return VQX_E_NULL;
+        int rc = check_view_batch(P.w, P.h, bpc, nframes);
+        if (rc != VQX_OK)
+            return rc;
+        g[p] = vqx::make_view_geometry(P.w, P.h, bpc, nframes);
+        wgs += g[p].workgroups;
+        bytes += g[p].workspace_bytes;
+    }
+    if (wgs * vqx::kChunkThreads > static_cast<int64_t>(0xffffffffu))
+        return VQX_E_NFRAMES;
+    const int sb = bpc == 8 ? 1 : 2;
+    if (launch) {
+        for (int p = 0; p < nplanes; ++p) {
+            const vqx_plane_pair &P = planes[p];
+            if (!view_extent_ok(P.ref_row_stride, P.ref_frame_stride, P.w, P.h, nframes, sb) ||
+                !view_extent_ok(P.dist_row_stride, P.dist_frame_stride, P.w, P.h, nframes, sb))
+                return VQX_E_STRIDE;
+        }
+        for (int p = 0; p < nplanes; ++p)
+            if (!aligned(planes[p].ref, sb) || !aligned(planes[p].dist, sb))
+                return VQX_E_ALIGN;
+        if (!aligned(out_noise, 8) || (need_moments && !aligned(out_moments, 8)))
+            return VQX_E_ALIGN;
+        for (int p = 0; p < nplanes; ++p) {
+            R[p] = vqx::PlaneView{planes[p].ref, planes[p].ref_row_stride, planes[p].ref_frame_stride};
+            D[p] = vqx::PlaneView{planes[p].dist, planes[p].dist_row_stride, planes[p].dist_frame_stride};
+        }
+    }
+    *ws_bytes = bytes;
+    return VQX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -153,6 +202,7 @@ const char *vqx_status_string(int status)
     case VQX_E_HIP: return "the HIP runtime reported an error";
     case VQX_E_NO_DEVICE: return "no usable HIP device";
     case VQX_E_STRIDE: return "plane view: row stride below w, negative frame stride, or extent past 2^62 bytes";
+    case VQX_E_PLANES: return "nplanes outside 1..VQX_MAX_PLANES";
     default: return "unknown status";
     }
 }
@@ -449,6 +499,59 @@ int vqx_psnr_int_view_ws(const void *ref, int64_t ref_row_stride, int64_t ref_fr
     const vqx::PlaneView D{dist, dist_row_stride, dist_frame_stride};
     if (vqx::launch_view_psnr_int(g, R, D, out_noise, static_cast<uint64_t *>(workspace),
                                   static_cast<hipStream_t>(stream)) != hipSuccess) {
+        (void)hipGetLastError();
+        return VQX_E_HIP;
+    }
+    return VQX_OK;
+}
+
+// ---------------------------------------------------------- several planes
+int vqx_planes_workspace_bytes(const vqx_plane_pair *planes, int nplanes, int bpc, int nframes, size_t *bytes)
+{
+    if (!bytes)
+        return VQX_E_NULL;
+    vqx::ViewGeometry g[VQX_MAX_PLANES];
+    return check_planes(planes, nplanes, bpc, nframes, false, nullptr, nullptr, false, g, nullptr, nullptr, bytes);
+}
+
+int vqx_plane_stats_planes_ws(const vqx_plane_pair *planes, int nplanes, int bpc, int nframes, uint64_t *out_noise,
+                              uint64_t *out_moments, void *workspace, size_t workspace_bytes, void *stream)
+{
+    vqx::ViewGeometry g[VQX_MAX_PLANES];
+    vqx::PlaneView R[VQX_MAX_PLANES], D[VQX_MAX_PLANES];
+    size_t need = 0;
+    int rc = check_planes(planes, nplanes, bpc, nframes, true, out_noise, out_moments, true, g, R, D, &need);
+    if (rc != VQX_OK)
+        return rc;
+    if (!workspace || !aligned(workspace, 16) || workspace_bytes < need)
+        return VQX_E_WORKSPACE;
+    rc = device_ready();
+    if (rc != VQX_OK)
+        return rc;
+    if (vqx::launch_planes_stats(g, R, D, nplanes, out_noise, out_moments, static_cast<uint64_t *>(workspace),
+                                 static_cast<hipStream_t>(stream)) != hipSuccess) {
+        (void)hipGetLastError();
+        return VQX_E_HIP;
+    }
+    return VQX_OK;
+}
+
+int vqx_psnr_int_planes_ws(const vqx_plane_pair *planes, int nplanes, int bpc, int nframes, uint64_t *out_noise,
+                           void *workspace, size_t workspace_bytes, void *stream)
+{
+    vqx::ViewGeometry g[VQX_MAX_PLANES];
+    vqx::PlaneView R[VQX_MAX_PLANES], D[VQX_MAX_PLANES];
+    size_t need = 0;
+    int rc = check_planes(planes, nplanes, bpc, nframes, true, out_noise, nullptr, false, g, R, D, &need);
+    if (rc != VQX_OK)
+        return rc;
+    if (!workspace || !aligned(workspace, 16) || workspace_bytes < need)
+        return VQX_E_WORKSPACE;
+    rc = device_ready();
+    if (rc != VQX_OK)
+        return rc;
+    if (vqx::launch_planes_psnr_int(g, R, D, nplanes, out_noise, static_cast<uint64_t *>(workspace),
+                                    static_cast<hipStream_t>(stream)) != hipSuccess) {
         (void)hipGetLastError();
         return VQX_E_HIP;
     }

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libvqx.so")
 
 OK = 0
-E_NULL, E_DIMS, E_BPC, E_NFRAMES, E_ALIGN, E_WORKSPACE, E_HIP, E_NO_DEVICE, E_STRIDE = range(-1, -10, -1)
+E_NULL, E_DIMS, E_BPC, E_NFRAMES, E_ALIGN, E_WORKSPACE, E_HIP, E_NO_DEVICE, E_STRIDE, E_PLANES = range(-1, -11, -1)
 MAX_PIXELS = 1 << 25
 
 # Every symbol include/vqx.h declares.
@@ -41,6 +41,9 @@ SYMBOLS = (
     "vqx_conclude_psnr_int_batch",
     "vqx_plane_stats_host_workspace_bytes",
     "vqx_plane_stats_host_ws",
+    "vqx_planes_workspace_bytes",
+    "vqx_plane_stats_planes_ws",
+    "vqx_psnr_int_planes_ws",
 )
 
 
@@ -88,6 +91,9 @@ def lib() -> ctypes.CDLL:
             "vqx_conclude_psnr_int_batch": (i, [vp, i, i, i, i, d, vp]),
             "vqx_plane_stats_host_workspace_bytes": (i, [i, i, i, i, ctypes.POINTER(sz)]),
             "vqx_plane_stats_host_ws": (i, [vp, vp, i, i, i, i, i, vp, vp, vp, sz, vp, vp]),
+            "vqx_planes_workspace_bytes": (i, [vp, i, i, i, ctypes.POINTER(sz)]),
+            "vqx_plane_stats_planes_ws": (i, [vp, i, i, i, vp, vp, vp, sz, vp]),
+            "vqx_psnr_int_planes_ws": (i, [vp, i, i, i, vp, vp, sz, vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -324,6 +330,75 @@ def psnr_int_view(ref, dist, bpc: int, stream=None):
     _check(lib().vqx_psnr_int_view_ws(*args, w, h, bpc, f, out.data_ptr(), ws.data_ptr(), ws.numel(),
                                       _stream_handle(dev, stream)), "psnr_int_view_ws")
     return out
+
+
+MAX_PLANES = 4
+
+
+class PlanePair(ctypes.Structure):
+    """vqx_plane_pair: a ref view and a dist view of one plane, and its size."""
+    _fields_ = [("ref", ctypes.c_void_p), ("ref_row_stride", ctypes.c_int64), ("ref_frame_stride", ctypes.c_int64),
+                ("dist", ctypes.c_void_p), ("dist_row_stride", ctypes.c_int64),
+                ("dist_frame_stride", ctypes.c_int64), ("w", ctypes.c_int), ("h", ctypes.c_int)]
+
+
+def plane_pairs(pairs, bpc: int):
+    """A ctypes array of PlanePair from [(ref view, dist view), ...] tensor
+    views (each [F][h][w] or [h][w], any row and frame stride), the views kept
+    alive alongside; every plane must have the same number of frames."""
+    arr = (PlanePair * max(1, len(pairs)))()
+    keep, frames = [], set()
+    for k, (ref, dist) in enumerate(pairs):
+        ref, (rp, rr, rf, dp, dr, df) = _views(ref, dist, bpc)
+        f, h, w = ref.shape
+        frames.add(f)
+        keep.append((ref, dist))
+        arr[k] = PlanePair(rp, rr, rf, dp, dr, df, w, h)
+    if len(frames) > 1:
+        raise ValueError("every plane needs the same number of frames")
+    return arr, keep, (frames.pop() if frames else 0)
+
+
+def planes_workspace_bytes(sizes, bpc: int, nframes: int) -> int:
+    """Device scratch of the several-planes entry points for planes of
+    sizes [(w, h), ...]."""
+    arr = (PlanePair * max(1, len(sizes)))()
+    for k, (w, h) in enumerate(sizes):
+        arr[k].w, arr[k].h = w, h
+    out = ctypes.c_size_t(0)
+    _check(lib().vqx_planes_workspace_bytes(arr, len(sizes), bpc, nframes, ctypes.byref(out)),
+           "planes_workspace_bytes")
+    return out.value
+
+
+def plane_stats_planes(pairs, bpc: int, stream=None):
+    """The five exact sums of every plane of every frame, all planes in one
+    launch of each stage: ``(noise [P][F], moments [P][F][4])`` int64 device
+    tensors."""
+    import torch
+    arr, keep, f = plane_pairs(pairs, bpc)
+    n = len(pairs)
+    dev = keep[0][0].device if keep else torch.device("cuda")
+    out = torch.empty(5 * n * f, dtype=torch.int64, device=dev)
+    ws = torch.empty(planes_workspace_bytes([(a.w, a.h) for a in arr[:n]], bpc, f), dtype=torch.uint8, device=dev)
+    _check(lib().vqx_plane_stats_planes_ws(arr, n, bpc, f, out[:n * f].data_ptr(), out[n * f:].data_ptr(),
+                                           ws.data_ptr(), ws.numel(), _stream_handle(dev, stream)),
+           "plane_stats_planes_ws")
+    return out[:n * f].view(n, f), out[n * f:].view(n, f, 4)
+
+
+def psnr_int_planes(pairs, bpc: int, stream=None):
+    """The integer psnr noise of every plane of every frame, all planes in one
+    launch of each stage: int64 [P][F] device tensor."""
+    import torch
+    arr, keep, f = plane_pairs(pairs, bpc)
+    n = len(pairs)
+    dev = keep[0][0].device if keep else torch.device("cuda")
+    out = torch.empty(n * f, dtype=torch.int64, device=dev)
+    ws = torch.empty(planes_workspace_bytes([(a.w, a.h) for a in arr[:n]], bpc, f), dtype=torch.uint8, device=dev)
+    _check(lib().vqx_psnr_int_planes_ws(arr, n, bpc, f, out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                        _stream_handle(dev, stream)), "psnr_int_planes_ws")
+    return out.view(n, f)
 
 
 def conclude_psnr_int(noise: int, w: int, h: int, bpc: int, psnr_max: float = 0.0):

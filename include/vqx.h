@@ -63,8 +63,9 @@ enum vqx_status {
     VQX_E_WORKSPACE = -6, /* workspace smaller than vqx_plane_stats_workspace_bytes() */
     VQX_E_HIP = -7,       /* the HIP runtime reported an error (launch or allocation) */
     VQX_E_NO_DEVICE = -8, /* no usable HIP device */
-    VQX_E_STRIDE = -9     /* plane views: a row stride below w, a negative frame stride,
+    VQX_E_STRIDE = -9,    /* plane views: a row stride below w, a negative frame stride,
                              or a plane whose last sample lies past 2^62 bytes */
+    VQX_E_PLANES = -10    /* several planes: nplanes outside 1..VQX_MAX_PLANES */
 };
 
 /* VQX_ABI_VERSION of the loaded library. */
@@ -314,6 +315,45 @@ int vqx_psnr_int_view_ws(const void *ref, int64_t ref_row_stride, int64_t ref_fr
                          const void *dist, int64_t dist_row_stride, int64_t dist_frame_stride,
                          int w, int h, int bpc, int nframes, uint64_t *out_noise,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * ------------------------------------------------------------ several planes
+ * Up to VQX_MAX_PLANES planes of the same frames at once -- Y, U and V of
+ * planar frames, say -- each a pair of views as above with its own w and h;
+ * bpc and nframes are common.  All planes go through one launch of each
+ * stage, and the results are those of the one-plane entry points for each
+ * plane, laid out plane after plane:
+ *   out_noise    uint64[nplanes][nframes]
+ *   out_moments  uint64[nplanes][nframes][4]  (vqx_plane_stats_planes_ws)
+ * `planes` is a host array read during the call.  Errors as for the views,
+ * and VQX_E_PLANES; VQX_E_NFRAMES also when all planes' tiles together
+ * exceed (2^32-1)/256; the workspace is vqx_planes_workspace_bytes() (64
+ * bytes per plane, frame and tile).
+ */
+#define VQX_MAX_PLANES 4
+
+typedef struct vqx_plane_pair {
+    const void *ref;            /* device pointer: sample (0, 0) of frame 0 */
+    int64_t ref_row_stride;     /* samples */
+    int64_t ref_frame_stride;   /* samples */
+    const void *dist;
+    int64_t dist_row_stride;
+    int64_t dist_frame_stride;
+    int w, h;                   /* the plane's size in samples */
+} vqx_plane_pair;
+
+/* Device scratch for these planes (only their w and h are read).  Host-only. */
+int vqx_planes_workspace_bytes(const vqx_plane_pair *planes, int nplanes, int bpc, int nframes,
+                               size_t *bytes);
+
+/* The five sums of every plane of every frame. */
+int vqx_plane_stats_planes_ws(const vqx_plane_pair *planes, int nplanes, int bpc, int nframes,
+                              uint64_t *out_noise, uint64_t *out_moments, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* The integer psnr noise of every plane of every frame. */
+int vqx_psnr_int_planes_ws(const vqx_plane_pair *planes, int nplanes, int bpc, int nframes,
+                           uint64_t *out_noise, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * The integer psnr conclusion (host only), on the stored scale:

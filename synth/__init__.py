@@ -4,6 +4,7 @@ Holds random-number draws only; none of the reductions is computed here.
 """
 
 from .workloads import (  # noqa: F401
+    CHROMA,
     WORKLOADS,
     Workload,
     constant_pair,

@@ -46,9 +46,10 @@ def test_status_codes_match_header():
     text = _header_text()
     for name, value in (("VQX_OK", 0), ("VQX_E_NULL", -1), ("VQX_E_DIMS", -2), ("VQX_E_BPC", -3),
                         ("VQX_E_NFRAMES", -4), ("VQX_E_ALIGN", -5), ("VQX_E_WORKSPACE", -6),
-                        ("VQX_E_HIP", -7), ("VQX_E_NO_DEVICE", -8), ("VQX_E_STRIDE", -9)):
+                        ("VQX_E_HIP", -7), ("VQX_E_NO_DEVICE", -8), ("VQX_E_STRIDE", -9),
+                        ("VQX_E_PLANES", -10)):
         assert re.search(rf"\b{name} = {value}\b", text), name
-    for s in range(-9, 1):
+    for s in range(-10, 1):
         assert vqx.status_string(s) and vqx.status_string(s) != "unknown status"
     assert vqx.status_string(-99) == "unknown status"
 
@@ -438,3 +439,58 @@ def test_host_argument_errors(L):
     if not _has_gpu():
         assert f(h, h, 16, 4, 8, 5, 2, b.noise, b.moments, base, need, None, None) == vqx.E_NO_DEVICE
         assert b.untouched()
+
+
+def _pairs(b, sizes, rrs=None, off=0):
+    arr = (vqx.PlanePair * len(sizes))()
+    for k, (w, h) in enumerate(sizes):
+        arr[k] = vqx.PlanePair(b.ref + off, rrs or w, w * h, b.dist, w, w * h, w, h)
+    return arr
+
+
+def test_planes_workspace_and_errors(L):
+    """Several planes: the workspace is the sum of the planes' view
+    workspaces; argument errors are reported before anything is queued."""
+    sizes = [(1920, 1080), (960, 540), (960, 540)]
+    want = sum(vqx.plane_view_workspace_bytes(w, h, 10, 7) for w, h in sizes)
+    assert vqx.planes_workspace_bytes(sizes, 10, 7) == want
+    with pytest.raises(vqx.VqxError) as e:
+        vqx.planes_workspace_bytes([(4, 4)] * 5, 10, 1)
+    assert e.value.status == vqx.E_PLANES
+    with pytest.raises(vqx.VqxError) as e:
+        vqx.planes_workspace_bytes([], 10, 1)
+    assert e.value.status == vqx.E_PLANES
+    with pytest.raises(vqx.VqxError) as e:
+        vqx.planes_workspace_bytes([(4, 4), (0, 4)], 10, 1)
+    assert e.value.status == vqx.E_DIMS
+    # all planes' tiles share one dispatch: (2^32-1)/256 in all
+    top = (2**32 - 1) // 256
+    assert vqx.planes_workspace_bytes([(1, 1)], 16, top) > 0
+    with pytest.raises(vqx.VqxError) as e:
+        vqx.planes_workspace_bytes([(1, 1), (1, 1)], 16, top // 2 + 1)
+    assert e.value.status == vqx.E_NFRAMES
+
+    b = _Buffers()
+    ws = np.zeros(8192, dtype=np.uint8)
+    base = (ws.ctypes.data + 255) // 256 * 256
+    small = [(16, 4), (8, 2)]
+    need = vqx.planes_workspace_bytes(small, 10, 2)
+    f = L.vqx_psnr_int_planes_ws
+    g = L.vqx_plane_stats_planes_ws
+    ok = _pairs(b, small)
+    assert f(None, 2, 10, 2, b.noise, base, need, None) == vqx.E_NULL
+    assert f(ok, 2, 10, 2, None, base, need, None) == vqx.E_NULL
+    assert g(ok, 2, 10, 2, b.noise, None, base, need, None) == vqx.E_NULL
+    assert f(ok, 0, 10, 2, b.noise, base, need, None) == vqx.E_PLANES
+    assert f(ok, 5, 10, 2, b.noise, base, need, None) == vqx.E_PLANES
+    assert f(ok, 2, 7, 2, b.noise, base, need, None) == vqx.E_BPC
+    assert f(ok, 2, 10, 0, b.noise, base, need, None) == vqx.E_NFRAMES
+    assert f(_pairs(b, small, rrs=3), 2, 10, 2, b.noise, base, need, None) == vqx.E_STRIDE
+    assert f(_pairs(b, small, off=1), 2, 10, 2, b.noise, base, need, None) == vqx.E_ALIGN
+    assert f(ok, 2, 10, 2, b.noise + 4, base, need, None) == vqx.E_ALIGN
+    assert f(ok, 2, 10, 2, b.noise, base, need - 1, None) == vqx.E_WORKSPACE
+    assert g(ok, 2, 10, 2, b.noise, b.moments, base + 8, need, None) == vqx.E_WORKSPACE
+    nul = _pairs(b, small)
+    nul[1].dist = None
+    assert f(nul, 2, 10, 2, b.noise, base, need, None) == vqx.E_NULL
+    assert b.untouched() and np.all(ws == 0)

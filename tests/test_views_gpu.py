@@ -203,3 +203,113 @@ def test_outputs_written_not_accumulated():
         want = oracle.exact_frame_sums(ref[k], dist[k])
         assert [int(o[k])] + [int(v) for v in o[f + 4 * k:f + 4 * k + 4]] == list(want)
         assert int(o[5 * f + k]) == oracle.int_noise(ref[k], dist[k])
+
+
+# ------------------------------------------------------------ several planes
+def check_planes(pairs_np, pairs_dev, bpc, label=""):
+    """pairs_np: [(ref [F][h][w], dist)] numpy views of what pairs_dev select.
+    Both several-planes entry points against the oracle, plane by plane,
+    and against the one-plane entry points."""
+    noise, moments = vqx.plane_stats_planes(pairs_dev, bpc)
+    inoise = vqx.psnr_int_planes(pairs_dev, bpc)
+    torch.cuda.synchronize()
+    noise, moments, inoise = noise.cpu().numpy(), moments.cpu().numpy(), inoise.cpu().numpy()
+    for p, ((rn, dn), (rd, dd)) in enumerate(zip(pairs_np, pairs_dev)):
+        f = rn.shape[0]
+        for k in range(f):
+            r = np.ascontiguousarray(rn[k])
+            d = np.ascontiguousarray(dn[k])
+            want = oracle.exact_frame_sums(r, d)
+            got = [int(noise[p, k])] + [int(v) for v in moments[p, k]]
+            assert got == list(want), f"{label} plane {p} frame {k}: five sums"
+            assert int(inoise[p, k]) == oracle.int_noise(r, d), f"{label} plane {p} frame {k}: integer noise"
+        n1, m1 = vqx.plane_stats_view(rd, dd, bpc)
+        i1 = vqx.psnr_int_view(rd, dd, bpc)
+        torch.cuda.synchronize()
+        assert (n1.cpu().numpy() == noise[p]).all() and (m1.cpu().numpy() == moments[p]).all()
+        assert (i1.cpu().numpy() == inoise[p]).all()
+    return noise, moments, inoise
+
+
+@pytest.mark.parametrize("bpc", [8, 10, 16])
+@pytest.mark.parametrize("chroma", ["420", "422", "444"])
+def test_planes_of_planar_yuv(bpc, chroma):
+    """Y, U and V of planar frames in one call of each entry point."""
+    w, h, f = 1920, 1080, 3
+    sx, sy = synth.CHROMA[chroma]
+    cw, ch = -(-w // sx), -(-h // sy)
+    sizes = [w * h, cw * ch, cw * ch]
+    frame = sum(sizes)
+    rng = np.random.default_rng(bpc * 7 + sx * 3 + sy)
+    buf_r = _rand(rng, (f, frame), bpc)
+    buf_d = np.clip(buf_r.astype(np.int64) + rng.integers(-300, 300, size=buf_r.shape, endpoint=True), 0,
+                    (1 << bpc) - 1).astype(_dtype(bpc))
+    R = torch.from_numpy(buf_r).cuda()
+    D = torch.from_numpy(buf_d).cuda()
+    off, pairs_np, pairs_dev = 0, [], []
+    for pw, ph, size in ((w, h, sizes[0]), (cw, ch, sizes[1]), (cw, ch, sizes[2])):
+        pairs_dev.append((torch.as_strided(R, (f, ph, pw), (frame, pw, 1), off),
+                          torch.as_strided(D, (f, ph, pw), (frame, pw, 1), off)))
+        pairs_np.append(tuple(np.lib.stride_tricks.as_strided(
+            b.reshape(-1)[off:], (f, ph, pw), (frame * b.itemsize, pw * b.itemsize, b.itemsize))
+            for b in (buf_r, buf_d)))
+        off += size
+    check_planes(pairs_np, pairs_dev, bpc, f"{chroma} {bpc}-bit")
+
+
+def test_planes_of_mixed_shapes():
+    """Four planes of unlike shapes and layouts: a pitched region, a row
+    longer than a tile, a 1x1 plane, and a plane whose ref and dist sit at
+    different offsets within 16 bytes."""
+    rng = np.random.default_rng(77)
+    f = 2
+    big_r = _rand(rng, (f, 300, 1100), 16)
+    big_d = _rand(rng, (f, 300, 1100), 16)
+    long_r = _rand(rng, (f, 2, 20000), 16)
+    long_d = _rand(rng, (f, 2, 20000), 16)
+    one_r = _rand(rng, (f, 1, 1), 16)
+    one_d = _rand(rng, (f, 1, 1), 16)
+    odd_r = _rand(rng, (f, 40, 70), 16)
+    odd_d = _rand(rng, (f, 40, 73), 16)
+    regions = [
+        ((big_r, big_d), (slice(None), slice(5, 290), slice(3, 1003))),
+        ((long_r, long_d), (slice(None), slice(None), slice(1, 19999))),
+        ((one_r, one_d), (slice(None), slice(None), slice(None))),
+    ]
+    pairs_np, pairs_dev = [], []
+    for (r, d), sl in regions:
+        pairs_np.append((r[sl], d[sl]))
+        pairs_dev.append((torch.from_numpy(r).cuda()[sl], torch.from_numpy(d).cuda()[sl]))
+    pairs_np.append((odd_r, odd_d[:, :, 3:]))
+    pairs_dev.append((torch.from_numpy(odd_r).cuda(), torch.from_numpy(odd_d).cuda()[:, :, 3:]))
+    check_planes(pairs_np, pairs_dev, 16, "mixed")
+
+
+def test_one_plane_and_outputs_written():
+    """One plane through the several-planes form equals the view form, and
+    the outputs are written, not added to (pre-filled outputs and workspace,
+    two calls in a row)."""
+    rng = np.random.default_rng(5)
+    ref = _rand(rng, (3, 50, 70), 12)
+    dist = _rand(rng, (3, 50, 70), 12)
+    R, D = torch.from_numpy(ref).cuda(), torch.from_numpy(dist).cuda()
+    check_planes([(ref, dist)], [(R, D)], 12, "one plane")
+    arr, keep, f = vqx.plane_pairs([(R, D), (R[:, ::2, :], D[:, ::2, :])], 12)
+    need = vqx.planes_workspace_bytes([(70, 50), (70, 25)], 12, 3)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    out = torch.full((2 * 3 + 2 * 3 * 5,), -1, dtype=torch.int64, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    L = vqx.lib()
+    for _ in range(2):
+        assert L.vqx_psnr_int_planes_ws(arr, 2, 12, 3, out[:6].data_ptr(), ws.data_ptr(), need, st) == 0
+        assert L.vqx_plane_stats_planes_ws(arr, 2, 12, 3, out[6:12].data_ptr(), out[12:].data_ptr(), ws.data_ptr(),
+                                           need, st) == 0
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    for p, (r, d) in enumerate(((ref, dist), (ref[:, ::2, :], dist[:, ::2, :]))):
+        for k in range(3):
+            rk, dk = np.ascontiguousarray(r[k]), np.ascontiguousarray(d[k])
+            assert int(o[3 * p + k]) == oracle.int_noise(rk, dk)
+            want = oracle.exact_frame_sums(rk, dk)
+            assert int(o[6 + 3 * p + k]) == want[0]
+            assert [int(v) for v in o[12 + 4 * (3 * p + k):12 + 4 * (3 * p + k) + 4]] == list(want[1:])
