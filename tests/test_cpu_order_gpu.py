@@ -153,3 +153,45 @@ def test_ties_past53():
 def test_small_frames_equal_exact():
     ref, dist = synth.uniform_planes(18, 22, 50, 16, seed=3, container_max=True)
     check(ref, dist, 16, expect_past53=False)
+
+
+def _check_outputs(ref, dist, bpc, out, f):
+    o1 = oracle.seq_batch_sums(ref, dist, bpc)
+    o2 = oracle.exact_batch_sums(ref, dist)
+    s = 1 << (bpc - 8)
+    o = out.cpu().numpy()
+    for k in range(f):
+        exact = [int(o[0, k])] + [int(v) for v in o[0, f + 4 * k:f + 4 * k + 4]]
+        cpu = [int(o[1, k])] + [int(v) for v in o[1, f + 4 * k:f + 4 * k + 4]]
+        assert exact == [int(v) for v in o2[k]], f"frame {k}: exact sums"
+        for j in range(5):
+            assert cpu[j] == int(float(o1[k][j]) * float(s ** UNIT_POWER[j])), f"frame {k} output {j}"
+
+
+def test_reused_workspace_and_side_stream():
+    """One workspace, filled with 0xFF first, serves batches of different
+    content, depth and size in turn on a non-default stream: nothing a call
+    reads is left over from an earlier call (the queue lengths, chunk
+    cases and maps are all written afresh), and outputs are written, not
+    added to."""
+    mixed = synth.past53_mixed(nframes=2)
+    odd = synth.odd_dark_bright(w=2560, h=1440, nframes=2)
+    small8 = synth.uniform_planes(333, 77, 4, 8, seed=8)
+    batches = [(mixed, 16), (odd, 16), (small8, 8), (mixed, 16)]
+    need = max(vqx.plane_stats_cpu_order_workspace_bytes(r.shape[2], r.shape[1], b, r.shape[0])
+               for (r, _), b in batches)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda:0")
+    side = torch.cuda.Stream()
+    L = vqx.lib()
+    for (ref, dist), bpc in batches:
+        f, h, w = ref.shape
+        r = torch.from_numpy(ref).cuda()
+        d = torch.from_numpy(dist).cuda()
+        out = torch.full((2, 5 * f), -1, dtype=torch.int64, device="cuda:0")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            assert L.vqx_plane_stats_batch_cpu_order_ws(
+                r.data_ptr(), d.data_ptr(), w, h, bpc, f, out[0, :f].data_ptr(), out[0, f:].data_ptr(),
+                out[1, :f].data_ptr(), out[1, f:].data_ptr(), ws.data_ptr(), need, side.cuda_stream) == 0
+        side.synchronize()
+        _check_outputs(ref, dist, bpc, out, f)
