@@ -18,7 +18,10 @@ kernel is the whole CPU-order step (``cpu_order_step``): the trace lists
 each of its kernels, and the traffic sums their counters per step.  This
 script never touches the GPU itself.
 
-    python bench_profile.py --workload 5 [--mode cpu-order] --out gpurun_out/profiles
+    python bench_profile.py --workload 5 [--mode cpu-order] --out <summaries> --work <work>
+
+The raw rocprofv3 output goes under ``--work``; the summaries record their
+commands with that directory written as ``<work>``.
 """
 
 from __future__ import annotations
@@ -60,6 +63,18 @@ def find(pattern_dir, suffix):
     if not hits:
         raise FileNotFoundError(f"no *{suffix} under {pattern_dir}")
     return hits[-1]
+
+
+def shown(cmd, args) -> str:
+    """A command as the summaries record it: repository paths relative, the
+    raw-output directory as <work>."""
+    text = " ".join(shlex.quote(c) for c in cmd)
+    work = os.path.abspath(args.work)
+    text = text.replace(work, "<work>")
+    rel = os.path.relpath(work, ROOT)
+    if not rel.startswith(".."):
+        text = text.replace(rel, "<work>")
+    return text.replace(ROOT + "/", "")
 
 
 def rows(path):
@@ -132,7 +147,7 @@ def profile_host(args, wl, wname, bench, src_sha):
     lines = [
         f"# rocprofv3 kernel and memory-copy trace: host-fed step, {wl.name} ({wname}), "
         f"{args.frames_per_upload} frames per upload",
-        f"command: cd <repo> && {' '.join(shlex.quote(c) for c in cmd).replace(ROOT + '/', '')}",
+        f"command: cd <repo> && {shown(cmd, args)}",
         f"date_utc: {time.strftime('%Y-%m-%dT%H:%M:%SZ', time.gmtime())}",
         f"kernel_source_sha256: {src_sha}",
         "",
@@ -162,8 +177,8 @@ def profile_host(args, wl, wname, bench, src_sha):
 def main(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--workload", type=int, default=None)
-    p.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "profiles"))
-    p.add_argument("--work", default=os.path.join(ROOT, "gpurun_out", "rocprof"))
+    p.add_argument("--out", default=os.path.join(ROOT, "_prof", "summaries"))
+    p.add_argument("--work", default=os.path.join(ROOT, "_prof", "rocprof"))
     p.add_argument("--cache", default="/tmp/vqx_inputs")
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--frames-per-upload", type=int, default=4)
@@ -230,7 +245,7 @@ def main(argv=None):
         bench_line = [ln for ln in f.read().splitlines() if ln.startswith("{")]
     lines = [
         f"# rocprofv3 kernel trace: {kernel}, {wl.name} ({wname})",
-        f"command: cd <repo> && {' '.join(shlex.quote(c) for c in trace_cmd).replace(ROOT + '/', '')}",
+        f"command: cd <repo> && {shown(trace_cmd, args)}",
         f"date_utc: {time.strftime('%Y-%m-%dT%H:%M:%SZ', time.gmtime())}",
         f"kernel_source_sha256: {src_sha}",
         "",
@@ -293,8 +308,8 @@ def main(argv=None):
     out = [
         f"# HBM traffic of {kernel}, {wl.name} ({wname}), from rocprofv3 counters"
         + (f" (summed over {', '.join(step_kernels)} per step)" if len(step_kernels) > 1 else ""),
-        f"command_fetch: cd <repo> && {' '.join(shlex.quote(c) for c in cmds['FETCH_SIZE']).replace(ROOT + '/', '')}",
-        f"command_write: cd <repo> && {' '.join(shlex.quote(c) for c in cmds['WRITE_SIZE']).replace(ROOT + '/', '')}",
+        f"command_fetch: cd <repo> && {shown(cmds['FETCH_SIZE'], args)}",
+        f"command_write: cd <repo> && {shown(cmds['WRITE_SIZE'], args)}",
         f"date_utc: {time.strftime('%Y-%m-%dT%H:%M:%SZ', time.gmtime())}",
         f"kernel_source_sha256: {src_sha}",
         f"copy_kernel_bytes_read_and_written: {copy_bytes}",
