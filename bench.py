@@ -5,10 +5,16 @@ One step = one batch through the whole path: the fused streaming kernel
 (stage 1), the exact per-frame combine (stage 2), which writes the frames'
 five sums (40 bytes each) straight into pinned host memory, and the host
 conclusions (MSE, PSNR and the four moments) in libvqx.  Steps run on one
-stream in groups of eight: each group ends with one completion event, and the
-host concludes a group's batches while the GPU runs the next group (an
-event record costs a few microseconds of command-processor time between
-kernels, so there is one per group, not per step).  Stage 1 of every step is
+stream by default; ``--streams N`` alternates them over N streams (step i on
+stream i % N, each with its own workspace), as a pipeline of batches would,
+and then consecutive steps overlap and a kernel's timed duration includes the
+overlap.
+Steps go in groups of eight: a group starts on every stream after one start
+event, ends when every stream has finished its steps of the group, and ends
+with one completion event; the host concludes a group's batches while the GPU
+runs the next group (an event record costs a few microseconds of
+command-processor time between kernels, so there is one per group, not per
+step).  Stage 1 of every step is
 timed with HIP events that its own dispatch stamps (hipExtLaunchKernel).  Inputs are resident in HBM before the
 timed region; two copies of the batch alternate so that the 256 MB Infinity
 Cache cannot serve a repeat.
@@ -94,6 +100,10 @@ def parse_args(argv=None):
                         "psnr-int: the integer psnr twin; yuv420: the integer psnr twin on the Y, U and V "
                         "planes of planar 4:2:0 frames; host: the exact sums of a batch in pinned host "
                         "memory, uploads overlapped with the reduction")
+    p.add_argument("--streams", type=int, default=1,
+                   help="streams the steps alternate over (step i on stream i %% N, each with its own "
+                        "workspace): with more than one, consecutive steps overlap as in a pipeline of "
+                        "batches, and a kernel's timed duration includes the overlap")
     p.add_argument("--frames-per-upload", type=int, default=4,
                    help="host mode: frames per upload")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -675,6 +685,10 @@ def main(argv=None):
     nslots = depth * group
     stream = torch.cuda.current_stream(dev)
     st = stream.cuda_stream
+    # every stream at the default priority
+    side = [torch.cuda.Stream(device=dev) for _ in range(max(1, args.streams) - 1)]
+    sts = [st] + [x.cuda_stream for x in side]
+    nst = len(sts)
     hip = HipEvents(vqx.hip_runtime())
     L = vqx.lib()
     mode = make_mode(args, vqx, L, hip, np, torch, dev, st, wl, ref_np, dist_np, planes, bufs)
@@ -683,6 +697,7 @@ def main(argv=None):
     sums_dev = [hip.device_pointer(sums[s].data_ptr()) for s in range(nslots)]
     sums_np = sums.numpy()
     ws, ws_bytes = mode.ws, mode.ws_bytes
+    wss = [ws] + [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(nst - 1)]
     total = args.warmup + args.steps
     # exact mode: stage 1 of every step stamps its own events; other modes:
     # events around each group of steps
@@ -691,6 +706,7 @@ def main(argv=None):
     ngroups = (total + group - 1) // group + 1
     ev_start = [hip.create() for _ in range(ngroups)] if not mode.per_step_events else []
     ev_done = [hip.create() for _ in range(ngroups)]
+    ev_join = [hip.create() for _ in range(nst)]  # the other streams' ends of a group
     torch.cuda.synchronize()
 
     # The host conclusion allocates nothing: libvqx concludes from the pinned
@@ -711,6 +727,8 @@ def main(argv=None):
         s = i % nslots
         r, d = bufs[i % 2]
         o = sums_dev[s]
+        st = sts[i % nst]
+        ws = wss[i % nst]
         if args.mode == "exact":
             rc = L.vqx_plane_stats_batch_ws_timed(r.data_ptr(), d.data_ptr(), w, h, bpc, nframes,
                                                   o, o + itemsize * nframes, ws.data_ptr(), ws_bytes,
@@ -755,10 +773,17 @@ def main(argv=None):
         for steps in groups:
             if len(pending) == depth:
                 conclude(*pending.pop(0))
+            # a group starts on every stream after the start event and ends
+            # when every stream has finished its steps of the group
             if not mode.per_step_events:
                 hip.record(ev_start[steps[0] // group], st)
+                for k in range(1, nst):
+                    hip.wait(sts[k], ev_start[steps[0] // group])
             for i in steps:
                 enqueue(i)
+            for k in range(1, nst):
+                hip.record(ev_join[k], sts[k])
+                hip.wait(st, ev_join[k])
             done = ev_done[steps[0] // group]
             hip.record(done, st)
             pending.append((steps, done))
@@ -788,7 +813,7 @@ def main(argv=None):
             g = a // group
             n = min(group, total - a)
             step_ms += [hip.elapsed_ms(ev_start[g], ev_done[g]) / n] * n
-    for ev in list(ev_begin.values()) + list(ev_end.values()) + ev_start + ev_done:
+    for ev in list(ev_begin.values()) + list(ev_end.values()) + ev_start + ev_done + ev_join:
         hip.destroy(ev)
 
     # every step must have produced the same sums
@@ -840,6 +865,7 @@ def main(argv=None):
                         + (", as planar 4:2:0 frames (Y, U, V each drawn with the recipe at its size)"
                            if args.mode == "yuv420" else ""),
             "w": w, "h": h, "bpc": bpc, "nframes": nframes, "mode": args.mode,
+            "streams": nst,
             "bytes_per_step": bytes_per_step,
             "hbm_gbs_whole_step": round(bytes_per_step * args.steps / elapsed / 1e9, 1),
         },
