@@ -20,6 +20,7 @@ from .vqx import (  # noqa: F401
     plane_stats_host_workspace_bytes,
     plane_stats_planes,
     plane_stats_view,
+    plane_stats_view_cpu_order,
     plane_stats_workspace_bytes,
     plane_view_workspace_bytes,
     planes_workspace_bytes,

@@ -106,6 +106,11 @@ hipError_t launch_view_stats(const ViewGeometry &g, const PlaneView &ref, const 
 hipError_t launch_view_psnr_int(const ViewGeometry &g, const PlaneView &ref, const PlaneView &dist,
                                 uint64_t *out_noise, uint64_t *partials, hipStream_t stream);
 
+// Copies a view's samples into a contiguous [nframes][h][w] array at `dst`
+// (uint8 at 8 bits, else uint16).
+hipError_t launch_gather_view(const PlaneView &view, int w, int h, int bpc, int nframes, void *dst,
+                              hipStream_t stream);
+
 // Several planes of the same frames (same bpc and nframes, each with its
 // own geometry, made by make_view_geometry) in one launch of each stage:
 // out_noise[p][f], out_moments[p][f][4]; the workspace holds every plane's

@@ -20,6 +20,8 @@
 // taken one by one); otherwise the tile is read sample by sample.  Integer
 // sums make the tiling irrelevant to the result.
 
+#include <type_traits>
+
 #include "plane_stats.h"
 #include "reduce.h"
 #include "terms.h"
@@ -364,6 +366,48 @@ hipError_t launch_multi(const ViewGeometry *g, const PlaneView *ref, const Plane
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ gather
+// Copies a view's samples into a contiguous [nframes][h][w] array: one
+// workgroup per (frame, row) pair in turn, a grid of at most kGatherWgs
+// workgroups.  Where the row's source and destination start at the same
+// offset within 16 bytes, its whole 16-byte vectors are copied as vectors
+// (consecutive threads, consecutive vectors) and the few samples before the
+// first and after the last one by one; otherwise sample by sample.
+constexpr int64_t kGatherWgs = 65536;
+
+template <int kBytes>
+__global__ __launch_bounds__(kThreads) void gather_view(PlaneView P, int w, int h, int64_t rows, void *dst)
+{
+    using T = typename std::conditional<kBytes == 1, uint8_t, uint16_t>::type;
+    constexpr int V = 16 / kBytes;
+    const int t = threadIdx.x;
+    for (int64_t fr = blockIdx.x; fr < rows; fr += gridDim.x) {
+        const int64_t f = fr / h;
+        const int64_t y = fr - f * h;
+        const T *src = static_cast<const T *>(P.base) + f * P.frame_stride + y * P.row_stride;
+        T *out = static_cast<T *>(dst) + fr * w;
+        const int ps = static_cast<int>(reinterpret_cast<uintptr_t>(src) & 15);
+        const int pd = static_cast<int>(reinterpret_cast<uintptr_t>(out) & 15);
+        if (ps != pd) {
+            for (int x = t; x < w; x += kThreads)
+                out[x] = src[x];
+            continue;
+        }
+        int head = ((16 - ps) & 15) / kBytes;
+        head = head < w ? head : w;
+        const int nvec = (w - head) / V;
+        const int tail_begin = head + nvec * V;
+        if (t < head)
+            out[t] = src[t];
+        if (t < w - tail_begin)
+            out[tail_begin + t] = src[tail_begin + t];
+        const u32x4 *vs = reinterpret_cast<const u32x4 *>(src + head);
+        u32x4 *vd = reinterpret_cast<u32x4 *>(out + head);
+        for (int v = t; v < nvec; v += kThreads)
+            vd[v] = __builtin_nontemporal_load(vs + v);
+    }
+}
+
 template <class Acc8T, class Acc16T>
 hipError_t launch_views(const ViewGeometry &g, const PlaneView &ref, const PlaneView &dist, uint64_t *out_noise,
                         uint64_t *out_moments, uint64_t *partials, hipStream_t stream)
@@ -420,6 +464,18 @@ hipError_t launch_view_psnr_int(const ViewGeometry &g, const PlaneView &ref, con
                                 uint64_t *out_noise, uint64_t *partials, hipStream_t stream)
 {
     return launch_views<AccInt8, AccInt16>(g, ref, dist, out_noise, nullptr, partials, stream);
+}
+
+hipError_t launch_gather_view(const PlaneView &view, int w, int h, int bpc, int nframes, void *dst,
+                              hipStream_t stream)
+{
+    const int64_t rows = static_cast<int64_t>(nframes) * h;
+    const dim3 grid(static_cast<unsigned>(rows < kGatherWgs ? rows : kGatherWgs));
+    if (bpc == 8)
+        gather_view<1><<<grid, kThreads, 0, stream>>>(view, w, h, rows, dst);
+    else
+        gather_view<2><<<grid, kThreads, 0, stream>>>(view, w, h, rows, dst);
+    return hipGetLastError();
 }
 
 hipError_t launch_planes_stats(const ViewGeometry *g, const PlaneView *ref, const PlaneView *dist, int nplanes,

@@ -183,6 +183,24 @@ int check_planes(const vqx_plane_pair *planes, int nplanes, int bpc, int nframes
     return VQX_OK;
 }
 
+// The CPU-order form over plane views: both views gathered into contiguous
+// planes after the contiguous form's workspace, then that form.
+struct ViewCpuOrderLayout {
+    size_t ref, dist, bytes;
+};
+
+ViewCpuOrderLayout view_cpu_order_layout(int w, int h, int bpc, int nframes)
+{
+    auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+    const vqx::Geometry g = vqx::make_geometry(w, h, bpc, nframes);
+    const size_t plane = static_cast<size_t>(g.pixels) * g.sample_bytes * nframes;
+    ViewCpuOrderLayout l{};
+    l.ref = up(vqx::cpu_order_layout(g).bytes);
+    l.dist = up(l.ref + plane);
+    l.bytes = up(l.dist + plane);
+    return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -336,6 +354,58 @@ int vqx_plane_stats_batch_cpu_order_ws(const void *ref, const void *dist, int w,
     hipError_t err = vqx::launch_plane_stats_cpu_order(g, ref, dist, out_noise, out_moments,
                                                        out_cpu_noise, out_cpu_moments, workspace,
                                                        static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) {
+        (void)hipGetLastError();
+        return VQX_E_HIP;
+    }
+    return VQX_OK;
+}
+
+int vqx_plane_stats_view_cpu_order_workspace_bytes(int w, int h, int bpc, int nframes, size_t *bytes)
+{
+    if (!bytes)
+        return VQX_E_NULL;
+    int rc = check_batch(w, h, bpc, nframes);
+    if (rc != VQX_OK)
+        return rc;
+    *bytes = view_cpu_order_layout(w, h, bpc, nframes).bytes;
+    return VQX_OK;
+}
+
+int vqx_plane_stats_view_cpu_order_ws(const void *ref, int64_t ref_row_stride, int64_t ref_frame_stride,
+                                      const void *dist, int64_t dist_row_stride, int64_t dist_frame_stride, int w,
+                                      int h, int bpc, int nframes, uint64_t *out_noise, uint64_t *out_moments,
+                                      uint64_t *out_cpu_noise, uint64_t *out_cpu_moments, void *workspace,
+                                      size_t workspace_bytes, void *stream)
+{
+    int rc = check_view_args(ref, ref_row_stride, ref_frame_stride, dist, dist_row_stride, dist_frame_stride, w, h,
+                             bpc, nframes, out_noise, out_moments, true);
+    if (rc != VQX_OK)
+        return rc;
+    rc = check_batch(w, h, bpc, nframes);
+    if (rc != VQX_OK)
+        return rc;
+    if (!out_cpu_noise || !out_cpu_moments)
+        return VQX_E_NULL;
+    if (!aligned(out_cpu_noise, 8) || !aligned(out_cpu_moments, 8))
+        return VQX_E_ALIGN;
+    const ViewCpuOrderLayout l = view_cpu_order_layout(w, h, bpc, nframes);
+    if (!workspace || !aligned(workspace, 16) || workspace_bytes < l.bytes)
+        return VQX_E_WORKSPACE;
+    rc = device_ready();
+    if (rc != VQX_OK)
+        return rc;
+    char *ws = static_cast<char *>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const vqx::Geometry g = vqx::make_geometry(w, h, bpc, nframes);
+    hipError_t err = vqx::launch_gather_view(vqx::PlaneView{ref, ref_row_stride, ref_frame_stride}, w, h, bpc,
+                                             nframes, ws + l.ref, s);
+    if (err == hipSuccess)
+        err = vqx::launch_gather_view(vqx::PlaneView{dist, dist_row_stride, dist_frame_stride}, w, h, bpc, nframes,
+                                      ws + l.dist, s);
+    if (err == hipSuccess)
+        err = vqx::launch_plane_stats_cpu_order(g, ws + l.ref, ws + l.dist, out_noise, out_moments, out_cpu_noise,
+                                                out_cpu_moments, workspace, s);
     if (err != hipSuccess) {
         (void)hipGetLastError();
         return VQX_E_HIP;

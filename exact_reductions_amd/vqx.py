@@ -41,6 +41,8 @@ SYMBOLS = (
     "vqx_conclude_psnr_int_batch",
     "vqx_plane_stats_host_workspace_bytes",
     "vqx_plane_stats_host_ws",
+    "vqx_plane_stats_view_cpu_order_workspace_bytes",
+    "vqx_plane_stats_view_cpu_order_ws",
     "vqx_planes_workspace_bytes",
     "vqx_plane_stats_planes_ws",
     "vqx_psnr_int_planes_ws",
@@ -91,6 +93,9 @@ def lib() -> ctypes.CDLL:
             "vqx_conclude_psnr_int_batch": (i, [vp, i, i, i, i, d, vp]),
             "vqx_plane_stats_host_workspace_bytes": (i, [i, i, i, i, ctypes.POINTER(sz)]),
             "vqx_plane_stats_host_ws": (i, [vp, vp, i, i, i, i, i, vp, vp, vp, sz, vp, vp]),
+            "vqx_plane_stats_view_cpu_order_workspace_bytes": (i, [i, i, i, i, ctypes.POINTER(sz)]),
+            "vqx_plane_stats_view_cpu_order_ws": (i, [vp, i64, i64, vp, i64, i64, i, i, i, i, vp, vp, vp, vp, vp,
+                                                      sz, vp]),
             "vqx_planes_workspace_bytes": (i, [vp, i, i, i, ctypes.POINTER(sz)]),
             "vqx_plane_stats_planes_ws": (i, [vp, i, i, i, vp, vp, vp, sz, vp]),
             "vqx_psnr_int_planes_ws": (i, [vp, i, i, i, vp, vp, sz, vp]),
@@ -330,6 +335,30 @@ def psnr_int_view(ref, dist, bpc: int, stream=None):
     _check(lib().vqx_psnr_int_view_ws(*args, w, h, bpc, f, out.data_ptr(), ws.data_ptr(), ws.numel(),
                                       _stream_handle(dev, stream)), "psnr_int_view_ws")
     return out
+
+
+def plane_stats_view_cpu_order_workspace_bytes(w: int, h: int, bpc: int, nframes: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().vqx_plane_stats_view_cpu_order_workspace_bytes(w, h, bpc, nframes, ctypes.byref(out)),
+           "plane_stats_view_cpu_order_workspace_bytes")
+    return out.value
+
+
+def plane_stats_view_cpu_order(ref, dist, bpc: int, stream=None):
+    """plane_stats_batch_cpu_order over plane views (any row and frame
+    stride): ``(noise [F], moments [F][4], cpu_noise [F], cpu_moments
+    [F][4])`` as int64 device tensors."""
+    import torch
+    ref, args = _views(ref, dist, bpc)
+    f, h, w = ref.shape
+    dev = ref.device
+    out = torch.empty((2, 5 * f), dtype=torch.int64, device=dev)
+    ws = torch.empty(plane_stats_view_cpu_order_workspace_bytes(w, h, bpc, f), dtype=torch.uint8, device=dev)
+    _check(lib().vqx_plane_stats_view_cpu_order_ws(*args, w, h, bpc, f, out[0, :f].data_ptr(), out[0, f:].data_ptr(),
+                                                   out[1, :f].data_ptr(), out[1, f:].data_ptr(), ws.data_ptr(),
+                                                   ws.numel(), _stream_handle(dev, stream)),
+           "plane_stats_view_cpu_order_ws")
+    return out[0, :f], out[0, f:].view(f, 4), out[1, :f], out[1, f:].view(f, 4)
 
 
 MAX_PLANES = 4

@@ -317,6 +317,26 @@ int vqx_psnr_int_view_ws(const void *ref, int64_t ref_row_stride, int64_t ref_fr
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The CPU-order form (vqx_plane_stats_batch_cpu_order_ws) over plane views:
+ * the exact sums and the CPU's running double sums, bit for bit past 2^53
+ * too, of views with any row and frame stride -- the CPU adds a view's
+ * samples in raster order, row after row, whatever the pitch [PSNR,
+ * Context; MOMENT, Context].  Both views are first copied into contiguous
+ * planes inside the workspace (about twice the contiguous form's time), then
+ * reduced as the contiguous form does.  Errors as for the views and the
+ * contiguous CPU-order form; the workspace is
+ * vqx_plane_stats_view_cpu_order_workspace_bytes() (the contiguous form's
+ * and both planes of the batch).
+ */
+int vqx_plane_stats_view_cpu_order_workspace_bytes(int w, int h, int bpc, int nframes, size_t *bytes);
+int vqx_plane_stats_view_cpu_order_ws(const void *ref, int64_t ref_row_stride, int64_t ref_frame_stride,
+                                      const void *dist, int64_t dist_row_stride,
+                                      int64_t dist_frame_stride, int w, int h, int bpc, int nframes,
+                                      uint64_t *out_noise, uint64_t *out_moments,
+                                      uint64_t *out_cpu_noise, uint64_t *out_cpu_moments,
+                                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * ------------------------------------------------------------ several planes
  * Up to VQX_MAX_PLANES planes of the same frames at once -- Y, U and V of
  * planar frames, say -- each a pair of views as above with its own w and h;

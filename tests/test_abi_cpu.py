@@ -494,3 +494,28 @@ def test_planes_workspace_and_errors(L):
     nul[1].dist = None
     assert f(nul, 2, 10, 2, b.noise, base, need, None) == vqx.E_NULL
     assert b.untouched() and np.all(ws == 0)
+
+
+def test_view_cpu_order_workspace_and_errors(L):
+    """The CPU-order form over views: its workspace holds the contiguous
+    form's and both planes of the batch; argument errors are reported before
+    anything is queued."""
+    need = vqx.plane_stats_view_cpu_order_workspace_bytes(3840, 2160, 16, 2)
+    assert need >= vqx.plane_stats_cpu_order_workspace_bytes(3840, 2160, 16, 2) + 2 * 3840 * 2160 * 2 * 2
+    b = _Buffers()
+    ws = np.zeros(16384, dtype=np.uint8)
+    base = (ws.ctypes.data + 255) // 256 * 256
+    need = vqx.plane_stats_view_cpu_order_workspace_bytes(16, 4, 10, 2)
+    f = L.vqx_plane_stats_view_cpu_order_ws
+    args = lambda **kw: [kw.get("ref", b.ref), kw.get("rrs", 16), kw.get("rfs", 64), kw.get("dist", b.dist),
+                         kw.get("drs", 16), kw.get("dfs", 64), 16, 4, kw.get("bpc", 10), 2, kw.get("noise", b.noise),
+                         b.moments, kw.get("cn", b.noise), b.moments, base, kw.get("ws", need), None]
+    assert f(*args(ref=None)) == vqx.E_NULL
+    assert f(*args(cn=None)) == vqx.E_NULL
+    assert f(*args(bpc=17)) == vqx.E_BPC
+    assert f(*args(rrs=15)) == vqx.E_STRIDE
+    assert f(*args(dfs=-1)) == vqx.E_STRIDE
+    assert f(*args(dist=b.dist + 1)) == vqx.E_ALIGN
+    assert f(*args(cn=b.noise + 4)) == vqx.E_ALIGN
+    assert f(*args(ws=need - 1)) == vqx.E_WORKSPACE
+    assert b.untouched() and np.all(ws == 0)

@@ -195,3 +195,47 @@ def test_reused_workspace_and_side_stream():
                 out[1, :f].data_ptr(), out[1, f:].data_ptr(), ws.data_ptr(), need, side.cuda_stream) == 0
         side.synchronize()
         _check_outputs(ref, dist, bpc, out, f)
+
+
+def _view_case(ref_np, dist_np, R, D, bpc):
+    """The view form against the sequential oracle on the selected samples,
+    and against the contiguous form."""
+    n, m, cn, cm = vqx.plane_stats_view_cpu_order(R, D, bpc)
+    torch.cuda.synchronize()
+    f = ref_np.shape[0]
+    out = torch.stack([torch.cat([n, m.reshape(-1)]), torch.cat([cn, cm.reshape(-1)])])
+    ref_c, dist_c = np.ascontiguousarray(ref_np), np.ascontiguousarray(dist_np)
+    _check_outputs(ref_c, dist_c, bpc, out, f)
+    n2, m2, cn2, cm2 = run(ref_c, dist_c, bpc)
+    assert (n.cpu().numpy() == n2).all() and (cn.cpu().numpy() == cn2).all()
+    assert (m.cpu().numpy() == m2).all() and (cm.cpu().numpy() == cm2).all()
+
+
+def test_view_form_pitched_region_past53():
+    """A 2560x1440 region of padded 16-bit planes whose sums pass 2^53."""
+    ref, dist = synth.past53_mixed(nframes=2)
+    f, h, w = ref.shape
+    big_r = np.zeros((f, h + 3, w + 70), dtype=np.uint16)
+    big_d = np.zeros_like(big_r)
+    big_r[:, 2:2 + h, 5:5 + w] = ref
+    big_d[:, 2:2 + h, 5:5 + w] = dist
+    sl = (slice(None), slice(2, 2 + h), slice(5, 5 + w))
+    R, D = torch.from_numpy(big_r).cuda()[sl], torch.from_numpy(big_d).cuda()[sl]
+    _view_case(big_r[sl], big_d[sl], R, D, 16)
+
+
+@pytest.mark.parametrize("bpc", [8, 12, 16])
+def test_view_form_odd_layouts(bpc):
+    """Odd pitches, ref and dist at different offsets, frame stride 0."""
+    rng = np.random.default_rng(bpc)
+    hi = 255 if bpc == 8 else 65535
+    dt = np.uint8 if bpc == 8 else np.uint16
+    big_r = rng.integers(0, hi, size=(3, 41, 101), endpoint=True).astype(dt)
+    big_d = rng.integers(0, hi, size=(3, 43, 97), endpoint=True).astype(dt)
+    R = torch.from_numpy(big_r).cuda()[:, 1:40, 3:90]
+    D = torch.from_numpy(big_d).cuda()[:, 2:41, 0:87]
+    _view_case(big_r[:, 1:40, 3:90], big_d[:, 2:41, 0:87], R, D, bpc)
+    one_r = torch.from_numpy(big_r[:1]).cuda().expand(4, 41, 101)
+    one_d = torch.from_numpy(big_d[:1, :41, :97]).cuda().expand(4, 41, 97)[:, :, :97]
+    _view_case(np.broadcast_to(big_r[:1, :, :97], (4, 41, 97)), np.broadcast_to(big_d[:1, :41, :97], (4, 41, 97)),
+               one_r[:, :, :97], one_d, bpc)
