@@ -240,36 +240,6 @@ __device__ __forceinline__ uint64_t wave_scan64(uint64_t v)
     return scan_step64<0x143, 0xc>(v);
 }
 
-__device__ __forceinline__ uint32_t wave_scan32(uint32_t v)
-{
-    v += from_below<0x111, 0xf>(0u, v);
-    v += from_below<0x112, 0xf>(0u, v);
-    v += from_below<0x114, 0xf>(0u, v);
-    v += from_below<0x118, 0xf>(0u, v);
-    v += from_below<0x142, 0xa>(0u, v);
-    return v + from_below<0x143, 0xc>(0u, v);
-}
-
-template <int CTRL, int ROWS>
-__device__ __forceinline__ RunMap run_scan_step(const RunMap &m)
-{
-    RunMap o;
-    o.C = from_below<CTRL, ROWS>(0u, m.C);
-    o.P = from_below<CTRL, ROWS>(0x10000u, m.P);  // the identity map
-    return run_then(o, m);
-}
-
-// Lane j gets the composite of the maps of lanes 0..j.
-__device__ __forceinline__ RunMap wave_scan_run(RunMap m)
-{
-    m = run_scan_step<0x111, 0xf>(m);
-    m = run_scan_step<0x112, 0xf>(m);
-    m = run_scan_step<0x114, 0xf>(m);
-    m = run_scan_step<0x118, 0xf>(m);
-    m = run_scan_step<0x142, 0xa>(m);
-    return run_scan_step<0x143, 0xc>(m);
-}
-
 // ---------------------------------------------------------- maps (64-bit)
 // The same two-state map with its increases of m written out: from parity
 // s, m grows by dm_s and ends with parity p_s.
@@ -921,88 +891,151 @@ __global__ __launch_bounds__(kThreads) void cpu_order_maps(const void *ref, cons
 }
 
 // ------------------------------------------------------------------ 4. walk
-// All 64 lanes of the walking wave hold the same S throughout.
+// All 64 lanes of the walking wave hold the same S throughout.  At every
+// level (the chunks of a block, the slabs of a chunk, groups of 4 vectors of
+// a slab, the terms of one group) the walk takes a row of up to 64 items,
+// item j in lane j, each with its exact total and its maps for up to two
+// binades, and moves S over them with wave scans.
 
-// Term by term through the vector that lane j holds.
-template <int KK>
-__device__ __forceinline__ uint64_t walk_vector(uint64_t S, const u32x4 &a, const u32x4 &b, int j)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t from_below64(uint64_t identity, uint64_t v)
 {
-    u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
-    if constexpr (KK != kSqDist) {
-        x.x = lane_value(a.x, j);
-        x.y = lane_value(a.y, j);
-        x.z = lane_value(a.z, j);
-        x.w = lane_value(a.w, j);
-    }
-    if constexpr (KK != kSqRef) {
-        y.x = lane_value(b.x, j);
-        y.y = lane_value(b.y, j);
-        y.z = lane_value(b.z, j);
-        y.w = lane_value(b.w, j);
-    }
-#pragma unroll
-    for (int i = 0; i < kTerms; ++i)
-        S = cpu_add(S, vector_term<KK>(x, y, i));
-    return S;
+    return static_cast<uint64_t>(from_below<CTRL, ROWS>(static_cast<uint32_t>(identity), static_cast<uint32_t>(v))) |
+           (static_cast<uint64_t>(
+                from_below<CTRL, ROWS>(static_cast<uint32_t>(identity >> 32), static_cast<uint32_t>(v >> 32)))
+            << 32);
 }
 
-// One row of 64 vectors, vector j in lane j (zero terms past the end, n of
-// them real), each lane with its vector's exact total and maps for binades
-// eA and eA + 1.  Repeatedly: if the rest of the row keeps S below 2^53, or
-// inside its binade, it is added or mapped at once; otherwise prefix scans
-// find the vector in which S crosses 2^53 or leaves its binade, S is moved
-// to just before it, and that one vector is walked term by term.
-template <int KK>
-__device__ __forceinline__ uint64_t walk_row(uint64_t S, const u32x4 &a, const u32x4 &b, int n, uint64_t tot,
-                                             const RunMap &mA, uint32_t rA, const RunMap &mB, uint32_t rB, int eA)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ Map2 map_scan_step(const Map2 &m)
 {
-    const int lane = threadIdx.x;
-    int from = 0;  // vectors before `from` are done
+    Map2 o;  // the identity where there is no source
+    o.dm0 = from_below64<CTRL, ROWS>(0, m.dm0);
+    o.dm1 = from_below64<CTRL, ROWS>(0, m.dm1);
+    o.p0 = from_below<CTRL, ROWS>(0u, m.p0);
+    o.p1 = from_below<CTRL, ROWS>(1u, m.p1);
+    return map_then(o, m);
+}
+
+// Lane j gets the composite of the maps of lanes 0..j, in lane order.
+__device__ __forceinline__ Map2 wave_scan_map(Map2 m)
+{
+    m = map_scan_step<0x111, 0xf>(m);
+    m = map_scan_step<0x112, 0xf>(m);
+    m = map_scan_step<0x114, 0xf>(m);
+    m = map_scan_step<0x118, 0xf>(m);
+    m = map_scan_step<0x142, 0xa>(m);
+    return map_scan_step<0x143, 0xc>(m);
+}
+
+// x if c, else y (field by field, so that nothing goes through a stack copy).
+__device__ __forceinline__ Map2 select_map(bool c, const Map2 &x, const Map2 &y)
+{
+    Map2 m;
+    m.dm0 = c ? x.dm0 : y.dm0;
+    m.dm1 = c ? x.dm1 : y.dm1;
+    m.p0 = c ? x.p0 : y.p0;
+    m.p1 = c ? x.p1 : y.p1;
+    return m;
+}
+
+// One item of a row: its exact total, and its maps for the binades in the
+// flags fa and fb (flags 0: no map); `none`: an item that adds nothing
+// (the identity in any binade).
+struct Item {
+    uint64_t T = 0;
+    Map2 a, b;
+    uint64_t fa = 0, fb = 0;
+    bool none = false;
+};
+
+// Moves S over items 0..n-1 of the row (n <= 64).  Repeatedly: below 2^53,
+// prefix sums of the totals find the item in which S gets there (every add
+// before it is exact); past it, prefix compositions of each item's map for
+// S's binade find the first item without one, or in which S leaves the
+// binade (m only grows, so if it ends inside the binade it stayed there).
+// S is moved to just before that item, which `one(S, j)` walks at a finer
+// level.
+template <class One>
+__device__ __forceinline__ uint64_t walk_items(uint64_t S, const Item &it, int n, One one)
+{
+    const int lane = threadIdx.x & 63;
+    int from = 0;  // items before `from` are done
     while (from < n) {
-        const bool act = lane >= from;
-        const uint64_t t = act ? tot : 0;
-        const uint64_t incl = wave_scan64(t);
-        const uint64_t rest = lane_value64(incl, 63);
-        if (S + rest < kTwo53)
-            return S + rest;
-        int jx;  // the vector in which the sum crosses 2^53 or leaves its binade
+        const bool act = lane >= from && lane < n;
+        int jx;
         if (S < kTwo53) {
+            const uint64_t t = act ? it.T : 0;
+            const uint64_t incl = wave_scan64(t);
+            const uint64_t rest = lane_value64(incl, 63);
+            if (S + rest < kTwo53)
+                return S + rest;
             jx = __builtin_ctzll(__ballot(act && S + incl >= kTwo53));
-            S += lane_value64(incl - t, jx);  // exact: every add before it stays below 2^53
+            S += lane_value64(incl - t, jx);
         } else {
             const int e = binade(S);
-            if (e != eA && e != eA + 1) {  // no maps for this binade
-                for (int j = from; j < n; ++j)
-                    S = walk_vector<KK>(S, a, b, j);
-                return S;
-            }
-            const bool inA = e == eA;
             const int k = e - 52;
-            const RunMap pre = wave_scan_run(act ? (inA ? mA : mB) : RunMap{});
-            const uint32_t rin = wave_scan32(act ? (inA ? rA : rB) : 0u);
-            const uint64_t terms = act ? static_cast<uint64_t>(lane - from + 1) * kTerms : 0;
-            const Map2 pm = run_map(pre, incl, terms, rin, k);
+            const bool use_a = (it.fa & 1u) && flags_binade(it.fa) == e;
+            const bool use_b = !use_a && (it.fb & 1u) && flags_binade(it.fb) == e;
+            const bool ok = it.none || use_a || use_b;
+            const Map2 pm = wave_scan_map(act && !it.none && ok ? select_map(use_a, it.a, it.b) : Map2{});
             const uint64_t mm = S >> k;
-            const uint64_t m2 = mm + pick(mm, pm.dm0, pm.dm1);  // m after vectors from..lane
-            const uint64_t leaves = __ballot(act && m2 >= kTwo53);
-            if (!leaves)
+            const uint64_t m2 = mm + pick(mm, pm.dm0, pm.dm1);  // m after items from..lane
+            const uint64_t bad = __ballot(act && (!ok || m2 >= kTwo53));
+            if (!bad)
                 return lane_value64(m2, 63) << k;
-            jx = __builtin_ctzll(leaves);
+            jx = __builtin_ctzll(bad);
             if (jx > from)
                 S = lane_value64(m2, jx - 1) << k;
         }
-        S = walk_vector<KK>(S, a, b, jx);
+        S = one(S, jx);
         from = jx + 1;
     }
     return S;
 }
 
-// Vectors [sb, se) (at most 256), read at once, one row of 64 at a time
-// with maps made here for S's binade and the next.
-template <int KK>
-__device__ __forceinline__ uint64_t walk_slab(uint64_t S, const u32x4 *R, const u32x4 *D, int64_t sb, int64_t se)
+// The map of one term t in binade 2^(k+52): m grows by h, less one on a tie
+// (t + 2^(k-1) a multiple of 2^k) when m + h is odd; after a tie m is even.
+__device__ __forceinline__ Map2 term_map(uint32_t t, int k)
 {
-    const int lane = threadIdx.x;
+    const uint32_t t2 = t + (1u << (k - 1));
+    const uint64_t h = t2 >> k;
+    const bool tie = (t2 & ((1u << k) - 1)) == 0;
+    const uint32_t hb = static_cast<uint32_t>(h) & 1u;
+    Map2 m;
+    m.dm0 = h - (tie && hb ? 1 : 0);       // from parity 0, m + h has h's parity
+    m.dm1 = h - (tie && !hb ? 1 : 0);      // from parity 1, the other one
+    m.p0 = tie ? 0u : hb;
+    m.p1 = tie ? 0u : hb ^ 1u;
+    return m;
+}
+
+// Term i (raster order) of the 32 that lane group g holds in LDS after
+// `consecutive` (vectors 4g .. 4g + 3).
+template <int KK>
+__device__ __forceinline__ uint32_t lds_term(const u32x4 *lds, int g, int i)
+{
+    const u32x4 zero = {0, 0, 0, 0};
+    const u32x4 a = KK != kSqDist ? lds[kLaneVectors * g + (i >> 3)] : zero;
+    const u32x4 b = KK != kSqRef ? lds[kSlabVectors + kLaneVectors * g + (i >> 3)] : zero;
+    const int w = (i >> 1) & 3;
+    const uint32_t wa = w == 0 ? a.x : w == 1 ? a.y : w == 2 ? a.z : a.w;
+    const uint32_t wb = w == 0 ? b.x : w == 1 ? b.y : w == 2 ? b.z : b.w;
+    const uint32_t r = (i & 1) ? wa >> 16 : wa & 0xffffu;
+    const uint32_t d = (i & 1) ? wb >> 16 : wb & 0xffffu;
+    return square_term<2>(KK, r, d);
+}
+
+// Vectors [sb, se) (at most 256) from S, with maps made here for S's binade
+// and the next (a slab's total is far below S past 2^53, so S crosses at
+// most one binade in it).  The slab goes through LDS so that lane g holds
+// vectors 4g .. 4g + 3, 32 consecutive terms: one row of 64 groups, and
+// inside the group where S crosses, one row of its 32 terms.
+template <int KK>
+__device__ __forceinline__ uint64_t walk_slab(uint64_t S, const u32x4 *R, const u32x4 *D, int64_t sb, int64_t se,
+                                              u32x4 *lds)
+{
+    const int lane = threadIdx.x & 63;
     const int eA = S >= kTwo53 ? binade(S) : 53;
     const int kA = eA - 52;
     u32x4 a[kLaneVectors], b[kLaneVectors];
@@ -1010,72 +1043,68 @@ __device__ __forceinline__ uint64_t walk_slab(uint64_t S, const u32x4 *R, const 
     for (int j = 0; j < kLaneVectors; ++j) {
         const int64_t v = sb + 64 * j + lane;
         load_vector<KK>(R, D, v, v < se, sb, a[j], b[j]);
+        keep_if<KK>(v < se, a[j], b[j]);
     }
+    consecutive<KK>(a, b, lds);
+    Item g;
+    RunMap mA, mB;
+    uint32_t rA = 0, rB = 0;
 #pragma unroll
-    for (int j = 0; j < kLaneVectors; ++j) {
-        const int64_t base = sb + 64 * j;
-        if (base >= se)
-            break;
-        keep_if<KK>(base + lane < se, a[j], b[j]);
-        RunMap mA, mB;
-        uint32_t rA = 0, rB = 0;
-        uint64_t tot = 0;
+    for (int j = 0; j < kLaneVectors; ++j)
 #pragma unroll
         for (int i = 0; i < kTerms; ++i) {
             const uint32_t t = vector_term<KK>(a[j], b[j], i);
-            tot += t;
+            g.T += t;
             run_add(mA, rA, t, kA);
             run_add(mB, rB, t, kA + 1);
         }
-        const int n = se - base < 64 ? static_cast<int>(se - base) : 64;
-        S = walk_row<KK>(S, a[j], b[j], n, tot, mA, rA, mB, rB, eA);
-    }
-    return S;
+    constexpr uint64_t n = kLaneVectors * kTerms;
+    g.a = run_map(mA, g.T, n, rA, kA);
+    g.b = run_map(mB, g.T, n, rB, kA + 1);
+    g.fa = map_flags(g.a, eA);
+    g.fb = map_flags(g.b, eA + 1);
+    return walk_items(S, g, 64, [&](uint64_t S1, int grp) {
+        // the 32 terms of group grp, term i in lane i
+        const int e1 = S1 >= kTwo53 ? binade(S1) : 53;
+        const uint32_t t = lane < kLaneVectors * kTerms ? lds_term<KK>(lds, grp, lane) : 0u;
+        Item x;
+        x.T = t;
+        x.a = term_map(t, e1 - 52);
+        x.b = term_map(t, e1 - 51);
+        x.fa = map_flags(x.a, e1);
+        x.fb = map_flags(x.b, e1 + 1);
+        return walk_items(S1, x, kLaneVectors * kTerms,
+                          [&](uint64_t S2, int i) { return cpu_add(S2, lane_value(t, i)); });
+    });
 }
 
-// One chunk, slab by slab with the slabs' stored maps.
+// One chunk, from its slab maps; a slab where they do not apply is walked
+// with maps made on the spot.
 template <int KK>
-__device__ __forceinline__ uint64_t walk_chunk(uint64_t S, const u32x4 *R, const u32x4 *D, const uint64_t *entry, int64_t cb,
-                               int64_t ce)
+__device__ __forceinline__ uint64_t walk_chunk(uint64_t S, const u32x4 *R, const u32x4 *D, const uint64_t *entry,
+                                               int64_t cb, int64_t ce, u32x4 *lds)
 {
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     if (entry[kChunkMap + 2] & kChunkOnly) {
         // no slab maps (S is not where the chunk map expects it): map each
         // slab on the spot
         for (int64_t sb = cb; sb < ce; sb += kSlabVectors)
-            S = walk_slab<KK>(S, R, D, sb, sb + kSlabVectors < ce ? sb + kSlabVectors : ce);
+            S = walk_slab<KK>(S, R, D, sb, sb + kSlabVectors < ce ? sb + kSlabVectors : ce, lds);
         return S;
     }
-    uint64_t T = 0, dm0 = 0, dm1 = 0, flags = 0, bdm0 = 0, bdm1 = 0, bflags = 0;
-    if (lane < kSlabs) {
-        T = entry[kSlabTotals + lane];
-        dm0 = entry[kSlabMapsA + 3 * lane + 0];
-        dm1 = entry[kSlabMapsA + 3 * lane + 1];
-        flags = entry[kSlabMapsA + 3 * lane + 2];
-        bdm0 = entry[kSlabMapsB + 3 * lane + 0];
-        bdm1 = entry[kSlabMapsB + 3 * lane + 1];
-        bflags = entry[kSlabMapsB + 3 * lane + 2];
+    const int n = static_cast<int>((ce - cb + kSlabVectors - 1) / kSlabVectors);  // slabs holding vectors
+    Item it;
+    if (lane < n) {
+        it.T = entry[kSlabTotals + lane];
+        it.fa = entry[kSlabMapsA + 3 * lane + 2];
+        it.a = map_from(entry[kSlabMapsA + 3 * lane + 0], entry[kSlabMapsA + 3 * lane + 1], it.fa);
+        it.fb = entry[kSlabMapsB + 3 * lane + 2];
+        it.b = map_from(entry[kSlabMapsB + 3 * lane + 0], entry[kSlabMapsB + 3 * lane + 1], it.fb);
     }
-    for (int j = 0; j < kSlabs; ++j) {
+    return walk_items(S, it, n, [&](uint64_t S1, int j) {
         const int64_t sb = cb + static_cast<int64_t>(j) * kSlabVectors;
-        if (sb >= ce)
-            break;
-        const int64_t se = sb + kSlabVectors < ce ? sb + kSlabVectors : ce;
-        const uint64_t fl = lane_value64(flags, j);
-        const uint64_t Tj = lane_value64(T, j);
-        if ((fl & 1u) && S + Tj < kTwo53) {  // totals are only stored with a map
-            S += Tj;
-            continue;
-        }
-        if ((fl & 1u) && map_apply(S, map_from(lane_value64(dm0, j), lane_value64(dm1, j), fl), flags_binade(fl)))
-            continue;
-        const uint64_t bfl = lane_value64(bflags, j);
-        if ((bfl & 1u) &&
-            map_apply(S, map_from(lane_value64(bdm0, j), lane_value64(bdm1, j), bfl), flags_binade(bfl)))
-            continue;
-        S = walk_slab<KK>(S, R, D, sb, se);
-    }
-    return S;
+        return walk_slab<KK>(S1, R, D, sb, sb + kSlabVectors < ce ? sb + kSlabVectors : ce, lds);
+    });
 }
 
 // ---------------------------------------------------- 4a. chunk and block maps
@@ -1206,99 +1235,36 @@ __global__ __launch_bounds__(kThreads) void cpu_order_compose(const void *ref, c
 }
 
 // ---------------------------------------------------------- 4b. the walk
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint64_t from_below64(uint64_t identity, uint64_t v)
-{
-    return static_cast<uint64_t>(from_below<CTRL, ROWS>(static_cast<uint32_t>(identity), static_cast<uint32_t>(v))) |
-           (static_cast<uint64_t>(
-                from_below<CTRL, ROWS>(static_cast<uint32_t>(identity >> 32), static_cast<uint32_t>(v >> 32)))
-            << 32);
-}
-
-template <int CTRL, int ROWS>
-__device__ __forceinline__ Map2 map_scan_step(const Map2 &m)
-{
-    Map2 o;  // the identity where there is no source
-    o.dm0 = from_below64<CTRL, ROWS>(0, m.dm0);
-    o.dm1 = from_below64<CTRL, ROWS>(0, m.dm1);
-    o.p0 = from_below<CTRL, ROWS>(0u, m.p0);
-    o.p1 = from_below<CTRL, ROWS>(1u, m.p1);
-    return map_then(o, m);
-}
-
-// Lane j gets the composite of the maps of lanes 0..j, in lane order.
-__device__ __forceinline__ Map2 wave_scan_map(Map2 m)
-{
-    m = map_scan_step<0x111, 0xf>(m);
-    m = map_scan_step<0x112, 0xf>(m);
-    m = map_scan_step<0x114, 0xf>(m);
-    m = map_scan_step<0x118, 0xf>(m);
-    m = map_scan_step<0x142, 0xa>(m);
-    return map_scan_step<0x143, 0xc>(m);
-}
-
-// The 64 chunks of one block, chunk b*64 + j in lane j, from S.
-// Repeatedly: below 2^53, prefix sums of the chunk totals find the chunk in
-// which S gets there; past it, prefix compositions of the chunk maps find
-// the first chunk without a map for S's binade or in which S leaves it;
-// S is moved to just before that chunk, which is walked slab by slab.
+// The 64 chunks of one block, chunk b*64 + j in lane j, from S, from their
+// compact records; a chunk where they do not apply is walked slab by slab.
 template <int KK>
 __device__ __forceinline__ uint64_t walk_block(uint64_t S, const u32x4 *R, const u32x4 *D, const uint64_t *cmaps,
                                                const uint64_t *entries, int64_t frame, int chunks, int block,
-                                               const FrameEdges &fe)
+                                               const FrameEdges &fe, u32x4 *lds)
 {
     const int lane = threadIdx.x & 63;
     const int c = block * kBlockChunks + lane;
     const int n = chunks - block * kBlockChunks < kBlockChunks ? chunks - block * kBlockChunks : kBlockChunks;
-    const bool in = lane < n;
-    const bool empty = !in || fe.vb + static_cast<int64_t>(c) * kChunkVectors >= fe.ve;
-    uint64_t T = 0, flags = 0;
-    Map2 m;
-    if (in) {
+    Item it;
+    it.none = lane >= n || fe.vb + static_cast<int64_t>(c) * kChunkVectors >= fe.ve;  // no vectors
+    if (lane < n) {
         const uint64_t *x = cmaps + ((frame * chunks + c) * kSquares + KK) * kCompact;
-        T = x[0];
-        m = map_from(x[1], x[2], x[3]);
-        flags = x[3];
+        it.T = x[0];
+        it.fa = x[3];
+        it.a = map_from(x[1], x[2], it.fa);
     }
-    int from = 0;  // chunks before `from` are done
-    while (from < n) {
-        const bool act = lane >= from;
-        int jx;  // the chunk to walk slab by slab
-        if (S < kTwo53) {
-            const uint64_t t = act ? T : 0;
-            const uint64_t incl = wave_scan64(t);
-            const uint64_t rest = lane_value64(incl, 63);
-            if (S + rest < kTwo53)
-                return S + rest;
-            jx = __builtin_ctzll(__ballot(act && S + incl >= kTwo53));
-            S += lane_value64(incl - t, jx);  // exact: every add before it stays below 2^53
-        } else {
-            const int e = binade(S);
-            const int k = e - 52;
-            const bool ok = empty || ((flags & 1u) && flags_binade(flags) == e);
-            const Map2 pm = wave_scan_map(act && !empty ? m : Map2{});
-            const uint64_t mm = S >> k;
-            const uint64_t m2 = mm + pick(mm, pm.dm0, pm.dm1);  // m after chunks from..lane
-            const uint64_t bad = __ballot(act && (!ok || m2 >= kTwo53));
-            if (!bad)
-                return lane_value64(m2, 63) << k;
-            jx = __builtin_ctzll(bad);
-            if (jx > from)
-                S = lane_value64(m2, jx - 1) << k;
-        }
-        const int64_t cb = fe.vb + static_cast<int64_t>(block * kBlockChunks + jx) * kChunkVectors;
+    return walk_items(S, it, n, [&](uint64_t S1, int j) {
+        const int64_t cb = fe.vb + static_cast<int64_t>(block * kBlockChunks + j) * kChunkVectors;
         const int64_t ce = cb + kChunkVectors < fe.ve ? cb + kChunkVectors : fe.ve;
-        S = walk_chunk<KK>(S, R, D, entries + static_cast<int64_t>(block * kBlockChunks + jx) * kSquares * kEntry,
-                           cb, ce);
-        from = jx + 1;
-    }
-    return S;
+        return walk_chunk<KK>(S1, R, D, entries + static_cast<int64_t>(block * kBlockChunks + j) * kSquares * kEntry,
+                              cb, ce, lds);
+    });
 }
 
 template <int KK>
 __device__ __forceinline__ void walk_frame(const void *ref, const void *dist, int64_t pixels, int chunks,
                                            const uint64_t *maps, const uint64_t *cmaps, const uint64_t *bmaps,
-                                           int64_t frame, uint64_t *dst)
+                                           int64_t frame, uint64_t *dst, u32x4 *lds)
 {
     const int lane = threadIdx.x;
     const FrameEdges fe = frame_edges<KK>(ref, dist, pixels, frame);
@@ -1326,7 +1292,7 @@ __device__ __forceinline__ void walk_frame(const void *ref, const void *dist, in
         const uint64_t fl = lane_value64(bfl, b);
         if ((fl & 1u) && map_apply(S, map_from(lane_value64(bdm0, b), lane_value64(bdm1, b), fl), flags_binade(fl)))
             continue;
-        S = walk_block<KK>(S, R, D, cmaps, entries, frame, chunks, b, fe);
+        S = walk_block<KK>(S, R, D, cmaps, entries, frame, chunks, b, fe, lds);
     }
     // the tail comes last
     for (int j = 0; j < fe.tail; ++j)
@@ -1342,19 +1308,22 @@ __global__ __launch_bounds__(64) void cpu_order_walk(const void *ref, const void
                                                      const uint64_t *cmaps, const uint64_t *bmaps,
                                                      uint64_t *out_cpu_noise, uint64_t *out_cpu_moments)
 {
+    __shared__ u32x4 lds[2 * kSlabVectors];  // a slab of each plane, for `consecutive`
     const int64_t frame = blockIdx.x / kSquares;
     const int kk = static_cast<int>(blockIdx.x - frame * kSquares);
     if (totals[frame * kSquares + kk] < kTwo53)
         return;
     switch (kk) {
     case kSqNoise:
-        walk_frame<kSqNoise>(ref, dist, pixels, chunks, maps, cmaps, bmaps, frame, &out_cpu_noise[frame]);
+        walk_frame<kSqNoise>(ref, dist, pixels, chunks, maps, cmaps, bmaps, frame, &out_cpu_noise[frame], lds);
         break;
     case kSqRef:
-        walk_frame<kSqRef>(ref, dist, pixels, chunks, maps, cmaps, bmaps, frame, &out_cpu_moments[4 * frame + 2]);
+        walk_frame<kSqRef>(ref, dist, pixels, chunks, maps, cmaps, bmaps, frame, &out_cpu_moments[4 * frame + 2],
+                           lds);
         break;
     default:
-        walk_frame<kSqDist>(ref, dist, pixels, chunks, maps, cmaps, bmaps, frame, &out_cpu_moments[4 * frame + 3]);
+        walk_frame<kSqDist>(ref, dist, pixels, chunks, maps, cmaps, bmaps, frame, &out_cpu_moments[4 * frame + 3],
+                            lds);
         break;
     }
 }
