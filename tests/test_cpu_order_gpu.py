@@ -239,3 +239,44 @@ def test_view_form_odd_layouts(bpc):
     one_d = torch.from_numpy(big_d[:1, :41, :97]).cuda().expand(4, 41, 97)[:, :, :97]
     _view_case(np.broadcast_to(big_r[:1, :, :97], (4, 41, 97)), np.broadcast_to(big_d[:1, :41, :97], (4, 41, 97)),
                one_r[:, :, :97], one_d, bpc)
+
+
+def _random_case(rng):
+    """A batch whose sums pass 2^53 (frames of 2^21 to 2^23 16-bit samples,
+    mostly bright), with a random share and layout of dark samples: spread
+    at random, in square blocks, or in whole rows; odd-only or any value."""
+    share = float(rng.choice([0.0, 0.01, 0.05, 0.1, 0.3], p=[0.1, 0.2, 0.25, 0.25, 0.2]))
+    lo = int(rng.choice([49152, 57344, 61440]))
+    w = int(rng.integers(1400, 4097))
+    need = int(1.05 * 2**53 / ((1 - share) * lo * lo)) + 1  # samples for the sums to pass 2^53
+    h = int(rng.integers(-(-need // w), max(-(-need // w), 8_388_608 // w) + 1))
+    nframes = int(rng.integers(1, 4))
+    dark_max = int(rng.choice([255, 4095, 16383]))
+    layout = rng.choice(["random", "blocks", "rows"])
+    odd = bool(rng.integers(0, 2))
+    planes = []
+    for _ in range(2):
+        bright = rng.integers(lo, 65535, size=(nframes, h, w), endpoint=True)
+        dark = rng.integers(0, dark_max, size=(nframes, h, w), endpoint=True)
+        if odd:
+            dark |= 1
+        if layout == "random":
+            mask = rng.random((nframes, h, w)) < share
+        elif layout == "blocks":
+            b = 64
+            cells = rng.random((nframes, -(-h // b), -(-w // b))) < share
+            mask = np.repeat(np.repeat(cells, b, axis=1), b, axis=2)[:, :h, :w]
+        else:
+            mask = np.broadcast_to((rng.random((nframes, h, 1)) < share), (nframes, h, w))
+        planes.append(np.where(mask, dark, bright).astype(np.uint16))
+    return planes[0], planes[1], (w, h, nframes, lo, dark_max, share, str(layout), odd)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_batches_past53(seed):
+    """Seeded random sizes (unaligned frames too), frame counts and content
+    mixes; bitwise against the sequential oracle on every frame and output."""
+    rng = np.random.default_rng(20530 + seed)
+    ref, dist, desc = _random_case(rng)
+    past = check(ref, dist, 16)
+    assert past > 0, f"case {desc} never passed 2^53"
