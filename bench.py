@@ -104,6 +104,10 @@ def parse_args(argv=None):
                    help="streams the steps alternate over (step i on stream i %% N, each with its own "
                         "workspace): with more than one, consecutive steps overlap as in a pipeline of "
                         "batches, and a kernel's timed duration includes the overlap")
+    p.add_argument("--pitch", type=int, default=0, metavar="SAMPLES",
+                   help="cpu-order and psnr-int modes: keep the planes resident with rows of SAMPLES samples "
+                        "(>= w; the frame inside the first w of each row) and reduce them through the "
+                        "plane-view entry points (default: contiguous)")
     p.add_argument("--frames-per-upload", type=int, default=4,
                    help="host mode: frames per upload")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -601,7 +605,8 @@ def make_mode(args, vqx, L, hip, np, torch, dev, st, wl, ref_np, dist_np, planes
         m.alg_bytes = wl.bytes_per_frame * nframes
     elif args.mode == "cpu-order":
         m.width = 10 * nframes
-        m.ws_bytes = vqx.plane_stats_cpu_order_workspace_bytes(w, h, bpc, nframes)
+        m.ws_bytes = (vqx.plane_stats_view_cpu_order_workspace_bytes(w, h, bpc, nframes) if args.pitch
+                      else vqx.plane_stats_cpu_order_workspace_bytes(w, h, bpc, nframes))
         m.metric = METRIC_CPU_ORDER
         m.kernel = "cpu_order_step"
         m.kernel_label = ("cpu_order_step (stage1_u16, cpu_order_prefix, cpu_order_maps, cpu_order_compose, "
@@ -674,7 +679,23 @@ def main(argv=None):
     # two resident copies of the batch, alternated step by step
     r0 = torch.from_numpy(ref_np).to(dev)
     d0 = torch.from_numpy(dist_np).to(dev)
-    bufs = [(r0, d0), (r0.clone(), d0.clone())]
+    if args.pitch == w:
+        args.pitch = 0
+    if args.pitch:
+        if args.mode not in ("cpu-order", "psnr-int") or args.pitch < w:
+            print("--pitch needs --mode cpu-order or psnr-int and a pitch >= w", file=sys.stderr)
+            return 2
+
+        def pitched(x):
+            big = torch.zeros((nframes, h, args.pitch), dtype=x.dtype, device=dev)
+            big[:, :, :w] = x
+            return big[:, :, :w]
+        bufs = [(pitched(r0), pitched(d0)), (pitched(r0), pitched(d0))]
+        del r0, d0
+    else:
+        bufs = [(r0, d0), (r0.clone(), d0.clone())]
+    rs = args.pitch or w  # row and frame strides of the resident planes, in samples
+    fs = rs * h
     # Sums land directly in pinned host memory that the GPU writes through
     # (zero-copy): the last kernel of a step stores its few bytes per frame
     # there, and no copy kernel runs.  `depth` groups of slots, so that the
@@ -733,12 +754,16 @@ def main(argv=None):
             rc = L.vqx_plane_stats_batch_ws_timed(r.data_ptr(), d.data_ptr(), w, h, bpc, nframes,
                                                   o, o + itemsize * nframes, ws.data_ptr(), ws_bytes,
                                                   st, ev_begin.get(i), ev_end.get(i))
+        elif args.mode == "cpu-order" and args.pitch:
+            rc = L.vqx_plane_stats_view_cpu_order_ws(r.data_ptr(), rs, fs, d.data_ptr(), rs, fs, w, h, bpc, nframes,
+                                                     o, o + itemsize * nframes, o + itemsize * 5 * nframes,
+                                                     o + itemsize * 6 * nframes, ws.data_ptr(), ws_bytes, st)
         elif args.mode == "cpu-order":
             rc = L.vqx_plane_stats_batch_cpu_order_ws(r.data_ptr(), d.data_ptr(), w, h, bpc, nframes,
                                                       o, o + itemsize * nframes, o + itemsize * 5 * nframes,
                                                       o + itemsize * 6 * nframes, ws.data_ptr(), ws_bytes, st)
         elif args.mode == "psnr-int":
-            rc = L.vqx_psnr_int_view_ws(r.data_ptr(), w, w * h, d.data_ptr(), w, w * h, w, h, bpc, nframes,
+            rc = L.vqx_psnr_int_view_ws(r.data_ptr(), rs, fs, d.data_ptr(), rs, fs, w, h, bpc, nframes,
                                         o, ws.data_ptr(), ws_bytes, st)
         else:
             rc = L.vqx_psnr_int_planes_ws(mode.plane_arrays[i % 2], len(planes), bpc, nframes, o, ws.data_ptr(),
@@ -842,7 +867,8 @@ def main(argv=None):
         read_ceiling = measure_read_ceiling(L, hip, torch, bufs, wl, ws, ws_bytes, st, mean_ms,
                                             mode.alg_bytes, min(args.steps, 200))
 
-    wname = f"{w}x{h}x{nframes}_{bpc}bit" + ("_yuv420" if args.mode == "yuv420" else "")
+    wname = (f"{w}x{h}x{nframes}_{bpc}bit" + ("_yuv420" if args.mode == "yuv420" else "")
+             + (f"_pitch{args.pitch}" if args.pitch else ""))
     traffic = stored_traffic(mode.kernel, wname, tuple(mode.sources))
     achieved = mode.alg_bytes / (mean_ms * 1e-3) / 1e9
 
@@ -866,6 +892,7 @@ def main(argv=None):
                            if args.mode == "yuv420" else ""),
             "w": w, "h": h, "bpc": bpc, "nframes": nframes, "mode": args.mode,
             "streams": nst,
+            "row_pitch": args.pitch or w,
             "bytes_per_step": bytes_per_step,
             "hbm_gbs_whole_step": round(bytes_per_step * args.steps / elapsed / 1e9, 1),
         },

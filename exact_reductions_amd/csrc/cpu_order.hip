@@ -379,17 +379,18 @@ __device__ __forceinline__ uint32_t vector_term(const u32x4 &a, const u32x4 &b, 
 // Every lane loads, so no branch separates the loads from the waits for
 // them and the next vectors can be in flight while these are used.
 template <int KK>
-__device__ __forceinline__ void load_vector(const u32x4 *R, const u32x4 *D, int64_t v, bool ok, int64_t safe,
-                                            u32x4 &a, u32x4 &b)
+__device__ __forceinline__ void load_vector(const u32x4 *R, const u32x4 *D, const VecMap &M, int64_t frame,
+                                            int64_t v, bool ok, int64_t safe, u32x4 &a, u32x4 &b)
 {
     const u32x4 zero = {0, 0, 0, 0};
-    const int64_t at = ok ? v : safe;
+    int64_t ar, ad;
+    map_vec(M, frame, ok ? v : safe, ar, ad);
     if constexpr (KK != kSqDist)
-        a = __builtin_nontemporal_load(R + at);
+        a = __builtin_nontemporal_load(R + ar);
     else
         a = zero;
     if constexpr (KK != kSqRef)
-        b = __builtin_nontemporal_load(D + at);
+        b = __builtin_nontemporal_load(D + ad);
     else
         b = zero;
 }
@@ -643,15 +644,15 @@ __device__ __forceinline__ void forget(u32x4 (&a)[kLaneVectors], u32x4 (&b)[kLan
 // Slab [sb, sb + 256) of the chunk [cb, ce), cb < ce; the slab may start
 // past ce in the chunk after a frame's last whole vector.
 template <int KK>
-__device__ __forceinline__ void load_item(ItemData &x, const u32x4 *R, const u32x4 *D, int64_t cb, int64_t sb,
-                                          int64_t ce)
+__device__ __forceinline__ void load_item(ItemData &x, const u32x4 *R, const u32x4 *D, const VecMap &M,
+                                          int64_t frame, int64_t cb, int64_t sb, int64_t ce)
 {
     const int lane = threadIdx.x & 63;
     x.ok = 0;
 #pragma unroll
     for (int j = 0; j < kLaneVectors; ++j) {
         const int64_t v = sb + 64 * j + lane;
-        load_vector<KK>(R, D, v, v < ce, cb, x.a[j], x.b[j]);
+        load_vector<KK>(R, D, M, frame, v, v < ce, cb, x.a[j], x.b[j]);
         x.ok |= (v < ce ? 1u : 0u) << j;
     }
 }
@@ -776,6 +777,7 @@ __device__ __forceinline__ void item_maps(ItemData &x, int si, int e, bool dual,
 // is slab i % kSlabs of the chunk queued at i / kSlabs.
 struct Slabs {
     const u32x4 *R, *D;
+    VecMap map;
     const uint64_t *queue;  // this square sum's queue
     uint64_t *maps;
     int64_t pixels;
@@ -783,7 +785,7 @@ struct Slabs {
 };
 
 struct SlabItem {
-    int64_t cb, sb, ce;
+    int64_t frame, cb, sb, ce;
     uint64_t *entry;
     int si, e;
     bool dual;
@@ -799,6 +801,7 @@ __device__ __forceinline__ SlabItem slab_item(const Slabs &Q, int64_t i)
     const int64_t e0 = static_cast<int64_t>(f) * Q.pixels;
     const int64_t vb = (e0 + V - 1) / V, ve = (e0 + Q.pixels) / V;
     SlabItem x;
+    x.frame = f;
     x.si = static_cast<int>(i % kSlabs);
     x.e = static_cast<int>((q >> 32) & 0xffu);
     x.dual = ((q >> 40) & 1u) != 0;
@@ -820,7 +823,7 @@ __device__ __forceinline__ void queue_maps(const Slabs &Q, int64_t i, int64_t st
         item_maps<KK>(d, it.si, it.e, it.dual, it.entry, lds);
     };
     SlabItem u = slab_item<KK>(Q, i);
-    load_item<KK>(x, Q.R, Q.D, u.cb, u.sb, u.ce);
+    load_item<KK>(x, Q.R, Q.D, Q.map, u.frame, u.cb, u.sb, u.ce);
     if constexpr (KK == kSqNoise) {
         for (;;) {
             map_item(x, u);
@@ -828,7 +831,7 @@ __device__ __forceinline__ void queue_maps(const Slabs &Q, int64_t i, int64_t st
             if (i >= n)
                 return;
             u = slab_item<KK>(Q, i);
-            load_item<KK>(x, Q.R, Q.D, u.cb, u.sb, u.ce);
+            load_item<KK>(x, Q.R, Q.D, Q.map, u.frame, u.cb, u.sb, u.ce);
         }
     } else {
         // Two buffers, taken in turn.  Each item mapped inside the loop
@@ -843,7 +846,7 @@ __device__ __forceinline__ void queue_maps(const Slabs &Q, int64_t i, int64_t st
                 return;
             }
             v = slab_item<KK>(Q, i);
-            load_item<KK>(y, Q.R, Q.D, v.cb, v.sb, v.ce);
+            load_item<KK>(y, Q.R, Q.D, Q.map, v.frame, v.cb, v.sb, v.ce);
             map_item(x, u);
             i += stride;
             if (i >= n) {
@@ -851,7 +854,7 @@ __device__ __forceinline__ void queue_maps(const Slabs &Q, int64_t i, int64_t st
                 return;
             }
             u = slab_item<KK>(Q, i);
-            load_item<KK>(x, Q.R, Q.D, u.cb, u.sb, u.ce);
+            load_item<KK>(x, Q.R, Q.D, Q.map, u.frame, u.cb, u.sb, u.ce);
             map_item(y, v);
         }
     }
@@ -862,7 +865,7 @@ __device__ __forceinline__ void queue_maps(const Slabs &Q, int64_t i, int64_t st
 // all).  Two-byte samples only.
 __global__ __launch_bounds__(kThreads) void cpu_order_maps(const void *ref, const void *dist, int64_t pixels,
                                                            int chunks, int nframes, const uint64_t *rec,
-                                                           const uint64_t *queue, uint64_t *maps)
+                                                           const uint64_t *queue, uint64_t *maps, VecMap vmap)
 {
     const int64_t w = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + threadIdx.x / 64;
     const int64_t W = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
@@ -873,6 +876,7 @@ __global__ __launch_bounds__(kThreads) void cpu_order_maps(const void *ref, cons
     Slabs Q;
     Q.R = static_cast<const u32x4 *>(ref);
     Q.D = static_cast<const u32x4 *>(dist);
+    Q.map = vmap;
     Q.maps = maps;
     Q.pixels = pixels;
     Q.chunks = static_cast<uint32_t>(chunks);
@@ -1026,14 +1030,21 @@ __device__ __forceinline__ uint32_t lds_term(const u32x4 *lds, int g, int i)
     return square_term<2>(KK, r, d);
 }
 
+// The planes as the walk reads them: their vectors through the map, of one
+// frame.
+struct Planes {
+    const u32x4 *R, *D;
+    VecMap map;
+    int64_t frame;
+};
+
 // Vectors [sb, se) (at most 256) from S, with maps made here for S's binade
 // and the next (a slab's total is far below S past 2^53, so S crosses at
 // most one binade in it).  The slab goes through LDS so that lane g holds
 // vectors 4g .. 4g + 3, 32 consecutive terms: one row of 64 groups, and
 // inside the group where S crosses, one row of its 32 terms.
 template <int KK>
-__device__ __forceinline__ uint64_t walk_slab(uint64_t S, const u32x4 *R, const u32x4 *D, int64_t sb, int64_t se,
-                                              u32x4 *lds)
+__device__ __forceinline__ uint64_t walk_slab(uint64_t S, const Planes &P, int64_t sb, int64_t se, u32x4 *lds)
 {
     const int lane = threadIdx.x & 63;
     const int eA = S >= kTwo53 ? binade(S) : 53;
@@ -1042,7 +1053,7 @@ __device__ __forceinline__ uint64_t walk_slab(uint64_t S, const u32x4 *R, const 
 #pragma unroll
     for (int j = 0; j < kLaneVectors; ++j) {
         const int64_t v = sb + 64 * j + lane;
-        load_vector<KK>(R, D, v, v < se, sb, a[j], b[j]);
+        load_vector<KK>(P.R, P.D, P.map, P.frame, v, v < se, sb, a[j], b[j]);
         keep_if<KK>(v < se, a[j], b[j]);
     }
     consecutive<KK>(a, b, lds);
@@ -1081,15 +1092,15 @@ __device__ __forceinline__ uint64_t walk_slab(uint64_t S, const u32x4 *R, const 
 // One chunk, from its slab maps; a slab where they do not apply is walked
 // with maps made on the spot.
 template <int KK>
-__device__ __forceinline__ uint64_t walk_chunk(uint64_t S, const u32x4 *R, const u32x4 *D, const uint64_t *entry,
-                                               int64_t cb, int64_t ce, u32x4 *lds)
+__device__ __forceinline__ uint64_t walk_chunk(uint64_t S, const Planes &P, const uint64_t *entry, int64_t cb,
+                                               int64_t ce, u32x4 *lds)
 {
     const int lane = threadIdx.x & 63;
     if (entry[kChunkMap + 2] & kChunkOnly) {
         // no slab maps (S is not where the chunk map expects it): map each
         // slab on the spot
         for (int64_t sb = cb; sb < ce; sb += kSlabVectors)
-            S = walk_slab<KK>(S, R, D, sb, sb + kSlabVectors < ce ? sb + kSlabVectors : ce, lds);
+            S = walk_slab<KK>(S, P, sb, sb + kSlabVectors < ce ? sb + kSlabVectors : ce, lds);
         return S;
     }
     const int n = static_cast<int>((ce - cb + kSlabVectors - 1) / kSlabVectors);  // slabs holding vectors
@@ -1103,7 +1114,7 @@ __device__ __forceinline__ uint64_t walk_chunk(uint64_t S, const u32x4 *R, const
     }
     return walk_items(S, it, n, [&](uint64_t S1, int j) {
         const int64_t sb = cb + static_cast<int64_t>(j) * kSlabVectors;
-        return walk_slab<KK>(S1, R, D, sb, sb + kSlabVectors < ce ? sb + kSlabVectors : ce, lds);
+        return walk_slab<KK>(S1, P, sb, sb + kSlabVectors < ce ? sb + kSlabVectors : ce, lds);
     });
 }
 
@@ -1238,7 +1249,7 @@ __global__ __launch_bounds__(kThreads) void cpu_order_compose(const void *ref, c
 // The 64 chunks of one block, chunk b*64 + j in lane j, from S, from their
 // compact records; a chunk where they do not apply is walked slab by slab.
 template <int KK>
-__device__ __forceinline__ uint64_t walk_block(uint64_t S, const u32x4 *R, const u32x4 *D, const uint64_t *cmaps,
+__device__ __forceinline__ uint64_t walk_block(uint64_t S, const Planes &P, const uint64_t *cmaps,
                                                const uint64_t *entries, int64_t frame, int chunks, int block,
                                                const FrameEdges &fe, u32x4 *lds)
 {
@@ -1256,7 +1267,7 @@ __device__ __forceinline__ uint64_t walk_block(uint64_t S, const u32x4 *R, const
     return walk_items(S, it, n, [&](uint64_t S1, int j) {
         const int64_t cb = fe.vb + static_cast<int64_t>(block * kBlockChunks + j) * kChunkVectors;
         const int64_t ce = cb + kChunkVectors < fe.ve ? cb + kChunkVectors : fe.ve;
-        return walk_chunk<KK>(S1, R, D, entries + static_cast<int64_t>(block * kBlockChunks + j) * kSquares * kEntry,
+        return walk_chunk<KK>(S1, P, entries + static_cast<int64_t>(block * kBlockChunks + j) * kSquares * kEntry,
                               cb, ce, lds);
     });
 }
@@ -1264,14 +1275,14 @@ __device__ __forceinline__ uint64_t walk_block(uint64_t S, const u32x4 *R, const
 template <int KK>
 __device__ __forceinline__ void walk_frame(const void *ref, const void *dist, int64_t pixels, int chunks,
                                            const uint64_t *maps, const uint64_t *cmaps, const uint64_t *bmaps,
-                                           int64_t frame, uint64_t *dst, u32x4 *lds)
+                                           int64_t frame, uint64_t *dst, u32x4 *lds, const VecMap &vmap)
 {
     const int lane = threadIdx.x;
+    // (mapped planes hold whole vectors only: no head or tail samples)
     const FrameEdges fe = frame_edges<KK>(ref, dist, pixels, frame);
     // the head comes first in raster order; it is far below 2^53, so exact
     uint64_t S = wave_total64(fe.hterm);
-    const u32x4 *R = static_cast<const u32x4 *>(ref);
-    const u32x4 *D = static_cast<const u32x4 *>(dist);
+    const Planes P{static_cast<const u32x4 *>(ref), static_cast<const u32x4 *>(dist), vmap, frame};
     const uint64_t *entries = maps + (frame * chunks * kSquares + KK) * kEntry;  // chunk c: + c * kSquares * kEntry
     // block b's record in lane b (a frame has at most 2^22 vectors: 32 blocks)
     const int blocks = frame_blocks(chunks);
@@ -1292,7 +1303,7 @@ __device__ __forceinline__ void walk_frame(const void *ref, const void *dist, in
         const uint64_t fl = lane_value64(bfl, b);
         if ((fl & 1u) && map_apply(S, map_from(lane_value64(bdm0, b), lane_value64(bdm1, b), fl), flags_binade(fl)))
             continue;
-        S = walk_block<KK>(S, R, D, cmaps, entries, frame, chunks, b, fe, lds);
+        S = walk_block<KK>(S, P, cmaps, entries, frame, chunks, b, fe, lds);
     }
     // the tail comes last
     for (int j = 0; j < fe.tail; ++j)
@@ -1306,7 +1317,7 @@ __device__ __forceinline__ void walk_frame(const void *ref, const void *dist, in
 __global__ __launch_bounds__(64) void cpu_order_walk(const void *ref, const void *dist, int64_t pixels, int chunks,
                                                      const uint64_t *totals, const uint64_t *maps,
                                                      const uint64_t *cmaps, const uint64_t *bmaps,
-                                                     uint64_t *out_cpu_noise, uint64_t *out_cpu_moments)
+                                                     uint64_t *out_cpu_noise, uint64_t *out_cpu_moments, VecMap vmap)
 {
     __shared__ u32x4 lds[2 * kSlabVectors];  // a slab of each plane, for `consecutive`
     const int64_t frame = blockIdx.x / kSquares;
@@ -1315,15 +1326,15 @@ __global__ __launch_bounds__(64) void cpu_order_walk(const void *ref, const void
         return;
     switch (kk) {
     case kSqNoise:
-        walk_frame<kSqNoise>(ref, dist, pixels, chunks, maps, cmaps, bmaps, frame, &out_cpu_noise[frame], lds);
+        walk_frame<kSqNoise>(ref, dist, pixels, chunks, maps, cmaps, bmaps, frame, &out_cpu_noise[frame], lds, vmap);
         break;
     case kSqRef:
         walk_frame<kSqRef>(ref, dist, pixels, chunks, maps, cmaps, bmaps, frame, &out_cpu_moments[4 * frame + 2],
-                           lds);
+                           lds, vmap);
         break;
     default:
         walk_frame<kSqDist>(ref, dist, pixels, chunks, maps, cmaps, bmaps, frame, &out_cpu_moments[4 * frame + 3],
-                            lds);
+                            lds, vmap);
         break;
     }
 }
@@ -1356,6 +1367,28 @@ hipError_t maps_resident_workgroups(int64_t &wgs)
 
 }  // namespace
 
+VecMap make_vec_map(int w, int h, int64_t ref_row_stride, int64_t ref_frame_stride, int64_t dist_row_stride,
+                    int64_t dist_frame_stride)
+{
+    constexpr int V = 8;  // two-byte samples per vector
+    VecMap M;
+    M.vpr = static_cast<uint32_t>(w / V);
+    M.frame_vecs = static_cast<int64_t>(h) * M.vpr;
+    // floor(r / vpr) = (r * magic) >> shift for every r < 2^22: with
+    // 2^(L-1) < vpr <= 2^L, shift = 22 + L and magic = ceil(2^shift / vpr),
+    // the error r * (magic - 2^shift / vpr) / 2^shift < 2^-L <= 1 / vpr
+    int L = 0;
+    while ((1u << L) < M.vpr)
+        ++L;
+    M.shift = 22 + L;
+    M.magic = ((1ull << M.shift) + M.vpr - 1) / M.vpr;
+    M.pad_row_r = ref_row_stride / V - M.vpr;
+    M.pad_row_d = dist_row_stride / V - M.vpr;
+    M.pad_frame_r = ref_frame_stride / V - M.frame_vecs;
+    M.pad_frame_d = dist_frame_stride / V - M.frame_vecs;
+    return M;
+}
+
 CpuOrderLayout cpu_order_layout(const Geometry &g)
 {
     auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
@@ -1375,7 +1408,7 @@ CpuOrderLayout cpu_order_layout(const Geometry &g)
 hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, const void *dist,
                                         uint64_t *out_noise, uint64_t *out_moments,
                                         uint64_t *out_cpu_noise, uint64_t *out_cpu_moments,
-                                        void *workspace, hipStream_t stream)
+                                        void *workspace, hipStream_t stream, const VecMap &map)
 {
     const CpuOrderLayout l = cpu_order_layout(g);
     char *ws = static_cast<char *>(workspace);
@@ -1386,8 +1419,11 @@ hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, cons
     uint64_t *cmaps = reinterpret_cast<uint64_t *>(ws + l.cmaps);
     uint64_t *bmaps = reinterpret_cast<uint64_t *>(ws + l.bmaps);
     // stage 1 with the low bits of the terms, at two-byte samples
-    hipError_t err = launch_plane_stats(g, ref, dist, nullptr, nullptr, rec, stream, nullptr, nullptr,
-                                        g.sample_bytes == 2);
+    if (map.vpr && g.sample_bytes != 2)
+        return hipErrorInvalidValue;
+    hipError_t err = map.vpr ? launch_stage1_mapped(g, ref, dist, rec, map, stream)
+                             : launch_plane_stats(g, ref, dist, nullptr, nullptr, rec, stream, nullptr, nullptr,
+                                                  g.sample_bytes == 2);
     if (err != hipSuccess)
         return err;
     const unsigned nf = static_cast<unsigned>(g.nframes);
@@ -1409,7 +1445,7 @@ hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, cons
     const int64_t slab_wgs = (g.workgroups * kSquares * kSlabs + kThreads / 64 - 1) / (kThreads / 64);
     const int64_t wgs = slab_wgs < resident ? slab_wgs : resident;
     cpu_order_maps<<<dim3(static_cast<unsigned>(wgs)), kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks,
-                                                                             g.nframes, rec, queue, maps);
+                                                                             g.nframes, rec, queue, maps, map);
     err = hipGetLastError();
     if (err != hipSuccess)
         return err;
@@ -1420,7 +1456,7 @@ hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, cons
     if (err != hipSuccess)
         return err;
     cpu_order_walk<<<dim3(nf * kSquares), 64, 0, stream>>>(ref, dist, g.pixels, g.chunks, totals, maps, cmaps,
-                                                           bmaps, out_cpu_noise, out_cpu_moments);
+                                                           bmaps, out_cpu_noise, out_cpu_moments, map);
     return hipGetLastError();
 }
 

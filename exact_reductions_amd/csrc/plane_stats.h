@@ -141,12 +141,47 @@ struct CpuOrderLayout {
 };
 CpuOrderLayout cpu_order_layout(const Geometry &g);
 
-// Both stages, then the three kernels that reproduce the CPU's running
-// double sums (cpu_order.hip): out_cpu_noise[F] and out_cpu_moments[F][4],
-// in the same units as the exact sums.
+// Where the CPU-order kernels find a batch's 16-byte vectors.  They index
+// them as if the batch were one contiguous [nframes][h][w] array (index v);
+// a pair of plane views whose rows are whole 16-byte aligned vectors maps v
+// of frame f to v + f*pad_frame + y*pad_row (in vectors) for each plane, y
+// the row of v in its frame.  vpr == 0: contiguous planes, v itself.
+struct VecMap {
+    uint32_t vpr = 0;        // vectors per row
+    int64_t frame_vecs = 0;  // vectors per frame, h * vpr
+    uint64_t magic = 0;      // y = (r * magic) >> shift for r < 2^22
+    int shift = 0;
+    int64_t pad_row_r = 0, pad_frame_r = 0, pad_row_d = 0, pad_frame_d = 0;
+};
+
+// The VecMap of two views of w x h planes (two-byte samples), strides in
+// samples; the caller has checked that rows are whole aligned vectors.
+VecMap make_vec_map(int w, int h, int64_t ref_row_stride, int64_t ref_frame_stride, int64_t dist_row_stride,
+                    int64_t dist_frame_stride);
+
+__device__ __forceinline__ void map_vec(const VecMap &M, int64_t frame, int64_t v, int64_t &vr, int64_t &vd)
+{
+    vr = vd = v;
+    if (M.vpr == 0)
+        return;
+    const uint64_t r = static_cast<uint64_t>(v - frame * M.frame_vecs);  // below 2^22
+    const int64_t y = static_cast<int64_t>((r * M.magic) >> M.shift);
+    vr += frame * M.pad_frame_r + y * M.pad_row_r;
+    vd += frame * M.pad_frame_d + y * M.pad_row_d;
+}
+
+// Stage 1, then the kernels that reproduce the CPU's running double sums
+// (cpu_order.hip): the exact sums, and out_cpu_noise[F] and
+// out_cpu_moments[F][4] in the same units.  `map`: where the vectors lie
+// (two-byte samples only; contiguous by default).
 hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, const void *dist,
                                         uint64_t *out_noise, uint64_t *out_moments,
                                         uint64_t *out_cpu_noise, uint64_t *out_cpu_moments,
-                                        void *workspace, hipStream_t stream);
+                                        void *workspace, hipStream_t stream, const VecMap &map = VecMap{});
+
+// The CPU-order form of stage 1 (two-byte samples, the low bits of the
+// terms too) with its vectors found through `map`.
+hipError_t launch_stage1_mapped(const Geometry &g, const void *ref, const void *dist, uint64_t *partials,
+                                const VecMap &map, hipStream_t stream);
 
 }  // namespace vqx

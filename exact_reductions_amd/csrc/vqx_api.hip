@@ -183,8 +183,16 @@ int check_planes(const vqx_plane_pair *planes, int nplanes, int bpc, int nframes
     return VQX_OK;
 }
 
-// The CPU-order form over plane views: both views gathered into contiguous
-// planes after the contiguous form's workspace, then that form.
+// Whether a view's rows are whole 16-byte aligned vectors of two-byte
+// samples, which the CPU-order kernels read in place.
+bool rows_of_vectors(const void *base, int64_t row_stride, int64_t frame_stride, int w, int bpc)
+{
+    return bpc > 8 && w % 8 == 0 && row_stride % 8 == 0 && frame_stride % 8 == 0 && aligned(base, 16);
+}
+
+// The CPU-order form over plane views that are not rows of vectors: both
+// views gathered into contiguous planes after the contiguous form's
+// workspace, then that form.
 struct ViewCpuOrderLayout {
     size_t ref, dist, bytes;
 };
@@ -398,7 +406,21 @@ int vqx_plane_stats_view_cpu_order_ws(const void *ref, int64_t ref_row_stride, i
     char *ws = static_cast<char *>(workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const vqx::Geometry g = vqx::make_geometry(w, h, bpc, nframes);
-    hipError_t err = vqx::launch_gather_view(vqx::PlaneView{ref, ref_row_stride, ref_frame_stride}, w, h, bpc,
+    hipError_t err;
+    if (rows_of_vectors(ref, ref_row_stride, ref_frame_stride, w, bpc) &&
+        rows_of_vectors(dist, dist_row_stride, dist_frame_stride, w, bpc)) {
+        // read in place: each vector of the contiguous order found in the views
+        const vqx::VecMap map = vqx::make_vec_map(w, h, ref_row_stride, ref_frame_stride, dist_row_stride,
+                                                  dist_frame_stride);
+        err = vqx::launch_plane_stats_cpu_order(g, ref, dist, out_noise, out_moments, out_cpu_noise,
+                                                out_cpu_moments, workspace, s, map);
+        if (err != hipSuccess) {
+            (void)hipGetLastError();
+            return VQX_E_HIP;
+        }
+        return VQX_OK;
+    }
+    err = vqx::launch_gather_view(vqx::PlaneView{ref, ref_row_stride, ref_frame_stride}, w, h, bpc,
                                              nframes, ws + l.ref, s);
     if (err == hipSuccess)
         err = vqx::launch_gather_view(vqx::PlaneView{dist, dist_row_stride, dist_frame_stride}, w, h, bpc, nframes,

@@ -321,12 +321,16 @@ int vqx_psnr_int_view_ws(const void *ref, int64_t ref_row_stride, int64_t ref_fr
  * the exact sums and the CPU's running double sums, bit for bit past 2^53
  * too, of views with any row and frame stride -- the CPU adds a view's
  * samples in raster order, row after row, whatever the pitch [PSNR,
- * Context; MOMENT, Context].  Both views are first copied into contiguous
- * planes inside the workspace (about twice the contiguous form's time), then
- * reduced as the contiguous form does.  Errors as for the views and the
+ * Context; MOMENT, Context].  Where both views hold two-byte samples (bpc
+ * 9..16) in rows of whole 16-byte vectors (w, both row strides and both
+ * frame strides multiples of 8 samples; both bases 16-byte aligned) they are
+ * read in place, at the contiguous form's speed.  Other views are first
+ * copied into contiguous planes inside the workspace (about twice the
+ * contiguous form's time), then reduced as the contiguous form does; the
+ * results are the same either way.  Errors as for the views and the
  * contiguous CPU-order form; the workspace is
  * vqx_plane_stats_view_cpu_order_workspace_bytes() (the contiguous form's
- * and both planes of the batch).
+ * and both planes of the batch, whichever way the call reads).
  */
 int vqx_plane_stats_view_cpu_order_workspace_bytes(int w, int h, int bpc, int nframes, size_t *bytes);
 int vqx_plane_stats_view_cpu_order_ws(const void *ref, int64_t ref_row_stride, int64_t ref_frame_stride,

@@ -241,6 +241,105 @@ def test_view_form_odd_layouts(bpc):
                one_r[:, :, :97], one_d, bpc)
 
 
+def _in_place_case(ref_np, dist_np, R, D, bpc, in_place=True):
+    """The view form through the C ABI with a workspace filled with 0xA5:
+    results as in _view_case, and views whose rows are whole aligned vectors
+    read in place (the part of the workspace past the contiguous form's is
+    left as it was), others gathered into it."""
+    f, h, w = R.shape
+    total = vqx.plane_stats_view_cpu_order_workspace_bytes(w, h, bpc, f)
+    own = vqx.plane_stats_cpu_order_workspace_bytes(w, h, bpc, f)
+    ws = torch.full((total,), 0xA5, dtype=torch.uint8, device="cuda:0")
+    out = torch.full((2, 5 * f), -1, dtype=torch.int64, device="cuda:0")
+    _, args = vqx._views(R, D, bpc)
+    torch.cuda.synchronize()
+    assert vqx.lib().vqx_plane_stats_view_cpu_order_ws(
+        *args, w, h, bpc, f, out[0, :f].data_ptr(), out[0, f:].data_ptr(), out[1, :f].data_ptr(),
+        out[1, f:].data_ptr(), ws.data_ptr(), total, torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    untouched = bool((ws[own:] == 0xA5).all())
+    assert untouched == in_place, "read in place" if in_place else "gathered"
+    _check_outputs(np.ascontiguousarray(ref_np), np.ascontiguousarray(dist_np), bpc, out, f)
+    n2, m2, cn2, cm2 = run(np.ascontiguousarray(ref_np), np.ascontiguousarray(dist_np), bpc)
+    o = out.cpu().numpy()
+    assert (o[0, :f] == n2).all() and (o[1, :f] == cn2).all()
+    assert (o[0, f:] == m2.reshape(-1)).all() and (o[1, f:] == cm2.reshape(-1)).all()
+
+
+def test_view_form_in_place_past53():
+    """A 2560x1440 region, 8 samples in, of 16-bit planes with different
+    pitches (2624 and 2696 samples), sums past 2^53: read in place."""
+    ref, dist = synth.past53_mixed(nframes=2)
+    f, h, w = ref.shape
+    big_r = np.zeros((f, h + 3, w + 64), dtype=np.uint16)
+    big_d = np.zeros((f, h + 4, w + 136), dtype=np.uint16)
+    big_r[:, 2:2 + h, 8:8 + w] = ref
+    big_d[:, 3:3 + h, 16:16 + w] = dist
+    sr = (slice(None), slice(2, 2 + h), slice(8, 8 + w))
+    sd = (slice(None), slice(3, 3 + h), slice(16, 16 + w))
+    R, D = torch.from_numpy(big_r).cuda()[sr], torch.from_numpy(big_d).cuda()[sd]
+    _in_place_case(big_r[sr], big_d[sd], R, D, 16)
+
+
+def test_view_form_in_place_repeated_frame():
+    """Frame stride 0 on both sides (one frame pair read three times) and a
+    contiguous dist beside a pitched ref: read in place."""
+    ref, dist = synth.odd_dark_bright(w=2560, h=1440, nframes=1)
+    h, w = ref.shape[1:]
+    big_r = np.zeros((1, h, w + 8), dtype=np.uint16)
+    big_r[:, :, :w] = ref
+    R = torch.from_numpy(big_r).cuda()[:, :, :w].expand(3, h, w)
+    D = torch.from_numpy(dist).cuda().expand(3, h, w)
+    _in_place_case(np.broadcast_to(ref, (3, h, w)), np.broadcast_to(dist, (3, h, w)), R, D, 16)
+
+
+@pytest.mark.parametrize("bpc", [9, 12, 16])
+@pytest.mark.parametrize("w,h,x0", [(8, 1, 0), (8, 300, 8), (96, 37, 16), (1024, 65, 8), (4096, 17, 24)])
+def test_view_form_in_place_small(bpc, w, h, x0):
+    """Small aligned views (rows of one vector, chunks with a ragged tail,
+    rows longer than a chunk's share) at several depths: read in place."""
+    rng = np.random.default_rng(w * 131 + h * 7 + bpc)
+    hi = (1 << bpc) - 1
+    big_r = rng.integers(0, hi, size=(3, h + 2, w + x0 + 40), endpoint=True).astype(np.uint16)
+    big_d = rng.integers(0, hi, size=(3, h + 1, w + x0 + 8), endpoint=True).astype(np.uint16)
+    sr = (slice(None), slice(1, 1 + h), slice(x0, x0 + w))
+    sd = (slice(None), slice(0, h), slice(x0, x0 + w))
+    R, D = torch.from_numpy(big_r).cuda()[sr], torch.from_numpy(big_d).cuda()[sd]
+    _in_place_case(big_r[sr], big_d[sd], R, D, bpc)
+
+
+def test_view_form_unaligned_gathered():
+    """A view 4 samples in, and one of width 100: gathered, same results."""
+    rng = np.random.default_rng(7)
+    big = rng.integers(0, 65535, size=(2, 50, 120), endpoint=True).astype(np.uint16)
+    big_d = rng.integers(0, 65535, size=(2, 50, 120), endpoint=True).astype(np.uint16)
+    s4 = (slice(None), slice(None), slice(4, 100))
+    _in_place_case(big[s4], big_d[s4], torch.from_numpy(big).cuda()[s4], torch.from_numpy(big_d).cuda()[s4], 16,
+                   in_place=False)
+    s100 = (slice(None), slice(None), slice(0, 100))
+    _in_place_case(big[s100], big_d[s100], torch.from_numpy(big).cuda()[s100],
+                   torch.from_numpy(big_d).cuda()[s100], 16, in_place=False)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_random_views_in_place_past53(seed):
+    """Seeded random batches past 2^53 as in the contiguous tests, widths
+    rounded to whole vectors, inside planes with random padded pitches."""
+    rng = np.random.default_rng(40530 + seed)
+    ref, dist, desc = _random_case(rng)
+    f, h, w = ref.shape
+    w8 = w - w % 8
+    pads = [int(rng.integers(0, 9)) * 8 for _ in range(4)]
+    views = []
+    for plane, (x0, extra) in zip((ref, dist), ((pads[0], pads[1]), (pads[2], pads[3]))):
+        big = np.zeros((f, h, x0 + w8 + extra), dtype=np.uint16)
+        big[:, :, x0:x0 + w8] = plane[:, :, :w8]
+        sl = (slice(None), slice(None), slice(x0, x0 + w8))
+        views.append((big[sl], torch.from_numpy(big).cuda()[sl]))
+    (rn, R), (dn, D) = views
+    _in_place_case(rn, dn, R, D, 16)
+
+
 def _random_case(rng):
     """A batch whose sums pass 2^53 (frames of 2^21 to 2^23 16-bit samples,
     mostly bright), with a random share and layout of dark samples: spread
