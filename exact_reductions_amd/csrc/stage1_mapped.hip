@@ -1,0 +1,97 @@
+// The CPU-order form of stage 1 over plane views read in place, for gfx950.
+//
+// Sources (web pages, cited by title and section):
+//   [PSNR]   "ADR-1440: float_psnr_hip adds its squared differences as
+//            integers and returns the CPU's score bit for bit"
+//   [MOMENT] "ADR-1447: float_moment_hip adds the float squares the CPU adds,
+//            and is bit-identical while the CPU's own sum is exact"
+//
+// The CPU adds a view's samples in raster order whatever its pitch [PSNR,
+// Context; MOMENT, Context], so the chunks of a view are those of the same
+// frames stored contiguously.  Where the view's rows are whole 16-byte
+// aligned vectors of two-byte samples, this kernel reads vector v of that
+// contiguous order where the view keeps it (map_vec) and writes the records
+// and low bits the contiguous CPU-order stage 1 writes for the same samples:
+// the same terms in the same lane accumulators and workgroup sums.
+
+#include <hip/hip_runtime.h>
+
+#include "plane_stats.h"
+#include "reduce.h"
+#include "terms.h"
+
+#pragma clang fp contract(off)
+
+namespace vqx {
+namespace {
+
+constexpr int kLaneIters = kChunkVectors / kThreads;  // vectors per lane per plane
+constexpr int kInFlight = 4;                          // vectors of each plane loaded before use
+static_assert(kLaneIters % kInFlight == 0, "whole load groups");
+
+// The CPU-order form of stage 1 over plane views whose rows are whole
+// 16-byte aligned vectors (two-byte samples, so frames hold no partial
+// vectors): the same chunks, terms, records and low bits as
+// stage1_u16<true>, each vector found through the VecMap.
+__global__ __launch_bounds__(kThreads) void stage1_u16_mapped(const void *ref, const void *dist, int64_t pixels,
+                                                              int chunks, uint64_t *part, VecMap M)
+{
+    const int64_t wg = blockIdx.x;
+    const int64_t frame = wg / chunks;
+    const int chunk = static_cast<int>(wg - frame * chunks);
+    const u32x4 *R = static_cast<const u32x4 *>(ref);
+    const u32x4 *D = static_cast<const u32x4 *>(dist);
+    const int64_t vb = frame * (pixels / 8), ve = vb + pixels / 8;
+    const int64_t cb = vb + static_cast<int64_t>(chunk) * kChunkVectors;
+    const int64_t ce = cb + kChunkVectors < ve ? cb + kChunkVectors : ve;
+    Acc16Low a;
+    if (cb < ce) {
+#pragma unroll 1
+        for (int i = 0; i < kLaneIters; i += kInFlight) {
+            u32x4 x[kInFlight], y[kInFlight];
+            bool ok[kInFlight];
+#pragma unroll
+            for (int u = 0; u < kInFlight; ++u) {
+                const int64_t v = cb + threadIdx.x + static_cast<int64_t>(i + u) * kThreads;
+                ok[u] = v < ce;
+                int64_t vr, vd;
+                map_vec(M, frame, ok[u] ? v : cb, vr, vd);
+                x[u] = __builtin_nontemporal_load(R + vr);
+                y[u] = __builtin_nontemporal_load(D + vd);
+            }
+#pragma unroll
+            for (int u = 0; u < kInFlight; ++u) {
+                const u32x4 zero = {0, 0, 0, 0};
+                add_vec(a, ok[u] ? x[u] : zero, ok[u] ? y[u] : zero);
+            }
+        }
+    }
+    const uint32_t v[8] = {static_cast<uint32_t>(a.noise & 0xffffu), static_cast<uint32_t>(a.noise >> 16),
+                           a.r1, a.d1,
+                           static_cast<uint32_t>(a.r2 & 0xffffu), static_cast<uint32_t>(a.r2 >> 16),
+                           static_cast<uint32_t>(a.d2 & 0xffffu), static_cast<uint32_t>(a.d2 >> 16)};
+    uint64_t s[8];
+    workgroup_sums(v, s);
+    const uint64_t rec[kSums] = {s[0] + (s[1] << 16), s[2], s[3], s[4] + (s[5] << 16), s[6] + (s[7] << 16)};
+    write_record(part, wg, rec);
+    const uint32_t low = workgroup_or((a.or_noise & 15u) | ((a.or_r2 & 15u) << 4) | ((a.or_d2 & 15u) << 8));
+    if (threadIdx.x == 0) {
+        part[wg * kRecordStride + kLowBits] = low;
+        if (wg == 0) {
+            part[kQueueCounts] = 0;
+            part[kQueueCounts + 1] = 0;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_stage1_mapped(const Geometry &g, const void *ref, const void *dist, uint64_t *partials,
+                                const VecMap &map, hipStream_t stream)
+{
+    stage1_u16_mapped<<<dim3(static_cast<unsigned>(g.workgroups)), kThreads, 0, stream>>>(ref, dist, g.pixels,
+                                                                                        g.chunks, partials, map);
+    return hipGetLastError();
+}
+
+}  // namespace vqx
