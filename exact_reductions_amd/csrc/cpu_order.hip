@@ -862,8 +862,9 @@ __device__ __forceinline__ void queue_maps(const Slabs &Q, int64_t i, int64_t st
 
 // A fixed grid of waves shares out the slabs of the three queues: wave w
 // takes slab items w, w + W, w + 2W, ... of each queue in turn (W waves in
-// all).  Two-byte samples only.
-__global__ __launch_bounds__(kThreads) void cpu_order_maps(const void *ref, const void *dist, int64_t pixels,
+// all).  Two-byte samples only.  Three waves per SIMD fit its registers
+// without spills (168 VGPRs), one more than the compiler picks unasked.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void cpu_order_maps(const void *ref, const void *dist, int64_t pixels,
                                                            int chunks, int nframes, const uint64_t *rec,
                                                            const uint64_t *queue, uint64_t *maps, VecMap vmap)
 {

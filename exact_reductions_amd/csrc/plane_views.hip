@@ -369,42 +369,80 @@ hipError_t launch_multi(const ViewGeometry *g, const PlaneView *ref, const Plane
 // ------------------------------------------------------------------ gather
 // Copies a view's samples into a contiguous [nframes][h][w] array: one
 // workgroup per (frame, row) pair in turn, a grid of at most kGatherWgs
-// workgroups.  Where the row's source and destination start at the same
-// offset within 16 bytes, its whole 16-byte vectors are copied as vectors
-// (consecutive threads, consecutive vectors) and the few samples before the
-// first and after the last one by one; otherwise sample by sample.
+// workgroups.  Each row's whole 16-byte destination vectors are written
+// whole (consecutive threads, consecutive vectors), the few samples before
+// the first and after the last one by one.  The source bytes of a
+// destination vector start at the same offset o within a 16-byte block for
+// the whole row: where o is 0 the vector is copied as it is, otherwise it is
+// cut from the two aligned blocks that hold it.  Those blocks each hold at
+// least one byte of the row, so they lie in pages of the view.
 constexpr int64_t kGatherWgs = 65536;
+
+// The 16 bytes at byte offset 4Q + r (r in 0..3, 4Q + r in 1..15) of the 32
+// bytes lo then hi.
+template <int Q>
+__device__ __forceinline__ u32x4 bytes_at(const u32x4 &lo, const u32x4 &hi, uint32_t r)
+{
+    const uint32_t d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    u32x4 o;
+    o.x = __builtin_amdgcn_alignbyte(d[Q + 1], d[Q + 0], r);
+    o.y = __builtin_amdgcn_alignbyte(d[Q + 2], d[Q + 1], r);
+    o.z = __builtin_amdgcn_alignbyte(d[Q + 3], d[Q + 2], r);
+    o.w = __builtin_amdgcn_alignbyte(d[Q + 4], d[Q + 3], r);
+    return o;
+}
+
+// Destination vectors 0..n-1 from the source blocks vs[0..n] at offset
+// 4Q + r (> 0).
+template <int Q>
+__device__ __forceinline__ void copy_shifted(const u32x4 *vs, u32x4 *vd, int n, uint32_t r)
+{
+    for (int v = threadIdx.x; v < n; v += kThreads)
+        vd[v] = bytes_at<Q>(vs[v], vs[v + 1], r);
+}
 
 template <int kBytes>
 __global__ __launch_bounds__(kThreads) void gather_view(PlaneView P, int w, int h, int64_t rows, void *dst)
 {
     using T = typename std::conditional<kBytes == 1, uint8_t, uint16_t>::type;
-    constexpr int V = 16 / kBytes;
     const int t = threadIdx.x;
     for (int64_t fr = blockIdx.x; fr < rows; fr += gridDim.x) {
         const int64_t f = fr / h;
         const int64_t y = fr - f * h;
         const T *src = static_cast<const T *>(P.base) + f * P.frame_stride + y * P.row_stride;
         T *out = static_cast<T *>(dst) + fr * w;
-        const int ps = static_cast<int>(reinterpret_cast<uintptr_t>(src) & 15);
-        const int pd = static_cast<int>(reinterpret_cast<uintptr_t>(out) & 15);
-        if (ps != pd) {
+        const uintptr_t sa = reinterpret_cast<uintptr_t>(src), oa = reinterpret_cast<uintptr_t>(out);
+        const uintptr_t da = (oa + 15) & ~static_cast<uintptr_t>(15);
+        const uintptr_t de = (oa + static_cast<uintptr_t>(w) * kBytes) & ~static_cast<uintptr_t>(15);
+        if (da >= de) {  // no whole destination vector
             for (int x = t; x < w; x += kThreads)
                 out[x] = src[x];
             continue;
         }
-        int head = ((16 - ps) & 15) / kBytes;
-        head = head < w ? head : w;
-        const int nvec = (w - head) / V;
-        const int tail_begin = head + nvec * V;
+        const int head = static_cast<int>((da - oa) / kBytes);
+        const int tail_begin = static_cast<int>((de - oa) / kBytes);
         if (t < head)
             out[t] = src[t];
         if (t < w - tail_begin)
             out[tail_begin + t] = src[tail_begin + t];
-        const u32x4 *vs = reinterpret_cast<const u32x4 *>(src + head);
-        u32x4 *vd = reinterpret_cast<u32x4 *>(out + head);
-        for (int v = t; v < nvec; v += kThreads)
-            vd[v] = __builtin_nontemporal_load(vs + v);
+        const int n = static_cast<int>((de - da) / 16);
+        const uintptr_t s0 = sa + (da - oa);  // source of the first destination vector
+        const u32x4 *vs = reinterpret_cast<const u32x4 *>(s0 & ~static_cast<uintptr_t>(15));
+        u32x4 *vd = reinterpret_cast<u32x4 *>(da);
+        const uint32_t o = static_cast<uint32_t>(s0 & 15);
+        switch (o >> 2) {
+        case 0:
+            if (o == 0) {
+                for (int v = t; v < n; v += kThreads)
+                    vd[v] = __builtin_nontemporal_load(vs + v);
+            } else {
+                copy_shifted<0>(vs, vd, n, o & 3);
+            }
+            break;
+        case 1: copy_shifted<1>(vs, vd, n, o & 3); break;
+        case 2: copy_shifted<2>(vs, vd, n, o & 3); break;
+        default: copy_shifted<3>(vs, vd, n, o & 3); break;
+        }
     }
 }
 
