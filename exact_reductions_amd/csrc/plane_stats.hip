@@ -27,11 +27,15 @@
 // (v_dot4_u32_u8), and noise = sum r^2 + sum d^2 - 2 sum r*d, an identity of
 // integers.
 // 9..16 bits: each sample is converted to float and the three products
-// (r-d)^2, r^2, d^2 are taken in binary32, round to nearest even, then read
-// back as uint32 (below 2^32 [MOMENT, Decision]) and added into 64-bit
-// integer lane accumulators.  Across the wave each 64-bit lane sum travels
-// as its low 16 bits and the rest, two uint32 sums -- the page's low/high
-// split at 16 bits [PSNR, Decision], moved from every term to once per lane.
+// (r-d)^2, r^2, d^2 are taken in binary32, round to nearest even; each is an
+// integer below 2^32 [MOMENT, Decision].  They are added into binary64 lane
+// accumulators: a lane adds at most 65 of them, so every partial sum is an
+// integer below 2^39, exact in binary64, and the lane's sum is read back as
+// a uint64 without loss.  Across the wave each lane sum travels as its low
+// 16 bits and the rest, two uint32 sums -- the page's low/high split at 16
+// bits [PSNR, Decision], moved from every term to once per lane.  The
+// CPU-order form keeps uint64 lanes, since it needs each term as an integer
+// anyway (for the OR of the low bits).
 
 #include <hip/hip_ext.h>
 
@@ -56,8 +60,9 @@ static_assert(kIters % kInFlight == 0, "whole load groups");
 // A lane sees at most kIters vectors plus one edge sample.
 //  8 bits: a lane's sum r^2 <= (8*16 + 1) * 255^2 < 2^23, so a wave's sum
 //          < 2^29; sum r and sum r*d are no larger.
-// 16 bits: a lane's 64-bit sum of squares is <= (8*8 + 1) * (2^32 - 1) <
-//          2^39; it is reduced across the wave as its low 16 bits (wave sum
+// 16 bits: a lane's sum of squares is <= (8*8 + 1) * (2^32 - 1) < 2^39
+//          (so exact in binary64 at every step); it is reduced across the
+//          wave as its low 16 bits (wave sum
 //          < 2^22) and the rest (lane value < 2^23, wave sum < 2^29); a
 //          lane's sample sum is <= 65 * 65535 < 2^23 (wave sum < 2^29).
 // Each wave64 total therefore fits uint32; the workgroup adds its waves in
@@ -65,6 +70,7 @@ static_assert(kIters % kInFlight == 0, "whole load groups");
 static_assert((kIters * 16 + 1) * 255ull * 255ull * 64ull < (1ull << 32), "8-bit wave budget");
 static_assert(((kIters * 8 + 1) * 0xffffffffull >> 16) * 64ull < (1ull << 32), "16-bit wave budget");
 static_assert((kIters * 8 + 1) * 65535ull * 64ull < (1ull << 32), "16-bit sample-sum budget");
+static_assert((kIters * 8 + 1) * 0xffffffffull < (1ull << 53), "16-bit lane sums exact in binary64");
 
 // ------------------------------------------------------------------ stage 1
 template <int kBytes, class Acc>
@@ -153,10 +159,10 @@ __global__ __launch_bounds__(kThreads) void stage1_u16(const void *ref, const vo
     Acc a;
     accumulate_chunk<2>(a, ref, dist, pixels, chunk, frame);
     // each 64-bit lane sum crosses the wave as (low 16 bits, the rest)
-    const uint32_t v[8] = {static_cast<uint32_t>(a.noise & 0xffffu), static_cast<uint32_t>(a.noise >> 16),
-                           a.r1, a.d1,
-                           static_cast<uint32_t>(a.r2 & 0xffffu), static_cast<uint32_t>(a.r2 >> 16),
-                           static_cast<uint32_t>(a.d2 & 0xffffu), static_cast<uint32_t>(a.d2 >> 16)};
+    const uint64_t n = lane_total(a.noise), r2 = lane_total(a.r2), d2 = lane_total(a.d2);
+    const uint32_t v[8] = {static_cast<uint32_t>(n & 0xffffu), static_cast<uint32_t>(n >> 16), a.r1, a.d1,
+                           static_cast<uint32_t>(r2 & 0xffffu), static_cast<uint32_t>(r2 >> 16),
+                           static_cast<uint32_t>(d2 & 0xffffu), static_cast<uint32_t>(d2 >> 16)};
     uint64_t s[8];
     workgroup_sums(v, s);
     const uint64_t rec[kSums] = {s[0] + (s[1] << 16), s[2], s[3], s[4] + (s[5] << 16),

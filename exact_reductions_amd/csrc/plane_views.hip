@@ -37,12 +37,14 @@ constexpr int kTileVecs = 2048;  // 16-byte vectors of each plane per tile, at m
 // A lane takes at most kTileVecs / kThreads = 8 vectors and kTileVecs * V /
 // kThreads samples (64 at two bytes, 128 at one):
 //  8 bits: a lane's sum r^2 <= (8*16 + 128) * 255^2 < 2^24, wave sum < 2^30;
-// 16 bits: a lane's 64-bit sum of squares <= (8*8 + 64) * (2^32 - 1) < 2^39,
-//          crossing the wave as its low 16 bits and the rest (< 2^23, wave
+// 16 bits: a lane's sum of squares <= (8*8 + 64) * (2^32 - 1) < 2^39 (exact
+//          in binary64 at every step), crossing the wave as its low 16 bits
+//          and the rest (< 2^23, wave
 //          sum < 2^29); a lane's sample sum <= 128 * 65535 < 2^23.
 static_assert((8 * 16 + 128) * 255ull * 255ull * 64ull < (1ull << 32), "8-bit wave budget");
 static_assert(((8 * 8 + 64) * 0xffffffffull >> 16) * 64ull < (1ull << 32), "16-bit wave budget");
 static_assert((8 * 8 + 64) * 65535ull * 64ull < (1ull << 32), "16-bit sample-sum budget");
+static_assert((8 * 8 + 64) * 0xffffffffull < (1ull << 53), "16-bit lane sums exact in binary64");
 static_assert(kTileVecs / kThreads == 8, "lane share");
 
 // ------------------------------------------------------- integer psnr terms
@@ -88,10 +90,10 @@ __device__ __forceinline__ void finish(const Acc8 &a, int64_t wg, uint64_t *part
 
 __device__ __forceinline__ void finish(const Acc16 &a, int64_t wg, uint64_t *part)
 {
-    const uint32_t v[8] = {static_cast<uint32_t>(a.noise & 0xffffu), static_cast<uint32_t>(a.noise >> 16),
-                           a.r1, a.d1,
-                           static_cast<uint32_t>(a.r2 & 0xffffu), static_cast<uint32_t>(a.r2 >> 16),
-                           static_cast<uint32_t>(a.d2 & 0xffffu), static_cast<uint32_t>(a.d2 >> 16)};
+    const uint64_t n = lane_total(a.noise), r2 = lane_total(a.r2), d2 = lane_total(a.d2);
+    const uint32_t v[8] = {static_cast<uint32_t>(n & 0xffffu), static_cast<uint32_t>(n >> 16), a.r1, a.d1,
+                           static_cast<uint32_t>(r2 & 0xffffu), static_cast<uint32_t>(r2 >> 16),
+                           static_cast<uint32_t>(d2 & 0xffffu), static_cast<uint32_t>(d2 >> 16)};
     uint64_t s[8];
     workgroup_sums(v, s);
     const uint64_t rec[kSums] = {s[0] + (s[1] << 16), s[2], s[3], s[4] + (s[5] << 16), s[6] + (s[7] << 16)};

@@ -48,13 +48,18 @@ __device__ __forceinline__ void add_dword(Acc8 &a, uint32_t r, uint32_t d)
 }
 
 // -------------------------------------------------------------- 16-bit terms
-// The float terms go into 64-bit integer lane accumulators (one
-// v_lshl_add_u64 per term on gfx950).  This is the leanest exact form:
-// fewer VALU operations per byte than adding the 16-bit halves separately,
-// which matters because the kernel runs near the HBM roofline, where power
-// (and with it the clock) depends on the work per byte.
+// The float terms go into binary64 lane accumulators: each term is an
+// integer below 2^32 and a lane adds at most a few hundred of them (the
+// kernels' budgets keep every lane sum below 2^53), so every partial sum is
+// an exact integer and the lane's total converts to uint64 without loss.
+// This is the leanest exact form on gfx950: a widening conversion and a
+// full-rate fp64 add per term, where a 64-bit integer add also needs a move
+// to zero the high half of each term's register pair, and adding the 16-bit
+// halves separately needs more.  That matters because the kernel runs near
+// the HBM roofline with its SIMDs also busy, where power (and with it the
+// clock) depends on the work per byte.
 struct Acc16 {
-    uint64_t noise = 0, r2 = 0, d2 = 0;
+    double noise = 0, r2 = 0, d2 = 0;
     uint32_t r1 = 0, d1 = 0;
 };
 
@@ -64,23 +69,25 @@ __device__ __forceinline__ void add_dword(Acc16 &a, uint32_t r, uint32_t d)
     const float r0 = static_cast<float>(r & 0xffffu), r1 = static_cast<float>(r >> 16);
     const float d0 = static_cast<float>(d & 0xffffu), d1 = static_cast<float>(d >> 16);
     // float_psnr: the square of the float difference [PSNR, Decision]
-    a.noise += float_square(r0 - d0);
-    a.noise += float_square(r1 - d1);
+    a.noise += static_cast<double>((r0 - d0) * (r0 - d0));
+    a.noise += static_cast<double>((r1 - d1) * (r1 - d1));
     // float_moment: the float squares of the samples [MOMENT, Decision]
-    a.r2 += float_square(r0);
-    a.r2 += float_square(r1);
-    a.d2 += float_square(d0);
-    a.d2 += float_square(d1);
+    a.r2 += static_cast<double>(r0 * r0);
+    a.r2 += static_cast<double>(r1 * r1);
+    a.d2 += static_cast<double>(d0 * d0);
+    a.d2 += static_cast<double>(d1 * d1);
     // the sample sums: r0 + r1 in one integer dot product
     const u16x2 ones = {1, 1};
     a.r1 = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, r), ones, a.r1, false);
     a.d1 = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, d), ones, a.d1, false);
 }
 
-// Acc16 that also ORs together the terms of each square sum, for their low
-// bits: a run of terms all multiples of 2^k rounds nowhere in a binade of
-// unit 2^k (the CPU-order mode reads this).
-struct Acc16Low : Acc16 {
+// Acc16's sums with uint64 lanes, and the OR of the terms of each square
+// sum, for their low bits: a run of terms all multiples of 2^k rounds
+// nowhere in a binade of unit 2^k (the CPU-order mode reads this).
+struct Acc16Low {
+    uint64_t noise = 0, r2 = 0, d2 = 0;
+    uint32_t r1 = 0, d1 = 0;
     uint32_t or_noise = 0, or_r2 = 0, or_d2 = 0;
 };
 
@@ -104,6 +111,10 @@ __device__ __forceinline__ void add_dword(Acc16Low &a, uint32_t r, uint32_t d)
     a.r1 = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, r), ones, a.r1, false);
     a.d1 = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, d), ones, a.d1, false);
 }
+
+// A lane's sum as uint64 (a double lane sum is an exact integer below 2^53).
+__device__ __forceinline__ uint64_t lane_total(double x) { return static_cast<uint64_t>(x); }
+__device__ __forceinline__ uint64_t lane_total(uint64_t x) { return x; }
 
 template <class Acc>
 __device__ __forceinline__ void add_vec(Acc &a, const u32x4 &r, const u32x4 &d)
