@@ -725,7 +725,8 @@ def main(argv=None):
     # events (a stamped dispatch costs the queue ~10 us of extra gaps, so
     # stamping every step would slow the stream it measures); other modes:
     # events around each group of steps
-    ev_begin = ({i: hip.create() for i in range(total) if i % STAMP_EVERY == STAMP_EVERY // 2}
+    phase = STAMP_EVERY // 2 if args.steps > STAMP_EVERY // 2 else 0
+    ev_begin = ({i: hip.create() for i in range(args.warmup, total) if (i - args.warmup) % STAMP_EVERY == phase}
                 if mode.per_step_events else {})
     ev_end = {i: hip.create() for i in ev_begin}
     ngroups = (total + group - 1) // group + 1
