@@ -474,6 +474,34 @@ __device__ __forceinline__ uint64_t wave_inclusive_then_total(uint64_t v, uint64
     return inc + below;
 }
 
+// wave_inclusive_then_total for N values at once, with one barrier between
+// the waves' totals and their use (each value has its own LDS row).
+template <int N>
+__device__ __forceinline__ void wave_inclusive_then_total_n(const uint64_t (&v)[N], uint64_t (*lds_totals)[kThreads / 64],
+                                                            uint64_t (&incl)[N], uint64_t (&total)[N])
+{
+    const int wave = threadIdx.x / 64;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        incl[j] = wave_scan64(v[j]);
+        if ((threadIdx.x & 63) == 63)
+            lds_totals[j][wave] = incl[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        uint64_t below = 0;
+        total[j] = 0;
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w) {
+            const uint64_t x = lds_totals[j][w];
+            below += w < wave ? x : 0;
+            total[j] += x;
+        }
+        incl[j] += below;
+    }
+}
+
 struct ChunkCase {
     bool queued, chunk_only;
     int e;
@@ -534,9 +562,10 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int6
             sq[kk][c] = x[record_field(kk)];
         low_bits[c] = static_cast<uint16_t>(x[kSums]);
     }
+    wave_inclusive_then_total_n<kSums>(local, lds, run, total);
 #pragma unroll
     for (int j = 0; j < kSums; ++j)
-        run[j] = wave_inclusive_then_total(local[j], lds[j], total[j]) - local[j];
+        run[j] -= local[j];
     if (t == 0) {
         // the exact sums (stage 2's results), then the CPU's where they are
         // the exact ones
