@@ -610,7 +610,7 @@ def make_mode(args, vqx, L, hip, np, torch, dev, st, wl, ref_np, dist_np, planes
                       else vqx.plane_stats_cpu_order_workspace_bytes(w, h, bpc, nframes))
         m.metric = METRIC_CPU_ORDER
         m.kernel = "cpu_order_step"
-        m.kernel_label = ("cpu_order_step (stage1_u16, cpu_order_prefix, cpu_order_maps, cpu_order_compose, "
+        m.kernel_label = ("cpu_order_step (stage1_u16, cpu_order_prefix, cpu_order_maps, "
                           "cpu_order_walk)")
         m.sources = CPU_ORDER_SOURCES
         m.alg_bytes = wl.bytes_per_frame * nframes + past53_bytes(ref_np, dist_np, bpc)

@@ -41,7 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "exact_reductions_amd", "csrc")
 STAGE1_SOURCES = [os.path.join(CSRC, f) for f in ("plane_stats.hip", "reduce.h")]
 CPU_ORDER_SOURCES = STAGE1_SOURCES + [os.path.join(CSRC, "cpu_order.hip")]
-CPU_ORDER_KERNELS = ("stage1_u16", "cpu_order_prefix", "cpu_order_maps", "cpu_order_compose", "cpu_order_walk")
+CPU_ORDER_KERNELS = ("stage1_u16", "cpu_order_prefix", "cpu_order_maps", "cpu_order_walk")
 VIEW_SOURCES = [os.path.join(CSRC, f) for f in ("plane_views.hip", "reduce.h")]
 VIEW_KERNELS = ("view_stage1", "view_combine")
 PLANES_KERNELS = ("views_stage1", "views_combine")
@@ -84,7 +84,7 @@ def rows(path):
 
 def short(name: str) -> str:
     for k in ("stage1_u16", "stage1_u8", "stage2_combine", "bitwise_not", "cpu_order_prefix",
-              "cpu_order_maps", "cpu_order_compose", "cpu_order_walk", "views_stage1", "views_combine",
+              "cpu_order_maps", "cpu_order_walk", "views_stage1", "views_combine",
               "view_stage1", "view_combine", "read_probe"):
         if k in name:
             return k

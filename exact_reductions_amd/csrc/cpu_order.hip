@@ -1158,6 +1158,8 @@ __device__ __forceinline__ uint64_t walk_chunk(uint64_t S, const Planes &P, cons
 //    cannot round), or from the block's chunk maps; flags 0 (no map) unless
 //    every part holds a map for one binade.  Chunks without vectors count
 //    as the identity.
+// The walk kernel's waves write them (one wave per block) before its first
+// wave walks the frame.
 constexpr int kCompact = 4;
 constexpr int kBlockChunks = 64;
 
@@ -1254,27 +1256,6 @@ __device__ __forceinline__ void compose_block(const void *ref, const void *dist,
     }
 }
 
-// One wave per (frame, square sum past 2^53, block); two-byte samples only.
-__global__ __launch_bounds__(kThreads) void cpu_order_compose(const void *ref, const void *dist, int64_t pixels,
-                                                              int chunks, int nframes, const uint64_t *rec,
-                                                              const uint64_t *totals, const uint64_t *maps,
-                                                              uint64_t *cmaps, uint64_t *bmaps)
-{
-    const int blocks = frame_blocks(chunks);
-    const int64_t w = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + threadIdx.x / 64;
-    const int64_t fk = w / blocks;  // frame * kSquares + kk
-    if (fk >= static_cast<int64_t>(nframes) * kSquares || totals[fk] < kTwo53)
-        return;
-    const int64_t frame = fk / kSquares;
-    const int kk = static_cast<int>(fk - frame * kSquares);
-    const int block = static_cast<int>(w - fk * blocks);
-    switch (kk) {
-    case kSqNoise: compose_block<kSqNoise>(ref, dist, pixels, chunks, rec, maps, frame, block, cmaps, bmaps); break;
-    case kSqRef: compose_block<kSqRef>(ref, dist, pixels, chunks, rec, maps, frame, block, cmaps, bmaps); break;
-    default: compose_block<kSqDist>(ref, dist, pixels, chunks, rec, maps, frame, block, cmaps, bmaps); break;
-    }
-}
-
 // ---------------------------------------------------------- 4b. the walk
 // The 64 chunks of one block, chunk b*64 + j in lane j, from S, from their
 // compact records; a chunk where they do not apply is walked slab by slab.
@@ -1307,7 +1288,7 @@ __device__ __forceinline__ void walk_frame(const void *ref, const void *dist, in
                                            const uint64_t *maps, const uint64_t *cmaps, const uint64_t *bmaps,
                                            int64_t frame, uint64_t *dst, u32x4 *lds, const VecMap &vmap)
 {
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     // (mapped planes hold whole vectors only: no head or tail samples)
     const FrameEdges fe = frame_edges<KK>(ref, dist, pixels, frame);
     // the head comes first in raster order; it is far below 2^53, so exact
@@ -1342,12 +1323,32 @@ __device__ __forceinline__ void walk_frame(const void *ref, const void *dist, in
         *dst = S;
 }
 
-// One wave per (frame, square sum); two-byte samples only.  Sums that stay
-// below 2^53 were written by the prefix scan.
-__global__ __launch_bounds__(64) void cpu_order_walk(const void *ref, const void *dist, int64_t pixels, int chunks,
-                                                     const uint64_t *totals, const uint64_t *maps,
-                                                     const uint64_t *cmaps, const uint64_t *bmaps,
-                                                     uint64_t *out_cpu_noise, uint64_t *out_cpu_moments, VecMap vmap)
+// One workgroup per (frame, square sum); two-byte samples only.  Sums that
+// stay below 2^53 were written by the prefix scan.  The workgroup's waves
+// first compose the frame's blocks (block b in wave b % kWalkWaves); after
+// the barrier that makes their records visible, wave 0 walks the frame.
+constexpr int kWalkWaves = 8;
+
+template <int KK>
+__device__ __forceinline__ void compose_then_walk(const void *ref, const void *dist, int64_t pixels, int chunks,
+                                                  const uint64_t *rec, const uint64_t *maps, uint64_t *cmaps,
+                                                  uint64_t *bmaps, int64_t frame, uint64_t *dst, u32x4 *lds,
+                                                  const VecMap &vmap)
+{
+    const int wave = threadIdx.x / 64;
+    for (int b = wave; b < frame_blocks(chunks); b += kWalkWaves)
+        compose_block<KK>(ref, dist, pixels, chunks, rec, maps, frame, b, cmaps, bmaps);
+    __syncthreads();
+    if (wave == 0)
+        walk_frame<KK>(ref, dist, pixels, chunks, maps, cmaps, bmaps, frame, dst, lds, vmap);
+}
+
+__global__ __launch_bounds__(64 * kWalkWaves) void cpu_order_walk(const void *ref, const void *dist, int64_t pixels,
+                                                                  int chunks, const uint64_t *rec,
+                                                                  const uint64_t *totals, const uint64_t *maps,
+                                                                  uint64_t *cmaps, uint64_t *bmaps,
+                                                                  uint64_t *out_cpu_noise, uint64_t *out_cpu_moments,
+                                                                  VecMap vmap)
 {
     __shared__ u32x4 lds[2 * kSlabVectors];  // a slab of each plane, for `consecutive`
     const int64_t frame = blockIdx.x / kSquares;
@@ -1356,15 +1357,16 @@ __global__ __launch_bounds__(64) void cpu_order_walk(const void *ref, const void
         return;
     switch (kk) {
     case kSqNoise:
-        walk_frame<kSqNoise>(ref, dist, pixels, chunks, maps, cmaps, bmaps, frame, &out_cpu_noise[frame], lds, vmap);
+        compose_then_walk<kSqNoise>(ref, dist, pixels, chunks, rec, maps, cmaps, bmaps, frame, &out_cpu_noise[frame],
+                                    lds, vmap);
         break;
     case kSqRef:
-        walk_frame<kSqRef>(ref, dist, pixels, chunks, maps, cmaps, bmaps, frame, &out_cpu_moments[4 * frame + 2],
-                           lds, vmap);
+        compose_then_walk<kSqRef>(ref, dist, pixels, chunks, rec, maps, cmaps, bmaps, frame,
+                                  &out_cpu_moments[4 * frame + 2], lds, vmap);
         break;
     default:
-        walk_frame<kSqDist>(ref, dist, pixels, chunks, maps, cmaps, bmaps, frame, &out_cpu_moments[4 * frame + 3],
-                            lds, vmap);
+        compose_then_walk<kSqDist>(ref, dist, pixels, chunks, rec, maps, cmaps, bmaps, frame,
+                                   &out_cpu_moments[4 * frame + 3], lds, vmap);
         break;
     }
 }
@@ -1479,14 +1481,9 @@ hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, cons
     err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    const int64_t compose_waves = static_cast<int64_t>(g.nframes) * kSquares * frame_blocks(g.chunks);
-    cpu_order_compose<<<dim3(static_cast<unsigned>((compose_waves + kThreads / 64 - 1) / (kThreads / 64))), kThreads,
-                        0, stream>>>(ref, dist, g.pixels, g.chunks, g.nframes, rec, totals, maps, cmaps, bmaps);
-    err = hipGetLastError();
-    if (err != hipSuccess)
-        return err;
-    cpu_order_walk<<<dim3(nf * kSquares), 64, 0, stream>>>(ref, dist, g.pixels, g.chunks, totals, maps, cmaps,
-                                                           bmaps, out_cpu_noise, out_cpu_moments, map);
+    cpu_order_walk<<<dim3(nf * kSquares), 64 * kWalkWaves, 0, stream>>>(ref, dist, g.pixels, g.chunks, rec, totals,
+                                                                        maps, cmaps, bmaps, out_cpu_noise,
+                                                                        out_cpu_moments, map);
     return hipGetLastError();
 }
 
