@@ -44,6 +44,11 @@ __global__ __launch_bounds__(kThreads) void stage1_u16_mapped(const void *ref, c
     const int64_t vb = frame * (pixels / 8), ve = vb + pixels / 8;
     const int64_t cb = vb + static_cast<int64_t>(chunk) * kChunkVectors;
     const int64_t ce = cb + kChunkVectors < ve ? cb + kChunkVectors : ve;
+    // map_vec written out for this frame: vector v of the frame's contiguous
+    // order lies in row y = (r * magic) >> shift, r = v - vb < 2^22, and
+    // magic < 2^24, so the product fits 64 bits from 32-bit factors
+    const int64_t fr = frame * M.pad_frame_r, fd = frame * M.pad_frame_d;
+    const uint32_t magic = static_cast<uint32_t>(M.magic);
     Acc16Low a;
     if (cb < ce) {
 #pragma unroll 1
@@ -52,12 +57,13 @@ __global__ __launch_bounds__(kThreads) void stage1_u16_mapped(const void *ref, c
             bool ok[kInFlight];
 #pragma unroll
             for (int u = 0; u < kInFlight; ++u) {
-                const int64_t v = cb + threadIdx.x + static_cast<int64_t>(i + u) * kThreads;
-                ok[u] = v < ce;
-                int64_t vr, vd;
-                map_vec(M, frame, ok[u] ? v : cb, vr, vd);
-                x[u] = __builtin_nontemporal_load(R + vr);
-                y[u] = __builtin_nontemporal_load(D + vd);
+                const int64_t v0 = cb + threadIdx.x + static_cast<int64_t>(i + u) * kThreads;
+                ok[u] = v0 < ce;
+                const int64_t v = ok[u] ? v0 : cb;
+                const uint32_t r = static_cast<uint32_t>(v - vb);
+                const int64_t row = static_cast<int64_t>((static_cast<uint64_t>(r) * magic) >> M.shift);
+                x[u] = __builtin_nontemporal_load(R + (v + fr + row * M.pad_row_r));
+                y[u] = __builtin_nontemporal_load(D + (v + fd + row * M.pad_row_d));
             }
 #pragma unroll
             for (int u = 0; u < kInFlight; ++u) {

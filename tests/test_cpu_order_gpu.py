@@ -308,6 +308,27 @@ def test_view_form_in_place_small(bpc, w, h, x0):
     _in_place_case(big_r[sr], big_d[sd], R, D, bpc)
 
 
+def test_view_form_in_place_15bit_past53():
+    """A 4096x4096 15-bit frame pair (bright, a few dark odd samples) inside
+    planes with 64 samples of row padding: the squares' sums pass 2^53 units
+    of 1/s^2, read in place."""
+    rng = np.random.default_rng(1515)
+    h = w = 4096
+    planes = []
+    for _ in range(2):
+        x = rng.integers(28000, 32767, size=(1, h, w), endpoint=True)
+        dark = rng.random((1, h, w)) < 0.02
+        x = np.where(dark, rng.integers(0, 2047, size=(1, h, w), endpoint=True) | 1, x).astype(np.uint16)
+        big = np.zeros((1, h, w + 64), dtype=np.uint16)
+        big[:, :, 32:32 + w] = x
+        planes.append(big)
+    sl = (slice(None), slice(None), slice(32, 32 + w))
+    o2 = oracle.exact_batch_sums(np.ascontiguousarray(planes[0][sl]), np.ascontiguousarray(planes[1][sl]))
+    assert o2[0][3] >= 2**53 and o2[0][4] >= 2**53
+    _in_place_case(planes[0][sl], planes[1][sl], torch.from_numpy(planes[0]).cuda()[sl],
+                   torch.from_numpy(planes[1]).cuda()[sl], 15)
+
+
 def test_view_form_unaligned_gathered():
     """A view 4 samples in, and one of width 100: gathered, same results."""
     rng = np.random.default_rng(7)
