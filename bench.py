@@ -106,7 +106,7 @@ def parse_args(argv=None):
                         "workspace): with more than one, consecutive steps overlap as in a pipeline of "
                         "batches, and a kernel's timed duration includes the overlap")
     p.add_argument("--pitch", type=int, default=0, metavar="SAMPLES",
-                   help="cpu-order and psnr-int modes: keep the planes resident with rows of SAMPLES samples "
+                   help="exact, cpu-order and psnr-int modes: keep the planes resident with rows of SAMPLES samples "
                         "(>= w; the frame inside the first w of each row) and reduce them through the "
                         "plane-view entry points (default: contiguous)")
     p.add_argument("--frames-per-upload", type=int, default=4,
@@ -595,8 +595,16 @@ def make_mode(args, vqx, L, hip, np, torch, dev, st, wl, ref_np, dist_np, planes
     w, h, bpc, nframes = wl.w, wl.h, wl.bpc, wl.nframes
     m = Mode()
     m.name = args.mode
-    m.per_step_events = args.mode == "exact"
-    if args.mode == "exact":
+    m.per_step_events = args.mode == "exact" and not args.pitch
+    if args.mode == "exact" and args.pitch:
+        m.width = 5 * nframes
+        m.ws_bytes = vqx.plane_view_workspace_bytes(w, h, bpc, nframes)
+        m.metric = METRIC
+        m.kernel = "view_step"
+        m.kernel_label = "view_step (view_stage1 exact sums, view_combine)"
+        m.sources = VIEW_SOURCES
+        m.alg_bytes = wl.bytes_per_frame * nframes
+    elif args.mode == "exact":
         m.width = 5 * nframes
         m.ws_bytes = vqx.plane_stats_workspace_bytes(w, h, bpc, nframes)
         m.metric = METRIC
@@ -683,8 +691,8 @@ def main(argv=None):
     if args.pitch == w:
         args.pitch = 0
     if args.pitch:
-        if args.mode not in ("cpu-order", "psnr-int") or args.pitch < w:
-            print("--pitch needs --mode cpu-order or psnr-int and a pitch >= w", file=sys.stderr)
+        if args.mode not in ("exact", "cpu-order", "psnr-int") or args.pitch < w:
+            print("--pitch needs --mode exact, cpu-order or psnr-int and a pitch >= w", file=sys.stderr)
             return 2
 
         def pitched(x):
@@ -755,7 +763,10 @@ def main(argv=None):
         o = sums_dev[s]
         st = sts[i % nst]
         ws = wss[i % nst]
-        if args.mode == "exact":
+        if args.mode == "exact" and args.pitch:
+            rc = L.vqx_plane_stats_view_ws(r.data_ptr(), rs, fs, d.data_ptr(), rs, fs, w, h, bpc, nframes,
+                                           o, o + itemsize * nframes, ws.data_ptr(), ws_bytes, st)
+        elif args.mode == "exact":
             rc = L.vqx_plane_stats_batch_ws_timed(r.data_ptr(), d.data_ptr(), w, h, bpc, nframes,
                                                   o, o + itemsize * nframes, ws.data_ptr(), ws_bytes,
                                                   st, ev_begin.get(i), ev_end.get(i))
@@ -868,7 +879,7 @@ def main(argv=None):
     bytes_per_step = ref_np[0].size * wl.bytes_per_sample * 2 * nframes
     mean_ms = statistics.fmean(step_ms)
     read_ceiling = None
-    if args.mode == "exact":
+    if args.mode == "exact" and not args.pitch:
         read_ceiling = measure_read_ceiling(L, hip, torch, bufs, wl, ws, ws_bytes, st, mean_ms,
                                             mode.alg_bytes, min(args.steps, 200))
 
