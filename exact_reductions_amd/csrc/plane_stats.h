@@ -184,4 +184,11 @@ hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, cons
 hipError_t launch_stage1_mapped(const Geometry &g, const void *ref, const void *dist, uint64_t *partials,
                                 const VecMap &map, hipStream_t stream);
 
+// The five exact sums of views whose rows are whole 16-byte aligned vectors
+// of two-byte samples: stage 1 with its vectors found through `map`, then
+// the per-frame combine; `partials` as for launch_plane_stats.
+hipError_t launch_plane_stats_mapped(const Geometry &g, const void *ref, const void *dist, uint64_t *out_noise,
+                                     uint64_t *out_moments, uint64_t *partials, const VecMap &map,
+                                     hipStream_t stream);
+
 }  // namespace vqx

@@ -1,4 +1,5 @@
-// The CPU-order form of stage 1 over plane views read in place, for gfx950.
+// Stage 1 over plane views read in place, for gfx950: the exact sums, and
+// the CPU-order form of them.
 //
 // Sources (web pages, cited by title and section):
 //   [PSNR]   "ADR-1440: float_psnr_hip adds its squared differences as
@@ -11,10 +12,14 @@
 // frames stored contiguously.  Where the view's rows are whole 16-byte
 // aligned vectors of two-byte samples, this kernel reads vector v of that
 // contiguous order where the view keeps it (map_vec) and writes the records
-// and low bits the contiguous CPU-order stage 1 writes for the same samples:
-// the same terms in the same lane accumulators and workgroup sums.
+// the contiguous stage 1 writes for the same samples -- with the low bits of
+// the terms in the CPU-order form -- from the same terms in the same lane
+// accumulators and workgroup sums.  Integer sums make the records, and so
+// the frame sums, those of the contiguous planes.
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "plane_stats.h"
 #include "reduce.h"
@@ -29,10 +34,12 @@ constexpr int kLaneIters = kChunkVectors / kThreads;  // vectors per lane per pl
 constexpr int kInFlight = 4;                          // vectors of each plane loaded before use
 static_assert(kLaneIters % kInFlight == 0, "whole load groups");
 
-// The CPU-order form of stage 1 over plane views whose rows are whole
-// 16-byte aligned vectors (two-byte samples, so frames hold no partial
-// vectors): the same chunks, terms, records and low bits as
-// stage1_u16<true>, each vector found through the VecMap.
+// Stage 1 over plane views whose rows are whole 16-byte aligned vectors
+// (two-byte samples, so frames hold no partial vectors): the same chunks,
+// terms and records as stage1_u16<kLowBitsOut>, each vector found through
+// the VecMap; kLowBitsOut: also the low bits of the terms and zero queue
+// lengths, for the CPU-order form.
+template <bool kLowBitsOut>
 __global__ __launch_bounds__(kThreads) void stage1_u16_mapped(const void *ref, const void *dist, int64_t pixels,
                                                               int chunks, uint64_t *part, VecMap M)
 {
@@ -49,7 +56,7 @@ __global__ __launch_bounds__(kThreads) void stage1_u16_mapped(const void *ref, c
     // magic < 2^24, so the product fits 64 bits from 32-bit factors
     const int64_t fr = frame * M.pad_frame_r, fd = frame * M.pad_frame_d;
     const uint32_t magic = static_cast<uint32_t>(M.magic);
-    Acc16Low a;
+    typename std::conditional<kLowBitsOut, Acc16Low, Acc16>::type a;
     if (cb < ce) {
 #pragma unroll 1
         for (int i = 0; i < kLaneIters; i += kInFlight) {
@@ -72,22 +79,31 @@ __global__ __launch_bounds__(kThreads) void stage1_u16_mapped(const void *ref, c
             }
         }
     }
-    const uint32_t v[8] = {static_cast<uint32_t>(a.noise & 0xffffu), static_cast<uint32_t>(a.noise >> 16),
-                           a.r1, a.d1,
-                           static_cast<uint32_t>(a.r2 & 0xffffu), static_cast<uint32_t>(a.r2 >> 16),
-                           static_cast<uint32_t>(a.d2 & 0xffffu), static_cast<uint32_t>(a.d2 >> 16)};
+    const uint64_t n = lane_total(a.noise), r2 = lane_total(a.r2), d2 = lane_total(a.d2);
+    const uint32_t v[8] = {static_cast<uint32_t>(n & 0xffffu), static_cast<uint32_t>(n >> 16), a.r1, a.d1,
+                           static_cast<uint32_t>(r2 & 0xffffu), static_cast<uint32_t>(r2 >> 16),
+                           static_cast<uint32_t>(d2 & 0xffffu), static_cast<uint32_t>(d2 >> 16)};
     uint64_t s[8];
     workgroup_sums(v, s);
     const uint64_t rec[kSums] = {s[0] + (s[1] << 16), s[2], s[3], s[4] + (s[5] << 16), s[6] + (s[7] << 16)};
     write_record(part, wg, rec);
-    const uint32_t low = workgroup_or((a.or_noise & 15u) | ((a.or_r2 & 15u) << 4) | ((a.or_d2 & 15u) << 8));
-    if (threadIdx.x == 0) {
-        part[wg * kRecordStride + kLowBits] = low;
-        if (wg == 0) {
-            part[kQueueCounts] = 0;
-            part[kQueueCounts + 1] = 0;
+    if constexpr (kLowBitsOut) {
+        const uint32_t low = workgroup_or((a.or_noise & 15u) | ((a.or_r2 & 15u) << 4) | ((a.or_d2 & 15u) << 8));
+        if (threadIdx.x == 0) {
+            part[wg * kRecordStride + kLowBits] = low;
+            if (wg == 0) {
+                part[kQueueCounts] = 0;
+                part[kQueueCounts + 1] = 0;
+            }
         }
     }
+}
+
+// One workgroup per frame adds the frame's records in uint64.
+__global__ __launch_bounds__(kThreads) void mapped_combine(const uint64_t *part, int chunks, uint64_t *out_noise,
+                                                           uint64_t *out_moments)
+{
+    combine_frame(part, chunks, blockIdx.x, out_noise, out_moments);
 }
 
 }  // namespace
@@ -95,8 +111,22 @@ __global__ __launch_bounds__(kThreads) void stage1_u16_mapped(const void *ref, c
 hipError_t launch_stage1_mapped(const Geometry &g, const void *ref, const void *dist, uint64_t *partials,
                                 const VecMap &map, hipStream_t stream)
 {
-    stage1_u16_mapped<<<dim3(static_cast<unsigned>(g.workgroups)), kThreads, 0, stream>>>(ref, dist, g.pixels,
-                                                                                        g.chunks, partials, map);
+    stage1_u16_mapped<true><<<dim3(static_cast<unsigned>(g.workgroups)), kThreads, 0, stream>>>(
+        ref, dist, g.pixels, g.chunks, partials, map);
+    return hipGetLastError();
+}
+
+hipError_t launch_plane_stats_mapped(const Geometry &g, const void *ref, const void *dist, uint64_t *out_noise,
+                                     uint64_t *out_moments, uint64_t *partials, const VecMap &map,
+                                     hipStream_t stream)
+{
+    stage1_u16_mapped<false><<<dim3(static_cast<unsigned>(g.workgroups)), kThreads, 0, stream>>>(
+        ref, dist, g.pixels, g.chunks, partials, map);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    mapped_combine<<<dim3(static_cast<unsigned>(g.nframes)), kThreads, 0, stream>>>(partials, g.chunks, out_noise,
+                                                                                   out_moments);
     return hipGetLastError();
 }
 

@@ -565,8 +565,22 @@ int vqx_plane_stats_view_ws(const void *ref, int64_t ref_row_stride, int64_t ref
         return rc;
     const vqx::PlaneView R{ref, ref_row_stride, ref_frame_stride};
     const vqx::PlaneView D{dist, dist_row_stride, dist_frame_stride};
-    if (vqx::launch_view_stats(g, R, D, out_noise, out_moments, static_cast<uint64_t *>(workspace),
-                               static_cast<hipStream_t>(stream)) != hipSuccess) {
+    hipError_t err;
+    const vqx::Geometry cg = vqx::make_geometry(w, h, bpc, nframes);
+    if (rows_of_vectors(ref, ref_row_stride, ref_frame_stride, w, bpc) &&
+        rows_of_vectors(dist, dist_row_stride, dist_frame_stride, w, bpc) &&
+        check_batch(w, h, bpc, nframes) == VQX_OK && workspace_bytes >= cg.workspace_bytes) {
+        // rows of whole vectors: the contiguous chunks, each vector found in the views
+        err = vqx::launch_plane_stats_mapped(cg, ref, dist, out_noise, out_moments,
+                                             static_cast<uint64_t *>(workspace),
+                                             vqx::make_vec_map(w, h, ref_row_stride, ref_frame_stride,
+                                                               dist_row_stride, dist_frame_stride),
+                                             static_cast<hipStream_t>(stream));
+    } else {
+        err = vqx::launch_view_stats(g, R, D, out_noise, out_moments, static_cast<uint64_t *>(workspace),
+                                     static_cast<hipStream_t>(stream));
+    }
+    if (err != hipSuccess) {
         (void)hipGetLastError();
         return VQX_E_HIP;
     }

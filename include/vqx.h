@@ -295,7 +295,12 @@ int vqx_conclude_batch(const uint64_t *noise, const uint64_t *moments, int w, in
  * (64 bytes per frame and tile).  Host-only. */
 int vqx_plane_view_workspace_bytes(int w, int h, int bpc, int nframes, size_t *bytes);
 
-/* The five sums of vqx_plane_stats_batch_ws, over plane views. */
+/* The five sums of vqx_plane_stats_batch_ws, over plane views.  Where both
+ * views hold two-byte samples (bpc 9..16) in rows of whole 16-byte vectors
+ * (w, both row strides and both frame strides multiples of 8 samples, both
+ * bases 16-byte aligned) they are read with the contiguous form's chunks,
+ * each vector found in place, at the contiguous form's speed; other views
+ * are read in tiles of whole rows.  The sums are the same either way. */
 int vqx_plane_stats_view_ws(const void *ref, int64_t ref_row_stride, int64_t ref_frame_stride,
                             const void *dist, int64_t dist_row_stride, int64_t dist_frame_stride,
                             int w, int h, int bpc, int nframes, uint64_t *out_noise,
