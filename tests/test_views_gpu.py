@@ -205,6 +205,47 @@ def test_outputs_written_not_accumulated():
         assert int(o[5 * f + k]) == oracle.int_noise(ref[k], dist[k])
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_random_views(seed):
+    """Seeded random views: depth, size, pitch, offsets, frame count and
+    frame stride (0 or the buffer's), half of them rows of whole aligned
+    vectors (read with the contiguous chunks at two-byte samples), half at
+    any offset (read in row tiles); against the oracle and the contiguous
+    entry point on the copied samples."""
+    rng = np.random.default_rng(7100 + seed)
+    aligned = seed % 2 == 0
+    bpc = int(rng.integers(9, 17)) if aligned else int(rng.integers(8, 17))
+    if aligned:
+        w = 8 * int(rng.integers(1, 500))
+        pitch = w + 8 * int(rng.integers(0, 12))
+        x0 = 8 * int(rng.integers(0, 4))
+    else:
+        w = int(rng.integers(1, 3000))
+        pitch = w + int(rng.integers(0, 40))
+        x0 = int(rng.integers(0, 20))
+    h = int(rng.integers(1, 300))
+    y0 = int(rng.integers(0, 4))
+    f = int(rng.integers(1, 5))
+    same_plane = bool(rng.integers(0, 4) == 0)
+    hi = (1 << bpc) - 1
+    fb = 1 if same_plane else f
+    big_r = _rand(rng, (fb, h + y0 + 1, pitch + x0), bpc, lo=hi // 3)
+    noise = rng.integers(-300, 300, size=big_r.shape, endpoint=True)
+    big_d = np.clip(big_r.astype(np.int64) + noise, 0, hi).astype(_dtype(bpc))
+    sl = (slice(None), slice(y0, y0 + h), slice(x0, x0 + w))
+    R, D = torch.from_numpy(big_r).cuda()[sl], torch.from_numpy(big_d).cuda()[sl]
+    rn, dn = big_r[sl], big_d[sl]
+    if same_plane:
+        R, D = R.expand(f, h, w), D.expand(f, h, w)
+        rn, dn = np.broadcast_to(rn, (f, h, w)), np.broadcast_to(dn, (f, h, w))
+    label = f"seed {seed}: bpc {bpc} {w}x{h}x{f} pitch {pitch} at ({x0},{y0}) same_plane {same_plane}"
+    noise_v, moments_v, _ = check_views(rn, dn, R, D, bpc, label)
+    n2, m2 = vqx.plane_stats_batch(torch.from_numpy(np.ascontiguousarray(rn)).cuda(),
+                                   torch.from_numpy(np.ascontiguousarray(dn)).cuda(), bpc)
+    torch.cuda.synchronize()
+    assert (n2.cpu().numpy() == noise_v).all() and (m2.cpu().numpy() == moments_v).all(), label
+
+
 # ------------------------------------------------------------ several planes
 def check_planes(pairs_np, pairs_dev, bpc, label=""):
     """pairs_np: [(ref [F][h][w], dist)] numpy views of what pairs_dev select.
