@@ -42,15 +42,17 @@
 //     slabs with ties chain their terms and compose the lanes' maps in
 //     order.  A fixed grid of waves shares out the queued slabs, each wave
 //     reading its next slab while mapping the current one;
-//  4. cpu_order_walk, one wave per frame and sum past 2^53, walks the frame
-//     in order with the running value S, 64 chunks at a time: a block that
-//     stays below 2^53 adds exactly; a block whose chunk maps (composed from
-//     their slab maps) are all for S's binade is composed into one map and
-//     applied if S stays in the binade; otherwise chunk by chunk, then slab
-//     by slab, then 64 vectors at a time with maps made on the spot for S's
-//     binade and the next, and only within a single vector term by term.
-//     Every step is checked against S itself, so a prediction only decides
-//     how fast the walk is, never what it returns.
+//  4. cpu_order_walk, one workgroup per frame and sum past 2^53: its waves
+//     first write a compact record per chunk (its map, its own or composed
+//     from its slab maps, and its total) and per block of 64 chunks (their
+//     composed map and total); then wave 0 walks the frame in order with
+//     the running value S: a block that stays below 2^53 adds exactly; a
+//     block whose map is for S's binade is applied if S stays in the binade;
+//     otherwise chunk by chunk, then slab by slab, then 64 groups of 32
+//     consecutive terms with maps made on the spot for S's binade and the
+//     next, and within the group where S crosses, term by term.  Every step
+//     is checked against S itself, so a prediction only decides how fast
+//     the walk is, never what it returns.
 //
 // One-byte samples (8 bits per component) never get there: their squares
 // are below 2^16 and a frame has at most 2^25 samples, so every sum stays
