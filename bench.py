@@ -77,6 +77,39 @@ STAGE1_SOURCES = [os.path.join(CSRC, f) for f in ("plane_stats.hip", "reduce.h")
 CPU_ORDER_SOURCES = STAGE1_SOURCES + [os.path.join(CSRC, "cpu_order.hip")]
 VIEW_SOURCES = [os.path.join(CSRC, f) for f in ("plane_views.hip", "reduce.h")]
 HOST_SOURCES = STAGE1_SOURCES + [os.path.join(CSRC, "host_stream.hip")]
+MAPPED_SOURCES = [os.path.join(CSRC, f) for f in ("stage1_mapped.hip", "reduce.h")]
+CPU_ORDER_KERNELS = ("stage1_u16", "cpu_order_prefix", "cpu_order_maps", "cpu_order_walk")
+
+
+def step_plan(mode: str, wl, pitch: int = 0):
+    """(kernel, step kernels, sources) of a bench mode: the name of the timed
+    step's dominant kernel (or of the whole step), the kernels one step runs
+    as rocprofv3 names them, and the sources they are built from.  Planes
+    with a pitch (rows of ``pitch`` samples) go through the view entry
+    points, which read rows of whole aligned 16-byte vectors of two-byte
+    samples in place with the contiguous chunks ("mapped") and gather or tile
+    other layouts."""
+    mapped = bool(pitch) and wl.bpc > 8 and wl.w % 8 == 0 and pitch % 8 == 0
+    if mode == "exact" and pitch:
+        if mapped:
+            return "mapped_step", ("stage1_u16_mapped", "mapped_combine"), MAPPED_SOURCES
+        return "view_step", ("view_stage1", "view_combine"), VIEW_SOURCES
+    if mode == "exact":
+        k = "stage1_u8" if wl.bpc == 8 else "stage1_u16"
+        return k, (k,), STAGE1_SOURCES
+    if mode == "cpu-order":
+        if pitch and mapped:
+            return ("cpu_order_step", ("stage1_u16_mapped",) + CPU_ORDER_KERNELS[1:],
+                    CPU_ORDER_SOURCES + [os.path.join(CSRC, "stage1_mapped.hip")])
+        if pitch:
+            return ("cpu_order_step", ("gather_view",) + CPU_ORDER_KERNELS,
+                    CPU_ORDER_SOURCES + [os.path.join(CSRC, "plane_views.hip")])
+        return "cpu_order_step", CPU_ORDER_KERNELS, CPU_ORDER_SOURCES
+    if mode == "psnr-int":
+        return "psnr_int_step", ("view_stage1", "view_combine"), VIEW_SOURCES
+    if mode == "yuv420":
+        return "psnr_int_yuv420_step", ("views_stage1", "views_combine"), VIEW_SOURCES
+    return "host_step", ("stage1_u16", "stage2_combine"), HOST_SOURCES
 UNIT_POWER = (2, 1, 1, 2, 2)  # noise, ref1, dist1, ref2, dist2: units 1/s^power
 STAMP_EVERY = 8  # exact mode: steps per stage-1 dispatch timed with its own events
 
@@ -596,39 +629,35 @@ def make_mode(args, vqx, L, hip, np, torch, dev, st, wl, ref_np, dist_np, planes
     m = Mode()
     m.name = args.mode
     m.per_step_events = args.mode == "exact" and not args.pitch
+    kernel, step_kernels, m.sources = step_plan(args.mode, wl, args.pitch)
     if args.mode == "exact" and args.pitch:
         m.width = 5 * nframes
         m.ws_bytes = vqx.plane_view_workspace_bytes(w, h, bpc, nframes)
         m.metric = METRIC
-        m.kernel = "view_step"
-        m.kernel_label = "view_step (view_stage1 exact sums, view_combine)"
-        m.sources = VIEW_SOURCES
+        m.kernel = kernel
+        m.kernel_label = f"{kernel} ({', '.join(step_kernels)})"
         m.alg_bytes = wl.bytes_per_frame * nframes
     elif args.mode == "exact":
         m.width = 5 * nframes
         m.ws_bytes = vqx.plane_stats_workspace_bytes(w, h, bpc, nframes)
         m.metric = METRIC
-        m.kernel = "stage1_u8" if bpc == 8 else "stage1_u16"
+        m.kernel = kernel
         m.kernel_label = m.kernel
-        m.sources = STAGE1_SOURCES
         m.alg_bytes = wl.bytes_per_frame * nframes
     elif args.mode == "cpu-order":
         m.width = 10 * nframes
         m.ws_bytes = (vqx.plane_stats_view_cpu_order_workspace_bytes(w, h, bpc, nframes) if args.pitch
                       else vqx.plane_stats_cpu_order_workspace_bytes(w, h, bpc, nframes))
         m.metric = METRIC_CPU_ORDER
-        m.kernel = "cpu_order_step"
-        m.kernel_label = ("cpu_order_step (stage1_u16, cpu_order_prefix, cpu_order_maps, "
-                          "cpu_order_walk)")
-        m.sources = CPU_ORDER_SOURCES
+        m.kernel = kernel
+        m.kernel_label = f"{kernel} ({', '.join(step_kernels)})"
         m.alg_bytes = wl.bytes_per_frame * nframes + past53_bytes(ref_np, dist_np, bpc)
     elif args.mode == "psnr-int":
         m.width = nframes
         m.ws_bytes = vqx.plane_view_workspace_bytes(w, h, bpc, nframes)
         m.metric = METRIC_PSNR_INT
-        m.kernel = "psnr_int_step"
-        m.kernel_label = "psnr_int_step (view_stage1 integer noise, view_combine)"
-        m.sources = VIEW_SOURCES
+        m.kernel = kernel
+        m.kernel_label = f"{kernel} (view_stage1 integer noise, view_combine)"
         m.alg_bytes = wl.bytes_per_frame * nframes
     else:  # yuv420
         m.width = 3 * nframes
@@ -641,9 +670,8 @@ def make_mode(args, vqx, L, hip, np, torch, dev, st, wl, ref_np, dist_np, planes
                       torch.as_strided(d, (nframes, ph, pw), (fs, pw, 1), off)) for off, pw, ph in planes]
             m.plane_arrays.append(vqx.plane_pairs(pairs, bpc)[0])
         m.metric = METRIC_YUV420
-        m.kernel = "psnr_int_yuv420_step"
-        m.kernel_label = "psnr_int_yuv420_step (views_stage1 integer noise, views_combine; Y, U, V in one launch each)"
-        m.sources = VIEW_SOURCES
+        m.kernel = kernel
+        m.kernel_label = f"{kernel} (views_stage1 integer noise, views_combine; Y, U, V in one launch each)"
         m.alg_bytes = 2 * ref_np.shape[1] * wl.bytes_per_sample * nframes
     m.ws = torch.empty(m.ws_bytes, dtype=torch.uint8, device=dev)
     return m

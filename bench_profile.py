@@ -38,14 +38,6 @@ import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-CSRC = os.path.join(ROOT, "exact_reductions_amd", "csrc")
-STAGE1_SOURCES = [os.path.join(CSRC, f) for f in ("plane_stats.hip", "reduce.h")]
-CPU_ORDER_SOURCES = STAGE1_SOURCES + [os.path.join(CSRC, "cpu_order.hip")]
-CPU_ORDER_KERNELS = ("stage1_u16", "cpu_order_prefix", "cpu_order_maps", "cpu_order_walk")
-VIEW_SOURCES = [os.path.join(CSRC, f) for f in ("plane_views.hip", "reduce.h")]
-VIEW_KERNELS = ("view_stage1", "view_combine")
-PLANES_KERNELS = ("views_stage1", "views_combine")
-HOST_SOURCES = STAGE1_SOURCES + [os.path.join(CSRC, "host_stream.hip")]
 COPY_MIB = 1024
 WARMUP = 300
 
@@ -83,7 +75,8 @@ def rows(path):
 
 
 def short(name: str) -> str:
-    for k in ("stage1_u16", "stage1_u8", "stage2_combine", "bitwise_not", "cpu_order_prefix",
+    for k in ("stage1_u16_mapped", "mapped_combine", "gather_view", "stage1_u16", "stage1_u8", "stage2_combine",
+              "bitwise_not", "cpu_order_prefix",
               "cpu_order_maps", "cpu_order_walk", "views_stage1", "views_combine",
               "view_stage1", "view_combine", "read_probe"):
         if k in name:
@@ -183,6 +176,7 @@ def main(argv=None):
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--frames-per-upload", type=int, default=4)
     p.add_argument("--mode", choices=("exact", "cpu-order", "psnr-int", "yuv420", "host"), default="exact")
+    p.add_argument("--pitch", type=int, default=0, help="as bench.py --pitch")
     args = p.parse_args(argv)
     cpu_order = args.mode == "cpu-order"
     views = args.mode in ("psnr-int", "yuv420")
@@ -190,26 +184,23 @@ def main(argv=None):
         args.workload = 2 if args.mode == "yuv420" else 5
 
     sys.path.insert(0, ROOT)
+    import bench as bench_mod
     import synth
     wl = synth.WORKLOADS[args.workload]
-    if cpu_order:
-        kernel, step_kernels, sources = "cpu_order_step", CPU_ORDER_KERNELS, CPU_ORDER_SOURCES
-    elif args.mode == "psnr-int":
-        kernel, step_kernels, sources = "psnr_int_step", VIEW_KERNELS, VIEW_SOURCES
-    elif args.mode == "yuv420":
-        kernel, step_kernels, sources = "psnr_int_yuv420_step", PLANES_KERNELS, VIEW_SOURCES
-    elif args.mode == "host":
-        kernel, step_kernels, sources = "host_step", ("stage1_u16", "stage2_combine"), HOST_SOURCES
-    else:
-        kernel = "stage1_u8" if wl.bpc == 8 else "stage1_u16"
-        step_kernels, sources = (kernel,), STAGE1_SOURCES
-    wname = f"{wl.w}x{wl.h}x{wl.nframes}_{wl.bpc}bit" + ("_yuv420" if args.mode == "yuv420" else "")
+    if args.pitch == wl.w:
+        args.pitch = 0
+    # the same plan as the bench's own (its summaries are looked up by name and sources)
+    kernel, step_kernels, sources = bench_mod.step_plan(args.mode, wl, args.pitch)
+    wname = (f"{wl.w}x{wl.h}x{wl.nframes}_{wl.bpc}bit" + ("_yuv420" if args.mode == "yuv420" else "")
+             + (f"_pitch{args.pitch}" if args.pitch else ""))
     os.makedirs(args.out, exist_ok=True)
     os.makedirs(args.work, exist_ok=True)
     bench = ["python3", os.path.join(ROOT, "bench.py"), "--workload", str(args.workload),
              "--no-cpu-baseline", "--input-cache", args.cache, "--mode", args.mode]
     if args.mode == "host":
         bench += ["--frames-per-upload", str(args.frames_per_upload)]
+    if args.pitch:
+        bench += ["--pitch", str(args.pitch)]
     h = hashlib.sha256()
     for path in sources:
         with open(path, "rb") as f:
@@ -220,7 +211,6 @@ def main(argv=None):
         frame = wl.w * wl.h + 2 * (-(-wl.w // 2)) * (-(-wl.h // 2))
         alg = 2 * frame * wl.bytes_per_sample * wl.nframes
     if cpu_order:
-        import bench as bench_mod
         ref, dist = synth.generate(args.workload)
         alg += bench_mod.past53_bytes(ref, dist, wl.bpc)
         del ref, dist
