@@ -141,8 +141,9 @@ struct CpuOrderLayout {
 };
 CpuOrderLayout cpu_order_layout(const Geometry &g);
 
-// Where the CPU-order kernels find a batch's 16-byte vectors.  They index
-// them as if the batch were one contiguous [nframes][h][w] array (index v);
+// Where the kernels that read plane views in place (the mapped stage 1, the
+// CPU-order maps and walk) find a batch's 16-byte vectors.  They index them
+// as if the batch were one contiguous [nframes][h][w] array (index v);
 // a pair of plane views whose rows are whole 16-byte aligned vectors maps v
 // of frame f to v + f*pad_frame + y*pad_row (in vectors) for each plane, y
 // the row of v in its frame.  vpr == 0: contiguous planes, v itself.
