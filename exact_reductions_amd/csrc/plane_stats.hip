@@ -26,16 +26,13 @@
 // integer dot products: sum r, sum d (v_sad_u8), sum r^2, sum d^2, sum r*d
 // (v_dot4_u32_u8), and noise = sum r^2 + sum d^2 - 2 sum r*d, an identity of
 // integers.
-// 9..16 bits: each sample is converted to float and the three products
-// (r-d)^2, r^2, d^2 are taken in binary32, round to nearest even; each is an
-// integer below 2^32 [MOMENT, Decision].  They are added into binary64 lane
-// accumulators: a lane adds at most 65 of them, so every partial sum is an
-// integer below 2^39, exact in binary64, and the lane's sum is read back as
-// a uint64 without loss.  Across the wave each lane sum travels as its low
-// 16 bits and the rest, two uint32 sums -- the page's low/high split at 16
-// bits [PSNR, Decision], moved from every term to once per lane.  The
-// CPU-order form keeps uint64 lanes, since it needs each term as an integer
-// anyway (for the OR of the low bits).
+// 9..16 bits: each sample is converted to float once and the three
+// products (r-d)^2, r^2, d^2 are taken in binary32, round to nearest even;
+// each is an integer below 2^32 [MOMENT, Decision], read back as uint32 and
+// added into a 64-bit integer lane accumulator.  Across the wave each lane
+// sum travels as its low 16 bits and the rest, two uint32 sums -- the
+// page's low/high split at 16 bits [PSNR, Decision], moved from every term
+// to once per lane.
 
 #include <hip/hip_ext.h>
 
@@ -60,9 +57,8 @@ static_assert(kIters % kInFlight == 0, "whole load groups");
 // A lane sees at most kIters vectors plus one edge sample.
 //  8 bits: a lane's sum r^2 <= (8*16 + 1) * 255^2 < 2^23, so a wave's sum
 //          < 2^29; sum r and sum r*d are no larger.
-// 16 bits: a lane's sum of squares is <= (8*8 + 1) * (2^32 - 1) < 2^39
-//          (so exact in binary64 at every step); it is reduced across the
-//          wave as its low 16 bits (wave sum
+// 16 bits: a lane's sum of squares is <= (8*8 + 1) * (2^32 - 1) < 2^39;
+//          it is reduced across the wave as its low 16 bits (wave sum
 //          < 2^22) and the rest (lane value < 2^23, wave sum < 2^29); a
 //          lane's sample sum is <= 65 * 65535 < 2^23 (wave sum < 2^29).
 // Each wave64 total therefore fits uint32; the workgroup adds its waves in
@@ -70,7 +66,6 @@ static_assert(kIters % kInFlight == 0, "whole load groups");
 static_assert((kIters * 16 + 1) * 255ull * 255ull * 64ull < (1ull << 32), "8-bit wave budget");
 static_assert(((kIters * 8 + 1) * 0xffffffffull >> 16) * 64ull < (1ull << 32), "16-bit wave budget");
 static_assert((kIters * 8 + 1) * 65535ull * 64ull < (1ull << 32), "16-bit sample-sum budget");
-static_assert((kIters * 8 + 1) * 0xffffffffull < (1ull << 53), "16-bit lane sums exact in binary64");
 
 // ------------------------------------------------------------------ stage 1
 template <int kBytes, class Acc>
@@ -155,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void stage1_u16(const void *ref, const vo
     const int64_t wg = blockIdx.x;
     const int64_t frame = wg / chunks;
     const int chunk = static_cast<int>(wg - frame * chunks);
-    using Acc = typename std::conditional<kLowBitsOut, Acc16Low, Acc16>::type;
+    using Acc = typename std::conditional<kLowBitsOut, Acc16Low, Acc16U64>::type;
     Acc a;
     accumulate_chunk<2>(a, ref, dist, pixels, chunk, frame);
     // each 64-bit lane sum crosses the wave as (low 16 bits, the rest)

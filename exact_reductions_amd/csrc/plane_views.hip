@@ -88,7 +88,7 @@ __device__ __forceinline__ void finish(const Acc8 &a, int64_t wg, uint64_t *part
     write_record(part, wg, rec);
 }
 
-__device__ __forceinline__ void finish(const Acc16 &a, int64_t wg, uint64_t *part)
+__device__ __forceinline__ void finish(const Acc16F64 &a, int64_t wg, uint64_t *part)
 {
     const uint64_t n = lane_total(a.noise), r2 = lane_total(a.r2), d2 = lane_total(a.d2);
     const uint32_t v[8] = {static_cast<uint32_t>(n & 0xffffu), static_cast<uint32_t>(n >> 16), a.r1, a.d1,
@@ -497,7 +497,7 @@ ViewGeometry make_view_geometry(int w, int h, int bpc, int nframes)
 hipError_t launch_view_stats(const ViewGeometry &g, const PlaneView &ref, const PlaneView &dist,
                              uint64_t *out_noise, uint64_t *out_moments, uint64_t *partials, hipStream_t stream)
 {
-    return launch_views<Acc8, Acc16>(g, ref, dist, out_noise, out_moments, partials, stream);
+    return launch_views<Acc8, Acc16F64>(g, ref, dist, out_noise, out_moments, partials, stream);
 }
 
 hipError_t launch_view_psnr_int(const ViewGeometry &g, const PlaneView &ref, const PlaneView &dist,
@@ -521,7 +521,7 @@ hipError_t launch_gather_view(const PlaneView &view, int w, int h, int bpc, int 
 hipError_t launch_planes_stats(const ViewGeometry *g, const PlaneView *ref, const PlaneView *dist, int nplanes,
                                uint64_t *out_noise, uint64_t *out_moments, uint64_t *partials, hipStream_t stream)
 {
-    return launch_multi<Acc8, Acc16>(g, ref, dist, nplanes, out_noise, out_moments, partials, stream);
+    return launch_multi<Acc8, Acc16F64>(g, ref, dist, nplanes, out_noise, out_moments, partials, stream);
 }
 
 hipError_t launch_planes_psnr_int(const ViewGeometry *g, const PlaneView *ref, const PlaneView *dist, int nplanes,

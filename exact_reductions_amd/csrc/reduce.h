@@ -48,39 +48,62 @@ __device__ __forceinline__ void add_dword(Acc8 &a, uint32_t r, uint32_t d)
 }
 
 // -------------------------------------------------------------- 16-bit terms
-// The float terms go into binary64 lane accumulators: each term is an
-// integer below 2^32 and a lane adds at most a few hundred of them (the
-// kernels' budgets keep every lane sum below 2^53), so every partial sum is
-// an exact integer and the lane's total converts to uint64 without loss.
-// This is the leanest exact form on gfx950: a widening conversion and a
-// full-rate fp64 add per term, where a 64-bit integer add also needs a move
-// to zero the high half of each term's register pair, and adding the 16-bit
-// halves separately needs more.  That matters because the kernel runs near
-// the HBM roofline with its SIMDs also busy, where power (and with it the
-// clock) depends on the work per byte.
-struct Acc16 {
+// Each sample is converted to float once; that value serves its own square
+// and the difference (left to itself, the compiler squares a sample as an
+// integer and converts the product, which converts each sample twice).  The
+// three products are integers below 2^32 [MOMENT, Decision].  Two lane
+// forms add them exactly, each where it measured faster:
+//  * Acc16U64, uint64 lanes (one v_lshl_add_u64 per term, plus a move that
+//    zeroes the high half of the term's register pair): the contiguous
+//    stage 1, 153.4 us per 3840x2160x32 batch against 155.9 us in binary64;
+//  * Acc16F64, binary64 lanes (a widening conversion and an fp64 add per
+//    term; a lane adds at most a few hundred terms, so every partial sum is
+//    an integer below 2^53, exact, and the total converts to uint64 without
+//    loss): the view kernels and the mapped stage 1.  It needs far fewer
+//    registers, which the view kernels' sample-by-sample path, bound by
+//    load latency, turns into occupancy (368 us against 497 us per batch
+//    of rows at mismatched offsets).
+// Either way the sums are exact integers.  The kernels run near the HBM
+// roofline with their SIMDs also busy, so the work per byte matters.
+struct Acc16U64 {
+    uint64_t noise = 0, r2 = 0, d2 = 0;
+    uint32_t r1 = 0, d1 = 0;
+};
+
+struct Acc16F64 {
     double noise = 0, r2 = 0, d2 = 0;
     uint32_t r1 = 0, d1 = 0;
 };
 
+// A float product (an integer below 2^32) as a term of a Lane sum: read
+// back as uint32 for integer lanes, widened for binary64 lanes.
+__device__ __forceinline__ uint32_t lane_term(float p, uint64_t) { return static_cast<uint32_t>(p); }
+__device__ __forceinline__ double lane_term(float p, double) { return static_cast<double>(p); }
+
 // Two samples of each plane packed in one dword.
-__device__ __forceinline__ void add_dword(Acc16 &a, uint32_t r, uint32_t d)
+template <class Acc>
+__device__ __forceinline__ void add_dword_16(Acc &a, uint32_t r, uint32_t d)
 {
-    const float r0 = static_cast<float>(r & 0xffffu), r1 = static_cast<float>(r >> 16);
-    const float d0 = static_cast<float>(d & 0xffffu), d1 = static_cast<float>(d >> 16);
+    using Lane = decltype(a.noise);
+    float r0 = static_cast<float>(r & 0xffffu), r1 = static_cast<float>(r >> 16);
+    float d0 = static_cast<float>(d & 0xffffu), d1 = static_cast<float>(d >> 16);
+    asm volatile("" : "+v"(r0), "+v"(r1), "+v"(d0), "+v"(d1));  // one conversion each
     // float_psnr: the square of the float difference [PSNR, Decision]
-    a.noise += static_cast<double>((r0 - d0) * (r0 - d0));
-    a.noise += static_cast<double>((r1 - d1) * (r1 - d1));
+    a.noise += lane_term((r0 - d0) * (r0 - d0), Lane{});
+    a.noise += lane_term((r1 - d1) * (r1 - d1), Lane{});
     // float_moment: the float squares of the samples [MOMENT, Decision]
-    a.r2 += static_cast<double>(r0 * r0);
-    a.r2 += static_cast<double>(r1 * r1);
-    a.d2 += static_cast<double>(d0 * d0);
-    a.d2 += static_cast<double>(d1 * d1);
+    a.r2 += lane_term(r0 * r0, Lane{});
+    a.r2 += lane_term(r1 * r1, Lane{});
+    a.d2 += lane_term(d0 * d0, Lane{});
+    a.d2 += lane_term(d1 * d1, Lane{});
     // the sample sums: r0 + r1 in one integer dot product
     const u16x2 ones = {1, 1};
     a.r1 = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, r), ones, a.r1, false);
     a.d1 = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, d), ones, a.d1, false);
 }
+
+__device__ __forceinline__ void add_dword(Acc16U64 &a, uint32_t r, uint32_t d) { add_dword_16(a, r, d); }
+__device__ __forceinline__ void add_dword(Acc16F64 &a, uint32_t r, uint32_t d) { add_dword_16(a, r, d); }
 
 // Acc16's sums with uint64 lanes, and the OR of the terms of each square
 // sum, for their low bits: a run of terms all multiples of 2^k rounds
@@ -93,8 +116,9 @@ struct Acc16Low {
 
 __device__ __forceinline__ void add_dword(Acc16Low &a, uint32_t r, uint32_t d)
 {
-    const float r0 = static_cast<float>(r & 0xffffu), r1 = static_cast<float>(r >> 16);
-    const float d0 = static_cast<float>(d & 0xffffu), d1 = static_cast<float>(d >> 16);
+    float r0 = static_cast<float>(r & 0xffffu), r1 = static_cast<float>(r >> 16);
+    float d0 = static_cast<float>(d & 0xffffu), d1 = static_cast<float>(d >> 16);
+    asm volatile("" : "+v"(r0), "+v"(r1), "+v"(d0), "+v"(d1));  // one conversion each
     const uint32_t n0 = float_square(r0 - d0), n1 = float_square(r1 - d1);
     const uint32_t a0 = float_square(r0), a1 = float_square(r1);
     const uint32_t b0 = float_square(d0), b1 = float_square(d1);

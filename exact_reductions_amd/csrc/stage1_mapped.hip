@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kThreads) void stage1_u16_mapped(const void *ref, c
     // magic < 2^24, so the product fits 64 bits from 32-bit factors
     const int64_t fr = frame * M.pad_frame_r, fd = frame * M.pad_frame_d;
     const uint32_t magic = static_cast<uint32_t>(M.magic);
-    typename std::conditional<kLowBitsOut, Acc16Low, Acc16>::type a;
+    typename std::conditional<kLowBitsOut, Acc16Low, Acc16F64>::type a;
     if (cb < ce) {
 #pragma unroll 1
         for (int i = 0; i < kLaneIters; i += kInFlight) {
