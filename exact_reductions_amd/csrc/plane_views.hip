@@ -182,6 +182,62 @@ __device__ __forceinline__ void add_samples(Acc &acc, const char *r, const char 
     add_dword(acc, load_sample<kBytes>(r, 0), load_sample<kBytes>(d, 0));
 }
 
+// A tile whose rows start at different offsets within 16 bytes, with ref
+// and dist at the same offset in every row: row by row, the samples before
+// the row's first whole vector and after its last one by one, the whole
+// vectors as vectors.  Work items (row, slot): the lane reads vector
+// t + slot * kThreads of the row, for `slots` slots per row, four items at
+// a time; a lane past the row's last vector reads its first and drops it.
+template <int kBytes, class Acc>
+__device__ __forceinline__ void accumulate_rows(Acc &acc, const char *r0, const char *d0, int64_t rs_r, int64_t rs_d,
+                                                const Tile &T)
+{
+    constexpr int V = 16 / kBytes;
+    const int t = threadIdx.x;
+    const int slots = (T.cw / V + kThreads - 1) / kThreads;
+    // the row's first sample of whole vectors and its number of them
+    auto row_vectors = [&](int y, int &head, int &nvec) {
+        const int ph = static_cast<int>(reinterpret_cast<uintptr_t>(r0 + y * rs_r * kBytes) & 15);
+        head = ((16 - ph) & 15) / kBytes;
+        head = head < T.cw ? head : T.cw;
+        nvec = (T.cw - head) / V;
+    };
+    for (int y = 0; y < T.rows; ++y) {
+        int head, nvec;
+        row_vectors(y, head, nvec);
+        const int tail_begin = head + nvec * V;
+        const int x = t < head ? t : tail_begin + (t - head);
+        if (x < T.cw && (t < head || x >= tail_begin))
+            add_samples<kBytes>(acc, r0 + (y * rs_r + x) * kBytes, d0 + (y * rs_d + x) * kBytes);
+    }
+    const int items = T.rows * slots;
+    int y = 0, s = 0;
+    for (int g = 0; g < items; g += 4) {
+        u32x4 a[4], b[4];
+        bool ok[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            int head, nvec;
+            row_vectors(y, head, nvec);
+            const int col = t + s * kThreads;
+            ok[u] = g + u < items && col < nvec;
+            const int64_t xr = y * rs_r + head + (ok[u] ? col : 0) * V;
+            const int64_t xd = y * rs_d + head + (ok[u] ? col : 0) * V;
+            a[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(r0 + xr * kBytes));
+            b[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(d0 + xd * kBytes));
+            if (++s == slots) {
+                s = 0;
+                y = y + 1 < T.rows ? y + 1 : y;  // past the last item: stay on the last row
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const u32x4 zero = {0, 0, 0, 0};
+            add_vec(acc, ok[u] ? a[u] : zero, ok[u] ? b[u] : zero);
+        }
+    }
+}
+
 template <int kBytes, class Acc>
 __device__ __forceinline__ void accumulate_tile(Acc &acc, const PlaneView &R, const PlaneView &D, int64_t frame,
                                                 const Tile &T)
@@ -239,9 +295,12 @@ __device__ __forceinline__ void accumulate_tile(Acc &acc, const PlaneView &R, co
                 add_vec(acc, ok[u] ? a[u] : zero, ok[u] ? b[u] : zero);
             }
         }
+    } else if (phase_r == phase_d && (((R.row_stride - D.row_stride) * kBytes) & 15) == 0 && T.cw >= 32 * V) {
+        // rows at different offsets within 16 bytes, ref and dist at the
+        // same one in each: row by row
+        accumulate_rows<kBytes>(acc, r0, d0, R.row_stride, D.row_stride, T);
     } else {
-        // rows at different offsets within 16 bytes, or ref and dist at
-        // different ones: sample by sample
+        // ref and dist at different offsets, or narrow rows: sample by sample
         const int n = T.rows * T.cw;
         FlatWalk fw(t, T.cw, R.row_stride, D.row_stride);
         for (int s = t; s < n; s += kThreads, fw.next())

@@ -277,9 +277,11 @@ int vqx_conclude_batch(const uint64_t *noise, const uint64_t *moments, int w, in
  * same w, h and nframes.  The results are the same function of the selected
  * samples as the contiguous entry points' [PSNR, Context and Decision;
  * MOMENT, Decision]; the tiling never changes an integer sum.  Fastest where
- * the rows of a plane start at one offset within 16 bytes (row_stride*bytes
- * a multiple of 16) and ref and dist at the same one; any other layout is
- * read sample by sample, still exactly.
+ * ref and dist start each row at the same offset within 16 bytes: such rows
+ * are read as 16-byte vectors (row by row where the offset changes from row
+ * to row, as with an odd pitch, for rows of at least 32 vectors); where ref
+ * and dist rows start at different offsets, or rows are narrower, samples
+ * are read one by one, still exactly.
  *
  * Common errors, in this order: VQX_E_NULL, VQX_E_DIMS, VQX_E_BPC,
  * VQX_E_NFRAMES (also when the batch needs more than (2^32-1)/256 tiles of
