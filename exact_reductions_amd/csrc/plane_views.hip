@@ -182,20 +182,38 @@ __device__ __forceinline__ void add_samples(Acc &acc, const char *r, const char 
     add_dword(acc, load_sample<kBytes>(r, 0), load_sample<kBytes>(d, 0));
 }
 
-// A tile whose rows start at different offsets within 16 bytes, with ref
-// and dist at the same offset in every row: row by row, the samples before
-// the row's first whole vector and after its last one by one, the whole
-// vectors as vectors.  Work items (row, slot): the lane reads vector
-// t + slot * kThreads of the row, for `slots` slots per row, four items at
-// a time; a lane past the row's last vector reads its first and drops it.
-template <int kBytes, class Acc>
+// The 16 bytes at byte offset 4Q + r (r in 0..3, 4Q + r in 1..15) of the 32
+// bytes lo then hi.
+template <int Q>
+__device__ __forceinline__ u32x4 bytes_at(const u32x4 &lo, const u32x4 &hi, uint32_t r)
+{
+    const uint32_t d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    u32x4 o;
+    o.x = __builtin_amdgcn_alignbyte(d[Q + 1], d[Q + 0], r);
+    o.y = __builtin_amdgcn_alignbyte(d[Q + 2], d[Q + 1], r);
+    o.z = __builtin_amdgcn_alignbyte(d[Q + 3], d[Q + 2], r);
+    o.w = __builtin_amdgcn_alignbyte(d[Q + 4], d[Q + 3], r);
+    return o;
+}
+
+// A tile read row by row, for rows that start at different offsets within
+// 16 bytes (an odd pitch) or ref and dist rows at different offsets, with
+// dist's offset past ref's the same in every row.  In each row the samples
+// before ref's first whole vector and after its last are read one by one,
+// the whole vectors as vectors: ref's aligned, dist's the same (Q < 0) or
+// cut from the two aligned blocks that hold them (bytes_at<Q>, shift rb;
+// both blocks hold bytes of the row).  Work items (row, slot): the lane
+// reads vector t + slot * kThreads of the row, for `slots` slots per row,
+// four items at a time; a lane past the row's last vector reads its first
+// and drops it.  Rows hold at least 32 vectors.
+template <int kBytes, int Q, class Acc>
 __device__ __forceinline__ void accumulate_rows(Acc &acc, const char *r0, const char *d0, int64_t rs_r, int64_t rs_d,
-                                                const Tile &T)
+                                                const Tile &T, uint32_t rb)
 {
     constexpr int V = 16 / kBytes;
     const int t = threadIdx.x;
     const int slots = (T.cw / V + kThreads - 1) / kThreads;
-    // the row's first sample of whole vectors and its number of them
+    // the row's first sample of whole ref vectors and its number of them
     auto row_vectors = [&](int y, int &head, int &nvec) {
         const int ph = static_cast<int>(reinterpret_cast<uintptr_t>(r0 + y * rs_r * kBytes) & 15);
         head = ((16 - ph) & 15) / kBytes;
@@ -224,7 +242,13 @@ __device__ __forceinline__ void accumulate_rows(Acc &acc, const char *r0, const 
             const int64_t xr = y * rs_r + head + (ok[u] ? col : 0) * V;
             const int64_t xd = y * rs_d + head + (ok[u] ? col : 0) * V;
             a[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(r0 + xr * kBytes));
-            b[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(d0 + xd * kBytes));
+            if constexpr (Q < 0) {
+                b[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(d0 + xd * kBytes));
+            } else {
+                const u32x4 *db = reinterpret_cast<const u32x4 *>(reinterpret_cast<uintptr_t>(d0 + xd * kBytes) &
+                                                                  ~static_cast<uintptr_t>(15));
+                b[u] = bytes_at<Q>(__builtin_nontemporal_load(db), __builtin_nontemporal_load(db + 1), rb);
+            }
             if (++s == slots) {
                 s = 0;
                 y = y + 1 < T.rows ? y + 1 : y;  // past the last item: stay on the last row
@@ -295,12 +319,24 @@ __device__ __forceinline__ void accumulate_tile(Acc &acc, const PlaneView &R, co
                 add_vec(acc, ok[u] ? a[u] : zero, ok[u] ? b[u] : zero);
             }
         }
-    } else if (phase_r == phase_d && (((R.row_stride - D.row_stride) * kBytes) & 15) == 0 && T.cw >= 32 * V) {
-        // rows at different offsets within 16 bytes, ref and dist at the
-        // same one in each: row by row
-        accumulate_rows<kBytes>(acc, r0, d0, R.row_stride, D.row_stride, T);
+    } else if ((((R.row_stride - D.row_stride) * kBytes) & 15) == 0 && T.cw >= 32 * V) {
+        // rows at different offsets within 16 bytes, or ref and dist at
+        // different ones (dist's past ref's the same in every row): row by row
+        const uint32_t o = static_cast<uint32_t>(phase_d - phase_r) & 15u;
+        const int64_t rs_r = R.row_stride, rs_d = D.row_stride;
+        if (o == 0)
+            accumulate_rows<kBytes, -1>(acc, r0, d0, rs_r, rs_d, T, 0u);
+        else if (o < 4)
+            accumulate_rows<kBytes, 0>(acc, r0, d0, rs_r, rs_d, T, o & 3u);
+        else if (o < 8)
+            accumulate_rows<kBytes, 1>(acc, r0, d0, rs_r, rs_d, T, o & 3u);
+        else if (o < 12)
+            accumulate_rows<kBytes, 2>(acc, r0, d0, rs_r, rs_d, T, o & 3u);
+        else
+            accumulate_rows<kBytes, 3>(acc, r0, d0, rs_r, rs_d, T, o & 3u);
     } else {
-        // ref and dist at different offsets, or narrow rows: sample by sample
+        // ref and dist rows drifting apart within 16 bytes, or narrow rows:
+        // sample by sample
         const int n = T.rows * T.cw;
         FlatWalk fw(t, T.cw, R.row_stride, D.row_stride);
         for (int s = t; s < n; s += kThreads, fw.next())
@@ -438,20 +474,6 @@ hipError_t launch_multi(const ViewGeometry *g, const PlaneView *ref, const Plane
 // cut from the two aligned blocks that hold it.  Those blocks each hold at
 // least one byte of the row, so they lie in pages of the view.
 constexpr int64_t kGatherWgs = 65536;
-
-// The 16 bytes at byte offset 4Q + r (r in 0..3, 4Q + r in 1..15) of the 32
-// bytes lo then hi.
-template <int Q>
-__device__ __forceinline__ u32x4 bytes_at(const u32x4 &lo, const u32x4 &hi, uint32_t r)
-{
-    const uint32_t d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    u32x4 o;
-    o.x = __builtin_amdgcn_alignbyte(d[Q + 1], d[Q + 0], r);
-    o.y = __builtin_amdgcn_alignbyte(d[Q + 2], d[Q + 1], r);
-    o.z = __builtin_amdgcn_alignbyte(d[Q + 3], d[Q + 2], r);
-    o.w = __builtin_amdgcn_alignbyte(d[Q + 4], d[Q + 3], r);
-    return o;
-}
 
 // Destination vectors 0..n-1 from the source blocks vs[0..n] at offset
 // 4Q + r (> 0).

@@ -276,12 +276,12 @@ int vqx_conclude_batch(const uint64_t *noise, const uint64_t *moments, int w, in
  * addressed sample readable.  ref and dist have views of their own, with the
  * same w, h and nframes.  The results are the same function of the selected
  * samples as the contiguous entry points' [PSNR, Context and Decision;
- * MOMENT, Decision]; the tiling never changes an integer sum.  Fastest where
- * ref and dist start each row at the same offset within 16 bytes: such rows
- * are read as 16-byte vectors (row by row where the offset changes from row
- * to row, as with an odd pitch, for rows of at least 32 vectors); where ref
- * and dist rows start at different offsets, or rows are narrower, samples
- * are read one by one, still exactly.
+ * MOMENT, Decision]; the tiling never changes an integer sum.  Rows are
+ * read as 16-byte vectors where dist starts each row the same distance past
+ * ref within 16 bytes (row strides differing by a multiple of 16 bytes),
+ * fastest where that distance is 0 and every row starts at one offset; rows
+ * narrower than 32 vectors at varying offsets, and ref and dist rows that
+ * drift apart from row to row, are read sample by sample, still exactly.
  *
  * Common errors, in this order: VQX_E_NULL, VQX_E_DIMS, VQX_E_BPC,
  * VQX_E_NFRAMES (also when the batch needs more than (2^32-1)/256 tiles of

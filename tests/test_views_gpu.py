@@ -133,6 +133,23 @@ def test_ref_and_dist_at_different_offsets():
     check_views(ref, dist, torch.from_numpy(ref).cuda(), torch.from_numpy(big).cuda()[:, :, 1:1 + w], 16)
 
 
+@pytest.mark.parametrize("bpc", [8, 10, 16])
+@pytest.mark.parametrize("pitch,xr,xd", [(2048, 0, 1), (2048, 3, 0), (2051, 1, 6), (2049, 0, 5), (2048, 7, 2)])
+def test_ref_and_dist_offsets_apart_one_pitch(bpc, pitch, xr, xd):
+    """ref and dist in buffers of one pitch at different column offsets: in
+    every row dist starts the same distance past ref within 16 bytes, and
+    its vectors are cut from aligned blocks (even and odd pitches, dist
+    before or after ref, at every depth)."""
+    rng = np.random.default_rng(pitch * 7 + xr * 3 + xd + bpc)
+    f, h, w = 2, 70, 1900
+    big_r = _rand(rng, (f, h + 2, pitch), bpc)
+    big_d = _rand(rng, (f, h + 2, pitch), bpc)
+    sr = (slice(None), slice(1, 1 + h), slice(xr, xr + w))
+    sd = (slice(None), slice(2, 2 + h), slice(xd, xd + w))
+    check_views(big_r[sr], big_d[sd], torch.from_numpy(big_r).cuda()[sr], torch.from_numpy(big_d).cuda()[sd], bpc,
+                f"pitch {pitch} ref at {xr}, dist at {xd}")
+
+
 @pytest.mark.parametrize("bpc,w", [(16, 40000), (8, 70000), (16, 16384), (16, 16385)])
 def test_rows_longer_than_a_tile(bpc, w):
     rng = np.random.default_rng(w)
