@@ -575,7 +575,7 @@ def run_host_mode(args, np, torch, vqx, wl, ref_np, dist_np, t_gen):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32 squares, exact f64 lane sums, u64 totals" if bpc > 8 else "fp32 squares, u64 sums",
+        "dtype": "fp32 squares, u64 sums",
         "data": "synthetic",
         "config": {
             "workload": f"{w}x{h} {bpc}-bit luma pair, {nframes} frames, "
@@ -927,8 +927,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("fp32 squares, exact f64 lane sums, u64 totals" if args.mode == "exact" and bpc > 8 else
-                  "fp32 squares, u64 sums" if args.mode in ("exact", "cpu-order") else "u32 squares, u64 sums"),
+        "dtype": "fp32 squares, u64 sums" if args.mode in ("exact", "cpu-order") else "u32 squares, u64 sums",
         "data": "synthetic",
         "config": {
             "workload": f"{w}x{h} {bpc}-bit luma pair, {nframes} frames, "
