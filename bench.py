@@ -81,17 +81,19 @@ MAPPED_SOURCES = [os.path.join(CSRC, f) for f in ("stage1_mapped.hip", "reduce.h
 CPU_ORDER_KERNELS = ("stage1_u16", "cpu_order_prefix", "cpu_order_maps", "cpu_order_walk")
 
 
-def step_plan(mode: str, wl, pitch: int = 0):
+def step_plan(mode: str, wl, pitch: int = 0, x0: int = 0):
     """(kernel, step kernels, sources) of a bench mode: the name of the timed
     step's dominant kernel (or of the whole step), the kernels one step runs
     as rocprofv3 names them, and the sources they are built from.  Planes
-    with a pitch (rows of ``pitch`` samples) go through the view entry
-    points, which read rows of whole aligned 16-byte vectors of two-byte
-    samples in place with the contiguous chunks ("mapped") and gather or tile
-    other layouts."""
+    with a pitch (rows of ``pitch`` samples, the frame ``x0`` samples into
+    each) go through the view entry points, which read rows of whole 16-byte
+    vectors of two-byte samples in place with the contiguous chunks
+    ("mapped": aligned vectors for the exact sums, vectors at any one offset
+    within 16 bytes for the CPU-order form) and gather or tile other
+    layouts."""
     mapped = bool(pitch) and wl.bpc > 8 and wl.w % 8 == 0 and pitch % 8 == 0
     if mode == "exact" and pitch:
-        if mapped:
+        if mapped and x0 % 8 == 0:
             return "mapped_step", ("stage1_u16_mapped", "mapped_combine"), MAPPED_SOURCES
         return "view_step", ("view_stage1", "view_combine"), VIEW_SOURCES
     if mode == "exact":
@@ -142,6 +144,8 @@ def parse_args(argv=None):
                    help="exact, cpu-order and psnr-int modes: keep the planes resident with rows of SAMPLES samples "
                         "(>= w; the frame inside the first w of each row) and reduce them through the "
                         "plane-view entry points (default: contiguous)")
+    p.add_argument("--x0", type=int, default=0, metavar="SAMPLES",
+                   help="with --pitch: the frame starts SAMPLES samples into each row (pitch >= x0 + w)")
     p.add_argument("--frames-per-upload", type=int, default=4,
                    help="host mode: frames per upload")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -629,7 +633,7 @@ def make_mode(args, vqx, L, hip, np, torch, dev, st, wl, ref_np, dist_np, planes
     m = Mode()
     m.name = args.mode
     m.per_step_events = args.mode == "exact" and not args.pitch
-    kernel, step_kernels, m.sources = step_plan(args.mode, wl, args.pitch)
+    kernel, step_kernels, m.sources = step_plan(args.mode, wl, args.pitch, args.x0 if args.pitch else 0)
     if args.mode == "exact" and args.pitch:
         m.width = 5 * nframes
         m.ws_bytes = vqx.plane_view_workspace_bytes(w, h, bpc, nframes)
@@ -716,17 +720,18 @@ def main(argv=None):
     # two resident copies of the batch, alternated step by step
     r0 = torch.from_numpy(ref_np).to(dev)
     d0 = torch.from_numpy(dist_np).to(dev)
-    if args.pitch == w:
+    if args.pitch == w and not args.x0:
         args.pitch = 0
     if args.pitch:
-        if args.mode not in ("exact", "cpu-order", "psnr-int") or args.pitch < w:
-            print("--pitch needs --mode exact, cpu-order or psnr-int and a pitch >= w", file=sys.stderr)
+        if args.mode not in ("exact", "cpu-order", "psnr-int") or args.x0 < 0 or args.pitch < args.x0 + w:
+            print("--pitch needs --mode exact, cpu-order or psnr-int and a pitch >= x0 + w", file=sys.stderr)
             return 2
+        x0 = args.x0
 
         def pitched(x):
             big = torch.zeros((nframes, h, args.pitch), dtype=x.dtype, device=dev)
-            big[:, :, :w] = x
-            return big[:, :, :w]
+            big[:, :, x0:x0 + w] = x
+            return big[:, :, x0:x0 + w]
         bufs = [(pitched(r0), pitched(d0)), (pitched(r0), pitched(d0))]
         del r0, d0
     else:
@@ -912,7 +917,7 @@ def main(argv=None):
                                             mode.alg_bytes, min(args.steps, 200))
 
     wname = (f"{w}x{h}x{nframes}_{bpc}bit" + ("_yuv420" if args.mode == "yuv420" else "")
-             + (f"_pitch{args.pitch}" if args.pitch else ""))
+             + (f"_pitch{args.pitch}" if args.pitch else "") + (f"_x{args.x0}" if args.pitch and args.x0 else ""))
     traffic = stored_traffic(mode.kernel, wname, tuple(mode.sources))
     achieved = mode.alg_bytes / (mean_ms * 1e-3) / 1e9
 
@@ -937,6 +942,7 @@ def main(argv=None):
             "w": w, "h": h, "bpc": bpc, "nframes": nframes, "mode": args.mode,
             "streams": nst,
             "row_pitch": args.pitch or w,
+            "x0": args.x0 if args.pitch else 0,
             "bytes_per_step": bytes_per_step,
             "hbm_gbs_whole_step": round(bytes_per_step * args.steps / elapsed / 1e9, 1),
         },

@@ -177,6 +177,7 @@ def main(argv=None):
     p.add_argument("--frames-per-upload", type=int, default=4)
     p.add_argument("--mode", choices=("exact", "cpu-order", "psnr-int", "yuv420", "host"), default="exact")
     p.add_argument("--pitch", type=int, default=0, help="as bench.py --pitch")
+    p.add_argument("--x0", type=int, default=0, help="as bench.py --x0")
     args = p.parse_args(argv)
     cpu_order = args.mode == "cpu-order"
     views = args.mode in ("psnr-int", "yuv420")
@@ -187,12 +188,13 @@ def main(argv=None):
     import bench as bench_mod
     import synth
     wl = synth.WORKLOADS[args.workload]
-    if args.pitch == wl.w:
+    if args.pitch == wl.w and not args.x0:
         args.pitch = 0
+    x0 = args.x0 if args.pitch else 0
     # the same plan as the bench's own (its summaries are looked up by name and sources)
-    kernel, step_kernels, sources = bench_mod.step_plan(args.mode, wl, args.pitch)
+    kernel, step_kernels, sources = bench_mod.step_plan(args.mode, wl, args.pitch, x0)
     wname = (f"{wl.w}x{wl.h}x{wl.nframes}_{wl.bpc}bit" + ("_yuv420" if args.mode == "yuv420" else "")
-             + (f"_pitch{args.pitch}" if args.pitch else ""))
+             + (f"_pitch{args.pitch}" if args.pitch else "") + (f"_x{x0}" if x0 else ""))
     os.makedirs(args.out, exist_ok=True)
     os.makedirs(args.work, exist_ok=True)
     bench = ["python3", os.path.join(ROOT, "bench.py"), "--workload", str(args.workload),
@@ -201,6 +203,8 @@ def main(argv=None):
         bench += ["--frames-per-upload", str(args.frames_per_upload)]
     if args.pitch:
         bench += ["--pitch", str(args.pitch)]
+    if x0:
+        bench += ["--x0", str(x0)]
     h = hashlib.sha256()
     for path in sources:
         with open(path, "rb") as f:

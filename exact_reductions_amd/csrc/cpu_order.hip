@@ -380,7 +380,9 @@ __device__ __forceinline__ uint32_t vector_term(const u32x4 &a, const u32x4 &b, 
 // `safe` (one known to exist) instead, for the caller to drop (keep_if).
 // Every lane loads, so no branch separates the loads from the waits for
 // them and the next vectors can be in flight while these are used.
-template <int KK>
+// kSh: the planes' vectors start at the map's phases within 16-byte
+// blocks (R and D then the bases rounded down to 16 bytes).
+template <int KK, bool kSh>
 __device__ __forceinline__ void load_vector(const u32x4 *R, const u32x4 *D, const VecMap &M, int64_t frame,
                                             int64_t v, bool ok, int64_t safe, u32x4 &a, u32x4 &b)
 {
@@ -388,11 +390,11 @@ __device__ __forceinline__ void load_vector(const u32x4 *R, const u32x4 *D, cons
     int64_t ar, ad;
     map_vec(M, frame, ok ? v : safe, ar, ad);
     if constexpr (KK != kSqDist)
-        a = __builtin_nontemporal_load(R + ar);
+        a = kSh ? load_vec16(R, ar, M.phase_r) : __builtin_nontemporal_load(R + ar);
     else
         a = zero;
     if constexpr (KK != kSqRef)
-        b = __builtin_nontemporal_load(D + ad);
+        b = kSh ? load_vec16(D, ad, M.phase_d) : __builtin_nontemporal_load(D + ad);
     else
         b = zero;
 }
@@ -674,7 +676,7 @@ __device__ __forceinline__ void forget(u32x4 (&a)[kLaneVectors], u32x4 (&b)[kLan
 
 // Slab [sb, sb + 256) of the chunk [cb, ce), cb < ce; the slab may start
 // past ce in the chunk after a frame's last whole vector.
-template <int KK>
+template <int KK, bool kSh>
 __device__ __forceinline__ void load_item(ItemData &x, const u32x4 *R, const u32x4 *D, const VecMap &M,
                                           int64_t frame, int64_t cb, int64_t sb, int64_t ce)
 {
@@ -683,7 +685,7 @@ __device__ __forceinline__ void load_item(ItemData &x, const u32x4 *R, const u32
 #pragma unroll
     for (int j = 0; j < kLaneVectors; ++j) {
         const int64_t v = sb + 64 * j + lane;
-        load_vector<KK>(R, D, M, frame, v, v < ce, cb, x.a[j], x.b[j]);
+        load_vector<KK, kSh>(R, D, M, frame, v, v < ce, cb, x.a[j], x.b[j]);
         x.ok |= (v < ce ? 1u : 0u) << j;
     }
 }
@@ -846,7 +848,7 @@ __device__ __forceinline__ SlabItem slab_item(const Slabs &Q, int64_t i)
 // Slab items i, i + stride, ... below n, in turn.  The next item's vectors
 // are read while the current one is mapped, except for the noise, which
 // reads both planes.
-template <int KK>
+template <int KK, bool kSh>
 __device__ __forceinline__ void queue_maps(const Slabs &Q, int64_t i, int64_t stride, int64_t n, u32x4 *lds)
 {
     ItemData x, y;
@@ -854,7 +856,7 @@ __device__ __forceinline__ void queue_maps(const Slabs &Q, int64_t i, int64_t st
         item_maps<KK>(d, it.si, it.e, it.dual, it.entry, lds);
     };
     SlabItem u = slab_item<KK>(Q, i);
-    load_item<KK>(x, Q.R, Q.D, Q.map, u.frame, u.cb, u.sb, u.ce);
+    load_item<KK, kSh>(x, Q.R, Q.D, Q.map, u.frame, u.cb, u.sb, u.ce);
     if constexpr (KK == kSqNoise) {
         for (;;) {
             map_item(x, u);
@@ -862,7 +864,7 @@ __device__ __forceinline__ void queue_maps(const Slabs &Q, int64_t i, int64_t st
             if (i >= n)
                 return;
             u = slab_item<KK>(Q, i);
-            load_item<KK>(x, Q.R, Q.D, Q.map, u.frame, u.cb, u.sb, u.ce);
+            load_item<KK, kSh>(x, Q.R, Q.D, Q.map, u.frame, u.cb, u.sb, u.ce);
         }
     } else {
         // Two buffers, taken in turn.  Each item mapped inside the loop
@@ -877,7 +879,7 @@ __device__ __forceinline__ void queue_maps(const Slabs &Q, int64_t i, int64_t st
                 return;
             }
             v = slab_item<KK>(Q, i);
-            load_item<KK>(y, Q.R, Q.D, Q.map, v.frame, v.cb, v.sb, v.ce);
+            load_item<KK, kSh>(y, Q.R, Q.D, Q.map, v.frame, v.cb, v.sb, v.ce);
             map_item(x, u);
             i += stride;
             if (i >= n) {
@@ -885,7 +887,7 @@ __device__ __forceinline__ void queue_maps(const Slabs &Q, int64_t i, int64_t st
                 return;
             }
             u = slab_item<KK>(Q, i);
-            load_item<KK>(x, Q.R, Q.D, Q.map, u.frame, u.cb, u.sb, u.ce);
+            load_item<KK, kSh>(x, Q.R, Q.D, Q.map, u.frame, u.cb, u.sb, u.ce);
             map_item(y, v);
         }
     }
@@ -895,6 +897,7 @@ __device__ __forceinline__ void queue_maps(const Slabs &Q, int64_t i, int64_t st
 // takes slab items w, w + W, w + 2W, ... of each queue in turn (W waves in
 // all).  Two-byte samples only.  Three waves per SIMD fit its registers
 // without spills (168 VGPRs), one more than the compiler picks unasked.
+template <bool kSh>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void cpu_order_maps(const void *ref, const void *dist, int64_t pixels,
                                                            int chunks, int nframes, const uint64_t *rec,
                                                            const uint64_t *queue, uint64_t *maps, VecMap vmap)
@@ -915,15 +918,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     int64_t n = static_cast<int64_t>(counts[kSqNoise]) * kSlabs;
     Q.queue = queue + kSqNoise * cap;
     if (w < n)
-        queue_maps<kSqNoise>(Q, w, W, n, lds);
+        queue_maps<kSqNoise, kSh>(Q, w, W, n, lds);
     n = static_cast<int64_t>(counts[kSqRef]) * kSlabs;
     Q.queue = queue + kSqRef * cap;
     if (w < n)
-        queue_maps<kSqRef>(Q, w, W, n, lds);
+        queue_maps<kSqRef, kSh>(Q, w, W, n, lds);
     n = static_cast<int64_t>(counts[kSqDist]) * kSlabs;
     Q.queue = queue + kSqDist * cap;
     if (w < n)
-        queue_maps<kSqDist>(Q, w, W, n, lds);
+        queue_maps<kSqDist, kSh>(Q, w, W, n, lds);
 }
 
 // ------------------------------------------------------------------ 4. walk
@@ -1075,7 +1078,7 @@ struct Planes {
 // most one binade in it).  The slab goes through LDS so that lane g holds
 // vectors 4g .. 4g + 3, 32 consecutive terms: one row of 64 groups, and
 // inside the group where S crosses, one row of its 32 terms.
-template <int KK>
+template <int KK, bool kSh>
 __device__ __forceinline__ uint64_t walk_slab(uint64_t S, const Planes &P, int64_t sb, int64_t se, u32x4 *lds)
 {
     const int lane = threadIdx.x & 63;
@@ -1085,7 +1088,7 @@ __device__ __forceinline__ uint64_t walk_slab(uint64_t S, const Planes &P, int64
 #pragma unroll
     for (int j = 0; j < kLaneVectors; ++j) {
         const int64_t v = sb + 64 * j + lane;
-        load_vector<KK>(P.R, P.D, P.map, P.frame, v, v < se, sb, a[j], b[j]);
+        load_vector<KK, kSh>(P.R, P.D, P.map, P.frame, v, v < se, sb, a[j], b[j]);
         keep_if<KK>(v < se, a[j], b[j]);
     }
     consecutive<KK>(a, b, lds);
@@ -1123,7 +1126,7 @@ __device__ __forceinline__ uint64_t walk_slab(uint64_t S, const Planes &P, int64
 
 // One chunk, from its slab maps; a slab where they do not apply is walked
 // with maps made on the spot.
-template <int KK>
+template <int KK, bool kSh>
 __device__ __forceinline__ uint64_t walk_chunk(uint64_t S, const Planes &P, const uint64_t *entry, int64_t cb,
                                                int64_t ce, u32x4 *lds)
 {
@@ -1132,7 +1135,7 @@ __device__ __forceinline__ uint64_t walk_chunk(uint64_t S, const Planes &P, cons
         // no slab maps (S is not where the chunk map expects it): map each
         // slab on the spot
         for (int64_t sb = cb; sb < ce; sb += kSlabVectors)
-            S = walk_slab<KK>(S, P, sb, sb + kSlabVectors < ce ? sb + kSlabVectors : ce, lds);
+            S = walk_slab<KK, kSh>(S, P, sb, sb + kSlabVectors < ce ? sb + kSlabVectors : ce, lds);
         return S;
     }
     const int n = static_cast<int>((ce - cb + kSlabVectors - 1) / kSlabVectors);  // slabs holding vectors
@@ -1146,7 +1149,7 @@ __device__ __forceinline__ uint64_t walk_chunk(uint64_t S, const Planes &P, cons
     }
     return walk_items(S, it, n, [&](uint64_t S1, int j) {
         const int64_t sb = cb + static_cast<int64_t>(j) * kSlabVectors;
-        return walk_slab<KK>(S1, P, sb, sb + kSlabVectors < ce ? sb + kSlabVectors : ce, lds);
+        return walk_slab<KK, kSh>(S1, P, sb, sb + kSlabVectors < ce ? sb + kSlabVectors : ce, lds);
     });
 }
 
@@ -1261,7 +1264,7 @@ __device__ __forceinline__ void compose_block(const void *ref, const void *dist,
 // ---------------------------------------------------------- 4b. the walk
 // The 64 chunks of one block, chunk b*64 + j in lane j, from S, from their
 // compact records; a chunk where they do not apply is walked slab by slab.
-template <int KK>
+template <int KK, bool kSh>
 __device__ __forceinline__ uint64_t walk_block(uint64_t S, const Planes &P, const uint64_t *cmaps,
                                                const uint64_t *entries, int64_t frame, int chunks, int block,
                                                const FrameEdges &fe, u32x4 *lds)
@@ -1280,12 +1283,12 @@ __device__ __forceinline__ uint64_t walk_block(uint64_t S, const Planes &P, cons
     return walk_items(S, it, n, [&](uint64_t S1, int j) {
         const int64_t cb = fe.vb + static_cast<int64_t>(block * kBlockChunks + j) * kChunkVectors;
         const int64_t ce = cb + kChunkVectors < fe.ve ? cb + kChunkVectors : fe.ve;
-        return walk_chunk<KK>(S1, P, entries + static_cast<int64_t>(block * kBlockChunks + j) * kSquares * kEntry,
+        return walk_chunk<KK, kSh>(S1, P, entries + static_cast<int64_t>(block * kBlockChunks + j) * kSquares * kEntry,
                               cb, ce, lds);
     });
 }
 
-template <int KK>
+template <int KK, bool kSh>
 __device__ __forceinline__ void walk_frame(const void *ref, const void *dist, int64_t pixels, int chunks,
                                            const uint64_t *maps, const uint64_t *cmaps, const uint64_t *bmaps,
                                            int64_t frame, uint64_t *dst, u32x4 *lds, const VecMap &vmap)
@@ -1316,7 +1319,7 @@ __device__ __forceinline__ void walk_frame(const void *ref, const void *dist, in
         const uint64_t fl = lane_value64(bfl, b);
         if ((fl & 1u) && map_apply(S, map_from(lane_value64(bdm0, b), lane_value64(bdm1, b), fl), flags_binade(fl)))
             continue;
-        S = walk_block<KK>(S, P, cmaps, entries, frame, chunks, b, fe, lds);
+        S = walk_block<KK, kSh>(S, P, cmaps, entries, frame, chunks, b, fe, lds);
     }
     // the tail comes last
     for (int j = 0; j < fe.tail; ++j)
@@ -1331,7 +1334,7 @@ __device__ __forceinline__ void walk_frame(const void *ref, const void *dist, in
 // the barrier that makes their records visible, wave 0 walks the frame.
 constexpr int kWalkWaves = 8;
 
-template <int KK>
+template <int KK, bool kSh>
 __device__ __forceinline__ void compose_then_walk(const void *ref, const void *dist, int64_t pixels, int chunks,
                                                   const uint64_t *rec, const uint64_t *maps, uint64_t *cmaps,
                                                   uint64_t *bmaps, int64_t frame, uint64_t *dst, u32x4 *lds,
@@ -1342,9 +1345,10 @@ __device__ __forceinline__ void compose_then_walk(const void *ref, const void *d
         compose_block<KK>(ref, dist, pixels, chunks, rec, maps, frame, b, cmaps, bmaps);
     __syncthreads();
     if (wave == 0)
-        walk_frame<KK>(ref, dist, pixels, chunks, maps, cmaps, bmaps, frame, dst, lds, vmap);
+        walk_frame<KK, kSh>(ref, dist, pixels, chunks, maps, cmaps, bmaps, frame, dst, lds, vmap);
 }
 
+template <bool kSh>
 __global__ __launch_bounds__(64 * kWalkWaves) void cpu_order_walk(const void *ref, const void *dist, int64_t pixels,
                                                                   int chunks, const uint64_t *rec,
                                                                   const uint64_t *totals, const uint64_t *maps,
@@ -1359,15 +1363,15 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cpu_order_walk(const void *re
         return;
     switch (kk) {
     case kSqNoise:
-        compose_then_walk<kSqNoise>(ref, dist, pixels, chunks, rec, maps, cmaps, bmaps, frame, &out_cpu_noise[frame],
+        compose_then_walk<kSqNoise, kSh>(ref, dist, pixels, chunks, rec, maps, cmaps, bmaps, frame, &out_cpu_noise[frame],
                                     lds, vmap);
         break;
     case kSqRef:
-        compose_then_walk<kSqRef>(ref, dist, pixels, chunks, rec, maps, cmaps, bmaps, frame,
+        compose_then_walk<kSqRef, kSh>(ref, dist, pixels, chunks, rec, maps, cmaps, bmaps, frame,
                                   &out_cpu_moments[4 * frame + 2], lds, vmap);
         break;
     default:
-        compose_then_walk<kSqDist>(ref, dist, pixels, chunks, rec, maps, cmaps, bmaps, frame,
+        compose_then_walk<kSqDist, kSh>(ref, dist, pixels, chunks, rec, maps, cmaps, bmaps, frame,
                                    &out_cpu_moments[4 * frame + 3], lds, vmap);
         break;
     }
@@ -1376,6 +1380,7 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cpu_order_walk(const void *re
 // Workgroups of the maps kernel that the current device holds at once (its
 // occupancy per CU, from its register and LDS use, times the CUs), asked
 // once per device.
+template <bool kSh>
 hipError_t maps_resident_workgroups(int64_t &wgs)
 {
     constexpr int kMaxDevices = 64;
@@ -1388,7 +1393,7 @@ hipError_t maps_resident_workgroups(int64_t &wgs)
     if (cached && (wgs = cache[dev].load(std::memory_order_relaxed)) > 0)
         return hipSuccess;
     int per_cu = 0, cus = 0;
-    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, cpu_order_maps, kThreads, 0);
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, cpu_order_maps<kSh>, kThreads, 0);
     if (err == hipSuccess)
         err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (err != hipSuccess)
@@ -1401,8 +1406,8 @@ hipError_t maps_resident_workgroups(int64_t &wgs)
 
 }  // namespace
 
-VecMap make_vec_map(int w, int h, int64_t ref_row_stride, int64_t ref_frame_stride, int64_t dist_row_stride,
-                    int64_t dist_frame_stride)
+VecMap make_vec_map(int w, int h, const void *ref, int64_t ref_row_stride, int64_t ref_frame_stride,
+                    const void *dist, int64_t dist_row_stride, int64_t dist_frame_stride)
 {
     constexpr int V = 8;  // two-byte samples per vector
     VecMap M;
@@ -1420,6 +1425,8 @@ VecMap make_vec_map(int w, int h, int64_t ref_row_stride, int64_t ref_frame_stri
     M.pad_row_d = dist_row_stride / V - M.vpr;
     M.pad_frame_r = ref_frame_stride / V - M.frame_vecs;
     M.pad_frame_d = dist_frame_stride / V - M.frame_vecs;
+    M.phase_r = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ref) & 15u);
+    M.phase_d = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dist) & 15u);
     return M;
 }
 
@@ -1470,22 +1477,30 @@ hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, cons
     err = hipGetLastError();
     if (err != hipSuccess || !two_byte)
         return err;
+    const bool shifted = (map.phase_r | map.phase_d) != 0;
     // as many workgroups as the device holds at once, never more than there
     // can be slabs
     int64_t resident = 0;
-    err = maps_resident_workgroups(resident);
+    err = shifted ? maps_resident_workgroups<true>(resident) : maps_resident_workgroups<false>(resident);
     if (err != hipSuccess)
         return err;
     const int64_t slab_wgs = (g.workgroups * kSquares * kSlabs + kThreads / 64 - 1) / (kThreads / 64);
-    const int64_t wgs = slab_wgs < resident ? slab_wgs : resident;
-    cpu_order_maps<<<dim3(static_cast<unsigned>(wgs)), kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks,
-                                                                             g.nframes, rec, queue, maps, map);
+    const dim3 wgs(static_cast<unsigned>(slab_wgs < resident ? slab_wgs : resident));
+    if (shifted)
+        cpu_order_maps<true><<<wgs, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, g.nframes, rec, queue,
+                                                           maps, map);
+    else
+        cpu_order_maps<false><<<wgs, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, g.nframes, rec, queue,
+                                                            maps, map);
     err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    cpu_order_walk<<<dim3(nf * kSquares), 64 * kWalkWaves, 0, stream>>>(ref, dist, g.pixels, g.chunks, rec, totals,
-                                                                        maps, cmaps, bmaps, out_cpu_noise,
-                                                                        out_cpu_moments, map);
+    if (shifted)
+        cpu_order_walk<true><<<dim3(nf * kSquares), 64 * kWalkWaves, 0, stream>>>(
+            ref, dist, g.pixels, g.chunks, rec, totals, maps, cmaps, bmaps, out_cpu_noise, out_cpu_moments, map);
+    else
+        cpu_order_walk<false><<<dim3(nf * kSquares), 64 * kWalkWaves, 0, stream>>>(
+            ref, dist, g.pixels, g.chunks, rec, totals, maps, cmaps, bmaps, out_cpu_noise, out_cpu_moments, map);
     return hipGetLastError();
 }
 

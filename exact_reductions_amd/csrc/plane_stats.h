@@ -7,6 +7,8 @@
 
 namespace vqx {
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 // Number of 64-bit sums in one partial record, in this order.
 enum : int { kNoise = 0, kRef1 = 1, kDist1 = 2, kRef2 = 3, kDist2 = 4, kSums = 5 };
 
@@ -144,7 +146,7 @@ CpuOrderLayout cpu_order_layout(const Geometry &g);
 // Where the kernels that read plane views in place (the mapped stage 1, the
 // CPU-order maps and walk) find a batch's 16-byte vectors.  They index them
 // as if the batch were one contiguous [nframes][h][w] array (index v);
-// a pair of plane views whose rows are whole 16-byte aligned vectors maps v
+// a pair of plane views whose rows are whole 16-byte vectors maps v
 // of frame f to v + f*pad_frame + y*pad_row (in vectors) for each plane, y
 // the row of v in its frame.  vpr == 0: contiguous planes, v itself.
 struct VecMap {
@@ -153,12 +155,48 @@ struct VecMap {
     uint64_t magic = 0;      // y = (r * magic) >> shift for r < 2^22
     int shift = 0;
     int64_t pad_row_r = 0, pad_frame_r = 0, pad_row_d = 0, pad_frame_d = 0;
+    // where each plane's vectors start within 16 bytes (the same for all of
+    // them: rows and frames are whole vectors apart); the kernels then take
+    // the plane's base rounded down to 16 bytes
+    uint32_t phase_r = 0, phase_d = 0;
 };
 
-// The VecMap of two views of w x h planes (two-byte samples), strides in
-// samples; the caller has checked that rows are whole aligned vectors.
-VecMap make_vec_map(int w, int h, int64_t ref_row_stride, int64_t ref_frame_stride, int64_t dist_row_stride,
-                    int64_t dist_frame_stride);
+// Vector i of a plane whose vectors start `phase` bytes past 16-byte
+// boundaries, P the plane's base rounded down to 16 bytes: the 16 bytes at
+// `phase` in blocks i and i + 1 (each holds bytes of the vector, so both lie
+// in the plane's pages).  phase is uniform; 0 loads one block.
+__device__ __forceinline__ u32x4_t load_vec16(const u32x4_t *P, int64_t i, uint32_t phase)
+{
+    const u32x4_t lo = __builtin_nontemporal_load(P + i);
+    if (phase == 0)
+        return lo;
+    const u32x4_t hi = __builtin_nontemporal_load(P + i + 1);
+    const uint32_t q = phase >> 2, r = phase & 3;
+    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    uint32_t s[5];
+#pragma unroll
+    for (int m = 0; m < 5; ++m)
+        s[m] = q == 0 ? w[m] : q == 1 ? w[m + 1] : q == 2 ? w[m + 2] : w[m + 3];
+    u32x4_t o;
+    o.x = __builtin_amdgcn_alignbyte(s[1], s[0], r);
+    o.y = __builtin_amdgcn_alignbyte(s[2], s[1], r);
+    o.z = __builtin_amdgcn_alignbyte(s[3], s[2], r);
+    o.w = __builtin_amdgcn_alignbyte(s[4], s[3], r);
+    return o;
+}
+
+// The VecMap of two views of w x h planes (two-byte samples) at `ref` and
+// `dist`, strides in samples; the caller has checked that rows are whole
+// vectors (w and the strides multiples of 8).  The phases are those of the
+// bases; the kernels then take the bases rounded down to 16 bytes
+// (vec_base).
+VecMap make_vec_map(int w, int h, const void *ref, int64_t ref_row_stride, int64_t ref_frame_stride,
+                    const void *dist, int64_t dist_row_stride, int64_t dist_frame_stride);
+
+inline const void *vec_base(const void *p)
+{
+    return reinterpret_cast<const void *>(reinterpret_cast<uintptr_t>(p) & ~static_cast<uintptr_t>(15));
+}
 
 __device__ __forceinline__ void map_vec(const VecMap &M, int64_t frame, int64_t v, int64_t &vr, int64_t &vd)
 {

@@ -10,7 +10,8 @@
 // The CPU adds a view's samples in raster order whatever its pitch [PSNR,
 // Context; MOMENT, Context], so the chunks of a view are those of the same
 // frames stored contiguously.  Where the view's rows are whole 16-byte
-// aligned vectors of two-byte samples, this kernel reads vector v of that
+// vectors of two-byte samples (16-byte aligned, or for the CPU-order form
+// all at one offset within 16 bytes), this kernel reads vector v of that
 // contiguous order where the view keeps it (map_vec) and writes the records
 // the contiguous stage 1 writes for the same samples -- with the low bits of
 // the terms in the CPU-order form -- from the same terms in the same lane
@@ -34,12 +35,13 @@ constexpr int kLaneIters = kChunkVectors / kThreads;  // vectors per lane per pl
 constexpr int kInFlight = 4;                          // vectors of each plane loaded before use
 static_assert(kLaneIters % kInFlight == 0, "whole load groups");
 
-// Stage 1 over plane views whose rows are whole 16-byte aligned vectors
+// Stage 1 over plane views whose rows are whole 16-byte vectors
 // (two-byte samples, so frames hold no partial vectors): the same chunks,
 // terms and records as stage1_u16<kLowBitsOut>, each vector found through
 // the VecMap; kLowBitsOut: also the low bits of the terms and zero queue
-// lengths, for the CPU-order form.
-template <bool kLowBitsOut>
+// lengths, for the CPU-order form; kSh: the vectors start at the map's
+// phases within 16-byte blocks (ref and dist the bases rounded down).
+template <bool kLowBitsOut, bool kSh>
 __global__ __launch_bounds__(kThreads) void stage1_u16_mapped(const void *ref, const void *dist, int64_t pixels,
                                                               int chunks, uint64_t *part, VecMap M)
 {
@@ -69,8 +71,9 @@ __global__ __launch_bounds__(kThreads) void stage1_u16_mapped(const void *ref, c
                 const int64_t v = ok[u] ? v0 : cb;
                 const uint32_t r = static_cast<uint32_t>(v - vb);
                 const int64_t row = static_cast<int64_t>((static_cast<uint64_t>(r) * magic) >> M.shift);
-                x[u] = __builtin_nontemporal_load(R + (v + fr + row * M.pad_row_r));
-                y[u] = __builtin_nontemporal_load(D + (v + fd + row * M.pad_row_d));
+                const int64_t ar = v + fr + row * M.pad_row_r, ad = v + fd + row * M.pad_row_d;
+                x[u] = kSh ? load_vec16(R, ar, M.phase_r) : __builtin_nontemporal_load(R + ar);
+                y[u] = kSh ? load_vec16(D, ad, M.phase_d) : __builtin_nontemporal_load(D + ad);
             }
 #pragma unroll
             for (int u = 0; u < kInFlight; ++u) {
@@ -111,8 +114,11 @@ __global__ __launch_bounds__(kThreads) void mapped_combine(const uint64_t *part,
 hipError_t launch_stage1_mapped(const Geometry &g, const void *ref, const void *dist, uint64_t *partials,
                                 const VecMap &map, hipStream_t stream)
 {
-    stage1_u16_mapped<true><<<dim3(static_cast<unsigned>(g.workgroups)), kThreads, 0, stream>>>(
-        ref, dist, g.pixels, g.chunks, partials, map);
+    const dim3 grid(static_cast<unsigned>(g.workgroups));
+    if (map.phase_r | map.phase_d)
+        stage1_u16_mapped<true, true><<<grid, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, partials, map);
+    else
+        stage1_u16_mapped<true, false><<<grid, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, partials, map);
     return hipGetLastError();
 }
 
@@ -120,7 +126,9 @@ hipError_t launch_plane_stats_mapped(const Geometry &g, const void *ref, const v
                                      uint64_t *out_moments, uint64_t *partials, const VecMap &map,
                                      hipStream_t stream)
 {
-    stage1_u16_mapped<false><<<dim3(static_cast<unsigned>(g.workgroups)), kThreads, 0, stream>>>(
+    if (map.phase_r | map.phase_d)
+        return hipErrorInvalidValue;  // whole aligned vectors only
+    stage1_u16_mapped<false, false><<<dim3(static_cast<unsigned>(g.workgroups)), kThreads, 0, stream>>>(
         ref, dist, g.pixels, g.chunks, partials, map);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)

@@ -185,9 +185,10 @@ int check_planes(const vqx_plane_pair *planes, int nplanes, int bpc, int nframes
 
 // Whether a view's rows are whole 16-byte aligned vectors of two-byte
 // samples, which the CPU-order kernels read in place.
-bool rows_of_vectors(const void *base, int64_t row_stride, int64_t frame_stride, int w, int bpc)
+bool rows_of_vectors(const void *base, int64_t row_stride, int64_t frame_stride, int w, int bpc,
+                     size_t base_align = 16)
 {
-    return bpc > 8 && w % 8 == 0 && row_stride % 8 == 0 && frame_stride % 8 == 0 && aligned(base, 16);
+    return bpc > 8 && w % 8 == 0 && row_stride % 8 == 0 && frame_stride % 8 == 0 && aligned(base, base_align);
 }
 
 // The CPU-order form over plane views that are not rows of vectors: both
@@ -407,13 +408,14 @@ int vqx_plane_stats_view_cpu_order_ws(const void *ref, int64_t ref_row_stride, i
     hipStream_t s = static_cast<hipStream_t>(stream);
     const vqx::Geometry g = vqx::make_geometry(w, h, bpc, nframes);
     hipError_t err;
-    if (rows_of_vectors(ref, ref_row_stride, ref_frame_stride, w, bpc) &&
-        rows_of_vectors(dist, dist_row_stride, dist_frame_stride, w, bpc)) {
-        // read in place: each vector of the contiguous order found in the views
-        const vqx::VecMap map = vqx::make_vec_map(w, h, ref_row_stride, ref_frame_stride, dist_row_stride,
-                                                  dist_frame_stride);
-        err = vqx::launch_plane_stats_cpu_order(g, ref, dist, out_noise, out_moments, out_cpu_noise,
-                                                out_cpu_moments, workspace, s, map);
+    if (rows_of_vectors(ref, ref_row_stride, ref_frame_stride, w, bpc, 2) &&
+        rows_of_vectors(dist, dist_row_stride, dist_frame_stride, w, bpc, 2)) {
+        // read in place: each vector of the contiguous order found in the
+        // views, at the same offset within 16 bytes throughout each view
+        const vqx::VecMap map = vqx::make_vec_map(w, h, ref, ref_row_stride, ref_frame_stride, dist,
+                                                  dist_row_stride, dist_frame_stride);
+        err = vqx::launch_plane_stats_cpu_order(g, vqx::vec_base(ref), vqx::vec_base(dist), out_noise, out_moments,
+                                                out_cpu_noise, out_cpu_moments, workspace, s, map);
         if (err != hipSuccess) {
             (void)hipGetLastError();
             return VQX_E_HIP;
@@ -573,8 +575,8 @@ int vqx_plane_stats_view_ws(const void *ref, int64_t ref_row_stride, int64_t ref
         // rows of whole vectors: the contiguous chunks, each vector found in the views
         err = vqx::launch_plane_stats_mapped(cg, ref, dist, out_noise, out_moments,
                                              static_cast<uint64_t *>(workspace),
-                                             vqx::make_vec_map(w, h, ref_row_stride, ref_frame_stride,
-                                                               dist_row_stride, dist_frame_stride),
+                                             vqx::make_vec_map(w, h, ref, ref_row_stride, ref_frame_stride,
+                                                               dist, dist_row_stride, dist_frame_stride),
                                              static_cast<hipStream_t>(stream));
     } else {
         err = vqx::launch_view_stats(g, R, D, out_noise, out_moments, static_cast<uint64_t *>(workspace),

@@ -48,3 +48,7 @@ def test_pitched_plans_follow_the_in_place_rule():
     assert bench.step_plan("cpu-order", wl, 3904)[1][0] == "stage1_u16_mapped"
     assert bench.step_plan("cpu-order", wl, 3844)[1][0] == "gather_view"
     assert bench.step_plan("exact", synth.WORKLOADS[1], 600)[1][0] == "view_stage1"  # one-byte samples
+    # a frame 4 samples into rows of whole vectors: in place for the CPU-order form only
+    assert bench.step_plan("cpu-order", wl, 3904, 4)[1][0] == "stage1_u16_mapped"
+    assert bench.step_plan("exact", wl, 3904, 4)[1][0] == "view_stage1"
+    assert bench.step_plan("exact", wl, 3904, 8)[1][0] == "stage1_u16_mapped"

@@ -330,16 +330,47 @@ def test_view_form_in_place_15bit_past53():
 
 
 def test_view_form_unaligned_gathered():
-    """A view 4 samples in, and one of width 100: gathered, same results."""
+    """A view 4 samples in with a pitch of 122 samples (its rows start at
+    different offsets within 16 bytes), and one of width 100: gathered,
+    same results."""
     rng = np.random.default_rng(7)
-    big = rng.integers(0, 65535, size=(2, 50, 120), endpoint=True).astype(np.uint16)
-    big_d = rng.integers(0, 65535, size=(2, 50, 120), endpoint=True).astype(np.uint16)
+    big = rng.integers(0, 65535, size=(2, 50, 122), endpoint=True).astype(np.uint16)
+    big_d = rng.integers(0, 65535, size=(2, 50, 122), endpoint=True).astype(np.uint16)
     s4 = (slice(None), slice(None), slice(4, 100))
     _in_place_case(big[s4], big_d[s4], torch.from_numpy(big).cuda()[s4], torch.from_numpy(big_d).cuda()[s4], 16,
                    in_place=False)
     s100 = (slice(None), slice(None), slice(0, 100))
     _in_place_case(big[s100], big_d[s100], torch.from_numpy(big).cuda()[s100],
                    torch.from_numpy(big_d).cuda()[s100], 16, in_place=False)
+
+
+@pytest.mark.parametrize("xr,xd", [(4, 4), (1, 7), (0, 3), (5, 0), (2, 6)])
+def test_view_form_shifted_in_place(xr, xd):
+    """Views xr and xd samples in (so 2*xr and 2*xd bytes into 16-byte
+    blocks) of planes whose pitches are whole vectors: read in place, two
+    blocks per vector, same results."""
+    rng = np.random.default_rng(70 + 8 * xr + xd)
+    big = rng.integers(0, 65535, size=(3, 50, 128), endpoint=True).astype(np.uint16)
+    big_d = rng.integers(0, 65535, size=(3, 51, 136), endpoint=True).astype(np.uint16)
+    sr = (slice(None), slice(None), slice(xr, xr + 96))
+    sd = (slice(None), slice(1, 51), slice(xd, xd + 96))
+    _in_place_case(big[sr], big_d[sd], torch.from_numpy(big).cuda()[sr], torch.from_numpy(big_d).cuda()[sd], 16)
+
+
+@pytest.mark.parametrize("xr,xd", [(11, 21), (13, 13)])
+def test_view_form_shifted_in_place_past53(xr, xd):
+    """The 2560x1440 case past 2^53 with the regions 11 and 21 (and 13 and
+    13) samples in: the maps and the walk read shifted vectors in place."""
+    ref, dist = synth.past53_mixed(nframes=2)
+    f, h, w = ref.shape
+    big_r = np.zeros((f, h + 3, w + 64), dtype=np.uint16)
+    big_d = np.zeros((f, h + 4, w + 136), dtype=np.uint16)
+    big_r[:, 2:2 + h, xr:xr + w] = ref
+    big_d[:, 3:3 + h, xd:xd + w] = dist
+    sr = (slice(None), slice(2, 2 + h), slice(xr, xr + w))
+    sd = (slice(None), slice(3, 3 + h), slice(xd, xd + w))
+    R, D = torch.from_numpy(big_r).cuda()[sr], torch.from_numpy(big_d).cuda()[sd]
+    _in_place_case(big_r[sr], big_d[sd], R, D, 16)
 
 
 @pytest.mark.parametrize("seed", range(3))
@@ -354,6 +385,26 @@ def test_random_views_in_place_past53(seed):
     views = []
     for plane, (x0, extra) in zip((ref, dist), ((pads[0], pads[1]), (pads[2], pads[3]))):
         big = np.zeros((f, h, x0 + w8 + extra), dtype=np.uint16)
+        big[:, :, x0:x0 + w8] = plane[:, :, :w8]
+        sl = (slice(None), slice(None), slice(x0, x0 + w8))
+        views.append((big[sl], torch.from_numpy(big).cuda()[sl]))
+    (rn, R), (dn, D) = views
+    _in_place_case(rn, dn, R, D, 16)
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_random_views_shifted_in_place_past53(seed):
+    """As above, the regions at any sample offset in their rows (pitches
+    whole vectors): each view's vectors at one offset within 16 bytes."""
+    rng = np.random.default_rng(40630 + seed)
+    ref, dist = _random_case(rng)[:2]
+    f, h, w = ref.shape
+    w8 = w - w % 8
+    views = []
+    for plane in (ref, dist):
+        x0 = int(rng.integers(0, 64))
+        pitch = (x0 + w8 + 7) // 8 * 8 + 8 * int(rng.integers(0, 4))
+        big = np.zeros((f, h, pitch), dtype=np.uint16)
         big[:, :, x0:x0 + w8] = plane[:, :, :w8]
         sl = (slice(None), slice(None), slice(x0, x0 + w8))
         views.append((big[sl], torch.from_numpy(big).cuda()[sl]))
