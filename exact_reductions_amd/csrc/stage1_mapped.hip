@@ -39,9 +39,17 @@ static_assert(kLaneIters % kInFlight == 0, "whole load groups");
 // (two-byte samples, so frames hold no partial vectors): the same chunks,
 // terms and records as stage1_u16<kLowBitsOut>, each vector found through
 // the VecMap; kLowBitsOut: also the low bits of the terms and zero queue
-// lengths, for the CPU-order form; kSh: the vectors start at the map's
-// phases within 16-byte blocks (ref and dist the bases rounded down).
-template <bool kLowBitsOut, bool kSh>
+// lengths, for the CPU-order form; kForm: as above (ref and dist the
+// bases rounded down to 16 bytes where a phase is not 0).
+// Where the planes' vectors start within 16-byte blocks: at 0 (one block
+// per vector); at one phase in both planes (kRotated: two blocks, the
+// vector's samples in rotated order, which neither an integer sum nor the
+// OR of the terms' low bits sees, and the same rotation pairs each ref
+// sample with its dist sample); or at other phases (kShifted: the samples
+// cut out in order).
+enum : int { kAligned = 0, kRotated = 1, kShifted = 2 };
+
+template <bool kLowBitsOut, int kForm>
 __global__ __launch_bounds__(kThreads) void stage1_u16_mapped(const void *ref, const void *dist, int64_t pixels,
                                                               int chunks, uint64_t *part, VecMap M)
 {
@@ -58,6 +66,13 @@ __global__ __launch_bounds__(kThreads) void stage1_u16_mapped(const void *ref, c
     // magic < 2^24, so the product fits 64 bits from 32-bit factors
     const int64_t fr = frame * M.pad_frame_r, fd = frame * M.pad_frame_d;
     const uint32_t magic = static_cast<uint32_t>(M.magic);
+    // kRotated: the bytes of a block at or past the phase
+    u32x4 keep;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int b = static_cast<int>(M.phase_r) - 4 * k;  // bytes of dword k before the phase
+        keep[k] = b <= 0 ? 0xffffffffu : b >= 4 ? 0u : 0xffffffffu << (8 * b);
+    }
     typename std::conditional<kLowBitsOut, Acc16Low, Acc16F64>::type a;
     if (cb < ce) {
 #pragma unroll 1
@@ -72,8 +87,23 @@ __global__ __launch_bounds__(kThreads) void stage1_u16_mapped(const void *ref, c
                 const uint32_t r = static_cast<uint32_t>(v - vb);
                 const int64_t row = static_cast<int64_t>((static_cast<uint64_t>(r) * magic) >> M.shift);
                 const int64_t ar = v + fr + row * M.pad_row_r, ad = v + fd + row * M.pad_row_d;
-                x[u] = kSh ? load_vec16(R, ar, M.phase_r) : __builtin_nontemporal_load(R + ar);
-                y[u] = kSh ? load_vec16(D, ad, M.phase_d) : __builtin_nontemporal_load(D + ad);
+                if constexpr (kForm == kRotated) {
+                    // vector = the part of block ar from the phase on and the
+                    // part of block ar + 1 before it, as one 16-byte value
+                    // whose samples are rotated (the same way in both
+                    // planes); cached loads, as block ar + 1 is also the next
+                    // vector's block ar
+                    const u32x4 lr = R[ar], hr = R[ar + 1];
+                    const u32x4 ld = D[ad], hd = D[ad + 1];
+                    x[u] = (lr & keep) | (hr & ~keep);
+                    y[u] = (ld & keep) | (hd & ~keep);
+                } else if constexpr (kForm == kShifted) {
+                    x[u] = load_vec16(R, ar, M.phase_r);
+                    y[u] = load_vec16(D, ad, M.phase_d);
+                } else {
+                    x[u] = __builtin_nontemporal_load(R + ar);
+                    y[u] = __builtin_nontemporal_load(D + ad);
+                }
             }
 #pragma unroll
             for (int u = 0; u < kInFlight; ++u) {
@@ -115,10 +145,15 @@ hipError_t launch_stage1_mapped(const Geometry &g, const void *ref, const void *
                                 const VecMap &map, hipStream_t stream)
 {
     const dim3 grid(static_cast<unsigned>(g.workgroups));
-    if (map.phase_r | map.phase_d)
-        stage1_u16_mapped<true, true><<<grid, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, partials, map);
+    if (map.phase_r == 0 && map.phase_d == 0)
+        stage1_u16_mapped<true, kAligned><<<grid, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, partials,
+                                                                        map);
+    else if (map.phase_r == map.phase_d)
+        stage1_u16_mapped<true, kRotated><<<grid, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, partials,
+                                                                        map);
     else
-        stage1_u16_mapped<true, false><<<grid, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, partials, map);
+        stage1_u16_mapped<true, kShifted><<<grid, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, partials,
+                                                                        map);
     return hipGetLastError();
 }
 
@@ -128,7 +163,7 @@ hipError_t launch_plane_stats_mapped(const Geometry &g, const void *ref, const v
 {
     if (map.phase_r | map.phase_d)
         return hipErrorInvalidValue;  // whole aligned vectors only
-    stage1_u16_mapped<false, false><<<dim3(static_cast<unsigned>(g.workgroups)), kThreads, 0, stream>>>(
+    stage1_u16_mapped<false, kAligned><<<dim3(static_cast<unsigned>(g.workgroups)), kThreads, 0, stream>>>(
         ref, dist, g.pixels, g.chunks, partials, map);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
