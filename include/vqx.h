@@ -330,11 +330,13 @@ int vqx_psnr_int_view_ws(const void *ref, int64_t ref_row_stride, int64_t ref_fr
  * samples in raster order, row after row, whatever the pitch [PSNR,
  * Context; MOMENT, Context].  Where both views hold two-byte samples (bpc
  * 9..16) in rows of whole 16-byte vectors (w, both row strides and both
- * frame strides multiples of 8 samples; both bases 16-byte aligned) they are
- * read in place, at the contiguous form's speed.  Other views are first
- * copied into contiguous planes inside the workspace (about twice the
- * contiguous form's time), then reduced as the contiguous form does; the
- * results are the same either way.  Errors as for the views and the
+ * frame strides multiples of 8 samples; each base aligned to its samples)
+ * they are read in place: at the contiguous form's speed where both bases
+ * are 16-byte aligned, else from the two aligned 16-byte blocks that hold
+ * each vector (about 1.25 times the contiguous form's time).  Other views
+ * are first copied into contiguous planes inside the workspace (about
+ * three times the contiguous form's time), then reduced as the contiguous
+ * form does; the results are the same either way.  Errors as for the views and the
  * contiguous CPU-order form; the workspace is
  * vqx_plane_stats_view_cpu_order_workspace_bytes() (the contiguous form's
  * and both planes of the batch, whichever way the call reads).
