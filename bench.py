@@ -88,19 +88,19 @@ def step_plan(mode: str, wl, pitch: int = 0, x0: int = 0):
     with a pitch (rows of ``pitch`` samples, the frame ``x0`` samples into
     each) go through the view entry points, which read rows of whole 16-byte
     vectors of two-byte samples in place with the contiguous chunks
-    ("mapped": aligned vectors for the exact sums, vectors at any one offset
+    ("mapped": aligned vectors for the exact sums, vectors at any offsets
     within 16 bytes for the CPU-order form) and gather or tile other
     layouts."""
-    mapped = bool(pitch) and wl.bpc > 8 and wl.w % 8 == 0 and pitch % 8 == 0
+    vectors = bool(pitch) and wl.bpc > 8 and wl.w % 8 == 0  # rows of whole vectors
     if mode == "exact" and pitch:
-        if mapped and x0 % 8 == 0:
+        if vectors and pitch % 8 == 0 and x0 % 8 == 0:
             return "mapped_step", ("stage1_u16_mapped", "mapped_combine"), MAPPED_SOURCES
         return "view_step", ("view_stage1", "view_combine"), VIEW_SOURCES
     if mode == "exact":
         k = "stage1_u8" if wl.bpc == 8 else "stage1_u16"
         return k, (k,), STAGE1_SOURCES
     if mode == "cpu-order":
-        if pitch and mapped:
+        if vectors:
             return ("cpu_order_step", ("stage1_u16_mapped",) + CPU_ORDER_KERNELS[1:],
                     CPU_ORDER_SOURCES + [os.path.join(CSRC, "stage1_mapped.hip")])
         if pitch:

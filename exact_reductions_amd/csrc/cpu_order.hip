@@ -380,21 +380,24 @@ __device__ __forceinline__ uint32_t vector_term(const u32x4 &a, const u32x4 &b, 
 // `safe` (one known to exist) instead, for the caller to drop (keep_if).
 // Every lane loads, so no branch separates the loads from the waits for
 // them and the next vectors can be in flight while these are used.
-// kSh: the planes' vectors start at the map's phases within 16-byte
-// blocks (R and D then the bases rounded down to 16 bytes).
+// kSh: the map is general (R and D the bases rounded down to 16 bytes;
+// each vector cut from the blocks that hold it).
 template <int KK, bool kSh>
 __device__ __forceinline__ void load_vector(const u32x4 *R, const u32x4 *D, const VecMap &M, int64_t frame,
                                             int64_t v, bool ok, int64_t safe, u32x4 &a, u32x4 &b)
 {
     const u32x4 zero = {0, 0, 0, 0};
     int64_t ar, ad;
-    map_vec(M, frame, ok ? v : safe, ar, ad);
+    if constexpr (kSh)
+        map_vec_bytes(M, frame, ok ? v : safe, ar, ad);
+    else
+        map_vec(M, frame, ok ? v : safe, ar, ad);
     if constexpr (KK != kSqDist)
-        a = kSh ? load_vec16(R, ar, M.phase_r) : __builtin_nontemporal_load(R + ar);
+        a = kSh ? load_vec16_at(R, ar) : __builtin_nontemporal_load(R + ar);
     else
         a = zero;
     if constexpr (KK != kSqRef)
-        b = kSh ? load_vec16(D, ad, M.phase_d) : __builtin_nontemporal_load(D + ad);
+        b = kSh ? load_vec16_at(D, ad) : __builtin_nontemporal_load(D + ad);
     else
         b = zero;
 }
@@ -1427,6 +1430,14 @@ VecMap make_vec_map(int w, int h, const void *ref, int64_t ref_row_stride, int64
     M.pad_frame_d = dist_frame_stride / V - M.frame_vecs;
     M.phase_r = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ref) & 15u);
     M.phase_d = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dist) & 15u);
+    M.row_bytes_r = 2 * ref_row_stride;
+    M.frame_bytes_r = 2 * ref_frame_stride;
+    M.row_bytes_d = 2 * dist_row_stride;
+    M.frame_bytes_d = 2 * dist_frame_stride;
+    const int64_t odd = (M.row_bytes_r | M.frame_bytes_r | M.row_bytes_d | M.frame_bytes_d) & 15;
+    M.general = (M.phase_r | M.phase_d | static_cast<uint32_t>(odd)) != 0;
+    M.same_phases = M.phase_r == M.phase_d && ((M.row_bytes_r - M.row_bytes_d) & 15) == 0 &&
+                    ((M.frame_bytes_r - M.frame_bytes_d) & 15) == 0;
     return M;
 }
 
@@ -1477,7 +1488,7 @@ hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, cons
     err = hipGetLastError();
     if (err != hipSuccess || !two_byte)
         return err;
-    const bool shifted = (map.phase_r | map.phase_d) != 0;
+    const bool shifted = map.general != 0;
     // as many workgroups as the device holds at once, never more than there
     // can be slabs
     int64_t resident = 0;

@@ -155,22 +155,23 @@ struct VecMap {
     uint64_t magic = 0;      // y = (r * magic) >> shift for r < 2^22
     int shift = 0;
     int64_t pad_row_r = 0, pad_frame_r = 0, pad_row_d = 0, pad_frame_d = 0;
-    // where each plane's vectors start within 16 bytes (the same for all of
-    // them: rows and frames are whole vectors apart); the kernels then take
-    // the plane's base rounded down to 16 bytes
+    // general != 0: some vector does not start on a 16-byte boundary.  The
+    // kernels then take each plane's base rounded down to 16 bytes and find
+    // vector (f, y, x) at byte phase + f*frame_bytes + y*row_bytes + 16*x
+    // from there; same_phases: ref's and dist's vectors start at the same
+    // offset within 16 bytes throughout.
+    uint32_t general = 0, same_phases = 0;
     uint32_t phase_r = 0, phase_d = 0;
+    int64_t row_bytes_r = 0, frame_bytes_r = 0, row_bytes_d = 0, frame_bytes_d = 0;
 };
 
-// Vector i of a plane whose vectors start `phase` bytes past 16-byte
-// boundaries, P the plane's base rounded down to 16 bytes: the 16 bytes at
-// `phase` in blocks i and i + 1 (each holds bytes of the vector, so both lie
-// in the plane's pages).  phase is uniform; 0 loads one block.
-__device__ __forceinline__ u32x4_t load_vec16(const u32x4_t *P, int64_t i, uint32_t phase)
+// The 16 bytes at `phase` (0..15) in two consecutive 16-byte blocks: a
+// vector that starts `phase` bytes past a 16-byte boundary lies in the
+// block that holds its first byte and the next (each holds bytes of the
+// vector, so both lie in the plane's pages).  phase may differ from lane
+// to lane; at 0 the result is lo.
+__device__ __forceinline__ u32x4_t vec16_at(const u32x4_t &lo, const u32x4_t &hi, uint32_t phase)
 {
-    const u32x4_t lo = __builtin_nontemporal_load(P + i);
-    if (phase == 0)
-        return lo;
-    const u32x4_t hi = __builtin_nontemporal_load(P + i + 1);
     const uint32_t q = phase >> 2, r = phase & 3;
     const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     uint32_t s[5];
@@ -185,11 +186,34 @@ __device__ __forceinline__ u32x4_t load_vec16(const u32x4_t *P, int64_t i, uint3
     return o;
 }
 
+// The 16 bytes at byte offset `at` (even, >= 0) from P, a 16-byte aligned
+// base: cut from the block that holds the first of them and the next one
+// (the same block again where `at` is a multiple of 16, so no read passes
+// the vector's own blocks).  Non-temporal loads: the planes are read once.
+__device__ __forceinline__ u32x4_t load_vec16_at(const u32x4_t *P, int64_t at)
+{
+    const int64_t block = at >> 4;
+    const uint32_t phase = static_cast<uint32_t>(at & 15);
+    return vec16_at(__builtin_nontemporal_load(P + block), __builtin_nontemporal_load(P + block + (phase ? 1 : 0)),
+                    phase);
+}
+
+// Byte offset of vector v (index in the batch's contiguous order) of frame
+// `frame` in each plane, from the bases rounded down (general maps, whose
+// frames span less than 2^31 bytes, so offsets inside a frame are 32-bit).
+__device__ __forceinline__ void map_vec_bytes(const VecMap &M, int64_t frame, int64_t v, int64_t &br, int64_t &bd)
+{
+    const uint32_t r = static_cast<uint32_t>(v - frame * M.frame_vecs);  // below 2^22
+    const uint32_t y = static_cast<uint32_t>((static_cast<uint64_t>(r) * M.magic) >> M.shift);
+    const uint32_t x16 = 16 * (r - y * M.vpr);
+    br = M.phase_r + frame * M.frame_bytes_r + (y * static_cast<uint32_t>(M.row_bytes_r) + x16);
+    bd = M.phase_d + frame * M.frame_bytes_d + (y * static_cast<uint32_t>(M.row_bytes_d) + x16);
+}
+
 // The VecMap of two views of w x h planes (two-byte samples) at `ref` and
-// `dist`, strides in samples; the caller has checked that rows are whole
-// vectors (w and the strides multiples of 8).  The phases are those of the
-// bases; the kernels then take the bases rounded down to 16 bytes
-// (vec_base).
+// `dist` (two-byte aligned), strides in samples; the caller has checked
+// that rows are whole vectors (w a multiple of 8).  Where `general` is set
+// the kernels take the bases rounded down to 16 bytes (vec_base).
 VecMap make_vec_map(int w, int h, const void *ref, int64_t ref_row_stride, int64_t ref_frame_stride,
                     const void *dist, int64_t dist_row_stride, int64_t dist_frame_stride);
 

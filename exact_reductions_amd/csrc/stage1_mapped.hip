@@ -41,13 +41,31 @@ static_assert(kLaneIters % kInFlight == 0, "whole load groups");
 // the VecMap; kLowBitsOut: also the low bits of the terms and zero queue
 // lengths, for the CPU-order form; kForm: as above (ref and dist the
 // bases rounded down to 16 bytes where a phase is not 0).
-// Where the planes' vectors start within 16-byte blocks: at 0 (one block
-// per vector); at one phase in both planes (kRotated: two blocks, the
-// vector's samples in rotated order, which neither an integer sum nor the
-// OR of the terms' low bits sees, and the same rotation pairs each ref
-// sample with its dist sample); or at other phases (kShifted: the samples
-// cut out in order).
-enum : int { kAligned = 0, kRotated = 1, kShifted = 2 };
+// Where the planes' vectors start within 16-byte blocks: all at 0 (one
+// block per vector, found with the map's pads); at the same phase in both
+// planes for every vector, the phase possibly changing from row to row
+// (kRotated: two blocks, the vector's samples in rotated order, which
+// neither an integer sum nor the OR of the terms' low bits sees, and the
+// same rotation pairs each ref sample with its dist sample); or otherwise
+// (kShifted: the samples cut out in order).  The last two find vectors with
+// the map's byte strides.  kRotatedUniform: kRotated where strides are
+// whole vectors, so one phase holds throughout and the vectors are found
+// with the pads.
+enum : int { kAligned = 0, kRotated = 1, kShifted = 2, kRotatedUniform = 3 };
+
+// Mask of the bytes of a 16-byte block at or past byte `ph` (0..15).
+__device__ __forceinline__ u32x4 bytes_from(uint32_t ph)
+{
+    const uint32_t sh = 8 * ph;
+    const uint64_t lo = sh >= 64 ? 0ull : ~0ull << (sh & 63);
+    const uint64_t hi = sh <= 64 ? ~0ull : ~0ull << ((sh - 64) & 63);
+    u32x4 m;
+    m.x = static_cast<uint32_t>(lo);
+    m.y = static_cast<uint32_t>(lo >> 32);
+    m.z = static_cast<uint32_t>(hi);
+    m.w = static_cast<uint32_t>(hi >> 32);
+    return m;
+}
 
 template <bool kLowBitsOut, int kForm>
 __global__ __launch_bounds__(kThreads) void stage1_u16_mapped(const void *ref, const void *dist, int64_t pixels,
@@ -66,13 +84,14 @@ __global__ __launch_bounds__(kThreads) void stage1_u16_mapped(const void *ref, c
     // magic < 2^24, so the product fits 64 bits from 32-bit factors
     const int64_t fr = frame * M.pad_frame_r, fd = frame * M.pad_frame_d;
     const uint32_t magic = static_cast<uint32_t>(M.magic);
-    // kRotated: the bytes of a block at or past the phase
-    u32x4 keep;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int b = static_cast<int>(M.phase_r) - 4 * k;  // bytes of dword k before the phase
-        keep[k] = b <= 0 ? 0xffffffffu : b >= 4 ? 0u : 0xffffffffu << (8 * b);
-    }
+    // general maps: each plane's frame from the 16-byte block that holds its
+    // first byte (Rf, Df), and 32-bit byte offsets from there (a frame's
+    // rows span less than 2^31 bytes on this path)
+    const int64_t fbr = M.phase_r + frame * M.frame_bytes_r, fbd = M.phase_d + frame * M.frame_bytes_d;
+    const u32x4 *Rf = R + (fbr >> 4), *Df = D + (fbd >> 4);
+    const uint32_t lor = static_cast<uint32_t>(fbr & 15), lod = static_cast<uint32_t>(fbd & 15);
+    const uint32_t rbr = static_cast<uint32_t>(M.row_bytes_r), rbd = static_cast<uint32_t>(M.row_bytes_d);
+    const u32x4 keep = bytes_from(M.phase_r);  // kRotatedUniform (phase_r == phase_d there)
     typename std::conditional<kLowBitsOut, Acc16Low, Acc16F64>::type a;
     if (cb < ce) {
 #pragma unroll 1
@@ -86,23 +105,35 @@ __global__ __launch_bounds__(kThreads) void stage1_u16_mapped(const void *ref, c
                 const int64_t v = ok[u] ? v0 : cb;
                 const uint32_t r = static_cast<uint32_t>(v - vb);
                 const int64_t row = static_cast<int64_t>((static_cast<uint64_t>(r) * magic) >> M.shift);
-                const int64_t ar = v + fr + row * M.pad_row_r, ad = v + fd + row * M.pad_row_d;
-                if constexpr (kForm == kRotated) {
-                    // vector = the part of block ar from the phase on and the
-                    // part of block ar + 1 before it, as one 16-byte value
-                    // whose samples are rotated (the same way in both
-                    // planes); cached loads, as block ar + 1 is also the next
-                    // vector's block ar
-                    const u32x4 lr = R[ar], hr = R[ar + 1];
-                    const u32x4 ld = D[ad], hd = D[ad + 1];
-                    x[u] = (lr & keep) | (hr & ~keep);
-                    y[u] = (ld & keep) | (hd & ~keep);
-                } else if constexpr (kForm == kShifted) {
-                    x[u] = load_vec16(R, ar, M.phase_r);
-                    y[u] = load_vec16(D, ad, M.phase_d);
-                } else {
+                if constexpr (kForm == kAligned) {
+                    const int64_t ar = v + fr + row * M.pad_row_r, ad = v + fd + row * M.pad_row_d;
                     x[u] = __builtin_nontemporal_load(R + ar);
                     y[u] = __builtin_nontemporal_load(D + ad);
+                } else if constexpr (kForm == kRotatedUniform) {
+                    const int64_t ar = v + fr + row * M.pad_row_r, ad = v + fd + row * M.pad_row_d;
+                    x[u] = (R[ar] & keep) | (R[ar + 1] & ~keep);
+                    y[u] = (D[ad] & keep) | (D[ad + 1] & ~keep);
+                } else {
+                    const uint32_t yr = static_cast<uint32_t>(row);
+                    const uint32_t x16 = 16 * (r - yr * M.vpr);
+                    const uint32_t br = lor + yr * rbr + x16, bd = lod + yr * rbd + x16;
+                    if constexpr (kForm == kRotated) {
+                        // the part of the vector's first block from its phase
+                        // on and the part of the next block before it, as one
+                        // 16-byte value whose samples are rotated (the same
+                        // way in both planes); cached loads, as the next block
+                        // is also the next vector's first
+                        const uint32_t ph = br & 15;
+                        const uint32_t nb = ph ? 1u : 0u;
+                        const u32x4 lr = Rf[br >> 4], hr = Rf[(br >> 4) + nb];
+                        const u32x4 ld = Df[bd >> 4], hd = Df[(bd >> 4) + nb];
+                        const u32x4 keep = bytes_from(ph);
+                        x[u] = (lr & keep) | (hr & ~keep);
+                        y[u] = (ld & keep) | (hd & ~keep);
+                    } else {
+                        x[u] = load_vec16_at(Rf, br);
+                        y[u] = load_vec16_at(Df, bd);
+                    }
                 }
             }
 #pragma unroll
@@ -145,10 +176,13 @@ hipError_t launch_stage1_mapped(const Geometry &g, const void *ref, const void *
                                 const VecMap &map, hipStream_t stream)
 {
     const dim3 grid(static_cast<unsigned>(g.workgroups));
-    if (map.phase_r == 0 && map.phase_d == 0)
+    if (!map.general)
         stage1_u16_mapped<true, kAligned><<<grid, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, partials,
                                                                         map);
-    else if (map.phase_r == map.phase_d)
+    else if (map.same_phases && ((map.row_bytes_r | map.frame_bytes_r) & 15) == 0)
+        stage1_u16_mapped<true, kRotatedUniform><<<grid, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks,
+                                                                               partials, map);
+    else if (map.same_phases)
         stage1_u16_mapped<true, kRotated><<<grid, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, partials,
                                                                         map);
     else
@@ -161,7 +195,7 @@ hipError_t launch_plane_stats_mapped(const Geometry &g, const void *ref, const v
                                      uint64_t *out_moments, uint64_t *partials, const VecMap &map,
                                      hipStream_t stream)
 {
-    if (map.phase_r | map.phase_d)
+    if (map.general)
         return hipErrorInvalidValue;  // whole aligned vectors only
     stage1_u16_mapped<false, kAligned><<<dim3(static_cast<unsigned>(g.workgroups)), kThreads, 0, stream>>>(
         ref, dist, g.pixels, g.chunks, partials, map);

@@ -185,10 +185,19 @@ int check_planes(const vqx_plane_pair *planes, int nplanes, int bpc, int nframes
 
 // Whether a view's rows are whole 16-byte aligned vectors of two-byte
 // samples, which the CPU-order kernels read in place.
-bool rows_of_vectors(const void *base, int64_t row_stride, int64_t frame_stride, int w, int bpc,
-                     size_t base_align = 16)
+bool rows_of_vectors(const void *base, int64_t row_stride, int64_t frame_stride, int w, int bpc)
 {
-    return bpc > 8 && w % 8 == 0 && row_stride % 8 == 0 && frame_stride % 8 == 0 && aligned(base, base_align);
+    return bpc > 8 && w % 8 == 0 && row_stride % 8 == 0 && frame_stride % 8 == 0 && aligned(base, 16);
+}
+
+// Rows of whole 16-byte vectors of two-byte samples, wherever they start,
+// whose frames span less than 2^31 bytes from their first row's start to
+// their last row's end (the mapped stage 1 keeps offsets inside a frame in
+// 32 bits).
+bool rows_of_any_vectors(const void *base, int64_t row_stride, int w, int h, int bpc)
+{
+    return bpc > 8 && w % 8 == 0 && aligned(base, 2) &&
+           (static_cast<int64_t>(h) - 1) * row_stride + w + 16 < (static_cast<int64_t>(1) << 30);
 }
 
 // The CPU-order form over plane views that are not rows of vectors: both
@@ -408,10 +417,9 @@ int vqx_plane_stats_view_cpu_order_ws(const void *ref, int64_t ref_row_stride, i
     hipStream_t s = static_cast<hipStream_t>(stream);
     const vqx::Geometry g = vqx::make_geometry(w, h, bpc, nframes);
     hipError_t err;
-    if (rows_of_vectors(ref, ref_row_stride, ref_frame_stride, w, bpc, 2) &&
-        rows_of_vectors(dist, dist_row_stride, dist_frame_stride, w, bpc, 2)) {
+    if (rows_of_any_vectors(ref, ref_row_stride, w, h, bpc) && rows_of_any_vectors(dist, dist_row_stride, w, h, bpc)) {
         // read in place: each vector of the contiguous order found in the
-        // views, at the same offset within 16 bytes throughout each view
+        // views, at whatever offset within 16 bytes its row puts it
         const vqx::VecMap map = vqx::make_vec_map(w, h, ref, ref_row_stride, ref_frame_stride, dist,
                                                   dist_row_stride, dist_frame_stride);
         err = vqx::launch_plane_stats_cpu_order(g, vqx::vec_base(ref), vqx::vec_base(dist), out_noise, out_moments,

@@ -329,14 +329,15 @@ int vqx_psnr_int_view_ws(const void *ref, int64_t ref_row_stride, int64_t ref_fr
  * too, of views with any row and frame stride -- the CPU adds a view's
  * samples in raster order, row after row, whatever the pitch [PSNR,
  * Context; MOMENT, Context].  Where both views hold two-byte samples (bpc
- * 9..16) in rows of whole 16-byte vectors (w, both row strides and both
- * frame strides multiples of 8 samples; each base aligned to its samples)
- * they are read in place: at the contiguous form's speed where both bases
- * are 16-byte aligned, else from the two aligned 16-byte blocks that hold
- * each vector (about 1.25 times the contiguous form's time).  Other views
- * are first copied into contiguous planes inside the workspace (about
- * three times the contiguous form's time), then reduced as the contiguous
- * form does; the results are the same either way.  Errors as for the views and the
+ * 9..16) in rows of whole 16-byte vectors (w a multiple of 8 samples; any
+ * strides; each base aligned to its samples; a frame's rows spanning less
+ * than 2^31 bytes) they are read in place: at the contiguous form's speed
+ * where both bases are 16-byte aligned and all strides multiples of 8
+ * samples, else from the two aligned 16-byte blocks that hold each vector
+ * (about 1.3 to 1.4 times the contiguous form's time).  Other views are
+ * first copied into contiguous planes inside the workspace (about three
+ * times the contiguous form's time), then reduced as the contiguous form
+ * does; the results are the same either way.  Errors as for the views and the
  * contiguous CPU-order form; the workspace is
  * vqx_plane_stats_view_cpu_order_workspace_bytes() (the contiguous form's
  * and both planes of the batch, whichever way the call reads).

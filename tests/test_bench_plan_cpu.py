@@ -46,7 +46,8 @@ def test_pitched_plans_follow_the_in_place_rule():
     assert bench.step_plan("exact", wl, 3904)[1][0] == "stage1_u16_mapped"   # whole aligned vectors
     assert bench.step_plan("exact", wl, 3844)[1][0] == "view_stage1"         # rows at other offsets
     assert bench.step_plan("cpu-order", wl, 3904)[1][0] == "stage1_u16_mapped"
-    assert bench.step_plan("cpu-order", wl, 3844)[1][0] == "gather_view"
+    assert bench.step_plan("cpu-order", wl, 3844)[1][0] == "stage1_u16_mapped"  # rows at varying phases
+    assert bench.step_plan("cpu-order", synth.WORKLOADS[1], 600)[1][0] == "gather_view"  # one-byte samples
     assert bench.step_plan("exact", synth.WORKLOADS[1], 600)[1][0] == "view_stage1"  # one-byte samples
     # a frame 4 samples into rows of whole vectors: in place for the CPU-order form only
     assert bench.step_plan("cpu-order", wl, 3904, 4)[1][0] == "stage1_u16_mapped"

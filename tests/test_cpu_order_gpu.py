@@ -331,14 +331,13 @@ def test_view_form_in_place_15bit_past53():
 
 def test_view_form_unaligned_gathered():
     """A view 4 samples in with a pitch of 122 samples (its rows start at
-    different offsets within 16 bytes), and one of width 100: gathered,
-    same results."""
+    different offsets within 16 bytes): read in place; one of width 100
+    (rows not whole vectors): gathered; same results."""
     rng = np.random.default_rng(7)
     big = rng.integers(0, 65535, size=(2, 50, 122), endpoint=True).astype(np.uint16)
     big_d = rng.integers(0, 65535, size=(2, 50, 122), endpoint=True).astype(np.uint16)
     s4 = (slice(None), slice(None), slice(4, 100))
-    _in_place_case(big[s4], big_d[s4], torch.from_numpy(big).cuda()[s4], torch.from_numpy(big_d).cuda()[s4], 16,
-                   in_place=False)
+    _in_place_case(big[s4], big_d[s4], torch.from_numpy(big).cuda()[s4], torch.from_numpy(big_d).cuda()[s4], 16)
     s100 = (slice(None), slice(None), slice(0, 100))
     _in_place_case(big[s100], big_d[s100], torch.from_numpy(big).cuda()[s100],
                    torch.from_numpy(big_d).cuda()[s100], 16, in_place=False)
@@ -355,6 +354,36 @@ def test_view_form_shifted_in_place(xr, xd):
     sr = (slice(None), slice(None), slice(xr, xr + 96))
     sd = (slice(None), slice(1, 51), slice(xd, xd + 96))
     _in_place_case(big[sr], big_d[sd], torch.from_numpy(big).cuda()[sr], torch.from_numpy(big_d).cuda()[sd], 16)
+
+
+@pytest.mark.parametrize("pr,pd,xr,xd", [(122, 122, 4, 4), (122, 122, 4, 5), (122, 131, 0, 0), (125, 127, 3, 1),
+                                         (121, 129, 2, 2)])
+def test_view_form_varying_phases_in_place(pr, pd, xr, xd):
+    """Pitches that are not whole vectors: each row starts at its own offset
+    within 16 bytes (the same in ref and dist, or not); read in place."""
+    rng = np.random.default_rng(pr * 1000 + pd + 10 * xr + xd)
+    big = rng.integers(0, 65535, size=(3, 40, pr), endpoint=True).astype(np.uint16)
+    big_d = rng.integers(0, 65535, size=(3, 41, pd), endpoint=True).astype(np.uint16)
+    sr = (slice(None), slice(None), slice(xr, xr + 96))
+    sd = (slice(None), slice(1, 41), slice(xd, xd + 96))
+    _in_place_case(big[sr], big_d[sd], torch.from_numpy(big).cuda()[sr], torch.from_numpy(big_d).cuda()[sd], 16)
+
+
+@pytest.mark.parametrize("er,ed", [(61, 63), (60, 60)])
+def test_view_form_varying_phases_in_place_past53(er, ed):
+    """The 2560x1440 region past 2^53 in planes whose pitches are w + er and
+    w + ed samples (rows at varying offsets within 16 bytes), 5 and 7
+    samples in: the maps and the walk cut each vector from its row."""
+    ref, dist = synth.past53_mixed(nframes=2)
+    f, h, w = ref.shape
+    big_r = np.zeros((f, h + 3, w + er), dtype=np.uint16)
+    big_d = np.zeros((f, h + 4, w + ed), dtype=np.uint16)
+    big_r[:, 2:2 + h, 5:5 + w] = ref
+    big_d[:, 3:3 + h, 7:7 + w] = dist
+    sr = (slice(None), slice(2, 2 + h), slice(5, 5 + w))
+    sd = (slice(None), slice(3, 3 + h), slice(7, 7 + w))
+    R, D = torch.from_numpy(big_r).cuda()[sr], torch.from_numpy(big_d).cuda()[sd]
+    _in_place_case(big_r[sr], big_d[sd], R, D, 16)
 
 
 @pytest.mark.parametrize("xr,xd", [(11, 21), (13, 13)])
@@ -394,8 +423,7 @@ def test_random_views_in_place_past53(seed):
 
 @pytest.mark.parametrize("seed", range(2))
 def test_random_views_shifted_in_place_past53(seed):
-    """As above, the regions at any sample offset in their rows (pitches
-    whole vectors): each view's vectors at one offset within 16 bytes."""
+    """As above, the regions at any sample offset in rows of any pitch."""
     rng = np.random.default_rng(40630 + seed)
     ref, dist = _random_case(rng)[:2]
     f, h, w = ref.shape
@@ -403,7 +431,7 @@ def test_random_views_shifted_in_place_past53(seed):
     views = []
     for plane in (ref, dist):
         x0 = int(rng.integers(0, 64))
-        pitch = (x0 + w8 + 7) // 8 * 8 + 8 * int(rng.integers(0, 4))
+        pitch = x0 + w8 + int(rng.integers(0, 40))
         big = np.zeros((f, h, pitch), dtype=np.uint16)
         big[:, :, x0:x0 + w8] = plane[:, :, :w8]
         sl = (slice(None), slice(None), slice(x0, x0 + w8))
