@@ -243,8 +243,8 @@ def test_view_form_odd_layouts(bpc):
 
 def _in_place_case(ref_np, dist_np, R, D, bpc, in_place=True):
     """The view form through the C ABI with a workspace filled with 0xA5:
-    results as in _view_case, and views whose rows are whole aligned vectors
-    read in place (the part of the workspace past the contiguous form's is
+    results as in _view_case, and views whose rows are whole vectors read
+    in place (the part of the workspace past the contiguous form's is
     left as it was), others gathered into it."""
     f, h, w = R.shape
     total = vqx.plane_stats_view_cpu_order_workspace_bytes(w, h, bpc, f)
