@@ -1436,8 +1436,6 @@ VecMap make_vec_map(int w, int h, const void *ref, int64_t ref_row_stride, int64
     M.frame_bytes_d = 2 * dist_frame_stride;
     const int64_t odd = (M.row_bytes_r | M.frame_bytes_r | M.row_bytes_d | M.frame_bytes_d) & 15;
     M.general = (M.phase_r | M.phase_d | static_cast<uint32_t>(odd)) != 0;
-    M.same_phases = M.phase_r == M.phase_d && ((M.row_bytes_r - M.row_bytes_d) & 15) == 0 &&
-                    ((M.frame_bytes_r - M.frame_bytes_d) & 15) == 0;
     return M;
 }
 

@@ -158,44 +158,31 @@ struct VecMap {
     // general != 0: some vector does not start on a 16-byte boundary.  The
     // kernels then take each plane's base rounded down to 16 bytes and find
     // vector (f, y, x) at byte phase + f*frame_bytes + y*row_bytes + 16*x
-    // from there; same_phases: ref's and dist's vectors start at the same
-    // offset within 16 bytes throughout.
-    uint32_t general = 0, same_phases = 0;
+    // from there.
+    uint32_t general = 0;
     uint32_t phase_r = 0, phase_d = 0;
     int64_t row_bytes_r = 0, frame_bytes_r = 0, row_bytes_d = 0, frame_bytes_d = 0;
 };
 
-// The 16 bytes at `phase` (0..15) in two consecutive 16-byte blocks: a
-// vector that starts `phase` bytes past a 16-byte boundary lies in the
-// block that holds its first byte and the next (each holds bytes of the
-// vector, so both lie in the plane's pages).  phase may differ from lane
-// to lane; at 0 the result is lo.
-__device__ __forceinline__ u32x4_t vec16_at(const u32x4_t &lo, const u32x4_t &hi, uint32_t phase)
-{
-    const uint32_t q = phase >> 2, r = phase & 3;
-    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    uint32_t s[5];
-#pragma unroll
-    for (int m = 0; m < 5; ++m)
-        s[m] = q == 0 ? w[m] : q == 1 ? w[m + 1] : q == 2 ? w[m + 2] : w[m + 3];
-    u32x4_t o;
-    o.x = __builtin_amdgcn_alignbyte(s[1], s[0], r);
-    o.y = __builtin_amdgcn_alignbyte(s[2], s[1], r);
-    o.z = __builtin_amdgcn_alignbyte(s[3], s[2], r);
-    o.w = __builtin_amdgcn_alignbyte(s[4], s[3], r);
-    return o;
-}
-
 // The 16 bytes at byte offset `at` (even, >= 0) from P, a 16-byte aligned
-// base: cut from the block that holds the first of them and the next one
-// (the same block again where `at` is a multiple of 16, so no read passes
-// the vector's own blocks).  Non-temporal loads: the planes are read once.
+// base: the four dwords from the dword that holds the first byte (one
+// dword-aligned load), then the dword after them where `at` is not a
+// multiple of 4 (else the last of the four again), and each dword of the
+// result cut from two neighbours with v_alignbyte.  Every dword read holds
+// a byte of the vector, so no read leaves the 16-byte blocks that hold it.
 __device__ __forceinline__ u32x4_t load_vec16_at(const u32x4_t *P, int64_t at)
 {
-    const int64_t block = at >> 4;
-    const uint32_t phase = static_cast<uint32_t>(at & 15);
-    return vec16_at(__builtin_nontemporal_load(P + block), __builtin_nontemporal_load(P + block + (phase ? 1 : 0)),
-                    phase);
+    const uint32_t *d = reinterpret_cast<const uint32_t *>(P) + (at >> 2);
+    const uint32_t r = static_cast<uint32_t>(at & 3);  // 0 or 2
+    u32x4_t lo;
+    __builtin_memcpy(&lo, d, sizeof(lo));
+    const uint32_t hi = d[r ? 4 : 3];
+    u32x4_t o;
+    o.x = __builtin_amdgcn_alignbyte(lo.y, lo.x, r);
+    o.y = __builtin_amdgcn_alignbyte(lo.z, lo.y, r);
+    o.z = __builtin_amdgcn_alignbyte(lo.w, lo.z, r);
+    o.w = __builtin_amdgcn_alignbyte(hi, lo.w, r);
+    return o;
 }
 
 // Byte offset of vector v (index in the batch's contiguous order) of frame

@@ -39,33 +39,12 @@ static_assert(kLaneIters % kInFlight == 0, "whole load groups");
 // (two-byte samples, so frames hold no partial vectors): the same chunks,
 // terms and records as stage1_u16<kLowBitsOut>, each vector found through
 // the VecMap; kLowBitsOut: also the low bits of the terms and zero queue
-// lengths, for the CPU-order form; kForm: as above (ref and dist the
-// bases rounded down to 16 bytes where a phase is not 0).
-// Where the planes' vectors start within 16-byte blocks: all at 0 (one
-// block per vector, found with the map's pads); at the same phase in both
-// planes for every vector, the phase possibly changing from row to row
-// (kRotated: two blocks, the vector's samples in rotated order, which
-// neither an integer sum nor the OR of the terms' low bits sees, and the
-// same rotation pairs each ref sample with its dist sample); or otherwise
-// (kShifted: the samples cut out in order).  The last two find vectors with
-// the map's byte strides.  kRotatedUniform: kRotated where strides are
-// whole vectors, so one phase holds throughout and the vectors are found
-// with the pads.
-enum : int { kAligned = 0, kRotated = 1, kShifted = 2, kRotatedUniform = 3 };
-
-// Mask of the bytes of a 16-byte block at or past byte `ph` (0..15).
-__device__ __forceinline__ u32x4 bytes_from(uint32_t ph)
-{
-    const uint32_t sh = 8 * ph;
-    const uint64_t lo = sh >= 64 ? 0ull : ~0ull << (sh & 63);
-    const uint64_t hi = sh <= 64 ? ~0ull : ~0ull << ((sh - 64) & 63);
-    u32x4 m;
-    m.x = static_cast<uint32_t>(lo);
-    m.y = static_cast<uint32_t>(lo >> 32);
-    m.z = static_cast<uint32_t>(hi);
-    m.w = static_cast<uint32_t>(hi >> 32);
-    return m;
-}
+// lengths, for the CPU-order form; kForm: where the planes' vectors start
+// within 16-byte blocks -- all at 0 (kAligned: one 16-byte load per vector,
+// found with the map's pads), or anywhere (kCut: ref and dist the bases
+// rounded down to 16 bytes, each vector found with the map's byte strides
+// and cut from dword-aligned loads).
+enum : int { kAligned = 0, kCut = 1 };
 
 template <bool kLowBitsOut, int kForm>
 __global__ __launch_bounds__(kThreads) void stage1_u16_mapped(const void *ref, const void *dist, int64_t pixels,
@@ -91,7 +70,6 @@ __global__ __launch_bounds__(kThreads) void stage1_u16_mapped(const void *ref, c
     const u32x4 *Rf = R + (fbr >> 4), *Df = D + (fbd >> 4);
     const uint32_t lor = static_cast<uint32_t>(fbr & 15), lod = static_cast<uint32_t>(fbd & 15);
     const uint32_t rbr = static_cast<uint32_t>(M.row_bytes_r), rbd = static_cast<uint32_t>(M.row_bytes_d);
-    const u32x4 keep = bytes_from(M.phase_r);  // kRotatedUniform (phase_r == phase_d there)
     typename std::conditional<kLowBitsOut, Acc16Low, Acc16F64>::type a;
     if (cb < ce) {
 #pragma unroll 1
@@ -109,31 +87,11 @@ __global__ __launch_bounds__(kThreads) void stage1_u16_mapped(const void *ref, c
                     const int64_t ar = v + fr + row * M.pad_row_r, ad = v + fd + row * M.pad_row_d;
                     x[u] = __builtin_nontemporal_load(R + ar);
                     y[u] = __builtin_nontemporal_load(D + ad);
-                } else if constexpr (kForm == kRotatedUniform) {
-                    const int64_t ar = v + fr + row * M.pad_row_r, ad = v + fd + row * M.pad_row_d;
-                    x[u] = (R[ar] & keep) | (R[ar + 1] & ~keep);
-                    y[u] = (D[ad] & keep) | (D[ad + 1] & ~keep);
                 } else {
                     const uint32_t yr = static_cast<uint32_t>(row);
                     const uint32_t x16 = 16 * (r - yr * M.vpr);
-                    const uint32_t br = lor + yr * rbr + x16, bd = lod + yr * rbd + x16;
-                    if constexpr (kForm == kRotated) {
-                        // the part of the vector's first block from its phase
-                        // on and the part of the next block before it, as one
-                        // 16-byte value whose samples are rotated (the same
-                        // way in both planes); cached loads, as the next block
-                        // is also the next vector's first
-                        const uint32_t ph = br & 15;
-                        const uint32_t nb = ph ? 1u : 0u;
-                        const u32x4 lr = Rf[br >> 4], hr = Rf[(br >> 4) + nb];
-                        const u32x4 ld = Df[bd >> 4], hd = Df[(bd >> 4) + nb];
-                        const u32x4 keep = bytes_from(ph);
-                        x[u] = (lr & keep) | (hr & ~keep);
-                        y[u] = (ld & keep) | (hd & ~keep);
-                    } else {
-                        x[u] = load_vec16_at(Rf, br);
-                        y[u] = load_vec16_at(Df, bd);
-                    }
+                    x[u] = load_vec16_at(Rf, lor + yr * rbr + x16);
+                    y[u] = load_vec16_at(Df, lod + yr * rbd + x16);
                 }
             }
 #pragma unroll
@@ -179,15 +137,8 @@ hipError_t launch_stage1_mapped(const Geometry &g, const void *ref, const void *
     if (!map.general)
         stage1_u16_mapped<true, kAligned><<<grid, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, partials,
                                                                         map);
-    else if (map.same_phases && ((map.row_bytes_r | map.frame_bytes_r) & 15) == 0)
-        stage1_u16_mapped<true, kRotatedUniform><<<grid, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks,
-                                                                               partials, map);
-    else if (map.same_phases)
-        stage1_u16_mapped<true, kRotated><<<grid, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, partials,
-                                                                        map);
     else
-        stage1_u16_mapped<true, kShifted><<<grid, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, partials,
-                                                                        map);
+        stage1_u16_mapped<true, kCut><<<grid, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, partials, map);
     return hipGetLastError();
 }
 

@@ -334,7 +334,7 @@ int vqx_psnr_int_view_ws(const void *ref, int64_t ref_row_stride, int64_t ref_fr
  * than 2^31 bytes) they are read in place: at the contiguous form's speed
  * where both bases are 16-byte aligned and all strides multiples of 8
  * samples, else from the two aligned 16-byte blocks that hold each vector
- * (about 1.3 to 1.4 times the contiguous form's time).  Other views are
+ * (about 1.2 times the contiguous form's time).  Other views are
  * first copied into contiguous planes inside the workspace (about three
  * times the contiguous form's time), then reduced as the contiguous form
  * does; the results are the same either way.  Errors as for the views and the
