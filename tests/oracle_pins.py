@@ -20,6 +20,7 @@ What the pins rest on:
 
 from __future__ import annotations
 
+import functools
 import json
 import math
 import os
@@ -340,6 +341,141 @@ def pin_exact_range_facts(impl):
     return fails
 
 
+# ------------------------------------------------ the CPU's order past 2^53
+
+def rn53(n: int) -> int:
+    """Nonnegative integer ``n`` rounded to 53 significant bits, ties to even.
+
+    binary64 keeps a 53-bit significand and rounds to nearest, ties to even
+    (IEEE 754's default).  Integers up to 2^53 fit as they are.  Otherwise,
+    with k = bitlength(n) - 53 and n = Q*2^k + r, keep Q and add one when r
+    is above half of 2^k, or exactly half and Q is odd.  Integers only.
+    """
+    k = n.bit_length() - 53
+    if k <= 0:
+        return n
+    q = n >> k
+    r = n - (q << k)
+    half = 1 << (k - 1)
+    if r > half or (r == half and (q & 1)):
+        q += 1
+    return q << k
+
+
+def binary64_running_sum(terms) -> int:
+    """The value a binary64 accumulator holds after adding the nonnegative
+    integer ``terms`` to zero one at a time, in the given order:
+    S <- rn53(S + t) at every add.
+
+    Every partial sum up to 2^53 is exact, so the prefix up to the last such
+    partial sum is taken with an exact int64 running total; the adds from
+    there on are done one by one.
+    """
+    terms = np.asarray(terms, dtype=np.int64).ravel()
+    if terms.size == 0:
+        return 0
+    prefix = np.cumsum(terms)  # exact: below 2^25 * 2^32
+    past = np.nonzero(prefix > TWO53)[0]
+    if past.size == 0:
+        return int(prefix[-1])
+    i0 = int(past[0])
+    s = int(prefix[i0 - 1]) if i0 else 0
+    for t in terms[i0:].tolist():
+        s = rn53(s + t)
+    return s
+
+
+def _binary32_square_units(x):
+    """The binary32 product x*x of each stored integer x, read back as an
+    integer (numpy's float32 multiply rounds to nearest even)."""
+    f = np.asarray(x).astype(np.float32)
+    return (f * f).astype(np.int64)
+
+
+@functools.lru_cache(maxsize=None)
+def _past53_frames():
+    """The three frames past 2^53 units, and the CPU's five sums of each as
+    integers in units, emulated in raster order (rows top to bottom, columns
+    left to right) with ``binary64_running_sum``."""
+    frames = {
+        "mixed 2560x1440": synth.past53_mixed(w=2560, h=1440),
+        "full-range 3840x2160": synth.past53_fullrange(w=3840, h=2160),
+        "odd dark, bright 3840x2160": synth.odd_dark_bright(w=3840, h=2160),
+    }
+    out = {}
+    for name, (ref, dist) in frames.items():
+        r = ref[0].astype(np.int64).ravel()
+        d = dist[0].astype(np.int64).ravel()
+        terms = (_binary32_square_units(np.abs(r - d)), r, d,
+                 _binary32_square_units(r), _binary32_square_units(d))
+        out[name] = (ref[0:1], dist[0:1], [binary64_running_sum(t) for t in terms])
+    return out
+
+
+def pin_past53_raster_order(impl):
+    """Past 2^53 units the CPU's running double rounds at every add, in the
+    order it visits the samples; no other order gives the same bits [float_psnr
+    page, Consequences: past 2^53 the CPU's sum rounds in sequence; float_moment
+    page, Alternatives: reproducing that sequence of roundings].  The CPU visits
+    rows top to bottom and each row left to right [float_psnr page, Context].
+    O1 must equal an integer-only emulation of S <- RN53(S + t) in that order,
+    bit for bit, on frames whose second moments pass 2^53 (ties at every binade,
+    full-range noise, and odd dark squares under bright ones past 2^54)."""
+    fails = []
+    for name, (ref, dist, want) in _past53_frames().items():
+        got = impl.seq(ref, dist, 16)[0]
+        if not any(w > TWO53 for w in want):
+            fails.append(f"{name}: no sum passes 2^53")
+        for k in range(5):
+            units = float(got[k]) * float(256 ** UNIT_POWER[k])  # exact: a power of two
+            if units != float(want[k]) or int(units) != want[k]:
+                fails.append(f"{name}: output {k} is {int(units)} units, the sequential "
+                             f"binary64 sum in raster order is {want[k]}")
+    return fails
+
+
+def pin_past53_bound_below_16_bits(impl):
+    """The bound's reading for 13..15 bits.  The pages state the bound at 16
+    bits only [float_moment page, Decision].  With the same stored integers, a
+    depth of bpc scales every CPU term, partial sum and mean by
+    2^(2*(16 - bpc)) (exact: a power of two), so the CPU's sums at bpc are the
+    16-bit sums scaled, and the bound must scale the same way.  Checked on the
+    mixed frame (values up to 65535 in the container, which the library
+    accepts at any depth): O1 at 13, 14 and 15 bits equals the raster-order
+    emulation scaled; the CPU mean lies within the bound of the exact mean;
+    and the bound is the 16-bit bound times 2^(2*(16 - bpc))."""
+    fails = []
+    ref, dist, want = _past53_frames()["mixed 2560x1440"]
+    exact = [int(v) for v in impl.exact(ref, dist)[0]]
+    pixels = ref.shape[-1] * ref.shape[-2]
+    for bpc in (13, 14, 15):
+        s = 1 << (bpc - 8)
+        got = impl.seq(ref, dist, bpc)[0]
+        for k in (0, 3, 4):
+            unit = float(s ** UNIT_POWER[k])
+            if float(got[k]) * unit != float(want[k]):
+                fails.append(f"bpc {bpc} output {k}: {float(got[k]) * unit} units, "
+                             f"emulation {want[k]}")
+            if exact[k] <= TWO53:
+                continue
+            e = max(binade_int(exact[k]), binade_int(want[k]))
+            b = impl.bound(pixels, e, bpc)
+            cpu_mean = float(got[k]) / pixels
+            exact_mean = (float(exact[k]) / unit) / pixels
+            if abs(cpu_mean - exact_mean) > b:
+                fails.append(f"bpc {bpc} output {k}: distance {abs(cpu_mean - exact_mean)} > bound {b}")
+            b16 = impl.bound(pixels, e, 16)
+            if b != b16 * 2.0 ** (2 * (16 - bpc)):
+                fails.append(f"bpc {bpc}: bound {b} is not the 16-bit bound {b16} times "
+                             f"2^{2 * (16 - bpc)}")
+    return fails
+
+
+def binade_int(n: int) -> int:
+    """e with 2^e <= n < 2^(e+1), for an integer n > 0."""
+    return n.bit_length() - 1
+
+
 ALL_PINS = [
     pin_q_matches_binary32_product,
     pin_q_tie_cases,
@@ -354,7 +490,12 @@ ALL_PINS = [
     pin_past53,
     pin_bound_printed_values,
     pin_exact_range_facts,
+    pin_past53_raster_order,
+    pin_past53_bound_below_16_bits,
 ]
+
+# Pins that take seconds (frames of millions of samples); run them last.
+SLOW_PINS = (pin_past53, pin_past53_raster_order, pin_past53_bound_below_16_bits)
 
 
 class RealOracle:

@@ -5,9 +5,10 @@ arithmetic (binary32 terms, a sequential float64 running sum via cumsum),
 each with one plausible mistake: the defects the pages report in earlier GPU
 twins (fp32 block sums, exact integer squares, stale accumulators), and the
 generic ones (a dropped term, a wrong sign, a transposed operand, a wrong
-scale, a wrong rounding).  The unmutated re-expression must pass every pin,
-and so must a double sum taken in another order (it changes nothing below
-2^53 and stays within the bound past it).
+scale, a wrong rounding, a double sum in another order).  The unmutated
+re-expression must pass every pin.  A double sum in another order changes
+nothing below 2^53 and stays within the bound past it, so only the pin of
+the CPU's raster order past 2^53 may catch it.
 """
 
 from __future__ import annotations
@@ -144,10 +145,25 @@ class M4bTiesAwaySquare(M4TruncatedSquare):
 
 
 class M5PairwiseDouble(NumpyOracle):
-    """A double sum in another (pairwise) order: allowed, not a mistake."""
+    """A double sum in another (pairwise) order."""
 
     def reduce(self, t, k):
         return float(np.sum(t.astype(np.float64)))
+
+
+class M5bColumnMajor(NumpyOracle):
+    """One running double, visiting the plane column by column."""
+
+    def reduce(self, t, k):
+        return float(np.cumsum(t.astype(np.float64).T.ravel())[-1]) if t.size else 0.0
+
+
+class M5cRowPartials(NumpyOracle):
+    """Each row summed into its own double, the row sums then added in order."""
+
+    def reduce(self, t, k):
+        rows = np.cumsum(t.astype(np.float64), axis=1)[:, -1]
+        return float(np.cumsum(rows)[-1]) if t.size else 0.0
 
 
 class M6NoResetBetweenFrames(NumpyOracle):
@@ -276,15 +292,16 @@ MUTANTS = [M1Fp32BlockSums, M2ExactIntegerSquares, M3U32BlockWrap, M4TruncatedSq
            M4bTiesAwaySquare, M6NoResetBetweenFrames, M7DropLastColumn, M8WrongSign,
            M9SwappedMoments, M10UnscaledSamples, M11ScaledOnce, M12NoiseInDouble,
            M13WrappedDifference, X1QTiesAway, X2QTruncate, X3ExactOffByOne,
-           X4ExactMomentsSwapped, B1BoundWithoutUnit, B2BoundWithoutExactPrefix]
+           X4ExactMomentsSwapped, B1BoundWithoutUnit, B2BoundWithoutExactPrefix,
+           M5PairwiseDouble, M5bColumnMajor, M5cRowPartials]
 
 # The cheap pins first; a mutant stops at its first failing pin.
-FAST_FIRST = sorted(oracle_pins.ALL_PINS, key=lambda p: p is oracle_pins.pin_past53)
+FAST_FIRST = sorted(oracle_pins.ALL_PINS, key=lambda p: p in oracle_pins.SLOW_PINS)
 
 
 def _first_failure(impl):
     for pin in FAST_FIRST:
-        if isinstance(impl, (M4TruncatedSquare,)) and pin is oracle_pins.pin_past53:
+        if isinstance(impl, (M4TruncatedSquare,)) and pin in oracle_pins.SLOW_PINS:
             continue  # per-sample Python rounding is too slow at 4K; other pins catch it
         fails = pin(impl)
         if fails:
@@ -296,10 +313,16 @@ def test_unmutated_reexpression_passes_every_pin():
     assert oracle_pins.run_all(NumpyOracle()) == {}
 
 
-def test_other_summation_order_passes_every_pin():
-    """M5: a pairwise double sum equals the sequential one below 2^53 and stays
-    within the bound past it, so it is not a defect the pins may flag."""
-    assert oracle_pins.run_all(M5PairwiseDouble()) == {}
+@pytest.mark.parametrize("order", [M5PairwiseDouble, M5bColumnMajor, M5cRowPartials],
+                         ids=["pairwise", "column_major", "row_partials"])
+def test_other_summation_order_fails_only_the_raster_order_pin(order):
+    """A double sum in another order equals the sequential one below 2^53 and
+    stays within the bound past it; only the CPU's own order of roundings past
+    2^53 [float_psnr page, Consequences] tells it apart."""
+    fails = oracle_pins.run_all(order())
+    assert set(fails) == {"pin_past53_raster_order", "pin_past53_bound_below_16_bits"}, fails
+    # within the bound at every depth: only the bit-for-bit order checks fail
+    assert all("emulation" in f for f in fails["pin_past53_bound_below_16_bits"]), fails
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=[m.__name__ for m in MUTANTS])
