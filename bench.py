@@ -114,6 +114,14 @@ def step_plan(mode: str, wl, pitch: int = 0, x0: int = 0):
     return "host_step", ("stage1_u16", "stage2_combine"), HOST_SOURCES
 UNIT_POWER = (2, 1, 1, 2, 2)  # noise, ref1, dist1, ref2, dist2: units 1/s^power
 STAMP_EVERY = 8  # exact mode: steps per stage-1 dispatch timed with its own events
+MIN_STAMPED = 8  # ... but at least this many stamped dispatches in a short run
+
+
+def stamp_interval(steps: int) -> int:
+    """Steps per stamped stage-1 dispatch: one in STAMP_EVERY, or more often
+    in a short run so that at least MIN_STAMPED timed dispatches are stamped
+    (every one when there are fewer than 2 * MIN_STAMPED steps)."""
+    return max(1, min(STAMP_EVERY, steps // MIN_STAMPED))
 
 
 def parse_args(argv=None):
@@ -762,12 +770,14 @@ def main(argv=None):
     ws, ws_bytes = mode.ws, mode.ws_bytes
     wss = [ws] + [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(nst - 1)]
     total = args.warmup + args.steps
-    # exact mode: stage 1 of one step in every STAMP_EVERY stamps its own
-    # events (a stamped dispatch costs the queue ~10 us of extra gaps, so
-    # stamping every step would slow the stream it measures); other modes:
-    # events around each group of steps
-    phase = STAMP_EVERY // 2 if args.steps > STAMP_EVERY // 2 else 0
-    ev_begin = ({i: hip.create() for i in range(args.warmup, total) if (i - args.warmup) % STAMP_EVERY == phase}
+    # exact mode: stage 1 of one step in every `every` stamps its own events
+    # (a stamped dispatch costs the queue ~10 us of extra gaps, so stamping
+    # every step of a long run would slow the stream it measures; a short
+    # run stamps more often to keep the mean stable); other modes: events
+    # around each group of steps
+    every = stamp_interval(args.steps)
+    phase = every // 2 if args.steps > every // 2 else 0
+    ev_begin = ({i: hip.create() for i in range(args.warmup, total) if (i - args.warmup) % every == phase}
                 if mode.per_step_events else {})
     ev_end = {i: hip.create() for i in ev_begin}
     ngroups = (total + group - 1) // group + 1
@@ -954,10 +964,15 @@ def main(argv=None):
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "traffic_source": (f"profiles/{mode.kernel}_{wname}_hbm_traffic.txt (rocprofv3 --pmc FETCH_SIZE, then "
+                               f"WRITE_SIZE, scaled by a copy kernel; taken for the same kernel source, not by "
+                               f"this run)" if traffic is not None else None),
             "kernel_us_mean": round(mean_ms * 1e3, 2),
             "kernel_us_median": round(statistics.median(step_ms) * 1e3, 2),
+            "kernel_us_min": round(min(step_ms) * 1e3, 2),
+            "kernel_us_max": round(max(step_ms) * 1e3, 2),
             "timed_by": (f"HIP events stamped by {len(step_ms)} of the {args.steps} timed stage-1 dispatches "
-                         f"(one in {STAMP_EVERY})" if mode.per_step_events else
+                         f"(one in {every})" if mode.per_step_events else
                          f"HIP events around each group of {group} timed steps, per step"),
             "algorithmic_bytes_per_launch": mode.alg_bytes,
         },

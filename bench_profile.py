@@ -12,6 +12,12 @@ Runs, each as a child process under its own time limit:
    through the shader cores); that kernel's counter reading scales the
    stage-1 reading into HBM bytes.
 
+With ``--valu``, one counter pass instead: instructions per dispatch and
+how busy the SIMDs were (``..._valu.txt``).  With ``--driver-cmd``, only 1.,
+over the default command
+``bench.py --gpus 1 --steps 20 --warmup 5`` as it is run for the record:
+``<kernel>_<w>x<h>x<frames>_driver_cmd_kernel_trace.txt``.
+
 Writes ``<kernel>_<w>x<h>x<frames>_kernel_trace.txt`` and
 ``..._hbm_traffic.txt`` into ``--out``.  With ``--mode cpu-order`` the
 kernel is the whole CPU-order step (``cpu_order_step``): the trace lists
@@ -167,6 +173,114 @@ def profile_host(args, wl, wname, bench, src_sha):
     return 0
 
 
+def kernel_trace(args, trace_cmd, steps, warmup, title, outname, step_kernels, src_sha, alg):
+    """Run ``trace_cmd`` (rocprofv3 --kernel-trace --stats over a bench run
+    of ``warmup`` + ``steps`` steps) and write its summary as ``outname``.
+    Returns (exit status, dispatches per step of each of the step's kernels)."""
+    tdir = trace_cmd[trace_cmd.index("-d") + 1]
+    rc = sh(trace_cmd, 300, os.path.join(args.work, "trace.log"))
+    if rc != 0:
+        return rc, {}
+    stats = rows(find(tdir, "kernel_stats.csv"))
+    with open(os.path.join(args.work, "trace.log")) as f:
+        bench_line = [ln for ln in f.read().splitlines() if ln.startswith("{")]
+    lines = [
+        f"# rocprofv3 kernel trace: {title}",
+        f"command: cd <repo> && {shown(trace_cmd, args)}",
+        f"date_utc: {time.strftime('%Y-%m-%dT%H:%M:%SZ', time.gmtime())}",
+        f"kernel_source_sha256: {src_sha}",
+        "",
+        f"{'kernel':<18} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_us':>12}",
+    ]
+    for r in stats:
+        name = short(r.get("Name", r.get("KernelName", "?")))
+        lines.append(f"{name:<18} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
+                     f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f} "
+                     f"{float(r['TotalDurationNs']) / 1e3:>12.1f}")
+    # each kernel's dispatches in launch order, from the trace; the bench
+    # times the dispatches after its warm-up ones
+    trace = rows(find(tdir, "kernel_trace.csv"))
+    timed_avg = {}
+    per_step = {}
+    for kname in step_kernels:
+        disp = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in trace
+                      if short(r["Kernel_Name"]) == kname)
+        k = max(1, round(len(disp) / (warmup + steps)))  # dispatches of this kernel per step
+        timed = [(e - b) / 1e3 for b, e in disp[k * warmup:]]
+        if timed:
+            timed_avg[kname] = statistics.fmean(timed)
+            per_step[kname] = k
+            lines += ["", f"{kname}: dispatches {len(disp)}, {k} per step (the first {k * warmup} are the "
+                          "bench's warm-up)",
+                      f"{kname}_avg_us_timed_dispatches: {statistics.fmean(timed):.2f}",
+                      f"{kname}_median_us_timed_dispatches: {statistics.median(timed):.2f}",
+                      f"{kname}_min_us_timed_dispatches: {min(timed):.2f}",
+                      f"{kname}_max_us_timed_dispatches: {max(timed):.2f}"]
+    if len(timed_avg) == len(step_kernels):
+        step_us = sum(timed_avg[k] * per_step[k] for k in step_kernels)
+        gbs = alg / (step_us * 1e-6) / 1e9
+        lines += ["", f"kernel_avg_us: {step_us:.2f}" + ("  (sum of the step's kernels)" if len(step_kernels) > 1
+                                                         else ""),
+                  f"kernel_algorithmic_bytes_per_launch: {alg}",
+                  f"kernel_achieved_GBps: {gbs:.1f}", f"kernel_frac_of_8000_GBps: {gbs / 8000:.4f}"]
+    if bench_line:
+        lines += ["", "bench line of the same run:", bench_line[-1]]
+    with open(os.path.join(args.out, outname), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines), flush=True)
+    return 0, per_step
+
+
+VALU_COUNTERS = ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD", "SQ_INSTS_LDS", "SQ_WAVES",
+                 "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+
+
+def profile_valu(args, wl, wname, kernel, step_kernels, bench, src_sha):
+    """One counter pass (seven counters, within one pass's limits) over a
+    short bench run: vector and scalar instructions, loads and LDS
+    instructions per dispatch, and how busy the SIMDs were."""
+    cdir = os.path.join(args.work, "valu")
+    cmd = ["rocprofv3", "--pmc", *VALU_COUNTERS, "--output-format", "csv", "-d", cdir, "-o", "p", "--"] + bench + [
+        "--steps", "5", "--warmup", "1"]
+    rc = sh(cmd, 120, os.path.join(args.work, "valu.log"))
+    if rc != 0:
+        return rc
+    per = {}
+    for r in rows(find(cdir, "counter_collection.csv")):
+        per.setdefault((short(r["Kernel_Name"]), r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    lines = [
+        f"# VALU counters of {kernel}, {wl.name} ({wname})",
+        f"command: cd <repo> && {shown(cmd, args)}",
+        f"date_utc: {time.strftime('%Y-%m-%dT%H:%M:%SZ', time.gmtime())}",
+        f"kernel_source_sha256: {src_sha}",
+        "",
+        "per-dispatch means over the run's dispatches (counters summed over the device, as rocprofv3 reports them):",
+    ]
+    names = sorted({k for k, _ in per})
+    for name in names:
+        for c in VALU_COUNTERS:
+            v = per.get((name, c))
+            if v:
+                lines.append(f"  {name:<18} {c:<17} n={len(v):>2} mean={statistics.fmean(v):.6g}")
+    lines += ["", "VALU busy = SQ_INSTS_VALU x 4 cycles (a wave64 instruction on a 16-lane SIMD; plain fp32 and",
+              "            32-bit integer instructions issue faster on gfx950, so this is an upper bound) /",
+              "            (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs):"]
+    for name in names:
+        v, g = per.get((name, "SQ_INSTS_VALU")), per.get((name, "GRBM_GUI_ACTIVE"))
+        if v and g:
+            lines.append(f"  {name:<18} {statistics.fmean(v) * 4 / (statistics.fmean(g) / 8 * 1024):.3f}")
+    pixels = wl.w * wl.h * wl.nframes
+    for name in step_kernels:
+        v = per.get((name, "SQ_INSTS_VALU"))
+        if v:
+            lines.append(f"  {name}: {statistics.fmean(v) * 64 / pixels:.2f} VALU lane instructions per pixel pair "
+                         "(all of the kernel's instructions over the batch's pixel pairs)")
+    with open(os.path.join(args.out, f"{kernel}_{wname}_valu.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines), flush=True)
+    return 0
+
+
 def main(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--workload", type=int, default=None)
@@ -178,6 +292,9 @@ def main(argv=None):
     p.add_argument("--mode", choices=("exact", "cpu-order", "psnr-int", "yuv420", "host"), default="exact")
     p.add_argument("--pitch", type=int, default=0, help="as bench.py --pitch")
     p.add_argument("--x0", type=int, default=0, help="as bench.py --x0")
+    p.add_argument("--valu", action="store_true", help="the VALU counter pass only")
+    p.add_argument("--driver-cmd", action="store_true",
+                   help="kernel trace only, over the plain default run: bench.py --gpus 1 --steps 20 --warmup 5")
     args = p.parse_args(argv)
     cpu_order = args.mode == "cpu-order"
     views = args.mode in ("psnr-int", "yuv420")
@@ -222,63 +339,31 @@ def main(argv=None):
     if args.mode == "host":
         return profile_host(args, wl, wname, bench, src_sha)
 
+    if args.valu:
+        return profile_valu(args, wl, wname, kernel, step_kernels, bench, src_sha)
+
+    if args.driver_cmd:
+        # the default bench command as it is run for the record (default
+        # workload and mode, cpu_baseline leg included), traced as it is
+        drv = ["python3", os.path.join(ROOT, "bench.py"), "--gpus", "1", "--steps", "20", "--warmup", "5"]
+        trace_cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d",
+                     os.path.join(args.work, "trace"), "-o", "trace", "--"] + drv
+        return kernel_trace(args, trace_cmd, 20, 5, f"{kernel}, {wl.name} ({wname}), the default bench command",
+                            f"{kernel}_{wname}_driver_cmd_kernel_trace.txt", step_kernels, src_sha, alg)[0]
+
     # 0. make the input cache outside the profiler
     rc = sh(bench + ["--steps", "1", "--warmup", "0"], 600, os.path.join(args.work, "prime.log"))
     if rc != 0:
         return rc
 
     # 1. kernel trace + stats
-    tdir = os.path.join(args.work, "trace")
-    trace_cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", tdir,
-                 "-o", "trace", "--"] + bench + ["--steps", str(args.steps), "--warmup", str(WARMUP)]
-    rc = sh(trace_cmd, 300, os.path.join(args.work, "trace.log"))
+    trace_cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d",
+                 os.path.join(args.work, "trace"), "-o", "trace", "--"] + bench + ["--steps", str(args.steps),
+                                                                                  "--warmup", str(WARMUP)]
+    rc, per_step = kernel_trace(args, trace_cmd, args.steps, WARMUP, f"{kernel}, {wl.name} ({wname})",
+                                f"{kernel}_{wname}_kernel_trace.txt", step_kernels, src_sha, alg)
     if rc != 0:
         return rc
-    stats = rows(find(tdir, "kernel_stats.csv"))
-    with open(os.path.join(args.work, "trace.log")) as f:
-        bench_line = [ln for ln in f.read().splitlines() if ln.startswith("{")]
-    lines = [
-        f"# rocprofv3 kernel trace: {kernel}, {wl.name} ({wname})",
-        f"command: cd <repo> && {shown(trace_cmd, args)}",
-        f"date_utc: {time.strftime('%Y-%m-%dT%H:%M:%SZ', time.gmtime())}",
-        f"kernel_source_sha256: {src_sha}",
-        "",
-        f"{'kernel':<18} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_us':>12}",
-    ]
-    for r in stats:
-        name = short(r.get("Name", r.get("KernelName", "?")))
-        lines.append(f"{name:<18} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
-                     f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f} "
-                     f"{float(r['TotalDurationNs']) / 1e3:>12.1f}")
-    # each kernel's dispatches in launch order, from the trace; the bench
-    # times the dispatches after its warm-up ones
-    trace = rows(find(tdir, "kernel_trace.csv"))
-    timed_avg = {}
-    per_step = {}
-    for kname in step_kernels:
-        disp = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in trace
-                      if short(r["Kernel_Name"]) == kname)
-        k = max(1, round(len(disp) / (WARMUP + args.steps)))  # dispatches of this kernel per step
-        timed = [(e - b) / 1e3 for b, e in disp[k * WARMUP:]]
-        if timed:
-            timed_avg[kname] = statistics.fmean(timed)
-            per_step[kname] = k
-            lines += ["", f"{kname}: dispatches {len(disp)}, {k} per step (the first {k * WARMUP} are the "
-                          "bench's warm-up)",
-                      f"{kname}_avg_us_timed_dispatches: {statistics.fmean(timed):.2f}",
-                      f"{kname}_median_us_timed_dispatches: {statistics.median(timed):.2f}"]
-    if len(timed_avg) == len(step_kernels):
-        step_us = sum(timed_avg[k] * per_step[k] for k in step_kernels)
-        gbs = alg / (step_us * 1e-6) / 1e9
-        lines += ["", f"kernel_avg_us: {step_us:.2f}" + ("  (sum of the step's kernels)" if len(step_kernels) > 1
-                                                         else ""),
-                  f"kernel_algorithmic_bytes_per_launch: {alg}",
-                  f"kernel_achieved_GBps: {gbs:.1f}", f"kernel_frac_of_8000_GBps: {gbs / 8000:.4f}"]
-    if bench_line:
-        lines += ["", "bench line of the same run:", bench_line[-1]]
-    with open(os.path.join(args.out, f"{kernel}_{wname}_kernel_trace.txt"), "w") as f:
-        f.write("\n".join(lines) + "\n")
-    print("\n".join(lines), flush=True)
 
     # 2./3. one counter per pass
     readings = {}

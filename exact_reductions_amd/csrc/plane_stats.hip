@@ -33,6 +33,28 @@
 // sum travels as its low 16 bits and the rest, two uint32 sums -- the
 // page's low/high split at 16 bits [PSNR, Decision], moved from every term
 // to once per lane.
+//
+// Two cheaper forms of the same terms apply where the samples allow them.
+// A lane loads kInFlight vectors of each plane at a time (a group); where
+// every sample of a wave's group passes a test, the wave takes the cheaper
+// form for that group, otherwise the general one above.  Every form adds
+// the same integers, so the choice cannot change a sum.
+//  * Small samples (depths up to 12 bits; every sample below 4096): a
+//    square below 2^24 is exact in binary32, so the float square is the
+//    integer square [PSNR, Decision: up to 12 bits the square is exact],
+//    and integer dot products give sum r^2, sum d^2, sum r*d, with
+//    sum (r-d)^2 = sum r^2 + sum d^2 - 2 sum r*d.
+//  * Bright samples (depths 13..16; every sample at least 49152): each
+//    moment square lies in [2^31, 2^32) (49152^2 > 2^31; q(65535) < 2^32),
+//    one binade, where a binary32 value is stored as the exponent field 158
+//    over a 23-bit m and equals (2^23 + m) * 2^8.  So the squares of a
+//    group add as plain uint32 sums of their bit patterns, and the sum of n
+//    squares is n * 2^31 + 2^8 * (sum of bits - n * 0x4F000000).  The
+//    noise squares stay below 16383^2 < 2^28, so a uint32 takes sixteen.
+//  The general form costs about 15 vector instructions per pixel pair; the
+//  bright one about 10, the small one about 3.  Where the SIMDs are busy,
+//  the clock drops under sustained load, so the work per byte decides
+//  whether the kernel stays on the HBM roofline.
 
 #include <hip/hip_ext.h>
 
@@ -66,12 +88,112 @@ static_assert(kIters % kInFlight == 0, "whole load groups");
 static_assert((kIters * 16 + 1) * 255ull * 255ull * 64ull < (1ull << 32), "8-bit wave budget");
 static_assert(((kIters * 8 + 1) * 0xffffffffull >> 16) * 64ull < (1ull << 32), "16-bit wave budget");
 static_assert((kIters * 8 + 1) * 65535ull * 64ull < (1ull << 32), "16-bit sample-sum budget");
+// Group forms, per lane and group (kInFlight vectors of each plane, 4
+// dwords each, two samples per dword):
+//  bright: each of the two noise sums takes one sample of each of the
+//          group's dwords, at most 16383^2 each; each moment sum adds the
+//          group's 2*4*kInFlight bit patterns, whose m parts stay below 2^23
+//          each;
+//  small:  sum r^2 (likewise sum d^2, sum r*d) of the group's samples, each
+//          square at most 4095^2; sum r^2 + sum d^2 fits too.
+constexpr int kGroupDwords = 4 * kInFlight;
+static_assert(kGroupDwords * 16383ull * 16383ull < (1ull << 32), "bright noise budget");
+static_assert(2ull * kGroupDwords * (1ull << 23) < (1ull << 32), "bright moment budget");
+static_assert(2ull * 2 * kGroupDwords * 4095ull * 4095ull < (1ull << 32), "small square budget");
+
+// Which cheaper form a 16-bit stage 1 tries per group.
+enum GroupForm : int { kGeneralOnly = 0, kBright = 1, kSmall = 2 };
+
+// Every sample of every lane of the wave at least 49152 (the top two bits
+// of each 16-bit half set).
+__device__ __forceinline__ bool wave_all_bright(const u32x4 (&a)[kInFlight], const u32x4 (&b)[kInFlight])
+{
+    uint32_t all = 0xffffffffu;
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            all &= a[u][j] & b[u][j];
+    return __all((all & 0xC000C000u) == 0xC000C000u);
+}
+
+// Every sample of every lane of the wave below 4096.
+__device__ __forceinline__ bool wave_all_small(const u32x4 (&a)[kInFlight], const u32x4 (&b)[kInFlight])
+{
+    uint32_t any = 0;
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            any |= a[u][j] | b[u][j];
+    return __all((any & 0xF000F000u) == 0);
+}
+
+// The bright form of one group (every sample at least 49152).
+__device__ __forceinline__ void add_group_bright(Acc16U64 &acc, const u32x4 (&a)[kInFlight],
+                                                 const u32x4 (&b)[kInFlight])
+{
+    uint32_t noise_even = 0, noise_odd = 0, bits_r = 0, bits_d = 0;
+    const u16x2 ones = {1, 1};
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t r = a[u][j], d = b[u][j];
+            // converted here: the general form converts the same samples,
+            // and a conversion shared above the branch would hold all of
+            // them in registers at once
+            asm volatile("" : "+v"(r), "+v"(d));
+            float r0 = static_cast<float>(r & 0xffffu), r1 = static_cast<float>(r >> 16);
+            float d0 = static_cast<float>(d & 0xffffu), d1 = static_cast<float>(d >> 16);
+            asm volatile("" : "+v"(r0), "+v"(r1), "+v"(d0), "+v"(d1));  // one conversion each
+            const float e0 = r0 - d0, e1 = r1 - d1;
+            noise_even += float_square(e0);
+            noise_odd += float_square(e1);
+            bits_r += __float_as_uint(r0 * r0);
+            bits_r += __float_as_uint(r1 * r1);
+            bits_d += __float_as_uint(d0 * d0);
+            bits_d += __float_as_uint(d1 * d1);
+            acc.r1 = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, r), ones, acc.r1, false);
+            acc.d1 = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, d), ones, acc.d1, false);
+        }
+    constexpr uint32_t n = 2 * kGroupDwords;  // squares in each moment sum
+    acc.noise += static_cast<uint64_t>(noise_even) + noise_odd;
+    acc.r2 += (static_cast<uint64_t>(n) << 31) + (static_cast<uint64_t>(bits_r - n * 0x4F000000u) << 8);
+    acc.d2 += (static_cast<uint64_t>(n) << 31) + (static_cast<uint64_t>(bits_d - n * 0x4F000000u) << 8);
+}
+
+// The small form of one group (every sample below 4096).
+__device__ __forceinline__ void add_group_small(Acc16U64 &acc, const u32x4 (&a)[kInFlight],
+                                                const u32x4 (&b)[kInFlight])
+{
+    uint32_t rr = 0, dd = 0, rd = 0;
+    const u16x2 ones = {1, 1};
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t r = a[u][j], d = b[u][j];
+            const u16x2 rv = __builtin_bit_cast(u16x2, r), dv = __builtin_bit_cast(u16x2, d);
+            rr = __builtin_amdgcn_udot2(rv, rv, rr, false);
+            dd = __builtin_amdgcn_udot2(dv, dv, dd, false);
+            rd = __builtin_amdgcn_udot2(rv, dv, rd, false);
+            acc.r1 = __builtin_amdgcn_udot2(rv, ones, acc.r1, false);
+            acc.d1 = __builtin_amdgcn_udot2(dv, ones, acc.d1, false);
+        }
+    // sum (r-d)^2 = sum r^2 + sum d^2 - 2 sum r*d, exact (2rd <= r^2 + d^2)
+    acc.noise += rr + dd - 2u * rd;
+    acc.r2 += rr;
+    acc.d2 += dd;
+}
 
 // ------------------------------------------------------------------ stage 1
-template <int kBytes, class Acc>
+template <int kBytes, class Acc, int kForm = kGeneralOnly>
 __device__ __forceinline__ void accumulate_chunk(Acc &acc, const void *ref, const void *dist,
                                                  int64_t pixels, int chunk, int64_t frame)
 {
+    static_assert(kForm == kGeneralOnly || (kBytes == 2 && std::is_same<Acc, Acc16U64>::value),
+                  "group forms add into the 16-bit uint64 lanes");
     constexpr int V = 16 / kBytes;  // samples per vector
     const int64_t e0 = frame * pixels;  // first sample of the frame
     const int64_t e1 = e0 + pixels;
@@ -111,9 +233,21 @@ __device__ __forceinline__ void accumulate_chunk(Acc &acc, const void *ref, cons
                 a[u] = __builtin_nontemporal_load(r + (i + u) * kThreads);
                 b[u] = __builtin_nontemporal_load(d + (i + u) * kThreads);
             }
+            bool cheaper = false;
+            if constexpr (kForm == kBright)
+                cheaper = wave_all_bright(a, b);
+            else if constexpr (kForm == kSmall)
+                cheaper = wave_all_small(a, b);
+            if (cheaper) {
+                if constexpr (kForm == kBright)
+                    add_group_bright(acc, a, b);
+                else if constexpr (kForm == kSmall)
+                    add_group_small(acc, a, b);
+            } else {
 #pragma unroll
-            for (int u = 0; u < kInFlight; ++u)
-                add_vec(acc, a[u], b[u]);
+                for (int u = 0; u < kInFlight; ++u)
+                    add_vec(acc, a[u], b[u]);
+            }
         }
     } else {
         for (int64_t v = cb + threadIdx.x; v < ce; v += kThreads) {
@@ -143,16 +277,18 @@ __global__ __launch_bounds__(kThreads) void stage1_u8(const void *ref, const voi
 // kLowBitsOut: also the OR of the low bits of each square sum's terms, in
 // the record's slot kLowBits, and zero queue lengths in record 0 (for the
 // CPU-order form).
-template <bool kLowBitsOut>
+// kForm: the cheaper group form tried (kGeneralOnly with kLowBitsOut).
+template <bool kLowBitsOut, int kForm>
 __global__ __launch_bounds__(kThreads) void stage1_u16(const void *ref, const void *dist,
                                                        int64_t pixels, int chunks, uint64_t *part)
 {
+    static_assert(!kLowBitsOut || kForm == kGeneralOnly, "the low bits come from the general form");
     const int64_t wg = blockIdx.x;
     const int64_t frame = wg / chunks;
     const int chunk = static_cast<int>(wg - frame * chunks);
     using Acc = typename std::conditional<kLowBitsOut, Acc16Low, Acc16U64>::type;
     Acc a;
-    accumulate_chunk<2>(a, ref, dist, pixels, chunk, frame);
+    accumulate_chunk<2, Acc, kForm>(a, ref, dist, pixels, chunk, frame);
     // each 64-bit lane sum crosses the wave as (low 16 bits, the rest)
     const uint64_t n = lane_total(a.noise), r2 = lane_total(a.r2), d2 = lane_total(a.d2);
     const uint32_t v[8] = {static_cast<uint32_t>(n & 0xffffu), static_cast<uint32_t>(n >> 16), a.r1, a.d1,
@@ -235,24 +371,24 @@ hipError_t launch_plane_stats(const Geometry &g, const void *ref, const void *di
     const dim3 grid1(static_cast<unsigned>(g.workgroups));
     int64_t pixels = g.pixels;
     int chunks = g.chunks;
+    // the cheaper group form that the depth makes likely: small samples up to
+    // 12 bits, bright ones above
+    const void *fn = g.sample_bytes == 1 ? reinterpret_cast<const void *>(&stage1_u8)
+                     : low_bits          ? reinterpret_cast<const void *>(&stage1_u16<true, kGeneralOnly>)
+                     : g.bpc <= 12       ? reinterpret_cast<const void *>(&stage1_u16<false, kSmall>)
+                                         : reinterpret_cast<const void *>(&stage1_u16<false, kBright>);
+    void *args[] = {const_cast<void **>(&ref), const_cast<void **>(&dist), &pixels, &chunks, &partials};
     if (stage1_begin || stage1_end) {
         // AMD's launch with events: the dispatch itself stamps the events,
         // so no marker packets are queued around the kernel
-        void *args[] = {const_cast<void **>(&ref), const_cast<void **>(&dist), &pixels, &chunks,
-                        &partials};
-        const void *fn = g.sample_bytes == 1 ? reinterpret_cast<const void *>(&stage1_u8)
-                         : low_bits           ? reinterpret_cast<const void *>(&stage1_u16<true>)
-                                              : reinterpret_cast<const void *>(&stage1_u16<false>);
         hipError_t e = hipExtLaunchKernel(fn, grid1, dim3(kThreads), args, 0, stream, stage1_begin,
                                           stage1_end, 0);
         if (e != hipSuccess)
             return e;
-    } else if (g.sample_bytes == 1) {
-        stage1_u8<<<grid1, kThreads, 0, stream>>>(ref, dist, pixels, chunks, partials);
-    } else if (low_bits) {
-        stage1_u16<true><<<grid1, kThreads, 0, stream>>>(ref, dist, pixels, chunks, partials);
     } else {
-        stage1_u16<false><<<grid1, kThreads, 0, stream>>>(ref, dist, pixels, chunks, partials);
+        hipError_t e = hipLaunchKernel(fn, grid1, dim3(kThreads), args, 0, stream);
+        if (e != hipSuccess)
+            return e;
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || (!out_noise && !out_moments))
