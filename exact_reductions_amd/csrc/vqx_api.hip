@@ -10,6 +10,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "plane_stats.h"
 #include "terms.h"
 #include "vqx.h"
@@ -219,6 +221,53 @@ ViewCpuOrderLayout view_cpu_order_layout(int w, int h, int bpc, int nframes)
     return l;
 }
 
+// The scratch of vqx_plane_stats_batch_noalloc: one array per GPU in the
+// library's device image.  In host code its name stands for a host-side
+// shadow, not a device address: only the address that hipGetSymbolAddress
+// returns (looked up once per device, with that device current) is ever
+// passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[VQX_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void *scratch_address[kMaxDevices];  // device address per device, null until looked up
+
+// The device address of `scratch` on the device of `stream` (the current
+// device for the null stream).
+int noalloc_scratch(hipStream_t stream, void **out)
+{
+    int current = 0, dev = 0;
+    if (hipGetDevice(&current) != hipSuccess) {
+        (void)hipGetLastError();
+        return VQX_E_HIP;
+    }
+    dev = current;
+    if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return VQX_E_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return VQX_E_NO_DEVICE;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_address[dev]) {
+        if (dev != current && hipSetDevice(dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return VQX_E_HIP;
+        }
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != current)
+            (void)hipSetDevice(current);
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return VQX_E_HIP;
+        }
+        scratch_address[dev] = p;
+    }
+    *out = scratch_address[dev];
+    return VQX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -239,6 +288,7 @@ const char *vqx_status_string(int status)
     case VQX_E_NO_DEVICE: return "no usable HIP device";
     case VQX_E_STRIDE: return "plane view: row stride below w, negative frame stride, or extent past 2^62 bytes";
     case VQX_E_PLANES: return "nplanes outside 1..VQX_MAX_PLANES";
+    case VQX_E_SCRATCH: return "the batch needs more scratch than VQX_NOALLOC_SCRATCH_BYTES";
     default: return "unknown status";
     }
 }
@@ -310,6 +360,31 @@ int vqx_plane_stats_batch_ws(const void *ref, const void *dist, int w, int h, in
 {
     return vqx_plane_stats_batch_ws_timed(ref, dist, w, h, bpc, nframes, out_noise, out_moments,
                                           workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+int vqx_plane_stats_batch_noalloc(const void *ref, const void *dist, int w, int h, int bpc, int nframes,
+                                  uint64_t *out_noise, uint64_t *out_moments, void *stream)
+{
+    int rc = check_stats_args(ref, dist, w, h, bpc, nframes, out_noise, out_moments);
+    if (rc != VQX_OK)
+        return rc;
+    const vqx::Geometry g = vqx::make_geometry(w, h, bpc, nframes);
+    if (g.workspace_bytes > VQX_NOALLOC_SCRATCH_BYTES)
+        return VQX_E_SCRATCH;
+    rc = device_ready();
+    if (rc != VQX_OK)
+        return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void *ws = nullptr;
+    rc = noalloc_scratch(s, &ws);
+    if (rc != VQX_OK)
+        return rc;
+    if (vqx::launch_plane_stats(g, ref, dist, out_noise, out_moments, static_cast<uint64_t *>(ws), s) !=
+        hipSuccess) {
+        (void)hipGetLastError();
+        return VQX_E_HIP;
+    }
+    return VQX_OK;
 }
 
 int vqx_plane_stats_batch(const void *ref, const void *dist, int w, int h, int bpc, int nframes,

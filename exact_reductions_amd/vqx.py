@@ -17,8 +17,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libvqx.so")
 
 OK = 0
-E_NULL, E_DIMS, E_BPC, E_NFRAMES, E_ALIGN, E_WORKSPACE, E_HIP, E_NO_DEVICE, E_STRIDE, E_PLANES = range(-1, -11, -1)
+(E_NULL, E_DIMS, E_BPC, E_NFRAMES, E_ALIGN, E_WORKSPACE, E_HIP, E_NO_DEVICE, E_STRIDE, E_PLANES,
+ E_SCRATCH) = range(-1, -12, -1)
 MAX_PIXELS = 1 << 25
+NOALLOC_SCRATCH_BYTES = 4 << 20
 
 # Every symbol include/vqx.h declares.
 SYMBOLS = (
@@ -26,6 +28,7 @@ SYMBOLS = (
     "vqx_status_string",
     "vqx_plane_stats_workspace_bytes",
     "vqx_plane_stats_batch",
+    "vqx_plane_stats_batch_noalloc",
     "vqx_plane_stats_batch_ws",
     "vqx_plane_stats_batch_ws_timed",
     "vqx_read_probe_timed",
@@ -78,6 +81,7 @@ def lib() -> ctypes.CDLL:
             "vqx_status_string": (ctypes.c_char_p, [i]),
             "vqx_plane_stats_workspace_bytes": (i, [i, i, i, i, ctypes.POINTER(sz)]),
             "vqx_plane_stats_batch": (i, [vp, vp, i, i, i, i, vp, vp, vp]),
+            "vqx_plane_stats_batch_noalloc": (i, [vp, vp, i, i, i, i, vp, vp, vp]),
             "vqx_plane_stats_batch_ws": (i, [vp, vp, i, i, i, i, vp, vp, vp, sz, vp]),
             "vqx_plane_stats_batch_ws_timed": (i, [vp, vp, i, i, i, i, vp, vp, vp, sz, vp, vp, vp]),
             "vqx_read_probe_timed": (i, [vp, vp, i, i, i, i, vp, sz, vp, vp, vp]),
@@ -227,6 +231,19 @@ def plane_stats_batch_cpu_order(ref, dist, bpc: int, stream=None):
         out[1, :f].data_ptr(), out[1, f:].data_ptr(), ws.data_ptr(), ws.numel(),
         _stream_handle(dev, stream)), "plane_stats_batch_cpu_order_ws")
     return out[0, :f], out[0, f:].view(f, 4), out[1, :f], out[1, f:].view(f, 4)
+
+
+def plane_stats_batch_noalloc(ref, dist, bpc: int, out_noise, out_moments, stream=None):
+    """vqx_plane_stats_batch_noalloc: the five sums into ``out_noise`` [F]
+    and ``out_moments`` [F][4] (int64 device tensors), with the library's
+    fixed per-GPU scratch and no allocation; calls that overlap on one GPU
+    race on that scratch."""
+    ref, dist = _planes(ref, dist, bpc)
+    f, h, w = ref.shape
+    _check(lib().vqx_plane_stats_batch_noalloc(
+        ref.data_ptr(), dist.data_ptr(), w, h, bpc, f, out_noise.data_ptr(), out_moments.data_ptr(),
+        _stream_handle(ref.device, stream)), "plane_stats_batch_noalloc")
+    return out_noise, out_moments
 
 
 def plane_stats_batch_selfalloc(ref, dist, bpc: int, out_noise, out_moments, stream=None):

@@ -65,7 +65,9 @@ enum vqx_status {
     VQX_E_NO_DEVICE = -8, /* no usable HIP device */
     VQX_E_STRIDE = -9,    /* plane views: a row stride below w, a negative frame stride,
                              or a plane whose last sample lies past 2^62 bytes */
-    VQX_E_PLANES = -10    /* several planes: nplanes outside 1..VQX_MAX_PLANES */
+    VQX_E_PLANES = -10,   /* several planes: nplanes outside 1..VQX_MAX_PLANES */
+    VQX_E_SCRATCH = -11   /* vqx_plane_stats_batch_noalloc: the batch needs more scratch than
+                             VQX_NOALLOC_SCRATCH_BYTES */
 };
 
 /* VQX_ABI_VERSION of the loaded library. */
@@ -127,6 +129,32 @@ int vqx_plane_stats_batch(const void *ref, const void *dist, int w, int h, int b
 int vqx_plane_stats_batch_ws(const void *ref, const void *dist, int w, int h, int bpc, int nframes,
                              uint64_t *out_noise, uint64_t *out_moments,
                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The five
+ * sums of vqx_plane_stats_batch_ws, with the same arguments minus the
+ * workspace, and no allocation of any kind: the scratch is one fixed array
+ * per GPU in the library's device memory, VQX_NOALLOC_SCRATCH_BYTES long,
+ * held by each GPU the library runs on until the process ends.  A batch
+ * whose vqx_plane_stats_workspace_bytes() exceeds it is rejected with
+ * VQX_E_SCRATCH (4 MiB holds, for example, 128 frames of 3840x2160 or 512
+ * of 1920x1080 at 9..16 bits).
+ *
+ * Every call on one GPU uses that GPU's one array, and the array keeps the
+ * last call's contents.  Each call writes every scratch byte it reads, so
+ * nothing needs clearing; but calls that overlap on one GPU (on two streams,
+ * or from two threads) race on the array, and the caller must order them.
+ * The first call on a device looks up the array's device address (a symbol
+ * lookup, no allocation) with that device current; the device is the one
+ * of `stream` (the current device for the null stream).
+ *
+ * Errors: as vqx_plane_stats_batch, VQX_E_SCRATCH (before anything is
+ * queued), and VQX_E_HIP if the address lookup fails.
+ */
+#define VQX_NOALLOC_SCRATCH_BYTES (4u << 20)
+int vqx_plane_stats_batch_noalloc(const void *ref, const void *dist, int w, int h, int bpc, int nframes,
+                                  uint64_t *out_noise, uint64_t *out_moments, void *stream);
 
 /*
  * As vqx_plane_stats_batch_ws, and also stamps two caller-created

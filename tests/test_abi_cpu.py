@@ -47,9 +47,11 @@ def test_status_codes_match_header():
     for name, value in (("VQX_OK", 0), ("VQX_E_NULL", -1), ("VQX_E_DIMS", -2), ("VQX_E_BPC", -3),
                         ("VQX_E_NFRAMES", -4), ("VQX_E_ALIGN", -5), ("VQX_E_WORKSPACE", -6),
                         ("VQX_E_HIP", -7), ("VQX_E_NO_DEVICE", -8), ("VQX_E_STRIDE", -9),
-                        ("VQX_E_PLANES", -10)):
+                        ("VQX_E_PLANES", -10), ("VQX_E_SCRATCH", -11)):
         assert re.search(rf"\b{name} = {value}\b", text), name
-    for s in range(-10, 1):
+    assert re.search(r"#define VQX_NOALLOC_SCRATCH_BYTES \(4u << 20\)", text)
+    assert vqx.NOALLOC_SCRATCH_BYTES == 4 << 20
+    for s in range(-11, 1):
         assert vqx.status_string(s) and vqx.status_string(s) != "unknown status"
     assert vqx.status_string(-99) == "unknown status"
 
@@ -130,11 +132,14 @@ ARG_ERRORS = [
 
 
 def _call(L, b, ws=None, ws_bytes=0, ref=None, dist=None, noise=None, moments=None, w=16, h=4,
-          bpc=8, nframes=2, ref_off=0, dist_off=0, noise_off=0):
+          bpc=8, nframes=2, ref_off=0, dist_off=0, noise_off=0, noalloc=False):
     ref = b.ref + ref_off if ref is None else ref
     dist = b.dist + dist_off if dist is None else dist
     noise = b.noise + noise_off if noise is None else noise
     moments = b.moments if moments is None else moments
+    if noalloc:
+        return L.vqx_plane_stats_batch_noalloc(ref or None, dist or None, w, h, bpc, nframes,
+                                               noise or None, moments or None, None)
     if ws is None:
         return L.vqx_plane_stats_batch(ref or None, dist or None, w, h, bpc, nframes,
                                        noise or None, moments or None, None)
@@ -143,16 +148,31 @@ def _call(L, b, ws=None, ws_bytes=0, ref=None, dist=None, noise=None, moments=No
 
 
 @pytest.mark.parametrize("name,kw,status", ARG_ERRORS, ids=[a[0] for a in ARG_ERRORS])
-@pytest.mark.parametrize("form", ["self-allocating", "workspace"])
+@pytest.mark.parametrize("form", ["self-allocating", "workspace", "no-alloc"])
 def test_argument_errors_leave_outputs_untouched(L, name, kw, status, form):
     b = _Buffers()
     if form == "workspace":
         ws = np.zeros(4096, dtype=np.uint8)
         got = _call(L, b, ws=(ws.ctypes.data + 255) // 256 * 256, ws_bytes=1024, **kw)
     else:
-        got = _call(L, b, **kw)
+        got = _call(L, b, noalloc=form == "no-alloc", **kw)
     assert got == status
     assert b.untouched()
+
+
+def test_noalloc_scratch_limit(L):
+    """A batch whose workspace exceeds the fixed scratch is rejected before
+    any device call (so also without a device), outputs untouched; the
+    largest batch that fits is not rejected for its size."""
+    b = _Buffers()
+    per_frame = vqx.plane_stats_workspace_bytes(3840, 2160, 16, 1)
+    fits = vqx.NOALLOC_SCRATCH_BYTES // per_frame
+    assert vqx.plane_stats_workspace_bytes(3840, 2160, 16, fits) <= vqx.NOALLOC_SCRATCH_BYTES
+    assert _call(L, b, w=3840, h=2160, bpc=16, nframes=fits + 1, noalloc=True) == vqx.E_SCRATCH
+    assert b.untouched()
+    if not _has_gpu():
+        assert _call(L, b, w=3840, h=2160, bpc=16, nframes=fits, noalloc=True) == vqx.E_NO_DEVICE
+        assert b.untouched()
 
 
 def test_cpu_order_arguments(L):
@@ -216,6 +236,7 @@ def test_valid_call_without_device_reports_no_device(L):
     ws = np.zeros(4096, dtype=np.uint8)
     base = (ws.ctypes.data + 255) // 256 * 256
     assert _call(L, b, ws=base, ws_bytes=1024) == vqx.E_NO_DEVICE
+    assert _call(L, b, noalloc=True) == vqx.E_NO_DEVICE
     assert b.untouched()
 
 
