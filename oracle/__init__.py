@@ -13,6 +13,9 @@ Two independent forms of the same definition:
   round-to-24-bits for the float square (``exact.py``).
 * ``int_*`` -- O3, the integer psnr twin: exact sums of (ref - dist)^2 and
   their score (``int_psnr.py``).
+* ``running_float_sums`` -- O4, the running binary32 sum of a buffer of
+  float terms, added one by one in buffer order (``running_float_sum.c``),
+  as the psnr_hvs CPU extractor sums its terms.
 
 Below 2^53 units the two agree bit for bit; past it O1 is the CPU's rounded
 value and O2 the exact one, within ``past53_bound``.
@@ -47,6 +50,9 @@ def _load():
             fn.restype = ctypes.c_int
             fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                            ctypes.c_int, ctypes.c_void_p]
+        lib.oracle_running_float_sums.restype = ctypes.c_int
+        lib.oracle_running_float_sums.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
+                                                  ctypes.c_void_p]
         lib.oracle_batch_sums.restype = ctypes.c_int
         lib.oracle_batch_sums.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                           ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -85,4 +91,19 @@ def seq_batch_sums(ref: np.ndarray, dist: np.ndarray, bpc: int) -> np.ndarray:
     rc = _load().oracle_batch_sums(ref.ctypes.data, dist.ctypes.data, w, h, bpc, f, out.ctypes.data)
     if rc != 0:
         raise ValueError("oracle_batch_sums rejected its arguments")
+    return out
+
+
+def running_float_sums(terms: np.ndarray) -> np.ndarray:
+    """O4: for ``[nsums][n]`` float32 terms, the ``[nsums]`` float32 values of
+    a binary32 accumulator after each buffer's terms are added one by one,
+    in order, from zero."""
+    terms = np.ascontiguousarray(terms, dtype=np.float32)
+    if terms.ndim == 1:
+        terms = terms[None, :]
+    nsums, n = terms.shape
+    out = np.zeros(nsums, dtype=np.float32)
+    rc = _load().oracle_running_float_sums(terms.ctypes.data, n, nsums, out.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_running_float_sums rejected its arguments")
     return out

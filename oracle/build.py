@@ -11,7 +11,7 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCE = os.path.join(HERE, "float_sums.c")
+SOURCES = [os.path.join(HERE, f) for f in ("float_sums.c", "running_float_sum.c")]
 LIBRARY = os.path.join(HERE, "libfloat_sums.so")
 
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fno-unsafe-math-optimizations",
@@ -19,9 +19,9 @@ CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fno-unsafe
 
 
 def build(verbose: bool = False) -> str:
-    """Compile float_sums.c into libfloat_sums.so beside it; return its path."""
+    """Compile the C sources into libfloat_sums.so beside them; return its path."""
     tmp = LIBRARY + ".tmp"
-    cmd = ["gcc", *CFLAGS, SOURCE, "-o", tmp]
+    cmd = ["gcc", *CFLAGS, *SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

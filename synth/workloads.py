@@ -230,3 +230,70 @@ def sha256(*arrays) -> str:
     for a in arrays:
         m.update(np.ascontiguousarray(a).tobytes())
     return m.hexdigest()
+
+
+# ------------------------------------------------------- float term buffers
+
+HVS_4K_BLOCKS = (548, 308)  # 8x8 blocks at a step of 7 over 3840x2160: 10 802 176 terms
+
+
+def hvs_like_terms(nblocks: int, nplanes: int = 1, seed: int = 1397) -> np.ndarray:
+    """Seeded stand-in for the psnr_hvs CPU extractor's term buffers:
+    ``[nplanes][nblocks * 64]`` float32, 64 terms per 8x8 block (row-major
+    within the block, blocks in raster order), each the binary32 square of a
+    masked coefficient error, most of them zero.
+
+    The real terms come from a DCT and CSF and masking tables that are not
+    available here; this draws their shape instead.  Per block, a scale
+    (lognormal around 8) times a weight falling off with the coefficient's
+    row + column (a synthetic stand-in for a contrast sensitivity curve)
+    times |N(0, 1)| gives the error; a per-block threshold between 0.12 and
+    0.9 of the scale (the plane's offset drawn in 0.12..0.3) masks it; the
+    term is the float square of what is left.  A plane has 15 to 32 % nonzero
+    terms, as the psnr_hvs page reports.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    r, c = np.meshgrid(np.arange(8), np.arange(8), indexing="ij")
+    weight = (1.0 / (1.0 + 0.25 * (r + c))).astype(np.float32).ravel()
+    out = np.empty((nplanes, nblocks * 64), dtype=np.float32)
+    for p in range(nplanes):
+        lo = rng.uniform(0.12, 0.3)
+        scale = (np.exp(rng.normal(0.0, 1.0, nblocks)) * 8.0).astype(np.float32)
+        mask = (scale * rng.uniform(lo, lo + 0.6, nblocks).astype(np.float32)).astype(np.float32)
+        err = (np.abs(rng.normal(0.0, 1.0, (nblocks, 64))).astype(np.float32) * scale[:, None]
+               * weight[None, :]).astype(np.float32)
+        v = np.maximum(err - mask[:, None], np.float32(0)).astype(np.float32)
+        out[p] = (v * v).ravel()
+    return out
+
+
+def float_terms(n: int, kind: str, seed: int) -> np.ndarray:
+    """Seeded float32 term buffers of ``n`` terms that stress a running float
+    sum: ``"uniform"`` (0..1), ``"spread"`` (magnitudes over 2^-30..2^30),
+    ``"tiny"`` (subnormals and the smallest normals), ``"ties"`` (small
+    integers and halves after a large first term, so that many adds fall
+    halfway between two floats), ``"stall"`` (a large first term, then terms
+    below half its last place, which never move the sum), ``"ascending"``
+    and ``"huge"`` (terms near the largest float, so that the sum overflows
+    to infinity)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if kind == "uniform":
+        t = rng.random(n, dtype=np.float32)
+    elif kind == "spread":
+        t = (rng.random(n) * 2.0 ** rng.integers(-30, 31, n)).astype(np.float32)
+    elif kind == "tiny":
+        bits = rng.integers(0, 1 << 24, n, dtype=np.uint32)
+        t = bits.view(np.float32).copy()
+    elif kind == "ties":
+        t = (rng.integers(0, 8, n) * 0.5).astype(np.float32)
+        t[0] = np.float32(2.0 ** 22)
+    elif kind == "stall":
+        t = (rng.random(n) * 0.49).astype(np.float32)
+        t[0] = np.float32(2.0 ** 24)
+    elif kind == "ascending":
+        t = np.sort(rng.random(n).astype(np.float32) * np.float32(1000.0))
+    elif kind == "huge":
+        t = (rng.random(n) * 1.0e37 + 1.0e37).astype(np.float32)
+    else:
+        raise ValueError(kind)
+    return t.astype(np.float32)
