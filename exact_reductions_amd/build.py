@@ -8,7 +8,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = [os.path.join(CSRC, f) for f in ("plane_stats.hip", "cpu_order.hip", "stage1_mapped.hip", "plane_views.hip", "host_stream.hip", "vqx_api.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("plane_stats.hip", "cpu_order.hip", "stage1_mapped.hip", "plane_views.hip", "host_stream.hip",
+                                            "float_sum.hip", "vqx_api.hip")]
 LIBRARY = os.path.join(HERE, "libvqx.so")
 ARCH = "gfx950"
 

@@ -1,0 +1,506 @@
+// The psnr_hvs CPU extractor's running float sum, reproduced on the device
+// bit for bit: for each buffer of float terms, the value a binary32
+// accumulator holds after the terms were added one by one, in order, from
+// zero.
+//
+// Sources (web pages, cited by title and section):
+//   [HVS]    "ADR-1397: GPU psnr_hvs twins reproduce the CPU's running float
+//            sum bit for bit"
+//   [MOMENT] "ADR-1447: float_moment_hip adds the float squares the CPU adds,
+//            and is bit-identical while the CPU's own sum is exact"
+//
+// calc_psnrhvs() adds every masked coefficient error of a plane into one
+// running float, and each add's rounding depends on the sum so far [HVS,
+// Context].  The page stores the terms on the device (64 per 8x8 block,
+// row-major, blocks in raster order) and sums them on the host [HVS,
+// Decision]; an order-preserving reduction on the device is its deferred
+// alternative [HVS, Alternatives].  This file is that reduction.
+//
+// The terms are nonnegative (squares), so the sum S never decreases.  While
+// S stays in one binade [2^E, 2^(E+1)), S = m * u with u = 2^(E-23) and
+// 2^23 <= m < 2^24 (zero and the subnormals share the unit 2^-149 with the
+// lowest normal binade, so there E = -126 and 0 <= m < 2^24).  A term t
+// moves m by h = t/u rounded half up, except on a tie (t/u exactly halfway
+// between two integers), where the result is whichever of m + h - 1 and
+// m + h is even.  So a run of terms acts on m as a two-state machine on m's
+// parity: the increase is the run's sum of h less the ties rounded down,
+// whose count depends only on the parity at the start -- the same algebra
+// as the CPU's double sums past 2^53 (cpu_order.hip), here with a unit that
+// is a power of two of any sign.  Such maps compose in order.
+//
+//  1. fsum_tile_totals: per tile of 4096 terms, the total in binary64 (a
+//     prediction only) and whether any term is negative or not finite;
+//  2. fsum_plan, per buffer: the running total at each tile start, which
+//     predicts the binade the float sum is in there, with a margin;
+//  3. fsum_tile_maps: each tile's map in the predicted binade (and the
+//     next, where the tile may cross into it);
+//  4. fsum_walk, one workgroup per buffer: with the running value S, scans
+//     up to 256 tile maps at once for S's binade and applies all of them up
+//     to the first tile that has no map for that binade or whose map leaves
+//     it; that tile is taken as 256 runs of 16 terms, scanned the same way,
+//     and the run where S leaves its binade is added term by term in
+//     binary32.  Every step is checked against S itself, so a prediction
+//     decides only how fast the walk is, never what it returns.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plane_stats.h"
+
+#pragma clang fp contract(off)
+
+namespace vqx {
+namespace {
+
+constexpr int kThreads = kFsThreads;               // four wave64s
+constexpr int kRun = kFsRunTerms;                  // terms per thread in a tile
+constexpr int kTile = kFsTileTerms;                // terms per tile
+constexpr int kPad = kTile + kTile / kRun;         // LDS words of a tile, one pad per run
+constexpr uint32_t kTop = 1u << 24;                // m at the top of a binade
+constexpr uint32_t kSat = 1u << 25;                // an increase this large leaves any binade
+constexpr uint32_t kNaN = 0x7fc00000u;
+constexpr uint32_t kInf = 0x7f800000u;
+static_assert(kThreads * kRun == kTile, "a tile is one run per thread");
+
+// The effect of a run of terms on m inside one binade: m grows by H less
+// the ties rounded down, td0 from an even start and td1 from an odd one.
+// H saturates at kSat (the run then certainly leaves the binade).
+struct Map {
+    uint32_t H, td0, td1;
+};
+
+__device__ __forceinline__ Map identity_map() { return {0u, 0u, 0u}; }
+__device__ __forceinline__ Map leaving_map() { return {kSat, 0u, 0u}; }
+
+// a, then b
+__device__ __forceinline__ Map compose(const Map &a, const Map &b)
+{
+    // m's parity after a, from each start parity
+    const uint32_t q0 = (a.H - a.td0) & 1u;
+    const uint32_t q1 = (1u + a.H - a.td1) & 1u;
+    Map c;
+    const uint32_t h = a.H + b.H;  // both <= kSat: no wrap
+    c.H = h > kSat ? kSat : h;
+    c.td0 = a.td0 + (q0 ? b.td1 : b.td0);
+    c.td1 = a.td1 + (q1 ? b.td1 : b.td0);
+    return c;
+}
+
+// One term (a binary32 bit pattern, nonnegative) in the binade whose unit is
+// 2^uexp.  t = M * 2^texp; h = M / 2^k rounded half up with k = uexp - texp.
+__device__ __forceinline__ Map term_map(uint32_t t, int uexp)
+{
+    const uint32_t ef = (t >> 23) & 0xffu;
+    const uint32_t M = ef ? ((t & 0x7fffffu) | 0x800000u) : (t & 0x7fffffu);
+    const int texp = ef ? static_cast<int>(ef) - 150 : -149;
+    const int k = uexp - texp;
+    uint32_t h = 0;
+    bool tie = false;
+    if (k <= 0) {
+        // t is a whole number of units
+        h = M == 0 ? 0u : (k <= -2 ? kSat : (M << -k));
+        h = h > kSat ? kSat : h;
+    } else if (k < 26) {
+        const uint32_t half = 1u << (k - 1);
+        h = (M + half) >> k;
+        tie = (M & ((1u << k) - 1u)) == half;
+    }  // else t < u/4: h = 0, no tie
+    // on a tie from parity p, m + h is rounded down when it is odd
+    return {h, tie ? (h & 1u) : 0u, tie ? ((h & 1u) ^ 1u) : 0u};
+}
+
+// S's binade: the unit's exponent and m.
+__device__ __forceinline__ void split(uint32_t S, int &uexp, uint32_t &m)
+{
+    const uint32_t ef = S >> 23;
+    if (ef <= 1) {  // zero, subnormal, or the lowest normal binade
+        uexp = -149;
+        m = S;
+    } else {
+        uexp = static_cast<int>(ef) - 150;
+        m = (S & 0x7fffffu) | 0x800000u;
+    }
+}
+
+// S from its binade and m (m <= 2^24; m == 2^24 is the next power of two,
+// or infinity above the largest binade).
+__device__ __forceinline__ uint32_t join(int uexp, uint32_t m)
+{
+    return (static_cast<uint32_t>(uexp + 149) << 23) + m;
+}
+
+__device__ __forceinline__ bool bad_term(uint32_t t)
+{
+    return (t > 0x80000000u) || ((t & 0x7f800000u) == 0x7f800000u);
+}
+
+// ------------------------------------------------------- workgroup scans
+// Inclusive ordered scan of the threads' maps (thread order = term order).
+// All threads must call it.
+__device__ __forceinline__ Map scan_maps(Map x)
+{
+    __shared__ Map wave_total[kThreads / 64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        Map y;
+        y.H = __shfl_up(x.H, d, 64);
+        y.td0 = __shfl_up(x.td0, d, 64);
+        y.td1 = __shfl_up(x.td1, d, 64);
+        if (lane >= d)
+            x = compose(y, x);
+    }
+    if (lane == 63)
+        wave_total[wave] = x;
+    __syncthreads();
+    Map before = identity_map();
+    for (int w = 0; w < wave; ++w)
+        before = compose(before, wave_total[w]);
+    __syncthreads();
+    return compose(before, x);
+}
+
+// Ordered composition of all the threads' maps; every thread gets it.
+__device__ __forceinline__ Map reduce_maps(Map x)
+{
+    __shared__ Map last;
+    x = scan_maps(x);
+    if (threadIdx.x == kThreads - 1)
+        last = x;
+    __syncthreads();
+    const Map r = last;
+    __syncthreads();
+    return r;
+}
+
+// The first thread whose flag is set, or kThreads.  All threads must call it.
+__device__ __forceinline__ int first_set(bool flag)
+{
+    __shared__ int first[kThreads / 64];
+    const uint64_t b = __ballot(flag);
+    if ((threadIdx.x & 63) == 0)
+        first[threadIdx.x >> 6] = b ? static_cast<int>(__builtin_ctzll(b)) + (threadIdx.x & ~63) : kThreads;
+    __syncthreads();
+    int f = kThreads;
+    for (int w = 0; w < kThreads / 64; ++w)
+        f = first[w] < f ? first[w] : f;
+    __syncthreads();
+    return f;
+}
+
+// A tile's terms into LDS, term i at i + i/kRun (a pad word per run keeps
+// each thread's run on its own banks); missing terms past the buffer's end
+// are zeros, which add nothing.
+__device__ __forceinline__ void load_tile(const float *terms, int64_t first, int64_t count, uint32_t *lds)
+{
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(terms) + first;
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+        const int i = threadIdx.x + j * kThreads;
+        lds[i + i / kRun] = i < count ? __builtin_nontemporal_load(src + i) : 0u;
+    }
+    __syncthreads();
+}
+
+// This thread's run of the tile in LDS, in the binade of unit 2^uexp.
+__device__ __forceinline__ Map run_map(const uint32_t *lds, int uexp)
+{
+    const uint32_t *r = lds + threadIdx.x * (kRun + 1);
+    Map x = identity_map();
+#pragma unroll
+    for (int j = 0; j < kRun; ++j)
+        x = compose(x, term_map(r[j], uexp));
+    return x;
+}
+
+// ------------------------------------------------------------- kernel 1
+// grid (tiles, buffers)
+__global__ __launch_bounds__(kThreads) void fsum_tile_totals(const float *terms, int64_t nterms, int ntiles,
+                                                             double *totals, uint32_t *bad)
+{
+    const int tile = blockIdx.x, buf = blockIdx.y;
+    const int64_t first = static_cast<int64_t>(tile) * kTile;
+    const int64_t count = nterms - first < kTile ? nterms - first : kTile;
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(terms) + static_cast<int64_t>(buf) * nterms + first;
+    double s = 0.0;
+    uint32_t b = 0;
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+        const int i = threadIdx.x + j * kThreads;
+        if (i < count) {
+            const uint32_t t = __builtin_nontemporal_load(src + i);
+            b |= bad_term(t) ? 1u : 0u;
+            s += static_cast<double>(__uint_as_float(t & 0x7fffffffu));
+        }
+    }
+    __shared__ double lds_s[kThreads];
+    __shared__ uint32_t lds_b[kThreads];
+    lds_s[threadIdx.x] = s;
+    lds_b[threadIdx.x] = b;
+    __syncthreads();
+    for (int off = kThreads / 2; off > 0; off >>= 1) {
+        if (static_cast<int>(threadIdx.x) < off) {
+            lds_s[threadIdx.x] += lds_s[threadIdx.x + off];
+            lds_b[threadIdx.x] |= lds_b[threadIdx.x + off];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        totals[static_cast<int64_t>(buf) * ntiles + tile] = lds_s[0];
+        bad[static_cast<int64_t>(buf) * ntiles + tile] = lds_b[0];
+    }
+}
+
+// ------------------------------------------------------------- kernel 2
+// The binade (as the unit's exponent) a value v >= 0 lies in, clamped to
+// the float range.
+__device__ __forceinline__ int unit_exponent_of(double v)
+{
+    if (!(v >= 0x1p-125))
+        return -149;
+    if (v >= 0x1p127)
+        return 127 - 23;
+    int e;
+    (void)frexp(v, &e);  // v = f * 2^e, 0.5 <= f < 1: binade e - 1
+    return (e - 1) - 23;
+}
+
+// One workgroup per buffer: the running total at each tile start and the
+// binades the float sum may be in over each tile.  plan = (unit exponent of
+// the first + 256) | (count << 16), count 0 (no maps), 1 or 2.
+__global__ __launch_bounds__(kThreads) void fsum_plan(const double *totals, const uint32_t *bad, int ntiles,
+                                                      uint32_t *plan, uint32_t *buffer_bad)
+{
+    const int buf = blockIdx.x;
+    const double *tot = totals + static_cast<int64_t>(buf) * ntiles;
+    const uint32_t *bd = bad + static_cast<int64_t>(buf) * ntiles;
+    uint32_t *pl = plan + static_cast<int64_t>(buf) * ntiles;
+    const int per = (ntiles + kThreads - 1) / kThreads;
+    const int lo = threadIdx.x * per, hi = lo + per < ntiles ? lo + per : ntiles;
+    double mine = 0.0;
+    uint32_t b = 0;
+    for (int i = lo; i < hi; ++i) {
+        mine += tot[i];
+        b |= bd[i];
+    }
+    __shared__ double ex[kThreads];
+    __shared__ uint32_t anybad;
+    if (threadIdx.x == 0)
+        anybad = 0;
+    ex[threadIdx.x] = mine;
+    __syncthreads();
+    if (b)
+        atomicOr(&anybad, 1u);
+    // exclusive prefix of the threads' totals (a prediction: the order of
+    // these double adds does not matter)
+    for (int d = 1; d < kThreads; d <<= 1) {
+        const double v = static_cast<int>(threadIdx.x) >= d ? ex[threadIdx.x - d] : 0.0;
+        __syncthreads();
+        ex[threadIdx.x] += v;
+        __syncthreads();
+    }
+    double p = ex[threadIdx.x] - mine;
+    constexpr double kMargin = 1.0 / 128;  // the float sum's drift from the exact one, allowed
+    for (int i = lo; i < hi; ++i) {
+        const int e_lo = unit_exponent_of(p * (1.0 - kMargin));
+        const int e_hi = unit_exponent_of((p + tot[i]) * (1.0 + kMargin));
+        const int n = e_hi - e_lo + 1;
+        pl[i] = static_cast<uint32_t>(e_lo + 256) | (static_cast<uint32_t>(n <= 2 ? n : 0) << 16);
+        p += tot[i];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0)
+        buffer_bad[buf] = anybad;
+}
+
+// ------------------------------------------------------------- kernel 3
+// grid (tiles, buffers): each planned tile's map in its one or two binades.
+__global__ __launch_bounds__(kThreads) void fsum_tile_maps(const float *terms, int64_t nterms, int ntiles,
+                                                           const uint32_t *plan, Map *maps)
+{
+    const int tile = blockIdx.x, buf = blockIdx.y;
+    const int64_t at = static_cast<int64_t>(buf) * ntiles + tile;
+    const uint32_t pl = plan[at];
+    const int n = static_cast<int>(pl >> 16);
+    if (n == 0)
+        return;
+    const int uexp = static_cast<int>(pl & 0xffffu) - 256;
+    __shared__ uint32_t lds[kPad];
+    const int64_t first = static_cast<int64_t>(tile) * kTile;
+    load_tile(terms + static_cast<int64_t>(buf) * nterms, first, nterms - first, lds);
+    for (int k = 0; k < n; ++k) {
+        const Map m = reduce_maps(run_map(lds, uexp + k));
+        if (threadIdx.x == 0)
+            maps[2 * at + k] = m;
+    }
+}
+
+// ------------------------------------------------------------- kernel 4
+// Applies a scanned map to (uexp, m): the new m, or kSat+ when it leaves.
+__device__ __forceinline__ uint32_t apply(const Map &x, uint32_t m)
+{
+    if (x.H >= kSat)
+        return kSat + kTop;
+    return m + x.H - ((m & 1u) ? x.td1 : x.td0);
+}
+
+// The tile in LDS, with S (bit pattern) at its start: S after it.  All
+// threads must call it.
+__device__ uint32_t walk_tile(const uint32_t *lds, uint32_t S)
+{
+    __shared__ uint32_t shared_S;
+    int r0 = 0;  // runs before r0 are added
+    while (r0 < kThreads && S != kInf) {
+        int uexp;
+        uint32_t m;
+        split(S, uexp, m);
+        const int me = static_cast<int>(threadIdx.x);
+        const Map x = me >= r0 ? run_map(lds, uexp) : identity_map();
+        const uint32_t after = apply(scan_maps(x), m);  // m after this thread's run
+        const int stop = first_set(me >= r0 && after >= kTop);
+        // S before run `stop` (after the whole tile if none stops)
+        if (me == 0)
+            shared_S = S;
+        __syncthreads();
+        if (me == stop - 1 && me >= r0)
+            shared_S = join(uexp, after);
+        __syncthreads();
+        S = shared_S;
+        __syncthreads();
+        if (stop == kThreads)
+            break;
+        // run `stop` reaches the binade's top exactly -- applied whole: the
+        // terms after the top add nothing in either binade -- or crosses
+        // it, and is added term by term in binary32
+        if (me == stop) {
+            if (after == kTop) {
+                shared_S = join(uexp, kTop);
+            } else {
+                float f = __uint_as_float(S);
+                const uint32_t *r = lds + stop * (kRun + 1);
+                for (int j = 0; j < kRun; ++j)
+                    f = f + __uint_as_float(r[j]);
+                shared_S = __float_as_uint(f);
+            }
+        }
+        __syncthreads();
+        S = shared_S;
+        __syncthreads();
+        r0 = stop + 1;
+    }
+    return S;
+}
+
+// One workgroup per buffer.
+__global__ __launch_bounds__(kThreads) void fsum_walk(const float *terms, int64_t nterms, int ntiles,
+                                                      const uint32_t *plan, const Map *maps,
+                                                      const uint32_t *buffer_bad, float *out)
+{
+    const int buf = blockIdx.x;
+    __shared__ uint32_t lds[kPad];
+    __shared__ uint32_t shared_S;
+    const float *tb = terms + static_cast<int64_t>(buf) * nterms;
+    if (ntiles == 0) {  // no terms: the accumulator's +0
+        if (threadIdx.x == 0)
+            out[buf] = 0.0f;
+        return;
+    }
+    if (buffer_bad[buf]) {
+        if (threadIdx.x == 0)
+            out[buf] = __uint_as_float(kNaN);
+        return;
+    }
+    uint32_t S = 0;  // +0
+    int t0 = 0;
+    while (t0 < ntiles && S != kInf) {
+        int uexp;
+        uint32_t m;
+        split(S, uexp, m);
+        // this thread's tile of the window, as a map in S's binade
+        const int tile = t0 + static_cast<int>(threadIdx.x);
+        Map x = identity_map();
+        if (tile < ntiles) {
+            const int64_t at = static_cast<int64_t>(buf) * ntiles + tile;
+            const uint32_t pl = plan[at];
+            const int e0 = static_cast<int>(pl & 0xffffu) - 256;
+            const int n = static_cast<int>(pl >> 16);
+            x = (uexp >= e0 && uexp < e0 + n) ? maps[2 * at + (uexp - e0)] : leaving_map();
+        }
+        const uint32_t after = apply(scan_maps(x), m);  // m after this thread's tile
+        const int me = static_cast<int>(threadIdx.x);
+        const int last = (ntiles - t0 < kThreads ? ntiles - t0 : kThreads) - 1;
+        const int stop = first_set(me <= last && after >= kTop);
+        const int end = stop == kThreads ? last + 1 : stop;  // tiles applied from the maps
+        // S before tile `end`
+        if (me == 0)
+            shared_S = S;
+        __syncthreads();
+        if (me == end - 1)
+            shared_S = join(uexp, after);
+        __syncthreads();
+        S = shared_S;
+        __syncthreads();
+        if (stop == kThreads) {
+            t0 += end;
+            continue;
+        }
+        // tile `stop` reaches the binade's top exactly (applied whole), or
+        // has no map for S's binade or leaves it (walked run by run)
+        if (me == stop)
+            shared_S = after == kTop ? 1u : 0u;
+        __syncthreads();
+        const bool top = shared_S != 0;
+        __syncthreads();
+        if (top) {
+            S = join(uexp, kTop);
+        } else {
+            const int64_t first = static_cast<int64_t>(t0 + stop) * kTile;
+            load_tile(tb, first, nterms - first, lds);
+            S = walk_tile(lds, S);
+        }
+        t0 += stop + 1;
+    }
+    if (threadIdx.x == 0)
+        out[buf] = __uint_as_float(S);
+}
+
+}  // namespace
+
+FloatSumLayout float_sum_layout(int64_t nterms, int nbuffers)
+{
+    auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+    FloatSumLayout l{};
+    l.ntiles = static_cast<int>((nterms + kTile - 1) / kTile);
+    const size_t cells = static_cast<size_t>(l.ntiles) * nbuffers;
+    l.totals = 0;
+    l.bad = up(l.totals + cells * sizeof(double));
+    l.plan = up(l.bad + cells * sizeof(uint32_t));
+    l.buffer_bad = up(l.plan + cells * sizeof(uint32_t));
+    l.maps = up(l.buffer_bad + static_cast<size_t>(nbuffers) * sizeof(uint32_t));
+    l.bytes = up(l.maps + cells * 2 * sizeof(Map));
+    return l;
+}
+
+hipError_t launch_float_sums(const float *terms, int64_t nterms, int nbuffers, float *out, void *workspace,
+                             hipStream_t stream)
+{
+    const FloatSumLayout l = float_sum_layout(nterms, nbuffers);
+    char *ws = static_cast<char *>(workspace);
+    double *totals = reinterpret_cast<double *>(ws + l.totals);
+    uint32_t *bad = reinterpret_cast<uint32_t *>(ws + l.bad);
+    uint32_t *plan = reinterpret_cast<uint32_t *>(ws + l.plan);
+    uint32_t *buffer_bad = reinterpret_cast<uint32_t *>(ws + l.buffer_bad);
+    Map *maps = reinterpret_cast<Map *>(ws + l.maps);
+    if (l.ntiles > 0) {
+        const dim3 grid(static_cast<unsigned>(l.ntiles), static_cast<unsigned>(nbuffers));
+        fsum_tile_totals<<<grid, kThreads, 0, stream>>>(terms, nterms, l.ntiles, totals, bad);
+        fsum_plan<<<dim3(static_cast<unsigned>(nbuffers)), kThreads, 0, stream>>>(totals, bad, l.ntiles, plan,
+                                                                                  buffer_bad);
+        fsum_tile_maps<<<grid, kThreads, 0, stream>>>(terms, nterms, l.ntiles, plan, maps);
+    }
+    fsum_walk<<<dim3(static_cast<unsigned>(nbuffers)), kThreads, 0, stream>>>(terms, nterms, l.ntiles, plan, maps,
+                                                                               buffer_bad, out);
+    return hipGetLastError();
+}
+
+}  // namespace vqx

@@ -241,4 +241,24 @@ hipError_t launch_plane_stats_mapped(const Geometry &g, const void *ref, const v
                                      uint64_t *out_moments, uint64_t *partials, const VecMap &map,
                                      hipStream_t stream);
 
+// The running float sum (float_sum.hip): buffers of float32 terms, each
+// summed in order into one binary32 accumulator.  Tiles of kFsTileTerms
+// terms, one workgroup of kFsThreads threads each, kFsRunTerms per thread.
+constexpr int kFsThreads = 256;
+constexpr int kFsRunTerms = 16;
+constexpr int kFsTileTerms = kFsThreads * kFsRunTerms;
+
+// Workspace of the running float sums: byte offsets of its parts.
+struct FloatSumLayout {
+    int ntiles;  // per buffer
+    size_t totals, bad, plan, buffer_bad, maps, bytes;
+};
+FloatSumLayout float_sum_layout(int64_t nterms, int nbuffers);
+
+// nbuffers buffers of nterms float32 terms each, one after another at
+// `terms`; out[k] gets buffer k's running sum (NaN if a term is negative or
+// not finite).
+hipError_t launch_float_sums(const float *terms, int64_t nterms, int nbuffers, float *out, void *workspace,
+                             hipStream_t stream);
+
 }  // namespace vqx

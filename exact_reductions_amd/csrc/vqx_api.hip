@@ -362,6 +362,42 @@ int vqx_plane_stats_batch_ws(const void *ref, const void *dist, int w, int h, in
                                           workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
+int vqx_float_sum_workspace_bytes(long long nterms, int nbuffers, size_t *bytes)
+{
+    if (!bytes)
+        return VQX_E_NULL;
+    if (nterms < 0 || nterms > (1ll << 36))
+        return VQX_E_DIMS;
+    if (nbuffers < 1 || nbuffers > 65535)
+        return VQX_E_NFRAMES;
+    *bytes = vqx::float_sum_layout(nterms, nbuffers).bytes;
+    return VQX_OK;
+}
+
+int vqx_float_running_sums_ws(const float *terms, long long nterms, int nbuffers, float *out_sums,
+                              void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!out_sums || (!terms && nterms > 0))
+        return VQX_E_NULL;
+    size_t need = 0;
+    int rc = vqx_float_sum_workspace_bytes(nterms, nbuffers, &need);
+    if (rc != VQX_OK)
+        return rc;
+    if (!aligned(terms, 4) || !aligned(out_sums, 4))
+        return VQX_E_ALIGN;
+    if (!workspace || !aligned(workspace, 16) || workspace_bytes < need)
+        return VQX_E_WORKSPACE;
+    rc = device_ready();
+    if (rc != VQX_OK)
+        return rc;
+    if (vqx::launch_float_sums(terms, nterms, nbuffers, out_sums, workspace, static_cast<hipStream_t>(stream)) !=
+        hipSuccess) {
+        (void)hipGetLastError();
+        return VQX_E_HIP;
+    }
+    return VQX_OK;
+}
+
 int vqx_plane_stats_batch_noalloc(const void *ref, const void *dist, int w, int h, int bpc, int nframes,
                                   uint64_t *out_noise, uint64_t *out_moments, void *stream)
 {

@@ -49,6 +49,8 @@ SYMBOLS = (
     "vqx_planes_workspace_bytes",
     "vqx_plane_stats_planes_ws",
     "vqx_psnr_int_planes_ws",
+    "vqx_float_sum_workspace_bytes",
+    "vqx_float_running_sums_ws",
 )
 
 
@@ -103,6 +105,8 @@ def lib() -> ctypes.CDLL:
             "vqx_planes_workspace_bytes": (i, [vp, i, i, i, ctypes.POINTER(sz)]),
             "vqx_plane_stats_planes_ws": (i, [vp, i, i, i, vp, vp, vp, sz, vp]),
             "vqx_psnr_int_planes_ws": (i, [vp, i, i, i, vp, vp, sz, vp]),
+            "vqx_float_sum_workspace_bytes": (i, [ctypes.c_longlong, i, ctypes.POINTER(sz)]),
+            "vqx_float_running_sums_ws": (i, [vp, ctypes.c_longlong, i, vp, vp, sz, vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -500,3 +504,34 @@ def plane_stats_host(ref, dist, bpc: int, frames_per_upload: int = 4, device=0, 
                                          out[:f].data_ptr(), out[f:].data_ptr(), ws.data_ptr(), ws.numel(),
                                          _stream_handle(dev, stream), cs), "plane_stats_host_ws")
     return out[:f], out[f:].view(f, 4)
+
+
+def float_sum_workspace_bytes(nterms: int, nbuffers: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().vqx_float_sum_workspace_bytes(nterms, nbuffers, ctypes.byref(out)), "float_sum_workspace_bytes")
+    return out.value
+
+
+def float_running_sums(terms, stream=None, out=None, workspace=None):
+    """The psnr_hvs running float sums: for ``terms`` [nbuffers][nterms]
+    float32 on the device, a [nbuffers] float32 device tensor with each
+    buffer's terms added one by one, in order, into a float from zero
+    (vqx_float_running_sums_ws).  The workspace comes from torch's caching
+    allocator unless given."""
+    import torch
+    if terms.dtype != torch.float32 or not terms.is_cuda:
+        raise TypeError("terms must be a float32 device tensor")
+    if terms.dim() == 1:
+        terms = terms.unsqueeze(0)
+    if terms.dim() != 2 or not terms.is_contiguous():
+        raise ValueError("terms must be a contiguous [nbuffers][nterms] tensor")
+    nb, n = terms.shape
+    if out is None:
+        out = torch.empty(nb, dtype=torch.float32, device=terms.device)
+    need = float_sum_workspace_bytes(n, nb)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=terms.device)
+    _check(lib().vqx_float_running_sums_ws(terms.data_ptr(), n, nb, out.data_ptr(), workspace.data_ptr(),
+                                           workspace.numel() * workspace.element_size(),
+                                           _stream_handle(terms.device, stream)), "float_running_sums_ws")
+    return out

@@ -440,6 +440,41 @@ int vqx_conclude_psnr_int(uint64_t noise, int w, int h, int bpc, double psnr_max
 int vqx_conclude_psnr_int_batch(const uint64_t *noise, int w, int h, int bpc, int nframes,
                                 double psnr_max, double *out);
 
+/* ------------------------------------------------------------------------
+ * The psnr_hvs running float sum [HVS = "ADR-1397: GPU psnr_hvs twins
+ * reproduce the CPU's running float sum bit for bit"].
+ *
+ * calc_psnrhvs() adds every masked coefficient error of a plane into one
+ * running float, so each add's rounding depends on the sum so far [HVS,
+ * Context]; the page's twins store the terms (64 per 8x8 block, row-major,
+ * blocks in raster order) and add them one by one into a float on the host
+ * [HVS, Decision].  This call does that sum on the device, with an
+ * order-preserving reduction [HVS, Alternatives]: for each of `nbuffers`
+ * buffers of `nterms` float32 terms, stored one after another at `terms`
+ * (device memory, 4-byte aligned), out_sums[k] (device, 4-byte aligned)
+ * receives, bit for bit, the float S after S = 0.0f; S += term, in buffer
+ * order, in IEEE binary32 round-to-nearest-even arithmetic.  The DCT, CSF
+ * and masking that make the terms are not part of it.
+ *
+ * Terms must be nonnegative and finite (squares); -0.0 adds like +0.0.  A
+ * buffer holding a negative, infinite or NaN term gets the quiet NaN
+ * 0x7fc00000 as its sum (a rule of this library, not of the CPU).  A sum
+ * that overflows is +infinity, as in the CPU's float.  nterms == 0 gives +0.
+ *
+ * Workspace: at least vqx_float_sum_workspace_bytes() bytes of device
+ * memory, 16-byte aligned, written before it is read (contents on entry do
+ * not matter); calls may not share one workspace concurrently.  The call
+ * only queues work on `stream`; results are valid once the stream passes it.
+ *
+ * Errors: VQX_E_NULL; VQX_E_DIMS (nterms < 0 or > 2^36); VQX_E_NFRAMES
+ * (nbuffers outside 1..65535); VQX_E_ALIGN; VQX_E_WORKSPACE; VQX_E_NO_DEVICE;
+ * VQX_E_HIP (launch failure, consumed).  Argument errors come before
+ * anything is queued and leave the outputs untouched.
+ */
+int vqx_float_sum_workspace_bytes(long long nterms, int nbuffers, size_t *bytes);
+int vqx_float_running_sums_ws(const float *terms, long long nterms, int nbuffers, float *out_sums,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
