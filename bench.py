@@ -70,6 +70,8 @@ METRIC_YUV420 = ("frames/s of the integer psnr twin on all three planes of plana
                  "(Y, U, V through plane views)")
 METRIC_HOST = ("frames/s of the exact sums of a batch in pinned host memory, PCIe upload included "
                "(3840x2160 16-bit)")
+METRIC_HVS_SUM = ("frames/s of the psnr_hvs running float sum of 3840x2160 luma planes (10 802 176 terms "
+                  "each, the float bit-identical to the CPU's sequential sum)")
 PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction, the published link rate
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "exact_reductions_amd", "csrc")
@@ -78,6 +80,8 @@ CPU_ORDER_SOURCES = STAGE1_SOURCES + [os.path.join(CSRC, "cpu_order.hip")]
 VIEW_SOURCES = [os.path.join(CSRC, f) for f in ("plane_views.hip", "reduce.h")]
 HOST_SOURCES = STAGE1_SOURCES + [os.path.join(CSRC, "host_stream.hip")]
 MAPPED_SOURCES = [os.path.join(CSRC, f) for f in ("stage1_mapped.hip", "reduce.h")]
+FLOAT_SUM_SOURCES = [os.path.join(CSRC, "float_sum.hip")]
+FLOAT_SUM_KERNELS = ("fsum_tile_totals", "fsum_plan", "fsum_tile_maps", "fsum_walk")
 CPU_ORDER_KERNELS = ("stage1_u16", "cpu_order_prefix", "cpu_order_maps", "cpu_order_walk")
 
 
@@ -111,6 +115,8 @@ def step_plan(mode: str, wl, pitch: int = 0, x0: int = 0):
         return "psnr_int_step", ("view_stage1", "view_combine"), VIEW_SOURCES
     if mode == "yuv420":
         return "psnr_int_yuv420_step", ("views_stage1", "views_combine"), VIEW_SOURCES
+    if mode == "hvs-sum":
+        return "float_sum_step", FLOAT_SUM_KERNELS, FLOAT_SUM_SOURCES
     return "host_step", ("stage1_u16", "stage2_combine"), HOST_SOURCES
 UNIT_POWER = (2, 1, 1, 2, 2)  # noise, ref1, dist1, ref2, dist2: units 1/s^power
 STAMP_EVERY = 8  # exact mode: steps per stage-1 dispatch timed with its own events
@@ -139,11 +145,14 @@ def parse_args(argv=None):
                    help="skip the oracle leg (and with it the parity gate); for profiler runs")
     p.add_argument("--input-cache", default=None, metavar="DIR",
                    help="keep the generated batch as .npy files in DIR and reuse them")
-    p.add_argument("--mode", choices=("exact", "cpu-order", "psnr-int", "yuv420", "host"), default="exact",
+    p.add_argument("--planes", type=int, default=32,
+                   help="hvs-sum mode: 3840x2160 term buffers per step")
+    p.add_argument("--mode", choices=("exact", "cpu-order", "psnr-int", "yuv420", "host", "hvs-sum"), default="exact",
                    help="exact: the exact sums (default); cpu-order: also the CPU's rounding past 2^53; "
                         "psnr-int: the integer psnr twin; yuv420: the integer psnr twin on the Y, U and V "
                         "planes of planar 4:2:0 frames; host: the exact sums of a batch in pinned host "
-                        "memory, uploads overlapped with the reduction")
+                        "memory, uploads overlapped with the reduction; hvs-sum: the psnr_hvs running float "
+                        "sum of psnr_hvs-like term buffers")
     p.add_argument("--streams", type=int, default=1,
                    help="streams the steps alternate over (step i on stream i %% N, each with its own "
                         "workspace): with more than one, consecutive steps overlap as in a pipeline of "
@@ -689,6 +698,129 @@ def make_mode(args, vqx, L, hip, np, torch, dev, st, wl, ref_np, dist_np, planes
     return m
 
 
+def run_hvs_sum(args, np, torch, synth, vqx):
+    """hvs-sum mode: each step sums ``args.planes`` psnr_hvs-like term
+    buffers of a 3840x2160 luma plane (548 x 308 blocks of 64 terms) with
+    vqx_float_running_sums_ws; two copies of the batch alternate, resident
+    in HBM.  The step is timed with HIP events around the timed region; the
+    roofline is the whole step against one read of the terms."""
+    dev = torch.device("cuda:0")
+    bw, bh = synth.HVS_4K_BLOCKS
+    n = bw * bh * 64
+    t_gen = time.perf_counter()
+    terms_np = synth.hvs_like_terms(bw * bh, args.planes, seed=1397)
+    t_gen = time.perf_counter() - t_gen
+    bufs = [torch.from_numpy(terms_np).to(dev) for _ in range(2)]
+    out = torch.empty(args.planes, dtype=torch.float32, device=dev)
+    ws_bytes = vqx.float_sum_workspace_bytes(n, args.planes)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    L = vqx.lib()
+    hip = HipEvents(vqx.hip_runtime())
+    st = torch.cuda.current_stream(dev).cuda_stream
+    torch.cuda.synchronize()
+
+    def step(i):
+        b = bufs[i % 2]
+        rc = L.vqx_float_running_sums_ws(b.data_ptr(), n, args.planes, out.data_ptr(), ws.data_ptr(), ws_bytes, st)
+        if rc != 0:
+            raise vqx.VqxError(rc, "vqx_float_running_sums_ws")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = hip.create(), hip.create()
+    t0 = time.perf_counter()
+    hip.record(e0, st)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    hip.record(e1, st)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    gpu_ms = hip.elapsed_ms(e0, e1) / args.steps
+    hip.destroy(e0)
+    hip.destroy(e1)
+    got = out.cpu().numpy()
+
+    alg = 4 * n * args.planes  # one read of the terms
+    achieved = alg / (gpu_ms * 1e-3) / 1e9
+    kernel, step_kernels, sources = step_plan("hvs-sum", None)
+    wname = f"3840x2160x{args.planes}_hvs"
+    traffic = stored_traffic(kernel, wname, tuple(sources))
+    result = {
+        "metric": METRIC_HVS_SUM,
+        "value": round(args.steps * args.planes / elapsed, 1),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 running sum (integer two-state maps inside a binade, binary32 adds where it crosses)",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{args.planes} psnr_hvs-like term buffers of a 3840x2160 luma plane "
+                         f"({bw}x{bh} blocks of 64 float32 terms, {n} each, 17-31 % nonzero)"),
+            "planes": args.planes, "terms_per_plane": n, "mode": "hvs-sum", "bytes_per_step": alg,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": f"{kernel} ({', '.join(step_kernels)})",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "traffic_source": (f"profiles/{kernel}_{wname}_hbm_traffic.txt" if traffic is not None else None),
+            "step_us_mean": round(gpu_ms * 1e3, 2),
+            "timed_by": "HIP events around the timed steps, per step",
+            "algorithmic_bytes_per_launch": alg,
+        },
+        "generation_s": round(t_gen, 1),
+    }
+    if not args.no_cpu_baseline:
+        want = oracle_module().running_float_sums(terms_np)
+        bad = int(np.count_nonzero(got.view(np.uint32) != want.view(np.uint32)))
+        result["parity"] = {"planes": args.planes, "failures": bad,
+                            "rule": "every running sum bit-identical to the sequential binary32 oracle"}
+        threads = cpu_threads()
+        result["cpu_baseline"] = time_oracle_float_sums(terms_np, threads)
+        if bad:
+            print(json.dumps({"error": "timed batch does not match the oracle", "parity": result["parity"]}),
+                  file=sys.stderr)
+            return 1
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def oracle_module():
+    import oracle
+    return oracle
+
+
+def time_oracle_float_sums(terms_np, threads):
+    """O4 (the sequential binary32 sum in C) over the batch's planes, one
+    plane per task on ``threads`` host threads, repeated to ~10 s."""
+    import concurrent.futures
+    oracle = oracle_module()
+    planes = terms_np.shape[0]
+    reps = 0
+    t0 = time.perf_counter()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as pool:
+        while time.perf_counter() - t0 < 10.0 or reps == 0:
+            list(pool.map(lambda k: oracle.running_float_sums(terms_np[k:k + 1]), range(planes)))
+            reps += 1
+    el = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    oracle.running_float_sums(terms_np[:1])
+    single = time.perf_counter() - t1
+    return {"value": round(reps * planes / el, 1), "unit": "frames/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} passes over the {planes} planes of the batch, the C sequential binary32 sum, "
+                      "one plane per task",
+            "single_thread_frames_per_s": round(1.0 / single, 1)}
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.workload is None:
@@ -709,6 +841,8 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.mode == "hvs-sum":
+        return run_hvs_sum(args, np, torch, synth, vqx)
     dev = torch.device("cuda:0")
     wl = synth.WORKLOADS[args.workload]
     w, h, bpc, nframes = wl.w, wl.h, wl.bpc, wl.nframes

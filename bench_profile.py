@@ -82,7 +82,7 @@ def rows(path):
 
 def short(name: str) -> str:
     for k in ("stage1_u16_mapped", "mapped_combine", "gather_view", "stage1_u16", "stage1_u8", "stage2_combine",
-              "bitwise_not", "cpu_order_prefix",
+              "bitwise_not", "cpu_order_prefix", "fsum_tile_totals", "fsum_plan", "fsum_tile_maps", "fsum_walk",
               "cpu_order_maps", "cpu_order_walk", "views_stage1", "views_combine",
               "view_stage1", "view_combine", "read_probe"):
         if k in name:
@@ -289,7 +289,9 @@ def main(argv=None):
     p.add_argument("--cache", default="/tmp/vqx_inputs")
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--frames-per-upload", type=int, default=4)
-    p.add_argument("--mode", choices=("exact", "cpu-order", "psnr-int", "yuv420", "host"), default="exact")
+    p.add_argument("--mode", choices=("exact", "cpu-order", "psnr-int", "yuv420", "host", "hvs-sum"),
+                   default="exact")
+    p.add_argument("--planes", type=int, default=32, help="hvs-sum mode: term buffers per step")
     p.add_argument("--pitch", type=int, default=0, help="as bench.py --pitch")
     p.add_argument("--x0", type=int, default=0, help="as bench.py --x0")
     p.add_argument("--valu", action="store_true", help="the VALU counter pass only")
@@ -335,6 +337,13 @@ def main(argv=None):
         ref, dist = synth.generate(args.workload)
         alg += bench_mod.past53_bytes(ref, dist, wl.bpc)
         del ref, dist
+    if args.mode == "hvs-sum":
+        bw, bh = synth.HVS_4K_BLOCKS
+        wname = f"3840x2160x{args.planes}_hvs"
+        alg = 4 * bw * bh * 64 * args.planes  # one read of the terms
+        bench += ["--planes", str(args.planes)]
+        wl = synth.Workload(0, f"{args.planes} psnr_hvs-like term buffers of a 3840x2160 plane", 3840, 2160,
+                            args.planes, 16, "psnr_hvs-like terms")
 
     if args.mode == "host":
         return profile_host(args, wl, wname, bench, src_sha)

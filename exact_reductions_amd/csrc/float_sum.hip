@@ -69,6 +69,14 @@ struct Map {
     uint32_t H, td0, td1;
 };
 
+// A tile's record: its plan (binades predicted) and its map in each.
+struct alignas(32) Rec {
+    uint32_t plan;  // (unit exponent of the first binade + 256) | (count << 16), count 0..2
+    Map m0, m1;     // maps in the first and the second planned binade
+    uint32_t unused;
+};
+static_assert(sizeof(Rec) == 32, "two 16-byte loads per record");
+
 __device__ __forceinline__ Map identity_map() { return {0u, 0u, 0u}; }
 __device__ __forceinline__ Map leaving_map() { return {kSat, 0u, 0u}; }
 
@@ -135,9 +143,10 @@ __device__ __forceinline__ bool bad_term(uint32_t t)
 }
 
 // ------------------------------------------------------- workgroup scans
-// Inclusive ordered scan of the threads' maps (thread order = term order).
-// All threads must call it.
-__device__ __forceinline__ Map scan_maps(Map x)
+// Ordered scan of the threads' maps (thread order = term order): returns
+// the inclusive prefix, and the exclusive one in `excl`.  All threads must
+// call it.
+__device__ __forceinline__ Map scan_maps(Map x, Map &excl)
 {
     __shared__ Map wave_total[kThreads / 64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -150,6 +159,12 @@ __device__ __forceinline__ Map scan_maps(Map x)
         if (lane >= d)
             x = compose(y, x);
     }
+    Map prev;
+    prev.H = __shfl_up(x.H, 1, 64);
+    prev.td0 = __shfl_up(x.td0, 1, 64);
+    prev.td1 = __shfl_up(x.td1, 1, 64);
+    if (lane == 0)
+        prev = identity_map();
     if (lane == 63)
         wave_total[wave] = x;
     __syncthreads();
@@ -157,7 +172,14 @@ __device__ __forceinline__ Map scan_maps(Map x)
     for (int w = 0; w < wave; ++w)
         before = compose(before, wave_total[w]);
     __syncthreads();
+    excl = compose(before, prev);
     return compose(before, x);
+}
+
+__device__ __forceinline__ Map scan_maps(Map x)
+{
+    Map excl;
+    return scan_maps(x, excl);
 }
 
 // Ordered composition of all the threads' maps; every thread gets it.
@@ -191,9 +213,9 @@ __device__ __forceinline__ int first_set(bool flag)
 // A tile's terms into LDS, term i at i + i/kRun (a pad word per run keeps
 // each thread's run on its own banks); missing terms past the buffer's end
 // are zeros, which add nothing.
-__device__ __forceinline__ void load_tile(const float *terms, int64_t first, int64_t count, uint32_t *lds)
+__device__ __forceinline__ void load_tile(const float *tile_base, int64_t count, uint32_t *lds)
 {
-    const uint32_t *src = reinterpret_cast<const uint32_t *>(terms) + first;
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(tile_base);
 #pragma unroll
     for (int j = 0; j < kRun; ++j) {
         const int i = threadIdx.x + j * kThreads;
@@ -214,40 +236,82 @@ __device__ __forceinline__ Map run_map(const uint32_t *lds, int uexp)
 }
 
 // ------------------------------------------------------------- kernel 1
-// grid (tiles, buffers)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// This thread's 16 terms of a tile: with 16-byte loads where the tile is
+// whole and 16-byte aligned (thread t takes vectors t, t+256, t+512 and
+// t+768), else term by term (thread t takes terms t, t+256, ...).  f(t) is
+// called on each term; zeros stand in past the buffer's end.
+template <class F>
+__device__ __forceinline__ void for_tile_terms(const float *tile_base, int64_t count, F &&f)
+{
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(tile_base);
+    if (count >= kTile && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+        const u32x4 *v = reinterpret_cast<const u32x4 *>(src);
+        u32x4 x[kRun / 4];
+#pragma unroll
+        for (int j = 0; j < kRun / 4; ++j)
+            x[j] = __builtin_nontemporal_load(v + threadIdx.x + j * kThreads);
+#pragma unroll
+        for (int j = 0; j < kRun / 4; ++j) {
+            const uint32_t t0 = x[j].x, t1 = x[j].y, t2 = x[j].z, t3 = x[j].w;
+            f(t0);
+            f(t1);
+            f(t2);
+            f(t3);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kRun; ++j) {
+            const int i = threadIdx.x + j * kThreads;
+            f(i < count ? __builtin_nontemporal_load(src + i) : 0u);
+        }
+    }
+}
+
+// Sum and OR over the workgroup; every thread gets both.  All threads must
+// call it.
+__device__ __forceinline__ void workgroup_sum_or(float &s, uint32_t &o)
+{
+    __shared__ float ls[kThreads / 64];
+    __shared__ uint32_t lo[kThreads / 64];
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) {
+        s += __shfl_down(s, d, 64);
+        o |= __shfl_down(o, d, 64);
+    }
+    if ((threadIdx.x & 63) == 0) {
+        ls[threadIdx.x >> 6] = s;
+        lo[threadIdx.x >> 6] = o;
+    }
+    __syncthreads();
+    s = 0.0f;
+    o = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+        s += ls[w];
+        o |= lo[w];
+    }
+    __syncthreads();
+}
+
+// grid (tiles, buffers): each tile's total (binary32 adds in any order: a
+// prediction only) and whether any term is negative or not finite.
 __global__ __launch_bounds__(kThreads) void fsum_tile_totals(const float *terms, int64_t nterms, int ntiles,
                                                              double *totals, uint32_t *bad)
 {
     const int tile = blockIdx.x, buf = blockIdx.y;
     const int64_t first = static_cast<int64_t>(tile) * kTile;
-    const int64_t count = nterms - first < kTile ? nterms - first : kTile;
-    const uint32_t *src = reinterpret_cast<const uint32_t *>(terms) + static_cast<int64_t>(buf) * nterms + first;
-    double s = 0.0;
+    float s = 0.0f;
     uint32_t b = 0;
-#pragma unroll
-    for (int j = 0; j < kRun; ++j) {
-        const int i = threadIdx.x + j * kThreads;
-        if (i < count) {
-            const uint32_t t = __builtin_nontemporal_load(src + i);
-            b |= bad_term(t) ? 1u : 0u;
-            s += static_cast<double>(__uint_as_float(t & 0x7fffffffu));
-        }
-    }
-    __shared__ double lds_s[kThreads];
-    __shared__ uint32_t lds_b[kThreads];
-    lds_s[threadIdx.x] = s;
-    lds_b[threadIdx.x] = b;
-    __syncthreads();
-    for (int off = kThreads / 2; off > 0; off >>= 1) {
-        if (static_cast<int>(threadIdx.x) < off) {
-            lds_s[threadIdx.x] += lds_s[threadIdx.x + off];
-            lds_b[threadIdx.x] |= lds_b[threadIdx.x + off];
-        }
-        __syncthreads();
-    }
+    for_tile_terms(terms + static_cast<int64_t>(buf) * nterms + first, nterms - first, [&](uint32_t t) {
+        b |= bad_term(t) ? 1u : 0u;
+        s += __uint_as_float(t & 0x7fffffffu);
+    });
+    workgroup_sum_or(s, b);
     if (threadIdx.x == 0) {
-        totals[static_cast<int64_t>(buf) * ntiles + tile] = lds_s[0];
-        bad[static_cast<int64_t>(buf) * ntiles + tile] = lds_b[0];
+        totals[static_cast<int64_t>(buf) * ntiles + tile] = static_cast<double>(s);
+        bad[static_cast<int64_t>(buf) * ntiles + tile] = b;
     }
 }
 
@@ -269,12 +333,12 @@ __device__ __forceinline__ int unit_exponent_of(double v)
 // binades the float sum may be in over each tile.  plan = (unit exponent of
 // the first + 256) | (count << 16), count 0 (no maps), 1 or 2.
 __global__ __launch_bounds__(kThreads) void fsum_plan(const double *totals, const uint32_t *bad, int ntiles,
-                                                      uint32_t *plan, uint32_t *buffer_bad)
+                                                      Rec *recs, uint32_t *buffer_bad)
 {
     const int buf = blockIdx.x;
     const double *tot = totals + static_cast<int64_t>(buf) * ntiles;
     const uint32_t *bd = bad + static_cast<int64_t>(buf) * ntiles;
-    uint32_t *pl = plan + static_cast<int64_t>(buf) * ntiles;
+    Rec *rc = recs + static_cast<int64_t>(buf) * ntiles;
     const int per = (ntiles + kThreads - 1) / kThreads;
     const int lo = threadIdx.x * per, hi = lo + per < ntiles ? lo + per : ntiles;
     double mine = 0.0;
@@ -305,7 +369,7 @@ __global__ __launch_bounds__(kThreads) void fsum_plan(const double *totals, cons
         const int e_lo = unit_exponent_of(p * (1.0 - kMargin));
         const int e_hi = unit_exponent_of((p + tot[i]) * (1.0 + kMargin));
         const int n = e_hi - e_lo + 1;
-        pl[i] = static_cast<uint32_t>(e_lo + 256) | (static_cast<uint32_t>(n <= 2 ? n : 0) << 16);
+        rc[i].plan = static_cast<uint32_t>(e_lo + 256) | (static_cast<uint32_t>(n <= 2 ? n : 0) << 16);
         p += tot[i];
     }
     __syncthreads();
@@ -314,24 +378,98 @@ __global__ __launch_bounds__(kThreads) void fsum_plan(const double *totals, cons
 }
 
 // ------------------------------------------------------------- kernel 3
+// A tile's map in the binade of unit 2^uexp, from the terms as loaded, where
+// no term is a tie and none is 2^22 units or more.  Then the map is the sum
+// of h = floor(t/u + 1/2) and no tie is rounded down.  In binary32, x = t/u
+// is exact (a power-of-two scale; where it falls below the normal range it
+// is far below 1/2, and h = 0 either way), x + 1/2 is exact below 2^22, and
+// the floor is exact: so h is read off floor(x + 1/2), and the term is a tie
+// exactly where x + 1/2 is an integer.  `simple` is false where that does
+// not hold (a tie, a large term, or a unit too small to scale to); the map
+// then comes from the ordered path.
+struct FastMap {
+    uint32_t H;
+    bool simple, leaves;
+};
+
+__device__ __forceinline__ float pow2(int e) { return __uint_as_float(static_cast<uint32_t>(e + 127) << 23); }
+
 // grid (tiles, buffers): each planned tile's map in its one or two binades.
 __global__ __launch_bounds__(kThreads) void fsum_tile_maps(const float *terms, int64_t nterms, int ntiles,
-                                                           const uint32_t *plan, Map *maps)
+                                                           Rec *recs)
 {
     const int tile = blockIdx.x, buf = blockIdx.y;
     const int64_t at = static_cast<int64_t>(buf) * ntiles + tile;
-    const uint32_t pl = plan[at];
+    const uint32_t pl = recs[at].plan;
     const int n = static_cast<int>(pl >> 16);
     if (n == 0)
         return;
     const int uexp = static_cast<int>(pl & 0xffffu) - 256;
-    __shared__ uint32_t lds[kPad];
     const int64_t first = static_cast<int64_t>(tile) * kTile;
-    load_tile(terms + static_cast<int64_t>(buf) * nterms, first, nterms - first, lds);
+    const float *tb = terms + static_cast<int64_t>(buf) * nterms + first;
+    // unscaled to units of the lower binade; the upper's units are twice as large
+    const bool scalable = uexp >= -126;
+    const float scale = pow2(scalable ? -uexp : 0);
+    uint32_t H0 = 0, H1 = 0, odd = 0;  // odd: bit 0 a tie or large term (lower), bit 1 (upper)
+    for_tile_terms(tb, nterms - first, [&](uint32_t t) {
+        const float x0 = __uint_as_float(t & 0x7fffffffu) * scale;
+        const float y0 = x0 + 0.5f;
+        const float f0 = floorf(y0);
+        odd |= (f0 == y0 || !(x0 < 0x1p22f)) ? 1u : 0u;
+        H0 += static_cast<uint32_t>(f0 < 0x1p22f ? f0 : 0.0f);
+        if (n == 2) {
+            const float x1 = x0 * 0.5f;
+            const float y1 = x1 + 0.5f;
+            const float f1 = floorf(y1);
+            odd |= (f1 == y1 || !(x1 < 0x1p22f)) ? 2u : 0u;
+            H1 += static_cast<uint32_t>(f1 < 0x1p22f ? f1 : 0.0f);
+        }
+    });
+    // a thread's sum of 16 terms below 2^22 stays below 2^26; one that
+    // reaches 2^24 leaves any binade, so the rest stays below 2^32
+    uint32_t leaves = (H0 >= kTop ? 1u : 0u) | (H1 >= kTop ? 2u : 0u);
+    float dummy = 0.0f;
+    uint32_t flags = odd | (leaves << 2) | (scalable ? 0u : 3u);
+    workgroup_sum_or(dummy, flags);
+    H0 = H0 >= kTop ? 0u : H0;
+    H1 = H1 >= kTop ? 0u : H1;
+    __shared__ uint32_t lh[2][kThreads / 64];
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) {
+        H0 += __shfl_down(H0, d, 64);
+        H1 += __shfl_down(H1, d, 64);
+    }
+    if ((threadIdx.x & 63) == 0) {
+        lh[0][threadIdx.x >> 6] = H0;
+        lh[1][threadIdx.x >> 6] = H1;
+    }
+    __syncthreads();
+    __shared__ uint32_t lds[kPad];
+    bool staged = false;
     for (int k = 0; k < n; ++k) {
-        const Map m = reduce_maps(run_map(lds, uexp + k));
-        if (threadIdx.x == 0)
-            maps[2 * at + k] = m;
+        Map m;
+        if (flags & ((4u << k))) {
+            m = leaving_map();
+        } else if (!(flags & (1u << k))) {
+            uint32_t h = 0;
+#pragma unroll
+            for (int w = 0; w < kThreads / 64; ++w)
+                h += lh[k][w];
+            m = {h > kSat ? kSat : h, 0u, 0u};
+        } else {
+            // ties, large terms or a tiny unit: in order, term by term
+            if (!staged) {
+                load_tile(tb, nterms - first, lds);
+                staged = true;
+            }
+            m = reduce_maps(run_map(lds, uexp + k));
+        }
+        if (threadIdx.x == 0) {
+            if (k == 0)
+                recs[at].m0 = m;
+            else
+                recs[at].m1 = m;
+        }
     }
 }
 
@@ -344,11 +482,34 @@ __device__ __forceinline__ uint32_t apply(const Map &x, uint32_t m)
     return m + x.H - ((m & 1u) ? x.td1 : x.td0);
 }
 
-// The tile in LDS, with S (bit pattern) at its start: S after it.  All
-// threads must call it.
-__device__ uint32_t walk_tile(const uint32_t *lds, uint32_t S)
+// The tile in LDS, with S (bit pattern) at its start: S after it.  A tile
+// over which the sum may cross more than two binades (the start of a sum)
+// is added term by term by one thread; any other run by run.  All threads
+// must call it.
+__device__ uint32_t walk_tile(const uint32_t *lds, uint32_t S, bool one_by_one)
 {
     __shared__ uint32_t shared_S;
+    if (one_by_one) {
+        if (threadIdx.x == 0) {
+            float f = __uint_as_float(S);
+            for (int r = 0; r < kThreads; ++r) {
+                // a run's 16 reads issued together, then its 16 adds
+                const uint32_t *p = lds + r * (kRun + 1);
+                float v[kRun];
+#pragma unroll
+                for (int j = 0; j < kRun; ++j)
+                    v[j] = __uint_as_float(p[j]);
+#pragma unroll
+                for (int j = 0; j < kRun; ++j)
+                    f = f + v[j];
+            }
+            shared_S = __float_as_uint(f);
+        }
+        __syncthreads();
+        S = shared_S;
+        __syncthreads();
+        return S;
+    }
     int r0 = 0;  // runs before r0 are added
     while (r0 < kThreads && S != kInf) {
         int uexp;
@@ -391,14 +552,17 @@ __device__ uint32_t walk_tile(const uint32_t *lds, uint32_t S)
     return S;
 }
 
-// One workgroup per buffer.
+// One workgroup per buffer.  A window is kWindow tiles, kPerThread
+// consecutive ones per thread.
+constexpr int kPerThread = 4;
+constexpr int kWindow = kThreads * kPerThread;
+
 __global__ __launch_bounds__(kThreads) void fsum_walk(const float *terms, int64_t nterms, int ntiles,
-                                                      const uint32_t *plan, const Map *maps,
-                                                      const uint32_t *buffer_bad, float *out)
+                                                      const Rec *recs, const uint32_t *buffer_bad, float *out)
 {
     const int buf = blockIdx.x;
     __shared__ uint32_t lds[kPad];
-    __shared__ uint32_t shared_S;
+    __shared__ uint32_t shared_S, shared_how;
     const float *tb = terms + static_cast<int64_t>(buf) * nterms;
     if (ntiles == 0) {  // no terms: the accumulator's +0
         if (threadIdx.x == 0)
@@ -410,55 +574,85 @@ __global__ __launch_bounds__(kThreads) void fsum_walk(const float *terms, int64_
             out[buf] = __uint_as_float(kNaN);
         return;
     }
+    const Rec *rb = recs + static_cast<int64_t>(buf) * ntiles;
+    const int me = static_cast<int>(threadIdx.x);
     uint32_t S = 0;  // +0
     int t0 = 0;
     while (t0 < ntiles && S != kInf) {
         int uexp;
-        uint32_t m;
-        split(S, uexp, m);
-        // this thread's tile of the window, as a map in S's binade
-        const int tile = t0 + static_cast<int>(threadIdx.x);
-        Map x = identity_map();
-        if (tile < ntiles) {
-            const int64_t at = static_cast<int64_t>(buf) * ntiles + tile;
-            const uint32_t pl = plan[at];
-            const int e0 = static_cast<int>(pl & 0xffffu) - 256;
-            const int n = static_cast<int>(pl >> 16);
-            x = (uexp >= e0 && uexp < e0 + n) ? maps[2 * at + (uexp - e0)] : leaving_map();
+        uint32_t m0;
+        split(S, uexp, m0);
+        // this thread's tiles of the window, as maps in S's binade
+        Map x[kPerThread];
+        int count[kPerThread];
+        Map mine = identity_map();
+#pragma unroll
+        for (int c = 0; c < kPerThread; ++c) {
+            const int tile = t0 + me * kPerThread + c;
+            x[c] = identity_map();
+            count[c] = -1;  // past the buffer's last tile
+            if (tile < ntiles) {
+                const Rec r = rb[tile];
+                const int e0 = static_cast<int>(r.plan & 0xffffu) - 256;
+                count[c] = static_cast<int>(r.plan >> 16);
+                x[c] = (count[c] >= 1 && uexp == e0) ? r.m0 : (count[c] == 2 && uexp == e0 + 1) ? r.m1 : leaving_map();
+            }
+            mine = compose(mine, x[c]);
         }
-        const uint32_t after = apply(scan_maps(x), m);  // m after this thread's tile
-        const int me = static_cast<int>(threadIdx.x);
-        const int last = (ntiles - t0 < kThreads ? ntiles - t0 : kThreads) - 1;
-        const int stop = first_set(me <= last && after >= kTop);
-        const int end = stop == kThreads ? last + 1 : stop;  // tiles applied from the maps
-        // S before tile `end`
-        if (me == 0)
-            shared_S = S;
-        __syncthreads();
-        if (me == end - 1)
-            shared_S = join(uexp, after);
-        __syncthreads();
-        S = shared_S;
-        __syncthreads();
+        Map before;
+        (void)scan_maps(mine, before);
+        // walk this thread's tiles from m at its first one
+        uint32_t m = apply(before, m0);
+        int local = kPerThread;  // this thread's first tile that stops (none)
+        uint32_t after = 0;
+        if (m < kTop) {
+#pragma unroll
+            for (int c = 0; c < kPerThread; ++c) {
+                if (local == kPerThread && count[c] >= 0) {
+                    const uint32_t a = apply(x[c], m);
+                    if (a >= kTop) {
+                        local = c;
+                        after = a;
+                    } else {
+                        m = a;
+                    }
+                }
+            }
+        }
+        const int stop = first_set(local < kPerThread);
         if (stop == kThreads) {
-            t0 += end;
+            // no tile of the window stops: S after its last tile
+            const int last = (ntiles - t0 < kWindow ? ntiles - t0 : kWindow) - 1;
+            if (me == last / kPerThread)
+                shared_S = join(uexp, m);
+            __syncthreads();
+            S = shared_S;
+            __syncthreads();
+            t0 += last + 1;
             continue;
         }
-        // tile `stop` reaches the binade's top exactly (applied whole), or
-        // has no map for S's binade or leaves it (walked run by run)
-        if (me == stop)
-            shared_S = after == kTop ? 1u : 0u;
+        // S before the stopping tile; that tile reaches the binade's top
+        // exactly (applied whole), or has no map for S's binade or leaves
+        // it (walked run by run, or term by term where the plan found it
+        // may cross more than two binades)
+        if (me == stop) {
+            shared_S = join(uexp, m);
+            shared_how = static_cast<uint32_t>(local) | (after == kTop ? 0x100u : 0u) |
+                         (count[local] == 0 ? 0x200u : 0u);
+        }
         __syncthreads();
-        const bool top = shared_S != 0;
+        S = shared_S;
+        const uint32_t how = shared_how;
         __syncthreads();
-        if (top) {
+        const int tile = t0 + stop * kPerThread + static_cast<int>(how & 0xffu);
+        if (how & 0x100u) {
             S = join(uexp, kTop);
         } else {
-            const int64_t first = static_cast<int64_t>(t0 + stop) * kTile;
-            load_tile(tb, first, nterms - first, lds);
-            S = walk_tile(lds, S);
+            const int64_t first = static_cast<int64_t>(tile) * kTile;
+            load_tile(tb + first, nterms - first, lds);
+            S = walk_tile(lds, S, (how & 0x200u) != 0);
         }
-        t0 += stop + 1;
+        t0 = tile + 1;
     }
     if (threadIdx.x == 0)
         out[buf] = __uint_as_float(S);
@@ -474,10 +668,9 @@ FloatSumLayout float_sum_layout(int64_t nterms, int nbuffers)
     const size_t cells = static_cast<size_t>(l.ntiles) * nbuffers;
     l.totals = 0;
     l.bad = up(l.totals + cells * sizeof(double));
-    l.plan = up(l.bad + cells * sizeof(uint32_t));
-    l.buffer_bad = up(l.plan + cells * sizeof(uint32_t));
-    l.maps = up(l.buffer_bad + static_cast<size_t>(nbuffers) * sizeof(uint32_t));
-    l.bytes = up(l.maps + cells * 2 * sizeof(Map));
+    l.recs = up(l.bad + cells * sizeof(uint32_t));
+    l.buffer_bad = up(l.recs + cells * sizeof(Rec));
+    l.bytes = up(l.buffer_bad + static_cast<size_t>(nbuffers) * sizeof(uint32_t));
     return l;
 }
 
@@ -488,17 +681,16 @@ hipError_t launch_float_sums(const float *terms, int64_t nterms, int nbuffers, f
     char *ws = static_cast<char *>(workspace);
     double *totals = reinterpret_cast<double *>(ws + l.totals);
     uint32_t *bad = reinterpret_cast<uint32_t *>(ws + l.bad);
-    uint32_t *plan = reinterpret_cast<uint32_t *>(ws + l.plan);
+    Rec *recs = reinterpret_cast<Rec *>(ws + l.recs);
     uint32_t *buffer_bad = reinterpret_cast<uint32_t *>(ws + l.buffer_bad);
-    Map *maps = reinterpret_cast<Map *>(ws + l.maps);
     if (l.ntiles > 0) {
         const dim3 grid(static_cast<unsigned>(l.ntiles), static_cast<unsigned>(nbuffers));
         fsum_tile_totals<<<grid, kThreads, 0, stream>>>(terms, nterms, l.ntiles, totals, bad);
-        fsum_plan<<<dim3(static_cast<unsigned>(nbuffers)), kThreads, 0, stream>>>(totals, bad, l.ntiles, plan,
+        fsum_plan<<<dim3(static_cast<unsigned>(nbuffers)), kThreads, 0, stream>>>(totals, bad, l.ntiles, recs,
                                                                                   buffer_bad);
-        fsum_tile_maps<<<grid, kThreads, 0, stream>>>(terms, nterms, l.ntiles, plan, maps);
+        fsum_tile_maps<<<grid, kThreads, 0, stream>>>(terms, nterms, l.ntiles, recs);
     }
-    fsum_walk<<<dim3(static_cast<unsigned>(nbuffers)), kThreads, 0, stream>>>(terms, nterms, l.ntiles, plan, maps,
+    fsum_walk<<<dim3(static_cast<unsigned>(nbuffers)), kThreads, 0, stream>>>(terms, nterms, l.ntiles, recs,
                                                                                buffer_bad, out);
     return hipGetLastError();
 }

@@ -256,14 +256,18 @@ def hvs_like_terms(nblocks: int, nplanes: int = 1, seed: int = 1397) -> np.ndarr
     r, c = np.meshgrid(np.arange(8), np.arange(8), indexing="ij")
     weight = (1.0 / (1.0 + 0.25 * (r + c))).astype(np.float32).ravel()
     out = np.empty((nplanes, nblocks * 64), dtype=np.float32)
+    err = np.empty((nblocks, 64), dtype=np.float32)  # reused: fresh pages are slow to touch
     for p in range(nplanes):
         lo = rng.uniform(0.12, 0.3)
         scale = (np.exp(rng.normal(0.0, 1.0, nblocks)) * 8.0).astype(np.float32)
         mask = (scale * rng.uniform(lo, lo + 0.6, nblocks).astype(np.float32)).astype(np.float32)
-        err = (np.abs(rng.normal(0.0, 1.0, (nblocks, 64))).astype(np.float32) * scale[:, None]
-               * weight[None, :]).astype(np.float32)
-        v = np.maximum(err - mask[:, None], np.float32(0)).astype(np.float32)
-        out[p] = (v * v).ravel()
+        rng.standard_normal(dtype=np.float32, out=err)
+        np.abs(err, out=err)
+        err *= scale[:, None]
+        err *= weight[None, :]
+        err -= mask[:, None]
+        np.maximum(err, np.float32(0), out=err)
+        np.multiply(err, err, out=out[p].reshape(nblocks, 64))
     return out
 
 
