@@ -34,18 +34,24 @@ namespace {
 constexpr int kTileVecs = 2048;  // 16-byte vectors of each plane per tile, at most
 
 // ----------------------------------------------------------------- budgets
-// A lane takes at most kTileVecs / kThreads = 8 vectors and kTileVecs * V /
-// kThreads samples (64 at two bytes, 128 at one):
-//  8 bits: a lane's sum r^2 <= (8*16 + 128) * 255^2 < 2^24, wave sum < 2^30;
-// 16 bits: a lane's sum of squares <= (8*8 + 64) * (2^32 - 1) < 2^39 (exact
-//          in binary64 at every step), crossing the wave as its low 16 bits
-//          and the rest (< 2^23, wave
-//          sum < 2^29); a lane's sample sum <= 128 * 65535 < 2^23.
-static_assert((8 * 16 + 128) * 255ull * 255ull * 64ull < (1ull << 32), "8-bit wave budget");
-static_assert(((8 * 8 + 64) * 0xffffffffull >> 16) * 64ull < (1ull << 32), "16-bit wave budget");
-static_assert((8 * 8 + 64) * 65535ull * 64ull < (1ull << 32), "16-bit sample-sum budget");
-static_assert((8 * 8 + 64) * 0xffffffffull < (1ull << 53), "16-bit lane sums exact in binary64");
-static_assert(kTileVecs / kThreads == 8, "lane share");
+// A tile holds at most kTileVecs * 16 bytes of each plane (rows * cw <=
+// kTileVecs * V samples, by the tiling), and whichever path reads it --
+// whole vectors, rows at their own offsets (up to rows * slots vectors and
+// one edge sample per row for a lane: up to 72 vectors and 64 samples when
+// a row is 32 vectors wide), or sample by sample -- each of its samples is
+// added by exactly one lane.  So a lane's, and a wave's, total is at most
+// the tile's:
+//  8 bits: sums of squares <= 32768 * 255^2 < 2^31, sample sums < 2^24;
+// 16 bits: a lane's sum of squares <= 16384 * (2^32 - 1) < 2^46 (exact in
+//          binary64 at every step), crossing the wave as its low 16 bits
+//          (wave sum < 2^22) and the rest (wave sum <= 16384 * 2^16 = 2^30);
+//          sample sums <= 16384 * 65535 < 2^30.
+constexpr unsigned long long kTileSamples8 = kTileVecs * 16ull, kTileSamples16 = kTileVecs * 8ull;
+static_assert(kTileSamples8 * 255ull * 255ull < (1ull << 32), "8-bit wave budget");
+static_assert(kTileSamples8 * 255ull < (1ull << 32), "8-bit sample-sum budget");
+static_assert((kTileSamples16 * 0xffffffffull >> 16) + 64ull * 0xffffull < (1ull << 32), "16-bit wave budget");
+static_assert(kTileSamples16 * 65535ull < (1ull << 32), "16-bit sample-sum budget");
+static_assert(kTileSamples16 * 0xffffffffull < (1ull << 53), "16-bit lane sums exact in binary64");
 
 // ------------------------------------------------------- integer psnr terms
 // 8 bits: sum (r-d)^2 = sum r^2 + sum d^2 - 2 sum r*d from dot products.

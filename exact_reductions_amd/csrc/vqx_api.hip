@@ -268,6 +268,48 @@ int noalloc_scratch(hipStream_t stream, void **out)
     return VQX_OK;
 }
 
+// The host-fed form's copy stream when the caller brings none: one per
+// device, created on first use (default priority, non-blocking) and kept
+// until the process ends.  Calls on one device share it; each call orders
+// its own copies and kernels with events, so shared use only serialises
+// the copies.
+std::mutex copy_stream_mutex;
+hipStream_t copy_streams[kMaxDevices];
+
+int cached_copy_stream(hipStream_t stream, hipStream_t *out)
+{
+    int current = 0, dev = 0;
+    if (hipGetDevice(&current) != hipSuccess) {
+        (void)hipGetLastError();
+        return VQX_E_HIP;
+    }
+    dev = current;
+    if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return VQX_E_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return VQX_E_NO_DEVICE;
+    std::lock_guard<std::mutex> lock(copy_stream_mutex);
+    if (!copy_streams[dev]) {
+        if (dev != current && hipSetDevice(dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return VQX_E_HIP;
+        }
+        hipStream_t c = nullptr;
+        const hipError_t e = hipStreamCreateWithFlags(&c, hipStreamNonBlocking);
+        if (dev != current)
+            (void)hipSetDevice(current);
+        if (e != hipSuccess || !c) {
+            (void)hipGetLastError();
+            return VQX_E_HIP;
+        }
+        copy_streams[dev] = c;
+    }
+    *out = copy_streams[dev];
+    return VQX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -590,18 +632,14 @@ int vqx_plane_stats_host_ws(const void *ref_host, const void *dist_host, int w, 
     if (rc != VQX_OK)
         return rc;
     hipStream_t copy = static_cast<hipStream_t>(copy_stream);
-    bool own = false;
     if (!copy) {
-        if (hipStreamCreateWithFlags(&copy, hipStreamNonBlocking) != hipSuccess) {
-            (void)hipGetLastError();
-            return VQX_E_HIP;
-        }
-        own = true;
+        rc = cached_copy_stream(static_cast<hipStream_t>(stream), &copy);
+        if (rc != VQX_OK)
+            return rc;
     }
-    hipError_t err = vqx::run_host_stream(w, h, bpc, nframes, frames_per_upload, ref_host, dist_host, out_noise,
-                                          out_moments, workspace, static_cast<hipStream_t>(stream), copy);
-    if (own)
-        (void)hipStreamDestroy(copy);
+    const hipError_t err = vqx::run_host_stream(w, h, bpc, nframes, frames_per_upload, ref_host, dist_host,
+                                                out_noise, out_moments, workspace, static_cast<hipStream_t>(stream),
+                                                copy);
     if (err != hipSuccess) {
         (void)hipGetLastError();
         return VQX_E_HIP;

@@ -157,32 +157,6 @@ int vqx_plane_stats_batch_noalloc(const void *ref, const void *dist, int w, int 
                                   uint64_t *out_noise, uint64_t *out_moments, void *stream);
 
 /*
- * As vqx_plane_stats_batch_ws, and also stamps two caller-created
- * hipEvent_t with the start and the end of the streaming kernel (stage 1):
- * the kernel is launched with hipExtLaunchKernel, whose dispatch records the
- * events itself, so hipEventElapsedTime gives that kernel's duration and no
- * extra packet is queued.  Either event may be NULL.  Results and errors are
- * those of vqx_plane_stats_batch_ws.
- */
-int vqx_plane_stats_batch_ws_timed(const void *ref, const void *dist, int w, int h, int bpc,
-                                   int nframes, uint64_t *out_noise, uint64_t *out_moments,
-                                   void *workspace, size_t workspace_bytes, void *stream,
-                                   void *stage1_begin, void *stage1_end);
-
-/*
- * Measurement only; it computes nothing of the method.  Reads both planes
- * with exactly the grid, chunks and 16-byte loads of
- * vqx_plane_stats_batch_ws's first kernel, but without its arithmetic (an
- * XOR of every word, written nowhere), so that its duration between the
- * events its dispatch stamps (either may be NULL) is the read time of that
- * access pattern: the practical ceiling to compare that kernel with.
- * Arguments, workspace and errors are those of vqx_plane_stats_batch_ws_timed
- * without the outputs; the workspace's contents are left unspecified.
- */
-int vqx_read_probe_timed(const void *ref, const void *dist, int w, int h, int bpc, int nframes,
-                         void *workspace, size_t workspace_bytes, void *stream, void *begin, void *end);
-
-/*
  * Device scratch needed by vqx_plane_stats_batch_cpu_order_ws.  Host-only.
  * Errors: VQX_E_NULL, VQX_E_DIMS, VQX_E_BPC, VQX_E_NFRAMES.
  */
@@ -241,10 +215,12 @@ int vqx_plane_stats_host_workspace_bytes(int w, int h, int bpc, int frames_per_u
  *                        pinned host memory mapped for the device
  *   stream               where the kernels run (work queued on it before
  *                        the call comes first); copy_stream: where the
- *                        copies run, or NULL for a stream of the call's own
- *                        (created and destroyed by the call, default
- *                        priority).  One stream for both is allowed:
- *                        the results are the same, nothing overlaps.
+ *                        copies run, or NULL for the library's copy stream
+ *                        of the device (created on the first such call,
+ *                        default priority, kept until the process ends and
+ *                        shared by such calls on that device).  One stream
+ *                        for both is allowed: the results are the same,
+ *                        nothing overlaps.
  * The call returns when every frame has been reduced and every copy is
  * done: the host buffers and the outputs are the caller's again.
  * Errors: VQX_E_NULL, VQX_E_DIMS, VQX_E_BPC, VQX_E_NFRAMES (nframes or
@@ -474,6 +450,43 @@ int vqx_conclude_psnr_int_batch(const uint64_t *noise, int w, int h, int bpc, in
 int vqx_float_sum_workspace_bytes(long long nterms, int nbuffers, size_t *bytes);
 int vqx_float_running_sums_ws(const float *terms, long long nterms, int nbuffers, float *out_sums,
                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Measurement entry points, outside the method's contract.
+ *
+ * These two exist to time the streaming kernel from inside a benchmark: one
+ * runs the same computation as vqx_plane_stats_batch_ws with its first
+ * kernel's dispatch stamping two events, the other reads the same bytes with
+ * the same access pattern and computes nothing.  No application needs
+ * them; they are kept in the library (rather than in a benchmark's own
+ * code) because the kernels they launch are the library's.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * As vqx_plane_stats_batch_ws, and also stamps two caller-created
+ * hipEvent_t with the start and the end of the streaming kernel (stage 1):
+ * the kernel is launched with hipExtLaunchKernel, whose dispatch records the
+ * events itself, so hipEventElapsedTime gives that kernel's duration and no
+ * extra packet is queued.  Either event may be NULL.  Results and errors are
+ * those of vqx_plane_stats_batch_ws.
+ */
+int vqx_plane_stats_batch_ws_timed(const void *ref, const void *dist, int w, int h, int bpc,
+                                   int nframes, uint64_t *out_noise, uint64_t *out_moments,
+                                   void *workspace, size_t workspace_bytes, void *stream,
+                                   void *stage1_begin, void *stage1_end);
+
+/*
+ * Computes nothing of the method.  Reads both planes with exactly the grid,
+ * chunks and 16-byte loads of vqx_plane_stats_batch_ws's first kernel, but
+ * without its arithmetic (an
+ * XOR of every word, written nowhere), so that its duration between the
+ * events its dispatch stamps (either may be NULL) is the read time of that
+ * access pattern: the practical ceiling to compare that kernel with.
+ * Arguments, workspace and errors are those of vqx_plane_stats_batch_ws_timed
+ * without the outputs; the workspace's contents are left unspecified.
+ */
+int vqx_read_probe_timed(const void *ref, const void *dist, int w, int h, int bpc, int nframes,
+                         void *workspace, size_t workspace_bytes, void *stream, void *begin, void *end);
 
 #ifdef __cplusplus
 }

@@ -9,6 +9,8 @@ bound.  The library's own host conclusions are checked the same way.
 
 from __future__ import annotations
 
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -34,6 +36,33 @@ def upload(a: np.ndarray):
     return t.to("cuda:0")
 
 
+def _rt():
+    rt = vqx.hip_runtime()
+    rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return rt
+
+
+def hip_events(k):
+    """k hipEvent_t handles made with the HIP runtime (default flags)."""
+    evs = [ctypes.c_void_p() for _ in range(k)]
+    for e in evs:
+        assert _rt().hipEventCreate(ctypes.byref(e)) == 0
+    return evs
+
+
+def elapsed_ms(a, b):
+    ms = ctypes.c_float()
+    assert _rt().hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+    return ms.value
+
+
+def destroy_events(*evs):
+    for e in evs:
+        _rt().hipEventDestroy(e)
+
+
 def device_sums(ref, dist, bpc, entry="caching", stream=None, prefill=None):
     """Run one batch through the library; return host int64 noise [F], moments [F][4]."""
     r, d = upload(ref), upload(dist)
@@ -52,6 +81,16 @@ def device_sums(ref, dist, bpc, entry="caching", stream=None, prefill=None):
         ws = torch.full((vqx.plane_stats_workspace_bytes(w, h, bpc, f),), 0xFF, dtype=torch.uint8,
                         device="cuda:0")
         vqx.plane_stats_batch_ws(r, d, bpc, noise, moments, ws, stream=stream)
+    elif entry == "timed":
+        # the bench's entry point: stage 1's dispatch stamps two events
+        h, w = ref.shape[1:]
+        ws = torch.full((vqx.plane_stats_workspace_bytes(w, h, bpc, f),), 0xFF, dtype=torch.uint8,
+                        device="cuda:0")
+        begin, end = hip_events(2)
+        vqx.plane_stats_batch_ws_timed(r, d, bpc, noise, moments, ws, begin, end, stream=stream)
+        (stream or torch.cuda.current_stream()).synchronize()
+        assert elapsed_ms(begin, end) > 0.0
+        destroy_events(begin, end)
     else:
         raise ValueError(entry)
     if stream is not None:
@@ -104,6 +143,16 @@ def test_workload_full_size(n, entry):
         # above 46341, so every square is a multiple of 2^8): equality holds
         assert np.all(o2[:, 3] >= oracle.TWO53)
         assert all(int(moments[f, 2]) / 65536.0 == o1[f, 3] for f in range(ref.shape[0]))
+
+
+@pytest.mark.parametrize("n", [1, 5])
+def test_timed_entry_point_full_size(n):
+    """The entry point the bench times, on the 8-bit latency batch and on the
+    3840x2160 16-bit batch the throughput figure is quoted on."""
+    wl = synth.WORKLOADS[n]
+    ref, dist = workload(n)
+    noise, moments = device_sums(ref, dist, wl.bpc, entry="timed", prefill=-1)
+    check(ref, dist, wl.bpc, noise, moments)
 
 
 @pytest.mark.parametrize("entry", ["selfalloc", "workspace_ff"])
@@ -291,14 +340,7 @@ def test_read_probe_then_sums(n, frames):
     r, d = upload(ref), upload(dist)
     f, h, w = ref.shape
     ws = torch.full((vqx.plane_stats_workspace_bytes(w, h, wl.bpc, f),), 0xFF, dtype=torch.uint8, device="cuda:0")
-    rt = vqx.hip_runtime()
-    import ctypes
-    rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-    rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-    rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
-    evs = [ctypes.c_void_p(), ctypes.c_void_p()]
-    for e in evs:
-        assert rt.hipEventCreate(ctypes.byref(e)) == 0
+    evs = hip_events(2)
     st = torch.cuda.current_stream().cuda_stream
     L = vqx.lib()
     assert L.vqx_read_probe_timed(r.data_ptr(), d.data_ptr(), w, h, wl.bpc, f, ws.data_ptr(), ws.numel(), st,
@@ -307,10 +349,8 @@ def test_read_probe_then_sums(n, frames):
     moments = torch.empty((f, 4), dtype=torch.int64, device="cuda:0")
     vqx.plane_stats_batch_ws(r, d, wl.bpc, noise, moments, ws)
     torch.cuda.synchronize()
-    ms = ctypes.c_float()
-    assert rt.hipEventElapsedTime(ctypes.byref(ms), evs[0], evs[1]) == 0 and ms.value > 0
-    for e in evs:
-        rt.hipEventDestroy(e)
+    assert elapsed_ms(evs[0], evs[1]) > 0
+    destroy_events(*evs)
     n_np, m_np = noise.cpu().numpy(), moments.cpu().numpy()
     for k in range(f):
         want = oracle.exact_frame_sums(ref[k], dist[k])

@@ -150,6 +150,27 @@ def test_ref_and_dist_offsets_apart_one_pitch(bpc, pitch, xr, xd):
                 f"pitch {pitch} ref at {xr}, dist at {xd}")
 
 
+@pytest.mark.parametrize("bpc,w", [(16, 256), (8, 512)])
+@pytest.mark.parametrize("ref_max", [True, False])
+def test_row_path_budget_at_max_values(bpc, w, ref_max):
+    """Rows of 32 vectors (the narrowest the row-by-row path takes) give 64
+    rows per tile, so a lane adds up to 64 whole vectors and 64 edge samples.
+    Every sample of one plane is the largest value and the other plane is
+    zero: each square sum of the tile is at its budget.  ref and dist start
+    at different offsets within 16 bytes (and at 8 bits the pitch, 522
+    bytes, moves every row to another offset), so every tile is read row by
+    row; 197 rows make three whole tiles and a ragged one."""
+    f, h = 2, 197
+    pitch = w + 7 + (1 if bpc == 16 else 3)
+    top = (1 << bpc) - 1
+    big_r = np.full((f, h, pitch), top if ref_max else 0, dtype=_dtype(bpc))
+    big_d = np.full((f, h, pitch), 0 if ref_max else top, dtype=_dtype(bpc))
+    sr = (slice(None), slice(None), slice(1, 1 + w))
+    sd = (slice(None), slice(None), slice(6, 6 + w))
+    check_views(big_r[sr], big_d[sd], torch.from_numpy(big_r).cuda()[sr], torch.from_numpy(big_d).cuda()[sd], bpc,
+                f"w {w} bpc {bpc}")
+
+
 @pytest.mark.parametrize("bpc,w", [(16, 40000), (8, 70000), (16, 16384), (16, 16385)])
 def test_rows_longer_than_a_tile(bpc, w):
     rng = np.random.default_rng(w)
