@@ -31,9 +31,10 @@
 //  1. stage 1 (plane_stats.hip) gives each chunk's exact totals;
 //  2. cpu_order_prefix scans them per frame (the exact running sum at each
 //     chunk start, which predicts the binade the CPU's sum is in there),
-//     writes every sum the CPU gets exactly (all of them below 2^53), maps
-//     the chunks past 2^53 inside which nothing can round, and queues the
-//     other chunks past 2^53;
+//     writes every sum in which no add of the CPU's can round (those below
+//     2^53, and those whose terms share enough trailing zero bits to stay
+//     exact past it), maps the chunks past 2^53 inside which nothing can
+//     round, and queues the other chunks past 2^53;
 //  3. cpu_order_maps computes, for every slab of 256 vectors of a queued
 //     chunk, its exact total and maps in the predicted binade (and the
 //     next one where the chunk may cross into it).  Most slabs need no
@@ -452,11 +453,17 @@ __device__ __forceinline__ uint32_t *queue_counts(uint64_t *rec) { return reinte
 //    record also holds the frame's few samples outside whole vectors)
 //    predicts the CPU's sum there; totals[f*3 + kk] = the frame's exact sum.
 //  * It writes the frame's five exact sums (so the CPU-order form needs no
-//    stage 2), and the CPU's values of the sums that stay below 2^53, which
-//    are the exact sums; the first moments always do (below 2^25 * 2^16 =
-//    2^41).
-//  * With `maps` (two-byte samples), each chunk whose exact range ends past
-//    2^53 gets its case: a chunk that starts past 2^53, is not predicted to
+//    stage 2), and the CPU's values of the sums in which no add can round,
+//    which are the exact sums: those that stay below 2^53 (the first
+//    moments always do: below 2^25 * 2^16 = 2^41), and those whose terms are
+//    all multiples of 2^j (the OR of the frame's low bits, j <= 4) and that
+//    stay below 2^(53+j) -- every partial sum is then a multiple of 2^j
+//    below 2^(53+j), which a double holds exactly (bright 16-bit content:
+//    every float square of a sample above 46340 is a multiple of 2^8).
+//    totals[f*3 + kk] is the frame's exact sum where the walk has to find
+//    the CPU's value, else 0.
+//  * With `maps` (two-byte samples), each chunk of such a sum whose exact
+//    range ends past 2^53 gets its case: a chunk that starts past 2^53, is not predicted to
 //    change binade and whose terms are all multiples of 2^k (stage 1's low
 //    bits; k <= 4 since sums stay below 2^57) gets its map from its total
 //    alone, since nothing inside it rounds; every other such chunk gets
@@ -544,8 +551,12 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int6
     // record for the passes below (each thread uses only its own chunks)
     __shared__ uint64_t sq[kSquares][kMaxFrameChunks];
     __shared__ uint16_t low_bits[kMaxFrameChunks];
+    __shared__ uint32_t frame_low;  // the OR of the frame's low bits
     const int64_t f = blockIdx.x;
     const int t = threadIdx.x;
+    if (t == 0)
+        frame_low = 0;
+    __syncthreads();
     const int per = (chunks + kThreads - 1) / kThreads;
     const int c0 = t * per < chunks ? t * per : chunks;
     const int c1 = c0 + per < chunks ? c0 + per : chunks;
@@ -556,6 +567,7 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int6
 #pragma unroll
     for (int j = 0; j < kSums; ++j)
         local[j] = 0;
+    uint32_t low_or = 0;
     for (int c = c0; c < c1; ++c) {
         uint64_t x[kSums + 1];
 #pragma unroll
@@ -568,8 +580,20 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int6
         for (int kk = 0; kk < kSquares; ++kk)
             sq[kk][c] = x[record_field(kk)];
         low_bits[c] = static_cast<uint16_t>(x[kSums]);
+        low_or |= static_cast<uint32_t>(x[kSums]);
     }
+    if (maps && low_or)
+        atomicOr(&frame_low, low_or);  // complete after the scan's barrier
     wave_inclusive_then_total_n<kSums>(local, lds, run, total);
+    // the square sums whose every add is exact (one-byte samples: all)
+    bool exact[kSquares];
+#pragma unroll
+    for (int kk = 0; kk < kSquares; ++kk) {
+        const uint32_t nib = (frame_low >> (4 * kk)) & 15u;
+        const int j = nib ? __builtin_ctz(nib) : 4;
+        const uint64_t T = total[record_field(kk)];
+        exact[kk] = !maps || T < kTwo53 || T < (kTwo53 << j);
+    }
 #pragma unroll
     for (int j = 0; j < kSums; ++j)
         run[j] -= local[j];
@@ -583,25 +607,30 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int6
         out_moments[4 * f + 3] = total[kDist2];
 #pragma unroll
         for (int kk = 0; kk < kSquares; ++kk)
-            totals[f * kSquares + kk] = total[record_field(kk)];
+            totals[f * kSquares + kk] = exact[kk] ? 0 : total[record_field(kk)];
         // otherwise the walk writes it
-        if (total[kNoise] < kTwo53)
+        if (exact[kSqNoise])
             out_cpu_noise[f] = total[kNoise];
         out_cpu_moments[4 * f + 0] = total[kRef1];
         out_cpu_moments[4 * f + 1] = total[kDist1];
-        if (total[kRef2] < kTwo53)
+        if (exact[kSqRef])
             out_cpu_moments[4 * f + 2] = total[kRef2];
-        if (total[kDist2] < kTwo53)
+        if (exact[kSqDist])
             out_cpu_moments[4 * f + 3] = total[kDist2];
     }
     const int64_t e0 = f * pixels;
     const int64_t nvec = (e0 + pixels) / V - (e0 + V - 1) / V;  // the frame's whole vectors
     if (!maps)  // one-byte samples: every sum stays below 2^53
         return;
+    // the walk takes no sum of this frame: no chunk to map or queue
+    if (exact[kSqNoise] && exact[kSqRef] && exact[kSqDist])
+        return;
     // pass 1: chunk maps, and how many chunks the thread queues
     uint64_t nq = 0;  // 21 bits per square sum
 #pragma unroll
     for (int kk = 0; kk < kSquares; ++kk) {
+        if (exact[kk])
+            continue;
         const int field = record_field(kk);
         uint64_t p = run[field];
         for (int c = c0; c < c1; ++c) {
@@ -637,6 +666,8 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int6
     const int64_t cap = static_cast<int64_t>(gridDim.x) * chunks;
 #pragma unroll
     for (int kk = 0; kk < kSquares; ++kk) {
+        if (exact[kk])
+            continue;
         const int field = record_field(kk);
         uint64_t p = run[field];
         int64_t slot = base[kk] + ((at >> (21 * kk)) & 0x1fffffu);
@@ -1331,8 +1362,8 @@ __device__ __forceinline__ void walk_frame(const void *ref, const void *dist, in
         *dst = S;
 }
 
-// One workgroup per (frame, square sum); two-byte samples only.  Sums that
-// stay below 2^53 were written by the prefix scan.  The workgroup's waves
+// One workgroup per (frame, square sum); two-byte samples only.  Sums in
+// which no add rounds were written by the prefix scan.  The workgroup's waves
 // first compose the frame's blocks (block b in wave b % kWalkWaves); after
 // the barrier that makes their records visible, wave 0 walks the frame.
 constexpr int kWalkWaves = 8;
@@ -1362,7 +1393,7 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cpu_order_walk(const void *re
     __shared__ u32x4 lds[2 * kSlabVectors];  // a slab of each plane, for `consecutive`
     const int64_t frame = blockIdx.x / kSquares;
     const int kk = static_cast<int>(blockIdx.x - frame * kSquares);
-    if (totals[frame * kSquares + kk] < kTwo53)
+    if (totals[frame * kSquares + kk] < kTwo53)  // the prefix wrote the CPU's value
         return;
     switch (kk) {
     case kSqNoise:

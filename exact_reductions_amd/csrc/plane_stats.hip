@@ -129,11 +129,14 @@ __device__ __forceinline__ bool wave_all_small(const u32x4 (&a)[kInFlight], cons
     return __all((any & 0xF000F000u) == 0);
 }
 
-// The bright form of one group (every sample at least 49152).
-__device__ __forceinline__ void add_group_bright(Acc16U64 &acc, const u32x4 (&a)[kInFlight],
-                                                 const u32x4 (&b)[kInFlight])
+// The bright form of one group (every sample at least 49152).  With the
+// low bits (Acc16Low) it also ORs the noise terms; the moment terms need
+// nothing: a float square in [2^31, 2^32) is a multiple of 2^8.
+template <class Acc>
+__device__ __forceinline__ void add_group_bright(Acc &acc, const u32x4 (&a)[kInFlight], const u32x4 (&b)[kInFlight])
 {
-    uint32_t noise_even = 0, noise_odd = 0, bits_r = 0, bits_d = 0;
+    constexpr bool kLow = std::is_same<Acc, Acc16Low>::value;
+    uint32_t noise_even = 0, noise_odd = 0, bits_r = 0, bits_d = 0, noise_or = 0;
     const u16x2 ones = {1, 1};
 #pragma unroll
     for (int u = 0; u < kInFlight; ++u)
@@ -148,8 +151,11 @@ __device__ __forceinline__ void add_group_bright(Acc16U64 &acc, const u32x4 (&a)
             float d0 = static_cast<float>(d & 0xffffu), d1 = static_cast<float>(d >> 16);
             asm volatile("" : "+v"(r0), "+v"(r1), "+v"(d0), "+v"(d1));  // one conversion each
             const float e0 = r0 - d0, e1 = r1 - d1;
-            noise_even += float_square(e0);
-            noise_odd += float_square(e1);
+            const uint32_t n0 = float_square(e0), n1 = float_square(e1);
+            noise_even += n0;
+            noise_odd += n1;
+            if constexpr (kLow)
+                noise_or |= n0 | n1;
             bits_r += __float_as_uint(r0 * r0);
             bits_r += __float_as_uint(r1 * r1);
             bits_d += __float_as_uint(d0 * d0);
@@ -161,6 +167,8 @@ __device__ __forceinline__ void add_group_bright(Acc16U64 &acc, const u32x4 (&a)
     acc.noise += static_cast<uint64_t>(noise_even) + noise_odd;
     acc.r2 += (static_cast<uint64_t>(n) << 31) + (static_cast<uint64_t>(bits_r - n * 0x4F000000u) << 8);
     acc.d2 += (static_cast<uint64_t>(n) << 31) + (static_cast<uint64_t>(bits_d - n * 0x4F000000u) << 8);
+    if constexpr (kLow)
+        acc.or_noise |= noise_or;
 }
 
 // The small form of one group (every sample below 4096).
@@ -192,8 +200,10 @@ template <int kBytes, class Acc, int kForm = kGeneralOnly>
 __device__ __forceinline__ void accumulate_chunk(Acc &acc, const void *ref, const void *dist,
                                                  int64_t pixels, int chunk, int64_t frame)
 {
-    static_assert(kForm == kGeneralOnly || (kBytes == 2 && std::is_same<Acc, Acc16U64>::value),
-                  "group forms add into the 16-bit uint64 lanes");
+    static_assert(kForm == kGeneralOnly ||
+                      (kBytes == 2 && (std::is_same<Acc, Acc16U64>::value ||
+                                       (kForm == kBright && std::is_same<Acc, Acc16Low>::value))),
+                  "group forms add into the 16-bit uint64 lanes (the bright one also with low bits)");
     constexpr int V = 16 / kBytes;  // samples per vector
     const int64_t e0 = frame * pixels;  // first sample of the frame
     const int64_t e1 = e0 + pixels;
@@ -277,12 +287,13 @@ __global__ __launch_bounds__(kThreads) void stage1_u8(const void *ref, const voi
 // kLowBitsOut: also the OR of the low bits of each square sum's terms, in
 // the record's slot kLowBits, and zero queue lengths in record 0 (for the
 // CPU-order form).
-// kForm: the cheaper group form tried (kGeneralOnly with kLowBitsOut).
+// kForm: the cheaper group form tried (with kLowBitsOut, the bright one or
+// none).
 template <bool kLowBitsOut, int kForm>
 __global__ __launch_bounds__(kThreads) void stage1_u16(const void *ref, const void *dist,
                                                        int64_t pixels, int chunks, uint64_t *part)
 {
-    static_assert(!kLowBitsOut || kForm == kGeneralOnly, "the low bits come from the general form");
+    static_assert(!kLowBitsOut || kForm != kSmall, "the small form keeps no squares to OR");
     const int64_t wg = blockIdx.x;
     const int64_t frame = wg / chunks;
     const int chunk = static_cast<int>(wg - frame * chunks);
@@ -374,7 +385,8 @@ hipError_t launch_plane_stats(const Geometry &g, const void *ref, const void *di
     // the cheaper group form that the depth makes likely: small samples up to
     // 12 bits, bright ones above
     const void *fn = g.sample_bytes == 1 ? reinterpret_cast<const void *>(&stage1_u8)
-                     : low_bits          ? reinterpret_cast<const void *>(&stage1_u16<true, kGeneralOnly>)
+                     : low_bits && g.bpc <= 12 ? reinterpret_cast<const void *>(&stage1_u16<true, kGeneralOnly>)
+                     : low_bits          ? reinterpret_cast<const void *>(&stage1_u16<true, kBright>)
                      : g.bpc <= 12       ? reinterpret_cast<const void *>(&stage1_u16<false, kSmall>)
                                          : reinterpret_cast<const void *>(&stage1_u16<false, kBright>);
     void *args[] = {const_cast<void **>(&ref), const_cast<void **>(&dist), &pixels, &chunks, &partials};

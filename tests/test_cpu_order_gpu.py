@@ -96,6 +96,46 @@ def test_odd_dark_samples_past54():
     check(ref, dist, 16, expect_past53=True)
 
 
+def _mid_bright(w, h, seed):
+    """A tenth of the samples in 4096..5792 (float squares in [2^24, 2^25):
+    multiples of 4 -- an odd square ties at 25 bits and goes to the even
+    significand -- some 4 mod 8), the rest in 49152..65535 (float squares
+    multiples of 2^8); both planes drawn alike."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for _ in range(2):
+        low = rng.random(size=(1, h, w)) < 0.1
+        mid = rng.integers(4096, 5792, size=(1, h, w), endpoint=True, dtype=np.uint16)
+        bright = rng.integers(49152, 65535, size=(1, h, w), endpoint=True, dtype=np.uint16)
+        out.append(np.where(low, mid, bright).astype(np.uint16))
+    return out[0], out[1]
+
+
+@pytest.mark.parametrize("w,h,walked", [(2560, 1440, False), (3840, 2160, False), (8192, 4096, True)])
+def test_shared_trailing_zeros_past53(w, h, walked):
+    """Terms that all are multiples of 2^j keep every partial sum a multiple
+    of 2^j, which a double holds exactly below 2^(53+j): there the CPU's sum
+    is the exact one, past 2^53 or not.  Here j = 2 for the squares of ref
+    and dist.  At 2560x1440 they end between 2^53 and 2^54, at 3840x2160
+    between 2^54 and 2^55 (no add rounds); in the largest frame, 2^25
+    samples, past 2^55, where the terms that are 4 mod 8 tie and the CPU's
+    sum rounds."""
+    ref, dist = _mid_bright(w, h, seed=w + h)
+    for plane in (ref, dist):
+        sq = plane.astype(np.float32) * plane.astype(np.float32)  # binary32 squares, as the CPU's
+        terms = sq.astype(np.uint64)
+        low = int(np.bitwise_or.reduce(terms.ravel() & np.uint64(15)))
+        assert (low & -low) == 4  # j = 2
+        total = int(terms.sum(dtype=np.uint64))
+        assert oracle.TWO53 <= total and (total >= 4 * oracle.TWO53) == walked
+    o1 = oracle.seq_batch_sums(ref, dist, 16)
+    o2 = oracle.exact_batch_sums(ref, dist)
+    for k in (3, 4):
+        cpu = float(o1[0][k]) * float(256 ** UNIT_POWER[k])  # in the integer units of the exact sum
+        assert (int(cpu) != int(o2[0][k])) == walked  # the CPU rounds past 2^(53+j) only
+    check(ref, dist, 16, expect_past53=True)
+
+
 def test_container_values_above_bpc():
     """A 10-bit container holding full-range values passes 2^53 too."""
     ref, dist = synth.uniform_planes(3840, 2160, 1, 10, seed=11, container_max=True)
