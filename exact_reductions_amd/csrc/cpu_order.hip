@@ -29,19 +29,19 @@
 // on the parity before it.  Such maps compose in order.
 //
 //  1. stage 1 (plane_stats.hip) gives each chunk's exact totals;
-//  2. cpu_order_prefix scans them per frame (the exact running sum at each
-//     chunk start, which predicts the binade the CPU's sum is in there),
-//     writes every sum in which no add of the CPU's can round (those below
+//  2. a prefix scan per frame (the exact running sum at each chunk start,
+//     which predicts the binade the CPU's sum is in there) writes every sum in which no add of the CPU's can round (those below
 //     2^53, and those whose terms share enough trailing zero bits to stay
 //     exact past it), maps the chunks past 2^53 inside which nothing can
 //     round, and queues the other chunks past 2^53;
-//  3. cpu_order_maps computes, for every slab of 256 vectors of a queued
-//     chunk, its exact total and maps in the predicted binade (and the
-//     next one where the chunk may cross into it).  Most slabs need no
+//  3. in the same launch (cpu_order_maps: a group of workgroups per frame,
+//     each running the frame's scan for itself), every slab of 256 vectors
+//     of a queued chunk gets its exact total and maps in the predicted
+//     binade (and the next one where the chunk may cross into it).  Most slabs need no
 //     ordered work: if every term is a multiple of the binade's unit nothing
 //     rounds, and without ties the map follows from two plain sums; only
 //     slabs with ties chain their terms and compose the lanes' maps in
-//     order.  A fixed grid of waves shares out the queued slabs, each wave
+//     order.  The frame's waves share out its queued slabs, each wave
 //     reading its next slab while mapping the current one;
 //  4. cpu_order_walk, one workgroup per frame and sum past 2^53: its waves
 //     first write a compact record per chunk (its map, its own or composed
@@ -441,14 +441,13 @@ constexpr uint64_t kChunkOnly = 1ull << 20;
 constexpr uint64_t kQueued = 1ull << 21;
 
 // Queues of chunks to map, one per square sum, each of capacity
-// nframes * chunks: an item is (frame * chunks + chunk) | e << 32 |
+// nframes * chunks, frame f's items in its own segment [f * chunks,
+// (f + 1) * chunks): an item is (frame * chunks + chunk) | e << 32 |
 // dual << 40, e the binade predicted at the chunk's start, dual set where
-// the chunk's exact range reaches 2^(e+1).  Their lengths sit in record 0
-// (kQueueCounts).
-__device__ __forceinline__ uint32_t *queue_counts(uint64_t *rec) { return reinterpret_cast<uint32_t *>(rec + kQueueCounts); }
+// the chunk's exact range reaches 2^(e+1).
 
 // ------------------------------------------------------------ 2. prefix scan
-// One workgroup per frame; thread t takes chunks [t * per, (t + 1) * per).
+// One workgroup scans a frame; thread t takes chunks [t * per, (t + 1) * per).
 //  * The exact sum of each square over the chunks before chunk c (chunk 0's
 //    record also holds the frame's few samples outside whole vectors)
 //    predicts the CPU's sum there; totals[f*3 + kk] = the frame's exact sum.
@@ -463,11 +462,11 @@ __device__ __forceinline__ uint32_t *queue_counts(uint64_t *rec) { return reinte
 //    totals[f*3 + kk] is the frame's exact sum where the walk has to find
 //    the CPU's value, else 0.
 //  * With `maps` (two-byte samples), each chunk of such a sum whose exact
-//    range ends past 2^53 gets its case: a chunk that starts past 2^53, is not predicted to
-//    change binade and whose terms are all multiples of 2^k (stage 1's low
-//    bits; k <= 4 since sums stay below 2^57) gets its map from its total
-//    alone, since nothing inside it rounds; every other such chunk gets
-//    chunk flags 0 and goes on its sum's queue for the maps kernel.
+//    range ends past 2^53 gets its case: a chunk that starts past 2^53, is
+//    not predicted to change binade and whose terms are all multiples of
+//    2^k (stage 1's low bits; k <= 4 since sums stay below 2^57) gets its
+//    map from its total alone, since nothing inside it rounds; every other
+//    such chunk goes on its sum's queue to have its slabs mapped.
 __device__ __forceinline__ uint64_t wave_inclusive_then_total(uint64_t v, uint64_t *lds_totals, uint64_t &total)
 {
     // inclusive scan inside the wave, then the totals of the waves below
@@ -538,24 +537,29 @@ __device__ __forceinline__ ChunkCase chunk_case(uint64_t p, uint64_t r, uint32_t
 // whole vectors, 2048 chunks.
 constexpr int kMaxFrameChunks = 2048;
 
-__global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int64_t pixels, int chunks,
-                                                             uint64_t *totals, uint64_t *out_noise,
-                                                             uint64_t *out_moments, uint64_t *out_cpu_noise,
-                                                             uint64_t *out_cpu_moments, uint64_t *maps,
-                                                             uint64_t *queue)
+// The LDS of frame_prefix.
+struct PrefixLds {
+    uint64_t scan[kSums + 1][kThreads / 64];
+    uint32_t nq[kSquares];  // the frame's queue length, per square sum
+    uint32_t frame_low;     // the OR of the frame's low bits
+};
+
+// The prefix scan of frame f, by one workgroup (all threads call it).  Each
+// workgroup that maps the frame's slabs runs it for itself (a frame's
+// records are a few tens of KB, read from L2 after the first); `writer`
+// (one workgroup per frame) also writes the sums, the totals and the chunk
+// maps.  Every such workgroup writes the frame's queue items (the same
+// values), into the frame's own segment of each queue (capacity `chunks`,
+// in chunk order), and leaves their numbers in L.nq.
+__device__ __forceinline__ void frame_prefix(PrefixLds &L, int64_t f, int nframes, const uint64_t *rec,
+                                             int64_t pixels, int chunks, bool writer, uint64_t *totals,
+                                             uint64_t *out_noise, uint64_t *out_moments, uint64_t *out_cpu_noise,
+                                             uint64_t *out_cpu_moments, uint64_t *maps, uint64_t *queue)
 {
     constexpr int V = 8;
-    __shared__ uint64_t lds[kSums + 1][kThreads / 64];
-    __shared__ uint32_t base[kSquares];
-    // each chunk's square sums and low bits, kept from the one read of its
-    // record for the passes below (each thread uses only its own chunks)
-    __shared__ uint64_t sq[kSquares][kMaxFrameChunks];
-    __shared__ uint16_t low_bits[kMaxFrameChunks];
-    __shared__ uint32_t frame_low;  // the OR of the frame's low bits
-    const int64_t f = blockIdx.x;
     const int t = threadIdx.x;
     if (t == 0)
-        frame_low = 0;
+        L.frame_low = 0;
     __syncthreads();
     const int per = (chunks + kThreads - 1) / kThreads;
     const int c0 = t * per < chunks ? t * per : chunks;
@@ -569,27 +573,19 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int6
         local[j] = 0;
     uint32_t low_or = 0;
     for (int c = c0; c < c1; ++c) {
-        uint64_t x[kSums + 1];
-#pragma unroll
-        for (int j = 0; j <= kSums; ++j)
-            x[j] = frec[c * kRecordStride + j];  // slot kSums is kLowBits
 #pragma unroll
         for (int j = 0; j < kSums; ++j)
-            local[j] += x[j];
-#pragma unroll
-        for (int kk = 0; kk < kSquares; ++kk)
-            sq[kk][c] = x[record_field(kk)];
-        low_bits[c] = static_cast<uint16_t>(x[kSums]);
-        low_or |= static_cast<uint32_t>(x[kSums]);
+            local[j] += frec[c * kRecordStride + j];
+        low_or |= static_cast<uint32_t>(frec[c * kRecordStride + kLowBits]);
     }
     if (maps && low_or)
-        atomicOr(&frame_low, low_or);  // complete after the scan's barrier
-    wave_inclusive_then_total_n<kSums>(local, lds, run, total);
+        atomicOr(&L.frame_low, low_or);  // complete after the scan's barrier
+    wave_inclusive_then_total_n<kSums>(local, L.scan, run, total);
     // the square sums whose every add is exact (one-byte samples: all)
     bool exact[kSquares];
 #pragma unroll
     for (int kk = 0; kk < kSquares; ++kk) {
-        const uint32_t nib = (frame_low >> (4 * kk)) & 15u;
+        const uint32_t nib = (L.frame_low >> (4 * kk)) & 15u;
         const int j = nib ? __builtin_ctz(nib) : 4;
         const uint64_t T = total[record_field(kk)];
         exact[kk] = !maps || T < kTwo53 || T < (kTwo53 << j);
@@ -597,7 +593,7 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int6
 #pragma unroll
     for (int j = 0; j < kSums; ++j)
         run[j] -= local[j];
-    if (t == 0) {
+    if (writer && t == 0) {
         // the exact sums (stage 2's results), then the CPU's where they are
         // the exact ones
         out_noise[f] = total[kNoise];
@@ -618,13 +614,16 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int6
         if (exact[kSqDist])
             out_cpu_moments[4 * f + 3] = total[kDist2];
     }
+    if (t < kSquares)
+        L.nq[t] = 0;
     const int64_t e0 = f * pixels;
     const int64_t nvec = (e0 + pixels) / V - (e0 + V - 1) / V;  // the frame's whole vectors
-    if (!maps)  // one-byte samples: every sum stays below 2^53
+    // one-byte samples (every sum stays below 2^53), or no sum of the frame
+    // that the walk takes: no chunk to map or queue
+    if (!maps || (exact[kSqNoise] && exact[kSqRef] && exact[kSqDist])) {
+        __syncthreads();
         return;
-    // the walk takes no sum of this frame: no chunk to map or queue
-    if (exact[kSqNoise] && exact[kSqRef] && exact[kSqDist])
-        return;
+    }
     // pass 1: chunk maps, and how many chunks the thread queues
     uint64_t nq = 0;  // 21 bits per square sum
 #pragma unroll
@@ -634,46 +633,42 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int6
         const int field = record_field(kk);
         uint64_t p = run[field];
         for (int c = c0; c < c1; ++c) {
-            const uint64_t T = sq[kk][c];
-            const uint32_t low = (static_cast<uint32_t>(low_bits[c]) >> (4 * kk)) & 15u;
+            const uint64_t T = frec[c * kRecordStride + field];
+            const uint32_t low = (static_cast<uint32_t>(frec[c * kRecordStride + kLowBits]) >> (4 * kk)) & 15u;
             const ChunkCase x = chunk_case(p, T, low, static_cast<int64_t>(c) * kChunkVectors < nvec);
             uint64_t *entry = maps + ((f * chunks + c) * kSquares + kk) * kEntry;
             if (x.chunk_only) {
-                const Map2 m = untied_map(T >> (x.e - 52));
-                entry[kChunkMap + 0] = m.dm0;
-                entry[kChunkMap + 1] = m.dm1;
-                entry[kChunkMap + 2] = map_flags(m, x.e) | kChunkOnly;
+                if (writer) {
+                    const Map2 m = untied_map(T >> (x.e - 52));
+                    entry[kChunkMap + 0] = m.dm0;
+                    entry[kChunkMap + 1] = m.dm1;
+                    entry[kChunkMap + 2] = map_flags(m, x.e) | kChunkOnly;
+                }
             } else {
-                entry[kChunkMap + 2] = x.queued ? kQueued : 0;
+                if (writer)
+                    entry[kChunkMap + 2] = x.queued ? kQueued : 0;
                 nq += x.queued ? 1ull << (21 * kk) : 0;
             }
             p += T;
         }
     }
-    // each queue's part for this frame, reserved in one add per sum
+    // each thread's first slot in the frame's segments, and their lengths
     uint64_t nq_total;
-    uint64_t at = wave_inclusive_then_total(nq, lds[kSums], nq_total) - nq;
-    if (t == 0) {
-        uint32_t *counts = queue_counts(rec);
-#pragma unroll
-        for (int kk = 0; kk < kSquares; ++kk) {
-            const uint32_t n = static_cast<uint32_t>(nq_total >> (21 * kk)) & 0x1fffffu;
-            base[kk] = n ? atomicAdd(&counts[kk], n) : 0u;
-        }
-    }
-    __syncthreads();
+    const uint64_t at = wave_inclusive_then_total(nq, L.scan[kSums], nq_total) - nq;
+    if (t < kSquares)
+        L.nq[t] = static_cast<uint32_t>(nq_total >> (21 * t)) & 0x1fffffu;
     // pass 2: the queue items, in chunk order within the frame
-    const int64_t cap = static_cast<int64_t>(gridDim.x) * chunks;
+    const int64_t cap = static_cast<int64_t>(nframes) * chunks;
 #pragma unroll
     for (int kk = 0; kk < kSquares; ++kk) {
         if (exact[kk])
             continue;
         const int field = record_field(kk);
         uint64_t p = run[field];
-        int64_t slot = base[kk] + ((at >> (21 * kk)) & 0x1fffffu);
+        int64_t slot = f * chunks + ((at >> (21 * kk)) & 0x1fffffu);
         for (int c = c0; c < c1; ++c) {
-            const uint64_t T = sq[kk][c];
-            const uint32_t low = (static_cast<uint32_t>(low_bits[c]) >> (4 * kk)) & 15u;
+            const uint64_t T = frec[c * kRecordStride + field];
+            const uint32_t low = (static_cast<uint32_t>(frec[c * kRecordStride + kLowBits]) >> (4 * kk)) & 15u;
             const ChunkCase x = chunk_case(p, T, low, static_cast<int64_t>(c) * kChunkVectors < nvec);
             if (x.queued)
                 queue[kk * cap + slot++] = static_cast<uint64_t>(f * chunks + c) |
@@ -682,6 +677,7 @@ __global__ __launch_bounds__(kThreads) void cpu_order_prefix(uint64_t *rec, int6
             p += T;
         }
     }
+    __syncthreads();  // the segments and their lengths, for the workgroup
 }
 
 // The planes' vectors of one slab.  As loaded, lane l holds vectors l,
@@ -927,20 +923,31 @@ __device__ __forceinline__ void queue_maps(const Slabs &Q, int64_t i, int64_t st
     }
 }
 
-// A fixed grid of waves shares out the slabs of the three queues: wave w
-// takes slab items w, w + W, w + 2W, ... of each queue in turn (W waves in
-// all).  Two-byte samples only.  Three waves per SIMD fit its registers
-// without spills (168 VGPRs), one more than the compiler picks unasked.
+// Steps 2 and 3 in one launch: `per_frame` workgroups per frame (grid
+// nframes * per_frame), each with the frame's prefix scan (frame_prefix),
+// then its share of the frame's queued slabs: wave w of the frame's
+// W = 4 * per_frame takes slab items w, w + W, ... of each of the frame's
+// queues in turn.  Workgroup 0 of each frame writes the prefix's results.
+// Two-byte samples map slabs; one-byte ones only scan (per_frame 1).
+// Three waves per SIMD fit its registers without spills (168 VGPRs), one
+// more than the compiler picks unasked.
 template <bool kSh>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void cpu_order_maps(const void *ref, const void *dist, int64_t pixels,
-                                                           int chunks, int nframes, const uint64_t *rec,
-                                                           const uint64_t *queue, uint64_t *maps, VecMap vmap)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void cpu_order_maps(
+    const void *ref, const void *dist, int64_t pixels, int chunks, int nframes, int per_frame, const uint64_t *rec,
+    uint64_t *totals, uint64_t *out_noise, uint64_t *out_moments, uint64_t *out_cpu_noise, uint64_t *out_cpu_moments,
+    uint64_t *queue, uint64_t *maps, VecMap vmap)
 {
-    const int64_t w = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + threadIdx.x / 64;
-    const int64_t W = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
-    const uint32_t *counts = reinterpret_cast<const uint32_t *>(rec + kQueueCounts);
+    __shared__ PrefixLds pl;
     __shared__ u32x4 lds_all[kThreads / 64][2 * kSlabVectors];
+    const int64_t f = blockIdx.x / per_frame;
+    const int j = static_cast<int>(blockIdx.x - f * per_frame);
+    frame_prefix(pl, f, nframes, rec, pixels, chunks, j == 0, totals, out_noise, out_moments, out_cpu_noise,
+                 out_cpu_moments, maps, queue);
+    if (!maps)
+        return;
     u32x4 *lds = lds_all[threadIdx.x / 64];
+    const int64_t w = static_cast<int64_t>(j) * (kThreads / 64) + threadIdx.x / 64;
+    const int64_t W = static_cast<int64_t>(per_frame) * (kThreads / 64);
     const int64_t cap = static_cast<int64_t>(nframes) * chunks;
     Slabs Q;
     Q.R = static_cast<const u32x4 *>(ref);
@@ -949,16 +956,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     Q.maps = maps;
     Q.pixels = pixels;
     Q.chunks = static_cast<uint32_t>(chunks);
-    int64_t n = static_cast<int64_t>(counts[kSqNoise]) * kSlabs;
-    Q.queue = queue + kSqNoise * cap;
+    int64_t n = static_cast<int64_t>(pl.nq[kSqNoise]) * kSlabs;
+    Q.queue = queue + kSqNoise * cap + f * chunks;
     if (w < n)
         queue_maps<kSqNoise, kSh>(Q, w, W, n, lds);
-    n = static_cast<int64_t>(counts[kSqRef]) * kSlabs;
-    Q.queue = queue + kSqRef * cap;
+    n = static_cast<int64_t>(pl.nq[kSqRef]) * kSlabs;
+    Q.queue = queue + kSqRef * cap + f * chunks;
     if (w < n)
         queue_maps<kSqRef, kSh>(Q, w, W, n, lds);
-    n = static_cast<int64_t>(counts[kSqDist]) * kSlabs;
-    Q.queue = queue + kSqDist * cap;
+    n = static_cast<int64_t>(pl.nq[kSqDist]) * kSlabs;
+    Q.queue = queue + kSqDist * cap + f * chunks;
     if (w < n)
         queue_maps<kSqDist, kSh>(Q, w, W, n, lds);
 }
@@ -1511,29 +1518,33 @@ hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, cons
     const bool two_byte = g.sample_bytes == 2;  // one-byte sums never reach 2^53
     if (g.chunks > kMaxFrameChunks)
         return hipErrorInvalidValue;
-    cpu_order_prefix<<<dim3(nf), kThreads, 0, stream>>>(rec, g.pixels, g.chunks, totals, out_noise, out_moments,
-                                                        out_cpu_noise, out_cpu_moments, two_byte ? maps : nullptr,
-                                                        queue);
+    const bool shifted = map.general != 0;
+    // at two-byte samples, as many workgroups per frame as the device holds
+    // at once over all frames (at least one), never more than the frame can
+    // have slabs for
+    int64_t per_frame = 1;
+    if (two_byte) {
+        int64_t resident = 0;
+        err = shifted ? maps_resident_workgroups<true>(resident) : maps_resident_workgroups<false>(resident);
+        if (err != hipSuccess)
+            return err;
+        const int64_t most = (static_cast<int64_t>(g.chunks) * kSquares * kSlabs + kThreads / 64 - 1) / (kThreads / 64);
+        per_frame = resident / g.nframes;
+        per_frame = per_frame < 1 ? 1 : per_frame > most ? most : per_frame;
+    }
+    const dim3 wgs(static_cast<unsigned>(g.nframes * per_frame));
+    const int pf = static_cast<int>(per_frame);
+    uint64_t *maps_arg = two_byte ? maps : nullptr;
+    if (shifted)
+        cpu_order_maps<true><<<wgs, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, g.nframes, pf, rec, totals,
+                                                           out_noise, out_moments, out_cpu_noise, out_cpu_moments,
+                                                           queue, maps_arg, map);
+    else
+        cpu_order_maps<false><<<wgs, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, g.nframes, pf, rec, totals,
+                                                            out_noise, out_moments, out_cpu_noise, out_cpu_moments,
+                                                            queue, maps_arg, map);
     err = hipGetLastError();
     if (err != hipSuccess || !two_byte)
-        return err;
-    const bool shifted = map.general != 0;
-    // as many workgroups as the device holds at once, never more than there
-    // can be slabs
-    int64_t resident = 0;
-    err = shifted ? maps_resident_workgroups<true>(resident) : maps_resident_workgroups<false>(resident);
-    if (err != hipSuccess)
-        return err;
-    const int64_t slab_wgs = (g.workgroups * kSquares * kSlabs + kThreads / 64 - 1) / (kThreads / 64);
-    const dim3 wgs(static_cast<unsigned>(slab_wgs < resident ? slab_wgs : resident));
-    if (shifted)
-        cpu_order_maps<true><<<wgs, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, g.nframes, rec, queue,
-                                                           maps, map);
-    else
-        cpu_order_maps<false><<<wgs, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, g.nframes, rec, queue,
-                                                            maps, map);
-    err = hipGetLastError();
-    if (err != hipSuccess)
         return err;
     if (shifted)
         cpu_order_walk<true><<<dim3(nf * kSquares), 64 * kWalkWaves, 0, stream>>>(

@@ -25,10 +25,6 @@ constexpr int kRecordStride = 8;
 // 8..11.
 constexpr int kLowBits = 5;
 
-// Slots kQueueCounts and kQueueCounts + 1 of record 0 hold the three uint32
-// lengths of the CPU-order form's queues of chunks to map (noise, ref^2,
-// dist^2); its stage 1 zeroes them, and its prefix kernel adds to them.
-constexpr int kQueueCounts = 6;
 
 // Work split of one batch.  Each plane is read as 16-byte vectors; the
 // vectors of a frame that lie wholly inside it are cut into chunks of
