@@ -687,6 +687,7 @@ __device__ __forceinline__ void frame_prefix(PrefixLds &L, int64_t f, int nframe
 struct ItemData {
     u32x4 a[kLaneVectors], b[kLaneVectors];
     uint32_t ok;
+    int all_ok;  // every vector of the slab inside the chunk (wave-uniform)
 };
 
 // Makes the compiler forget what it knows of the vectors' values, so that
@@ -712,6 +713,7 @@ __device__ __forceinline__ void load_item(ItemData &x, const u32x4 *R, const u32
 {
     const int lane = threadIdx.x & 63;
     x.ok = 0;
+    x.all_ok = sb + kSlabVectors <= ce;
 #pragma unroll
     for (int j = 0; j < kLaneVectors; ++j) {
         const int64_t v = sb + 64 * j + lane;
@@ -755,21 +757,71 @@ __device__ __forceinline__ void consecutive(u32x4 (&a)[kLaneVectors], u32x4 (&b)
     wave_lds_sync();  // the next slab may overwrite the buffer
 }
 
-// What one pass over the lane's consecutive terms gathers for binade
-// 2^(k+52): their sum of rr and its smallest rr (a tie where 0), and their
-// run map.
+// What one pass over the lane's 32 consecutive terms gathers for binade
+// 2^(k+52), a pair of terms (j, j + 16) at a time in the two 16-bit halves
+// of a register: only the low k + 1 <= 5 bits of t2 = t + 2^(k-1) matter
+// here (rr, whether it is a tie, and h's parity), and they come from the
+// terms' low 16 bits.  Bit i of `untied` and `odd` is term i's (j in bit j,
+// j + 16 in bit j + 16: term order); rr2 holds the two halves' sums of rr.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
 struct SlabPass {
-    uint32_t rr_sum = 0, rr_min = ~0u;
-    RunMap m;
+    uint32_t rr2 = 0;   // sum of rr, per 16-bit half
+    uint32_t untied = 0;  // bit i: term i is no tie (rr > 0)
+    uint32_t odd = 0;   // bit i: h_i is odd (bit k of t2)
 };
 
-__device__ __forceinline__ void pass_term(SlabPass &p, uint32_t t, int k)
+template <int J>
+__device__ __forceinline__ void pass_pair(SlabPass &p, uint32_t ta, uint32_t tb, int k)
 {
-    const uint32_t t2 = t + (1u << (k - 1));
-    const uint32_t rr = t2 & ((1u << k) - 1);
-    p.rr_sum += rr;
-    p.rr_min = min(p.rr_min, rr);
-    run_step(p.m, t2, k);
+    static_assert(J >= 0 && J < 16, "pair index");
+    const u16x2 half = {static_cast<unsigned short>(1u << (k - 1)), static_cast<unsigned short>(1u << (k - 1))};
+    const u16x2 mask = {static_cast<unsigned short>((1u << k) - 1), static_cast<unsigned short>((1u << k) - 1)};
+    const u16x2 one = {1, 1};
+    // the low halves of terms J and J + 16, then t2 and rr of each
+    const u16x2 t2 = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(tb, ta, 0x05040100u)) + half;
+    const u16x2 rr = t2 & mask;
+    p.rr2 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, p.rr2) + rr);
+    // 1 where rr > 0 (not a tie), in bits J and J + 16: min(rr, 1) per half
+    uint32_t untied;
+    asm("v_pk_min_u16 %0, %1, %2" : "=v"(untied) : "v"(__builtin_bit_cast(uint32_t, rr)), "v"(__builtin_bit_cast(uint32_t, one)));
+    p.untied |= untied << J;
+    // bit k of each half, rotated to bits J and J + 16
+    const uint32_t rot = __builtin_amdgcn_alignbit(__builtin_bit_cast(uint32_t, t2), __builtin_bit_cast(uint32_t, t2),
+                                                   static_cast<uint32_t>(k - J) & 31u);
+    p.odd |= rot & ((1u << J) | (1u << (J + 16)));
+}
+
+// The lane's run map from its pass (RunMap's packing: per start parity s,
+// ties rounded down and the parity after).  From parity s, m + h_i has
+// parity s ^ odd_0 ^ ... ^ odd_i up to the first tie; after a tie m is even,
+// so from there on it is the XOR of odd over the terms since that tie --
+// a prefix XOR in segments that start after each tie.  A tie rounds down
+// where that parity is 1.
+__device__ __forceinline__ RunMap lane_run_map(const SlabPass &p)
+{
+    const uint32_t tie = ~p.untied;
+    RunMap m;
+    if (tie == 0) {
+        const uint32_t x = static_cast<uint32_t>(__builtin_popcount(p.odd)) & 1u;
+        m.C = 0;
+        m.P = x | ((x ^ 1u) << 16);
+        return m;
+    }
+    uint32_t sx = p.odd, head = tie << 1;
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) {
+        sx ^= (sx << d) & ~head;
+        head |= head << d;
+    }
+    const uint32_t first = tie & (0u - tie);
+    const uint32_t upto_first = (first << 1) - 1u;  // bits 0 .. first tie (all of them if it is bit 31)
+    const uint32_t rest = static_cast<uint32_t>(__builtin_popcount(tie & sx & ~upto_first));
+    const uint32_t x1 = (sx & first) ? 1u : 0u;  // parity of m + h at the first tie, from s = 0
+    m.C = (rest + x1) | ((rest + (x1 ^ 1u)) << 16);
+    const uint32_t after = (tie >> 31) ? 0u : (sx >> 31);
+    m.P = after | (after << 16);
+    return m;
 }
 
 // The slab's map in binade 2^(k+52) from its exact total T, the OR of its
@@ -782,10 +834,23 @@ __device__ __forceinline__ Map2 slab_map(uint64_t T, uint32_t low_bits, const Sl
     constexpr uint64_t n = 64 * kLaneVectors * kTerms;
     if (__all((low_bits & ((1u << k) - 1)) == 0))
         return untied_map(T >> k);
-    const uint32_t RR = wave_total32(p.rr_sum);
-    if (!__any(p.rr_min == 0))
+    const uint32_t RR = wave_total32((p.rr2 & 0xffffu) + (p.rr2 >> 16));
+    if (__all(p.untied == ~0u))
         return untied_map((T + (n << (k - 1)) - RR) >> k);
-    return run_map(wave_run(p.m), T, n, RR, k);
+    return run_map(wave_run(lane_run_map(p)), T, n, RR, k);
+}
+
+// The pass over the lane's 32 consecutive terms, pair by pair.
+template <int KK>
+__device__ __forceinline__ void pass_slab(SlabPass &p, const u32x4 (&a)[kLaneVectors], const u32x4 (&b)[kLaneVectors],
+                                          int k)
+{
+    static_assert(kLaneVectors * kTerms == 32, "two halves of 16 terms");
+#define VQX_PAIR(J) pass_pair<J>(p, vector_term<KK>(a[(J) / 8], b[(J) / 8], (J) % 8), \
+                                 vector_term<KK>(a[(J) / 8 + 2], b[(J) / 8 + 2], (J) % 8), k)
+    VQX_PAIR(0); VQX_PAIR(1); VQX_PAIR(2); VQX_PAIR(3); VQX_PAIR(4); VQX_PAIR(5); VQX_PAIR(6); VQX_PAIR(7);
+    VQX_PAIR(8); VQX_PAIR(9); VQX_PAIR(10); VQX_PAIR(11); VQX_PAIR(12); VQX_PAIR(13); VQX_PAIR(14); VQX_PAIR(15);
+#undef VQX_PAIR
 }
 
 // Slab si of its chunk; lane 0 writes its part of the entry.  One pass over
@@ -796,33 +861,33 @@ template <int KK>
 __device__ __forceinline__ void item_maps(ItemData &x, int si, int e, bool dual, uint64_t *entry, u32x4 *lds)
 {
     const int k = e - 52;
+    if (__builtin_amdgcn_readfirstlane(x.all_ok) == 0) {  // a slab past the frame's last vector
 #pragma unroll
-    for (int j = 0; j < kLaneVectors; ++j)
-        keep_if<KK>((x.ok >> j) & 1u, x.a[j], x.b[j]);
+        for (int j = 0; j < kLaneVectors; ++j)
+            keep_if<KK>((x.ok >> j) & 1u, x.a[j], x.b[j]);
+    }
     consecutive<KK>(x.a, x.b, lds);
-    uint64_t tot = 0;
-    uint32_t low_bits = 0;
-    SlabPass p;
+    // the lane's total (a 64-bit sum kept as two words and a carry add)
+    uint32_t lo = 0, hi = 0, low_bits = 0;
 #pragma unroll
     for (int j = 0; j < kLaneVectors; ++j)
 #pragma unroll
         for (int i = 0; i < kTerms; ++i) {
             const uint32_t t = vector_term<KK>(x.a[j], x.b[j], i);
-            tot += t;
+            unsigned int carry;
+            lo = __builtin_addc(lo, t, 0u, &carry);
+            hi += carry;
             low_bits |= t;
-            pass_term(p, t, k);
         }
-    const uint64_t T = wave_total64(tot);
+    const uint64_t T = wave_total64(lo | (static_cast<uint64_t>(hi) << 32));
+    SlabPass p;
+    pass_slab<KK>(p, x.a, x.b, k);
     const Map2 slab = slab_map(T, low_bits, p, k);
     Map2 slab_b;
     if (dual) {
         forget<KK>(x.a, x.b);
         SlabPass q;
-#pragma unroll
-        for (int j = 0; j < kLaneVectors; ++j)
-#pragma unroll
-            for (int i = 0; i < kTerms; ++i)
-                pass_term(q, vector_term<KK>(x.a[j], x.b[j], i), k + 1);
+        pass_slab<KK>(q, x.a, x.b, k + 1);
         slab_b = slab_map(T, low_bits, q, k + 1);
     }
     if ((threadIdx.x & 63) == 0) {
@@ -841,10 +906,10 @@ __device__ __forceinline__ void item_maps(ItemData &x, int si, int e, bool dual,
 struct Slabs {
     const u32x4 *R, *D;
     VecMap map;
-    const uint64_t *queue;  // this square sum's queue
+    const uint64_t *queue;  // this square sum's queue segment of the frame
     uint64_t *maps;
-    int64_t pixels;
-    uint32_t chunks;
+    int64_t frame, vb, ve;  // the frame, its first whole vector and one past its last
+    uint32_t first;         // frame * chunks: the frame's first queue index
 };
 
 struct SlabItem {
@@ -854,43 +919,51 @@ struct SlabItem {
     bool dual;
 };
 
+// Slab item i (wave-uniform) of the frame's queue segment.
 template <int KK>
 __device__ __forceinline__ SlabItem slab_item(const Slabs &Q, int64_t i)
 {
-    constexpr int V = 8;
     const uint64_t q = Q.queue[i / kSlabs];
     const uint32_t idx = static_cast<uint32_t>(q);
-    const uint32_t f = idx / Q.chunks, c = idx - f * Q.chunks;
-    const int64_t e0 = static_cast<int64_t>(f) * Q.pixels;
-    const int64_t vb = (e0 + V - 1) / V, ve = (e0 + Q.pixels) / V;
+    const uint32_t c = idx - Q.first;
     SlabItem x;
-    x.frame = f;
+    x.frame = Q.frame;
     x.si = static_cast<int>(i % kSlabs);
     x.e = static_cast<int>((q >> 32) & 0xffu);
     x.dual = ((q >> 40) & 1u) != 0;
-    x.cb = vb + static_cast<int64_t>(c) * kChunkVectors;
-    x.ce = x.cb + kChunkVectors < ve ? x.cb + kChunkVectors : ve;
+    x.cb = Q.vb + static_cast<int64_t>(c) * kChunkVectors;
+    x.ce = x.cb + kChunkVectors < Q.ve ? x.cb + kChunkVectors : Q.ve;
     x.sb = x.cb + static_cast<int64_t>(x.si) * kSlabVectors;
     x.entry = Q.maps + (static_cast<uint64_t>(idx) * kSquares + KK) * kEntry;
     return x;
 }
 
-// Slab items i, i + stride, ... below n, in turn.  The next item's vectors
-// are read while the current one is mapped, except for the noise, which
-// reads both planes.
+// Slab items below n of the frame's queue segment, handed out one at a time
+// from the counter `ticket` to whichever wave of the frame's workgroups
+// asks first.  The next item's vectors are read while the current one is
+// mapped, except for the noise, which reads both planes.
 template <int KK, bool kSh>
-__device__ __forceinline__ void queue_maps(const Slabs &Q, int64_t i, int64_t stride, int64_t n, u32x4 *lds)
+__device__ __forceinline__ void queue_maps(const Slabs &Q, uint32_t *ticket, int64_t n, u32x4 *lds)
 {
+    auto next = [&]() -> int64_t {
+        uint32_t t = 0;
+        if ((threadIdx.x & 63) == 0)
+            t = atomicAdd(ticket, 1u);
+        return static_cast<int64_t>(__builtin_amdgcn_readfirstlane(t));
+    };
     ItemData x, y;
     auto map_item = [&](ItemData &d, const SlabItem &it) {
         item_maps<KK>(d, it.si, it.e, it.dual, it.entry, lds);
     };
+    int64_t i = next();
+    if (i >= n)
+        return;
     SlabItem u = slab_item<KK>(Q, i);
     load_item<KK, kSh>(x, Q.R, Q.D, Q.map, u.frame, u.cb, u.sb, u.ce);
     if constexpr (KK == kSqNoise) {
         for (;;) {
             map_item(x, u);
-            i += stride;
+            i = next();
             if (i >= n)
                 return;
             u = slab_item<KK>(Q, i);
@@ -903,7 +976,7 @@ __device__ __forceinline__ void queue_maps(const Slabs &Q, int64_t i, int64_t st
         // loads of the one after it.
         SlabItem v;
         for (;;) {
-            i += stride;
+            i = next();
             if (i >= n) {
                 map_item(x, u);
                 return;
@@ -911,7 +984,7 @@ __device__ __forceinline__ void queue_maps(const Slabs &Q, int64_t i, int64_t st
             v = slab_item<KK>(Q, i);
             load_item<KK, kSh>(y, Q.R, Q.D, Q.map, v.frame, v.cb, v.sb, v.ce);
             map_item(x, u);
-            i += stride;
+            i = next();
             if (i >= n) {
                 map_item(y, v);
                 return;
@@ -923,51 +996,59 @@ __device__ __forceinline__ void queue_maps(const Slabs &Q, int64_t i, int64_t st
     }
 }
 
-// Steps 2 and 3 in one launch: `per_frame` workgroups per frame (grid
-// nframes * per_frame), each with the frame's prefix scan (frame_prefix),
-// then its share of the frame's queued slabs: wave w of the frame's
-// W = 4 * per_frame takes slab items w, w + W, ... of each of the frame's
-// queues in turn.  Workgroup 0 of each frame writes the prefix's results.
-// Two-byte samples map slabs; one-byte ones only scan (per_frame 1).
-// Three waves per SIMD fit its registers without spills (168 VGPRs), one
-// more than the compiler picks unasked.
+// Steps 2 and 3 in one launch: a group of workgroups per frame (the grid a
+// multiple of nframes), each with the frame's prefix scan (frame_prefix),
+// then the frame's queued slabs, which its waves take one at a time from
+// the frame's counters (one per queue, in turn).  Workgroup 0 of each
+// frame writes the prefix's results.
+// Two-byte samples map slabs; one-byte ones only scan (one workgroup per
+// frame).
+// Four waves per SIMD fit its registers without spills (128 VGPRs).
 template <bool kSh>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void cpu_order_maps(
-    const void *ref, const void *dist, int64_t pixels, int chunks, int nframes, int per_frame, const uint64_t *rec,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void cpu_order_maps(
+    const void *ref, const void *dist, int64_t pixels, int chunks, int nframes, uint64_t *rec,
     uint64_t *totals, uint64_t *out_noise, uint64_t *out_moments, uint64_t *out_cpu_noise, uint64_t *out_cpu_moments,
     uint64_t *queue, uint64_t *maps, VecMap vmap)
 {
     __shared__ PrefixLds pl;
     __shared__ u32x4 lds_all[kThreads / 64][2 * kSlabVectors];
-    const int64_t f = blockIdx.x / per_frame;
-    const int j = static_cast<int>(blockIdx.x - f * per_frame);
+    // frame f's workgroups are f, f + nframes, ...: spread over the launch
+    // order, so that each frame has workgroups of every age on the CUs
+    // (older waves issue first) and the frames progress together
+    const int64_t f = blockIdx.x % nframes;
+    const int j = static_cast<int>(blockIdx.x / nframes);
     frame_prefix(pl, f, nframes, rec, pixels, chunks, j == 0, totals, out_noise, out_moments, out_cpu_noise,
                  out_cpu_moments, maps, queue);
     if (!maps)
         return;
-    u32x4 *lds = lds_all[threadIdx.x / 64];
-    const int64_t w = static_cast<int64_t>(j) * (kThreads / 64) + threadIdx.x / 64;
-    const int64_t W = static_cast<int64_t>(per_frame) * (kThreads / 64);
+    // the wave's index, made wave-uniform so that the items' bookkeeping
+    // runs on the scalar unit
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / 64));
+    u32x4 *lds = lds_all[wave];
+    uint32_t *tickets = reinterpret_cast<uint32_t *>(rec + f * chunks * kRecordStride + kTickets);
     const int64_t cap = static_cast<int64_t>(nframes) * chunks;
+    constexpr int V = 8;
     Slabs Q;
     Q.R = static_cast<const u32x4 *>(ref);
     Q.D = static_cast<const u32x4 *>(dist);
     Q.map = vmap;
     Q.maps = maps;
-    Q.pixels = pixels;
-    Q.chunks = static_cast<uint32_t>(chunks);
+    Q.frame = f;
+    Q.vb = (f * pixels + V - 1) / V;
+    Q.ve = (f * pixels + pixels) / V;
+    Q.first = static_cast<uint32_t>(f * chunks);
     int64_t n = static_cast<int64_t>(pl.nq[kSqNoise]) * kSlabs;
     Q.queue = queue + kSqNoise * cap + f * chunks;
-    if (w < n)
-        queue_maps<kSqNoise, kSh>(Q, w, W, n, lds);
+    if (n > 0)
+        queue_maps<kSqNoise, kSh>(Q, tickets + kSqNoise, n, lds);
     n = static_cast<int64_t>(pl.nq[kSqRef]) * kSlabs;
     Q.queue = queue + kSqRef * cap + f * chunks;
-    if (w < n)
-        queue_maps<kSqRef, kSh>(Q, w, W, n, lds);
+    if (n > 0)
+        queue_maps<kSqRef, kSh>(Q, tickets + kSqRef, n, lds);
     n = static_cast<int64_t>(pl.nq[kSqDist]) * kSlabs;
     Q.queue = queue + kSqDist * cap + f * chunks;
-    if (w < n)
-        queue_maps<kSqDist, kSh>(Q, w, W, n, lds);
+    if (n > 0)
+        queue_maps<kSqDist, kSh>(Q, tickets + kSqDist, n, lds);
 }
 
 // ------------------------------------------------------------------ 4. walk
@@ -1521,7 +1602,11 @@ hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, cons
     const bool shifted = map.general != 0;
     // at two-byte samples, as many workgroups per frame as the device holds
     // at once over all frames (at least one), never more than the frame can
-    // have slabs for
+    // have slabs for, and at most kMaxPerFrame: each runs the frame's scan
+    // for itself, and past that more of them cost more scans than they save
+    // (a 3840x2160x32 batch with nothing to map: 166 us a step at 16
+    // against 169 us at 32)
+    constexpr int64_t kMaxPerFrame = 16;
     int64_t per_frame = 1;
     if (two_byte) {
         int64_t resident = 0;
@@ -1531,16 +1616,16 @@ hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, cons
         const int64_t most = (static_cast<int64_t>(g.chunks) * kSquares * kSlabs + kThreads / 64 - 1) / (kThreads / 64);
         per_frame = resident / g.nframes;
         per_frame = per_frame < 1 ? 1 : per_frame > most ? most : per_frame;
+        per_frame = per_frame > kMaxPerFrame ? kMaxPerFrame : per_frame;
     }
     const dim3 wgs(static_cast<unsigned>(g.nframes * per_frame));
-    const int pf = static_cast<int>(per_frame);
     uint64_t *maps_arg = two_byte ? maps : nullptr;
     if (shifted)
-        cpu_order_maps<true><<<wgs, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, g.nframes, pf, rec, totals,
+        cpu_order_maps<true><<<wgs, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, g.nframes, rec, totals,
                                                            out_noise, out_moments, out_cpu_noise, out_cpu_moments,
                                                            queue, maps_arg, map);
     else
-        cpu_order_maps<false><<<wgs, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, g.nframes, pf, rec, totals,
+        cpu_order_maps<false><<<wgs, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, g.nframes, rec, totals,
                                                             out_noise, out_moments, out_cpu_noise, out_cpu_moments,
                                                             queue, maps_arg, map);
     err = hipGetLastError();

@@ -25,6 +25,12 @@ constexpr int kRecordStride = 8;
 // 8..11.
 constexpr int kLowBits = 5;
 
+// Slots kTickets and kTickets + 1 of the record of each frame's chunk 0
+// hold three uint32 counters (noise, ref^2, dist^2) from which the
+// CPU-order form's maps kernel hands out slab items; its stage 1 zeroes
+// them.
+constexpr int kTickets = 6;
+
 
 // Work split of one batch.  Each plane is read as 16-byte vectors; the
 // vectors of a frame that lie wholly inside it are cut into chunks of

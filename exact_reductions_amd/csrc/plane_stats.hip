@@ -285,7 +285,8 @@ __global__ __launch_bounds__(kThreads) void stage1_u8(const void *ref, const voi
 }
 
 // kLowBitsOut: also the OR of the low bits of each square sum's terms, in
-// the record's slot kLowBits (for the CPU-order form).
+// the record's slot kLowBits, and zero item tickets in each frame's chunk 0
+// (for the CPU-order form).
 // kForm: the cheaper group form tried (with kLowBitsOut, the bright one or
 // none).
 template <bool kLowBitsOut, int kForm>
@@ -311,8 +312,13 @@ __global__ __launch_bounds__(kThreads) void stage1_u16(const void *ref, const vo
     write_record(part, wg, rec);
     if constexpr (kLowBitsOut) {
         const uint32_t low = workgroup_or((a.or_noise & 15u) | ((a.or_r2 & 15u) << 4) | ((a.or_d2 & 15u) << 8));
-        if (threadIdx.x == 0)
+        if (threadIdx.x == 0) {
             part[wg * kRecordStride + kLowBits] = low;
+            if (chunk == 0) {
+                part[wg * kRecordStride + kTickets] = 0;
+                part[wg * kRecordStride + kTickets + 1] = 0;
+            }
+        }
     }
 }
 

@@ -38,8 +38,8 @@ static_assert(kLaneIters % kInFlight == 0, "whole load groups");
 // Stage 1 over plane views whose rows are whole 16-byte vectors
 // (two-byte samples, so frames hold no partial vectors): the same chunks,
 // terms and records as stage1_u16<kLowBitsOut>, each vector found through
-// the VecMap; kLowBitsOut: also the low bits of the terms, for the
-// CPU-order form; kForm: where the planes' vectors start
+// the VecMap; kLowBitsOut: also the low bits of the terms and zero item
+// tickets, for the CPU-order form; kForm: where the planes' vectors start
 // within 16-byte blocks -- all at 0 (kAligned: one 16-byte load per vector,
 // found with the map's pads), or anywhere (kCut: ref and dist the bases
 // rounded down to 16 bytes, each vector found with the map's byte strides
@@ -111,8 +111,13 @@ __global__ __launch_bounds__(kThreads) void stage1_u16_mapped(const void *ref, c
     write_record(part, wg, rec);
     if constexpr (kLowBitsOut) {
         const uint32_t low = workgroup_or((a.or_noise & 15u) | ((a.or_r2 & 15u) << 4) | ((a.or_d2 & 15u) << 8));
-        if (threadIdx.x == 0)
+        if (threadIdx.x == 0) {
             part[wg * kRecordStride + kLowBits] = low;
+            if (chunk == 0) {
+                part[wg * kRecordStride + kTickets] = 0;
+                part[wg * kRecordStride + kTickets + 1] = 0;
+            }
+        }
     }
 }
 
