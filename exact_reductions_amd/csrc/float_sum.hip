@@ -216,10 +216,19 @@ __device__ __forceinline__ int first_set(bool flag)
 __device__ __forceinline__ void load_tile(const float *tile_base, int64_t count, uint32_t *lds)
 {
     const uint32_t *src = reinterpret_cast<const uint32_t *>(tile_base);
+    // every lane loads (past the end, the tile's first term, dropped after),
+    // so that no branch stands between the 16 loads and their waits: they
+    // are all in flight at once
+    uint32_t v[kRun];
 #pragma unroll
     for (int j = 0; j < kRun; ++j) {
         const int i = threadIdx.x + j * kThreads;
-        lds[i + i / kRun] = i < count ? __builtin_nontemporal_load(src + i) : 0u;
+        v[j] = __builtin_nontemporal_load(src + (i < count ? i : 0));
+    }
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+        const int i = threadIdx.x + j * kThreads;
+        lds[i + i / kRun] = i < count ? v[j] : 0u;
     }
     __syncthreads();
 }
@@ -238,35 +247,57 @@ __device__ __forceinline__ Map run_map(const uint32_t *lds, int uexp)
 // ------------------------------------------------------------- kernel 1
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// This thread's 16 terms of a tile: with 16-byte loads where the tile is
-// whole and 16-byte aligned (thread t takes vectors t, t+256, t+512 and
-// t+768), else term by term (thread t takes terms t, t+256, ...).  f(t) is
-// called on each term; zeros stand in past the buffer's end.
-template <class F>
-__device__ __forceinline__ void for_tile_terms(const float *tile_base, int64_t count, F &&f)
+// This thread's 16 terms of a tile, loaded: with 16-byte loads where the
+// tile is whole and 16-byte aligned (thread t takes vectors t, t+256, t+512
+// and t+768), else term by term (thread t takes terms t, t+256, ...); zeros
+// stand in past the buffer's end.  The order of a thread's terms does not
+// matter to the users (sums, ORs, counts).
+struct TileTerms {
+    u32x4 x[kRun / 4];
+};
+
+__device__ __forceinline__ TileTerms load_tile_terms(const float *tile_base, int64_t count)
 {
     const uint32_t *src = reinterpret_cast<const uint32_t *>(tile_base);
+    TileTerms t;
     if (count >= kTile && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
         const u32x4 *v = reinterpret_cast<const u32x4 *>(src);
-        u32x4 x[kRun / 4];
 #pragma unroll
         for (int j = 0; j < kRun / 4; ++j)
-            x[j] = __builtin_nontemporal_load(v + threadIdx.x + j * kThreads);
-#pragma unroll
-        for (int j = 0; j < kRun / 4; ++j) {
-            const uint32_t t0 = x[j].x, t1 = x[j].y, t2 = x[j].z, t3 = x[j].w;
-            f(t0);
-            f(t1);
-            f(t2);
-            f(t3);
-        }
+            t.x[j] = __builtin_nontemporal_load(v + threadIdx.x + j * kThreads);
     } else {
+        // branch-free loads, as in load_tile
 #pragma unroll
         for (int j = 0; j < kRun; ++j) {
             const int i = threadIdx.x + j * kThreads;
-            f(i < count ? __builtin_nontemporal_load(src + i) : 0u);
+            t.x[j / 4][j % 4] = __builtin_nontemporal_load(src + (i < count ? i : 0));
+        }
+#pragma unroll
+        for (int j = 0; j < kRun; ++j) {
+            const int i = threadIdx.x + j * kThreads;
+            t.x[j / 4][j % 4] = i < count ? t.x[j / 4][j % 4] : 0u;
         }
     }
+    return t;
+}
+
+template <class F>
+__device__ __forceinline__ void for_terms(const TileTerms &t, F &&f)
+{
+#pragma unroll
+    for (int j = 0; j < kRun / 4; ++j) {
+        const uint32_t t0 = t.x[j].x, t1 = t.x[j].y, t2 = t.x[j].z, t3 = t.x[j].w;
+        f(t0);
+        f(t1);
+        f(t2);
+        f(t3);
+    }
+}
+
+template <class F>
+__device__ __forceinline__ void for_tile_terms(const float *tile_base, int64_t count, F &&f)
+{
+    for_terms(load_tile_terms(tile_base, count), f);
 }
 
 // Sum and OR over the workgroup; every thread gets both.  All threads must
@@ -333,9 +364,11 @@ __device__ __forceinline__ int unit_exponent_of(double v)
 // binades the float sum may be in over each tile.  plan = (unit exponent of
 // the first + 256) | (count << 16), count 0 (no maps), 1 or 2.
 __global__ __launch_bounds__(kThreads) void fsum_plan(const double *totals, const uint32_t *bad, int ntiles,
-                                                      Rec *recs, uint32_t *buffer_bad)
+                                                      Rec *recs, uint32_t *buffer_bad, uint32_t *ordered)
 {
     const int buf = blockIdx.x;
+    if (buf == 0 && threadIdx.x == 0)
+        ordered[0] = 0;  // the ordered-path queue, filled by fsum_tile_maps
     const double *tot = totals + static_cast<int64_t>(buf) * ntiles;
     const uint32_t *bd = bad + static_cast<int64_t>(buf) * ntiles;
     Rec *rc = recs + static_cast<int64_t>(buf) * ntiles;
@@ -384,55 +417,63 @@ __global__ __launch_bounds__(kThreads) void fsum_plan(const double *totals, cons
 // is exact (a power-of-two scale; where it falls below the normal range it
 // is far below 1/2, and h = 0 either way), x + 1/2 is exact below 2^22, and
 // the floor is exact: so h is read off floor(x + 1/2), and the term is a tie
-// exactly where x + 1/2 is an integer.  `simple` is false where that does
-// not hold (a tie, a large term, or a unit too small to scale to); the map
-// then comes from the ordered path.
-struct FastMap {
-    uint32_t H;
-    bool simple, leaves;
-};
-
+// exactly where x + 1/2 is an integer.  Where that does not hold (a tie, a
+// large term, or a unit too small to scale to) the map comes from the
+// ordered path.  A sum of h that reaches 2^24 marks the tile as leaving the
+// binade: with a large term that mark may be early, which only sends the
+// walk through the tile run by run.
 __device__ __forceinline__ float pow2(int e) { return __uint_as_float(static_cast<uint32_t>(e + 127) << 23); }
 
 // grid (tiles, buffers): each planned tile's map in its one or two binades.
 __global__ __launch_bounds__(kThreads) void fsum_tile_maps(const float *terms, int64_t nterms, int ntiles,
-                                                           Rec *recs)
+                                                           Rec *recs, uint32_t *ordered)
 {
     const int tile = blockIdx.x, buf = blockIdx.y;
     const int64_t at = static_cast<int64_t>(buf) * ntiles + tile;
+    const int64_t first = static_cast<int64_t>(tile) * kTile;
+    const float *tb = terms + static_cast<int64_t>(buf) * nterms + first;
+    // the terms are read before the plan arrives (only a sum's first tiles
+    // have none), so the two reads are in flight together
+    const TileTerms terms_in = load_tile_terms(tb, nterms - first);
     const uint32_t pl = recs[at].plan;
     const int n = static_cast<int>(pl >> 16);
     if (n == 0)
         return;
     const int uexp = static_cast<int>(pl & 0xffffu) - 256;
-    const int64_t first = static_cast<int64_t>(tile) * kTile;
-    const float *tb = terms + static_cast<int64_t>(buf) * nterms + first;
     // unscaled to units of the lower binade; the upper's units are twice as large
     const bool scalable = uexp >= -126;
     const float scale = pow2(scalable ? -uexp : 0);
-    uint32_t H0 = 0, H1 = 0, odd = 0;  // odd: bit 0 a tie or large term (lower), bit 1 (upper)
-    for_tile_terms(tb, nterms - first, [&](uint32_t t) {
-        const float x0 = __uint_as_float(t & 0x7fffffffu) * scale;
+    // per binade: the sum of h (in binary32: exact while below 2^24, and
+    // at least 2^24 once the exact sum is), the smallest fraction of t/u +
+    // 1/2 (0 where a term ties) and the largest t/u.  A buffer holding a
+    // negative or non-finite term gets NaN whatever its maps say.
+    float Hf0 = 0.0f, Hf1 = 0.0f, lo0 = 1.0f, lo1 = 1.0f, top = 0.0f;
+    for_terms(terms_in, [&](uint32_t t) {
+        const float x0 = __uint_as_float(t) * scale;
         const float y0 = x0 + 0.5f;
         const float f0 = floorf(y0);
-        odd |= (f0 == y0 || !(x0 < 0x1p22f)) ? 1u : 0u;
-        H0 += static_cast<uint32_t>(f0 < 0x1p22f ? f0 : 0.0f);
+        lo0 = fminf(lo0, y0 - f0);
+        top = fmaxf(top, x0);
+        Hf0 += f0;
         if (n == 2) {
             const float x1 = x0 * 0.5f;
             const float y1 = x1 + 0.5f;
             const float f1 = floorf(y1);
-            odd |= (f1 == y1 || !(x1 < 0x1p22f)) ? 2u : 0u;
-            H1 += static_cast<uint32_t>(f1 < 0x1p22f ? f1 : 0.0f);
+            lo1 = fminf(lo1, y1 - f1);
+            Hf1 += f1;
         }
     });
-    // a thread's sum of 16 terms below 2^22 stays below 2^26; one that
-    // reaches 2^24 leaves any binade, so the rest stays below 2^32
-    uint32_t leaves = (H0 >= kTop ? 1u : 0u) | (H1 >= kTop ? 2u : 0u);
+    // odd: bit 0 a tie or a large term in the lower binade, bit 1 in the upper
+    const uint32_t odd = ((lo0 == 0.0f || !(top < 0x1p22f)) ? 1u : 0u) |
+                         ((n == 2 && (lo1 == 0.0f || !(top < 0x1p23f))) ? 2u : 0u);
+    // a thread whose sum reaches 2^24 leaves any binade; the others' sums
+    // are exact integers below 2^24
+    const uint32_t leaves = (Hf0 >= 0x1p24f ? 1u : 0u) | (Hf1 >= 0x1p24f ? 2u : 0u);
+    uint32_t H0 = static_cast<uint32_t>(Hf0 < 0x1p24f ? Hf0 : 0.0f);
+    uint32_t H1 = static_cast<uint32_t>(Hf1 < 0x1p24f ? Hf1 : 0.0f);
     float dummy = 0.0f;
     uint32_t flags = odd | (leaves << 2) | (scalable ? 0u : 3u);
     workgroup_sum_or(dummy, flags);
-    H0 = H0 >= kTop ? 0u : H0;
-    H1 = H1 >= kTop ? 0u : H1;
     __shared__ uint32_t lh[2][kThreads / 64];
 #pragma unroll
     for (int d = 32; d > 0; d >>= 1) {
@@ -444,32 +485,61 @@ __global__ __launch_bounds__(kThreads) void fsum_tile_maps(const float *terms, i
         lh[1][threadIdx.x >> 6] = H1;
     }
     __syncthreads();
-    __shared__ uint32_t lds[kPad];
-    bool staged = false;
-    for (int k = 0; k < n; ++k) {
-        Map m;
-        if (flags & ((4u << k))) {
-            m = leaving_map();
-        } else if (!(flags & (1u << k))) {
-            uint32_t h = 0;
+    // a tile that needs the ordered path in any of its binades goes on the
+    // queue of fsum_ordered_maps, which writes all its maps
+    if (flags & 3u) {
+        if (threadIdx.x == 0)
+            ordered[1 + atomicAdd(&ordered[0], 1u)] = static_cast<uint32_t>(at);
+        return;
+    }
+    if (threadIdx.x == 0) {
+        for (int k = 0; k < n; ++k) {
+            Map m;
+            if (flags & (4u << k)) {
+                m = leaving_map();
+            } else {
+                uint32_t h = 0;
 #pragma unroll
-            for (int w = 0; w < kThreads / 64; ++w)
-                h += lh[k][w];
-            m = {h > kSat ? kSat : h, 0u, 0u};
-        } else {
-            // ties, large terms or a tiny unit: in order, term by term
-            if (!staged) {
-                load_tile(tb, nterms - first, lds);
-                staged = true;
+                for (int w = 0; w < kThreads / 64; ++w)
+                    h += lh[k][w];
+                m = {h > kSat ? kSat : h, 0u, 0u};
             }
-            m = reduce_maps(run_map(lds, uexp + k));
-        }
-        if (threadIdx.x == 0) {
             if (k == 0)
                 recs[at].m0 = m;
             else
                 recs[at].m1 = m;
         }
+    }
+}
+
+// The queued tiles' maps in their planned binades, in order, term by term
+// (ties, large terms, or a unit too small to scale to): a fixed grid of
+// workgroups takes the queue's items in turn.  ordered[0] is the queue's
+// length, zeroed by fsum_plan; items (buffer * ntiles + tile) follow.
+__global__ __launch_bounds__(kThreads) void fsum_ordered_maps(const float *terms, int64_t nterms, int ntiles,
+                                                              Rec *recs, const uint32_t *ordered)
+{
+    __shared__ uint32_t lds[kPad];
+    const uint32_t count = ordered[0];
+    for (uint32_t i = blockIdx.x; i < count; i += gridDim.x) {
+        const uint32_t at = ordered[1 + i];
+        const int buf = static_cast<int>(at / static_cast<uint32_t>(ntiles));
+        const int tile = static_cast<int>(at - static_cast<uint32_t>(buf) * static_cast<uint32_t>(ntiles));
+        const uint32_t pl = recs[at].plan;
+        const int n = static_cast<int>(pl >> 16);
+        const int uexp = static_cast<int>(pl & 0xffffu) - 256;
+        const int64_t first = static_cast<int64_t>(tile) * kTile;
+        load_tile(terms + static_cast<int64_t>(buf) * nterms + first, nterms - first, lds);
+        for (int k = 0; k < n; ++k) {
+            const Map m = reduce_maps(run_map(lds, uexp + k));
+            if (threadIdx.x == 0) {
+                if (k == 0)
+                    recs[at].m0 = m;
+                else
+                    recs[at].m1 = m;
+            }
+        }
+        __syncthreads();  // before the next item overwrites the LDS
     }
 }
 
@@ -482,27 +552,70 @@ __device__ __forceinline__ uint32_t apply(const Map &x, uint32_t m)
     return m + x.H - ((m & 1u) ? x.td1 : x.td0);
 }
 
+// Exclusive prefix sum of the threads' counts, in thread order; `total`
+// gets the workgroup's.  All threads must call it.
+__device__ __forceinline__ uint32_t scan_counts(uint32_t c, uint32_t &total)
+{
+    __shared__ uint32_t wave_total[kThreads / 64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t x = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_up(x, d, 64);
+        x += lane >= d ? y : 0u;
+    }
+    if (lane == 63)
+        wave_total[wave] = x;
+    __syncthreads();
+    uint32_t before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+        before += w < wave ? wave_total[w] : 0u;
+        total += wave_total[w];
+    }
+    __syncthreads();
+    return before + x - c;
+}
+
 // The tile in LDS, with S (bit pattern) at its start: S after it.  A tile
 // over which the sum may cross more than two binades (the start of a sum)
-// is added term by term by one thread; any other run by run.  All threads
-// must call it.
+// is added term by term by one thread, its zero terms left out (adding a
+// zero leaves the sum as it was [HVS, Consequences]; -0 too, to a sum that
+// is +0 or positive); any other tile run by run.  All threads must call it.
 __device__ uint32_t walk_tile(const uint32_t *lds, uint32_t S, bool one_by_one)
 {
     __shared__ uint32_t shared_S;
     if (one_by_one) {
+        __shared__ uint32_t nonzero[kTile];
+        // the tile's nonzero terms, in order, packed
+        const uint32_t *mine = lds + threadIdx.x * (kRun + 1);
+        uint32_t count = 0;
+#pragma unroll
+        for (int j = 0; j < kRun; ++j)
+            count += (mine[j] & 0x7fffffffu) ? 1u : 0u;
+        uint32_t total;
+        uint32_t at = scan_counts(count, total);
+#pragma unroll
+        for (int j = 0; j < kRun; ++j)
+            if (mine[j] & 0x7fffffffu)
+                nonzero[at++] = mine[j];
+        __syncthreads();
         if (threadIdx.x == 0) {
             float f = __uint_as_float(S);
-            for (int r = 0; r < kThreads; ++r) {
-                // a run's 16 reads issued together, then its 16 adds
-                const uint32_t *p = lds + r * (kRun + 1);
+            uint32_t i = 0;
+            for (; i + kRun <= total; i += kRun) {
+                // 16 reads issued together, then their 16 adds
                 float v[kRun];
 #pragma unroll
                 for (int j = 0; j < kRun; ++j)
-                    v[j] = __uint_as_float(p[j]);
+                    v[j] = __uint_as_float(nonzero[i + j]);
 #pragma unroll
                 for (int j = 0; j < kRun; ++j)
                     f = f + v[j];
             }
+            for (; i < total; ++i)
+                f = f + __uint_as_float(nonzero[i]);
             shared_S = __float_as_uint(f);
         }
         __syncthreads();
@@ -552,6 +665,9 @@ __device__ uint32_t walk_tile(const uint32_t *lds, uint32_t S, bool one_by_one)
     return S;
 }
 
+// Workgroups of fsum_ordered_maps.
+constexpr int64_t kOrderedGrid = 1024;
+
 // One workgroup per buffer.  A window is kWindow tiles, kPerThread
 // consecutive ones per thread.
 constexpr int kPerThread = 4;
@@ -586,17 +702,24 @@ __global__ __launch_bounds__(kThreads) void fsum_walk(const float *terms, int64_
         Map x[kPerThread];
         int count[kPerThread];
         Map mine = identity_map();
+        // the records first, all in flight at once (a tile past the buffer's
+        // last reads the last one's record and drops it)
+        Rec rv[kPerThread];
 #pragma unroll
         for (int c = 0; c < kPerThread; ++c) {
             const int tile = t0 + me * kPerThread + c;
-            x[c] = identity_map();
-            count[c] = -1;  // past the buffer's last tile
-            if (tile < ntiles) {
-                const Rec r = rb[tile];
-                const int e0 = static_cast<int>(r.plan & 0xffffu) - 256;
-                count[c] = static_cast<int>(r.plan >> 16);
-                x[c] = (count[c] >= 1 && uexp == e0) ? r.m0 : (count[c] == 2 && uexp == e0 + 1) ? r.m1 : leaving_map();
-            }
+            rv[c] = rb[tile < ntiles ? tile : ntiles - 1];
+        }
+#pragma unroll
+        for (int c = 0; c < kPerThread; ++c) {
+            const int tile = t0 + me * kPerThread + c;
+            const Rec &r = rv[c];
+            const int e0 = static_cast<int>(r.plan & 0xffffu) - 256;
+            const int cnt = static_cast<int>(r.plan >> 16);
+            const bool in = tile < ntiles;
+            count[c] = in ? cnt : -1;  // -1: past the buffer's last tile
+            const Map y = (cnt >= 1 && uexp == e0) ? r.m0 : (cnt == 2 && uexp == e0 + 1) ? r.m1 : leaving_map();
+            x[c] = in ? y : identity_map();
             mine = compose(mine, x[c]);
         }
         Map before;
@@ -670,7 +793,8 @@ FloatSumLayout float_sum_layout(int64_t nterms, int nbuffers)
     l.bad = up(l.totals + cells * sizeof(double));
     l.recs = up(l.bad + cells * sizeof(uint32_t));
     l.buffer_bad = up(l.recs + cells * sizeof(Rec));
-    l.bytes = up(l.buffer_bad + static_cast<size_t>(nbuffers) * sizeof(uint32_t));
+    l.ordered = up(l.buffer_bad + static_cast<size_t>(nbuffers) * sizeof(uint32_t));
+    l.bytes = up(l.ordered + (1 + cells) * sizeof(uint32_t));
     return l;
 }
 
@@ -683,12 +807,22 @@ hipError_t launch_float_sums(const float *terms, int64_t nterms, int nbuffers, f
     uint32_t *bad = reinterpret_cast<uint32_t *>(ws + l.bad);
     Rec *recs = reinterpret_cast<Rec *>(ws + l.recs);
     uint32_t *buffer_bad = reinterpret_cast<uint32_t *>(ws + l.buffer_bad);
+    uint32_t *ordered = reinterpret_cast<uint32_t *>(ws + l.ordered);
+    // queue items are 32-bit tile indices (terms resident in device memory
+    // keep the tile count far below 2^32)
+    if (static_cast<int64_t>(l.ntiles) * nbuffers >= (int64_t{1} << 32))
+        return hipErrorInvalidValue;
     if (l.ntiles > 0) {
         const dim3 grid(static_cast<unsigned>(l.ntiles), static_cast<unsigned>(nbuffers));
         fsum_tile_totals<<<grid, kThreads, 0, stream>>>(terms, nterms, l.ntiles, totals, bad);
         fsum_plan<<<dim3(static_cast<unsigned>(nbuffers)), kThreads, 0, stream>>>(totals, bad, l.ntiles, recs,
-                                                                                  buffer_bad);
-        fsum_tile_maps<<<grid, kThreads, 0, stream>>>(terms, nterms, l.ntiles, recs);
+                                                                                  buffer_bad, ordered);
+        fsum_tile_maps<<<grid, kThreads, 0, stream>>>(terms, nterms, l.ntiles, recs, ordered);
+        // the queue's length is known on the device only: a grid the size of
+        // a few workgroups per CU, each taking items in turn
+        const int64_t cells = static_cast<int64_t>(l.ntiles) * nbuffers;
+        const unsigned ogrid = static_cast<unsigned>(cells < kOrderedGrid ? cells : kOrderedGrid);
+        fsum_ordered_maps<<<dim3(ogrid), kThreads, 0, stream>>>(terms, nterms, l.ntiles, recs, ordered);
     }
     fsum_walk<<<dim3(static_cast<unsigned>(nbuffers)), kThreads, 0, stream>>>(terms, nterms, l.ntiles, recs,
                                                                                buffer_bad, out);

@@ -253,7 +253,7 @@ constexpr int kFsTileTerms = kFsThreads * kFsRunTerms;
 // Workspace of the running float sums: byte offsets of its parts.
 struct FloatSumLayout {
     int ntiles;  // per buffer
-    size_t totals, bad, recs, buffer_bad, bytes;
+    size_t totals, bad, recs, buffer_bad, ordered, bytes;
 };
 FloatSumLayout float_sum_layout(int64_t nterms, int nbuffers);
 
