@@ -146,19 +146,35 @@ __device__ __forceinline__ bool bad_term(uint32_t t)
 // Ordered scan of the threads' maps (thread order = term order): returns
 // the inclusive prefix, and the exclusive one in `excl`.  All threads must
 // call it.
+// The map of the lane CTRL (a DPP row shift or row broadcast) selects
+// below this one, or the identity where there is none (ROWS: the rows that
+// receive one).
+// (Each move stays a move of its own: folded into the arithmetic that
+// follows, a move with a row mask leaves the masked rows' destination as it
+// was rather than the identity's, which compose does not tolerate.)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ Map map_below(const Map &x)
+{
+    Map y;
+    y.H = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x.H), CTRL, ROWS, 0xf, false));
+    y.td0 = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x.td0), CTRL, ROWS, 0xf, false));
+    y.td1 = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x.td1), CTRL, ROWS, 0xf, false));
+    asm volatile("" : "+v"(y.H), "+v"(y.td0), "+v"(y.td1));
+    return y;
+}
+
 __device__ __forceinline__ Map scan_maps(Map x, Map &excl)
 {
     __shared__ Map wave_total[kThreads / 64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        Map y;
-        y.H = __shfl_up(x.H, d, 64);
-        y.td0 = __shfl_up(x.td0, d, 64);
-        y.td1 = __shfl_up(x.td1, d, 64);
-        if (lane >= d)
-            x = compose(y, x);
-    }
+    // inclusive, in lane order: row_shr 1, 2, 4, 8 inside each row of 16,
+    // then row_bcast 15 (into rows 1 and 3) and 31 (into rows 2 and 3)
+    x = compose(map_below<0x111, 0xf>(x), x);
+    x = compose(map_below<0x112, 0xf>(x), x);
+    x = compose(map_below<0x114, 0xf>(x), x);
+    x = compose(map_below<0x118, 0xf>(x), x);
+    x = compose(map_below<0x142, 0xa>(x), x);
+    x = compose(map_below<0x143, 0xc>(x), x);
     Map prev;
     prev.H = __shfl_up(x.H, 1, 64);
     prev.td0 = __shfl_up(x.td0, 1, 64);
@@ -233,14 +249,40 @@ __device__ __forceinline__ void load_tile(const float *tile_base, int64_t count,
     __syncthreads();
 }
 
-// This thread's run of the tile in LDS, in the binade of unit 2^uexp.
+__device__ __forceinline__ float pow2(int e) { return __uint_as_float(static_cast<uint32_t>(e + 127) << 23); }
+
+// This thread's run of the tile in LDS, in the binade of unit 2^uexp.  Where
+// the unit scales to in binary32 and the run holds no tie and no term of
+// 2^22 units or more, h = floor(t/u + 1/2) read off binary32 (exact, as in
+// fsum_tile_maps) and summed in binary32 (exact below 2^24; a run that
+// reaches 2^24 leaves any binade, and saturates); otherwise term by term
+// in integers.
 __device__ __forceinline__ Map run_map(const uint32_t *lds, int uexp)
 {
     const uint32_t *r = lds + threadIdx.x * (kRun + 1);
+    uint32_t v[kRun];
+#pragma unroll
+    for (int j = 0; j < kRun; ++j)
+        v[j] = r[j];
+    if (uexp >= -126) {
+        const float scale = pow2(-uexp);
+        float H = 0.0f, lo = 1.0f, top = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kRun; ++j) {
+            const float x = __uint_as_float(v[j]) * scale;
+            const float y = x + 0.5f;
+            const float f = floorf(y);
+            lo = fminf(lo, y - f);
+            top = fmaxf(top, x);
+            H += f;
+        }
+        if (lo != 0.0f && top < 0x1p22f)
+            return H < 0x1p24f ? Map{static_cast<uint32_t>(H), 0u, 0u} : leaving_map();
+    }
     Map x = identity_map();
 #pragma unroll
     for (int j = 0; j < kRun; ++j)
-        x = compose(x, term_map(r[j], uexp));
+        x = compose(x, term_map(v[j], uexp));
     return x;
 }
 
@@ -422,7 +464,6 @@ __global__ __launch_bounds__(kThreads) void fsum_plan(const double *totals, cons
 // ordered path.  A sum of h that reaches 2^24 marks the tile as leaving the
 // binade: with a large term that mark may be early, which only sends the
 // walk through the tile run by run.
-__device__ __forceinline__ float pow2(int e) { return __uint_as_float(static_cast<uint32_t>(e + 127) << 23); }
 
 // grid (tiles, buffers): each planned tile's map in its one or two binades.
 __global__ __launch_bounds__(kThreads) void fsum_tile_maps(const float *terms, int64_t nterms, int ntiles,
@@ -652,8 +693,13 @@ __device__ uint32_t walk_tile(const uint32_t *lds, uint32_t S, bool one_by_one)
             } else {
                 float f = __uint_as_float(S);
                 const uint32_t *r = lds + stop * (kRun + 1);
+                float v[kRun];
+#pragma unroll
                 for (int j = 0; j < kRun; ++j)
-                    f = f + __uint_as_float(r[j]);
+                    v[j] = __uint_as_float(r[j]);
+#pragma unroll
+                for (int j = 0; j < kRun; ++j)
+                    f = f + v[j];
                 shared_S = __float_as_uint(f);
             }
         }
