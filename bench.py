@@ -81,7 +81,7 @@ VIEW_SOURCES = [os.path.join(CSRC, f) for f in ("plane_views.hip", "reduce.h")]
 HOST_SOURCES = STAGE1_SOURCES + [os.path.join(CSRC, "host_stream.hip")]
 MAPPED_SOURCES = [os.path.join(CSRC, f) for f in ("stage1_mapped.hip", "reduce.h")]
 FLOAT_SUM_SOURCES = [os.path.join(CSRC, "float_sum.hip")]
-FLOAT_SUM_KERNELS = ("fsum_tile_totals", "fsum_plan", "fsum_tile_maps", "fsum_walk")
+FLOAT_SUM_KERNELS = ("fsum_tile_totals", "fsum_plan", "fsum_tile_maps", "fsum_ordered_maps", "fsum_walk")
 CPU_ORDER_KERNELS = ("stage1_u16", "cpu_order_maps", "cpu_order_walk")
 
 
@@ -948,12 +948,18 @@ def main(argv=None):
     plane_dims = [(w, h)] if planes is None else [(pw, ph) for _, pw, ph in planes]
     itemsize = 8
 
+    # host time spent inside each step's library call (argument checks,
+    # launches): the library's own per-call cost, which bounds the step of a
+    # small batch
+    call_s = np.zeros(total, dtype=np.float64)
+
     def enqueue(i):
         s = i % nslots
         r, d = bufs[i % 2]
         o = sums_dev[s]
         st = sts[i % nst]
         ws = wss[i % nst]
+        t_call = time.perf_counter()
         if args.mode == "exact" and args.pitch:
             rc = L.vqx_plane_stats_view_ws(r.data_ptr(), rs, fs, d.data_ptr(), rs, fs, w, h, bpc, nframes,
                                            o, o + itemsize * nframes, ws.data_ptr(), ws_bytes, st)
@@ -975,6 +981,7 @@ def main(argv=None):
         else:
             rc = L.vqx_psnr_int_planes_ws(mode.plane_arrays[i % 2], len(planes), bpc, nframes, o, ws.data_ptr(),
                                           ws_bytes, st)
+        call_s[i] = time.perf_counter() - t_call
         if rc != 0:
             raise vqx.VqxError(rc, f"libvqx entry point ({args.mode})")
 
@@ -1118,6 +1125,11 @@ def main(argv=None):
             "algorithmic_bytes_per_launch": mode.alg_bytes,
         },
         "generation_s": round(t_gen, 1),
+        "host_call_us": {
+            "mean": round(float(call_s[args.warmup:].mean()) * 1e6, 1),
+            "median": round(float(np.median(call_s[args.warmup:])) * 1e6, 1),
+            "what": "host time inside the step's library call (checks and launches), timed steps",
+        },
     }
     if read_ceiling:
         out["read_ceiling"] = read_ceiling

@@ -82,7 +82,7 @@ def rows(path):
 
 def short(name: str) -> str:
     for k in ("stage1_u16_mapped", "mapped_combine", "gather_view", "stage1_u16", "stage1_u8", "stage2_combine",
-              "bitwise_not", "fsum_tile_totals", "fsum_plan", "fsum_tile_maps", "fsum_walk",
+              "bitwise_not", "fsum_tile_totals", "fsum_plan", "fsum_tile_maps", "fsum_ordered_maps", "fsum_walk",
               "cpu_order_maps", "cpu_order_walk", "views_stage1", "views_combine",
               "view_stage1", "view_combine", "read_probe"):
         if k in name:
