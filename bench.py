@@ -81,7 +81,7 @@ VIEW_SOURCES = [os.path.join(CSRC, f) for f in ("plane_views.hip", "reduce.h")]
 HOST_SOURCES = STAGE1_SOURCES + [os.path.join(CSRC, "host_stream.hip")]
 MAPPED_SOURCES = [os.path.join(CSRC, f) for f in ("stage1_mapped.hip", "reduce.h")]
 FLOAT_SUM_SOURCES = [os.path.join(CSRC, "float_sum.hip")]
-FLOAT_SUM_KERNELS = ("fsum_tile_totals", "fsum_plan", "fsum_tile_maps", "fsum_ordered_maps", "fsum_walk")
+FLOAT_SUM_KERNELS = ("fsum_tile_totals", "fsum_plan", "fsum_tile_maps", "fsum_walk")
 CPU_ORDER_KERNELS = ("stage1_u16", "cpu_order_maps", "cpu_order_walk")
 
 

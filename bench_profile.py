@@ -82,7 +82,7 @@ def rows(path):
 
 def short(name: str) -> str:
     for k in ("stage1_u16_mapped", "mapped_combine", "gather_view", "stage1_u16", "stage1_u8", "stage2_combine",
-              "bitwise_not", "fsum_tile_totals", "fsum_plan", "fsum_tile_maps", "fsum_ordered_maps", "fsum_walk",
+              "bitwise_not", "fsum_tile_totals", "fsum_plan", "fsum_tile_maps", "fsum_walk",
               "cpu_order_maps", "cpu_order_walk", "views_stage1", "views_combine",
               "view_stage1", "view_combine", "read_probe"):
         if k in name:
@@ -218,9 +218,31 @@ def kernel_trace(args, trace_cmd, steps, warmup, title, outname, step_kernels, s
                       f"{kname}_max_us_timed_dispatches: {max(timed):.2f}"]
     if len(timed_avg) == len(step_kernels):
         step_us = sum(timed_avg[k] * per_step[k] for k in step_kernels)
+        how = "  (sum of the step's kernels)" if len(step_kernels) > 1 else ""
+        if len(step_kernels) > 1:
+            # kernels of a step may run at once on two streams: the step is
+            # the span from its first kernel's start to its last one's end
+            disp = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), short(r["Kernel_Name"]))
+                          for r in trace if short(r["Kernel_Name"]) in step_kernels)
+            spans, cur = [], None
+            for b, e, kname in disp:
+                if kname == step_kernels[0]:
+                    if cur:
+                        spans.append(cur[1] - cur[0])
+                    cur = [b, e]
+                elif cur:
+                    cur[1] = max(cur[1], e)
+            if cur:
+                spans.append(cur[1] - cur[0])
+            spans = [x / 1e3 for x in spans[warmup:]]
+            if spans:
+                step_us = statistics.fmean(spans)
+                how = "  (per step, the first kernel's start to the last kernel's end)"
+                lines += ["", f"step_span_us_timed_steps: mean {step_us:.2f}, median "
+                              f"{statistics.median(spans):.2f}, min {min(spans):.2f}, max {max(spans):.2f} "
+                              f"over {len(spans)} steps"]
         gbs = alg / (step_us * 1e-6) / 1e9
-        lines += ["", f"kernel_avg_us: {step_us:.2f}" + ("  (sum of the step's kernels)" if len(step_kernels) > 1
-                                                         else ""),
+        lines += ["", f"kernel_avg_us: {step_us:.2f}" + how,
                   f"kernel_algorithmic_bytes_per_launch: {alg}",
                   f"kernel_achieved_GBps: {gbs:.1f}", f"kernel_frac_of_8000_GBps: {gbs / 8000:.4f}"]
     if bench_line:

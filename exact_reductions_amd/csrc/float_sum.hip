@@ -33,17 +33,31 @@
 //  2. fsum_plan, per buffer: the running total at each tile start, which
 //     predicts the binade the float sum is in there, with a margin;
 //  3. fsum_tile_maps: each tile's map in the predicted binade (and the
-//     next, where the tile may cross into it);
-//  4. fsum_walk, one workgroup per buffer: with the running value S, scans
-//     up to 256 tile maps at once for S's binade and applies all of them up
-//     to the first tile that has no map for that binade or whose map leaves
-//     it; that tile is taken as 256 runs of 16 terms, scanned the same way,
-//     and the run where S leaves its binade is added term by term in
-//     binary32.  Every step is checked against S itself, so a prediction
-//     decides only how fast the walk is, never what it returns.
+//     next, where the tile may cross into it), tiles handed out across the
+//     buffers so that all buffers' maps appear at one pace; a tile with a
+//     tie or a large term goes on a queue instead;
+//  4. fsum_walk: one workgroup per buffer walks it -- with the running
+//     value S, scans up to 1024 tile maps at once for S's binade and
+//     applies all of them up to the first tile that has no map for that
+//     binade or whose map leaves it; that tile is taken as 256 runs of 16
+//     terms, scanned the same way, and the run where S leaves its binade is
+//     added term by term in binary32 -- while further workgroups take the
+//     queue's tiles and make their maps term by term, in order.  Every step
+//     is checked against S itself, so a prediction decides only how fast
+//     the walk is, never what it returns.
+//
+// Step 4 runs on a second stream while step 3 still makes the maps: each
+// map is published in 64-bit words that carry their own "ready" bit,
+// written and read with relaxed device-scope atomics (single-copy atomic
+// and coherent across the XCDs' L2s, so no fence is needed: a word is
+// either seen whole or seen as not ready).  A walk waits at a tile whose
+// map is not out yet; its waits are bounded, and past the bound it adds
+// such a tile from its terms, which needs no map.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <cstdlib>
 
 #include "plane_stats.h"
 
@@ -69,13 +83,67 @@ struct Map {
     uint32_t H, td0, td1;
 };
 
-// A tile's record: its plan (binades predicted) and its map in each.
+// A tile's record: its plan (binades predicted) and its maps, published.
+//   w0: bit 63 ready, bit 62 queued (the maps come from the ordered path,
+//       not out yet), bits 61..60 the count of planned binades (0..2),
+//       bits 59..52 the first binade's unit exponent + 149, bits 51..0 the
+//       map in the first binade;
+//   w1: bit 63 ready, bits 51..0 the map in the second binade.
+// A map is H (bits 25..0, at most kSat), td0 (38..26) and td1 (51..39);
+// td0, td1 count ties, at most a tile's 4096 terms.
 struct alignas(32) Rec {
+    uint64_t w0, w1;
     uint32_t plan;  // (unit exponent of the first binade + 256) | (count << 16), count 0..2
-    Map m0, m1;     // maps in the first and the second planned binade
-    uint32_t unused;
+    uint32_t unused[3];
 };
-static_assert(sizeof(Rec) == 32, "two 16-byte loads per record");
+static_assert(sizeof(Rec) == 32, "records stay 32 bytes");
+
+constexpr uint64_t kReady = 1ull << 63;
+constexpr uint64_t kQueued = 1ull << 62;
+
+__device__ __forceinline__ uint64_t pack_map(const Map &m)
+{
+    return static_cast<uint64_t>(m.H) | (static_cast<uint64_t>(m.td0) << 26) | (static_cast<uint64_t>(m.td1) << 39);
+}
+
+__device__ __forceinline__ Map unpack_map(uint64_t w)
+{
+    return {static_cast<uint32_t>(w) & 0x3ffffffu, static_cast<uint32_t>(w >> 26) & 0x1fffu,
+            static_cast<uint32_t>(w >> 39) & 0x1fffu};
+}
+
+// w0's fields other than the map
+__device__ __forceinline__ uint64_t rec_head(int count, int uexp)
+{
+    return (static_cast<uint64_t>(count) << 60) | (static_cast<uint64_t>(uexp + 149) << 52);
+}
+
+// Publication and observation of a record word (relaxed, device scope).
+__device__ __forceinline__ void publish(uint64_t *p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t observe(const uint64_t *p)
+{
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void publish(uint32_t *p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t observe(const uint32_t *p)
+{
+    return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The ordered-path queue: queue[0] counts the items taken, queue[1] the
+// walks beside the maps that have ended, queue[2] those of them that gave
+// up, and item k is queue[3 + k] = (buffer * ntiles + tile) + 1, 0 until it
+// is written.
+constexpr int kQueueHead = 3;
 
 __device__ __forceinline__ Map identity_map() { return {0u, 0u, 0u}; }
 __device__ __forceinline__ Map leaving_map() { return {kSat, 0u, 0u}; }
@@ -371,9 +439,11 @@ __device__ __forceinline__ void workgroup_sum_or(float &s, uint32_t &o)
 // grid (tiles, buffers): each tile's total (binary32 adds in any order: a
 // prediction only) and whether any term is negative or not finite.
 __global__ __launch_bounds__(kThreads) void fsum_tile_totals(const float *terms, int64_t nterms, int ntiles,
-                                                             double *totals, uint32_t *bad)
+                                                             double *totals, uint32_t *bad, uint32_t *queue)
 {
     const int tile = blockIdx.x, buf = blockIdx.y;
+    if (threadIdx.x == 0)
+        queue[kQueueHead + static_cast<int64_t>(buf) * ntiles + tile] = 0;  // one queue slot per tile
     const int64_t first = static_cast<int64_t>(tile) * kTile;
     float s = 0.0f;
     uint32_t b = 0;
@@ -409,8 +479,11 @@ __global__ __launch_bounds__(kThreads) void fsum_plan(const double *totals, cons
                                                       Rec *recs, uint32_t *buffer_bad, uint32_t *ordered)
 {
     const int buf = blockIdx.x;
-    if (buf == 0 && threadIdx.x == 0)
+    if (buf == 0 && threadIdx.x == 0) {
         ordered[0] = 0;  // the ordered-path queue, filled by fsum_tile_maps
+        ordered[1] = 0;
+        ordered[2] = 0;
+    }
     const double *tot = totals + static_cast<int64_t>(buf) * ntiles;
     const uint32_t *bd = bad + static_cast<int64_t>(buf) * ntiles;
     Rec *rc = recs + static_cast<int64_t>(buf) * ntiles;
@@ -444,7 +517,11 @@ __global__ __launch_bounds__(kThreads) void fsum_plan(const double *totals, cons
         const int e_lo = unit_exponent_of(p * (1.0 - kMargin));
         const int e_hi = unit_exponent_of((p + tot[i]) * (1.0 + kMargin));
         const int n = e_hi - e_lo + 1;
-        rc[i].plan = static_cast<uint32_t>(e_lo + 256) | (static_cast<uint32_t>(n <= 2 ? n : 0) << 16);
+        const int count = n <= 2 ? n : 0;
+        rc[i].plan = static_cast<uint32_t>(e_lo + 256) | (static_cast<uint32_t>(count) << 16);
+        // a tile without maps is ready now; the others once their maps are
+        rc[i].w0 = count == 0 ? kReady | rec_head(0, e_lo) : 0;
+        rc[i].w1 = 0;
         p += tot[i];
     }
     __syncthreads();
@@ -465,11 +542,15 @@ __global__ __launch_bounds__(kThreads) void fsum_plan(const double *totals, cons
 // binade: with a large term that mark may be early, which only sends the
 // walk through the tile run by run.
 
-// grid (tiles, buffers): each planned tile's map in its one or two binades.
+// One workgroup per tile, handed out tile by tile across the buffers (tile
+// 0 of every buffer, then tile 1, ...): each planned tile's map in its one
+// or two binades, published.
 __global__ __launch_bounds__(kThreads) void fsum_tile_maps(const float *terms, int64_t nterms, int ntiles,
-                                                           Rec *recs, uint32_t *ordered)
+                                                           int nbuffers, Rec *recs, uint32_t *ordered)
 {
-    const int tile = blockIdx.x, buf = blockIdx.y;
+    const uint32_t cell = blockIdx.x;
+    const int tile = static_cast<int>(cell / static_cast<uint32_t>(nbuffers));
+    const int buf = static_cast<int>(cell - static_cast<uint32_t>(tile) * static_cast<uint32_t>(nbuffers));
     const int64_t at = static_cast<int64_t>(buf) * ntiles + tile;
     const int64_t first = static_cast<int64_t>(tile) * kTile;
     const float *tb = terms + static_cast<int64_t>(buf) * nterms + first;
@@ -527,61 +608,54 @@ __global__ __launch_bounds__(kThreads) void fsum_tile_maps(const float *terms, i
     }
     __syncthreads();
     // a tile that needs the ordered path in any of its binades goes on the
-    // queue of fsum_ordered_maps, which writes all its maps
+    // queue, whose takers write all its maps; until then its record says so
     if (flags & 3u) {
-        if (threadIdx.x == 0)
-            ordered[1 + atomicAdd(&ordered[0], 1u)] = static_cast<uint32_t>(at);
+        if (threadIdx.x == 0) {
+            publish(&recs[at].w0, kReady | kQueued | rec_head(n, uexp));
+            publish(&ordered[kQueueHead + atomicAdd(&ordered[0], 1u)], static_cast<uint32_t>(at) + 1u);
+        }
         return;
     }
     if (threadIdx.x == 0) {
+        Map m[2];
         for (int k = 0; k < n; ++k) {
-            Map m;
             if (flags & (4u << k)) {
-                m = leaving_map();
+                m[k] = leaving_map();
             } else {
                 uint32_t h = 0;
 #pragma unroll
                 for (int w = 0; w < kThreads / 64; ++w)
                     h += lh[k][w];
-                m = {h > kSat ? kSat : h, 0u, 0u};
+                m[k] = {h > kSat ? kSat : h, 0u, 0u};
             }
-            if (k == 0)
-                recs[at].m0 = m;
-            else
-                recs[at].m1 = m;
         }
+        if (n == 2)
+            publish(&recs[at].w1, kReady | pack_map(m[1]));
+        publish(&recs[at].w0, kReady | rec_head(n, uexp) | pack_map(m[0]));
     }
 }
 
-// The queued tiles' maps in their planned binades, in order, term by term
-// (ties, large terms, or a unit too small to scale to): a fixed grid of
-// workgroups takes the queue's items in turn.  ordered[0] is the queue's
-// length, zeroed by fsum_plan; items (buffer * ntiles + tile) follow.
-__global__ __launch_bounds__(kThreads) void fsum_ordered_maps(const float *terms, int64_t nterms, int ntiles,
-                                                              Rec *recs, const uint32_t *ordered)
+// A queued tile's maps in its planned binades, in order, term by term
+// (ties, large terms, or a unit too small to scale to), published.  All
+// threads must call it.
+__device__ void ordered_maps(const float *terms, int64_t nterms, int ntiles, Rec *recs, uint32_t at, uint32_t *lds)
 {
-    __shared__ uint32_t lds[kPad];
-    const uint32_t count = ordered[0];
-    for (uint32_t i = blockIdx.x; i < count; i += gridDim.x) {
-        const uint32_t at = ordered[1 + i];
-        const int buf = static_cast<int>(at / static_cast<uint32_t>(ntiles));
-        const int tile = static_cast<int>(at - static_cast<uint32_t>(buf) * static_cast<uint32_t>(ntiles));
-        const uint32_t pl = recs[at].plan;
-        const int n = static_cast<int>(pl >> 16);
-        const int uexp = static_cast<int>(pl & 0xffffu) - 256;
-        const int64_t first = static_cast<int64_t>(tile) * kTile;
-        load_tile(terms + static_cast<int64_t>(buf) * nterms + first, nterms - first, lds);
-        for (int k = 0; k < n; ++k) {
-            const Map m = reduce_maps(run_map(lds, uexp + k));
-            if (threadIdx.x == 0) {
-                if (k == 0)
-                    recs[at].m0 = m;
-                else
-                    recs[at].m1 = m;
-            }
-        }
-        __syncthreads();  // before the next item overwrites the LDS
+    const int buf = static_cast<int>(at / static_cast<uint32_t>(ntiles));
+    const int tile = static_cast<int>(at - static_cast<uint32_t>(buf) * static_cast<uint32_t>(ntiles));
+    const uint32_t pl = recs[at].plan;
+    const int n = static_cast<int>(pl >> 16);
+    const int uexp = static_cast<int>(pl & 0xffffu) - 256;
+    const int64_t first = static_cast<int64_t>(tile) * kTile;
+    load_tile(terms + static_cast<int64_t>(buf) * nterms + first, nterms - first, lds);
+    Map m[2];
+    for (int k = 0; k < n; ++k)
+        m[k] = reduce_maps(run_map(lds, uexp + k));
+    if (threadIdx.x == 0) {
+        if (n == 2)
+            publish(&recs[at].w1, kReady | pack_map(m[1]));
+        publish(&recs[at].w0, kReady | rec_head(n, uexp) | pack_map(m[0]));
     }
+    __syncthreads();  // before the next item overwrites the LDS
 }
 
 // ------------------------------------------------------------- kernel 4
@@ -711,120 +785,267 @@ __device__ uint32_t walk_tile(const uint32_t *lds, uint32_t S, bool one_by_one)
     return S;
 }
 
-// Workgroups of fsum_ordered_maps.
-constexpr int64_t kOrderedGrid = 1024;
+// Workgroups of the walk kernel that take the queue's items.
+constexpr int kTakers = 64;
 
 // One workgroup per buffer.  A window is kWindow tiles, kPerThread
 // consecutive ones per thread.
 constexpr int kPerThread = 4;
 constexpr int kWindow = kThreads * kPerThread;
 
-__global__ __launch_bounds__(kThreads) void fsum_walk(const float *terms, int64_t nterms, int ntiles,
-                                                      const Rec *recs, const uint32_t *buffer_bad, float *out)
+// The walk waits where a map is not out yet.  While it waits one lane
+// looks at the tile's record and at one kAhead tiles on (the map kernel
+// hands tiles out in order, so most of the tiles between are out by then),
+// every kNap (s_sleep units of 64 clocks); a taker of the queue does the
+// same for the queue's next item.  Beside the map kernel a wait gets new
+// maps within microseconds; one that lasts kWaitBound (wall clock ticks,
+// 100 MHz) means the map kernel is not running beside it (a tool or a
+// graph that runs the two streams' kernels one after the other): the walk
+// gives up its buffer, which the walk after the map kernel takes.  There, a
+// wait that long makes the walk add a tile without its map from the tile's
+// terms (which needs no map) instead.
+constexpr int kAhead = 128;
+constexpr int kNap = 16;
+constexpr uint64_t kWaitBound = 100000;  // 1 ms, unless VQX_FLOAT_SUM_WAIT_TICKS sets it
+
+// The queue's takers beside the map kernel: workgroup nbuffers + j takes
+// items j, j + kTakers, ... as fsum_tile_maps writes them, until every walk
+// beside it has ended.
+__device__ void take_queue(const float *terms, int64_t nterms, int ntiles, int nbuffers, Rec *recs,
+                           uint32_t *queue, uint64_t wait_bound, uint32_t *lds)
 {
-    const int buf = blockIdx.x;
+    __shared__ uint32_t shared_item;
+    const uint32_t cells = static_cast<uint32_t>(ntiles) * static_cast<uint32_t>(nbuffers);
+    for (uint32_t i = blockIdx.x - static_cast<uint32_t>(nbuffers);; i += kTakers) {
+        if (threadIdx.x == 0) {
+            uint32_t item = 0;
+            const uint64_t start = wall_clock64();
+            for (;;) {
+                item = i < cells ? observe(&queue[kQueueHead + i]) : 0u;
+                if (item != 0 || observe(&queue[1]) == static_cast<uint32_t>(nbuffers) ||
+                    wall_clock64() - start > wait_bound)
+                    break;
+                __builtin_amdgcn_s_sleep(kNap);
+            }
+            shared_item = item;
+        }
+        __syncthreads();
+        const uint32_t item = shared_item;
+        __syncthreads();
+        if (item == 0)
+            return;  // every walk beside the map kernel has ended (or the bound is reached)
+        ordered_maps(terms, nterms, ntiles, recs, item - 1u, lds);
+    }
+}
+
+// The queue's takers after the map kernel, where a walk gave up its buffer
+// (or all walk there): the queued tiles whose maps are not out.
+__device__ void take_rest(const float *terms, int64_t nterms, int ntiles, int nbuffers, Rec *recs,
+                          const uint32_t *queue, bool all, uint32_t *lds)
+{
+    if (!all && queue[2] == 0)
+        return;  // every walk beside the map kernel finished its buffer
+    const uint32_t count = queue[0];
+    for (uint32_t i = blockIdx.x - static_cast<uint32_t>(nbuffers); i < count; i += kTakers) {
+        const uint32_t at = queue[kQueueHead + i] - 1u;
+        if (observe(&recs[at].w0) & kQueued)
+            ordered_maps(terms, nterms, ntiles, recs, at, lds);
+    }
+}
+
+// Workgroups 0 .. nbuffers-1: one per buffer, the buffer's running sum
+// into out[buf]; then kTakers takers of the queue (none where there are no
+// tiles).  wait_bound: kWaitBound, or as set.  live: beside
+// fsum_tile_maps, on the second stream; each walk
+// sets done[buf] to 1 where it wrote out[buf], to 0 where it gave up.
+// Otherwise after fsum_tile_maps: the buffers whose done is 0 (all of them
+// where done is null).
+__global__ __launch_bounds__(kThreads) void fsum_walk(const float *terms, int64_t nterms, int ntiles, int nbuffers,
+                                                      Rec *recs, const uint32_t *buffer_bad, uint32_t *queue,
+                                                      uint32_t *done, float *out, int live, uint64_t wait_bound)
+{
     __shared__ uint32_t lds[kPad];
-    __shared__ uint32_t shared_S, shared_how;
+    if (static_cast<int>(blockIdx.x) >= nbuffers) {
+        if (live)
+            take_queue(terms, nterms, ntiles, nbuffers, recs, queue, wait_bound, lds);
+        else
+            take_rest(terms, nterms, ntiles, nbuffers, recs, queue, done == nullptr, lds);
+        return;
+    }
+    if (!live && done && done[blockIdx.x])
+        return;  // walked beside the map kernel
+    const int buf = blockIdx.x;
+    // beside the map kernel, this workgroup's few waves share each SIMD
+    // with its: it issues first, since the buffer's result waits on it
+    __builtin_amdgcn_s_setprio(3);
+    __shared__ uint32_t shared_S, shared_how, shared_late;
     const float *tb = terms + static_cast<int64_t>(buf) * nterms;
-    if (ntiles == 0) {  // no terms: the accumulator's +0
-        if (threadIdx.x == 0)
-            out[buf] = 0.0f;
-        return;
-    }
-    if (buffer_bad[buf]) {
-        if (threadIdx.x == 0)
-            out[buf] = __uint_as_float(kNaN);
-        return;
-    }
     const Rec *rb = recs + static_cast<int64_t>(buf) * ntiles;
     const int me = static_cast<int>(threadIdx.x);
-    uint32_t S = 0;  // +0
+    uint32_t S = 0;  // +0, the accumulator's start (and the sum of no terms)
+    if (ntiles > 0 && buffer_bad[buf])
+        S = kNaN;
     int t0 = 0;
-    while (t0 < ntiles && S != kInf) {
-        int uexp;
-        uint32_t m0;
-        split(S, uexp, m0);
-        // this thread's tiles of the window, as maps in S's binade
-        Map x[kPerThread];
-        int count[kPerThread];
-        Map mine = identity_map();
-        // the records first, all in flight at once (a tile past the buffer's
-        // last reads the last one's record and drops it)
-        Rec rv[kPerThread];
+    bool patient = true;   // waits allowed (after the map kernel: the bound not reached)
+    bool gave_up = false;  // beside it: a wait reached the bound
+    while (t0 < ntiles && S != kInf && S != kNaN) {
+        // the window's records, read once: this thread's tiles are
+        // t0 + me*kPerThread + c (a tile past the buffer's last reads the
+        // last one's record and drops it)
+        uint64_t w0[kPerThread], w1[kPerThread];
 #pragma unroll
         for (int c = 0; c < kPerThread; ++c) {
             const int tile = t0 + me * kPerThread + c;
-            rv[c] = rb[tile < ntiles ? tile : ntiles - 1];
+            const Rec &r = rb[tile < ntiles ? tile : ntiles - 1];
+            w0[c] = observe(&r.w0);
+            w1[c] = observe(&r.w1);
         }
-#pragma unroll
-        for (int c = 0; c < kPerThread; ++c) {
-            const int tile = t0 + me * kPerThread + c;
-            const Rec &r = rv[c];
-            const int e0 = static_cast<int>(r.plan & 0xffffu) - 256;
-            const int cnt = static_cast<int>(r.plan >> 16);
-            const bool in = tile < ntiles;
-            count[c] = in ? cnt : -1;  // -1: past the buffer's last tile
-            const Map y = (cnt >= 1 && uexp == e0) ? r.m0 : (cnt == 2 && uexp == e0 + 1) ? r.m1 : leaving_map();
-            x[c] = in ? y : identity_map();
-            mine = compose(mine, x[c]);
-        }
-        Map before;
-        (void)scan_maps(mine, before);
-        // walk this thread's tiles from m at its first one
-        uint32_t m = apply(before, m0);
-        int local = kPerThread;  // this thread's first tile that stops (none)
-        uint32_t after = 0;
-        if (m < kTop) {
+        const int wend = ntiles - t0 < kWindow ? ntiles : t0 + kWindow;
+        const bool walk_queued = !patient;  // otherwise queued tiles wait for their takers
+        int lo = t0;          // the window's tiles before lo are added
+        int wait_at = -1;     // a tile whose map is not out yet: wait, then read again from there
+        while (lo < wend && S != kInf) {
+            int uexp;
+            uint32_t m0;
+            split(S, uexp, m0);
+            Map x[kPerThread];
+            int count[kPerThread];
+            uint32_t late = 0;  // tiles whose map is not out yet
+            Map mine = identity_map();
 #pragma unroll
             for (int c = 0; c < kPerThread; ++c) {
-                if (local == kPerThread && count[c] >= 0) {
-                    const uint32_t a = apply(x[c], m);
-                    if (a >= kTop) {
-                        local = c;
-                        after = a;
-                    } else {
-                        m = a;
+                const int tile = t0 + me * kPerThread + c;
+                const bool in = tile >= lo && tile < wend;
+                const uint64_t a = w0[c];
+                const bool ready = (a & kReady) != 0, queued = (a & kQueued) != 0;
+                const int cnt = static_cast<int>((a >> 60) & 3u);
+                const int e0 = static_cast<int>((a >> 52) & 0xffu) - 149;
+                // no map for S's binade: the tile stops the scan and is
+                // added from its terms
+                Map y = leaving_map();
+                bool wait = !ready || (queued && !walk_queued);
+                if (ready && !queued) {
+                    if (cnt >= 1 && uexp == e0) {
+                        y = unpack_map(a);
+                    } else if (cnt == 2 && uexp == e0 + 1) {
+                        if (w1[c] & kReady)
+                            y = unpack_map(w1[c]);
+                        else
+                            wait = true;
+                    }
+                }
+                wait = wait && patient;
+                late |= (in && wait) ? (1u << c) : 0u;
+                count[c] = in ? (ready ? cnt : 1) : -1;  // -1: not in this pass
+                x[c] = in ? y : identity_map();
+                mine = compose(mine, x[c]);
+            }
+            Map before;
+            (void)scan_maps(mine, before);
+            // walk this thread's tiles from m at its first one
+            uint32_t m = apply(before, m0);
+            int local = kPerThread;  // this thread's first tile that stops (none)
+            uint32_t after = 0;
+            if (m < kTop) {
+#pragma unroll
+                for (int c = 0; c < kPerThread; ++c) {
+                    if (local == kPerThread && count[c] >= 0) {
+                        const uint32_t a = apply(x[c], m);
+                        if (a >= kTop) {
+                            local = c;
+                            after = a;
+                        } else {
+                            m = a;
+                        }
                     }
                 }
             }
-        }
-        const int stop = first_set(local < kPerThread);
-        if (stop == kThreads) {
-            // no tile of the window stops: S after its last tile
-            const int last = (ntiles - t0 < kWindow ? ntiles - t0 : kWindow) - 1;
-            if (me == last / kPerThread)
+            const int stop = first_set(local < kPerThread);
+            if (stop == kThreads) {
+                // no tile of the pass stops: S after the window's last tile
+                if (me == (wend - 1 - t0) / kPerThread)
+                    shared_S = join(uexp, m);
+                __syncthreads();
+                S = shared_S;
+                __syncthreads();
+                lo = wend;
+                break;
+            }
+            // S before the stopping tile; that tile has no map out yet (wait
+            // for it), reaches the binade's top exactly (applied whole), or
+            // has no map for S's binade or leaves it (walked run by run, or
+            // term by term where the plan found it may cross more than two
+            // binades)
+            if (me == stop) {
                 shared_S = join(uexp, m);
+                shared_how = static_cast<uint32_t>(local) | (after == kTop ? 0x100u : 0u) |
+                             (count[local] == 0 ? 0x200u : 0u) | (((late >> local) & 1u) ? 0x400u : 0u);
+            }
             __syncthreads();
             S = shared_S;
+            const uint32_t how = shared_how;
             __syncthreads();
-            t0 += last + 1;
-            continue;
+            const int tile = t0 + stop * kPerThread + static_cast<int>(how & 0xffu);
+            lo = tile;
+            if (how & 0x400u) {
+                wait_at = tile;
+                break;
+            }
+            if (how & 0x100u) {
+                S = join(uexp, kTop);
+            } else {
+                const int64_t first = static_cast<int64_t>(tile) * kTile;
+                load_tile(tb + first, nterms - first, lds);
+                S = walk_tile(lds, S, (how & 0x200u) != 0);
+            }
+            lo = tile + 1;
         }
-        // S before the stopping tile; that tile reaches the binade's top
-        // exactly (applied whole), or has no map for S's binade or leaves
-        // it (walked run by run, or term by term where the plan found it
-        // may cross more than two binades)
-        if (me == stop) {
-            shared_S = join(uexp, m);
-            shared_how = static_cast<uint32_t>(local) | (after == kTop ? 0x100u : 0u) |
-                         (count[local] == 0 ? 0x200u : 0u);
+        if (wait_at >= 0) {
+            // one lane waits, within the bound, until the tile's maps are
+            // out (its queued mark gone, where queued tiles are waited for)
+            // and the record kAhead tiles on (or the last) is written; the
+            // workgroup then reads the window again
+            if (me == 0) {
+                const int probe = wait_at + kAhead < ntiles ? wait_at + kAhead : ntiles - 1;
+                auto maps_out = [&]() {
+                    const uint64_t a = observe(&rb[wait_at].w0);
+                    if (!(a & kReady) || ((a & kQueued) && !walk_queued))
+                        return false;
+                    if (((a >> 60) & 3u) == 2u && !(a & kQueued) && !(observe(&rb[wait_at].w1) & kReady))
+                        return false;
+                    return (observe(&rb[probe].w0) & kReady) != 0;
+                };
+                const uint64_t start = wall_clock64();
+                bool out_yet = maps_out();
+                while (!out_yet && wall_clock64() - start <= wait_bound) {
+                    __builtin_amdgcn_s_sleep(kNap);
+                    out_yet = maps_out();
+                }
+                shared_late = out_yet ? 0u : 1u;
+            }
+            __syncthreads();
+            const bool bound = shared_late != 0;
+            __syncthreads();
+            if (bound) {
+                if (live) {
+                    gave_up = true;
+                    break;
+                }
+                patient = false;  // from here on, tiles without maps are added from their terms
+            }
         }
-        __syncthreads();
-        S = shared_S;
-        const uint32_t how = shared_how;
-        __syncthreads();
-        const int tile = t0 + stop * kPerThread + static_cast<int>(how & 0xffu);
-        if (how & 0x100u) {
-            S = join(uexp, kTop);
-        } else {
-            const int64_t first = static_cast<int64_t>(tile) * kTile;
-            load_tile(tb + first, nterms - first, lds);
-            S = walk_tile(lds, S, (how & 0x200u) != 0);
-        }
-        t0 = tile + 1;
+        t0 = lo;
     }
-    if (threadIdx.x == 0)
-        out[buf] = __uint_as_float(S);
+    if (threadIdx.x == 0) {
+        if (!gave_up)
+            out[buf] = __uint_as_float(S);
+        if (live) {
+            done[buf] = gave_up ? 0u : 1u;
+            if (gave_up)
+                atomicAdd(&queue[2], 1u);
+            atomicAdd(&queue[1], 1u);  // the takers beside the map kernel stop once every walk has ended
+        }
+    }
 }
 
 }  // namespace
@@ -839,13 +1060,14 @@ FloatSumLayout float_sum_layout(int64_t nterms, int nbuffers)
     l.bad = up(l.totals + cells * sizeof(double));
     l.recs = up(l.bad + cells * sizeof(uint32_t));
     l.buffer_bad = up(l.recs + cells * sizeof(Rec));
-    l.ordered = up(l.buffer_bad + static_cast<size_t>(nbuffers) * sizeof(uint32_t));
-    l.bytes = up(l.ordered + (1 + cells) * sizeof(uint32_t));
+    l.done = up(l.buffer_bad + static_cast<size_t>(nbuffers) * sizeof(uint32_t));
+    l.ordered = up(l.done + static_cast<size_t>(nbuffers) * sizeof(uint32_t));
+    l.bytes = up(l.ordered + (kQueueHead + cells) * sizeof(uint32_t));
     return l;
 }
 
 hipError_t launch_float_sums(const float *terms, int64_t nterms, int nbuffers, float *out, void *workspace,
-                             hipStream_t stream)
+                             hipStream_t stream, const SideStream *side)
 {
     const FloatSumLayout l = float_sum_layout(nterms, nbuffers);
     char *ws = static_cast<char *>(workspace);
@@ -853,25 +1075,64 @@ hipError_t launch_float_sums(const float *terms, int64_t nterms, int nbuffers, f
     uint32_t *bad = reinterpret_cast<uint32_t *>(ws + l.bad);
     Rec *recs = reinterpret_cast<Rec *>(ws + l.recs);
     uint32_t *buffer_bad = reinterpret_cast<uint32_t *>(ws + l.buffer_bad);
+    uint32_t *done = reinterpret_cast<uint32_t *>(ws + l.done);
     uint32_t *ordered = reinterpret_cast<uint32_t *>(ws + l.ordered);
-    // queue items are 32-bit tile indices (terms resident in device memory
-    // keep the tile count far below 2^32)
-    if (static_cast<int64_t>(l.ntiles) * nbuffers >= (int64_t{1} << 32))
+    // queue items and the map grid's workgroups are counted in 32 bits
+    // (terms resident in device memory keep the tile count far below 2^32)
+    const int64_t cells = static_cast<int64_t>(l.ntiles) * nbuffers;
+    if (cells >= (int64_t{1} << 32))
         return hipErrorInvalidValue;
+    // the bound of one wait of the walk (wall clock ticks of 10 ns); 0 makes
+    // the walk beside the map kernel give every buffer to the walk after it
+    uint64_t bound = kWaitBound;
+    if (const char *e = std::getenv("VQX_FLOAT_SUM_WAIT_TICKS")) {
+        char *end = nullptr;
+        const unsigned long long v = std::strtoull(e, &end, 10);
+        if (end != e && *end == '\0' && v <= 100000000ull)  // at most one second
+            bound = v;
+    }
     if (l.ntiles > 0) {
         const dim3 grid(static_cast<unsigned>(l.ntiles), static_cast<unsigned>(nbuffers));
-        fsum_tile_totals<<<grid, kThreads, 0, stream>>>(terms, nterms, l.ntiles, totals, bad);
+        fsum_tile_totals<<<grid, kThreads, 0, stream>>>(terms, nterms, l.ntiles, totals, bad, ordered);
         fsum_plan<<<dim3(static_cast<unsigned>(nbuffers)), kThreads, 0, stream>>>(totals, bad, l.ntiles, recs,
                                                                                   buffer_bad, ordered);
-        fsum_tile_maps<<<grid, kThreads, 0, stream>>>(terms, nterms, l.ntiles, recs, ordered);
-        // the queue's length is known on the device only: a grid the size of
-        // a few workgroups per CU, each taking items in turn
-        const int64_t cells = static_cast<int64_t>(l.ntiles) * nbuffers;
-        const unsigned ogrid = static_cast<unsigned>(cells < kOrderedGrid ? cells : kOrderedGrid);
-        fsum_ordered_maps<<<dim3(ogrid), kThreads, 0, stream>>>(terms, nterms, l.ntiles, recs, ordered);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess)
+            return err;
+        // the fork: the walk beside the maps starts once the plan is out
+        if (side) {
+            err = hipEventRecord(side->fork, stream);
+            if (err != hipSuccess)
+                return err;
+        }
+        fsum_tile_maps<<<dim3(static_cast<unsigned>(cells)), kThreads, 0, stream>>>(terms, nterms, l.ntiles,
+                                                                                    nbuffers, recs, ordered);
+        err = hipGetLastError();
+        if (err != hipSuccess)
+            return err;
+        // enqueued after the map kernel, so that where the two streams
+        // share one hardware queue the walk simply follows it
+        if (side) {
+            err = hipStreamWaitEvent(side->stream, side->fork, 0);
+            if (err != hipSuccess)
+                return err;
+            fsum_walk<<<dim3(static_cast<unsigned>(nbuffers + kTakers)), kThreads, 0, side->stream>>>(
+                terms, nterms, l.ntiles, nbuffers, recs, buffer_bad, ordered, done, out, 1, bound);
+            err = hipGetLastError();
+            if (err == hipSuccess)
+                err = hipEventRecord(side->join, side->stream);
+            if (err == hipSuccess)
+                err = hipStreamWaitEvent(stream, side->join, 0);
+            if (err != hipSuccess)
+                return err;
+        }
     }
-    fsum_walk<<<dim3(static_cast<unsigned>(nbuffers)), kThreads, 0, stream>>>(terms, nterms, l.ntiles, recs,
-                                                                               buffer_bad, out);
+    // after the map kernel on the caller's stream: the buffers the walk
+    // beside it gave up, or all; with no tiles, the walks alone (each
+    // writes +0) and no takers
+    const bool beside = l.ntiles > 0 && side;
+    fsum_walk<<<dim3(static_cast<unsigned>(l.ntiles > 0 ? nbuffers + kTakers : nbuffers)), kThreads, 0, stream>>>(
+        terms, nterms, l.ntiles, nbuffers, recs, buffer_bad, ordered, beside ? done : nullptr, out, 0, bound);
     return hipGetLastError();
 }
 

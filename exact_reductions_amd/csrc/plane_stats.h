@@ -253,14 +253,24 @@ constexpr int kFsTileTerms = kFsThreads * kFsRunTerms;
 // Workspace of the running float sums: byte offsets of its parts.
 struct FloatSumLayout {
     int ntiles;  // per buffer
-    size_t totals, bad, recs, buffer_bad, ordered, bytes;
+    size_t totals, bad, recs, buffer_bad, done, ordered, bytes;
 };
 FloatSumLayout float_sum_layout(int64_t nterms, int nbuffers);
 
+// A second stream on the device, with two events, on which the walk runs
+// while the tile maps are still being made (fork: after the plan; join:
+// the caller's stream waits for the walk).  The caller keeps other users
+// off it for the length of one launch_float_sums call.
+struct SideStream {
+    hipStream_t stream;
+    hipEvent_t fork, join;
+};
+
 // nbuffers buffers of nterms float32 terms each, one after another at
 // `terms`; out[k] gets buffer k's running sum (NaN if a term is negative or
-// not finite).
+// not finite).  side may be null: then the walk follows the maps on
+// `stream` alone.
 hipError_t launch_float_sums(const float *terms, int64_t nterms, int nbuffers, float *out, void *workspace,
-                             hipStream_t stream);
+                             hipStream_t stream, const SideStream *side);
 
 }  // namespace vqx

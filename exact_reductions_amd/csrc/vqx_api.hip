@@ -310,6 +310,56 @@ int cached_copy_stream(hipStream_t stream, hipStream_t *out)
     return VQX_OK;
 }
 
+// The float sums' second stream and its two events: one set per device,
+// made on first use (default priority, non-blocking) and kept until the
+// process ends.  A call holds side_mutex while it enqueues its work, so
+// that calls from several host threads do not interleave their records
+// and waits on the shared events.
+std::mutex side_mutex;
+vqx::SideStream side_streams[kMaxDevices];
+bool side_made[kMaxDevices];
+
+// *out: the set of the device `stream` belongs to, or null where it cannot
+// be made (the walk then follows the maps on the caller's stream).  Call
+// with side_mutex held.
+int float_sum_side(hipStream_t stream, const vqx::SideStream **out)
+{
+    *out = nullptr;
+    int current = 0, dev = 0;
+    if (hipGetDevice(&current) != hipSuccess) {
+        (void)hipGetLastError();
+        return VQX_E_HIP;
+    }
+    dev = current;
+    if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return VQX_E_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return VQX_E_NO_DEVICE;
+    if (!side_made[dev]) {
+        side_made[dev] = true;  // one attempt per device
+        if (dev != current && hipSetDevice(dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return VQX_OK;
+        }
+        vqx::SideStream s{};
+        bool ok = hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) == hipSuccess;
+        ok = ok && hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) == hipSuccess;
+        ok = ok && hipEventCreateWithFlags(&s.join, hipEventDisableTiming) == hipSuccess;
+        if (dev != current)
+            (void)hipSetDevice(current);
+        if (!ok) {
+            (void)hipGetLastError();
+            return VQX_OK;
+        }
+        side_streams[dev] = s;
+    }
+    if (side_streams[dev].stream)
+        *out = &side_streams[dev];
+    return VQX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -432,8 +482,13 @@ int vqx_float_running_sums_ws(const float *terms, long long nterms, int nbuffers
     rc = device_ready();
     if (rc != VQX_OK)
         return rc;
-    if (vqx::launch_float_sums(terms, nterms, nbuffers, out_sums, workspace, static_cast<hipStream_t>(stream)) !=
-        hipSuccess) {
+    std::lock_guard<std::mutex> lock(side_mutex);
+    const vqx::SideStream *side = nullptr;
+    rc = float_sum_side(static_cast<hipStream_t>(stream), &side);
+    if (rc != VQX_OK)
+        return rc;
+    if (vqx::launch_float_sums(terms, nterms, nbuffers, out_sums, workspace, static_cast<hipStream_t>(stream),
+                               side) != hipSuccess) {
         (void)hipGetLastError();
         return VQX_E_HIP;
     }

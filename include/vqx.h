@@ -441,6 +441,13 @@ int vqx_conclude_psnr_int_batch(const uint64_t *noise, int w, int h, int bpc, in
  * memory, 16-byte aligned, written before it is read (contents on entry do
  * not matter); calls may not share one workspace concurrently.  The call
  * only queues work on `stream`; results are valid once the stream passes it.
+ * Part of the work runs on a second stream of the device's own (made on the
+ * first call, kept until the process ends), forked from `stream` and joined
+ * back to it by events; a graph captured from `stream` takes it in.  The
+ * environment variable VQX_FLOAT_SUM_WAIT_TICKS (0 to 100000000, in 10 ns
+ * ticks, read on each call) bounds one wait of the part on that stream for
+ * the maps made on `stream` (default 100000: past it the part after them
+ * does the work); the results do not depend on it.
  *
  * Errors: VQX_E_NULL; VQX_E_DIMS (nterms < 0 or > 2^36); VQX_E_NFRAMES
  * (nbuffers outside 1..65535); VQX_E_ALIGN; VQX_E_WORKSPACE; VQX_E_NO_DEVICE;

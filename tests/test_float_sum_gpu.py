@@ -132,3 +132,72 @@ def test_no_terms_and_workspace_reuse():
         out = vqx.float_running_sums(t, workspace=ws)
         torch.cuda.synchronize()
         assert_bitwise(terms, out.cpu().numpy())
+
+
+def test_calls_from_two_host_threads():
+    """Calls on two streams from two host threads at once: each call's walk
+    runs on the device's second stream, which the calls share in turn."""
+    import threading
+    inputs = [synth.hvs_like_terms(2500, 3, seed=20 + k) for k in range(2)]
+    want = [oracle.running_float_sums(x) for x in inputs]
+    errors = []
+
+    def work(k):
+        try:
+            s = torch.cuda.Stream()
+            t = torch.from_numpy(inputs[k]).cuda()
+            torch.cuda.synchronize()
+            for _ in range(6):
+                with torch.cuda.stream(s):
+                    out = vqx.float_running_sums(t, stream=s)
+                s.synchronize()
+                got = out.cpu().numpy()
+                if not np.array_equal(got.view(np.uint32), want[k].view(np.uint32)):
+                    errors.append((k, got, want[k]))
+        except Exception as e:  # reported below, in the test's thread
+            errors.append((k, repr(e)))
+
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors[:2]
+
+
+def test_graph_capture_replays():
+    """The call captured into a graph (its second stream joins the capture)
+    gives the eager result on every replay, with eager work between."""
+    terms = synth.hvs_like_terms(1800, 2, seed=31)
+    want = oracle.running_float_sums(terms)
+    t = torch.from_numpy(terms).cuda()
+    ws = torch.empty(vqx.float_sum_workspace_bytes(terms.shape[1], 2), dtype=torch.uint8, device="cuda:0")
+    out = torch.full((2,), -7.0, dtype=torch.float32, device="cuda:0")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        vqx.float_running_sums(t, stream=s, out=out, workspace=ws)  # eager, before the capture
+    s.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), want.view(np.uint32))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        vqx.float_running_sums(t, stream=s, out=out, workspace=ws)
+    for k in range(3):
+        out.fill_(-7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (k, got, want)
+        _ = (t * 2.0).sum().item()  # eager work between replays
+
+
+def test_walk_beside_the_maps_gives_up(monkeypatch):
+    """With the bound of one wait set to 0 the walk beside the map kernel
+    gives up at its first wait; the walk after the map kernel (with its own
+    takers of the queue) then walks those buffers, to the same bits."""
+    monkeypatch.setenv("VQX_FLOAT_SUM_WAIT_TICKS", "0")
+    cases = [synth.hvs_like_terms(2200, 3, seed=41),
+             np.stack([synth.float_terms(3 * 4096 + 77, "ties", seed=5),
+                       synth.float_terms(3 * 4096 + 77, "spread", seed=6)])]
+    for terms in cases:
+        assert_bitwise(terms, device_sums(terms))
