@@ -34,26 +34,28 @@
 //     predicts the binade the float sum is in there, with a margin;
 //  3. fsum_tile_maps: each tile's map in the predicted binade (and the
 //     next, where the tile may cross into it), tiles handed out across the
-//     buffers so that all buffers' maps appear at one pace; a tile with a
-//     tie or a large term goes on a queue instead;
+//     buffers so that all buffers' maps appear at one pace; from binary32
+//     sums of h, or term by term in order where the tile holds a tie or a
+//     large term;
 //  4. fsum_walk: one workgroup per buffer walks it -- with the running
 //     value S, scans up to 1024 tile maps at once for S's binade and
 //     applies all of them up to the first tile that has no map for that
 //     binade or whose map leaves it; that tile is taken as 256 runs of 16
 //     terms, scanned the same way, and the run where S leaves its binade is
-//     added term by term in binary32 -- while further workgroups take the
-//     queue's tiles and make their maps term by term, in order.  Every step
-//     is checked against S itself, so a prediction decides only how fast
-//     the walk is, never what it returns.
+//     added term by term in binary32.  Every step is checked against S
+//     itself, so a prediction decides only how fast the walk is, never what
+//     it returns.
 //
 // Step 4 runs on a second stream while step 3 still makes the maps: each
 // map is published in 64-bit words that carry their own "ready" bit,
 // written and read with relaxed device-scope atomics (single-copy atomic
 // and coherent across the XCDs' L2s, so no fence is needed: a word is
 // either seen whole or seen as not ready).  A walk waits at a tile whose
-// map is not out yet; its waits are bounded, and past the bound it adds
-// such a tile from its terms, which needs no map.
+// map is not out yet; its waits are bounded, and a walk that reaches the
+// bound leaves its buffer to step 4 again, run after step 3 on the
+// caller's stream.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -84,8 +86,7 @@ struct Map {
 };
 
 // A tile's record: its plan (binades predicted) and its maps, published.
-//   w0: bit 63 ready, bit 62 queued (the maps come from the ordered path,
-//       not out yet), bits 61..60 the count of planned binades (0..2),
+//   w0: bit 63 ready, bits 61..60 the count of planned binades (0..2),
 //       bits 59..52 the first binade's unit exponent + 149, bits 51..0 the
 //       map in the first binade;
 //   w1: bit 63 ready, bits 51..0 the map in the second binade.
@@ -99,7 +100,6 @@ struct alignas(32) Rec {
 static_assert(sizeof(Rec) == 32, "records stay 32 bytes");
 
 constexpr uint64_t kReady = 1ull << 63;
-constexpr uint64_t kQueued = 1ull << 62;
 
 __device__ __forceinline__ uint64_t pack_map(const Map &m)
 {
@@ -129,21 +129,18 @@ __device__ __forceinline__ uint64_t observe(const uint64_t *p)
     return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void publish(uint32_t *p, uint32_t v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 __device__ __forceinline__ uint32_t observe(const uint32_t *p)
 {
     return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The ordered-path queue: queue[0] counts the items taken, queue[1] the
-// walks beside the maps that have ended, queue[2] those of them that gave
-// up, and item k is queue[3 + k] = (buffer * ntiles + tile) + 1, 0 until it
-// is written.
-constexpr int kQueueHead = 3;
+// A buffer's done word, per call: open (cleared by fsum_plan), walked by
+// the walk beside the map kernel (which then writes the result), given up
+// by it, or claimed by the walk after the map kernel (which then writes
+// the result).  The two walks change it by compare-and-swap from open, so
+// exactly one of them writes each result.
+enum : uint32_t { kOpen = 0, kWalked = 1, kGivenUp = 2, kClaimed = 3 };
+
 
 __device__ __forceinline__ Map identity_map() { return {0u, 0u, 0u}; }
 __device__ __forceinline__ Map leaving_map() { return {kSat, 0u, 0u}; }
@@ -439,11 +436,9 @@ __device__ __forceinline__ void workgroup_sum_or(float &s, uint32_t &o)
 // grid (tiles, buffers): each tile's total (binary32 adds in any order: a
 // prediction only) and whether any term is negative or not finite.
 __global__ __launch_bounds__(kThreads) void fsum_tile_totals(const float *terms, int64_t nterms, int ntiles,
-                                                             double *totals, uint32_t *bad, uint32_t *queue)
+                                                             double *totals, uint32_t *bad)
 {
     const int tile = blockIdx.x, buf = blockIdx.y;
-    if (threadIdx.x == 0)
-        queue[kQueueHead + static_cast<int64_t>(buf) * ntiles + tile] = 0;  // one queue slot per tile
     const int64_t first = static_cast<int64_t>(tile) * kTile;
     float s = 0.0f;
     uint32_t b = 0;
@@ -474,59 +469,130 @@ __device__ __forceinline__ int unit_exponent_of(double v)
 
 // One workgroup per buffer: the running total at each tile start and the
 // binades the float sum may be in over each tile.  plan = (unit exponent of
-// the first + 256) | (count << 16), count 0 (no maps), 1 or 2.
+// the first + 256) | (count << 16), count 0 (no maps), 1 or 2.  The totals
+// pass through LDS kPlanChunk at a time: read coalesced (every load of a
+// chunk in flight at once), summed in order by thread runs of kPlanPer, the
+// runs' sums scanned, the plans made along each run, and the records
+// written coalesced.
+constexpr int kPlanPer = 16;
+constexpr int kPlanChunk = kThreads * kPlanPer;
+
 __global__ __launch_bounds__(kThreads) void fsum_plan(const double *totals, const uint32_t *bad, int ntiles,
-                                                      Rec *recs, uint32_t *buffer_bad, uint32_t *ordered)
+                                                      Rec *recs, uint32_t *buffer_bad, uint32_t *done)
 {
     const int buf = blockIdx.x;
-    if (buf == 0 && threadIdx.x == 0) {
-        ordered[0] = 0;  // the ordered-path queue, filled by fsum_tile_maps
-        ordered[1] = 0;
-        ordered[2] = 0;
-    }
+    const int me = static_cast<int>(threadIdx.x);
+    if (me == 0)
+        done[buf] = kOpen;
     const double *tot = totals + static_cast<int64_t>(buf) * ntiles;
     const uint32_t *bd = bad + static_cast<int64_t>(buf) * ntiles;
     Rec *rc = recs + static_cast<int64_t>(buf) * ntiles;
-    const int per = (ntiles + kThreads - 1) / kThreads;
-    const int lo = threadIdx.x * per, hi = lo + per < ntiles ? lo + per : ntiles;
-    double mine = 0.0;
-    uint32_t b = 0;
-    for (int i = lo; i < hi; ++i) {
-        mine += tot[i];
-        b |= bd[i];
-    }
+    // chunk entry i at i + i/kPlanPer: a pad per run keeps a run's serial
+    // reads (and the plans' writes) spread over the banks
+    __shared__ double tl[kPlanChunk + kThreads];
+    __shared__ uint32_t pl[kPlanChunk + kThreads];
     __shared__ double ex[kThreads];
+    constexpr double kMargin = 1.0 / 128;  // the float sum's drift from the exact one, allowed
+    double base = 0.0;  // the running total before the chunk (a prediction: any order of adds will do)
+    uint32_t b = 0;
+    for (int c0 = 0; c0 < ntiles; c0 += kPlanChunk) {
+        const int cn = ntiles - c0 < kPlanChunk ? ntiles - c0 : kPlanChunk;
+        double v[kPlanPer];
+        uint32_t f[kPlanPer];
+#pragma unroll
+        for (int j = 0; j < kPlanPer; ++j) {
+            const int i = me + j * kThreads;
+            const int64_t at = c0 + (i < cn ? i : 0);
+            v[j] = tot[at];
+            f[j] = bd[at];
+        }
+#pragma unroll
+        for (int j = 0; j < kPlanPer; ++j) {
+            const int i = me + j * kThreads;
+            tl[i + i / kPlanPer] = i < cn ? v[j] : 0.0;
+            b |= i < cn ? f[j] : 0u;
+        }
+        __syncthreads();
+        const double *run = tl + me * (kPlanPer + 1);
+        double mine = 0.0;
+#pragma unroll
+        for (int j = 0; j < kPlanPer; ++j)
+            mine += run[j];
+        ex[me] = mine;
+        __syncthreads();
+        for (int d = 1; d < kThreads; d <<= 1) {
+            const double y = me >= d ? ex[me - d] : 0.0;
+            __syncthreads();
+            ex[me] += y;
+            __syncthreads();
+        }
+        double p = base + (ex[me] - mine);
+        const double chunk_total = ex[kThreads - 1];
+        uint32_t *mine_pl = pl + me * (kPlanPer + 1);
+#pragma unroll
+        for (int j = 0; j < kPlanPer; ++j) {
+            const double t = run[j];
+            const int e_lo = unit_exponent_of(p * (1.0 - kMargin));
+            const int e_hi = unit_exponent_of((p + t) * (1.0 + kMargin));
+            const int n = e_hi - e_lo + 1;
+            const int count = n <= 2 ? n : 0;
+            mine_pl[j] = static_cast<uint32_t>(e_lo + 256) | (static_cast<uint32_t>(count) << 16);
+            p += t;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kPlanPer; ++j) {
+            const int i = me + j * kThreads;
+            if (i < cn) {
+                const uint32_t plan = pl[i + i / kPlanPer];
+                Rec &r = rc[c0 + i];
+                r.plan = plan;
+                // a tile without maps is ready now; the others once their maps are
+                r.w0 = (plan >> 16) == 0 ? kReady | rec_head(0, static_cast<int>(plan & 0xffffu) - 256) : 0;
+                r.w1 = 0;
+            }
+        }
+        base += chunk_total;
+        __syncthreads();  // before the next chunk overwrites the LDS
+    }
     __shared__ uint32_t anybad;
-    if (threadIdx.x == 0)
+    if (me == 0)
         anybad = 0;
-    ex[threadIdx.x] = mine;
     __syncthreads();
     if (b)
         atomicOr(&anybad, 1u);
-    // exclusive prefix of the threads' totals (a prediction: the order of
-    // these double adds does not matter)
-    for (int d = 1; d < kThreads; d <<= 1) {
-        const double v = static_cast<int>(threadIdx.x) >= d ? ex[threadIdx.x - d] : 0.0;
-        __syncthreads();
-        ex[threadIdx.x] += v;
-        __syncthreads();
-    }
-    double p = ex[threadIdx.x] - mine;
-    constexpr double kMargin = 1.0 / 128;  // the float sum's drift from the exact one, allowed
-    for (int i = lo; i < hi; ++i) {
-        const int e_lo = unit_exponent_of(p * (1.0 - kMargin));
-        const int e_hi = unit_exponent_of((p + tot[i]) * (1.0 + kMargin));
-        const int n = e_hi - e_lo + 1;
-        const int count = n <= 2 ? n : 0;
-        rc[i].plan = static_cast<uint32_t>(e_lo + 256) | (static_cast<uint32_t>(count) << 16);
-        // a tile without maps is ready now; the others once their maps are
-        rc[i].w0 = count == 0 ? kReady | rec_head(0, e_lo) : 0;
-        rc[i].w1 = 0;
-        p += tot[i];
-    }
     __syncthreads();
-    if (threadIdx.x == 0)
+    if (me == 0)
         buffer_bad[buf] = anybad;
+}
+
+// A tile's maps in its planned binades, in order, term by term (where it
+// holds a tie, a large term, or its unit is too small to scale to),
+// published.  All threads must call it.
+__device__ void ordered_maps(const float *terms, int64_t nterms, int ntiles, Rec *recs, uint32_t at, uint32_t *lds)
+{
+    const int buf = static_cast<int>(at / static_cast<uint32_t>(ntiles));
+    const int tile = static_cast<int>(at - static_cast<uint32_t>(buf) * static_cast<uint32_t>(ntiles));
+    const uint32_t pl = recs[at].plan;
+    const int n = static_cast<int>(pl >> 16);
+    const int uexp = static_cast<int>(pl & 0xffffu) - 256;
+    const int64_t first = static_cast<int64_t>(tile) * kTile;
+    load_tile(terms + static_cast<int64_t>(buf) * nterms + first, nterms - first, lds);
+    Map m[2];
+    for (int k = 0; k < n; ++k) {
+        // this thread's run, term by term (one term in registers at a time)
+        const uint32_t *r = lds + threadIdx.x * (kRun + 1);
+        Map x = identity_map();
+#pragma unroll 1
+        for (int j = 0; j < kRun; ++j)
+            x = compose(x, term_map(r[j], uexp + k));
+        m[k] = reduce_maps(x);
+    }
+    if (threadIdx.x == 0) {
+        if (n == 2)
+            publish(&recs[at].w1, kReady | pack_map(m[1]));
+        publish(&recs[at].w0, kReady | rec_head(n, uexp) | pack_map(m[0]));
+    }
 }
 
 // ------------------------------------------------------------- kernel 3
@@ -546,7 +612,7 @@ __global__ __launch_bounds__(kThreads) void fsum_plan(const double *totals, cons
 // 0 of every buffer, then tile 1, ...): each planned tile's map in its one
 // or two binades, published.
 __global__ __launch_bounds__(kThreads) void fsum_tile_maps(const float *terms, int64_t nterms, int ntiles,
-                                                           int nbuffers, Rec *recs, uint32_t *ordered)
+                                                           int nbuffers, Rec *recs)
 {
     const uint32_t cell = blockIdx.x;
     const int tile = static_cast<int>(cell / static_cast<uint32_t>(nbuffers));
@@ -607,13 +673,13 @@ __global__ __launch_bounds__(kThreads) void fsum_tile_maps(const float *terms, i
         lh[1][threadIdx.x >> 6] = H1;
     }
     __syncthreads();
-    // a tile that needs the ordered path in any of its binades goes on the
-    // queue, whose takers write all its maps; until then its record says so
+    // a tile that needs the ordered path in any of its binades (a tie, a
+    // large term, or a unit too small to scale to) has all its maps made
+    // term by term, in order, from the tile staged in LDS (read again: such
+    // tiles are few)
     if (flags & 3u) {
-        if (threadIdx.x == 0) {
-            publish(&recs[at].w0, kReady | kQueued | rec_head(n, uexp));
-            publish(&ordered[kQueueHead + atomicAdd(&ordered[0], 1u)], static_cast<uint32_t>(at) + 1u);
-        }
+        __shared__ uint32_t lds[kPad];
+        ordered_maps(terms, nterms, ntiles, recs, static_cast<uint32_t>(at), lds);
         return;
     }
     if (threadIdx.x == 0) {
@@ -633,29 +699,6 @@ __global__ __launch_bounds__(kThreads) void fsum_tile_maps(const float *terms, i
             publish(&recs[at].w1, kReady | pack_map(m[1]));
         publish(&recs[at].w0, kReady | rec_head(n, uexp) | pack_map(m[0]));
     }
-}
-
-// A queued tile's maps in its planned binades, in order, term by term
-// (ties, large terms, or a unit too small to scale to), published.  All
-// threads must call it.
-__device__ void ordered_maps(const float *terms, int64_t nterms, int ntiles, Rec *recs, uint32_t at, uint32_t *lds)
-{
-    const int buf = static_cast<int>(at / static_cast<uint32_t>(ntiles));
-    const int tile = static_cast<int>(at - static_cast<uint32_t>(buf) * static_cast<uint32_t>(ntiles));
-    const uint32_t pl = recs[at].plan;
-    const int n = static_cast<int>(pl >> 16);
-    const int uexp = static_cast<int>(pl & 0xffffu) - 256;
-    const int64_t first = static_cast<int64_t>(tile) * kTile;
-    load_tile(terms + static_cast<int64_t>(buf) * nterms + first, nterms - first, lds);
-    Map m[2];
-    for (int k = 0; k < n; ++k)
-        m[k] = reduce_maps(run_map(lds, uexp + k));
-    if (threadIdx.x == 0) {
-        if (n == 2)
-            publish(&recs[at].w1, kReady | pack_map(m[1]));
-        publish(&recs[at].w0, kReady | rec_head(n, uexp) | pack_map(m[0]));
-    }
-    __syncthreads();  // before the next item overwrites the LDS
 }
 
 // ------------------------------------------------------------- kernel 4
@@ -785,8 +828,6 @@ __device__ uint32_t walk_tile(const uint32_t *lds, uint32_t S, bool one_by_one)
     return S;
 }
 
-// Workgroups of the walk kernel that take the queue's items.
-constexpr int kTakers = 64;
 
 // One workgroup per buffer.  A window is kWindow tiles, kPerThread
 // consecutive ones per thread.
@@ -796,85 +837,45 @@ constexpr int kWindow = kThreads * kPerThread;
 // The walk waits where a map is not out yet.  While it waits one lane
 // looks at the tile's record and at one kAhead tiles on (the map kernel
 // hands tiles out in order, so most of the tiles between are out by then),
-// every kNap (s_sleep units of 64 clocks); a taker of the queue does the
-// same for the queue's next item.  Beside the map kernel a wait gets new
-// maps within microseconds; one that lasts kWaitBound (wall clock ticks,
-// 100 MHz) means the map kernel is not running beside it (a tool or a
-// graph that runs the two streams' kernels one after the other): the walk
-// gives up its buffer, which the walk after the map kernel takes.  There, a
-// wait that long makes the walk add a tile without its map from the tile's
-// terms (which needs no map) instead.
+// every kNap (s_sleep units of 64 clocks).  Beside the map kernel a wait
+// gets new maps within microseconds; one that lasts the bound (kWaitBound
+// wall clock ticks of 10 ns, unless set otherwise) means the map kernel is
+// not running beside it (a tool or a graph that runs the two streams'
+// kernels one after the other): the walk gives up its buffer.  The walk
+// after the map kernel waits up to the same bound for the buffer's done
+// word to leave kOpen, and walks the buffer where it was given up or where
+// it claims it; it never waits for a map: every map is out by then.
 constexpr int kAhead = 128;
 constexpr int kNap = 16;
-constexpr uint64_t kWaitBound = 100000;  // 1 ms, unless VQX_FLOAT_SUM_WAIT_TICKS sets it
+constexpr uint64_t kWaitBound = 100000;  // 1 ms
 
-// The queue's takers beside the map kernel: workgroup nbuffers + j takes
-// items j, j + kTakers, ... as fsum_tile_maps writes them, until every walk
-// beside it has ended.
-__device__ void take_queue(const float *terms, int64_t nterms, int ntiles, int nbuffers, Rec *recs,
-                           uint32_t *queue, uint64_t wait_bound, uint32_t *lds)
-{
-    __shared__ uint32_t shared_item;
-    const uint32_t cells = static_cast<uint32_t>(ntiles) * static_cast<uint32_t>(nbuffers);
-    for (uint32_t i = blockIdx.x - static_cast<uint32_t>(nbuffers);; i += kTakers) {
-        if (threadIdx.x == 0) {
-            uint32_t item = 0;
-            const uint64_t start = wall_clock64();
-            for (;;) {
-                item = i < cells ? observe(&queue[kQueueHead + i]) : 0u;
-                if (item != 0 || observe(&queue[1]) == static_cast<uint32_t>(nbuffers) ||
-                    wall_clock64() - start > wait_bound)
-                    break;
-                __builtin_amdgcn_s_sleep(kNap);
-            }
-            shared_item = item;
-        }
-        __syncthreads();
-        const uint32_t item = shared_item;
-        __syncthreads();
-        if (item == 0)
-            return;  // every walk beside the map kernel has ended (or the bound is reached)
-        ordered_maps(terms, nterms, ntiles, recs, item - 1u, lds);
-    }
-}
-
-// The queue's takers after the map kernel, where a walk gave up its buffer
-// (or all walk there): the queued tiles whose maps are not out.
-__device__ void take_rest(const float *terms, int64_t nterms, int ntiles, int nbuffers, Rec *recs,
-                          const uint32_t *queue, bool all, uint32_t *lds)
-{
-    if (!all && queue[2] == 0)
-        return;  // every walk beside the map kernel finished its buffer
-    const uint32_t count = queue[0];
-    for (uint32_t i = blockIdx.x - static_cast<uint32_t>(nbuffers); i < count; i += kTakers) {
-        const uint32_t at = queue[kQueueHead + i] - 1u;
-        if (observe(&recs[at].w0) & kQueued)
-            ordered_maps(terms, nterms, ntiles, recs, at, lds);
-    }
-}
-
-// Workgroups 0 .. nbuffers-1: one per buffer, the buffer's running sum
-// into out[buf]; then kTakers takers of the queue (none where there are no
-// tiles).  wait_bound: kWaitBound, or as set.  live: beside
-// fsum_tile_maps, on the second stream; each walk
-// sets done[buf] to 1 where it wrote out[buf], to 0 where it gave up.
-// Otherwise after fsum_tile_maps: the buffers whose done is 0 (all of them
-// where done is null).
-__global__ __launch_bounds__(kThreads) void fsum_walk(const float *terms, int64_t nterms, int ntiles, int nbuffers,
-                                                      Rec *recs, const uint32_t *buffer_bad, uint32_t *queue,
-                                                      uint32_t *done, float *out, int live, uint64_t wait_bound)
+// One workgroup per buffer: the buffer's running sum into out[buf].
+// live: beside fsum_tile_maps, on the second stream.  Otherwise after it,
+// on the caller's stream: the buffers the walk beside gave up or did not
+// finish in time (all of them where done is null).
+__global__ __launch_bounds__(kThreads) void fsum_walk(const float *terms, int64_t nterms, int ntiles,
+                                                      const Rec *recs, const uint32_t *buffer_bad, uint32_t *done,
+                                                      float *out, int live, uint64_t wait_bound)
 {
     __shared__ uint32_t lds[kPad];
-    if (static_cast<int>(blockIdx.x) >= nbuffers) {
-        if (live)
-            take_queue(terms, nterms, ntiles, nbuffers, recs, queue, wait_bound, lds);
-        else
-            take_rest(terms, nterms, ntiles, nbuffers, recs, queue, done == nullptr, lds);
-        return;
-    }
-    if (!live && done && done[blockIdx.x])
-        return;  // walked beside the map kernel
     const int buf = blockIdx.x;
+    if (!live && done) {
+        __shared__ uint32_t shared_state;
+        if (threadIdx.x == 0) {
+            const uint64_t start = wall_clock64();
+            uint32_t state = observe(&done[buf]);
+            while (state == kOpen && wall_clock64() - start <= wait_bound) {
+                __builtin_amdgcn_s_sleep(kNap);
+                state = observe(&done[buf]);
+            }
+            if (state == kOpen)
+                state = atomicCAS(&done[buf], kOpen, kClaimed);  // kOpen: claimed here
+            shared_state = state;
+        }
+        __syncthreads();
+        if (shared_state == kWalked)
+            return;  // walked beside the map kernel
+    }
     // beside the map kernel, this workgroup's few waves share each SIMD
     // with its: it issues first, since the buffer's result waits on it
     __builtin_amdgcn_s_setprio(3);
@@ -886,7 +887,7 @@ __global__ __launch_bounds__(kThreads) void fsum_walk(const float *terms, int64_
     if (ntiles > 0 && buffer_bad[buf])
         S = kNaN;
     int t0 = 0;
-    bool patient = true;   // waits allowed (after the map kernel: the bound not reached)
+    bool patient = live != 0;  // waits allowed (beside the map kernel, within the bound)
     bool gave_up = false;  // beside it: a wait reached the bound
     while (t0 < ntiles && S != kInf && S != kNaN) {
         // the window's records, read once: this thread's tiles are
@@ -901,7 +902,6 @@ __global__ __launch_bounds__(kThreads) void fsum_walk(const float *terms, int64_
             w1[c] = observe(&r.w1);
         }
         const int wend = ntiles - t0 < kWindow ? ntiles : t0 + kWindow;
-        const bool walk_queued = !patient;  // otherwise queued tiles wait for their takers
         int lo = t0;          // the window's tiles before lo are added
         int wait_at = -1;     // a tile whose map is not out yet: wait, then read again from there
         while (lo < wend && S != kInf) {
@@ -917,14 +917,14 @@ __global__ __launch_bounds__(kThreads) void fsum_walk(const float *terms, int64_
                 const int tile = t0 + me * kPerThread + c;
                 const bool in = tile >= lo && tile < wend;
                 const uint64_t a = w0[c];
-                const bool ready = (a & kReady) != 0, queued = (a & kQueued) != 0;
+                const bool ready = (a & kReady) != 0;
                 const int cnt = static_cast<int>((a >> 60) & 3u);
                 const int e0 = static_cast<int>((a >> 52) & 0xffu) - 149;
                 // no map for S's binade: the tile stops the scan and is
                 // added from its terms
                 Map y = leaving_map();
-                bool wait = !ready || (queued && !walk_queued);
-                if (ready && !queued) {
+                bool wait = !ready;
+                if (ready) {
                     if (cnt >= 1 && uexp == e0) {
                         y = unpack_map(a);
                     } else if (cnt == 2 && uexp == e0 + 1) {
@@ -1002,16 +1002,15 @@ __global__ __launch_bounds__(kThreads) void fsum_walk(const float *terms, int64_
         }
         if (wait_at >= 0) {
             // one lane waits, within the bound, until the tile's maps are
-            // out (its queued mark gone, where queued tiles are waited for)
-            // and the record kAhead tiles on (or the last) is written; the
-            // workgroup then reads the window again
+            // out and the record kAhead tiles on (or the last) is written;
+            // the workgroup then reads the window again
             if (me == 0) {
                 const int probe = wait_at + kAhead < ntiles ? wait_at + kAhead : ntiles - 1;
                 auto maps_out = [&]() {
                     const uint64_t a = observe(&rb[wait_at].w0);
-                    if (!(a & kReady) || ((a & kQueued) && !walk_queued))
+                    if (!(a & kReady))
                         return false;
-                    if (((a >> 60) & 3u) == 2u && !(a & kQueued) && !(observe(&rb[wait_at].w1) & kReady))
+                    if (((a >> 60) & 3u) == 2u && !(observe(&rb[wait_at].w1) & kReady))
                         return false;
                     return (observe(&rb[probe].w0) & kReady) != 0;
                 };
@@ -1037,14 +1036,10 @@ __global__ __launch_bounds__(kThreads) void fsum_walk(const float *terms, int64_
         t0 = lo;
     }
     if (threadIdx.x == 0) {
-        if (!gave_up)
+        if (!live)
             out[buf] = __uint_as_float(S);
-        if (live) {
-            done[buf] = gave_up ? 0u : 1u;
-            if (gave_up)
-                atomicAdd(&queue[2], 1u);
-            atomicAdd(&queue[1], 1u);  // the takers beside the map kernel stop once every walk has ended
-        }
+        else if (atomicCAS(&done[buf], kOpen, gave_up ? kGivenUp : kWalked) == kOpen && !gave_up)
+            out[buf] = __uint_as_float(S);  // not claimed by the walk after the map kernel
     }
 }
 
@@ -1061,8 +1056,7 @@ FloatSumLayout float_sum_layout(int64_t nterms, int nbuffers)
     l.recs = up(l.bad + cells * sizeof(uint32_t));
     l.buffer_bad = up(l.recs + cells * sizeof(Rec));
     l.done = up(l.buffer_bad + static_cast<size_t>(nbuffers) * sizeof(uint32_t));
-    l.ordered = up(l.done + static_cast<size_t>(nbuffers) * sizeof(uint32_t));
-    l.bytes = up(l.ordered + (kQueueHead + cells) * sizeof(uint32_t));
+    l.bytes = up(l.done + static_cast<size_t>(nbuffers) * sizeof(uint32_t));
     return l;
 }
 
@@ -1076,8 +1070,7 @@ hipError_t launch_float_sums(const float *terms, int64_t nterms, int nbuffers, f
     Rec *recs = reinterpret_cast<Rec *>(ws + l.recs);
     uint32_t *buffer_bad = reinterpret_cast<uint32_t *>(ws + l.buffer_bad);
     uint32_t *done = reinterpret_cast<uint32_t *>(ws + l.done);
-    uint32_t *ordered = reinterpret_cast<uint32_t *>(ws + l.ordered);
-    // queue items and the map grid's workgroups are counted in 32 bits
+    // the map grid's workgroups are counted in 32 bits
     // (terms resident in device memory keep the tile count far below 2^32)
     const int64_t cells = static_cast<int64_t>(l.ntiles) * nbuffers;
     if (cells >= (int64_t{1} << 32))
@@ -1093,20 +1086,35 @@ hipError_t launch_float_sums(const float *terms, int64_t nterms, int nbuffers, f
     }
     if (l.ntiles > 0) {
         const dim3 grid(static_cast<unsigned>(l.ntiles), static_cast<unsigned>(nbuffers));
-        fsum_tile_totals<<<grid, kThreads, 0, stream>>>(terms, nterms, l.ntiles, totals, bad, ordered);
-        fsum_plan<<<dim3(static_cast<unsigned>(nbuffers)), kThreads, 0, stream>>>(totals, bad, l.ntiles, recs,
-                                                                                  buffer_bad, ordered);
+        fsum_tile_totals<<<grid, kThreads, 0, stream>>>(terms, nterms, l.ntiles, totals, bad);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess)
             return err;
-        // the fork: the walk beside the maps starts once the plan is out
+        // the fork: the walk beside the maps starts once the plan is out.
+        // The event is the plan kernel's own completion, which puts no
+        // marker between it and the map kernel -- except while the stream
+        // is captured into a graph, which follows recorded events only.
+        bool capturing = false;
         if (side) {
-            err = hipEventRecord(side->fork, stream);
+            hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+            err = hipStreamIsCapturing(stream, &st);
+            if (err != hipSuccess)
+                return err;
+            capturing = st != hipStreamCaptureStatusNone;
+        }
+        {
+            int nt = l.ntiles;
+            void *args[] = {&totals, &bad, &nt, &recs, &buffer_bad, &done};
+            err = hipExtLaunchKernel(reinterpret_cast<const void *>(&fsum_plan), dim3(static_cast<unsigned>(nbuffers)),
+                                     dim3(kThreads), args, 0, stream, nullptr,
+                                     side && !capturing ? side->fork : nullptr, 0);
+            if (err == hipSuccess && side && capturing)
+                err = hipEventRecord(side->fork, stream);
             if (err != hipSuccess)
                 return err;
         }
         fsum_tile_maps<<<dim3(static_cast<unsigned>(cells)), kThreads, 0, stream>>>(terms, nterms, l.ntiles,
-                                                                                    nbuffers, recs, ordered);
+                                                                                    nbuffers, recs);
         err = hipGetLastError();
         if (err != hipSuccess)
             return err;
@@ -1116,24 +1124,30 @@ hipError_t launch_float_sums(const float *terms, int64_t nterms, int nbuffers, f
             err = hipStreamWaitEvent(side->stream, side->fork, 0);
             if (err != hipSuccess)
                 return err;
-            fsum_walk<<<dim3(static_cast<unsigned>(nbuffers + kTakers)), kThreads, 0, side->stream>>>(
-                terms, nterms, l.ntiles, nbuffers, recs, buffer_bad, ordered, done, out, 1, bound);
-            err = hipGetLastError();
-            if (err == hipSuccess)
+            int nt = l.ntiles, live = 1;
+            const Rec *rc = recs;
+            const uint32_t *bb = buffer_bad;
+            void *args[] = {const_cast<float **>(&terms), &nterms, &nt, &rc, &bb, &done, &out, &live, &bound};
+            err = hipExtLaunchKernel(reinterpret_cast<const void *>(&fsum_walk), dim3(static_cast<unsigned>(nbuffers)),
+                                     dim3(kThreads), args, 0, side->stream, nullptr,
+                                     capturing ? nullptr : side->join, 0);
+            if (err == hipSuccess && capturing)
                 err = hipEventRecord(side->join, side->stream);
-            if (err == hipSuccess)
-                err = hipStreamWaitEvent(stream, side->join, 0);
             if (err != hipSuccess)
                 return err;
         }
     }
     // after the map kernel on the caller's stream: the buffers the walk
-    // beside it gave up, or all; with no tiles, the walks alone (each
-    // writes +0) and no takers
+    // beside it gave up or did not finish within the bound, or all (each
+    // writes +0 where there are no tiles); then the join, which also keeps
+    // the stream from passing the call before the walk beside has ended
     const bool beside = l.ntiles > 0 && side;
-    fsum_walk<<<dim3(static_cast<unsigned>(l.ntiles > 0 ? nbuffers + kTakers : nbuffers)), kThreads, 0, stream>>>(
-        terms, nterms, l.ntiles, nbuffers, recs, buffer_bad, ordered, beside ? done : nullptr, out, 0, bound);
-    return hipGetLastError();
+    fsum_walk<<<dim3(static_cast<unsigned>(nbuffers)), kThreads, 0, stream>>>(
+        terms, nterms, l.ntiles, recs, buffer_bad, beside ? done : nullptr, out, 0, bound);
+    hipError_t err = hipGetLastError();
+    if (err == hipSuccess && beside)
+        err = hipStreamWaitEvent(stream, side->join, 0);
+    return err;
 }
 
 }  // namespace vqx

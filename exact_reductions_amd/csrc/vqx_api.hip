@@ -345,8 +345,9 @@ int float_sum_side(hipStream_t stream, const vqx::SideStream **out)
         }
         vqx::SideStream s{};
         bool ok = hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) == hipSuccess;
-        ok = ok && hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) == hipSuccess;
-        ok = ok && hipEventCreateWithFlags(&s.join, hipEventDisableTiming) == hipSuccess;
+        // (events that a launch can record, so timing events)
+        ok = ok && hipEventCreate(&s.fork) == hipSuccess;
+        ok = ok && hipEventCreate(&s.join) == hipSuccess;
         if (dev != current)
             (void)hipSetDevice(current);
         if (!ok) {
