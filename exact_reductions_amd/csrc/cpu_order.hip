@@ -690,23 +690,6 @@ struct ItemData {
     int all_ok;  // every vector of the slab inside the chunk (wave-uniform)
 };
 
-// Makes the compiler forget what it knows of the vectors' values, so that
-// the terms derived from them are recomputed rather than kept live (the
-// paths that need them again are the uncommon ones).
-template <int KK>
-__device__ __forceinline__ void forget(u32x4 (&a)[kLaneVectors], u32x4 (&b)[kLaneVectors])
-{
-#pragma unroll
-    for (int j = 0; j < kLaneVectors; ++j) {
-        if constexpr (KK != kSqDist)
-            asm volatile("" : "+v"(a[j]));
-        if constexpr (KK != kSqRef)
-            asm volatile("" : "+v"(b[j]));
-    }
-}
-
-// Slab [sb, sb + 256) of the chunk [cb, ce), cb < ce; the slab may start
-// past ce in the chunk after a frame's last whole vector.
 template <int KK, bool kSh>
 __device__ __forceinline__ void load_item(ItemData &x, const u32x4 *R, const u32x4 *D, const VecMap &M,
                                           int64_t frame, int64_t cb, int64_t sb, int64_t ce)
@@ -731,11 +714,34 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Rearranges the slab through the wave's LDS (kSlabVectors vectors per
-// plane) so that lane l holds vectors 4l .. 4l + 3: its 32 terms are then
-// consecutive in raster order.
+// Rearranges the slab through the wave's LDS (kSlabVectors vectors, one
+// plane after the other) so that lane l holds vectors 4l .. 4l + 3: its 32
+// terms are then consecutive in raster order.
 template <int KK>
 __device__ __forceinline__ void consecutive(u32x4 (&a)[kLaneVectors], u32x4 (&b)[kLaneVectors], u32x4 *lds)
+{
+    const int lane = threadIdx.x & 63;
+    auto transpose = [&](u32x4 (&x)[kLaneVectors]) {
+#pragma unroll
+        for (int j = 0; j < kLaneVectors; ++j)
+            lds[64 * j + lane] = x[j];
+        wave_lds_sync();
+#pragma unroll
+        for (int j = 0; j < kLaneVectors; ++j)
+            x[j] = lds[kLaneVectors * lane + j];
+        wave_lds_sync();  // the next use may overwrite the buffer
+    };
+    if constexpr (KK != kSqDist)
+        transpose(a);
+    if constexpr (KK != kSqRef)
+        transpose(b);
+}
+
+// The same with both planes' slabs in LDS at once (2 kSlabVectors vectors:
+// plane a, then plane b), each left there in load order (vector v at v):
+// the walk reads single terms from it afterwards.
+template <int KK>
+__device__ __forceinline__ void consecutive_kept(u32x4 (&a)[kLaneVectors], u32x4 (&b)[kLaneVectors], u32x4 *lds)
 {
     const int lane = threadIdx.x & 63;
     u32x4 *la = lds, *lb = lds + kSlabVectors;
@@ -754,42 +760,37 @@ __device__ __forceinline__ void consecutive(u32x4 (&a)[kLaneVectors], u32x4 (&b)
         if constexpr (KK != kSqRef)
             b[j] = lb[kLaneVectors * lane + j];
     }
-    wave_lds_sync();  // the next slab may overwrite the buffer
+    wave_lds_sync();
 }
 
 // What one pass over the lane's 32 consecutive terms gathers for binade
-// 2^(k+52), a pair of terms (j, j + 16) at a time in the two 16-bit halves
-// of a register: only the low k + 1 <= 5 bits of t2 = t + 2^(k-1) matter
-// here (rr, whether it is a tie, and h's parity), and they come from the
-// terms' low 16 bits.  Bit i of `untied` and `odd` is term i's (j in bit j,
-// j + 16 in bit j + 16: term order); rr2 holds the two halves' sums of rr.
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
+// 2^(k+52), four terms at a time, one per byte of a register: only the low
+// k + 1 <= 5 bits of t2 = t + 2^(k-1) matter here (rr, whether it is a
+// tie, and h's parity), and they come from the terms' low k + 1 bits.
+// Quad J holds terms J, J + 8, J + 16 and J + 24 (bytes 0..3), each masked
+// to its low k + 1 bits, so that adding 2^(k-1) to every byte carries into
+// no other byte.  Bit i of `untied` and `odd` is term i's (term order);
+// rr4 holds the four bytes' sums of rr (at most 8 terms of rr < 2^k <= 16
+// each: below 256).
 struct SlabPass {
-    uint32_t rr2 = 0;   // sum of rr, per 16-bit half
+    uint32_t rr4 = 0;     // sum of rr, per byte
     uint32_t untied = 0;  // bit i: term i is no tie (rr > 0)
-    uint32_t odd = 0;   // bit i: h_i is odd (bit k of t2)
+    uint32_t odd = 0;     // bit i: h_i is odd (bit k of t2)
 };
 
 template <int J>
-__device__ __forceinline__ void pass_pair(SlabPass &p, uint32_t ta, uint32_t tb, int k)
+__device__ __forceinline__ void pass_quad(SlabPass &p, uint32_t quad, int k)
 {
-    static_assert(J >= 0 && J < 16, "pair index");
-    const u16x2 half = {static_cast<unsigned short>(1u << (k - 1)), static_cast<unsigned short>(1u << (k - 1))};
-    const u16x2 mask = {static_cast<unsigned short>((1u << k) - 1), static_cast<unsigned short>((1u << k) - 1)};
-    const u16x2 one = {1, 1};
-    // the low halves of terms J and J + 16, then t2 and rr of each
-    const u16x2 t2 = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(tb, ta, 0x05040100u)) + half;
-    const u16x2 rr = t2 & mask;
-    p.rr2 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, p.rr2) + rr);
-    // 1 where rr > 0 (not a tie), in bits J and J + 16: min(rr, 1) per half
-    uint32_t untied;
-    asm("v_pk_min_u16 %0, %1, %2" : "=v"(untied) : "v"(__builtin_bit_cast(uint32_t, rr)), "v"(__builtin_bit_cast(uint32_t, one)));
-    p.untied |= untied << J;
-    // bit k of each half, rotated to bits J and J + 16
-    const uint32_t rot = __builtin_amdgcn_alignbit(__builtin_bit_cast(uint32_t, t2), __builtin_bit_cast(uint32_t, t2),
-                                                   static_cast<uint32_t>(k - J) & 31u);
-    p.odd |= rot & ((1u << J) | (1u << (J + 16)));
+    static_assert(J >= 0 && J < 8, "quad index");
+    constexpr uint32_t kBytes = 0x01010101u;
+    const uint32_t t2 = (quad & (((2u << k) - 1u) * kBytes)) + (1u << (k - 1)) * kBytes;
+    const uint32_t rr = t2 & (((1u << k) - 1u) * kBytes);
+    p.rr4 += rr;
+    // bit 7 of each byte: rr > 0 (rr + 127 stays below 256); then bit 7
+    // and bit k of byte b rotated to bit 8b + J
+    const uint32_t nz = rr + 0x7f7f7f7fu;
+    p.untied |= __builtin_amdgcn_alignbit(nz, nz, static_cast<uint32_t>(7 - J)) & (kBytes << J);
+    p.odd |= __builtin_amdgcn_alignbit(t2, t2, static_cast<uint32_t>(k - J) & 31u) & (kBytes << J);
 }
 
 // The lane's run map from its pass (RunMap's packing: per start parity s,
@@ -834,29 +835,32 @@ __device__ __forceinline__ Map2 slab_map(uint64_t T, uint32_t low_bits, const Sl
     constexpr uint64_t n = 64 * kLaneVectors * kTerms;
     if (__all((low_bits & ((1u << k) - 1)) == 0))
         return untied_map(T >> k);
-    const uint32_t RR = wave_total32((p.rr2 & 0xffffu) + (p.rr2 >> 16));
+    const uint32_t RR = wave_total32((p.rr4 & 0xffu) + ((p.rr4 >> 8) & 0xffu) + ((p.rr4 >> 16) & 0xffu) + (p.rr4 >> 24));
     if (__all(p.untied == ~0u))
         return untied_map((T + (n << (k - 1)) - RR) >> k);
     return run_map(wave_run(lane_run_map(p)), T, n, RR, k);
 }
 
-// The pass over the lane's 32 consecutive terms, pair by pair.
-template <int KK>
-__device__ __forceinline__ void pass_slab(SlabPass &p, const u32x4 (&a)[kLaneVectors], const u32x4 (&b)[kLaneVectors],
-                                          int k)
+// The pass over the lane's 32 consecutive terms, quad by quad: quads[J]
+// holds the low bytes of terms J, J + 8, J + 16 and J + 24.
+__device__ __forceinline__ void pass_slab(SlabPass &p, const uint32_t (&quads)[8], int k)
 {
-    static_assert(kLaneVectors * kTerms == 32, "two halves of 16 terms");
-#define VQX_PAIR(J) pass_pair<J>(p, vector_term<KK>(a[(J) / 8], b[(J) / 8], (J) % 8), \
-                                 vector_term<KK>(a[(J) / 8 + 2], b[(J) / 8 + 2], (J) % 8), k)
-    VQX_PAIR(0); VQX_PAIR(1); VQX_PAIR(2); VQX_PAIR(3); VQX_PAIR(4); VQX_PAIR(5); VQX_PAIR(6); VQX_PAIR(7);
-    VQX_PAIR(8); VQX_PAIR(9); VQX_PAIR(10); VQX_PAIR(11); VQX_PAIR(12); VQX_PAIR(13); VQX_PAIR(14); VQX_PAIR(15);
-#undef VQX_PAIR
+    static_assert(kLaneVectors * kTerms == 32, "four quarters of 8 terms");
+    pass_quad<0>(p, quads[0], k);
+    pass_quad<1>(p, quads[1], k);
+    pass_quad<2>(p, quads[2], k);
+    pass_quad<3>(p, quads[3], k);
+    pass_quad<4>(p, quads[4], k);
+    pass_quad<5>(p, quads[5], k);
+    pass_quad<6>(p, quads[6], k);
+    pass_quad<7>(p, quads[7], k);
 }
 
-// Slab si of its chunk; lane 0 writes its part of the entry.  One pass over
-// the terms gives the total, the low bits and the pass for the predicted
-// binade; a slab whose chunk may cross into the next binade gets a second
-// pass for it.
+// Slab si of its chunk; lane 0 writes its part of the entry.  The terms
+// are made once: their sum (the total), and the low bytes of each quad
+// (J, J + 8, J + 16, J + 24), which are all the passes need (the low bits,
+// and the pass for the predicted binade; a slab whose chunk may cross into
+// the next binade gets a second pass for it).
 template <int KK>
 __device__ __forceinline__ void item_maps(ItemData &x, int si, int e, bool dual, uint64_t *entry, u32x4 *lds)
 {
@@ -868,26 +872,34 @@ __device__ __forceinline__ void item_maps(ItemData &x, int si, int e, bool dual,
     }
     consecutive<KK>(x.a, x.b, lds);
     // the lane's total (a 64-bit sum kept as two words and a carry add)
-    uint32_t lo = 0, hi = 0, low_bits = 0;
+    uint32_t lo = 0, hi = 0, quad_or = 0;
+    uint32_t quads[8];
 #pragma unroll
-    for (int j = 0; j < kLaneVectors; ++j)
+    for (int J = 0; J < 8; ++J) {
+        uint32_t t[4];
 #pragma unroll
-        for (int i = 0; i < kTerms; ++i) {
-            const uint32_t t = vector_term<KK>(x.a[j], x.b[j], i);
+        for (int v = 0; v < 4; ++v) {
+            t[v] = vector_term<KK>(x.a[v], x.b[v], J);  // term J + 8v
             unsigned int carry;
-            lo = __builtin_addc(lo, t, 0u, &carry);
+            lo = __builtin_addc(lo, t[v], 0u, &carry);
             hi += carry;
-            low_bits |= t;
         }
+        // bytes 0..3: the low bytes of terms J, J + 8, J + 16, J + 24
+        const uint32_t lo2 = __builtin_amdgcn_perm(t[1], t[0], 0x0c0c0400u);
+        const uint32_t hi2 = __builtin_amdgcn_perm(t[3], t[2], 0x0c0c0400u);
+        quads[J] = lo2 | (hi2 << 16);
+        quad_or |= quads[J];
+    }
+    // the OR of the terms' low bytes (only bits below k <= 4 are asked)
+    const uint32_t low_bits = (quad_or | (quad_or >> 8) | (quad_or >> 16) | (quad_or >> 24)) & 0xffu;
     const uint64_t T = wave_total64(lo | (static_cast<uint64_t>(hi) << 32));
     SlabPass p;
-    pass_slab<KK>(p, x.a, x.b, k);
+    pass_slab(p, quads, k);
     const Map2 slab = slab_map(T, low_bits, p, k);
     Map2 slab_b;
     if (dual) {
-        forget<KK>(x.a, x.b);
         SlabPass q;
-        pass_slab<KK>(q, x.a, x.b, k + 1);
+        pass_slab(q, quads, k + 1);
         slab_b = slab_map(T, low_bits, q, k + 1);
     }
     if ((threadIdx.x & 63) == 0) {
@@ -1003,15 +1015,16 @@ __device__ __forceinline__ void queue_maps(const Slabs &Q, uint32_t *ticket, int
 // frame writes the prefix's results.
 // Two-byte samples map slabs; one-byte ones only scan (one workgroup per
 // frame).
-// Four waves per SIMD fit its registers without spills (128 VGPRs).
+// Five waves per SIMD fit its registers without spills (96 VGPRs), and its
+// LDS (a 4 KB buffer per wave).
 template <bool kSh>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void cpu_order_maps(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) void cpu_order_maps(
     const void *ref, const void *dist, int64_t pixels, int chunks, int nframes, uint64_t *rec,
     uint64_t *totals, uint64_t *out_noise, uint64_t *out_moments, uint64_t *out_cpu_noise, uint64_t *out_cpu_moments,
     uint64_t *queue, uint64_t *maps, VecMap vmap)
 {
     __shared__ PrefixLds pl;
-    __shared__ u32x4 lds_all[kThreads / 64][2 * kSlabVectors];
+    __shared__ u32x4 lds_all[kThreads / 64][kSlabVectors];
     // frame f's workgroups are f, f + nframes, ...: spread over the launch
     // order, so that each frame has workgroups of every age on the CUs
     // (older waves issue first) and the frames progress together
@@ -1213,7 +1226,7 @@ __device__ __forceinline__ uint64_t walk_slab(uint64_t S, const Planes &P, int64
         load_vector<KK, kSh>(P.R, P.D, P.map, P.frame, v, v < se, sb, a[j], b[j]);
         keep_if<KK>(v < se, a[j], b[j]);
     }
-    consecutive<KK>(a, b, lds);
+    consecutive_kept<KK>(a, b, lds);
     Item g;
     RunMap mA, mB;
     uint32_t rA = 0, rB = 0;
@@ -1478,7 +1491,7 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cpu_order_walk(const void *re
                                                                   uint64_t *out_cpu_noise, uint64_t *out_cpu_moments,
                                                                   VecMap vmap)
 {
-    __shared__ u32x4 lds[2 * kSlabVectors];  // a slab of each plane, for `consecutive`
+    __shared__ u32x4 lds[2 * kSlabVectors];  // a slab of each plane, for `consecutive_kept`
     const int64_t frame = blockIdx.x / kSquares;
     const int kk = static_cast<int>(blockIdx.x - frame * kSquares);
     if (totals[frame * kSquares + kk] < kTwo53)  // the prefix wrote the CPU's value
@@ -1602,11 +1615,13 @@ hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, cons
     const bool shifted = map.general != 0;
     // at two-byte samples, as many workgroups per frame as the device holds
     // at once over all frames (at least one), never more than the frame can
-    // have slabs for, and at most kMaxPerFrame: each runs the frame's scan
-    // for itself, and past that more of them cost more scans than they save
-    // (a 3840x2160x32 batch with nothing to map: 166 us a step at 16
-    // against 169 us at 32)
-    constexpr int64_t kMaxPerFrame = 16;
+    // have slabs for, and with at most kScanChunks chunks scanned per frame:
+    // each workgroup runs the frame's scan for itself, and past that more
+    // of them cost more scans than they save (a 3840x2160x32 batch, 507
+    // chunks a frame, with nothing to map: 166 us a step at 16 workgroups a
+    // frame against 169 us at 32; a 2560x1440x64 one, 225 chunks, maps
+    // 1.5 us faster at 20 than at 16)
+    constexpr int64_t kScanChunks = 8192;
     int64_t per_frame = 1;
     if (two_byte) {
         int64_t resident = 0;
@@ -1616,7 +1631,8 @@ hipError_t launch_plane_stats_cpu_order(const Geometry &g, const void *ref, cons
         const int64_t most = (static_cast<int64_t>(g.chunks) * kSquares * kSlabs + kThreads / 64 - 1) / (kThreads / 64);
         per_frame = resident / g.nframes;
         per_frame = per_frame < 1 ? 1 : per_frame > most ? most : per_frame;
-        per_frame = per_frame > kMaxPerFrame ? kMaxPerFrame : per_frame;
+        const int64_t scans = kScanChunks / g.chunks;
+        per_frame = per_frame > scans ? (scans > 1 ? scans : 1) : per_frame;
     }
     const dim3 wgs(static_cast<unsigned>(g.nframes * per_frame));
     uint64_t *maps_arg = two_byte ? maps : nullptr;
