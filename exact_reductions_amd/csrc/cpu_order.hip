@@ -60,6 +60,7 @@
 // below 2^41 and step 2 already gives the CPU's values.
 
 #include <atomic>
+#include <type_traits>
 
 #include "plane_stats.h"
 #include "terms.h"
@@ -566,13 +567,42 @@ __device__ __forceinline__ void frame_prefix(PrefixLds &L, int64_t f, int nframe
     const int c1 = c0 + per < chunks ? c0 + per : chunks;
     const uint64_t *frec = rec + f * chunks * kRecordStride;
     // the thread's sums of each record field, then their exclusive prefixes
-    // over the frame and the frame's totals
+    // over the frame and the frame's totals.  The thread's first kKept
+    // chunks (all of them up to kKept * kThreads chunks a frame) keep what
+    // the passes below need in registers: read once, all loads in flight
+    // together (a chunk the thread lacks reads chunk 0 and drops it).
+    constexpr int kKept = 2;
     uint64_t local[kSums], run[kSums], total[kSums];
+    uint64_t kept_t[kKept][kSquares];
+    uint32_t kept_low[kKept];
 #pragma unroll
     for (int j = 0; j < kSums; ++j)
         local[j] = 0;
     uint32_t low_or = 0;
-    for (int c = c0; c < c1; ++c) {
+    {
+        uint64_t v[kKept][kSums + 1];
+#pragma unroll
+        for (int i = 0; i < kKept; ++i) {
+            const int c = c0 + i < c1 ? c0 + i : 0;
+#pragma unroll
+            for (int j = 0; j <= kSums; ++j)
+                v[i][j] = frec[c * kRecordStride + j];  // kLowBits follows the sums
+        }
+        static_assert(kLowBits == kSums, "the low bits follow the sums in a record");
+#pragma unroll
+        for (int i = 0; i < kKept; ++i) {
+            const bool mine = c0 + i < c1;
+#pragma unroll
+            for (int j = 0; j < kSums; ++j)
+                local[j] += mine ? v[i][j] : 0;
+            kept_low[i] = mine ? static_cast<uint32_t>(v[i][kSums]) : 0u;
+            low_or |= kept_low[i];
+#pragma unroll
+            for (int kk = 0; kk < kSquares; ++kk)
+                kept_t[i][kk] = mine ? v[i][record_field(kk)] : 0;
+        }
+    }
+    for (int c = c0 + kKept; c < c1; ++c) {
 #pragma unroll
         for (int j = 0; j < kSums; ++j)
             local[j] += frec[c * kRecordStride + j];
@@ -624,17 +654,33 @@ __device__ __forceinline__ void frame_prefix(PrefixLds &L, int64_t f, int nframe
         __syncthreads();
         return;
     }
+    // f(c, T, low bits) for the thread's chunks of square sum kk, in order:
+    // the kept ones from registers (each at a fixed index), then the rest
+    auto each_chunk = [&](auto kkc, auto f) {
+        constexpr int kk = decltype(kkc)::value;
+#pragma unroll
+        for (int i = 0; i < kKept; ++i)
+            if (c0 + i < c1)
+                f(c0 + i, kept_t[i][kk], kept_low[i]);
+        for (int c = c0 + kKept; c < c1; ++c)
+            f(c, frec[c * kRecordStride + record_field(kk)], static_cast<uint32_t>(frec[c * kRecordStride + kLowBits]));
+    };
+    // each square sum in turn, with its index known at compile time
+    auto each_square = [&](auto body) {
+        body(std::integral_constant<int, 0>{});
+        body(std::integral_constant<int, 1>{});
+        body(std::integral_constant<int, 2>{});
+    };
+    static_assert(kSquares == 3, "three square sums");
     // pass 1: chunk maps, and how many chunks the thread queues
     uint64_t nq = 0;  // 21 bits per square sum
-#pragma unroll
-    for (int kk = 0; kk < kSquares; ++kk) {
+    each_square([&](auto kkc) {
+        constexpr int kk = decltype(kkc)::value;
         if (exact[kk])
-            continue;
-        const int field = record_field(kk);
-        uint64_t p = run[field];
-        for (int c = c0; c < c1; ++c) {
-            const uint64_t T = frec[c * kRecordStride + field];
-            const uint32_t low = (static_cast<uint32_t>(frec[c * kRecordStride + kLowBits]) >> (4 * kk)) & 15u;
+            return;
+        uint64_t p = run[record_field(kk)];
+        each_chunk(kkc, [&](int c, uint64_t T, uint32_t lows) {
+            const uint32_t low = (lows >> (4 * kk)) & 15u;
             const ChunkCase x = chunk_case(p, T, low, static_cast<int64_t>(c) * kChunkVectors < nvec);
             uint64_t *entry = maps + ((f * chunks + c) * kSquares + kk) * kEntry;
             if (x.chunk_only) {
@@ -650,8 +696,8 @@ __device__ __forceinline__ void frame_prefix(PrefixLds &L, int64_t f, int nframe
                 nq += x.queued ? 1ull << (21 * kk) : 0;
             }
             p += T;
-        }
-    }
+        });
+    });
     // each thread's first slot in the frame's segments, and their lengths
     uint64_t nq_total;
     const uint64_t at = wave_inclusive_then_total(nq, L.scan[kSums], nq_total) - nq;
@@ -659,24 +705,22 @@ __device__ __forceinline__ void frame_prefix(PrefixLds &L, int64_t f, int nframe
         L.nq[t] = static_cast<uint32_t>(nq_total >> (21 * t)) & 0x1fffffu;
     // pass 2: the queue items, in chunk order within the frame
     const int64_t cap = static_cast<int64_t>(nframes) * chunks;
-#pragma unroll
-    for (int kk = 0; kk < kSquares; ++kk) {
+    each_square([&](auto kkc) {
+        constexpr int kk = decltype(kkc)::value;
         if (exact[kk])
-            continue;
-        const int field = record_field(kk);
-        uint64_t p = run[field];
+            return;
+        uint64_t p = run[record_field(kk)];
         int64_t slot = f * chunks + ((at >> (21 * kk)) & 0x1fffffu);
-        for (int c = c0; c < c1; ++c) {
-            const uint64_t T = frec[c * kRecordStride + field];
-            const uint32_t low = (static_cast<uint32_t>(frec[c * kRecordStride + kLowBits]) >> (4 * kk)) & 15u;
+        each_chunk(kkc, [&](int c, uint64_t T, uint32_t lows) {
+            const uint32_t low = (lows >> (4 * kk)) & 15u;
             const ChunkCase x = chunk_case(p, T, low, static_cast<int64_t>(c) * kChunkVectors < nvec);
             if (x.queued)
                 queue[kk * cap + slot++] = static_cast<uint64_t>(f * chunks + c) |
                                            (static_cast<uint64_t>(x.e) << 32) |
                                            (static_cast<uint64_t>(x.dual) << 40);
             p += T;
-        }
-    }
+        });
+    });
     __syncthreads();  // the segments and their lengths, for the workgroup
 }
 
