@@ -201,3 +201,31 @@ def test_walk_beside_the_maps_gives_up(monkeypatch):
                        synth.float_terms(3 * 4096 + 77, "spread", seed=6)])]
     for terms in cases:
         assert_bitwise(terms, device_sums(terms))
+
+
+def test_alternating_workspaces_and_inputs():
+    """Calls alternate two workspaces and two inputs of different shapes: a
+    record word left in a workspace by the call before last is never taken
+    for this call's (every word is cleared before the maps are made)."""
+    a = synth.hvs_like_terms(2600, 3, seed=51)
+    b = np.stack([synth.float_terms(5 * 4096 + 9, kind, seed=52 + i) for i, kind in enumerate(("ties", "spread", "uniform"))])
+    want = {0: oracle.running_float_sums(a), 1: oracle.running_float_sums(b)}
+    ts = {0: torch.from_numpy(a).cuda(), 1: torch.from_numpy(b).cuda()}
+    wss = [torch.full((max(vqx.float_sum_workspace_bytes(x.shape[1], 3) for x in (a, b)),), 0xFF,
+                      dtype=torch.uint8, device="cuda:0") for _ in range(2)]
+    for call in range(8):
+        which = (call // 2) % 2  # inputs a, a, b, b, a, a, b, b; workspaces 0, 1, 0, 1, ...
+        out = vqx.float_running_sums(ts[which], workspace=wss[call % 2])
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), want[which].view(np.uint32)), (call, got, want[which])
+
+
+def test_walks_racing_for_buffers(monkeypatch):
+    """A bound of 50 ticks (0.5 us): the walk after the map kernel claims
+    most buffers while the walk beside it is still on them; the
+    compare-and-swap on each buffer's done word lets exactly one write it."""
+    monkeypatch.setenv("VQX_FLOAT_SUM_WAIT_TICKS", "50")
+    terms = synth.hvs_like_terms(3000, 8, seed=61)
+    for _ in range(3):
+        assert_bitwise(terms, device_sums(terms))
