@@ -538,6 +538,10 @@ __device__ __forceinline__ ChunkCase chunk_case(uint64_t p, uint64_t r, uint32_t
 // whole vectors, 2048 chunks.
 constexpr int kMaxFrameChunks = 2048;
 
+// Records staged per round of frame_prefix: 256 records of 64 bytes, the
+// maps kernel's transpose buffers (idle during the scan).
+constexpr int kStageRecords = 256;
+
 // The LDS of frame_prefix.
 struct PrefixLds {
     uint64_t scan[kSums + 1][kThreads / 64];
@@ -552,7 +556,7 @@ struct PrefixLds {
 // maps.  Every such workgroup writes the frame's queue items (the same
 // values), into the frame's own segment of each queue (capacity `chunks`,
 // in chunk order), and leaves their numbers in L.nq.
-__device__ __forceinline__ void frame_prefix(PrefixLds &L, int64_t f, int nframes, const uint64_t *rec,
+__device__ __forceinline__ void frame_prefix(PrefixLds &L, u32x4 *stage, int64_t f, int nframes, const uint64_t *rec,
                                              int64_t pixels, int chunks, bool writer, uint64_t *totals,
                                              uint64_t *out_noise, uint64_t *out_moments, uint64_t *out_cpu_noise,
                                              uint64_t *out_cpu_moments, uint64_t *maps, uint64_t *queue)
@@ -569,8 +573,7 @@ __device__ __forceinline__ void frame_prefix(PrefixLds &L, int64_t f, int nframe
     // the thread's sums of each record field, then their exclusive prefixes
     // over the frame and the frame's totals.  The thread's first kKept
     // chunks (all of them up to kKept * kThreads chunks a frame) keep what
-    // the passes below need in registers: read once, all loads in flight
-    // together (a chunk the thread lacks reads chunk 0 and drops it).
+    // the passes below need in registers, read once.
     constexpr int kKept = 2;
     uint64_t local[kSums], run[kSums], total[kSums];
     uint64_t kept_t[kKept][kSquares];
@@ -580,15 +583,58 @@ __device__ __forceinline__ void frame_prefix(PrefixLds &L, int64_t f, int nframe
         local[j] = 0;
     uint32_t low_or = 0;
     {
-        uint64_t v[kKept][kSums + 1];
-#pragma unroll
-        for (int i = 0; i < kKept; ++i) {
-            const int c = c0 + i < c1 ? c0 + i : 0;
-#pragma unroll
-            for (int j = 0; j <= kSums; ++j)
-                v[i][j] = frec[c * kRecordStride + j];  // kLowBits follows the sums
-        }
         static_assert(kLowBits == kSums, "the low bits follow the sums in a record");
+        static_assert(kRecordStride == 8, "a record is four 16-byte vectors");
+        uint64_t v[kKept][kSums + 1];
+        if (per <= kKept) {
+            // the frame's records pass through `stage` (kStageRecords at a
+            // time) read as consecutive 16-byte vectors, 1 KB per load
+            // instruction, rather than one record per lane (64 lines per
+            // instruction); each thread then takes its chunks' six words
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(frec);
+#pragma unroll
+            for (int i = 0; i < kKept; ++i)
+#pragma unroll
+                for (int j = 0; j <= kSums; ++j)
+                    v[i][j] = 0;
+            for (int r0 = 0; r0 < chunks; r0 += kStageRecords) {
+                const int n = chunks - r0 < kStageRecords ? chunks - r0 : kStageRecords;
+                u32x4 w[kStageRecords * 4 / kThreads];
+#pragma unroll
+                for (int k = 0; k < kStageRecords * 4 / kThreads; ++k) {
+                    const int idx = t + k * kThreads;  // vector idx of the round's records
+                    w[k] = src[static_cast<int64_t>(r0) * 4 + (idx < 4 * n ? idx : 0)];
+                }
+#pragma unroll
+                for (int k = 0; k < kStageRecords * 4 / kThreads; ++k)
+                    stage[t + k * kThreads] = w[k];
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < kKept; ++i) {
+                    const int c = c0 + i;
+                    if (c < c1 && c >= r0 && c < r0 + n) {
+                        const u32x4 *x = stage + (c - r0) * 4;
+#pragma unroll
+                        for (int q = 0; q < 3; ++q) {
+                            const u32x4 y = x[q];
+                            v[i][2 * q] = y.x | (static_cast<uint64_t>(y.y) << 32);
+                            v[i][2 * q + 1] = y.z | (static_cast<uint64_t>(y.w) << 32);
+                        }
+                    }
+                }
+                __syncthreads();  // before the next round overwrites the stage
+            }
+        } else {
+            // all loads in flight together (a chunk the thread lacks reads
+            // chunk 0 and drops it)
+#pragma unroll
+            for (int i = 0; i < kKept; ++i) {
+                const int c = c0 + i < c1 ? c0 + i : 0;
+#pragma unroll
+                for (int j = 0; j <= kSums; ++j)
+                    v[i][j] = frec[c * kRecordStride + j];  // kLowBits follows the sums
+            }
+        }
 #pragma unroll
         for (int i = 0; i < kKept; ++i) {
             const bool mine = c0 + i < c1;
@@ -608,8 +654,15 @@ __device__ __forceinline__ void frame_prefix(PrefixLds &L, int64_t f, int nframe
             local[j] += frec[c * kRecordStride + j];
         low_or |= static_cast<uint32_t>(frec[c * kRecordStride + kLowBits]);
     }
-    if (maps && low_or)
-        atomicOr(&L.frame_low, low_or);  // complete after the scan's barrier
+    if (maps) {
+        // the wave's OR first: an LDS atomic from every lane on one word
+        // serializes (~3 us a workgroup), one per wave does not
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1)
+            low_or |= __shfl_xor(low_or, d, 64);
+        if ((t & 63) == 0 && low_or)
+            atomicOr(&L.frame_low, low_or);  // complete after the scan's barrier
+    }
     wave_inclusive_then_total_n<kSums>(local, L.scan, run, total);
     // the square sums whose every add is exact (one-byte samples: all)
     bool exact[kSquares];
@@ -1074,8 +1127,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
     // (older waves issue first) and the frames progress together
     const int64_t f = blockIdx.x % nframes;
     const int j = static_cast<int>(blockIdx.x / nframes);
-    frame_prefix(pl, f, nframes, rec, pixels, chunks, j == 0, totals, out_noise, out_moments, out_cpu_noise,
+    static_assert(sizeof(lds_all) >= kStageRecords * 64, "the stage fits the transpose buffers");
+    // the scan at a raised issue priority: the SIMDs issue older waves
+    // first, so a workgroup still scanning beside others already mapping
+    // (a tight VALU loop) would otherwise wait behind them
+    __builtin_amdgcn_s_setprio(2);
+    frame_prefix(pl, &lds_all[0][0], f, nframes, rec, pixels, chunks, j == 0, totals, out_noise, out_moments, out_cpu_noise,
                  out_cpu_moments, maps, queue);
+    __builtin_amdgcn_s_setprio(0);
     if (!maps)
         return;
     // the wave's index, made wave-uniform so that the items' bookkeeping
