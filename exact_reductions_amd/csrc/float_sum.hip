@@ -409,15 +409,52 @@ __device__ __forceinline__ void for_tile_terms(const float *tile_base, int64_t c
 
 // Sum and OR over the workgroup; every thread gets both.  All threads must
 // call it.
+// Wave64 sums and ORs by DPP, at VALU speed (lane shuffles go through the
+// LDS crossbar): quad swaps and row rotates total each row of 16 lanes in
+// all its lanes, then row broadcasts carry rows 0..2 into the rows above,
+// so lane 63 ends with the wave's total.  (+ and | are commutative, so the
+// rows a broadcast leaves out keep their value either way.)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_from(uint32_t v)
+{
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROWS, 0xf, false));
+}
+
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op)
+{
+    v = op(v, dpp_from<0xb1, 0xf>(v));   // quad_perm [1,0,3,2]
+    v = op(v, dpp_from<0x4e, 0xf>(v));   // quad_perm [2,3,0,1]
+    v = op(v, dpp_from<0x124, 0xf>(v));  // row_ror:4
+    v = op(v, dpp_from<0x128, 0xf>(v));  // row_ror:8
+    v = op(v, dpp_from<0x142, 0xa>(v));  // row_bcast:15 into rows 1, 3
+    v = op(v, dpp_from<0x143, 0xc>(v));  // row_bcast:31 into rows 2, 3
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+__device__ __forceinline__ uint32_t wave_or_u32(uint32_t v)
+{
+    return wave_reduce(v, [](uint32_t a, uint32_t b) { return a | b; });
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v)
+{
+    return wave_reduce(v, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v)
+{
+    return __uint_as_float(wave_reduce(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+        return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+    }));
+}
+
 __device__ __forceinline__ void workgroup_sum_or(float &s, uint32_t &o)
 {
     __shared__ float ls[kThreads / 64];
     __shared__ uint32_t lo[kThreads / 64];
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) {
-        s += __shfl_down(s, d, 64);
-        o |= __shfl_down(o, d, 64);
-    }
+    s = wave_sum_f32(s);
+    o = wave_or_u32(o);
     if ((threadIdx.x & 63) == 0) {
         ls[threadIdx.x >> 6] = s;
         lo[threadIdx.x >> 6] = o;
@@ -659,20 +696,23 @@ __global__ __launch_bounds__(kThreads) void fsum_tile_maps(const float *terms, i
     const uint32_t leaves = (Hf0 >= 0x1p24f ? 1u : 0u) | (Hf1 >= 0x1p24f ? 2u : 0u);
     uint32_t H0 = static_cast<uint32_t>(Hf0 < 0x1p24f ? Hf0 : 0.0f);
     uint32_t H1 = static_cast<uint32_t>(Hf1 < 0x1p24f ? Hf1 : 0.0f);
-    float dummy = 0.0f;
-    uint32_t flags = odd | (leaves << 2) | (scalable ? 0u : 3u);
-    workgroup_sum_or(dummy, flags);
-    __shared__ uint32_t lh[2][kThreads / 64];
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) {
-        H0 += __shfl_down(H0, d, 64);
-        H1 += __shfl_down(H1, d, 64);
-    }
-    if ((threadIdx.x & 63) == 0) {
-        lh[0][threadIdx.x >> 6] = H0;
-        lh[1][threadIdx.x >> 6] = H1;
+    // the workgroup's flags and sums of h (each thread's below 2^24, so
+    // the 256 add up below 2^32), one barrier for all three
+    __shared__ uint32_t lh[3][kThreads / 64];
+    {
+        const uint32_t wf = wave_or_u32(odd | (leaves << 2) | (scalable ? 0u : 3u));
+        const uint32_t w0 = wave_sum_u32(H0), w1 = wave_sum_u32(H1);
+        if ((threadIdx.x & 63) == 0) {
+            lh[0][threadIdx.x >> 6] = w0;
+            lh[1][threadIdx.x >> 6] = w1;
+            lh[2][threadIdx.x >> 6] = wf;
+        }
     }
     __syncthreads();
+    uint32_t flags = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w)
+        flags |= lh[2][w];
     // a tile that needs the ordered path in any of its binades (a tie, a
     // large term, or a unit too small to scale to) has all its maps made
     // term by term, in order, from the tile staged in LDS (read again: such
