@@ -93,6 +93,22 @@ def test_many_buffers_one_call():
     assert_bitwise(terms, device_sums(terms))
 
 
+def test_thousands_of_small_buffers():
+    """4099 buffers of 700 terms in one call: the plan, map and walk grids
+    far past the device's resident workgroups, each buffer one ragged tile."""
+    kinds = ["uniform", "spread", "tiny", "ties", "stall", "ascending"]
+    rows = [synth.float_terms(700, kinds[k % len(kinds)], seed=100 + k) for k in range(4099)]
+    terms = np.stack(rows)
+    assert_bitwise(terms, device_sums(terms))
+
+
+def test_largest_buffer_count():
+    """65535 buffers (the most a call takes) of 3 terms each."""
+    rng = np.random.Generator(np.random.PCG64(65535))
+    terms = (rng.random((65535, 3)) * 2.0 ** rng.integers(-20, 21, (65535, 3))).astype(np.float32)
+    assert_bitwise(terms, device_sums(terms))
+
+
 def test_zeros_and_edges():
     cases = [
         np.zeros(10_000, dtype=np.float32),
