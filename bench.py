@@ -130,6 +130,14 @@ def stamp_interval(steps: int) -> int:
     return max(1, min(STAMP_EVERY, steps // MIN_STAMPED))
 
 
+def stamped_steps(steps: int) -> list:
+    """The timed steps (counted from 0) whose stage-1 dispatch is stamped:
+    one in stamp_interval(steps), from the middle of the first interval."""
+    every = stamp_interval(steps)
+    phase = every // 2 if steps > every // 2 else 0
+    return [j for j in range(steps) if j % every == phase]
+
+
 def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
@@ -929,12 +937,10 @@ def main(argv=None):
     # run stamps more often to keep the mean stable); other modes: events
     # around each group of steps
     every = stamp_interval(args.steps)
-    phase = every // 2 if args.steps > every // 2 else 0
     # the stamps only time the dispatch, and the host never waits on them, so
     # they are made without the system-scope fence (a write-back of the L2s
     # that an ordinary event performs when it is reached)
-    ev_begin = ({i: hip.create(HIP_EVENT_DISABLE_SYSTEM_FENCE)
-                 for i in range(args.warmup, total) if (i - args.warmup) % every == phase}
+    ev_begin = ({args.warmup + j: hip.create(HIP_EVENT_DISABLE_SYSTEM_FENCE) for j in stamped_steps(args.steps)}
                 if mode.per_step_events else {})
     ev_end = {i: hip.create(HIP_EVENT_DISABLE_SYSTEM_FENCE) for i in ev_begin}
     ngroups = (total + group - 1) // group + 1

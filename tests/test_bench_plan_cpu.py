@@ -53,3 +53,25 @@ def test_pitched_plans_follow_the_in_place_rule():
     assert bench.step_plan("cpu-order", wl, 3904, 4)[1][0] == "stage1_u16_mapped"
     assert bench.step_plan("exact", wl, 3904, 4)[1][0] == "view_stage1"
     assert bench.step_plan("exact", wl, 3904, 8)[1][0] == "stage1_u16_mapped"
+
+
+def test_stamping_events_flag_is_the_runtimes():
+    """The bench's stamping events are made without the system-scope fence:
+    its flag must be the HIP runtime's own hipEventDisableSystemFence."""
+    header = "/opt/rocm/include/hip/hip_runtime_api.h"
+    if not os.path.exists(header):
+        pytest.skip("no ROCm headers")
+    with open(header) as f:
+        m = re.search(r"#define\s+hipEventDisableSystemFence\s+(0x[0-9a-fA-F]+)", f.read())
+    assert m, "hipEventDisableSystemFence not defined in the HIP header"
+    assert bench.HIP_EVENT_DISABLE_SYSTEM_FENCE == int(m.group(1), 16)
+
+
+@pytest.mark.parametrize("steps", [1, 3, 8, 15, 16, 20, 63, 64, 65, 500])
+def test_short_runs_stamp_enough_dispatches(steps):
+    """At least MIN_STAMPED of the timed dispatches are stamped (all of them
+    in a run shorter than that), and never more often than needed."""
+    stamped = bench.stamped_steps(steps)
+    assert len(stamped) >= min(steps, bench.MIN_STAMPED)
+    assert all(0 <= j < steps for j in stamped) and stamped == sorted(set(stamped))
+    assert 1 <= bench.stamp_interval(steps) <= bench.STAMP_EVERY
