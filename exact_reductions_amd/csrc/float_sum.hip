@@ -9,9 +9,9 @@
 //   [MOMENT] "ADR-1447: float_moment_hip adds the float squares the CPU adds,
 //            and is bit-identical while the CPU's own sum is exact"
 //
-// calc_psnrhvs() adds every masked coefficient error of a plane into one
-// running float, and each add's rounding depends on the sum so far [HVS,
-// Context].  The page stores the terms on the device (64 per 8x8 block,
+// calc_psnrhvs() accumulates all of a plane's masked coefficient errors in
+// a single float, one at a time, so the rounding of each add depends on
+// the value accumulated before it [HVS, Context].  The page stores the terms on the device (64 per 8x8 block,
 // row-major, blocks in raster order) and sums them on the host [HVS,
 // Decision]; an order-preserving reduction on the device is its deferred
 // alternative [HVS, Alternatives].  This file is that reduction.

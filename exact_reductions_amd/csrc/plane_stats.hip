@@ -22,7 +22,7 @@
 // the reduction order irrelevant].
 //
 // 8 bits: every square is below 2^16 (< 2^24, exact in binary32 [PSNR,
-// Context]), so the float square IS the integer square, and the kernel uses
+// Context]), so the float and the integer square agree, and the kernel uses
 // integer dot products: sum r, sum d (v_sad_u8), sum r^2, sum d^2, sum r*d
 // (v_dot4_u32_u8), and noise = sum r^2 + sum d^2 - 2 sum r*d, an identity of
 // integers.
@@ -40,8 +40,8 @@
 // form for that group, otherwise the general one above.  Every form adds
 // the same integers, so the choice cannot change a sum.
 //  * Small samples (depths up to 12 bits; every sample below 4096): a
-//    square below 2^24 is exact in binary32, so the float square is the
-//    integer square [PSNR, Decision: up to 12 bits the square is exact],
+//    square below 2^24 is exact in binary32, so the float and the integer
+//    square agree [PSNR, Decision: at 12 bits or fewer no square rounds],
 //    and integer dot products give sum r^2, sum d^2, sum r*d, with
 //    sum (r-d)^2 = sum r^2 + sum d^2 - 2 sum r*d.
 //  * Bright samples (depths 13..16; every sample at least 49152): each

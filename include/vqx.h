@@ -420,9 +420,9 @@ int vqx_conclude_psnr_int_batch(const uint64_t *noise, int w, int h, int bpc, in
  * The psnr_hvs running float sum [HVS = "ADR-1397: GPU psnr_hvs twins
  * reproduce the CPU's running float sum bit for bit"].
  *
- * calc_psnrhvs() adds every masked coefficient error of a plane into one
- * running float, so each add's rounding depends on the sum so far [HVS,
- * Context]; the page's twins store the terms (64 per 8x8 block, row-major,
+ * calc_psnrhvs() accumulates all of a plane's masked coefficient errors in
+ * a single float, one at a time, so the rounding of each add depends on the
+ * value accumulated before it [HVS, Context]; the page's twins store the terms (64 per 8x8 block, row-major,
  * blocks in raster order) and add them one by one into a float on the host
  * [HVS, Decision].  This call does that sum on the device, with an
  * order-preserving reduction [HVS, Alternatives]: for each of `nbuffers`

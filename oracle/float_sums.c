@@ -13,8 +13,9 @@
  *   [PSNR]   "ADR-1440: float_psnr_hip adds its squared differences as
  *            integers and returns the CPU's score bit for bit" -- Context.
  *            The CPU turns both planes into float samples divided by
- *            scaler = 2^(bpc-8), squares each difference in float and adds
- *            the squares into a double, row by row.
+ *            scaler = 2^(bpc-8), forms the float square of every sample
+ *            difference and accumulates those squares in one double,
+ *            visiting the rows from the top.
  *   [MOMENT] "ADR-1447: float_moment_hip adds the float squares the CPU
  *            adds, and is bit-identical while the CPU's own sum is exact" --
  *            Context.  One double per output collects the (scaled) samples

@@ -9,12 +9,13 @@
  *
  * Source (web page, cited by title and section):
  *   [HVS] "ADR-1397: GPU psnr_hvs twins reproduce the CPU's running float
- *         sum bit for bit" -- Context: calc_psnrhvs() adds every masked
- *         coefficient error of a plane into one running float, 64 terms per
- *         8x8 block, and each add's rounding depends on the sum so far;
- *         Decision: the terms are stored row-major within a block, blocks in
- *         raster order, and the host adds a plane's terms one by one into a
- *         single float; the reference is built with contraction off.
+ *         sum bit for bit" -- Context: calc_psnrhvs() accumulates all of a
+ *         plane's masked coefficient errors (an 8x8 block gives 64) in a
+ *         single float, so the rounding of each add depends on the value
+ *         accumulated before it; Decision: the terms are laid out row-major
+ *         inside a block with the blocks in raster order, the host folds
+ *         them into one float in that order, and the reference code is
+ *         compiled without contraction.
  *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math.  On x86-64 a float add is
  * one SSE binary32 addition, rounded to nearest, ties to even; nothing here

@@ -74,7 +74,7 @@ def test_workloads(n):
 
 
 def test_past53_mixed_bit_identical():
-    """The 2560x1440 frame with a tenth of its samples below 4096: the CPU's
+    """The 2560x1440 frame in which one sample in ten is below 4096: the CPU's
     adds round, and the device returns the CPU's rounded value exactly."""
     ref, dist = synth.past53_mixed(nframes=2)
     assert check(ref, dist, 16, expect_past53=True) == 4
