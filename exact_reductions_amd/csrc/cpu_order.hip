@@ -30,10 +30,11 @@
 //
 //  1. stage 1 (plane_stats.hip) gives each chunk's exact totals;
 //  2. a prefix scan per frame (the exact running sum at each chunk start,
-//     which predicts the binade the CPU's sum is in there) writes every sum in which no add of the CPU's can round (those below
-//     2^53, and those whose terms share enough trailing zero bits to stay
-//     exact past it), maps the chunks past 2^53 inside which nothing can
-//     round, and queues the other chunks past 2^53;
+//     which predicts the binade the CPU's sum is in there) writes every
+//     sum in which no add of the CPU's can round (those below 2^53, and
+//     those whose terms share enough trailing zero bits to stay exact past
+//     it), maps the chunks past 2^53 inside which nothing can round, and
+//     queues the other chunks past 2^53;
 //  3. in the same launch (cpu_order_maps: a group of workgroups per frame,
 //     each running the frame's scan for itself), every slab of 256 vectors
 //     of a queued chunk gets its exact total and maps in the predicted

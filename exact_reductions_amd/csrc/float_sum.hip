@@ -11,10 +11,11 @@
 //
 // calc_psnrhvs() accumulates all of a plane's masked coefficient errors in
 // a single float, one at a time, so the rounding of each add depends on
-// the value accumulated before it [HVS, Context].  The page stores the terms on the device (64 per 8x8 block,
-// row-major, blocks in raster order) and sums them on the host [HVS,
-// Decision]; an order-preserving reduction on the device is its deferred
-// alternative [HVS, Alternatives].  This file is that reduction.
+// the value accumulated before it [HVS, Context].  The page stores the
+// terms on the device (64 per 8x8 block, row-major, blocks in raster
+// order) and sums them on the host [HVS, Decision]; an order-preserving
+// reduction on the device is its deferred alternative [HVS,
+// Alternatives].  This file is that reduction.
 //
 // The terms are nonnegative (squares), so the sum S never decreases.  While
 // S stays in one binade [2^E, 2^(E+1)), S = m * u with u = 2^(E-23) and
