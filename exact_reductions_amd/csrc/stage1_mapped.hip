@@ -41,10 +41,21 @@ static_assert(kLaneIters % kInFlight == 0, "whole load groups");
 // the VecMap; kLowBitsOut: also the low bits of the terms and zero item
 // tickets, for the CPU-order form; kForm: where the planes' vectors start
 // within 16-byte blocks -- all at 0 (kAligned: one 16-byte load per vector,
-// found with the map's pads), or anywhere (kCut: ref and dist the bases
-// rounded down to 16 bytes, each vector found with the map's byte strides
-// and cut from dword-aligned loads).
-enum : int { kAligned = 0, kCut = 1 };
+// found with the map's pads), at multiples of 4 bytes (kDword: ref and dist
+// the bases rounded down to 16 bytes, each vector found with the map's byte
+// strides and read with one dword-aligned 16-byte load), or anywhere (kCut:
+// the same, each vector cut from dword-aligned loads).
+enum : int { kAligned = 0, kCut = 1, kDword = 2 };
+
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+// The 16 bytes at byte offset `at` (a multiple of 4) from P, in one load,
+// non-temporal as every other read of the terms.
+__device__ __forceinline__ u32x4 load_vec16_dword(const u32x4 *P, uint32_t at)
+{
+    return __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4_a4 *>(reinterpret_cast<const unsigned char *>(P) + at));
+}
 
 template <bool kLowBitsOut, int kForm>
 __global__ __launch_bounds__(kThreads) void stage1_u16_mapped(const void *ref, const void *dist, int64_t pixels,
@@ -87,6 +98,11 @@ __global__ __launch_bounds__(kThreads) void stage1_u16_mapped(const void *ref, c
                     const int64_t ar = v + fr + row * M.pad_row_r, ad = v + fd + row * M.pad_row_d;
                     x[u] = __builtin_nontemporal_load(R + ar);
                     y[u] = __builtin_nontemporal_load(D + ad);
+                } else if constexpr (kForm == kDword) {
+                    const uint32_t yr = static_cast<uint32_t>(row);
+                    const uint32_t x16 = 16 * (r - yr * M.vpr);
+                    x[u] = load_vec16_dword(Rf, lor + yr * rbr + x16);
+                    y[u] = load_vec16_dword(Df, lod + yr * rbd + x16);
                 } else {
                     const uint32_t yr = static_cast<uint32_t>(row);
                     const uint32_t x16 = 16 * (r - yr * M.vpr);
@@ -137,6 +153,10 @@ hipError_t launch_stage1_mapped(const Geometry &g, const void *ref, const void *
     if (!map.general)
         stage1_u16_mapped<true, kAligned><<<grid, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, partials,
                                                                         map);
+    else if (((map.phase_r | map.phase_d) & 3u) == 0 &&
+             ((map.row_bytes_r | map.row_bytes_d | map.frame_bytes_r | map.frame_bytes_d) & 3) == 0)
+        // every vector starts at a multiple of 4 bytes from its base
+        stage1_u16_mapped<true, kDword><<<grid, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, partials, map);
     else
         stage1_u16_mapped<true, kCut><<<grid, kThreads, 0, stream>>>(ref, dist, g.pixels, g.chunks, partials, map);
     return hipGetLastError();
